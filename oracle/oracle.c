@@ -1,0 +1,171 @@
+/*
+ * CPU oracle (fp64). TEST INFRASTRUCTURE ONLY: see oracle.h for the contract,
+ * the format reading and who may use it. Built with gcc -O2, no -ffast-math.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int or_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double or_half_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -24);              /* subnormal: f * 2^-14 / 1024 */
+    } else if (e == 31) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024 + f), e - 25);  /* (1 + f/1024) * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+/*
+ * 6-bit fields of the Q4_K scale bytes s[0..11]:
+ *   j < 4 : sc[j] = low 6 bits of s[j],   m[j] = low 6 bits of s[j+4]
+ *   j >= 4: sc[j] = low nibble of s[j+4]  | (top 2 bits of s[j-4]) << 4
+ *           m[j]  = high nibble of s[j+4] | (top 2 bits of s[j])   << 4
+ */
+void or_q4k_unpack_scales(const uint8_t s[12], int sc[8], int m[8]) {
+    for (int j = 0; j < 4; ++j) {
+        sc[j] = s[j] & 63;
+        m[j] = s[j + 4] & 63;
+    }
+    for (int j = 4; j < 8; ++j) {
+        sc[j] = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+        m[j] = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+    }
+}
+
+/* Quant (0..15) of weight i (0..255) of a Q4_K block's 128 nibble bytes. */
+static int q4k_quant(const uint8_t* qs, int i) {
+    int g = i / 64;          /* 64-weight group, 32 bytes each */
+    int r = i % 64;
+    uint8_t byte = qs[32 * g + (r % 32)];
+    return (r < 32) ? (byte & 15) : (byte >> 4);
+}
+
+void or_q4k_dequant_block(const uint8_t blk[144], double w[256]) {
+    double d = or_half_to_double(rd16(blk));
+    double dmin = or_half_to_double(rd16(blk + 2));
+    int sc[8], m[8];
+    or_q4k_unpack_scales(blk + 4, sc, m);
+    const uint8_t* qs = blk + 16;
+    for (int i = 0; i < 256; ++i) {
+        int j = i / 32;
+        w[i] = d * sc[j] * q4k_quant(qs, i) - dmin * m[j];
+    }
+}
+
+void or_q8_0_dequant_block(const uint8_t blk[34], double w[32]) {
+    double d = or_half_to_double(rd16(blk));
+    for (int i = 0; i < 32; ++i) w[i] = d * (double)(int8_t)blk[2 + i];
+}
+
+void or_q4k_dequant_row(const uint8_t* row, int64_t K, double* w) {
+    for (int64_t b = 0; b < K / 256; ++b) or_q4k_dequant_block(row + 144 * b, w + 256 * b);
+}
+
+void or_q8_0_dequant_row(const uint8_t* row, int64_t K, double* w) {
+    for (int64_t b = 0; b < K / 32; ++b) or_q8_0_dequant_block(row + 34 * b, w + 32 * b);
+}
+
+/* Plain dot product, sequential in k, of a dequantized row with x. */
+static void dot_row(const double* w, const float* x, int64_t K, double* y, double* a) {
+    double s = 0.0, t = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = w[k] * (double)x[k];
+        s += p;
+        t += fabs(p);
+    }
+    *y = s;
+    if (a) *a = t;
+}
+
+typedef void (*dequant_row_fn)(const uint8_t*, int64_t, double*);
+
+static void gemv_dense(dequant_row_fn deq, int64_t row_bytes, const uint8_t* W, int64_t K,
+                       const float* x, const int64_t* rows, int64_t nrows, double* y, double* a) {
+#pragma omp parallel
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < nrows; ++i) {
+            int64_t r = rows ? rows[i] : i;
+            deq(W + r * row_bytes, K, w);
+            dot_row(w, x, K, &y[i], a ? &a[i] : NULL);
+        }
+        free(w);
+    }
+}
+
+void or_gemv_q4k(const uint8_t* W, int64_t M, int64_t K, const float* x,
+                 const int64_t* rows, int64_t nrows, double* y, double* a) {
+    (void)M;
+    gemv_dense(or_q4k_dequant_row, (K / 256) * 144, W, K, x, rows, nrows, y, a);
+}
+
+void or_gemv_q8_0(const uint8_t* W, int64_t M, int64_t K, const float* x,
+                  const int64_t* rows, int64_t nrows, double* y, double* a) {
+    (void)M;
+    gemv_dense(or_q8_0_dequant_row, (K / 32) * 34, W, K, x, rows, nrows, y, a);
+}
+
+void or_gemv_q4k_factored(const uint8_t* W, int64_t M, int64_t K, const float* x,
+                          const int64_t* rows, int64_t nrows, double* y) {
+    (void)M;
+    int64_t nb = K / 256;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t r = rows ? rows[i] : i;
+        const uint8_t* row = W + r * nb * 144;
+        double acc = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t* blk = row + 144 * b;
+            double d = or_half_to_double(rd16(blk));
+            double dmin = or_half_to_double(rd16(blk + 2));
+            int sc[8], m[8];
+            or_q4k_unpack_scales(blk + 4, sc, m);
+            for (int j = 0; j < 8; ++j) {
+                double S = 0.0, X = 0.0;
+                for (int l = 0; l < 32; ++l) {
+                    double xv = (double)x[256 * b + 32 * j + l];
+                    S += q4k_quant(blk + 16, 32 * j + l) * xv;
+                    X += xv;
+                }
+                acc += d * sc[j] * S - dmin * m[j] * X;
+            }
+        }
+        y[i] = acc;
+    }
+}
+
+void or_gemm_q4k(const uint8_t* W, int64_t M, int64_t K, const float* X, int64_t ldx,
+                 int64_t N, const int64_t* rows, int64_t nrows, double* Y, double* A) {
+    for (int64_t n = 0; n < N; ++n)
+        or_gemv_q4k(W, M, K, X + n * ldx, rows, nrows, Y + n * nrows, A ? A + n * nrows : NULL);
+}
+
+int64_t or_argmax(const double* y, int64_t n) {
+    if (n <= 0) return -1;
+    int64_t best = 0;
+    for (int64_t i = 1; i < n; ++i)
+        if (y[i] > y[best]) best = i;   /* strict: ties keep the lower index */
+    return best;
+}

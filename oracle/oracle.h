@@ -1,0 +1,84 @@
+/*
+ * CPU oracle for the quantized GEMV / small-N GEMM / LM-head argmax path.
+ *
+ * TEST INFRASTRUCTURE ONLY. It is plain, slow and written to be checked by eye
+ * against the definitions; it shares no code with the GPU library and the GPU
+ * library never links it. Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load it.
+ *
+ * Everything is computed in fp64 with sequential (k = 0, 1, 2, ...) summation.
+ *
+ * Formats. The pages name the block formats (the dotLLM README, "Key Features /
+ * Performance: Quantized inference" lists FP16, Q8_0 and Q4_K_M with fused
+ * scale x int dot products on the quantized blocks; its CUDA backend news entry
+ * lists decode GEMV for Q8_0 and Q4_K) but print no byte layout. The layout used
+ * here is the GGUF reading:
+ *   Q4_K (144 B / 256 weights): fp16 d, fp16 dmin, 12 bytes of 6-bit sub-scales
+ *     sc[0..7] and mins m[0..7], 128 bytes of nibbles. Weight 32*j + l of the
+ *     block is d*sc[j]*q - dmin*m[j], q its 4-bit quant. Quant byte 32*g + l
+ *     holds weight 64*g + l in its low nibble and weight 64*g + 32 + l in its
+ *     high nibble.
+ *   Q8_0 (34 B / 32 weights): fp16 d, 32 int8 q; weight i is d*q[i].
+ * Compatibility of this reading with real GGUF files is parity unpinned (no
+ * file, decoder or format document is available); the pins in the tests fix the
+ * oracle to the reading itself.
+ */
+#ifndef QG_ORACLE_H
+#define QG_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* IEEE binary16 bit pattern -> double, exactly (subnormals, inf, NaN). */
+double or_half_to_double(uint16_t h);
+
+/* Unpack the twelve 6-bit-field bytes of a Q4_K block into sc[8], m[8]. */
+void or_q4k_unpack_scales(const uint8_t s[12], int sc[8], int m[8]);
+
+/* Dequantize one block. w receives 256 (Q4_K) or 32 (Q8_0) doubles. */
+void or_q4k_dequant_block(const uint8_t blk[144], double w[256]);
+void or_q8_0_dequant_block(const uint8_t blk[34], double w[32]);
+
+/* Dequantize a whole row of K weights (K/256 Q4_K or K/32 Q8_0 blocks). */
+void or_q4k_dequant_row(const uint8_t* row, int64_t K, double* w);
+void or_q8_0_dequant_row(const uint8_t* row, int64_t K, double* w);
+
+/*
+ * y = W x for the rows listed in rows[0..nrows) (rows == NULL: rows 0..nrows-1).
+ * W is canonical row-major blocks, M rows of K weights. Outputs are indexed by
+ * list position i: y[i] = sum_k w[r][k] * x[k], a[i] = sum_k |w[r][k] * x[k]|
+ * (a may be NULL). Dense form: dequantize the row, then one sequential dot.
+ */
+void or_gemv_q4k(const uint8_t* W, int64_t M, int64_t K, const float* x,
+                 const int64_t* rows, int64_t nrows, double* y, double* a);
+void or_gemv_q8_0(const uint8_t* W, int64_t M, int64_t K, const float* x,
+                  const int64_t* rows, int64_t nrows, double* y, double* a);
+
+/*
+ * Factored Q4_K form: per 32-weight sub-block, S = sum q*x and X = sum x, then
+ * y += d*sc*S - dmin*m*X. Same result as the dense form up to rounding order.
+ */
+void or_gemv_q4k_factored(const uint8_t* W, int64_t M, int64_t K, const float* x,
+                          const int64_t* rows, int64_t nrows, double* y);
+
+/*
+ * Small-N product Y[:, n] = W X[:, n], n < N. X is column-major with leading
+ * dimension ldx (column n starts at X + n*ldx). Outputs: Y[n*nrows + i] and
+ * A[n*nrows + i] (A may be NULL) for listed row i.
+ */
+void or_gemm_q4k(const uint8_t* W, int64_t M, int64_t K, const float* X, int64_t ldx,
+                 int64_t N, const int64_t* rows, int64_t nrows, double* Y, double* A);
+
+/* Lowest index i with y[i] == max_j y[j] (first maximum); -1 if n <= 0. */
+int64_t or_argmax(const double* y, int64_t n);
+
+/* Number of OpenMP threads the row loops use (1 without OpenMP). */
+int or_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

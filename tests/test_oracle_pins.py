@@ -1,0 +1,308 @@
+"""Pins of the fp64 CPU oracle against facts that do not come from the oracle itself:
+hand-derived closed-form blocks, the IEEE binary16 definition checked exhaustively
+against numpy, encode/decode round trips through independently written encoders,
+integer special cases that reduce to numpy's integer matmul, linearity in x,
+zero scales, and the argmax convention of numpy.argmax.
+
+The definitions pinned: y = W x with W the dequantized block matrix (the plain
+sequential dot product of "Building a Fully Custom C# LLM Runtime", VectorMath
+sample, widened to fp64), the per-row bound sum|w*x|, and the greedy token choice
+(first maximum) of "Why Local LLMs Don't Need C++ or Python", section 2.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import blockenc as enc
+
+G = enc.golden()
+
+
+# ---------------------------------------------------------------- fp16 decode
+def test_fp16_decode_exhaustive_vs_numpy():
+    L = oracle.lib()
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([L.or_half_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_fp16_decode_closed_forms():
+    # (-1)^s * 2^(e-15) * (1 + f/1024); subnormal 2^-14 * f/1024
+    assert oracle.half_to_double(0x3C00) == 1.0
+    assert oracle.half_to_double(0x3800) == 0.5
+    assert oracle.half_to_double(0xC000) == -2.0
+    assert oracle.half_to_double(0x7BFF) == 65504.0
+    assert oracle.half_to_double(0x0001) == 2.0 ** -24
+    assert oracle.half_to_double(0x03FF) == 1023 * 2.0 ** -24
+    assert oracle.half_to_double(0x0400) == 2.0 ** -14
+    assert oracle.half_to_double(0x8000) == 0.0 and np.signbit(oracle.half_to_double(0x8000))
+    assert np.isinf(oracle.half_to_double(0x7C00))
+    assert np.isnan(oracle.half_to_double(0x7E00))
+
+
+# ---------------------------------------------------------------- scale fields
+@pytest.mark.parametrize("name", ["A", "B", "C"])
+def test_scale_unpack_golden(name):
+    g = G[name]
+    sc, m = oracle.q4k_unpack_scales(g["block"][4:16])
+    assert list(sc) == g["sc"]
+    assert list(m) == g["m"]
+
+
+def test_scale_pack_unpack_roundtrip():
+    rng = np.random.default_rng(5)
+    cases = [([0] * 8, [0] * 8), ([63] * 8, [63] * 8), ([15, 16, 31, 32, 47, 48, 62, 63], [16, 15, 48, 47, 0, 63, 32, 31])]
+    cases += [(rng.integers(0, 64, 8), rng.integers(0, 64, 8)) for _ in range(200)]
+    for sc, m in cases:
+        s2, m2 = oracle.q4k_unpack_scales(enc.pack_scales(sc, m))
+        assert list(s2) == [int(v) for v in sc] and list(m2) == [int(v) for v in m]
+
+
+def test_scale_bytes_are_a_bijection():
+    # every 12-byte pattern maps to distinct fields: flipping any single bit changes
+    # exactly one field by a power of two
+    base = np.zeros(12, np.uint8)
+    sc0, m0 = oracle.q4k_unpack_scales(base)
+    for byte in range(12):
+        for bit in range(8):
+            s = base.copy()
+            s[byte] = 1 << bit
+            sc, m = oracle.q4k_unpack_scales(s)
+            diff = np.concatenate([sc - sc0, m - m0])
+            nz = np.flatnonzero(diff)
+            assert nz.size == 1 and diff[nz[0]] in (1, 2, 4, 8, 16, 32)
+
+
+# ---------------------------------------------------------------- Q4_K blocks
+@pytest.mark.parametrize("name", ["A", "B", "C"])
+def test_q4k_golden_blocks(name):
+    g = G[name]
+    w = oracle.q4k_dequant_block(g["block"])
+    assert w.sum() == g["sum"]
+    for i, v in g["w"].items():
+        assert w[i] == v, (name, i, w[i], v)
+
+
+def test_q4k_block_c_every_weight():
+    # Block C: weight 64g+l (l<32) = l mod 16, weight 64g+32+l = g
+    w = oracle.q4k_dequant_block(G["C"]["block"])
+    i = np.arange(256)
+    expect = np.where(i % 64 < 32, (i % 64) % 16, i // 64)
+    assert np.array_equal(w, expect.astype(np.float64))
+
+
+def test_q4k_golden_rows_and_ek_probes():
+    # A row of K=512 = [block A, block B]; x = e_k returns weight k; x = 1 returns the sums.
+    row = np.concatenate([G["A"]["block"], G["B"]["block"]])
+    W = np.stack([row, row])  # two identical rows
+    K = 512
+    ones = np.ones(K, np.float32)
+    y, a = oracle.gemv_q4k(W, 2, K, ones)
+    assert np.all(y == G["A"]["sum"] + G["B"]["sum"])
+    wa = oracle.q4k_dequant_block(G["A"]["block"])
+    for k in (0, 37, 255, 256, 256 + 15, 511):
+        e = np.zeros(K, np.float32)
+        e[k] = 1.0
+        y, a = oracle.gemv_q4k(W, 2, K, e)
+        expect = G["A"]["w"].get(k) if k < 256 else G["B"]["w"].get(k - 256)
+        if expect is None:
+            expect = wa[k] if k < 256 else None
+        if expect is not None:
+            assert y[0] == expect and y[1] == expect
+        assert a[0] == abs(y[0])
+
+
+def test_q4k_encode_decode_random_blocks():
+    rng = np.random.default_rng(11)
+    for _ in range(100):
+        d, dmin, sc, m, q = enc.random_q4k_params(rng)
+        blk = enc.q4k_block(enc.half_bits(d), enc.half_bits(dmin), sc, m, q)
+        w = oracle.q4k_dequant_block(blk)
+        ref = enc.q4k_weights(d, dmin, sc, m, q)
+        assert np.array_equal(w, ref)
+
+
+def test_q4k_bruteforce_tiny_matrices():
+    # M <= 4, K in {256, 512}: blocks encoded from chosen parameters, expected y from
+    # the parameters with numpy's float64 matmul.
+    rng = np.random.default_rng(12)
+    for M, K in [(1, 256), (3, 256), (4, 512), (2, 512)]:
+        nb = K // 256
+        blocks, Wd = [], np.zeros((M, K))
+        for r in range(M):
+            row = []
+            for b in range(nb):
+                d, dmin, sc, m, q = enc.random_q4k_params(rng)
+                row.append(enc.q4k_block(enc.half_bits(d), enc.half_bits(dmin), sc, m, q))
+                Wd[r, 256 * b:256 * (b + 1)] = enc.q4k_weights(d, dmin, sc, m, q)
+            blocks.append(np.concatenate(row))
+        W = np.stack(blocks)
+        x = rng.standard_normal(K).astype(np.float32)
+        y, a = oracle.gemv_q4k(W, M, K, x)
+        ref = Wd @ x.astype(np.float64)
+        aref = np.abs(Wd * x.astype(np.float64)).sum(axis=1)
+        assert np.allclose(y, ref, rtol=0, atol=1e-12 * aref.max())
+        assert np.allclose(a, aref, rtol=1e-13, atol=0)
+
+
+def test_q4k_integer_special_case_is_integer_matmul():
+    # d = 1, dmin = 0, sc = 1: W is the quant matrix itself; with integer x the product
+    # is an exact integer, compared with numpy's int64 matmul.
+    rng = np.random.default_rng(13)
+    M, K = 5, 768
+    Q = rng.integers(0, 16, (M, K))
+    W = np.stack([np.concatenate([enc.q4k_block(0x3C00, 0, [1] * 8, [0] * 8, Q[r, 256 * b:256 * (b + 1)])
+                                  for b in range(K // 256)]) for r in range(M)])
+    xi = rng.integers(-50, 51, K)
+    y, _ = oracle.gemv_q4k(W, M, K, xi.astype(np.float32))
+    assert np.array_equal(y, (Q @ xi).astype(np.float64))
+
+
+def test_q4k_dense_vs_factored():
+    M, K = 16, 1024
+    W = workloads.q4k_blocks(M, K, key=(99, 1))
+    x = workloads.x_vector(K, key=(99, 2))
+    y, a = oracle.gemv_q4k(W, M, K, x)
+    yf = oracle.gemv_q4k_factored(W, M, K, x)
+    assert np.all(np.abs(y - yf) <= 1e-12 * a)
+
+
+def test_q4k_linearity_in_x():
+    rng = np.random.default_rng(14)
+    M, K = 8, 512
+    W = workloads.q4k_blocks(M, K, key=(98, 1))
+    xa = rng.integers(-8, 9, K).astype(np.float32)
+    xb = rng.integers(-8, 9, K).astype(np.float32)
+    xc = (2.0 * xa - 3.0 * xb).astype(np.float32)  # exact in float32
+    ya, aa = oracle.gemv_q4k(W, M, K, xa)
+    yb, ab = oracle.gemv_q4k(W, M, K, xb)
+    yc, ac = oracle.gemv_q4k(W, M, K, xc)
+    assert np.all(np.abs(yc - (2 * ya - 3 * yb)) <= 1e-12 * (2 * aa + 3 * ab))
+
+
+def test_q4k_zero_scales_give_zero():
+    M, K = 4, 512
+    W = workloads.q4k_blocks(M, K, key=(97, 1)).reshape(M, K // 256, 144).copy()
+    x = workloads.x_vector(K, key=(97, 2))
+    Z = W.copy()
+    Z[:, :, 0:4] = 0  # d = dmin = 0
+    y, a = oracle.gemv_q4k(Z.reshape(M, -1), M, K, x)
+    assert np.all(y == 0) and np.all(a == 0)
+    Z = W.copy()
+    Z[:, :, 4:16] = 0  # sc = m = 0
+    y, a = oracle.gemv_q4k(Z.reshape(M, -1), M, K, x)
+    assert np.all(y == 0)
+
+
+def test_q4k_min_term_alone():
+    # q = 0 everywhere: w = -dmin*m[j]; with x = 1 the row sum is -32*dmin*sum(m)
+    m = [3, 0, 63, 1, 17, 32, 5, 60]
+    blk = enc.q4k_block(0x3C00, 0x3400, [7] * 8, m, np.zeros(256, int))  # dmin = 0.25
+    y, _ = oracle.gemv_q4k(blk[None, :], 1, 256, np.ones(256, np.float32))
+    assert y[0] == -32 * 0.25 * sum(m)
+
+
+# ---------------------------------------------------------------- Q8_0 blocks
+@pytest.mark.parametrize("name", ["Q8A", "Q8B", "Q8C"])
+def test_q8_0_golden_blocks(name):
+    g = G[name]
+    w = oracle.q8_0_dequant_block(g["block"])
+    assert w.sum() == g["sum"]
+    for i, v in g["w"].items():
+        assert w[i] == v
+
+
+def test_q8_0_decodes_minus_128():
+    blk = enc.q8_0_block(0x3C00, [-128] + [0] * 31)
+    assert oracle.q8_0_dequant_block(blk)[0] == -128.0
+
+
+def test_q8_0_integer_special_case_is_integer_matmul():
+    rng = np.random.default_rng(15)
+    M, K = 7, 320
+    Q = rng.integers(-127, 128, (M, K))
+    W = np.stack([np.concatenate([enc.q8_0_block(0x3C00, Q[r, 32 * b:32 * (b + 1)]) for b in range(K // 32)])
+                  for r in range(M)])
+    xi = rng.integers(-100, 101, K)
+    y, a = oracle.gemv_q8_0(W, M, K, xi.astype(np.float32))
+    assert np.array_equal(y, (Q @ xi).astype(np.float64))
+    assert np.array_equal(a, (np.abs(Q) @ np.abs(xi)).astype(np.float64))
+
+
+def test_q8_0_scaled_blocks_vs_params():
+    rng = np.random.default_rng(16)
+    M, K = 3, 256
+    Wd = np.zeros((M, K))
+    rows = []
+    for r in range(M):
+        row = []
+        for b in range(K // 32):
+            d = float(np.float16(rng.uniform(0.001, 0.02)))
+            q = rng.integers(-127, 128, 32)
+            row.append(enc.q8_0_block(enc.half_bits(d), q))
+            Wd[r, 32 * b:32 * (b + 1)] = d * q
+        rows.append(np.concatenate(row))
+    W = np.stack(rows)
+    x = rng.standard_normal(K).astype(np.float32)
+    y, a = oracle.gemv_q8_0(W, M, K, x)
+    aref = np.abs(Wd * x.astype(np.float64)).sum(1)
+    assert np.allclose(y, Wd @ x.astype(np.float64), rtol=0, atol=1e-12 * aref.max())
+
+
+def test_q8_0_zero_scale():
+    W = workloads.q8_0_blocks(4, 128, key=(96, 1)).reshape(4, 4, 34).copy()
+    W[:, :, 0:2] = 0
+    y, a = oracle.gemv_q8_0(W.reshape(4, -1), 4, 128, workloads.x_vector(128, key=(96, 2)))
+    assert np.all(y == 0)
+
+
+# ---------------------------------------------------------------- rows subset, small N
+def test_row_subset_matches_full():
+    M, K = 40, 512
+    W = workloads.q4k_blocks(M, K, key=(95, 1))
+    x = workloads.x_vector(K, key=(95, 2))
+    y, a = oracle.gemv_q4k(W, M, K, x)
+    rows = np.array([39, 0, 17, 17, 3])
+    ys, as_ = oracle.gemv_q4k(W, M, K, x, rows=rows)
+    assert np.array_equal(ys, y[rows]) and np.array_equal(as_, a[rows])
+
+
+def test_gemm_columns_equal_gemv():
+    M, K, N = 9, 512, 5
+    W = workloads.q4k_blocks(M, K, key=(94, 1))
+    X = workloads.x_columns(K, N, key=(94, 2))
+    Y, A = oracle.gemm_q4k(W, M, K, X)
+    for n in range(N):
+        y, a = oracle.gemv_q4k(W, M, K, X[n])
+        assert np.array_equal(Y[n], y) and np.array_equal(A[n], a)
+
+
+# ---------------------------------------------------------------- argmax
+def test_argmax_matches_numpy_first_maximum():
+    rng = np.random.default_rng(17)
+    for n in (1, 2, 7, 1000):
+        y = rng.standard_normal(n)
+        assert oracle.argmax(y) == int(np.argmax(y))
+    y = np.array([1.0, 5.0, 3.0, 5.0, 5.0])
+    assert oracle.argmax(y) == 1 == int(np.argmax(y))
+    assert oracle.argmax(np.full(9, -2.0)) == 0
+    assert oracle.argmax(np.array([])) == -1
+
+
+def test_argmax_on_constructed_lm_head():
+    # Q8_0 rows with constant quant c_r and x = 1: logit_r = d * K * c_r (d = 1/4).
+    K = 64
+    c = np.array([3, -7, 12, 12, 0, 11, -127, 12])
+    W = np.stack([np.concatenate([enc.q8_0_block(0x3400, [cr] * 32) for _ in range(K // 32)]) for cr in c])
+    y, _ = oracle.gemv_q8_0(W, len(c), K, np.ones(K, np.float32))
+    assert np.array_equal(y, 0.25 * K * c)
+    assert oracle.argmax(y) == 2  # three-way tie at 12 -> lowest index
+
+
+def test_tolerance_formula():
+    a = np.array([0.0, 1.0, 1000.0])
+    assert np.allclose(oracle.tolerance(a), [1e-6, 1e-3 + 1e-6, 1.0 + 1e-6])
