@@ -1,0 +1,155 @@
+/*
+ * qgemv.h - C ABI of the MI355X (gfx950) quantized GEMV library.
+ *
+ * What it computes (sources named by page title and section):
+ *   - y = W x with W stored as GGUF-style Q4_K super-blocks or Q8_0 blocks and
+ *     the dot products done directly on the packed blocks, dequantizing in
+ *     registers ("dotLLM" README, Key Features / Performance: quantized inference
+ *     with fused scale x int dot products on the quantized blocks; its news entry
+ *     on the CUDA backend's custom quantized GEMV for decode; "Why Local LLMs Don't
+ *     Need C++ or Python", section 1: dequantization multipliers and accumulators
+ *     live in registers).
+ *   - Y = W X for a few columns in one pass over the weights: the batched
+ *     verification of K draft tokens (same page, section 4: the weights cross the
+ *     memory bus once for the whole candidate batch) and the 32-token prefill tile
+ *     (section 3).
+ *   - the vocabulary projection fused with an on-device argmax that leaves one
+ *     int32 token id (plus its logit) in device memory (same page, section 2).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked "host". They must be 16-byte
+ *     aligned (hipMalloc and torch allocations are); otherwise QG_ERR_ALIGN.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronizes. Results are valid once the caller
+ *     synchronizes or orders later work on the same stream.
+ *   - The caller allocates and frees every buffer, including workspaces; the
+ *     library holds no device memory of its own. Outputs must not alias inputs.
+ *   - Arguments are validated on the host before anything is launched; on error
+ *     the call returns a status, launches nothing and qg_last_error() (per host
+ *     thread) describes the problem. A failed launch returns QG_ERR_DEVICE. A
+ *     fault inside a kernel surfaces at the caller's next synchronization.
+ *   - Calls are thread-safe. Two calls that share one workspace must be ordered
+ *     on one stream (they would race otherwise).
+ *
+ * Weight layout: the GEMV entry points take the *packed* layout written by
+ * qg_pack_q4k / qg_pack_q8_0, a byte permutation of the canonical row-major block
+ * stream of exactly the same size (the dotLLM README's row-interleaved weight
+ * repacking at load time, re-designed for 64-lane wavefronts). Canonical blocks:
+ *   Q4_K, 144 B per 256 weights: fp16 d, fp16 dmin, 12 bytes of 6-bit sub-scales
+ *     and mins, 128 bytes of 4-bit quants; weight = d*sc*q - dmin*m.
+ *   Q8_0, 34 B per 32 weights: fp16 d, 32 int8 q; weight = d*q.
+ *
+ * Workspaces: entry points that split a row's dot product across workgroups or
+ * reduce across the whole launch take a workspace. Its first
+ * QG_WORKSPACE_COUNTER_BYTES bytes hold counters that must be zero before the
+ * first use (allocate it zero-filled, or call qg_workspace_clear once); every
+ * call that completes leaves them zero again. Size it with the matching
+ * *_workspace_bytes query; a smaller workspace gives QG_ERR_WORKSPACE.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QG_ABI_VERSION 1
+#define QG_WORKSPACE_COUNTER_BYTES 65536
+#define QG_MAX_BATCH 8
+#define QG_SMALLN_MAX 32
+
+typedef void* qg_stream_t; /* hipStream_t */
+
+typedef enum {
+    QG_OK = 0,
+    QG_ERR_NULL = 1,        /* a required pointer is NULL */
+    QG_ERR_SHAPE = 2,       /* M, K, N, ld* or batch size out of range */
+    QG_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+    QG_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+    QG_ERR_DEVICE = 5,      /* HIP error at launch or device query */
+    QG_ERR_UNSUPPORTED = 6  /* current device is not gfx950 */
+} qg_status;
+
+/* Library and status helpers (host only, never fail). */
+int qg_abi_version(void);
+const char* qg_status_string(int status);   /* static string */
+const char* qg_last_error(void);            /* detail of this thread's last failure */
+
+/* Size in bytes of an M x K matrix in Q4_K (K % 256 == 0) or Q8_0 (K % 32 == 0)
+ * blocks; 0 for an invalid shape. Canonical and packed sizes are identical. */
+size_t qg_q4k_bytes(int64_t M, int64_t K);
+size_t qg_q8_0_bytes(int64_t M, int64_t K);
+
+/* Repack canonical row-major blocks (src) into the packed layout (dst), both
+ * device buffers of qg_*_bytes(M, K); src and dst must not overlap. Load-time
+ * work, asynchronous on `stream`. */
+int qg_pack_q4k(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t stream);
+int qg_pack_q8_0(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t stream);
+
+/* Zero-fill `bytes` of a workspace with a kernel (no memset node, so it can sit
+ * in a captured graph). */
+int qg_workspace_clear(void* workspace, size_t bytes, qg_stream_t stream);
+
+/*
+ * y[M] = W x[K], W an M x K Q4_K matrix in packed layout, x and y fp32.
+ * 1 <= M <= 2^31-1, K % 256 == 0, 256 <= K <= 2^24.
+ */
+size_t qgemv_q4k_workspace_bytes(int64_t M, int64_t K);
+int qgemv_q4k(const void* w_packed, const float* x, float* y, int64_t M, int64_t K,
+              void* workspace, size_t workspace_bytes, qg_stream_t stream);
+
+/*
+ * Several independent Q4_K GEMVs in one launch (the dotLLM README's fused decode
+ * dispatch of Q/K/V and of gate/up). Problems must not write overlapping outputs.
+ * 1 <= count <= QG_MAX_BATCH. Each entry follows qgemv_q4k's rules.
+ */
+typedef struct {
+    const void* w_packed;
+    const float* x;
+    float* y;
+    int64_t M;
+    int64_t K;
+} qg_gemv_problem;
+size_t qgemv_q4k_batch_workspace_bytes(const qg_gemv_problem* problems /* host */, int count);
+int qgemv_q4k_batch(const qg_gemv_problem* problems /* host */, int count,
+                    void* workspace, size_t workspace_bytes, qg_stream_t stream);
+
+/*
+ * y[M] = W x[K], W an M x K Q8_0 matrix in packed layout. K % 32 == 0.
+ */
+size_t qgemv_q8_0_workspace_bytes(int64_t M, int64_t K);
+int qgemv_q8_0(const void* w_packed, const float* x, float* y, int64_t M, int64_t K,
+               void* workspace, size_t workspace_bytes, qg_stream_t stream);
+
+/*
+ * Small-N verify / prefill product, one pass over the weights:
+ *   Y[:, n] = W X[:, n] for 0 <= n < N, 1 <= N <= QG_SMALLN_MAX.
+ * X is column-major K x N with leading dimension ldx >= K (column n starts at
+ * X + n*ldx); Y is column-major M x N with ldy >= M. ldx and ldy must be
+ * multiples of 4. N <= 8 runs fp32 FMA on the vector ALUs; larger N uses fp16
+ * matrix-core products with fp32 accumulation.
+ */
+size_t qgemm_q4k_smalln_workspace_bytes(int64_t M, int64_t K, int64_t N);
+int qgemm_q4k_smalln(const void* w_packed, const float* X, int64_t ldx, float* Y, int64_t ldy,
+                     int64_t M, int64_t K, int64_t N,
+                     void* workspace, size_t workspace_bytes, qg_stream_t stream);
+
+/*
+ * Fused LM head: logits = W x (W an M x K Q8_0 matrix, packed) reduced on the
+ * device to the first maximum: out_index[0] = min{ i : logit_i = max_j logit_j }
+ * and, if out_value is not NULL, out_value[0] = logit_{out_index}. The logits
+ * never leave the chip. 1 <= M <= 2^31-1 (the index is int32). NaN logits never
+ * win. out_index / out_value are device pointers (4-byte alignment suffices).
+ */
+size_t lmhead_argmax_workspace_bytes(int64_t M, int64_t K);
+int lmhead_argmax(const void* w_packed_q8_0, const float* x, int64_t M, int64_t K,
+                  void* workspace, size_t workspace_bytes,
+                  int32_t* out_index, float* out_value, qg_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,249 @@
+"""Python binding of libqgemv.so, the MI355X (gfx950) quantized GEMV library.
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels. torch supplies device memory and the current stream. The binding
+raises if the compiled library is missing: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemv.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "qgemv.h")
+
+WORKSPACE_COUNTER_BYTES = 65536
+MAX_BATCH = 8
+SMALLN_MAX = 32
+
+_lib = None
+
+
+class QGError(RuntimeError):
+    def __init__(self, func: str, status: int, detail: str):
+        super().__init__(f"{func}: status {status}: {detail}")
+        self.status = status
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("w_packed", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+_P, _I64, _SZ, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+
+_SIGS = {
+    "qg_abi_version": (_I, []),
+    "qg_status_string": (ctypes.c_char_p, [_I]),
+    "qg_last_error": (ctypes.c_char_p, []),
+    "qg_q4k_bytes": (_SZ, [_I64, _I64]),
+    "qg_q8_0_bytes": (_SZ, [_I64, _I64]),
+    "qg_pack_q4k": (_I, [_P, _P, _I64, _I64, _P]),
+    "qg_pack_q8_0": (_I, [_P, _P, _I64, _I64, _P]),
+    "qg_workspace_clear": (_I, [_P, _SZ, _P]),
+    "qgemv_q4k_workspace_bytes": (_SZ, [_I64, _I64]),
+    "qgemv_q4k": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
+    "qgemv_q4k_batch_workspace_bytes": (_SZ, [ctypes.POINTER(_Problem), _I]),
+    "qgemv_q4k_batch": (_I, [ctypes.POINTER(_Problem), _I, _P, _SZ, _P]),
+    "qgemv_q8_0_workspace_bytes": (_SZ, [_I64, _I64]),
+    "qgemv_q8_0": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
+    "qgemm_q4k_smalln_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "qgemm_q4k_smalln": (_I, [_P, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
+    "lmhead_argmax_workspace_bytes": (_SZ, [_I64, _I64]),
+    "lmhead_argmax": (_I, [_P, _P, _I64, _I64, _P, _SZ, _P, _P, _P]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqgemv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with quantized_gemv_argmax_amd.build.build() "
+                               "(hipcc, gfx950); there is no fallback implementation")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/qgemv.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def status_string(s: int) -> str:
+    return lib().qg_status_string(int(s)).decode()
+
+
+def last_error() -> str:
+    return lib().qg_last_error().decode()
+
+
+def _check(func: str, status: int):
+    if status != 0:
+        raise QGError(func, status, f"{status_string(status)}: {last_error()}")
+
+
+def _stream(device=None) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+# ------------------------------------------------------------------ workspace
+class Workspace:
+    """A zero-initialised device buffer reused across calls on one stream.
+
+    Its leading counter area is left zero by every completed call, so it only
+    needs zeroing once, at allocation."""
+
+    def __init__(self, device=None, nbytes: int = 0):
+        self.device = torch.device(device if device is not None else "cuda")
+        self.buf = None
+        if nbytes:
+            self.ensure(nbytes)
+
+    def ensure(self, nbytes: int):
+        if nbytes and (self.buf is None or self.buf.numel() < nbytes):
+            self.buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=self.device)
+        return self
+
+    def ptr(self) -> int | None:
+        return None if self.buf is None else self.buf.data_ptr()
+
+    def nbytes(self) -> int:
+        return 0 if self.buf is None else self.buf.numel()
+
+
+_default_ws: dict = {}
+
+
+def default_workspace(device=None) -> Workspace:
+    dev = torch.device(device if device is not None else "cuda")
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    if key not in _default_ws:
+        _default_ws[key] = Workspace(dev)
+    return _default_ws[key]
+
+
+def _ws(ws: Workspace | None, need: int, device) -> Workspace:
+    ws = ws if ws is not None else default_workspace(device)
+    ws.ensure(need)
+    return ws
+
+
+# ------------------------------------------------------------------ sizes / packing
+def q4k_bytes(M: int, K: int) -> int:
+    return int(lib().qg_q4k_bytes(M, K))
+
+
+def q8_0_bytes(M: int, K: int) -> int:
+    return int(lib().qg_q8_0_bytes(M, K))
+
+
+def pack_q4k(canonical: torch.Tensor, M: int, K: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Repack canonical Q4_K bytes (uint8 device tensor) into the library's layout."""
+    _need_cuda(canonical)
+    n = q4k_bytes(M, K)
+    if canonical.numel() != n or canonical.dtype != torch.uint8:
+        raise ValueError(f"expected {n} uint8 bytes of Q4_K blocks")
+    out = out if out is not None else torch.empty(n, dtype=torch.uint8, device=canonical.device)
+    _check("qg_pack_q4k", lib().qg_pack_q4k(_ptr(canonical), _ptr(out), M, K, _stream(canonical.device)))
+    return out
+
+
+def pack_q8_0(canonical: torch.Tensor, M: int, K: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    _need_cuda(canonical)
+    n = q8_0_bytes(M, K)
+    if canonical.numel() != n or canonical.dtype != torch.uint8:
+        raise ValueError(f"expected {n} uint8 bytes of Q8_0 blocks")
+    out = out if out is not None else torch.empty(n, dtype=torch.uint8, device=canonical.device)
+    _check("qg_pack_q8_0", lib().qg_pack_q8_0(_ptr(canonical), _ptr(out), M, K, _stream(canonical.device)))
+    return out
+
+
+# ------------------------------------------------------------------ products
+def qgemv_q4k(w: torch.Tensor, x: torch.Tensor, M: int, K: int, y: torch.Tensor | None = None,
+              ws: Workspace | None = None) -> torch.Tensor:
+    """y[M] = W x for a packed Q4_K matrix (fp32 x, y)."""
+    _need_cuda(w, x, y)
+    y = y if y is not None else torch.empty(M, dtype=torch.float32, device=x.device)
+    need = int(lib().qgemv_q4k_workspace_bytes(M, K))
+    ws = _ws(ws, need, x.device)
+    _check("qgemv_q4k", lib().qgemv_q4k(_ptr(w), _ptr(x), _ptr(y), M, K, ws.ptr(), ws.nbytes(), _stream(x.device)))
+    return y
+
+
+def qgemv_q4k_batch(problems, ws: Workspace | None = None):
+    """problems: list of (w_packed, x, y, M, K); one launch for all of them."""
+    arr = (_Problem * len(problems))()
+    dev = None
+    for i, (w, x, y, M, K) in enumerate(problems):
+        _need_cuda(w, x, y)
+        dev = x.device
+        arr[i] = _Problem(_ptr(w), _ptr(x), _ptr(y), M, K)
+    need = int(lib().qgemv_q4k_batch_workspace_bytes(arr, len(problems)))
+    ws = _ws(ws, need, dev)
+    _check("qgemv_q4k_batch", lib().qgemv_q4k_batch(arr, len(problems), ws.ptr(), ws.nbytes(), _stream(dev)))
+    return [p[2] for p in problems]
+
+
+def qgemv_q8_0(w: torch.Tensor, x: torch.Tensor, M: int, K: int, y: torch.Tensor | None = None,
+               ws: Workspace | None = None) -> torch.Tensor:
+    _need_cuda(w, x, y)
+    y = y if y is not None else torch.empty(M, dtype=torch.float32, device=x.device)
+    need = int(lib().qgemv_q8_0_workspace_bytes(M, K))
+    ws = _ws(ws, need, x.device)
+    _check("qgemv_q8_0", lib().qgemv_q8_0(_ptr(w), _ptr(x), _ptr(y), M, K, ws.ptr(), ws.nbytes(), _stream(x.device)))
+    return y
+
+
+def qgemm_q4k_smalln(w: torch.Tensor, X: torch.Tensor, M: int, K: int, Y: torch.Tensor | None = None,
+                     ws: Workspace | None = None) -> torch.Tensor:
+    """X: (N, ldx) fp32, row n = column n of the K x N operand (ldx >= K, ldx % 4 == 0).
+    Returns Y as (N, ldy) with Y[n, :M] = W X[n, :K]."""
+    _need_cuda(w, X, Y)
+    N, ldx = X.shape
+    if X.stride(1) != 1 or X.stride(0) != ldx:
+        raise ValueError("X must be a contiguous (N, ldx) tensor")
+    if Y is None:
+        ldy = (M + 3) // 4 * 4
+        Y = torch.empty((N, ldy), dtype=torch.float32, device=X.device)
+    ldy = Y.shape[1]
+    need = int(lib().qgemm_q4k_smalln_workspace_bytes(M, K, N))
+    ws = _ws(ws, need, X.device)
+    _check("qgemm_q4k_smalln", lib().qgemm_q4k_smalln(_ptr(w), _ptr(X), ldx, _ptr(Y), ldy, M, K, N,
+                                                        ws.ptr(), ws.nbytes(), _stream(X.device)))
+    return Y
+
+
+def lmhead_argmax(w: torch.Tensor, x: torch.Tensor, M: int, K: int, out_index: torch.Tensor | None = None,
+                  out_value: torch.Tensor | None = None, ws: Workspace | None = None):
+    """Fused Q8_0 LM head + argmax. Returns (index int32[1], value float32[1]) device tensors."""
+    _need_cuda(w, x, out_index, out_value)
+    out_index = out_index if out_index is not None else torch.empty(1, dtype=torch.int32, device=x.device)
+    out_value = out_value if out_value is not None else torch.empty(1, dtype=torch.float32, device=x.device)
+    need = int(lib().lmhead_argmax_workspace_bytes(M, K))
+    ws = _ws(ws, need, x.device)
+    _check("lmhead_argmax", lib().lmhead_argmax(_ptr(w), _ptr(x), M, K, ws.ptr(), ws.nbytes(), _ptr(out_index),
+                                                  _ptr(out_value), _stream(x.device)))
+    return out_index, out_value

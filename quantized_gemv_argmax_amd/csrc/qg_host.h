@@ -1,0 +1,37 @@
+// Host-side helpers of the C ABI: argument checks, the per-thread error text, the
+// workspace plan and the device check.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdarg>
+#include <cstddef>
+
+#include "../../include/qgemv.h"
+
+namespace qg {
+
+// Rows per packed tile: one wavefront lane per row.
+constexpr int kTileRows = 64;
+constexpr int kCounterSlots = QG_WORKSPACE_COUNTER_BYTES / 4;
+
+int fail(int status, const char* fmt, ...);   // records the message, returns status
+void clear_error();
+
+bool aligned16(const void* p);
+
+// Returns QG_OK if the current device is gfx950, else an error status.
+int check_device();
+
+// Translate a launch error into QG_ERR_DEVICE (records the HIP message).
+int launch_status(const char* what);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Reads an optional "A,B" integer pair from an environment variable (tuning
+// sweeps); returns false when unset or malformed.
+bool env_pair(const char* name, int* a, int* b);
+
+}  // namespace qg

@@ -1,0 +1,116 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, and its host-side validation returns the documented status
+codes without launching anything (no GPU needed)."""
+import ctypes
+
+import pytest
+
+import quantized_gemv_argmax_amd as qg
+
+OK, ENULL, ESHAPE, EALIGN, EWS, EDEV, EUNSUP = range(7)
+# Fake, never-dereferenced device addresses with the alignment the checks look at.
+A, B, C = 0x10000, 0x20000, 0x30000
+
+
+@pytest.fixture(scope="module")
+def L():
+    return qg.lib()
+
+
+def test_loads_and_version(L):
+    assert L.qg_abi_version() == 1
+
+
+def test_every_header_function_is_exported(L):
+    names = qg.header_functions()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(L, n), n
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert qg.status_string(s) != "unknown status"
+    assert qg.status_string(99) == "unknown status"
+
+
+def test_sizes(L):
+    assert L.qg_q4k_bytes(4096, 4096) == 9437184
+    assert L.qg_q4k_bytes(3584, 18944) == 3584 * 74 * 144
+    assert L.qg_q8_0_bytes(11008, 4096) == 47906816
+    assert L.qg_q8_0_bytes(152064, 3584) == 579059712
+    assert L.qg_q4k_bytes(4096, 4000) == 0
+    assert L.qg_q4k_bytes(0, 256) == 0
+    assert L.qg_q8_0_bytes(5, 48) == 0
+
+
+def test_gemv_validation(L):
+    f = L.qgemv_q4k
+    assert f(None, A, B, 64, 256, None, 0, None) == ENULL
+    assert "NULL" in qg.last_error()
+    assert f(C, A, B, 64, 300, None, 0, None) == ESHAPE
+    assert f(C, A, B, 0, 256, None, 0, None) == ESHAPE
+    assert f(C, A, B, 2**31, 256, None, 0, None) == ESHAPE
+    assert f(C + 4, A, B, 64, 256, None, 0, None) == EALIGN
+    assert f(C, A + 8, B, 64, 256, None, 0, None) == EALIGN
+    # a narrow matrix is split over workgroups and needs a workspace
+    need = L.qgemv_q4k_workspace_bytes(3584, 3584)
+    assert need > qg.WORKSPACE_COUNTER_BYTES
+    assert f(C, A, B, 3584, 3584, None, 0, None) == EWS
+    assert f(C, A, B, 3584, 3584, 0x40000, need - 1, None) == EWS
+    assert f(C, A, B, 3584, 3584, 0x40008, need, None) == EALIGN
+
+
+def test_batch_validation(L):
+    P = qg._Problem
+    arr = (P * 9)()
+    for i in range(9):
+        arr[i] = P(C, A, B, 64, 256)
+    assert L.qgemv_q4k_batch(arr, 0, None, 0, None) == ESHAPE
+    assert L.qgemv_q4k_batch(arr, 9, None, 0, None) == ESHAPE
+    arr[1] = P(C, None, B, 64, 256)
+    assert L.qgemv_q4k_batch(arr, 2, None, 0, None) == ENULL
+    assert L.qgemv_q4k_batch(None, 1, None, 0, None) == ENULL
+    arr[1] = P(C, A, B, 64, 1000)
+    assert L.qgemv_q4k_batch(arr, 2, None, 0, None) == ESHAPE
+
+
+def test_q8_0_and_lmhead_validation(L):
+    assert L.qgemv_q8_0(C, A, B, 10, 33, None, 0, None) == ESHAPE
+    assert L.qgemv_q8_0(C, A, None, 10, 64, None, 0, None) == ENULL
+    assert L.lmhead_argmax(C, A, 1000, 3584, 0x40000, 1 << 20, None, None, None) == ENULL
+    assert L.lmhead_argmax(C, A, 1000, 3584, None, 0, B, None, None) == EWS
+    assert L.lmhead_argmax(C, A, 1000, 3584, 0x40000, 16, B, None, None) == EWS
+    assert L.lmhead_argmax(C, A, 1000, 3584, 0x40000, 1 << 20, B + 2, None, None) == EALIGN
+    assert L.lmhead_argmax(C, A, 2**31, 3584, 0x40000, 1 << 20, B, None, None) == ESHAPE
+    assert L.lmhead_argmax_workspace_bytes(152064, 3584) >= qg.WORKSPACE_COUNTER_BYTES + 2376 * 8
+
+
+def test_smalln_validation(L):
+    f = L.qgemm_q4k_smalln
+    assert f(C, A, 256, B, 64, 64, 256, 0, None, 0, None) == ESHAPE
+    assert f(C, A, 256, B, 64, 64, 256, 33, None, 0, None) == ESHAPE
+    assert f(C, A, 128, B, 64, 64, 256, 5, None, 0, None) == ESHAPE   # ldx < K
+    assert f(C, A, 256, B, 60, 64, 256, 5, None, 0, None) == ESHAPE   # ldy < M
+    assert f(C, A, 258, B, 64, 64, 256, 5, None, 0, None) == ESHAPE   # ldx % 4
+    assert f(C, A + 4, 256, B, 64, 64, 256, 5, None, 0, None) == EALIGN
+    assert L.qgemm_q4k_smalln_workspace_bytes(3584, 3584, 5) > 0
+    assert L.qgemm_q4k_smalln_workspace_bytes(3584, 3584, 33) == 0
+
+
+def test_pack_validation(L):
+    assert L.qg_pack_q4k(None, A, 64, 256, None) == ENULL
+    assert L.qg_pack_q4k(A, B, 64, 100, None) == ESHAPE
+    assert L.qg_pack_q4k(A, A + 16, 64, 256, None) == ESHAPE  # overlap
+    assert L.qg_pack_q8_0(A + 2, B, 64, 64, None) == EALIGN
+
+
+def test_valid_call_without_gpu_reports_device_error(L):
+    # all arguments valid: the only remaining check is the device query, which
+    # fails here (no GPU visible) instead of launching anything
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    st = L.qgemv_q4k(C, A, B, 64, 256, None, 0, None)
+    assert st in (EDEV, EUNSUP)

@@ -1,0 +1,72 @@
+"""GPU parity of the small-N Q4_K product (verify / prefill tile) against the oracle,
+per (row, column), plus the invariant that column n equals the GEMV of x_n."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemv_argmax_amd as qg
+import workloads
+from tests.gpu_helpers import assert_within, case, packed_q4k, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_smalln(M, K, N, key, rows=None):
+    W = workloads.q4k_blocks(M, K, key=key)
+    X = workloads.x_columns(K, N, key=key)
+    case(f"qgemm_q4k_smalln M={M} K={K} N={N} key={key}")
+    wp = packed_q4k(W, M, K)
+    Y = qg.qgemm_q4k_smalln(wp, to_dev(X), M, K)
+    torch.cuda.synchronize()
+    Y = Y.cpu().numpy()[:, :M]
+    Yr, Ar = oracle.gemm_q4k(W, M, K, X, rows=rows)
+    if rows is not None:
+        Y = Y[:, rows]
+    return W, X, wp, Y, Yr, Ar
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 9, 16, 17, 32])
+@pytest.mark.parametrize("M,K", [(200, 512), (65, 768), (1, 256)])
+def test_smalln_small(M, K, N):
+    _, _, _, Y, Yr, Ar = run_smalln(M, K, N, key=(30, M, K, N))
+    for n in range(N):
+        assert_within(Y[n], Yr[n], Ar[n], f"smalln M={M} K={K} N={N} col {n}")
+
+
+@pytest.mark.parametrize("N", [5, 32])
+@pytest.mark.parametrize("name,M,K", [m for m in workloads.LAYER_MATRICES])
+def test_smalln_7b_shapes(name, M, K, N):
+    rows = sample_rows(M, 192, seed=M + K + N)
+    _, _, _, Y, Yr, Ar = run_smalln(M, K, N, key=(5, 0, workloads.LAYER_MATRICES.index((name, M, K)), N), rows=rows)
+    for n in range(N):
+        assert_within(Y[n], Yr[n], Ar[n], f"smalln {name} N={N} col {n}")
+
+
+@pytest.mark.parametrize("N", [5, 32])
+def test_columns_match_gemv(N):
+    M, K = 3584, 3584
+    W, X, wp, Y, Yr, Ar = run_smalln(M, K, N, key=(31, N), rows=np.arange(0, M, 7))
+    for n in range(N):
+        y = qg.qgemv_q4k(wp, to_dev(X[n]), M, K).cpu().numpy()
+        # both within tolerance of the same oracle column, hence within 2 tol of each other
+        tol = oracle.tolerance(Ar[n])
+        assert np.all(np.abs(y[::7] - Y[n]) <= 2 * tol)
+
+
+def test_padded_leading_dimensions():
+    M, K, N = 130, 512, 5
+    W = workloads.q4k_blocks(M, K, key=(32,))
+    X = workloads.x_columns(K, N, key=(32,))
+    ldx, ldy = K + 12, M + 10
+    Xp = np.zeros((N, ldx), np.float32)
+    Xp[:, :K] = X
+    case("qgemm_q4k_smalln padded ld")
+    wp = packed_q4k(W, M, K)
+    Yd = torch.full((N, ldy), 123.0, device="cuda:0")
+    qg.qgemm_q4k_smalln(wp, to_dev(Xp), M, K, Y=Yd)
+    Y = Yd.cpu().numpy()
+    assert np.all(Y[:, M:] == 123.0)  # padding untouched
+    Yr, Ar = oracle.gemm_q4k(W, M, K, X)
+    for n in range(N):
+        assert_within(Y[n, :M], Yr[n], Ar[n], f"padded col {n}")
