@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized GEMV hot path on one MI355X.
+
+Step = one batch-1 decode pass of a 7B-shaped model's projections: 28 layers x
+{Wq 3584x3584, Wk 512x3584, Wv 512x3584, Wo 3584x3584, gate 18944x3584,
+up 18944x3584, down 3584x18944}, all Q4_K (3,670,474,752 weight bytes), each with
+its own fp32 activation vector. Launches follow the layer's dependency stages
+{q,k,v} -> {o} -> {gate,up} -> {down}: one grouped launch per stage, 112 per step,
+replayed from a captured HIP graph. Inputs are resident in HBM before timing; the
+3.67 GB sweep is far larger than the 256 MB Infinity Cache, so it streams from HBM.
+
+Printed (one JSON line): whole-step throughput in GB/s of algorithmic bytes
+(weights + x + y), equivalent tokens/s (bytes per token as the pages' bandwidth
+wall divides them), the roofline entry of the dominant kernel (Q4_K GEMV: bytes
+per launch / average launch duration from HIP events on the launch stream), the
+fp64 CPU oracle timed on a bounded sample, and the other hot-path rows (single
+4096x4096 Q4_K GEMV, Q8_0 11008x4096 / 4096x11008, fused 152064x3584 LM head +
+argmax, small-N verify N=5 and N=32 over the same 196 matrices), each timed with
+rotation over enough weight copies to defeat the Infinity Cache.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Q4_K GEMV achieved HBM GB/s (% of peak) and equiv. tokens/s at 7B shapes"
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def graph_ms(torch, fn, reps: int, warm: int = 2) -> float:
+    """Capture fn() into a HIP graph, replay it `reps` times, return ms per replay."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=28, help=argparse.SUPPRESS)
+    ap.add_argument("--no-rows", action="store_true", help="skip the other hot-path rows")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the projections would shard by rows across GPUs). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_gemv_argmax_amd as qg
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    qg.lib()
+    ws = qg.Workspace(dev, 64 << 20)
+
+    # ------------------------------------------------------------ 7B decode step
+    n_layers = args.layers
+    t0 = time.time()
+    layers = []
+    cpu_sample = []
+    w_bytes = 0
+    xy_bytes = 0
+    for L in range(n_layers):
+        mats = []
+        for i, (name, M, K) in enumerate(wl.LAYER_MATRICES):
+            W = wl.q4k_blocks(M, K, key=(3, L, i))
+            canon = torch.from_numpy(W.reshape(-1)).to(dev)
+            wp = qg.pack_q4k(canon, M, K)
+            del canon
+            x = wl.x_vector(K, key=(3, L, i))
+            mats.append((wp, torch.from_numpy(x).to(dev), torch.empty(M, dtype=torch.float32, device=dev), M, K))
+            w_bytes += W.size
+            xy_bytes += 4 * (K + M)
+            if L == 0:
+                cpu_sample.append((W, x, M, K))
+        layers.append(mats)
+        if L % 7 == 6:
+            log(f"generated and packed {L + 1}/{n_layers} layers ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    step_bytes = w_bytes + xy_bytes
+    stages = [[layers[L][i] for i in st] for L in range(n_layers) for st in wl.LAYER_STAGES]
+
+    def step():
+        for st in stages:
+            qg.qgemv_q4k_batch(st, ws=ws)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    log("warm-up done; capturing the step graph")
+
+    # timed region: K steps replayed from one captured graph, events on the stream
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"step {ms_step:.4f} ms -> {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s)")
+
+    # roofline of the dominant kernel: per-launch events, with the GPU kept busy by
+    # graph replays queued first so that every event pair brackets GPU time only
+    ev = []
+    for _ in range(8):
+        g.replay()
+    for st in stages:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        qg.qgemv_q4k_batch(st, ws=ws)
+        b.record()
+        ev.append((a, b, sum(p[0].numel() + 4 * (p[3] + p[4]) for p in st)))
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b, _ in ev])  # ms
+    lbytes = np.array([n for _, _, n in ev], dtype=np.float64)
+    achieved = lbytes.sum() / (durs.sum() * 1e-3) / 1e9
+    per_stage = {}
+    for k, name in enumerate(["qkv", "o", "gate_up", "down"]):
+        d = durs[k::4]
+        per_stage[name] = {"avg_us": round(float(d.mean() * 1e3), 3),
+                           "bytes": int(lbytes[k]),
+                           "GBps": round(float(lbytes[k] / (d.mean() * 1e-3) / 1e9), 1)}
+    log(f"dominant kernel: {achieved:.1f} GB/s over {len(ev)} launches, per stage {per_stage}")
+    roofline = {"kernel": "q4k_gemv_kernel", "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "launches_per_step": len(stages), "avg_launch_us": round(float(durs.mean() * 1e3), 3),
+                "avg_bytes_per_launch": int(lbytes.mean()), "per_stage": per_stage}
+
+    rows = {}
+    if not args.no_rows:
+        rows = other_rows(torch, np, qg, wl, dev, ws, layers, n_layers)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cpu_sample, args.cpu_seconds, step_bytes, w_bytes)
+
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "7B-shaped decode step, batch 1: %d layers x {Wq 3584x3584, Wk 512x3584, Wv 512x3584, "
+                        "Wo 3584x3584, gate 18944x3584, up 18944x3584, down 3584x18944}, Q4_K weights, "
+                        "fp32 x per matrix" % n_layers,
+            "bytes_per_step": int(step_bytes),
+            "weight_bytes_per_step": int(w_bytes),
+            "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+            "equiv_tokens_per_s": round(1e3 / ms_step, 1),
+            "launches_per_step": len(stages),
+            "timing": "HIP graph of one step, replayed; events on the launch stream",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
+    rows = {}
+
+    # context: a plain device-to-device copy of 1 GiB (read + write bytes)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ms = graph_ms(torch, lambda: dst.copy_(src), 10)
+    rows["context_copy_1GiB"] = {"us": round(ms * 1e3, 1), "GBps": round(2 * src.numel() / (ms * 1e-3) / 1e9, 1)}
+    log(f"row copy: {rows['context_copy_1GiB']}")
+    del src, dst
+
+    def rotated(wp, count):
+        return [wp.clone() for _ in range(count)]
+
+    # single Q4_K GEMV 4096x4096, 128 copies (1.2 GB) rotated
+    M, K = 4096, 4096
+    W = wl.q4k_blocks(M, K, key=(1, 0))
+    wp = qg.pack_q4k(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
+    R = max(2, -(-(1 << 30) // wp.numel()))
+    copies = rotated(wp, R)
+    x = torch.from_numpy(wl.x_vector(K, key=(1, 0))).to(dev)
+    y = torch.empty(M, device=dev)
+    ms = graph_ms(torch, lambda: [qg.qgemv_q4k(c, x, M, K, y=y, ws=ws) for c in copies], 20) / R
+    b = W.size + 4 * (M + K)
+    rows["q4k_gemv_4096x4096"] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                                  "bytes": b, "copies_rotated": R}
+    log(f"row q4k 4096^2: {rows['q4k_gemv_4096x4096']}")
+    del copies
+
+    # Q8_0 GEMVs 11008x4096 and 4096x11008, rotated
+    for (M, K) in [(11008, 4096), (4096, 11008)]:
+        W = wl.q8_0_blocks(M, K, key=(2, M))
+        wp = qg.pack_q8_0(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
+        R = max(2, -(-(1 << 30) // wp.numel()))
+        copies = rotated(wp, R)
+        x = torch.from_numpy(wl.x_vector(K, key=(2, M))).to(dev)
+        y = torch.empty(M, device=dev)
+        ms = graph_ms(torch, lambda: [qg.qgemv_q8_0(c, x, M, K, y=y, ws=ws) for c in copies], 20) / R
+        b = W.size + 4 * (M + K)
+        rows[f"q8_0_gemv_{M}x{K}"] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                                      "bytes": b, "copies_rotated": R}
+        log(f"row q8_0 {M}x{K}: {rows[f'q8_0_gemv_{M}x{K}']}")
+        del copies
+
+    # fused LM head + argmax 152064x3584 Q8_0, 2 copies
+    M, K = wl.VOCAB, wl.HIDDEN
+    W = wl.q8_0_blocks(M, K, key=(4, 0))
+    wp = qg.pack_q8_0(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
+    del W
+    copies = [wp, wp.clone()]
+    x = torch.from_numpy(wl.x_vector(K, key=(4, 1, 0, 0))).to(dev)
+    oi = torch.empty(1, dtype=torch.int32, device=dev)
+    ov = torch.empty(1, dtype=torch.float32, device=dev)
+    ms = graph_ms(torch, lambda: [qg.lmhead_argmax(c, x, M, K, out_index=oi, out_value=ov, ws=ws) for c in copies],
+                  20) / 2
+    b = wp.numel() + 4 * K + 8 * (-(-M // 64)) * 2 + 8
+    # unfused comparison: Q8_0 GEMV writing the 608,256-byte logit vector + torch argmax
+    logits = torch.empty(M, device=dev)
+    ms_unfused = graph_ms(torch, lambda: [(qg.qgemv_q8_0(c, x, M, K, y=logits, ws=ws), torch.argmax(logits))
+                                          for c in copies], 20) / 2
+    h = torch.empty(M, dtype=torch.float32, pin_memory=True)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(20):
+        h.copy_(logits, non_blocking=False)
+    d2h_us = (time.perf_counter() - t) / 20 * 1e6
+    hi = torch.empty(1, dtype=torch.int32, pin_memory=True)
+    t = time.perf_counter()
+    for _ in range(20):
+        hi.copy_(oi, non_blocking=False)
+    d2h4_us = (time.perf_counter() - t) / 20 * 1e6
+    rows["lmhead_argmax_152064x3584"] = {
+        "us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": int(b),
+        "unfused_gemv_plus_torch_argmax_us": round(ms_unfused * 1e3, 3),
+        "d2h_logits_608256B_us": round(d2h_us, 2), "d2h_index_4B_us": round(d2h4_us, 2)}
+    log(f"row lmhead: {rows['lmhead_argmax_152064x3584']}")
+    del copies, wp
+
+    # small-N verify over the 196 decode matrices (weights read once per call)
+    for N in (5, 32):
+        Xs, Ys = [], []
+        for L in range(n_layers):
+            for i, (name, M, K) in enumerate(wl.LAYER_MATRICES):
+                Xs.append(torch.from_numpy(wl.x_columns(K, N, key=(5, L, i, N))).to(dev))
+                Ys.append(torch.empty((N, (M + 3) // 4 * 4), device=dev))
+        flat = [m for Lm in layers for m in Lm]
+
+        def vstep():
+            for (wp_, _, _, M_, K_), X_, Y_ in zip(flat, Xs, Ys):
+                qg.qgemm_q4k_smalln(wp_, X_, M_, K_, Y=Y_, ws=ws)
+
+        ms = graph_ms(torch, vstep, 5)
+        wb = sum(m[0].numel() for m in flat)
+        b = wb + sum(4 * N * (m[3] + m[4]) for m in flat)
+        rows[f"smalln_verify_N{N}"] = {"ms_per_step": round(ms, 4), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                                       "bytes": int(b), "verified_tokens_per_s": round(N * 1e3 / ms, 1),
+                                       "launches_per_step": len(flat)}
+        log(f"row smalln N={N}: {rows[f'smalln_verify_N{N}']}")
+        del Xs, Ys
+    return rows
+
+
+def cpu_baseline(sample, seconds, step_bytes, w_bytes):
+    """The fp64 C oracle (OpenMP over rows) on layer 0's seven matrices, repeated for
+    about `seconds`; reported as GB/s of algorithmic bytes and equivalent tok/s."""
+    import oracle
+
+    oracle.lib()
+    done_bytes = 0
+    passes = 0
+    t = time.perf_counter()
+    while True:
+        for W, x, M, K in sample:
+            oracle.gemv_q4k(W, M, K, x)
+            done_bytes += W.size + 4 * (M + K)
+        passes += 1
+        if time.perf_counter() - t >= seconds:
+            break
+    el = time.perf_counter() - t
+    gbs = done_bytes / el / 1e9
+    log(f"cpu oracle: {passes} passes over layer 0, {gbs:.3f} GB/s, {oracle.num_threads()} threads")
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"layer 0 of the decode step (7 Q4_K matrices, {sum(s[0].size for s in sample)} weight bytes), "
+                      f"{passes} passes in {el:.1f} s",
+            "equiv_tokens_per_s": round(gbs * 1e9 / step_bytes, 4)}
+
+
+if __name__ == "__main__":
+    main()

@@ -51,22 +51,19 @@ struct Q4Args {
 };
 
 struct SbData {
+    float4 xv;  // this lane's 4 activations of the super-block (for the sub-block sums)
     uint4 s[9];
 };
 
-QG_DEV void load_sb(SbData& d, const uint4* __restrict__ seg, int rt, bool active) {
-    if (active) {
+QG_DEV void load_sb(SbData& d, const uint4* __restrict__ seg, const float* __restrict__ xb, int rt, int lane) {
+    d.xv = qg_x4(xb, lane);
 #pragma unroll
-        for (int s = 0; s < 9; ++s) d.s[s] = seg[s * rt];
-    } else {
-#pragma unroll
-        for (int s = 0; s < 9; ++s) d.s[s] = make_uint4(0, 0, 0, 0);
-    }
+    for (int s = 0; s < 9; ++s) d.s[s] = seg[s * rt];
 }
 
 // Dot product of one super-block row segment set with x[256b .. 256b+255].
-QG_DEV float sb_dot(const SbData& d, qg_uniform_f32 xs, const float* __restrict__ xb, int lane) {
-    const QgSub8 X = qg_subblock_sums(xb, lane);
+QG_DEV float sb_dot(const SbData& d, qg_uniform_f32 xs) {
+    const QgSub8 X = qg_subblock_sums(d.xv);
     float S[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) S[j] = 0.f;
@@ -129,7 +126,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(Q4Args a) {
     const int tile = local / P.splits;
     const int ks = local - tile * P.splits;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nb = P.nb;
     const int rt = min(qg::kTileRows, P.M - tile * qg::kTileRows);
     const bool active = lane < rt;
@@ -140,19 +137,22 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(Q4Args a) {
     const int wb0 = b0 + wave * (b1 - b0) / W;
     const int wb1 = b0 + (wave + 1) * (b1 - b0) / W;
 
+    // lanes past a ragged tile's end re-read the tile's last row (no divergent
+    // branches around the loads, so the loads stay counted and pipelined)
     const uint4* __restrict__ seg =
-        reinterpret_cast<const uint4*>(P.w + (size_t)tile * qg::kTileRows * nb * 144) + lane;
+        reinterpret_cast<const uint4*>(P.w + (size_t)tile * qg::kTileRows * nb * 144) + (active ? lane : rt - 1);
     qg_uniform_f32 xs = (qg_uniform_f32)P.x;
 
     float acc = 0.f;
     if (wb0 < wb1) {
         SbData cur, nxt;
-        load_sb(cur, seg + (size_t)wb0 * 9 * rt, rt, active);
-        for (int b = wb0; b < wb1; ++b) {
-            if (b + 1 < wb1) load_sb(nxt, seg + (size_t)(b + 1) * 9 * rt, rt, active);
-            acc += sb_dot(cur, xs + 256 * b, P.x + 256 * b, lane);
+        load_sb(cur, seg + (size_t)wb0 * 9 * rt, P.x + 256 * wb0, rt, lane);
+        for (int b = wb0; b < wb1 - 1; ++b) {
+            load_sb(nxt, seg + (size_t)(b + 1) * 9 * rt, P.x + 256 * (b + 1), rt, lane);
+            acc += sb_dot(cur, xs + 256 * b);
             cur = nxt;
         }
+        acc += sb_dot(cur, xs + 256 * (wb1 - 1));
     }
 
     float v = acc;
@@ -216,7 +216,7 @@ int plan_batch(const qg_gemv_problem* pr, int count, Q4Args* args, Plan* plan) {
     int W = 2;
     int fixed_wpt = 0;
     int ew = 0, es = 0;
-    if (qg::env_pair("QG_Q4K_CFG", &ew, &es) && (ew == 1 || ew == 2 || ew == 4 || ew == 8) && es >= 1) {
+    if (qg::env_pair("QG_Q4K_CFG", &ew, &es) && (ew == 1 || ew == 2 || ew == 4 || ew == 8 || ew == 16) && es >= 1) {
         W = ew;
         fixed_wpt = es;  // wavefronts per tile
     }
@@ -317,7 +317,8 @@ int qgemv_q4k_batch(const qg_gemv_problem* problems, int count, void* ws, size_t
         case 1: launch<1>(a, p.total_wg, s); break;
         case 2: launch<2>(a, p.total_wg, s); break;
         case 4: launch<4>(a, p.total_wg, s); break;
-        default: launch<8>(a, p.total_wg, s); break;
+        case 8: launch<8>(a, p.total_wg, s); break;
+        default: launch<16>(a, p.total_wg, s); break;
     }
     return qg::launch_status("qgemv_q4k");
 }

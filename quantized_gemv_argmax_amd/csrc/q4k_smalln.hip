@@ -40,22 +40,23 @@ struct SbData {
     uint4 s[9];
 };
 
-QG_DEV void load_sb(SbData& d, const uint4* __restrict__ seg, int rt, bool active) {
-    if (active) {
+QG_DEV void load_sb(SbData& d, const uint4* __restrict__ seg, int rt) {
 #pragma unroll
-        for (int s = 0; s < 9; ++s) d.s[s] = seg[s * rt];
-    } else {
-#pragma unroll
-        for (int s = 0; s < 9; ++s) d.s[s] = make_uint4(0, 0, 0, 0);
-    }
+    for (int s = 0; s < 9; ++s) d.s[s] = seg[s * rt];
 }
 
 // ------------------------------------------------------------------ VALU, N <= 8
 template <int N>
-QG_DEV void sb_dot_n(float (&acc)[N], const SbData& d, const SnProb& P, int b, int lane) {
+QG_DEV void load_xv(float4 (&xv)[N], const SnProb& P, int b, int lane) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) xv[n] = qg_x4(P.X + n * P.ldx + 256 * b, lane);
+}
+
+template <int N>
+QG_DEV void sb_dot_n(float (&acc)[N], const SbData& d, const float4 (&xv)[N], const SnProb& P, int b) {
     QgSub8 X[N];
 #pragma unroll
-    for (int n = 0; n < N; ++n) X[n] = qg_subblock_sums(P.X + n * P.ldx + 256 * b, lane);
+    for (int n = 0; n < N; ++n) X[n] = qg_subblock_sums(xv[n]);
     float S[8][N];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_valu_kernel(SnProb P, float
     const int wg = blockIdx.x;
     const int tile = wg / P.splits;
     const int ks = wg - tile * P.splits;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nb = P.nb;
     const int rt = min(qg::kTileRows, P.M - tile * qg::kTileRows);
     const bool active = lane < rt;
@@ -146,19 +147,26 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_valu_kernel(SnProb P, float
     const int b1 = (int)((int64_t)(ks + 1) * nb / P.splits);
     const int wb0 = b0 + wave * (b1 - b0) / W;
     const int wb1 = b0 + (wave + 1) * (b1 - b0) / W;
-    const uint4* __restrict__ seg = reinterpret_cast<const uint4*>(P.w + (size_t)tile * qg::kTileRows * nb * 144) + lane;
+    const uint4* __restrict__ seg =
+        reinterpret_cast<const uint4*>(P.w + (size_t)tile * qg::kTileRows * nb * 144) + (active ? lane : rt - 1);
 
     float acc[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) acc[n] = 0.f;
     if (wb0 < wb1) {
         SbData cur, nxt;
-        load_sb(cur, seg + (size_t)wb0 * 9 * rt, rt, active);
-        for (int b = wb0; b < wb1; ++b) {
-            if (b + 1 < wb1) load_sb(nxt, seg + (size_t)(b + 1) * 9 * rt, rt, active);
-            sb_dot_n<N>(acc, cur, P, b, lane);
+        float4 xc[N], xn[N];
+        load_xv<N>(xc, P, wb0, lane);
+        load_sb(cur, seg + (size_t)wb0 * 9 * rt, rt);
+        for (int b = wb0; b < wb1 - 1; ++b) {
+            load_xv<N>(xn, P, b + 1, lane);
+            load_sb(nxt, seg + (size_t)(b + 1) * 9 * rt, rt);
+            sb_dot_n<N>(acc, cur, xc, P, b);
             cur = nxt;
+#pragma unroll
+            for (int n = 0; n < N; ++n) xc[n] = xn[n];
         }
+        sb_dot_n<N>(acc, cur, xc, P, wb1 - 1);
     }
     if constexpr (W > 1) {
         __shared__ float red[W][N][64];
@@ -212,7 +220,7 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_mfma_kernel(SnProb P, float
     const int wg = blockIdx.x;
     const int tile = wg / P.splits;
     const int ks = wg - tile * P.splits;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15, s = lane >> 4;
     const int nb = P.nb;
     const int rt = min(qg::kTileRows, P.M - tile * qg::kTileRows);

@@ -42,20 +42,18 @@ struct Q8Prob {
 // 4h..4h+3 (the scale segment is fetched for both halves; the second fetch hits
 // the cache). Keeps the in-flight register footprint of a lane at 9 segments.
 struct HalfMb {
+    float2 xv;  // this lane's 2 activations of the half macro-block (block sums)
     uint4 s[9];
 };
 
-QG_DEV void load_half(HalfMb& d, const uint4* __restrict__ seg, int unit, int rt, bool active) {
+QG_DEV void load_half(HalfMb& d, const uint4* __restrict__ seg, const float* __restrict__ x, int unit, int rt,
+                      int lane) {
     const int mb = unit >> 1, h = unit & 1;
+    d.xv = *reinterpret_cast<const float2*>(x + 128 * unit + 2 * lane);
     const uint4* base = seg + (size_t)mb * 17 * rt;
-    if (active) {
-        d.s[0] = base[0];
+    d.s[0] = base[0];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) d.s[1 + s] = base[(size_t)(1 + 8 * h + s) * rt];
-    } else {
-#pragma unroll
-        for (int s = 0; s < 9; ++s) d.s[s] = make_uint4(0, 0, 0, 0);
-    }
+    for (int s = 0; s < 8; ++s) d.s[1 + s] = base[(size_t)(1 + 8 * h + s) * rt];
 }
 
 QG_DEV float blk_dot(const uint4 a, const uint4 b, qg_uniform_f32 xs) {
@@ -72,13 +70,12 @@ QG_DEV float blk_dot(const uint4 a, const uint4 b, qg_uniform_f32 xs) {
     return s;
 }
 
-// Sums of x over the four 32-element blocks at xb (lane t loads x[2t], x[2t+1];
-// lanes 16k..16k+15 cover block k).
+// Sums of x over four 32-element blocks (lane t holds x[2t], x[2t+1]; lanes
+// 16k..16k+15 cover block k).
 struct QgSub4 {
     float v[4];
 };
-QG_DEV QgSub4 block_sums4(const float* __restrict__ xb, int lane) {
-    const float2 xv = *reinterpret_cast<const float2*>(xb + 2 * lane);
+QG_DEV QgSub4 block_sums4(const float2 xv) {
     float s = xv.x + xv.y;
     s += __shfl_xor(s, 1, 64);
     s += __shfl_xor(s, 2, 64);
@@ -92,8 +89,8 @@ QG_DEV QgSub4 block_sums4(const float* __restrict__ xb, int lane) {
 
 // Dot of half a macro-block (Q8_0 blocks 4h..4h+3 of macro-block mb) with the
 // 128 activations at xs / xb.
-QG_DEV float half_dot(const HalfMb& d, int h, qg_uniform_f32 xs, const float* __restrict__ xb, int lane) {
-    const QgSub4 X = block_sums4(xb, lane);
+QG_DEV float half_dot(const HalfMb& d, int h, qg_uniform_f32 xs) {
+    const QgSub4 X = block_sums4(d.xv);
     const uint32_t dw0 = h ? d.s[0].z : d.s[0].x;
     const uint32_t dw1 = h ? d.s[0].w : d.s[0].y;
     const float dk[4] = {qg_half_lo(dw0), qg_half_hi(dw0), qg_half_lo(dw1), qg_half_hi(dw1)};
@@ -127,7 +124,7 @@ QG_DEV float row_partial(const Q8Prob& P, int tile, int m0, int m1, bool with_ta
     const int rt = min(qg::kTileRows, P.M - tile * qg::kTileRows);
     const bool active = lane < rt;
     const uint8_t* tbase = P.w + (size_t)tile * qg::kTileRows * P.nbq * 34;
-    const uint4* __restrict__ seg = reinterpret_cast<const uint4*>(tbase) + lane;
+    const uint4* __restrict__ seg = reinterpret_cast<const uint4*>(tbase) + (active ? lane : rt - 1);
     qg_uniform_f32 xs = (qg_uniform_f32)P.x;
     // units are half macro-blocks: [2*m0, 2*m1)
     const int u0 = 2 * m0, u1 = 2 * m1;
@@ -136,12 +133,13 @@ QG_DEV float row_partial(const Q8Prob& P, int tile, int m0, int m1, bool with_ta
     float acc = 0.f;
     if (wu0 < wu1) {
         HalfMb cur, nxt;
-        load_half(cur, seg, wu0, rt, active);
-        for (int u = wu0; u < wu1; ++u) {
-            if (u + 1 < wu1) load_half(nxt, seg, u + 1, rt, active);
-            acc += half_dot(cur, u & 1, xs + 128 * u, P.x + 128 * u, lane);
+        load_half(cur, seg, P.x, wu0, rt, lane);
+        for (int u = wu0; u < wu1 - 1; ++u) {
+            load_half(nxt, seg, P.x, u + 1, rt, lane);
+            acc += half_dot(cur, u & 1, xs + 128 * u);
             cur = nxt;
         }
+        acc += half_dot(cur, (wu1 - 1) & 1, xs + 128 * (wu1 - 1));
     }
     if (with_tail && P.tb > 0 && wave == W - 1 && active) {
         const uint8_t* rowtail = tbase + (size_t)P.nmb * 17 * rt * 16 + (size_t)lane * P.tb * 34;
@@ -170,7 +168,7 @@ __global__ __launch_bounds__(64 * W) void q8_0_gemv_kernel(Q8Prob P, float* __re
     const int wg = blockIdx.x;
     const int tile = wg / P.splits;
     const int ks = wg - tile * P.splits;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int m0 = (int)((int64_t)ks * P.nmb / P.splits);
     const int m1 = (int)((int64_t)(ks + 1) * P.nmb / P.splits);
     const float acc = row_partial<W>(P, tile, m0, m1, ks == P.splits - 1, lane, wave);
@@ -217,7 +215,7 @@ __global__ __launch_bounds__(64 * W) void lmhead_argmax_kernel(Q8Prob P, float2*
                                                                  uint32_t* cnt, int32_t* out_index,
                                                                  float* out_value) {
     const int tile = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float acc = row_partial<W>(P, tile, 0, P.nmb, true, lane, wave);
     float v = wg_reduce<W>(acc, lane, wave);
     if (wave != 0) return;

@@ -40,14 +40,18 @@ QG_DEV float qg_sum8(float v) {
     return v;
 }
 
-// Sums of x over the eight 32-element sub-blocks of the 256 elements at xb:
-// lane t loads x[4t..4t+3]; lanes 8j..8j+7 cover sub-block j. Returns sub-block j's
-// sum in every lane for j = 0..7 as wavefront-uniform values.
+// Sums of x over the eight 32-element sub-blocks of 256 activations: lane t holds
+// x[4t..4t+3] (one float4 load, issued ahead of the weight loads it is consumed
+// with so that waiting for it never waits for prefetched weights); lanes
+// 8j..8j+7 cover sub-block j. Returns sub-block j's sum for j = 0..7 as
+// wavefront-uniform values.
 struct QgSub8 {
     float v[8];
 };
-QG_DEV QgSub8 qg_subblock_sums(const float* __restrict__ xb, int lane) {
-    const float4 xv = *reinterpret_cast<const float4*>(xb + 4 * lane);
+QG_DEV float4 qg_x4(const float* __restrict__ xb, int lane) {
+    return *reinterpret_cast<const float4*>(xb + 4 * lane);
+}
+QG_DEV QgSub8 qg_subblock_sums(const float4 xv) {
     float s = ((xv.x + xv.y) + xv.z) + xv.w;
     s = qg_sum8(s);
     QgSub8 r;
