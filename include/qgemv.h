@@ -39,12 +39,11 @@
  *     and mins, 128 bytes of 4-bit quants; weight = d*sc*q - dmin*m.
  *   Q8_0, 34 B per 32 weights: fp16 d, 32 int8 q; weight = d*q.
  *
- * Workspaces: entry points that split a row's dot product across workgroups or
- * reduce across the whole launch take a workspace. Its first
- * QG_WORKSPACE_COUNTER_BYTES bytes hold counters that must be zero before the
- * first use (allocate it zero-filled, or call qg_workspace_clear once); every
- * call that completes leaves them zero again. Size it with the matching
- * *_workspace_bytes query; a smaller workspace gives QG_ERR_WORKSPACE.
+ * Workspaces: the GEMV and small-N entry points take a workspace argument for
+ * ABI stability but use none today (their *_workspace_bytes query returns 0 and
+ * NULL is accepted). lmhead_argmax needs lmhead_argmax_workspace_bytes(M, K)
+ * bytes of scratch for its per-workgroup partial results; the contents need no
+ * initialisation and are dead after the call.
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -57,7 +56,6 @@ extern "C" {
 #endif
 
 #define QG_ABI_VERSION 1
-#define QG_WORKSPACE_COUNTER_BYTES 65536
 #define QG_MAX_BATCH 8
 #define QG_SMALLN_MAX 32
 
@@ -89,8 +87,8 @@ size_t qg_q8_0_bytes(int64_t M, int64_t K);
 int qg_pack_q4k(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t stream);
 int qg_pack_q8_0(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t stream);
 
-/* Zero-fill `bytes` of a workspace with a kernel (no memset node, so it can sit
- * in a captured graph). */
+/* Zero-fill `bytes` of a device buffer with a kernel (no memset node, so it can
+ * sit in a captured graph). */
 int qg_workspace_clear(void* workspace, size_t bytes, qg_stream_t stream);
 
 /*

@@ -16,7 +16,6 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "qgemv.h")
 
-WORKSPACE_COUNTER_BYTES = 65536
 MAX_BATCH = 8
 SMALLN_MAX = 32
 
@@ -111,10 +110,7 @@ def _need_cuda(*ts):
 
 # ------------------------------------------------------------------ workspace
 class Workspace:
-    """A zero-initialised device buffer reused across calls on one stream.
-
-    Its leading counter area is left zero by every completed call, so it only
-    needs zeroing once, at allocation."""
+    """A device scratch buffer reused across calls on one stream (grown on demand)."""
 
     def __init__(self, device=None, nbytes: int = 0):
         self.device = torch.device(device if device is not None else "cuda")

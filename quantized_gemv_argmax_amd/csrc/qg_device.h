@@ -6,14 +6,15 @@
 
 #define QG_DEV __device__ __forceinline__
 
+// Rows per packed tile. Sixteen rows are one DPP row of a wavefront.
+#define QG_TILE_ROWS 16
+
 // Loads through the constant address space are selected as scalar (SMEM) loads
-// whenever the address is wavefront-uniform: activation values shared by all 64
-// rows of a wavefront land in SGPRs and feed the FMAs directly.
+// whenever the address is wavefront-uniform.
 typedef const __attribute__((address_space(4))) float* qg_uniform_f32;
 
 // Hide a value's bit pattern from the optimizer so that byte-wise conversions
-// stay v_cvt_f32_ubyte{0..3} on the masked word instead of one bit-field extract
-// per nibble.
+// stay v_cvt_f32_ubyte{0..3} on the masked word.
 QG_DEV uint32_t qg_opaque(uint32_t v) {
     asm volatile("" : "+v"(v));
     return v;
@@ -31,33 +32,164 @@ QG_DEV float qg_readlane(float v, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
-// Sum over each aligned group of 8 lanes; every lane of the group gets the same
-// (bitwise identical) value.
-QG_DEV float qg_sum8(float v) {
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    return v;
+// ---------------------------------------------------------------------------
+// DPP row broadcast (row_newbcast:L): every lane of a 16-lane DPP row reads the
+// operand of lane L of its own row. Used to share activation registers across the
+// 16 weight rows a DPP row processes, at no instruction cost.
+//
+// Hazard rule on gfx9: a VGPR written by a VALU instruction needs two wait states
+// before any DPP instruction reads it (through any operand, the accumulator of
+// v_dot2c included). The compiler cannot see inside inline assembly, so the
+// blocks below schedule their own instructions to respect it: every mask is
+// computed at least two instructions before the dot product that reads it, each
+// accumulator is re-read at least two instructions after its last write, and the
+// activation pairs are produced by qg_cvt_pairs*, which end with s_nop 1.
+// A v_dot2c result read by an ordinary VALU instruction two instructions after
+// the DPP dot product was observed stale on gfx950, so each block ends with
+// s_nop 4 before the compiler's own code reads the accumulators.
+
+// Broadcast of lane L of this DPP row (compiler-tracked, hazards handled by it).
+template <int L>
+QG_DEV float qg_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + L, 0xf, 0xf, true));
 }
 
-// Sums of x over the eight 32-element sub-blocks of 256 activations: lane t holds
-// x[4t..4t+3] (one float4 load, issued ahead of the weight loads it is consumed
-// with so that waiting for it never waits for prefetched weights); lanes
-// 8j..8j+7 cover sub-block j. Returns sub-block j's sum for j = 0..7 as
-// wavefront-uniform values.
-struct QgSub8 {
-    float v[8];
-};
-QG_DEV float4 qg_x4(const float* __restrict__ xb, int lane) {
-    return *reinterpret_cast<const float4*>(xb + 4 * lane);
+// Q4_K: one 16-byte quant segment (4 dwords, 32 weights) against the activation
+// pairs of lanes LA (dwords 0, 1) and LB (dwords 2, 3) of this DPP row. For each
+// dword: low nibbles of bytes 0,2 / 1,3 go to lo0 / lo1 with pairs x[r+0] / x[r+1],
+// high nibbles of bytes 0,2 / 1,3 go to hi0 / hi1 with pairs x[r+2] / x[r+3]
+// (r = 0 for dwords 0 and 2, r = 4 for dwords 1 and 3). The nibbles are masked in
+// place and read as fp16 subnormals (q * 2^-24, high ones 16q * 2^-24).
+template <int LA, int LB>
+QG_DEV void qg_q4_seg_dot(float& lo0, float& hi0, float& lo1, float& hi1, const uint4 q, const uint32_t (&x)[8]) {
+    uint32_t m0, m1, m2, m3, m4, m5, m6, m7, t;
+    asm("v_and_b32 %4, 0xf000f, %13\n\t"
+        "v_and_b32 %5, 0xf000f0, %13\n\t"
+        "v_lshrrev_b32 %12, 8, %13\n\t"
+        "v_and_b32 %6, 0xf000f, %12\n\t"
+        "v_and_b32 %7, 0xf000f0, %12\n\t"
+        "v_and_b32 %8, 0xf000f, %14\n\t"
+        "v_and_b32 %9, 0xf000f0, %14\n\t"
+        "v_lshrrev_b32 %12, 8, %14\n\t"
+        "v_and_b32 %10, 0xf000f, %12\n\t"
+        "v_and_b32 %11, 0xf000f0, %12\n\t"
+        "v_dot2c_f32_f16_dpp %0, %17, %4 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %1, %19, %5 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %2, %18, %6 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %3, %20, %7 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+        "v_and_b32 %4, 0xf000f, %15\n\t"
+        "v_and_b32 %5, 0xf000f0, %15\n\t"
+        "v_lshrrev_b32 %12, 8, %15\n\t"
+        "v_and_b32 %6, 0xf000f, %12\n\t"
+        "v_and_b32 %7, 0xf000f0, %12\n\t"
+        "v_dot2c_f32_f16_dpp %0, %21, %8 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %1, %23, %9 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %2, %22, %10 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %3, %24, %11 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+        "v_and_b32 %8, 0xf000f, %16\n\t"
+        "v_and_b32 %9, 0xf000f0, %16\n\t"
+        "v_lshrrev_b32 %12, 8, %16\n\t"
+        "v_and_b32 %10, 0xf000f, %12\n\t"
+        "v_and_b32 %11, 0xf000f0, %12\n\t"
+        "v_dot2c_f32_f16_dpp %0, %17, %4 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %1, %19, %5 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %2, %18, %6 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %3, %20, %7 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %0, %21, %8 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %1, %23, %9 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %2, %22, %10 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %3, %24, %11 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 4"
+        : "+v"(lo0), "+v"(hi0), "+v"(lo1), "+v"(hi1), "=&v"(m0), "=&v"(m1), "=&v"(m2), "=&v"(m3), "=&v"(m4),
+          "=&v"(m5), "=&v"(m6), "=&v"(m7), "=&v"(t)
+        : "v"(q.x), "v"(q.y), "v"(q.z), "v"(q.w), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]),
+          "v"(x[6]), "v"(x[7]), "n"(LA), "n"(LB));
 }
-QG_DEV QgSub8 qg_subblock_sums(const float4 xv) {
-    float s = ((xv.x + xv.y) + xv.z) + xv.w;
-    s = qg_sum8(s);
-    QgSub8 r;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r.v[j] = qg_readlane(s, 8 * j);
+
+// Q8_0: one 16-byte quant segment (16 int8) against the activation pairs of lanes
+// LA (dwords 0, 1: pairs x[0..3]) and LB (dwords 2, 3: pairs x[0..3]). The quants
+// are biased to bytes (q ^ 0x80 = q + 128), bytes 0,2 and 1,3 of each dword masked
+// in place and read as fp16 subnormals ((q + 128) * 2^-24). Dwords 0 and 2 feed
+// a0 / a1, dwords 1 and 3 feed a2 / a3.
+template <int LA, int LB>
+QG_DEV void qg_q8_seg_dot(float& a0, float& a1, float& a2, float& a3, const uint4 q, const uint32_t (&x)[4]) {
+    uint32_t u0, m0, t0, n0, u1, m1, t1, n1;
+    asm("v_xor_b32 %4, 0x80808080, %12\n\t"
+        "v_and_b32 %5, 0xff00ff, %4\n\t"
+        "v_lshrrev_b32 %6, 8, %4\n\t"
+        "v_and_b32 %7, 0xff00ff, %6\n\t"
+        "v_xor_b32 %8, 0x80808080, %13\n\t"
+        "v_and_b32 %9, 0xff00ff, %8\n\t"
+        "v_lshrrev_b32 %10, 8, %8\n\t"
+        "v_and_b32 %11, 0xff00ff, %10\n\t"
+        "v_dot2c_f32_f16_dpp %0, %16, %5 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %1, %17, %7 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
+        "v_xor_b32 %4, 0x80808080, %14\n\t"
+        "v_and_b32 %5, 0xff00ff, %4\n\t"
+        "v_lshrrev_b32 %6, 8, %4\n\t"
+        "v_and_b32 %7, 0xff00ff, %6\n\t"
+        "v_dot2c_f32_f16_dpp %2, %18, %9 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %3, %19, %11 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
+        "v_xor_b32 %8, 0x80808080, %15\n\t"
+        "v_and_b32 %9, 0xff00ff, %8\n\t"
+        "v_lshrrev_b32 %10, 8, %8\n\t"
+        "v_and_b32 %11, 0xff00ff, %10\n\t"
+        "v_dot2c_f32_f16_dpp %0, %16, %5 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %1, %17, %7 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %2, %18, %9 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %3, %19, %11 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 4"
+        : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "=&v"(u0), "=&v"(m0), "=&v"(t0), "=&v"(n0), "=&v"(u1), "=&v"(m1),
+          "=&v"(t1), "=&v"(n1)
+        : "v"(q.x), "v"(q.y), "v"(q.z), "v"(q.w), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "n"(LA), "n"(LB));
+}
+
+// Eight fp16x2 pairs (round to nearest even) from four float4, in the order
+// (a.x,a.z) (a.y,a.w) (b.x,b.z) (b.y,b.w) (c...) (d...), then two wait states.
+struct QgPairs8 {
+    uint32_t p[8];
+};
+QG_DEV QgPairs8 qg_cvt_pairs(const float4 a, const float4 b, const float4 c, const float4 d) {
+    QgPairs8 r;
+    asm volatile(
+        "v_cvt_pk_f16_f32 %0, %8, %10\n\t"
+        "v_cvt_pk_f16_f32 %1, %9, %11\n\t"
+        "v_cvt_pk_f16_f32 %2, %12, %14\n\t"
+        "v_cvt_pk_f16_f32 %3, %13, %15\n\t"
+        "v_cvt_pk_f16_f32 %4, %16, %18\n\t"
+        "v_cvt_pk_f16_f32 %5, %17, %19\n\t"
+        "v_cvt_pk_f16_f32 %6, %20, %22\n\t"
+        "v_cvt_pk_f16_f32 %7, %21, %23\n\t"
+        "s_nop 1"
+        : "=&v"(r.p[0]), "=&v"(r.p[1]), "=&v"(r.p[2]), "=&v"(r.p[3]), "=&v"(r.p[4]), "=&v"(r.p[5]),
+          "=&v"(r.p[6]), "=&v"(r.p[7])
+        : "v"(a.x), "v"(a.y), "v"(a.z), "v"(a.w), "v"(b.x), "v"(b.y), "v"(b.z), "v"(b.w), "v"(c.x), "v"(c.y),
+          "v"(c.z), "v"(c.w), "v"(d.x), "v"(d.y), "v"(d.z), "v"(d.w));
     return r;
+}
+
+// Four fp16x2 pairs from two float4: (a.x,a.z) (a.y,a.w) (b.x,b.z) (b.y,b.w),
+// then two wait states.
+struct QgPairs4 {
+    uint32_t p[4];
+};
+QG_DEV QgPairs4 qg_cvt_pairs4(const float4 a, const float4 b) {
+    QgPairs4 r;
+    asm volatile(
+        "v_cvt_pk_f16_f32 %0, %4, %6\n\t"
+        "v_cvt_pk_f16_f32 %1, %5, %7\n\t"
+        "v_cvt_pk_f16_f32 %2, %8, %10\n\t"
+        "v_cvt_pk_f16_f32 %3, %9, %11\n\t"
+        "s_nop 1"
+        : "=&v"(r.p[0]), "=&v"(r.p[1]), "=&v"(r.p[2]), "=&v"(r.p[3])
+        : "v"(a.x), "v"(a.y), "v"(a.z), "v"(a.w), "v"(b.x), "v"(b.y), "v"(b.z), "v"(b.w));
+    return r;
+}
+
+// Sum over each quad of lanes (all four lanes get the same value).
+QG_DEV float qg_quad_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, true));  // [1,0,3,2]
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, true));  // [2,3,0,1]
 }
 
 // Q4_K 6-bit fields: four bytes of sub-scales / mins per word, as packed bytes.
@@ -76,12 +208,9 @@ QG_DEV QgScales qg_q4k_scales(uint32_t s0, uint32_t s1, uint32_t s2) {
     return r;
 }
 
-// Agent-scope ticket: returns the counter's previous value (wavefront-uniform).
-QG_DEV uint32_t qg_ticket(uint32_t* counter, int lane) {
-    uint32_t old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    return (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
-}
-QG_DEV void qg_ticket_reset(uint32_t* counter, int lane) {
-    if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Sum of a value over the four DPP rows (lanes i, i+16, i+32, i+48).
+QG_DEV float qg_sum_rows4(float v) {
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
 }

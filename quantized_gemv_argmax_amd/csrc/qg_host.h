@@ -12,10 +12,6 @@
 
 namespace qg {
 
-// Rows per packed tile: one wavefront lane per row.
-constexpr int kTileRows = 64;
-constexpr int kCounterSlots = QG_WORKSPACE_COUNTER_BYTES / 4;
-
 int fail(int status, const char* fmt, ...);   // records the message, returns status
 void clear_error();
 

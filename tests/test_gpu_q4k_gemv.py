@@ -77,7 +77,7 @@ def test_zero_scales_give_exact_zero():
     assert np.all(y == 0)
 
 
-def test_deterministic_and_counters_left_zero():
+def test_deterministic():
     M, K = 3584, 3584
     W = workloads.q4k_blocks(M, K, key=(12,))
     x = to_dev(workloads.x_vector(K, key=(12,)))
@@ -88,7 +88,6 @@ def test_deterministic_and_counters_left_zero():
     y2 = qg.qgemv_q4k(wp, x, M, K, ws=ws).clone()
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
-    assert int(ws.buf[:qg.WORKSPACE_COUNTER_BYTES].sum().item()) == 0
 
 
 def test_pack_is_a_permutation():
@@ -100,6 +99,8 @@ def test_pack_is_a_permutation():
     assert np.array_equal(np.sort(p), np.sort(W.reshape(-1)))
     # segment 0 of super-block 0 of row i of tile 0 is bytes 0..15 of that row
     assert np.array_equal(p[16 * 5:16 * 6], W[5, :16])
+    # segment 1 of super-block 0 of row 3 of tile 0 (16 rows): offset (1 * 16 + 3) * 16
+    assert np.array_equal(p[16 * 19:16 * 20], W[3, 16:32])
 
 
 def test_batch_matches_oracle_per_problem():
