@@ -72,6 +72,8 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="skip the other hot-path rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="end with one plain 256 MiB device copy (a reference dispatch for traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -211,6 +213,11 @@ def main():
         "rows": rows,
     }
     print(json.dumps(out), flush=True)
+    if args.copy_ref:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):

@@ -35,6 +35,7 @@
 // Rounding x to fp16 changes each product by at most 2^-11 relative, well inside
 // the 1e-3 * sum|w*x| bound; accumulation is fp32.
 #include <algorithm>
+#include <cstdlib>
 
 #include "qg_device.h"
 #include "qg_host.h"
@@ -50,9 +51,12 @@ struct Q4Prob {
     int32_t M, nb, tiles, wg_begin;
 };
 
+// Kernel arguments. The first tile of every problem is repeated in a compact
+// array at the front, so a workgroup finds its problem with one scalar load.
 struct Q4Args {
-    Q4Prob p[QG_MAX_BATCH];
+    int32_t begin[QG_MAX_BATCH];
     int32_t count;
+    Q4Prob p[QG_MAX_BATCH];
 };
 
 struct SbIn {
@@ -68,7 +72,7 @@ QG_DEV void load_sb(SbIn& d, const uint4* __restrict__ seg, const float* __restr
     d.xd = *reinterpret_cast<const float4*>(xb + 36);
     const uint4* sb = seg + (size_t)b * 9 * rt;
 #pragma unroll
-    for (int s = 0; s < 9; ++s) d.s[s] = sb[s * rt];
+    for (int s = 0; s < 9; ++s) d.s[s] = qg_stream_load(sb + s * rt);
 }
 
 // Contribution of one super-block for this lane's row.
@@ -134,12 +138,15 @@ QG_DEV float sb_dot(const SbIn& d) {
     return fmaf(dd * 16777216.0f, t, -dm * mn);
 }
 
-template <int W>
+// MODE 0: one super-block per K-group; 1: several, one register buffer (load,
+// compute, load, ...); 2: several, two register buffers (ping-pong prefetch).
+template <int W, int MODE>
 __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(Q4Args a) {
     const int wg = blockIdx.x;
     int k = 0;
-    for (int i = 1; i < a.count; ++i)
-        if (wg >= a.p[i].wg_begin) k = i;
+#pragma unroll
+    for (int i = 1; i < QG_MAX_BATCH; ++i)
+        if (i < a.count && wg >= a.begin[i]) k = i;
     const Q4Prob P = a.p[k];
 
     const int tile = wg - P.wg_begin;
@@ -158,19 +165,36 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(Q4Args a) {
     const uint4* __restrict__ seg =
         reinterpret_cast<const uint4*>(P.w + (size_t)tile * T * nb * 144) + min(i, rt - 1);
 
-    const int niter = (nb + G - 1) / G;
     float acc = 0.f;
-    SbIn cur, nxt;
-    load_sb(cur, seg, xk, min(kg, nb - 1), rt);
-    for (int it = 0; it < niter - 1; ++it) {
-        load_sb(nxt, seg, xk, min(kg + G * (it + 1), nb - 1), rt);
-        const float v = sb_dot(cur);
-        acc += (kg + G * it < nb) ? v : 0.f;
-        cur = nxt;
+    if constexpr (MODE == 0) {  // one super-block per K-group (4W >= K/256)
+        SbIn b0;
+        load_sb(b0, seg, xk, min(kg, nb - 1), rt);
+        const float v0 = sb_dot(b0);
+        acc = (kg < nb) ? v0 : 0.f;
+    } else if constexpr (MODE == 1) {
+        const int niter = (nb + G - 1) / G;
+        for (int it = 0; it < niter; ++it) {
+            SbIn b0;
+            load_sb(b0, seg, xk, min(kg + G * it, nb - 1), rt);
+            const float v0 = sb_dot(b0);
+            acc += (kg + G * it < nb) ? v0 : 0.f;
+        }
+    } else {
+    const int niter = (nb + G - 1) / G;
+    // ping-pong between two register buffers: the loads of one super-block stay in
+    // flight while the other is computed, with no register copies in between
+    SbIn b0, b1;
+    load_sb(b0, seg, xk, min(kg, nb - 1), rt);
+    for (int it = 0;; it += 2) {
+        if (it + 1 < niter) load_sb(b1, seg, xk, min(kg + G * (it + 1), nb - 1), rt);
+        const float v0 = sb_dot(b0);
+        acc += (kg + G * it < nb) ? v0 : 0.f;
+        if (it + 1 >= niter) break;
+        if (it + 2 < niter) load_sb(b0, seg, xk, min(kg + G * (it + 2), nb - 1), rt);
+        const float v1 = sb_dot(b1);
+        acc += (kg + G * (it + 1) < nb) ? v1 : 0.f;
+        if (it + 2 >= niter) break;
     }
-    {
-        const float v = sb_dot(cur);
-        acc += (kg + G * (niter - 1) < nb) ? v : 0.f;
     }
 
     float v = qg_sum_rows4(acc);
@@ -186,6 +210,122 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(Q4Args a) {
         }
     }
     if (lane < rt) P.y[tile * T + lane] = v;
+}
+
+// Persistent form: a fixed grid of workgroups walks the tiles of all problems
+// (tile = blockIdx.x, + gridDim.x, ...). Each K-group keeps the loads of its next
+// work item (next super-block, or the first super-block of the next tile) in flight
+// while it computes the current one, so a wavefront streams continuously and no
+// workgroup is launched or retired per tile.
+QG_DEV int find_prob(const Q4Args& a, int gt) {
+    int k = 0;
+#pragma unroll
+    for (int i = 1; i < QG_MAX_BATCH; ++i)
+        if (i < a.count && gt >= a.begin[i]) k = i;
+    return k;
+}
+
+template <int W>
+QG_DEV void load_item(SbIn& d, const Q4Prob& P, int tile, int it, int kg, int i, int xoff) {
+    constexpr int G = 4 * W;
+    const int rt = min(T, P.M - tile * T);
+    const uint4* seg = reinterpret_cast<const uint4*>(P.w + (size_t)tile * T * P.nb * 144) + min(i, rt - 1);
+    load_sb(d, seg, P.x + xoff, min(kg + G * it, P.nb - 1), rt);
+}
+
+// Work item of a workgroup: super-block iteration `it` of global tile `gt`
+// (problem k). `valid` is false past the end of the workgroup's tile sequence.
+struct Item {
+    int gt, it, k;
+    bool valid;
+};
+
+// The item after c in this workgroup's sequence. Past the end, the result keeps
+// c's address (its load is re-issued and unused) and is marked invalid; every call
+// advances (it + 1, or gt + gridDim.x), so the sequence ends after at most
+// total_tiles * iterations steps.
+template <int W>
+QG_DEV Item next_item(const Q4Args& a, const Item c, int total_tiles) {
+    constexpr int G = 4 * W;
+    Item n = c;
+    bool ok = true;
+    n.it = c.it + 1;
+    if (n.it == (a.p[c.k].nb + G - 1) / G) {
+        n.gt = c.gt + gridDim.x;
+        n.it = 0;
+        ok = n.gt < total_tiles;
+        if (ok) n.k = find_prob(a, n.gt);
+    }
+    if (!ok) {
+        n.gt = c.gt;
+        n.it = c.it;
+        n.k = c.k;
+    }
+    n.valid = ok && c.valid;
+    return n;
+}
+
+template <int W>
+struct PersistState {
+    float acc = 0.f;
+    int parity = 0;
+};
+
+// Compute item c from buffer d; on the last super-block of a tile, reduce over the
+// K-groups and wavefronts and store the tile's 16 outputs.
+template <int W>
+QG_DEV void process(PersistState<W>& st, float (&red)[2][W][T], const Q4Args& a, const SbIn& d, const Item c, int lane,
+                    int wave, int kg) {
+    constexpr int G = 4 * W;
+    const Q4Prob& P = a.p[c.k];
+    const float v = sb_dot(d);
+    st.acc += (kg + G * c.it < P.nb) ? v : 0.f;
+    if (c.it == (P.nb + G - 1) / G - 1) {
+        const int tile = c.gt - P.wg_begin;
+        const int rt = min(T, P.M - tile * T);
+        float r = qg_sum_rows4(st.acc);
+        if constexpr (W > 1) {
+            if (lane < T) red[st.parity][wave][lane] = r;
+            __syncthreads();
+            if (wave == 0 && lane < T) {
+                r = red[st.parity][0][lane];
+#pragma unroll
+                for (int w = 1; w < W; ++w) r += red[st.parity][w][lane];
+            }
+            st.parity ^= 1;
+        }
+        if (wave == 0 && lane < rt) P.y[tile * T + lane] = r;
+        st.acc = 0.f;
+    }
+}
+
+template <int W>
+__global__ __launch_bounds__(64 * W) void q4k_gemv_persist_kernel(Q4Args a, int total_tiles) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i = lane & 15;
+    const int kg = 4 * wave + (lane >> 4);
+    const int p = i >> 1;
+    const int xoff = 64 * (p >> 1) + 16 * (p & 1) + 8 * (i & 1);
+    __shared__ float red[2][W][T];
+
+    PersistState<W> st;
+    Item c0{(int)blockIdx.x, 0, find_prob(a, blockIdx.x), true};
+    SbIn b0, b1;
+    load_item<W>(b0, a.p[c0.k], c0.gt - a.p[c0.k].wg_begin, c0.it, kg, i, xoff);
+    // ping-pong between two register buffers: the loads of one item stay in
+    // flight while the other is computed, with no register copies in between
+    while (true) {
+        const Item c1 = next_item<W>(a, c0, total_tiles);
+        load_item<W>(b1, a.p[c1.k], c1.gt - a.p[c1.k].wg_begin, c1.it, kg, i, xoff);
+        process<W>(st, red, a, b0, c0, lane, wave, kg);
+        if (!c1.valid) break;
+        const Item c2 = next_item<W>(a, c1, total_tiles);
+        load_item<W>(b0, a.p[c2.k], c2.gt - a.p[c2.k].wg_begin, c2.it, kg, i, xoff);
+        process<W>(st, red, a, b1, c1, lane, wave, kg);
+        if (!c2.valid) break;
+        c0 = c2;
+    }
 }
 
 __global__ void q4k_pack_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t M, int nb) {
@@ -206,8 +346,20 @@ __global__ void q4k_pack_kernel(const uint4* __restrict__ src, uint4* __restrict
 // Launch plan: one workgroup per 16-row tile; W wavefronts (4W K-groups) each.
 struct Plan {
     int W = 1;
-    int total_wg = 0;
+    int total_wg = 0;  // tiles over all problems
 };
+
+int cu_count() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 void plan_batch(const qg_gemv_problem* pr, int count, Q4Args* args, Plan* plan) {
     int64_t tiles_total = 0;
@@ -216,12 +368,14 @@ void plan_batch(const qg_gemv_problem* pr, int count, Q4Args* args, Plan* plan) 
         tiles_total += qg::ceil_div(pr[i].M, T);
         nb_max = std::max(nb_max, (int)(pr[i].K / 256));
     }
-    // About 4 wavefronts per CU at least, and no more K-groups per tile than
-    // there are super-blocks.
+    // Enough K-groups per tile that every super-block of a row has its own
+    // (all of a tile's weights are requested at once), up to 4 wavefronts; a
+    // measured sweep over the 7B decode shapes put W = 4 first for every stage.
+    (void)tiles_total;
     int W = 1;
-    while (W < 8 && tiles_total * W < 1024 && 4 * (2 * W) <= nb_max + 3) W *= 2;
+    while (W < 4 && 4 * W < nb_max) W *= 2;
     int ew = 0, eu = 0;
-    if (qg::env_pair("QG_Q4K_CFG", &ew, &eu) && (ew == 1 || ew == 2 || ew == 4 || ew == 8)) W = ew;
+    if (qg::env_pair("QG_Q4K_CFG", &ew, &eu) && (ew == 1 || ew == 2 || ew == 4 || ew == 8 || ew == 16)) W = ew;
     plan->W = W;
     int wg = 0;
     for (int i = 0; i < count; ++i) {
@@ -233,6 +387,7 @@ void plan_batch(const qg_gemv_problem* pr, int count, Q4Args* args, Plan* plan) 
         P.nb = (int32_t)(pr[i].K / 256);
         P.tiles = (int32_t)qg::ceil_div(pr[i].M, T);
         P.wg_begin = wg;
+        args->begin[i] = wg;
         wg += P.tiles;
     }
     args->count = count;
@@ -258,8 +413,23 @@ int validate(const qg_gemv_problem* pr, int count) {
 }
 
 template <int W>
-void launch(const Q4Args& a, int grid, hipStream_t s) {
-    hipLaunchKernelGGL(q4k_gemv_kernel<W>, dim3(grid), dim3(64 * W), 0, s, a);
+void launch(const Q4Args& a, int tiles, hipStream_t s) {
+    bool multi = false;  // some K-group walks more than one super-block
+    for (int i = 0; i < a.count; ++i) multi = multi || a.p[i].nb > 4 * W;
+    // A grid of one workgroup per tile measured faster than a persistent grid on
+    // the 7B decode shapes; QG_Q4K_PERSIST=n selects a persistent grid of n
+    // workgroups per CU.
+    const char* e = getenv("QG_Q4K_PERSIST");
+    const int per_cu = (e && *e) ? atoi(e) : 0;
+    const int grid = per_cu > 0 ? std::min(tiles, per_cu * cu_count()) : tiles;
+    if (grid < tiles)
+        hipLaunchKernelGGL(q4k_gemv_persist_kernel<W>, dim3(grid), dim3(64 * W), 0, s, a, tiles);
+    else if (!multi)
+        hipLaunchKernelGGL((q4k_gemv_kernel<W, 0>), dim3(tiles), dim3(64 * W), 0, s, a);
+    else if constexpr (W >= 16)
+        hipLaunchKernelGGL((q4k_gemv_kernel<W, 1>), dim3(tiles), dim3(64 * W), 0, s, a);
+    else
+        hipLaunchKernelGGL((q4k_gemv_kernel<W, 2>), dim3(tiles), dim3(64 * W), 0, s, a);
 }
 
 }  // namespace
@@ -288,7 +458,8 @@ int qgemv_q4k_batch(const qg_gemv_problem* problems, int count, void* ws, size_t
         case 1: launch<1>(a, p.total_wg, s); break;
         case 2: launch<2>(a, p.total_wg, s); break;
         case 4: launch<4>(a, p.total_wg, s); break;
-        default: launch<8>(a, p.total_wg, s); break;
+        case 8: launch<8>(a, p.total_wg, s); break;
+        default: launch<16>(a, p.total_wg, s); break;
     }
     return qg::launch_status("qgemv_q4k");
 }

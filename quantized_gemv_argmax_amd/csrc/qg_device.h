@@ -13,6 +13,18 @@
 // whenever the address is wavefront-uniform.
 typedef const __attribute__((address_space(4))) float* qg_uniform_f32;
 
+// Weight loads: read once per call, so they are marked non-temporal (streamed
+// past the caches) unless QG_TEMPORAL_WEIGHTS is defined.
+QG_DEV uint4 qg_stream_load(const uint4* p) {
+#ifdef QG_TEMPORAL_WEIGHTS
+    return *p;
+#else
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const u4 v = __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+#endif
+}
+
 // Hide a value's bit pattern from the optimizer so that byte-wise conversions
 // stay v_cvt_f32_ubyte{0..3} on the masked word.
 QG_DEV uint32_t qg_opaque(uint32_t v) {
