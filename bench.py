@@ -63,6 +63,33 @@ def graph_ms(torch, fn, reps: int, warm: int = 2) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "q4k_gemv_7b_decode_step_traffic.md")
+TRAFFIC_SOURCES = ("quantized_gemv_argmax_amd/csrc/q4k_gemv.hip", "quantized_gemv_argmax_amd/csrc/qg_device.h")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per Q4_K GEMV launch from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy's counts), or None when the kernel sources have
+    changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as fh:
+            kv = dict(line.split(": ", 1) for line in fh.read().splitlines() if ": " in line and not line.startswith(" "))
+    except OSError:
+        return None
+    if kv.get("kernel-source-hash", "").strip() != kernel_source_hash():
+        return None
+    return float(kv["traffic-per-launch-bytes"])
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,53 +155,52 @@ def main():
     torch.cuda.synchronize()
     log("warm-up done; capturing the step graph")
 
-    # timed region: K steps replayed from one captured graph, events on the stream
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    torch.cuda.synchronize()
+    # timed region: K steps replayed from one captured graph; an event before every
+    # replay and one after the last, all on the stream the graph is launched on
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
     for _ in range(args.warmup):
         g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
+    for k in range(args.steps):
+        evs[k].record()
         g.replay()
-    e1.record()
+    evs[-1].record()
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    per_step = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps)])  # ms
+    ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
-    log(f"step {ms_step:.4f} ms -> {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s)")
+    log(f"step {ms_step:.4f} ms -> {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s); "
+        f"median {np.median(per_step):.4f} ms, best {per_step.min():.4f} ms, cv {per_step.std() / per_step.mean():.4f}")
 
-    # roofline of the dominant kernel: per-launch events, with the GPU kept busy by
-    # graph replays queued first so that every event pair brackets GPU time only
-    ev = []
-    for _ in range(8):
-        g.replay()
-    for st in stages:
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        qg.qgemv_q4k_batch(st, ws=ws)
-        b.record()
-        ev.append((a, b, sum(p[0].numel() + 4 * (p[3] + p[4]) for p in st)))
-    torch.cuda.synchronize()
-    durs = np.array([a.elapsed_time(b) for a, b, _ in ev])  # ms
-    lbytes = np.array([n for _, _, n in ev], dtype=np.float64)
-    achieved = lbytes.sum() / (durs.sum() * 1e-3) / 1e9
+    # roofline of the dominant kernel (every launch of the step is a Q4_K GEMV): the
+    # average launch duration is the timed region's length over its launch count
+    # (launches run back to back inside the graph); per stage, the same for a graph
+    # of one stage's 28 launches (different layers, so the weights stay cold)
+    n_launch = len(stages)
+    avg_launch_ms = ms_step / n_launch
+    avg_launch_bytes = step_bytes / n_launch
+    achieved = avg_launch_bytes / (avg_launch_ms * 1e-3) / 1e9
     per_stage = {}
     for k, name in enumerate(["qkv", "o", "gate_up", "down"]):
-        d = durs[k::4]
-        per_stage[name] = {"avg_us": round(float(d.mean() * 1e3), 3),
-                           "bytes": int(lbytes[k]),
-                           "GBps": round(float(lbytes[k] / (d.mean() * 1e-3) / 1e9), 1)}
-    log(f"dominant kernel: {achieved:.1f} GB/s over {len(ev)} launches, per stage {per_stage}")
+        sts = stages[k::4]
+        nb = sum(p[0].numel() + 4 * (p[3] + p[4]) for p in sts[0])
+
+        def stage_fn(sts=sts):
+            for st in sts:
+                qg.qgemv_q4k_batch(st, ws=ws)
+        us = graph_ms(torch, stage_fn, reps=max(10, args.steps // 2)) * 1e3 / len(sts)
+        per_stage[name] = {"avg_us": round(us, 3), "bytes": int(nb), "GBps": round(nb / (us * 1e-6) / 1e9, 1)}
+    log(f"dominant kernel: {achieved:.1f} GB/s, {avg_launch_ms * 1e3:.3f} us per launch; per stage {per_stage}")
+    traffic = measured_traffic()
     roofline = {"kernel": "q4k_gemv_kernel", "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "launches_per_step": len(stages), "avg_launch_us": round(float(durs.mean() * 1e3), 3),
-                "avg_bytes_per_launch": int(lbytes.mean()), "per_stage": per_stage}
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": None if traffic is None else int(traffic),
+                "launches_per_step": n_launch, "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+                "avg_bytes_per_launch": int(avg_launch_bytes), "per_stage": per_stage}
 
     rows = {}
     if not args.no_rows:
@@ -205,6 +231,9 @@ def main():
             "weight_bytes_per_step": int(w_bytes),
             "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
             "equiv_tokens_per_s": round(1e3 / ms_step, 1),
+            "ms_per_step_median": round(float(np.median(per_step)), 4),
+            "ms_per_step_best": round(float(per_step.min()), 4),
+            "ms_per_step_cv": round(float(per_step.std() / per_step.mean()), 4),
             "launches_per_step": len(stages),
             "timing": "HIP graph of one step, replayed; events on the launch stream",
         },
