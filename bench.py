@@ -327,27 +327,38 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     log(f"row lmhead: {rows['lmhead_argmax_152064x3584']}")
     del copies, wp
 
-    # small-N verify over the 196 decode matrices (weights read once per call)
+    # small-N verify over the 196 decode matrices (weights read once per call), one
+    # grouped launch per dependency stage as in the decode step
     for N in (5, 32):
-        Xs, Ys = [], []
+        sstages = []
         for L in range(n_layers):
-            for i, (name, M, K) in enumerate(wl.LAYER_MATRICES):
-                Xs.append(torch.from_numpy(wl.x_columns(K, N, key=(5, L, i, N))).to(dev))
-                Ys.append(torch.empty((N, (M + 3) // 4 * 4), device=dev))
-        flat = [m for Lm in layers for m in Lm]
+            for st in wl.LAYER_STAGES:
+                grp = []
+                for i in st:
+                    wp_, _, _, M_, K_ = layers[L][i]
+                    X_ = torch.from_numpy(wl.x_columns(K_, N, key=(5, L, i, N))).to(dev)
+                    grp.append((wp_, X_, torch.empty((N, (M_ + 3) // 4 * 4), device=dev), M_, K_))
+                sstages.append(grp)
 
-        def vstep():
-            for (wp_, _, _, M_, K_), X_, Y_ in zip(flat, Xs, Ys):
-                qg.qgemm_q4k_smalln(wp_, X_, M_, K_, Y=Y_, ws=ws)
+        def vstep(sts=sstages):
+            for grp in sts:
+                qg.qgemm_q4k_smalln_batch(grp, ws=ws)
 
         ms = graph_ms(torch, vstep, 5)
+        flat = [m for grp in sstages for m in grp]
         wb = sum(m[0].numel() for m in flat)
         b = wb + sum(4 * N * (m[3] + m[4]) for m in flat)
+        per_stage = {}
+        for k, name in enumerate(["qkv", "o", "gate_up", "down"]):
+            sts = sstages[k::4]
+            nb_ = sum(m[0].numel() + 4 * N * (m[3] + m[4]) for m in sts[0])
+            us = graph_ms(torch, lambda sts=sts: vstep(sts), 5) * 1e3 / len(sts)
+            per_stage[name] = {"avg_us": round(us, 3), "GBps": round(nb_ / (us * 1e-6) / 1e9, 1)}
         rows[f"smalln_verify_N{N}"] = {"ms_per_step": round(ms, 4), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
                                        "bytes": int(b), "verified_tokens_per_s": round(N * 1e3 / ms, 1),
-                                       "launches_per_step": len(flat)}
+                                       "launches_per_step": len(sstages), "per_stage": per_stage}
         log(f"row smalln N={N}: {rows[f'smalln_verify_N{N}']}")
-        del Xs, Ys
+        del sstages, flat
     return rows
 
 

@@ -123,17 +123,39 @@ int qgemv_q8_0(const void* w_packed, const float* x, float* y, int64_t M, int64_
                void* workspace, size_t workspace_bytes, qg_stream_t stream);
 
 /*
- * Small-N verify / prefill product, one pass over the weights:
+ * Small-N verify / prefill product, one pass over the weights ("Why Local LLMs
+ * Don't Need C++ or Python", section 4, batched verification; section 3, the
+ * 32-token prefill tile):
  *   Y[:, n] = W X[:, n] for 0 <= n < N, 1 <= N <= QG_SMALLN_MAX.
  * X is column-major K x N with leading dimension ldx >= K (column n starts at
  * X + n*ldx); Y is column-major M x N with ldy >= M. ldx and ldy must be
- * multiples of 4. N <= 8 runs fp32 FMA on the vector ALUs; larger N uses fp16
- * matrix-core products with fp32 accumulation.
+ * multiples of 4. Each 32-weight sub-block is a 16 x 16 x 32 fp16 matrix-core
+ * product of the activations (rounded to fp16) with the quants, accumulated and
+ * scaled in fp32. Only Y[0..M) of each column is written. No workspace.
  */
 size_t qgemm_q4k_smalln_workspace_bytes(int64_t M, int64_t K, int64_t N);
 int qgemm_q4k_smalln(const void* w_packed, const float* X, int64_t ldx, float* Y, int64_t ldy,
                      int64_t M, int64_t K, int64_t N,
                      void* workspace, size_t workspace_bytes, qg_stream_t stream);
+
+/*
+ * Several independent small-N products in one launch (the same grouping as
+ * qgemv_q4k_batch). 1 <= count <= QG_MAX_BATCH; each entry follows
+ * qgemm_q4k_smalln's rules; outputs must not overlap.
+ */
+typedef struct {
+    const void* w_packed;
+    const float* X;
+    int64_t ldx;
+    float* Y;
+    int64_t ldy;
+    int64_t M;
+    int64_t K;
+    int64_t N;
+} qg_gemm_problem;
+size_t qgemm_q4k_smalln_batch_workspace_bytes(const qg_gemm_problem* problems /* host */, int count);
+int qgemm_q4k_smalln_batch(const qg_gemm_problem* problems /* host */, int count,
+                           void* workspace, size_t workspace_bytes, qg_stream_t stream);
 
 /*
  * Fused LM head: logits = W x (W an M x K Q8_0 matrix, packed) reduced on the

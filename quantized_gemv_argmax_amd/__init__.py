@@ -33,6 +33,12 @@ class _Problem(ctypes.Structure):
                 ("M", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
+class _GemmProblem(ctypes.Structure):
+    _fields_ = [("w_packed", ctypes.c_void_p), ("X", ctypes.c_void_p), ("ldx", ctypes.c_int64),
+                ("Y", ctypes.c_void_p), ("ldy", ctypes.c_int64), ("M", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("N", ctypes.c_int64)]
+
+
 _P, _I64, _SZ, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
 
 _SIGS = {
@@ -52,6 +58,8 @@ _SIGS = {
     "qgemv_q8_0": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "qgemm_q4k_smalln_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "qgemm_q4k_smalln": (_I, [_P, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
+    "qgemm_q4k_smalln_batch_workspace_bytes": (_SZ, [ctypes.POINTER(_GemmProblem), _I]),
+    "qgemm_q4k_smalln_batch": (_I, [ctypes.POINTER(_GemmProblem), _I, _P, _SZ, _P]),
     "lmhead_argmax_workspace_bytes": (_SZ, [_I64, _I64]),
     "lmhead_argmax": (_I, [_P, _P, _I64, _I64, _P, _SZ, _P, _P, _P]),
 }
@@ -230,6 +238,25 @@ def qgemm_q4k_smalln(w: torch.Tensor, X: torch.Tensor, M: int, K: int, Y: torch.
     _check("qgemm_q4k_smalln", lib().qgemm_q4k_smalln(_ptr(w), _ptr(X), ldx, _ptr(Y), ldy, M, K, N,
                                                         ws.ptr(), ws.nbytes(), _stream(X.device)))
     return Y
+
+
+def qgemm_q4k_smalln_batch(problems, ws: Workspace | None = None):
+    """problems: list of (w_packed, X, Y, M, K) with X (N, ldx) and Y (N, ldy) as in
+    qgemm_q4k_smalln; one launch for all of them. Returns the Y tensors."""
+    arr = (_GemmProblem * len(problems))()
+    dev = None
+    for i, (w, X, Y, M, K) in enumerate(problems):
+        _need_cuda(w, X, Y)
+        dev = X.device
+        N, ldx = X.shape
+        if X.stride(1) != 1 or X.stride(0) != ldx or Y.stride(1) != 1 or Y.shape[0] != N:
+            raise ValueError("X and Y must be contiguous (N, ld) tensors with the same N")
+        arr[i] = _GemmProblem(_ptr(w), _ptr(X), ldx, _ptr(Y), Y.stride(0), M, K, N)
+    need = int(lib().qgemm_q4k_smalln_batch_workspace_bytes(arr, len(problems)))
+    ws = _ws(ws, need, dev)
+    _check("qgemm_q4k_smalln_batch",
+           lib().qgemm_q4k_smalln_batch(arr, len(problems), ws.ptr(), ws.nbytes(), _stream(dev)))
+    return [p[2] for p in problems]
 
 
 def lmhead_argmax(w: torch.Tensor, x: torch.Tensor, M: int, K: int, out_index: torch.Tensor | None = None,

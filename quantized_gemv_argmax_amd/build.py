@@ -11,11 +11,14 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqgemv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Packed-FP32 VALU instructions are disabled for all device code.
+# Packed-FP32 VALU instructions are disabled for all device code. Matrix-core
+# results go straight to VGPRs (the small-N kernel scales every product in fp32;
+# AGPR results would cost one copy instruction per element).
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -7,21 +7,33 @@
 // (section 3). Each weight byte is loaded from HBM once per call and applied to
 // all N columns.
 //
-// Both kernels read the 16-row-tile packed layout of q4k_gemv.hip and give a
-// wavefront four consecutive tiles (64 rows, lane = 16 * tile + row for the vector
-// kernel). A workgroup of W wavefronts owns those 64 rows and splits K among its
-// wavefronts; partial results meet in LDS in a fixed order.
+// Matrix-core formulation. For one 32-weight sub-block j of a 16-row tile,
+//     S_j[n][r] = sum_k x[k][n] * q[r][k]
+// is a 16 x 16 x 32 product: the A operand carries the activations of 16 columns
+// (fp16), the B operand the 4-bit quants of the 16 rows. The quants enter B
+// without any conversion: masking a dword with 0x000F000F leaves two fp16
+// subnormals q * 2^-24 (0x00F000F0: 16q * 2^-24), which the fp16 matrix cores
+// multiply exactly. A second product against an all-ones B gives the sub-block
+// sums X_j[n] of the same fp16 activations, in the same output layout. The
+// Q4_K affine form (dotLLM README, Key Features: fused scale x int dot products)
+// is then applied per sub-block in fp32:
+//     y[r][n] += 2^24 d sc_j S_j[n][r] - dmin m_j X_j[n].
+// v_mfma_f32_16x16x32_f16 lane layout: lane l holds A[l % 16][8 (l / 16) + 0..7],
+// B[8 (l / 16) + 0..7][l % 16] and D[4 (l / 16) + e][l % 16], e = 0..3; so lane
+// l loads row l % 16 of the tile (its quant bytes 8 (l / 16)..+7 of each
+// sub-block) and column l % 16 of the activations, and ends with row l % 16,
+// columns 4 (l / 16) + e.
 //
-// N <= 8: vector-ALU kernel. Every lane accumulates its own row; the activations
-// of the N columns are wavefront-uniform and arrive through scalar loads; fp32 FMA.
-// N > 8: matrix-core kernel. Lane (i = lane % 16, s = lane / 16) loads quant
-// segment 1 + 4t + s of row i of each of the four tiles, so the four lane groups
-// cover half a super-block per round t; dword u of a lane's segment (4 low-nibble
-// and 4 high-nibble weights) is that lane's 8-element K slice of MFMA step (t, u).
-// The lane dequantizes those weights to fp16 in registers (d*sc*q - dmin*m in
-// fp32, then one rounding); the B operand carries the matching 8 activations of
-// each column, converted to fp16; v_mfma_f32_16x16x32_f16 accumulates in fp32.
+// Within a lane's 8-element K slice the order is that of the masked dwords:
+// bytes 0, 2, 1, 3, 4, 6, 5, 7; the activations are packed in the same order.
+//
+// Grid: one workgroup per 16-row tile of the packed layout (q4k_gemv.hip), its W
+// wavefronts splitting K in units of 256 / C weights (C = column blocks of 16);
+// partial results meet in LDS in a fixed order, so results are deterministic. No
+// workspace, no cross-workgroup traffic. Rows past a ragged tile's end and
+// columns past N re-read the last row / column; their results are dropped.
 #include <algorithm>
+#include <climits>
 
 #include "qg_device.h"
 #include "qg_host.h"
@@ -31,6 +43,7 @@ namespace {
 constexpr int T = QG_TILE_ROWS;
 
 typedef _Float16 qg_h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 qg_h2 __attribute__((ext_vector_type(2)));
 typedef float qg_f4 __attribute__((ext_vector_type(4)));
 
 struct SnProb {
@@ -38,327 +51,198 @@ struct SnProb {
     const float* X;
     float* Y;
     int64_t ldx, ldy;
-    int32_t M, nb, N, tiles;
+    int32_t M, nb, N, tiles, wg_begin;
+};
+struct SnArgs {
+    int32_t begin[QG_MAX_BATCH];
+    int32_t count;
+    SnProb p[QG_MAX_BATCH];
 };
 
-// Row i of tile `tile_in_group` of this wavefront's 64-row tile group, clamped
-// into the matrix: returns the segment-0 pointer of super-block 0 and the segment
-// stride (rows of its tile); `active` tells whether the row exists.
-QG_DEV const uint4* row_base(const SnProb& P, int group, int tile_in_group, int i, int& stride, bool& active) {
-    const int t = 4 * group + tile_in_group;
-    const bool tile_ok = t < P.tiles;
-    const int tc = tile_ok ? t : P.tiles - 1;
-    const int rt = min(T, P.M - tc * T);
-    active = tile_ok && i < rt;
-    stride = rt;
-    return reinterpret_cast<const uint4*>(P.w + (size_t)tc * T * P.nb * 144) + min(i, rt - 1);
-}
-
-// ------------------------------------------------------------------ VALU, N <= 8
-template <int N>
-struct SbN {
-    uint4 s[9];
-    float4 xv[N];  // this lane's 4 activations of each column (sub-block sums)
+// Inputs of one unit: super-block b, sub-block pairs g0 .. g0 + U - 1 (U = 4 / C).
+template <int C>
+struct SnIn {
+    static constexpr int U = 4 / C;
+    uint4 hdr;                 // d, dmin, 12 scale bytes of this lane's row
+    uint2 q[U];                // quant bytes 8 (l / 16)..+7 of sub-blocks 2g and 2g + 1
+    float4 x[U][2][C][2];      // [pair][low / high sub-block][column block][first / second 4]
 };
 
-template <int N>
-QG_DEV void load_sbn(SbN<N>& d, const uint4* __restrict__ seg, int stride, const SnProb& P, int b, int lane) {
+template <int C>
+QG_DEV void load_w(SnIn<C>& d, const uint4* __restrict__ seg, int rt, int u, int s) {
+    constexpr int U = SnIn<C>::U;
+    const int b = u / C, g0 = (u % C) * U;
+    const uint4* sb = seg + (size_t)b * 9 * rt;
+    d.hdr = qg_stream_load(sb);
 #pragma unroll
-    for (int n = 0; n < N; ++n) d.xv[n] = *reinterpret_cast<const float4*>(P.X + n * P.ldx + 256 * b + 4 * lane);
-    const uint4* sb = seg + (size_t)b * 9 * stride;
-#pragma unroll
-    for (int s = 0; s < 9; ++s) d.s[s] = sb[s * stride];
+    for (int gi = 0; gi < U; ++gi) {
+        const uint4* sg = sb + (size_t)(1 + 2 * (g0 + gi) + (s >> 1)) * rt;
+        const uint2* p = reinterpret_cast<const uint2*>(sg) + (s & 1);
+        typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+        const u2 v = __builtin_nontemporal_load(reinterpret_cast<const u2*>(p));
+        d.q[gi] = make_uint2(v.x, v.y);
+    }
 }
 
-// Sums of x over the eight 32-element sub-blocks (lane t holds x[4t..4t+3]).
-QG_DEV void subblock_sums(const float4 xv, float (&X)[8]) {
-    float s = ((xv.x + xv.y) + xv.z) + xv.w;
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
-    s += __shfl_xor(s, 4, 64);
+// xc[c] = start of column 16 c + (l % 16) (clamped to N - 1) at this lane's K slice.
+template <int C>
+QG_DEV void load_x(SnIn<C>& d, const float* const (&xc)[C], int u) {
+    constexpr int U = SnIn<C>::U;
+    const int b = u / C, g0 = (u % C) * U;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) X[j] = qg_readlane(s, 8 * j);
-}
-
-template <int N>
-QG_DEV void sb_dot_n(float (&acc)[N], const SbN<N>& d, const SnProb& P, int b) {
-    float X[N][8];
+    for (int gi = 0; gi < U; ++gi)
 #pragma unroll
-    for (int n = 0; n < N; ++n) subblock_sums(d.xv[n], X[n]);
-    float S[8][N];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int n = 0; n < N; ++n) S[j][n] = 0.f;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int g = p >> 1, h = p & 1;
-        const uint32_t qw[4] = {d.s[1 + p].x, d.s[1 + p].y, d.s[1 + p].z, d.s[1 + p].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t l4 = qg_opaque(qw[i] & 0x0f0f0f0fu);
-            const uint32_t h4 = qg_opaque(qw[i] & 0xf0f0f0f0u);
-            const float fl[4] = {qg_ub0(l4), qg_ub1(l4), qg_ub2(l4), qg_ub3(l4)};
-            const float fh[4] = {qg_ub0(h4), qg_ub1(h4), qg_ub2(h4), qg_ub3(h4)};
-#pragma unroll
-            for (int n = 0; n < N; ++n) {
-                qg_uniform_f32 xl = (qg_uniform_f32)(P.X + n * P.ldx) + 256 * b + 64 * g + 16 * h + 4 * i;
-                qg_uniform_f32 xh = xl + 32;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    S[2 * g][n] = fmaf(fl[k], xl[k], S[2 * g][n]);
-                    S[2 * g + 1][n] = fmaf(fh[k], xh[k], S[2 * g + 1][n]);
-                }
+            for (int c = 0; c < C; ++c) {
+                const float* p = xc[c] + 256 * b + 64 * (g0 + gi) + 32 * h;
+                d.x[gi][h][c][0] = *reinterpret_cast<const float4*>(p);
+                d.x[gi][h][c][1] = *reinterpret_cast<const float4*>(p + 4);
             }
-        }
-    }
-    const uint4 hd = d.s[0];
-    const float dd = qg_half_lo(hd.x), dm = qg_half_hi(hd.x);
-    const QgScales sc = qg_q4k_scales(hd.y, hd.z, hd.w);
-    const float scf[8] = {qg_ub0(sc.sc03), qg_ub1(sc.sc03) * 0.0625f, qg_ub2(sc.sc03), qg_ub3(sc.sc03) * 0.0625f,
-                          qg_ub0(sc.sc47), qg_ub1(sc.sc47) * 0.0625f, qg_ub2(sc.sc47), qg_ub3(sc.sc47) * 0.0625f};
-    const float mf[8] = {qg_ub0(sc.m03), qg_ub1(sc.m03), qg_ub2(sc.m03), qg_ub3(sc.m03),
-                         qg_ub0(sc.m47), qg_ub1(sc.m47), qg_ub2(sc.m47), qg_ub3(sc.m47)};
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-        float t = scf[0] * S[0][n];
-        float mn = mf[0] * X[n][0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) {
-            t = fmaf(scf[j], S[j][n], t);
-            mn = fmaf(mf[j], X[n][j], mn);
-        }
-        acc[n] += fmaf(dd, t, -dm * mn);
-    }
 }
 
-template <int N, int W>
-__global__ __launch_bounds__(64 * W) void q4k_smalln_valu_kernel(SnProb P) {
-    const int group = blockIdx.x;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nb = P.nb;
-    int stride;
-    bool active;
-    const uint4* __restrict__ seg = row_base(P, group, lane >> 4, lane & 15, stride, active);
-    const int row = group * 64 + lane;  // tiles of a group are consecutive rows
-    const int wb0 = wave * nb / W, wb1 = (wave + 1) * nb / W;
-
-    float acc[N];
-#pragma unroll
-    for (int n = 0; n < N; ++n) acc[n] = 0.f;
-    if (wb0 < wb1) {
-        SbN<N> cur, nxt;
-        load_sbn<N>(cur, seg, stride, P, wb0, lane);
-        for (int b = wb0; b < wb1 - 1; ++b) {
-            load_sbn<N>(nxt, seg, stride, P, b + 1, lane);
-            sb_dot_n<N>(acc, cur, P, b);
-            cur = nxt;
-        }
-        sb_dot_n<N>(acc, cur, P, wb1 - 1);
-    }
-    if constexpr (W > 1) {
-        __shared__ float red[W][N][64];
-#pragma unroll
-        for (int n = 0; n < N; ++n) red[wave][n][lane] = acc[n];
-        __syncthreads();
-        if (wave != 0) return;
-#pragma unroll
-        for (int n = 0; n < N; ++n) {
-            float v = red[0][n][lane];
-#pragma unroll
-            for (int w = 1; w < W; ++w) v += red[w][n][lane];
-            acc[n] = v;
-        }
-    }
-    if (active)
-#pragma unroll
-        for (int n = 0; n < N; ++n) P.Y[n * P.ldy + row] = acc[n];
+QG_DEV uint32_t pk_rne(float a, float b) {
+    const qg_h2 h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
 }
 
-// ------------------------------------------------------------------ MFMA, N > 8
-QG_DEV uint32_t pk_h2(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
-}
-
-// 8 fp16 weights of one dword of quants: low nibbles (scale dsl, min dml) then
-// high nibbles (dsh already divided by 16, min dmh).
-QG_DEV qg_h8 dequant8(uint32_t w, float dsl, float dml, float dsh, float dmh) {
-    const uint32_t l4 = qg_opaque(w & 0x0f0f0f0fu);
-    const uint32_t h4 = qg_opaque(w & 0xf0f0f0f0u);
+// Eight activations in the masked-dword order 0, 2, 1, 3, 4, 6, 5, 7, as fp16.
+QG_DEV qg_h8 a_operand(const float4 lo, const float4 hi) {
     uint4 r;
-    r.x = pk_h2(fmaf(qg_ub0(l4), dsl, -dml), fmaf(qg_ub1(l4), dsl, -dml));
-    r.y = pk_h2(fmaf(qg_ub2(l4), dsl, -dml), fmaf(qg_ub3(l4), dsl, -dml));
-    r.z = pk_h2(fmaf(qg_ub0(h4), dsh, -dmh), fmaf(qg_ub1(h4), dsh, -dmh));
-    r.w = pk_h2(fmaf(qg_ub2(h4), dsh, -dmh), fmaf(qg_ub3(h4), dsh, -dmh));
+    r.x = pk_rne(lo.x, lo.z);
+    r.y = pk_rne(lo.y, lo.w);
+    r.z = pk_rne(hi.x, hi.z);
+    r.w = pk_rne(hi.y, hi.w);
     return __builtin_bit_cast(qg_h8, r);
 }
 
-QG_DEV qg_h8 to_h8(const float4 a, const float4 b) {
-    uint4 r;
-    r.x = pk_h2(a.x, a.y);
-    r.y = pk_h2(a.z, a.w);
-    r.z = pk_h2(b.x, b.y);
-    r.w = pk_h2(b.z, b.w);
-    return __builtin_bit_cast(qg_h8, r);
-}
-
-struct MfW {
-    uint4 hdr[4];
-    uint4 q[2][4];  // [round t][tile r]
-};
-
-QG_DEV void load_mfw(MfW& d, const uint4* const (&base)[4], const int (&stride)[4], int b, int s) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) d.hdr[r] = base[r][(size_t)b * 9 * stride[r]];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) d.q[t][r] = base[r][((size_t)b * 9 + 1 + 4 * t + s) * stride[r]];
-}
-
-// Activations of one round of a super-block for column block c: 4 steps u, each
-// a low and a high float4 (k0 = first low-nibble position of this lane group).
-template <int C>
-QG_DEV void load_x(float4 (&xs)[C][4][2], const float* const (&xcol)[C], int64_t k0) {
-#pragma unroll
-    for (int c = 0; c < C; ++c)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            xs[c][u][0] = *reinterpret_cast<const float4*>(xcol[c] + k0 + 4 * u);
-            xs[c][u][1] = *reinterpret_cast<const float4*>(xcol[c] + k0 + 4 * u + 32);
-        }
-}
+// Byte k of a packed word, as float.
+QG_DEV float byte_f(uint32_t v, int k) { return (float)((v >> (8 * k)) & 0xffu); }
 
 template <int C>
-QG_DEV void mfma_round(qg_f4 (&D)[4][C], const MfW& d, const float4 (&xs)[C][4][2], const float (&cmask)[C], int t,
-                       int s) {
-    float dsl[4], dml[4], dsh[4], dmh[4];
+QG_DEV void unit_dot(qg_f4 (&acc)[C], const SnIn<C>& d, int u) {
+    constexpr int U = SnIn<C>::U;
+    const int g0 = (u % C) * U;
+    const float dd = qg_half_lo(d.hdr.x) * 16777216.0f;  // quants enter as q * 2^-24
+    const float dm = qg_half_hi(d.hdr.x);
+    const QgScales sc = qg_q4k_scales(d.hdr.y, d.hdr.z, d.hdr.w);
+    const qg_h8 ones = __builtin_bit_cast(qg_h8, make_uint4(0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u));
+    const qg_f4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float dd = qg_half_lo(d.hdr[r].x), dm = qg_half_hi(d.hdr[r].x);
-        const QgScales sc = qg_q4k_scales(d.hdr[r].y, d.hdr[r].z, d.hdr[r].w);
-        const int sh = 16 * (s >> 1);  // byte pair (2g, 2g+1) within the word
-        const uint32_t scw = (t == 0 ? sc.sc03 : sc.sc47) >> sh;
-        const uint32_t mw = (t == 0 ? sc.m03 : sc.m47) >> sh;
-        dsl[r] = dd * qg_ub0(scw);
-        dsh[r] = dd * qg_ub1(scw) * 0.0625f;
-        dml[r] = dm * qg_ub0(mw);
-        dmh[r] = dm * qg_ub1(mw);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        qg_h8 B[C];
+    for (int gi = 0; gi < U; ++gi) {
+        const int g = g0 + gi;  // sub-blocks 2g (low nibbles) and 2g + 1 (high nibbles)
+        const uint32_t scw = (g < 2) ? sc.sc03 : sc.sc47;
+        const uint32_t mw = (g < 2) ? sc.m03 : sc.m47;
+        const int kb = 2 * (g & 1);
+        const float s_lo = dd * byte_f(scw, kb);
+        const float s_hi = dd * 0.0625f * byte_f(scw, kb + 1);
+        const float m_lo = dm * byte_f(mw, kb);
+        const float m_hi = dm * byte_f(mw, kb + 1);
+
+        const uint32_t w0 = d.q[gi].x, w1 = d.q[gi].y;
+        const uint32_t w0s = w0 >> 8, w1s = w1 >> 8;
+        const qg_h8 b_lo = __builtin_bit_cast(
+            qg_h8, make_uint4(w0 & 0x000f000fu, w0s & 0x000f000fu, w1 & 0x000f000fu, w1s & 0x000f000fu));
+        const qg_h8 b_hi = __builtin_bit_cast(
+            qg_h8, make_uint4(w0 & 0x00f000f0u, w0s & 0x00f000f0u, w1 & 0x00f000f0u, w1s & 0x00f000f0u));
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const float m = cmask[c];
-            const float4 lo = make_float4(xs[c][u][0].x * m, xs[c][u][0].y * m, xs[c][u][0].z * m, xs[c][u][0].w * m);
-            const float4 hi = make_float4(xs[c][u][1].x * m, xs[c][u][1].y * m, xs[c][u][1].z * m, xs[c][u][1].w * m);
-            B[c] = to_h8(lo, hi);
-        }
+            const qg_h8 a_lo = a_operand(d.x[gi][0][c][0], d.x[gi][0][c][1]);
+            const qg_h8 a_hi = a_operand(d.x[gi][1][c][0], d.x[gi][1][c][1]);
+            const qg_f4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, zero, 0, 0, 0);
+            const qg_f4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, zero, 0, 0, 0);
+            const qg_f4 x0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, ones, zero, 0, 0, 0);
+            const qg_f4 x1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, ones, zero, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t qu = (&d.q[t][r].x)[u];
-            const qg_h8 A = dequant8(qu, dsl[r], dml[r], dsh[r], dmh[r]);
-#pragma unroll
-            for (int c = 0; c < C; ++c) D[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[c], D[r][c], 0, 0, 0);
+            for (int e = 0; e < 4; ++e) {
+                float v = acc[c][e];
+                v = fmaf(s_lo, s0[e], v);
+                v = fmaf(s_hi, s1[e], v);
+                v = fmaf(-m_lo, x0[e], v);
+                v = fmaf(-m_hi, x1[e], v);
+                acc[c][e] = v;
+            }
         }
     }
 }
 
 template <int C, int W>
-__global__ __launch_bounds__(64 * W) void q4k_smalln_mfma_kernel(SnProb P) {
-    const int group = blockIdx.x;
+__global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
+    const int wg = blockIdx.x;
+    int k = 0;
+#pragma unroll
+    for (int i = 1; i < QG_MAX_BATCH; ++i)
+        if (i < a.count && wg >= a.begin[i]) k = i;
+    const SnProb P = a.p[k];
+
+    const int tile = wg - P.wg_begin;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15, s = lane >> 4;
-    const int nb = P.nb;
-    const int wb0 = wave * nb / W, wb1 = (wave + 1) * nb / W;
+    const int rt = min(T, P.M - tile * T);
+    const uint4* __restrict__ seg =
+        reinterpret_cast<const uint4*>(P.w + (size_t)tile * T * P.nb * 144) + min(i, rt - 1);
+    const float* xc[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) xc[c] = P.X + (int64_t)min(16 * c + i, P.N - 1) * P.ldx + 8 * s;
 
-    const uint4* base[4];
-    int stride[4];
+    const int units = P.nb * C;
+    const int niter = (units - wave + W - 1) / W;  // units wave, wave + W, ...
+    qg_f4 acc[C];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        bool act;
-        base[r] = row_base(P, group, r, i, stride[r], act);
-    }
-    const float* xcol[C];
-    float cmask[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-        const int n = 16 * c + i;
-        cmask[c] = n < P.N ? 1.f : 0.f;
-        xcol[c] = P.X + (int64_t)(n < P.N ? n : 0) * P.ldx;
-    }
+    for (int c = 0; c < C; ++c) acc[c] = qg_f4{0.f, 0.f, 0.f, 0.f};
 
-    qg_f4 D[4][C];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < C; ++c) D[r][c] = qg_f4{0.f, 0.f, 0.f, 0.f};
-
-    if (wb0 < wb1) {
-        MfW cur, nxt;
-        load_mfw(cur, base, stride, wb0, s);
-        for (int b = wb0; b < wb1; ++b) {
-            float4 xs[C][4][2];
-            const int64_t k0 = 256 * (int64_t)b + 64 * (s >> 1) + 16 * (s & 1);
-            // activations before the prefetch, so waiting for them never waits for it
-            load_x<C>(xs, xcol, k0);
-            mfma_round<C>(D, cur, xs, cmask, 0, s);
-            load_x<C>(xs, xcol, k0 + 128);
-            load_mfw(nxt, base, stride, min(b + 1, wb1 - 1), s);
-            mfma_round<C>(D, cur, xs, cmask, 1, s);
-            cur = nxt;
+    if (niter > 0) {
+        // ping-pong: the weight loads of the next unit are in flight while this one
+        // is computed; activations (L2-resident) are loaded at the top of their own
+        // iteration, before the next unit's weights, so waiting for them never waits
+        // for those weights
+        SnIn<C> b0, b1;
+        load_w<C>(b0, seg, rt, wave, s);
+        for (int it = 0;; it += 2) {
+            const int u0 = wave + W * it;
+            load_x<C>(b0, xc, u0);
+            if (it + 1 < niter) load_w<C>(b1, seg, rt, u0 + W, s);
+            unit_dot<C>(acc, b0, u0);
+            if (it + 1 >= niter) break;
+            load_x<C>(b1, xc, u0 + W);
+            if (it + 2 < niter) load_w<C>(b0, seg, rt, u0 + 2 * W, s);
+            unit_dot<C>(acc, b1, u0 + W);
+            if (it + 2 >= niter) break;
         }
     }
 
-    // D[r][c] element e of lane (i, s): row 16r + 4s + e of the group, column 16c + i.
     if constexpr (W > 1) {
-        __shared__ float red[W][4][C][4][64];
+        __shared__ float red[W][C * 4][64];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int c = 0; c < C; ++c)
 #pragma unroll
-            for (int c = 0; c < C; ++c)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) red[wave][r][c][e][lane] = D[r][c][e];
+            for (int e = 0; e < 4; ++e) red[wave][4 * c + e][lane] = acc[c][e];
         __syncthreads();
         if (wave != 0) return;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float v = red[0][r][c][e][lane];
-#pragma unroll
-                    for (int w = 1; w < W; ++w) v += red[w][r][c][e][lane];
-                    D[r][c][e] = v;
-                }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int c = 0; c < C; ++c)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int row = group * 64 + 16 * r + 4 * s + e;
-                const int n = 16 * c + i;
-                if (row < P.M && n < P.N) P.Y[(int64_t)n * P.ldy + row] = D[r][c][e];
+                float v = red[0][4 * c + e][lane];
+#pragma unroll
+                for (int w = 1; w < W; ++w) v += red[w][4 * c + e][lane];
+                acc[c][e] = v;
             }
+    }
+    if (i < rt) {
+        const int row = tile * T + i;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int n = 16 * c + 4 * s + e;
+                if (n < P.N) P.Y[(int64_t)n * P.ldy + row] = acc[c][e];
+            }
+    }
 }
 
 // ------------------------------------------------------------------ host side
-int choose_w(const SnProb& P, bool mfma) {
-    const int64_t groups = qg::ceil_div(P.M, 64);
-    int W = 1;
-    while (W < 8 && groups * W < 1024 && 2 * W <= P.nb) W *= 2;
-    int ew = 0, eu = 0;
-    if (qg::env_pair(mfma ? "QG_SNM_CFG" : "QG_SNV_CFG", &ew, &eu) && (ew == 1 || ew == 2 || ew == 4 || ew == 8)) W = ew;
-    if (mfma && W > 4) W = 4;
-    return W;
-}
-
 int sn_validate(const void* w, const float* X, int64_t ldx, const float* Y, int64_t ldy, int64_t M, int64_t K,
                 int64_t N) {
     if (!w || !X || !Y) return qg::fail(QG_ERR_NULL, "NULL pointer");
@@ -388,25 +272,55 @@ SnProb make_sn(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy
     return P;
 }
 
-template <int N>
-void launch_valu(const SnProb& P, int W, hipStream_t s) {
-    const dim3 grid((unsigned)qg::ceil_div(P.M, 64));
-    switch (W) {
-        case 1: hipLaunchKernelGGL((q4k_smalln_valu_kernel<N, 1>), grid, dim3(64), 0, s, P); break;
-        case 2: hipLaunchKernelGGL((q4k_smalln_valu_kernel<N, 2>), grid, dim3(128), 0, s, P); break;
-        case 4: hipLaunchKernelGGL((q4k_smalln_valu_kernel<N, 4>), grid, dim3(256), 0, s, P); break;
-        default: hipLaunchKernelGGL((q4k_smalln_valu_kernel<N, 8>), grid, dim3(512), 0, s, P); break;
-    }
+// Wavefronts per workgroup: enough K units per wavefront to pipeline, at most 8.
+int choose_w(const SnArgs& a, int C) {
+    int units = INT_MAX;
+    for (int i = 0; i < a.count; ++i) units = std::min(units, a.p[i].nb * C);
+    int W = 1;
+    while (W < 4 && 2 * W <= units) W *= 2;
+    int ew = 0, eu = 0;
+    if (qg::env_pair("QG_SN_CFG", &ew, &eu) && (ew == 1 || ew == 2 || ew == 4 || ew == 8)) W = ew;
+    return W;
 }
 
 template <int C>
-void launch_mfma(const SnProb& P, int W, hipStream_t s) {
-    const dim3 grid((unsigned)qg::ceil_div(P.M, 64));
+void launch(const SnArgs& a, int grid, int W, hipStream_t s) {
     switch (W) {
-        case 1: hipLaunchKernelGGL((q4k_smalln_mfma_kernel<C, 1>), grid, dim3(64), 0, s, P); break;
-        case 2: hipLaunchKernelGGL((q4k_smalln_mfma_kernel<C, 2>), grid, dim3(128), 0, s, P); break;
-        default: hipLaunchKernelGGL((q4k_smalln_mfma_kernel<C, 4>), grid, dim3(256), 0, s, P); break;
+        case 1: hipLaunchKernelGGL((q4k_smalln_kernel<C, 1>), dim3(grid), dim3(64), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((q4k_smalln_kernel<C, 2>), dim3(grid), dim3(128), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((q4k_smalln_kernel<C, 4>), dim3(grid), dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((q4k_smalln_kernel<C, 8>), dim3(grid), dim3(512), 0, s, a); break;
     }
+}
+
+int run(const qg_gemm_problem* probs, int count, hipStream_t stream) {
+    if (!probs) return qg::fail(QG_ERR_NULL, "NULL problem list");
+    if (count < 1 || count > QG_MAX_BATCH)
+        return qg::fail(QG_ERR_SHAPE, "count=%d not in [1, %d]", count, QG_MAX_BATCH);
+    SnArgs a{};
+    a.count = count;
+    int64_t wgs = 0;
+    int nmax = 0;
+    for (int i = 0; i < count; ++i) {
+        const qg_gemm_problem& q = probs[i];
+        int st = sn_validate(q.w_packed, q.X, q.ldx, q.Y, q.ldy, q.M, q.K, q.N);
+        if (st) return st;
+        a.p[i] = make_sn(q.w_packed, q.X, q.ldx, q.Y, q.ldy, q.M, q.K, q.N);
+        a.p[i].wg_begin = (int32_t)wgs;
+        a.begin[i] = (int32_t)wgs;
+        wgs += a.p[i].tiles;
+        nmax = std::max(nmax, a.p[i].N);
+    }
+    if (wgs > INT32_MAX) return qg::fail(QG_ERR_SHAPE, "too many tiles in one batch");
+    int st = qg::check_device();
+    if (st) return st;
+    const int C = nmax > 16 ? 2 : 1;
+    const int W = choose_w(a, C);
+    if (C == 1)
+        launch<1>(a, (int)wgs, W, stream);
+    else
+        launch<2>(a, (int)wgs, W, stream);
+    return qg::launch_status("qgemm_q4k_smalln");
 }
 
 }  // namespace
@@ -425,31 +339,22 @@ int qgemm_q4k_smalln(const void* w, const float* X, int64_t ldx, float* Y, int64
     (void)ws;
     (void)ws_bytes;
     qg::clear_error();
-    int st = sn_validate(w, X, ldx, Y, ldy, M, K, N);
-    if (st) return st;
-    SnProb P = make_sn(w, X, ldx, Y, ldy, M, K, N);
-    st = qg::check_device();
-    if (st) return st;
-    hipStream_t s = (hipStream_t)stream;
-    const bool mfma = P.N > 8;
-    const int W = choose_w(P, mfma);
-    switch (P.N) {
-        case 1: launch_valu<1>(P, W, s); break;
-        case 2: launch_valu<2>(P, W, s); break;
-        case 3: launch_valu<3>(P, W, s); break;
-        case 4: launch_valu<4>(P, W, s); break;
-        case 5: launch_valu<5>(P, W, s); break;
-        case 6: launch_valu<6>(P, W, s); break;
-        case 7: launch_valu<7>(P, W, s); break;
-        case 8: launch_valu<8>(P, W, s); break;
-        default:
-            if (P.N <= 16)
-                launch_mfma<1>(P, W, s);
-            else
-                launch_mfma<2>(P, W, s);
-            break;
-    }
-    return qg::launch_status("qgemm_q4k_smalln");
+    const qg_gemm_problem p{w, X, ldx, Y, ldy, M, K, N};
+    return run(&p, 1, (hipStream_t)stream);
+}
+
+size_t qgemm_q4k_smalln_batch_workspace_bytes(const qg_gemm_problem* problems, int count) {
+    (void)problems;
+    (void)count;
+    return 0;
+}
+
+int qgemm_q4k_smalln_batch(const qg_gemm_problem* problems, int count, void* ws, size_t ws_bytes,
+                           qg_stream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    qg::clear_error();
+    return run(problems, count, (hipStream_t)stream);
 }
 
 }  // extern "C"

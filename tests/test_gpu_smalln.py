@@ -70,3 +70,23 @@ def test_padded_leading_dimensions():
     Yr, Ar = oracle.gemm_q4k(W, M, K, X)
     for n in range(N):
         assert_within(Y[n, :M], Yr[n], Ar[n], f"padded col {n}")
+
+
+def test_batch_mixed_problems():
+    # the attention-input stage with N=5, plus ragged problems with other N in the
+    # same launch (the launch uses the widest column count of the batch)
+    shapes = [(3584, 3584, 5), (512, 3584, 5), (512, 3584, 5), (77, 768, 3), (33, 512, 17)]
+    probs, refs = [], []
+    for i, (M, K, N) in enumerate(shapes):
+        W = workloads.q4k_blocks(M, K, key=(33, i))
+        X = workloads.x_columns(K, N, key=(33, i))
+        Y = torch.full((N, (M + 3) // 4 * 4), float("nan"), device="cuda:0")
+        probs.append((packed_q4k(W, M, K), to_dev(X), Y, M, K))
+        refs.append(oracle.gemm_q4k(W, M, K, X, rows=np.arange(0, M, 5)))
+    case("qgemm_q4k_smalln_batch mixed")
+    qg.qgemm_q4k_smalln_batch(probs)
+    torch.cuda.synchronize()
+    for (w, X, Y, M, K), (Yr, Ar) in zip(probs, refs):
+        Yc = Y.cpu().numpy()[:, :M][:, ::5]
+        for n in range(X.shape[0]):
+            assert_within(Yc[n], Yr[n], Ar[n], f"batch M={M} K={K} col {n}")
