@@ -180,21 +180,29 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(Q4Args a) {
             acc += (kg + G * it < nb) ? v0 : 0.f;
         }
     } else {
-    const int niter = (nb + G - 1) / G;
-    // ping-pong between two register buffers: the loads of one super-block stay in
-    // flight while the other is computed, with no register copies in between
-    SbIn b0, b1;
-    load_sb(b0, seg, xk, min(kg, nb - 1), rt);
-    for (int it = 0;; it += 2) {
-        if (it + 1 < niter) load_sb(b1, seg, xk, min(kg + G * (it + 1), nb - 1), rt);
-        const float v0 = sb_dot(b0);
-        acc += (kg + G * it < nb) ? v0 : 0.f;
-        if (it + 1 >= niter) break;
-        if (it + 2 < niter) load_sb(b0, seg, xk, min(kg + G * (it + 2), nb - 1), rt);
-        const float v1 = sb_dot(b1);
-        acc += (kg + G * (it + 1) < nb) ? v1 : 0.f;
-        if (it + 2 >= niter) break;
-    }
+        const int niter = (nb + G - 1) / G;
+        // Ping-pong between two register buffers over pairs of super-blocks: the
+        // loads of one stay in flight while the other is computed. The loads are
+        // unconditional (the index is clamped to the last super-block) and the pair
+        // loop has a single exit, so the loop-carried load state, and with it every
+        // wait count, is exact: waiting for one super-block never waits for the next.
+        SbIn b0, b1;
+        load_sb(b0, seg, xk, min(kg, nb - 1), rt);
+        int it = 0;
+        for (; it + 2 <= niter; it += 2) {
+            load_sb(b1, seg, xk, min(kg + G * (it + 1), nb - 1), rt);
+            __builtin_amdgcn_sched_barrier(0);  // issue the loads before any wait
+            const float v0 = sb_dot(b0);
+            acc += (kg + G * it < nb) ? v0 : 0.f;
+            load_sb(b0, seg, xk, min(kg + G * (it + 2), nb - 1), rt);
+            __builtin_amdgcn_sched_barrier(0);
+            const float v1 = sb_dot(b1);
+            acc += (kg + G * (it + 1) < nb) ? v1 : 0.f;
+        }
+        if (it < niter) {
+            const float v0 = sb_dot(b0);
+            acc += (kg + G * it < nb) ? v0 : 0.f;
+        }
     }
 
     float v = qg_sum_rows4(acc);

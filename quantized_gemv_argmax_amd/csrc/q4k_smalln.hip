@@ -27,11 +27,13 @@
 // Within a lane's 8-element K slice the order is that of the masked dwords:
 // bytes 0, 2, 1, 3, 4, 6, 5, 7; the activations are packed in the same order.
 //
-// Grid: one workgroup per 16-row tile of the packed layout (q4k_gemv.hip), its W
-// wavefronts splitting K in units of 256 / C weights (C = column blocks of 16);
-// partial results meet in LDS in a fixed order, so results are deterministic. No
-// workspace, no cross-workgroup traffic. Rows past a ragged tile's end and
-// columns past N re-read the last row / column; their results are dropped.
+// Grid: one workgroup per TW consecutive 16-row tiles of the packed layout
+// (q4k_gemv.hip); its W wavefronts split K in units of 64 weights (two
+// sub-blocks), each wavefront applying one unit's activations to all TW tiles.
+// Partial results meet in LDS in a fixed order, so results are deterministic. No
+// workspace, no cross-workgroup traffic. Rows past a ragged tile's end and tiles
+// past the matrix end re-read the last row / tile, columns past N read zeros;
+// their results are dropped.
 #include <algorithm>
 #include <climits>
 
@@ -59,46 +61,63 @@ struct SnArgs {
     SnProb p[QG_MAX_BATCH];
 };
 
-// Inputs of one unit: super-block b, sub-block pairs g0 .. g0 + U - 1 (U = 4 / C).
-template <int C>
+// Inputs of one unit: sub-blocks 2g and 2g + 1 of super-block b (u = 4 b + g) of
+// TW consecutive tiles.
+template <int C, int TW>
 struct SnIn {
-    static constexpr int U = 4 / C;
-    uint4 hdr;                 // d, dmin, 12 scale bytes of this lane's row
-    uint2 q[U];                // quant bytes 8 (l / 16)..+7 of sub-blocks 2g and 2g + 1
-    float4 x[U][2][C][2];      // [pair][low / high sub-block][column block][first / second 4]
+    uint4 hdr[TW];        // d, dmin, 12 scale bytes of this lane's row in each tile
+    uint2 q[TW];          // quant bytes 8 (l / 16)..+7 of sub-blocks 2g and 2g + 1
+    float4 x[2][C][2];    // [low / high sub-block][column block][first / second 4]
 };
 
-template <int C>
-QG_DEV void load_w(SnIn<C>& d, const uint4* __restrict__ seg, int rt, int u, int s) {
-    constexpr int U = SnIn<C>::U;
-    const int b = u / C, g0 = (u % C) * U;
-    const uint4* sb = seg + (size_t)b * 9 * rt;
-    d.hdr = qg_stream_load(sb);
+// All loads are raw buffer loads: a wavefront-uniform resource and unit offset
+// (scalar registers) plus a fixed per-lane offset, so no vector instruction
+// computes an address inside the K loop. Activation lanes of columns past N get
+// an offset beyond the resource's range: the hardware returns zeros for them
+// without a memory access (their products land in output columns that are not
+// stored).
+typedef unsigned int qg_u4v __attribute__((ext_vector_type(4)));
+typedef unsigned int qg_u2v __attribute__((ext_vector_type(2)));
+constexpr uint32_t kOutOfRange = 0x80000000u;  // >= every resource size used here
+constexpr int kNonTemporal = 2;                 // buffer-load cache policy: nt
+
+struct SnLane {
+    uint32_t hdr[2], q[2];   // per tile: byte offset of this lane's header / quant bytes
+    uint32_t x[2];           // per column block: byte offset of this lane's activations
+};
+
+template <int TW>
+struct SnTiles {
+    __amdgpu_buffer_rsrc_t w[TW];  // one tile each
+    int32_t rt[TW];                // rows of the tile
+};
+
+template <int C, int TW>
+QG_DEV void load_w(SnIn<C, TW>& d, const SnTiles<TW>& tl, const SnLane& ln, int u) {
+    const int b = u >> 2, g = u & 3;
 #pragma unroll
-    for (int gi = 0; gi < U; ++gi) {
-        const uint4* sg = sb + (size_t)(1 + 2 * (g0 + gi) + (s >> 1)) * rt;
-        const uint2* p = reinterpret_cast<const uint2*>(sg) + (s & 1);
-        typedef unsigned int u2 __attribute__((ext_vector_type(2)));
-        const u2 v = __builtin_nontemporal_load(reinterpret_cast<const u2*>(p));
-        d.q[gi] = make_uint2(v.x, v.y);
+    for (int t = 0; t < TW; ++t) {
+        const int sb = b * 9 * 16 * tl.rt[t];
+        const qg_u4v h = __builtin_amdgcn_raw_buffer_load_b128(tl.w[t], ln.hdr[t], sb, kNonTemporal);
+        d.hdr[t] = make_uint4(h.x, h.y, h.z, h.w);
+        const qg_u2v q = __builtin_amdgcn_raw_buffer_load_b64(tl.w[t], ln.q[t], sb + (1 + 2 * g) * 16 * tl.rt[t],
+                                                              kNonTemporal);
+        d.q[t] = make_uint2(q.x, q.y);
     }
 }
 
-// xc[c] = start of column 16 c + (l % 16) (clamped to N - 1) at this lane's K slice.
-template <int C>
-QG_DEV void load_x(SnIn<C>& d, const float* const (&xc)[C], int u) {
-    constexpr int U = SnIn<C>::U;
-    const int b = u / C, g0 = (u % C) * U;
+template <int C, int TW>
+QG_DEV void load_x(SnIn<C, TW>& d, __amdgpu_buffer_rsrc_t xr, const SnLane& ln, int u) {
 #pragma unroll
-    for (int gi = 0; gi < U; ++gi)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                const float* p = xc[c] + 256 * b + 64 * (g0 + gi) + 32 * h;
-                d.x[gi][h][c][0] = *reinterpret_cast<const float4*>(p);
-                d.x[gi][h][c][1] = *reinterpret_cast<const float4*>(p + 4);
-            }
+        for (int c = 0; c < C; ++c) {
+            const int so = u * 256 + 128 * h;
+            const qg_u4v v0 = __builtin_amdgcn_raw_buffer_load_b128(xr, ln.x[c], so, 0);
+            const qg_u4v v1 = __builtin_amdgcn_raw_buffer_load_b128(xr, ln.x[c], so + 16, 0);
+            d.x[h][c][0] = __builtin_bit_cast(float4, v0);
+            d.x[h][c][1] = __builtin_bit_cast(float4, v1);
+        }
 }
 
 QG_DEV uint32_t pk_rne(float a, float b) {
@@ -119,27 +138,40 @@ QG_DEV qg_h8 a_operand(const float4 lo, const float4 hi) {
 // Byte k of a packed word, as float.
 QG_DEV float byte_f(uint32_t v, int k) { return (float)((v >> (8 * k)) & 0xffu); }
 
-template <int C>
-QG_DEV void unit_dot(qg_f4 (&acc)[C], const SnIn<C>& d, int u) {
-    constexpr int U = SnIn<C>::U;
-    const int g0 = (u % C) * U;
-    const float dd = qg_half_lo(d.hdr.x) * 16777216.0f;  // quants enter as q * 2^-24
-    const float dm = qg_half_hi(d.hdr.x);
-    const QgScales sc = qg_q4k_scales(d.hdr.y, d.hdr.z, d.hdr.w);
+template <int C, int TW>
+QG_DEV void unit_dot(qg_f4 (&acc)[TW][C], const SnIn<C, TW>& d, int u) {
+    const int g = u & 3;  // sub-blocks 2g (low nibbles) and 2g + 1 (high nibbles)
     const qg_h8 ones = __builtin_bit_cast(qg_h8, make_uint4(0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u));
     const qg_f4 zero = {0.f, 0.f, 0.f, 0.f};
+    // activations and their sub-block sums, shared by the TW tiles
+    qg_h8 a_lo[C], a_hi[C];
+    qg_f4 x_lo[C], x_hi[C];
 #pragma unroll
-    for (int gi = 0; gi < U; ++gi) {
-        const int g = g0 + gi;  // sub-blocks 2g (low nibbles) and 2g + 1 (high nibbles)
-        const uint32_t scw = (g < 2) ? sc.sc03 : sc.sc47;
-        const uint32_t mw = (g < 2) ? sc.m03 : sc.m47;
+    for (int c = 0; c < C; ++c) {
+        a_lo[c] = a_operand(d.x[0][c][0], d.x[0][c][1]);
+        a_hi[c] = a_operand(d.x[1][c][0], d.x[1][c][1]);
+        x_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[c], ones, zero, 0, 0, 0);
+        x_hi[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[c], ones, zero, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+        const uint4 hd = d.hdr[t];
+        const float dd = qg_half_lo(hd.x) * 16777216.0f;  // quants enter as q * 2^-24
+        const float dm = qg_half_hi(hd.x);
+        // 6-bit scale and min of sub-blocks 2g, 2g + 1 (both forms computed and
+        // selected, so that no branch splits the wait counts)
+        const uint32_t sc03 = hd.y & 0x3f3f3f3fu, m03 = hd.z & 0x3f3f3f3fu;
+        const uint32_t sc47 = (hd.w & 0x0f0f0f0fu) | ((hd.y >> 2) & 0x30303030u);
+        const uint32_t m47 = ((hd.w >> 4) & 0x0f0f0f0fu) | ((hd.z >> 2) & 0x30303030u);
+        const uint32_t scw = qg_opaque(g < 2 ? sc03 : sc47);
+        const uint32_t mw = qg_opaque(g < 2 ? m03 : m47);
         const int kb = 2 * (g & 1);
         const float s_lo = dd * byte_f(scw, kb);
         const float s_hi = dd * 0.0625f * byte_f(scw, kb + 1);
         const float m_lo = dm * byte_f(mw, kb);
         const float m_hi = dm * byte_f(mw, kb + 1);
 
-        const uint32_t w0 = d.q[gi].x, w1 = d.q[gi].y;
+        const uint32_t w0 = d.q[t].x, w1 = d.q[t].y;
         const uint32_t w0s = w0 >> 8, w1s = w1 >> 8;
         const qg_h8 b_lo = __builtin_bit_cast(
             qg_h8, make_uint4(w0 & 0x000f000fu, w0s & 0x000f000fu, w1 & 0x000f000fu, w1s & 0x000f000fu));
@@ -147,26 +179,22 @@ QG_DEV void unit_dot(qg_f4 (&acc)[C], const SnIn<C>& d, int u) {
             qg_h8, make_uint4(w0 & 0x00f000f0u, w0s & 0x00f000f0u, w1 & 0x00f000f0u, w1s & 0x00f000f0u));
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const qg_h8 a_lo = a_operand(d.x[gi][0][c][0], d.x[gi][0][c][1]);
-            const qg_h8 a_hi = a_operand(d.x[gi][1][c][0], d.x[gi][1][c][1]);
-            const qg_f4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, zero, 0, 0, 0);
-            const qg_f4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, zero, 0, 0, 0);
-            const qg_f4 x0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, ones, zero, 0, 0, 0);
-            const qg_f4 x1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, ones, zero, 0, 0, 0);
+            const qg_f4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[c], b_lo, zero, 0, 0, 0);
+            const qg_f4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[c], b_hi, zero, 0, 0, 0);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float v = acc[c][e];
+                float v = acc[t][c][e];
                 v = fmaf(s_lo, s0[e], v);
                 v = fmaf(s_hi, s1[e], v);
-                v = fmaf(-m_lo, x0[e], v);
-                v = fmaf(-m_hi, x1[e], v);
-                acc[c][e] = v;
+                v = fmaf(-m_lo, x_lo[c][e], v);
+                v = fmaf(-m_hi, x_hi[c][e], v);
+                acc[t][c][e] = v;
             }
         }
     }
 }
 
-template <int C, int W>
+template <int C, int TW, int W>
 __global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
     const int wg = blockIdx.x;
     int k = 0;
@@ -175,70 +203,99 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
         if (i < a.count && wg >= a.begin[i]) k = i;
     const SnProb P = a.p[k];
 
-    const int tile = wg - P.wg_begin;
+    const int tile0 = (wg - P.wg_begin) * TW;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15, s = lane >> 4;
-    const int rt = min(T, P.M - tile * T);
-    const uint4* __restrict__ seg =
-        reinterpret_cast<const uint4*>(P.w + (size_t)tile * T * P.nb * 144) + min(i, rt - 1);
-    const float* xc[C];
+    SnTiles<TW> tl;
+    SnLane ln;
 #pragma unroll
-    for (int c = 0; c < C; ++c) xc[c] = P.X + (int64_t)min(16 * c + i, P.N - 1) * P.ldx + 8 * s;
-
-    const int units = P.nb * C;
+    for (int t = 0; t < TW; ++t) {
+        // a tile past the matrix end (TW > 1, ragged tile count) re-reads the last tile
+        const int tc = min(tile0 + t, P.tiles - 1);
+        tl.rt[t] = min(T, P.M - tc * T);
+        tl.w[t] = __builtin_amdgcn_make_buffer_rsrc((void*)(P.w + (size_t)tc * T * P.nb * 144), (short)0,
+                                                    tl.rt[t] * P.nb * 144, 0x00020000);
+        const uint32_t r = (uint32_t)min(i, tl.rt[t] - 1);
+        ln.hdr[t] = 16 * r;
+        ln.q[t] = 16 * r + 8 * (s & 1) + (uint32_t)(s >> 1) * 16 * tl.rt[t];
+    }
+    // activations: column n = 16 c + i of X, this lane's 8-element K slice
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)P.X, (short)0, (int)(((int64_t)(P.N - 1) * P.ldx + (int64_t)P.nb * 256) * 4), 0x00020000);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int n = 16 * c + i;
+        ln.x[c] = n < P.N ? (uint32_t)(((int64_t)n * P.ldx + 8 * s) * 4) : kOutOfRange;
+    }
+    const int units = P.nb * 4;
     const int niter = (units - wave + W - 1) / W;  // units wave, wave + W, ...
-    qg_f4 acc[C];
+    qg_f4 acc[TW][C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) acc[c] = qg_f4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[t][c] = qg_f4{0.f, 0.f, 0.f, 0.f};
 
+    // Ping-pong over pairs of units: the inputs of the next unit are in flight
+    // while one is computed (activations first, so waiting for one unit's inputs
+    // never waits for the next unit's). The loads are unconditional (the unit index
+    // is clamped to the wavefront's last unit) and the pair loop has a single exit,
+    // so the loop-carried load state, and with it every wait count, is exact.
     if (niter > 0) {
-        // ping-pong: the weight loads of the next unit are in flight while this one
-        // is computed; activations (L2-resident) are loaded at the top of their own
-        // iteration, before the next unit's weights, so waiting for them never waits
-        // for those weights
-        SnIn<C> b0, b1;
-        load_w<C>(b0, seg, rt, wave, s);
-        for (int it = 0;; it += 2) {
+        const int ulast = wave + W * (niter - 1);
+        SnIn<C, TW> b0, b1;
+        load_x<C, TW>(b0, xr, ln, wave);
+        load_w<C, TW>(b0, tl, ln, wave);
+        int it = 0;
+        for (; it + 2 <= niter; it += 2) {
             const int u0 = wave + W * it;
-            load_x<C>(b0, xc, u0);
-            if (it + 1 < niter) load_w<C>(b1, seg, rt, u0 + W, s);
-            unit_dot<C>(acc, b0, u0);
-            if (it + 1 >= niter) break;
-            load_x<C>(b1, xc, u0 + W);
-            if (it + 2 < niter) load_w<C>(b0, seg, rt, u0 + 2 * W, s);
-            unit_dot<C>(acc, b1, u0 + W);
-            if (it + 2 >= niter) break;
+            load_x<C, TW>(b1, xr, ln, u0 + W);
+            load_w<C, TW>(b1, tl, ln, u0 + W);
+            __builtin_amdgcn_sched_barrier(0);  // issue the loads before any wait
+            unit_dot<C, TW>(acc, b0, u0);
+            const int u2 = min(u0 + 2 * W, ulast);
+            load_x<C, TW>(b0, xr, ln, u2);
+            load_w<C, TW>(b0, tl, ln, u2);
+            __builtin_amdgcn_sched_barrier(0);
+            unit_dot<C, TW>(acc, b1, u0 + W);
         }
+        if (it < niter) unit_dot<C, TW>(acc, b0, wave + W * it);
     }
 
     if constexpr (W > 1) {
-        __shared__ float red[W][C * 4][64];
+        __shared__ float red[W][TW * C * 4][64];
 #pragma unroll
-        for (int c = 0; c < C; ++c)
+        for (int t = 0; t < TW; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) red[wave][4 * c + e][lane] = acc[c][e];
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) red[wave][(t * C + c) * 4 + e][lane] = acc[t][c][e];
         __syncthreads();
         if (wave != 0) return;
 #pragma unroll
-        for (int c = 0; c < C; ++c)
+        for (int t = 0; t < TW; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float v = red[0][4 * c + e][lane];
+            for (int c = 0; c < C; ++c)
 #pragma unroll
-                for (int w = 1; w < W; ++w) v += red[w][4 * c + e][lane];
-                acc[c][e] = v;
-            }
+                for (int e = 0; e < 4; ++e) {
+                    float v = red[0][(t * C + c) * 4 + e][lane];
+#pragma unroll
+                    for (int w = 1; w < W; ++w) v += red[w][(t * C + c) * 4 + e][lane];
+                    acc[t][c][e] = v;
+                }
     }
-    if (i < rt) {
-        const int row = tile * T + i;
 #pragma unroll
-        for (int c = 0; c < C; ++c)
+    for (int t = 0; t < TW; ++t) {
+        if (tile0 + t < P.tiles && i < tl.rt[t]) {
+            const int row = (tile0 + t) * T + i;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int n = 16 * c + 4 * s + e;
-                if (n < P.N) P.Y[(int64_t)n * P.ldy + row] = acc[c][e];
-            }
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int n = 16 * c + 4 * s + e;
+                    if (n < P.N) P.Y[(int64_t)n * P.ldy + row] = acc[t][c][e];
+                }
+        }
     }
 }
 
@@ -272,24 +329,32 @@ SnProb make_sn(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy
     return P;
 }
 
-// Wavefronts per workgroup: enough K units per wavefront to pipeline, at most 8.
-int choose_w(const SnArgs& a, int C) {
+// Launch shape: W wavefronts per workgroup (each with at least two 64-weight K
+// units to pipeline), TW tiles per wavefront (activations shared by the tiles:
+// two for more than 16 columns, where activation traffic dominates).
+struct SnCfg {
+    int W, TW;
+};
+SnCfg choose_cfg(const SnArgs& a, int C) {
     int units = INT_MAX;
-    for (int i = 0; i < a.count; ++i) units = std::min(units, a.p[i].nb * C);
-    int W = 1;
-    while (W < 4 && 2 * W <= units) W *= 2;
-    int ew = 0, eu = 0;
-    if (qg::env_pair("QG_SN_CFG", &ew, &eu) && (ew == 1 || ew == 2 || ew == 4 || ew == 8)) W = ew;
-    return W;
+    for (int i = 0; i < a.count; ++i) units = std::min(units, a.p[i].nb * 4);
+    SnCfg c{1, C == 2 ? 2 : 1};
+    while (c.W < 4 && 2 * c.W <= units / 2) c.W *= 2;
+    int ew = 0, et = 0;
+    if (qg::env_pair("QG_SN_CFG", &ew, &et)) {
+        if (ew == 1 || ew == 2 || ew == 4 || ew == 8) c.W = ew;
+        if (et == 1 || et == 2) c.TW = et;
+    }
+    return c;
 }
 
-template <int C>
+template <int C, int TW>
 void launch(const SnArgs& a, int grid, int W, hipStream_t s) {
     switch (W) {
-        case 1: hipLaunchKernelGGL((q4k_smalln_kernel<C, 1>), dim3(grid), dim3(64), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((q4k_smalln_kernel<C, 2>), dim3(grid), dim3(128), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((q4k_smalln_kernel<C, 4>), dim3(grid), dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((q4k_smalln_kernel<C, 8>), dim3(grid), dim3(512), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 1>), dim3(grid), dim3(64), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 2>), dim3(grid), dim3(128), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 4>), dim3(grid), dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 8>), dim3(grid), dim3(512), 0, s, a); break;
     }
 }
 
@@ -299,27 +364,33 @@ int run(const qg_gemm_problem* probs, int count, hipStream_t stream) {
         return qg::fail(QG_ERR_SHAPE, "count=%d not in [1, %d]", count, QG_MAX_BATCH);
     SnArgs a{};
     a.count = count;
-    int64_t wgs = 0;
     int nmax = 0;
     for (int i = 0; i < count; ++i) {
         const qg_gemm_problem& q = probs[i];
         int st = sn_validate(q.w_packed, q.X, q.ldx, q.Y, q.ldy, q.M, q.K, q.N);
         if (st) return st;
         a.p[i] = make_sn(q.w_packed, q.X, q.ldx, q.Y, q.ldy, q.M, q.K, q.N);
+        nmax = std::max(nmax, a.p[i].N);
+    }
+    const int C = nmax > 16 ? 2 : 1;
+    const SnCfg cfg = choose_cfg(a, C);
+    int64_t wgs = 0;
+    for (int i = 0; i < count; ++i) {
         a.p[i].wg_begin = (int32_t)wgs;
         a.begin[i] = (int32_t)wgs;
-        wgs += a.p[i].tiles;
-        nmax = std::max(nmax, a.p[i].N);
+        wgs += qg::ceil_div(a.p[i].tiles, cfg.TW);
     }
     if (wgs > INT32_MAX) return qg::fail(QG_ERR_SHAPE, "too many tiles in one batch");
     int st = qg::check_device();
     if (st) return st;
-    const int C = nmax > 16 ? 2 : 1;
-    const int W = choose_w(a, C);
-    if (C == 1)
-        launch<1>(a, (int)wgs, W, stream);
+    if (C == 1 && cfg.TW == 1)
+        launch<1, 1>(a, (int)wgs, cfg.W, stream);
+    else if (C == 1)
+        launch<1, 2>(a, (int)wgs, cfg.W, stream);
+    else if (cfg.TW == 1)
+        launch<2, 1>(a, (int)wgs, cfg.W, stream);
     else
-        launch<2>(a, (int)wgs, W, stream);
+        launch<2, 2>(a, (int)wgs, cfg.W, stream);
     return qg::launch_status("qgemm_q4k_smalln");
 }
 
