@@ -57,9 +57,9 @@ QG_DEV void load_half(HalfIn& d, const uint4* __restrict__ seg, const float* __r
     d.xa = *reinterpret_cast<const float4*>(xb);
     d.xb = *reinterpret_cast<const float4*>(xb + 4);
     const uint4* base = seg + (size_t)mb * 17 * rt;
-    d.s[0] = base[0];
+    d.s[0] = base[0];  // the scales serve both halves: a cached load
 #pragma unroll
-    for (int s = 0; s < 8; ++s) d.s[1 + s] = base[(size_t)(1 + 8 * h + s) * rt];
+    for (int s = 0; s < 8; ++s) d.s[1 + s] = qg_stream_load(base + (size_t)(1 + 8 * h + s) * rt);
 }
 
 // Contribution of half macro-block h for this lane's row.
@@ -134,19 +134,30 @@ QG_DEV float tile_rows(const Q8Prob& P, int tile, int lane, int wave) {
 
     float acc = 0.f;
     if (nu > 0) {
+        // Ping-pong between two register buffers over pairs of half macro-blocks:
+        // the loads of one stay in flight while the other is computed. Loads are
+        // unconditional (index clamped to the last one) and the pair loop has a
+        // single exit, so every wait count is exact.
         const int niter = (nu + G - 1) / G;
-        HalfIn cur, nxt;
-        load_half(cur, seg, xk, min(kg, nu - 1), rt);
-        for (int it = 0; it < niter - 1; ++it) {
+        HalfIn b0, b1;
+        load_half(b0, seg, xk, min(kg, nu - 1), rt);
+        int it = 0;
+        for (; it + 2 <= niter; it += 2) {
             const int u = kg + G * it;
-            load_half(nxt, seg, xk, min(u + G, nu - 1), rt);
-            const float v = half_dot(cur, u & 1);
-            acc += (u < nu) ? v : 0.f;
-            cur = nxt;
+            load_half(b1, seg, xk, min(u + G, nu - 1), rt);
+            __builtin_amdgcn_sched_barrier(0);  // issue the loads before any wait
+            const float v0 = half_dot(b0, u & 1);
+            acc += (u < nu) ? v0 : 0.f;
+            load_half(b0, seg, xk, min(u + 2 * G, nu - 1), rt);
+            __builtin_amdgcn_sched_barrier(0);
+            const float v1 = half_dot(b1, (u + G) & 1);
+            acc += (u + G < nu) ? v1 : 0.f;
         }
-        const int u = kg + G * (niter - 1);
-        const float v = half_dot(cur, u & 1);
-        acc += (u < nu) ? v : 0.f;
+        if (it < niter) {
+            const int u = kg + G * it;
+            const float v0 = half_dot(b0, u & 1);
+            acc += (u < nu) ? v0 : 0.f;
+        }
     }
     if (P.tb > 0 && kg == 0 && i < rt) {
         const uint8_t* rowtail = tbase + (size_t)P.nmb * 17 * rt * 16 + (size_t)i * P.tb * 34;
