@@ -329,21 +329,30 @@ SnProb make_sn(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy
     return P;
 }
 
-// Launch shape: W wavefronts per workgroup (each with at least two 64-weight K
-// units to pipeline), TW tiles per wavefront (activations shared by the tiles:
-// two for more than 16 columns, where activation traffic dominates).
+// Launch shape: W wavefronts per workgroup (up to 8, each with at least two
+// 64-weight K units to pipeline) and TW tiles per wavefront. Sharing one unit's
+// activations among TW tiles divides the activation traffic (which for 16-row
+// tiles exceeds the weight traffic once N > 2) by TW, at the price of TW times
+// fewer workgroups: one tile up to 256 tiles in the batch (about one workgroup
+// per CU), two above that, and for more than 16 columns four above 1024 tiles.
 struct SnCfg {
     int W, TW;
 };
 SnCfg choose_cfg(const SnArgs& a, int C) {
     int units = INT_MAX;
-    for (int i = 0; i < a.count; ++i) units = std::min(units, a.p[i].nb * 4);
-    SnCfg c{1, C == 2 ? 2 : 1};
-    while (c.W < 4 && 2 * c.W <= units / 2) c.W *= 2;
+    int64_t tiles = 0;
+    for (int i = 0; i < a.count; ++i) {
+        units = std::min(units, a.p[i].nb * 4);
+        tiles += a.p[i].tiles;
+    }
+    SnCfg c{1, tiles > 256 ? 2 : 1};
+    if (C == 2 && tiles > 1024) c.TW = 4;
+    const int wmax = c.TW == 4 ? 4 : 8;
+    while (c.W < wmax && 2 * c.W <= units / 2) c.W *= 2;
     int ew = 0, et = 0;
     if (qg::env_pair("QG_SN_CFG", &ew, &et)) {
         if (ew == 1 || ew == 2 || ew == 4 || ew == 8) c.W = ew;
-        if (et == 1 || et == 2) c.TW = et;
+        if (et == 1 || et == 2 || et == 4) c.TW = et;
     }
     return c;
 }
@@ -383,14 +392,15 @@ int run(const qg_gemm_problem* probs, int count, hipStream_t stream) {
     if (wgs > INT32_MAX) return qg::fail(QG_ERR_SHAPE, "too many tiles in one batch");
     int st = qg::check_device();
     if (st) return st;
-    if (C == 1 && cfg.TW == 1)
-        launch<1, 1>(a, (int)wgs, cfg.W, stream);
-    else if (C == 1)
-        launch<1, 2>(a, (int)wgs, cfg.W, stream);
-    else if (cfg.TW == 1)
-        launch<2, 1>(a, (int)wgs, cfg.W, stream);
-    else
-        launch<2, 2>(a, (int)wgs, cfg.W, stream);
+    const int key = 10 * C + cfg.TW;
+    switch (key) {
+        case 11: launch<1, 1>(a, (int)wgs, cfg.W, stream); break;
+        case 12: launch<1, 2>(a, (int)wgs, cfg.W, stream); break;
+        case 14: launch<1, 4>(a, (int)wgs, cfg.W, stream); break;
+        case 21: launch<2, 1>(a, (int)wgs, cfg.W, stream); break;
+        case 22: launch<2, 2>(a, (int)wgs, cfg.W, stream); break;
+        default: launch<2, 4>(a, (int)wgs, cfg.W, stream); break;
+    }
     return qg::launch_status("qgemm_q4k_smalln");
 }
 
