@@ -81,9 +81,10 @@ typedef unsigned int qg_u2v __attribute__((ext_vector_type(2)));
 constexpr uint32_t kOutOfRange = 0x80000000u;  // >= every resource size used here
 constexpr int kNonTemporal = 2;                 // buffer-load cache policy: nt
 
+template <int C, int TW>
 struct SnLane {
-    uint32_t hdr[2], q[2];   // per tile: byte offset of this lane's header / quant bytes
-    uint32_t x[2];           // per column block: byte offset of this lane's activations
+    uint32_t hdr[TW], q[TW];  // per tile: byte offset of this lane's header / quant bytes
+    uint32_t x[C];            // per column block: byte offset of this lane's activations
 };
 
 template <int TW>
@@ -93,7 +94,7 @@ struct SnTiles {
 };
 
 template <int C, int TW>
-QG_DEV void load_w(SnIn<C, TW>& d, const SnTiles<TW>& tl, const SnLane& ln, int u) {
+QG_DEV void load_w(SnIn<C, TW>& d, const SnTiles<TW>& tl, const SnLane<C, TW>& ln, int u) {
     const int b = u >> 2, g = u & 3;
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
@@ -107,7 +108,7 @@ QG_DEV void load_w(SnIn<C, TW>& d, const SnTiles<TW>& tl, const SnLane& ln, int 
 }
 
 template <int C, int TW>
-QG_DEV void load_x(SnIn<C, TW>& d, __amdgpu_buffer_rsrc_t xr, const SnLane& ln, int u) {
+QG_DEV void load_x(SnIn<C, TW>& d, __amdgpu_buffer_rsrc_t xr, const SnLane<C, TW>& ln, int u) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15, s = lane >> 4;
     SnTiles<TW> tl;
-    SnLane ln;
+    SnLane<C, TW> ln;
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
         // a tile past the matrix end (TW > 1, ragged tile count) re-reads the last tile

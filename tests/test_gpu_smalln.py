@@ -90,3 +90,27 @@ def test_batch_mixed_problems():
         Yc = Y.cpu().numpy()[:, :M][:, ::5]
         for n in range(X.shape[0]):
             assert_within(Yc[n], Yr[n], Ar[n], f"batch M={M} K={K} col {n}")
+
+
+@pytest.mark.parametrize("cfg", ["1,1", "2,2", "4,4", "8,1", "8,2", "4,2"])
+@pytest.mark.parametrize("N", [5, 32])
+def test_launch_shapes(cfg, N, monkeypatch):
+    # every (wavefronts, tiles per wavefront) shape the launcher can pick, on a batch
+    # whose tile counts are not multiples of the tiles per wavefront and whose K
+    # ranges leave some wavefronts with an odd number of units (or none)
+    monkeypatch.setenv("QG_SN_CFG", cfg)
+    shapes = [(530, 1024), (77, 256), (16, 768), (1000, 512)]
+    probs, refs = [], []
+    for i, (M, K) in enumerate(shapes):
+        W = workloads.q4k_blocks(M, K, key=(34, i))
+        X = workloads.x_columns(K, N, key=(34, i, N))
+        Y = torch.full((N, (M + 3) // 4 * 4), float("nan"), device="cuda:0")
+        probs.append((packed_q4k(W, M, K), to_dev(X), Y, M, K))
+        refs.append(oracle.gemm_q4k(W, M, K, X))
+    case(f"qgemm_q4k_smalln_batch cfg={cfg} N={N}")
+    qg.qgemm_q4k_smalln_batch(probs)
+    torch.cuda.synchronize()
+    for (w, X, Y, M, K), (Yr, Ar) in zip(probs, refs):
+        Yc = Y.cpu().numpy()[:, :M]
+        for n in range(N):
+            assert_within(Yc[n], Yr[n], Ar[n], f"cfg {cfg} M={M} K={K} col {n}")
