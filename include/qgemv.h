@@ -39,11 +39,15 @@
  *     and mins, 128 bytes of 4-bit quants; weight = d*sc*q - dmin*m.
  *   Q8_0, 34 B per 32 weights: fp16 d, 32 int8 q; weight = d*q.
  *
- * Workspaces: the GEMV and small-N entry points take a workspace argument for
- * ABI stability but use none today (their *_workspace_bytes query returns 0 and
- * NULL is accepted). lmhead_argmax needs lmhead_argmax_workspace_bytes(M, K)
- * bytes of scratch for its per-workgroup partial results; the contents need no
- * initialisation and are dead after the call.
+ * Workspaces: every entry point takes a caller-owned workspace and reports the
+ * bytes it needs through its *_workspace_bytes query (0 means none; NULL is then
+ * accepted). A workspace must be all-zero when first used (qg_workspace_clear,
+ * or any zero-filled allocation) and every call leaves it all-zero again, so one
+ * workspace can serve every entry point in turn. The GEMV entry points use none
+ * today. qgemm_q4k_smalln* use it, when a launch splits K among workgroups, as
+ * 64-bit exchange slots in which the partial sums of an output element meet;
+ * lmhead_argmax uses it for its per-workgroup (max, index) partial results. A
+ * call that fails on the device may leave a workspace dirty: clear it again.
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -131,7 +135,10 @@ int qgemv_q8_0(const void* w_packed, const float* x, float* y, int64_t M, int64_
  * X + n*ldx); Y is column-major M x N with ldy >= M. ldx and ldy must be
  * multiples of 4. Each 32-weight sub-block is a 16 x 16 x 32 fp16 matrix-core
  * product of the activations (rounded to fp16) with the quants, accumulated and
- * scaled in fp32. Only Y[0..M) of each column is written. No workspace.
+ * scaled in fp32. Only Y[0..M) of each column is written. When the launch
+ * splits K among workgroups (small M), their partial sums meet in a fixed order
+ * through the workspace (qgemm_q4k_smalln_workspace_bytes), so results are
+ * deterministic.
  */
 size_t qgemm_q4k_smalln_workspace_bytes(int64_t M, int64_t K, int64_t N);
 int qgemm_q4k_smalln(const void* w_packed, const float* X, int64_t ldx, float* Y, int64_t ldy,

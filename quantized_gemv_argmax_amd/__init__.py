@@ -118,7 +118,8 @@ def _need_cuda(*ts):
 
 # ------------------------------------------------------------------ workspace
 class Workspace:
-    """A device scratch buffer reused across calls on one stream (grown on demand)."""
+    """A device scratch buffer reused across calls on one stream (grown on demand).
+    It starts all-zero, as the library requires, and every call leaves it so."""
 
     def __init__(self, device=None, nbytes: int = 0):
         self.device = torch.device(device if device is not None else "cuda")

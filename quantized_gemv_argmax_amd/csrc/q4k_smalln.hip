@@ -52,12 +52,14 @@ struct SnProb {
     const uint8_t* w;
     const float* X;
     float* Y;
+    unsigned long long* slots;  // split-K exchange slots: KS - 1 arrays of M * N (KS > 1)
     int64_t ldx, ldy;
     int32_t M, nb, N, tiles, wg_begin;
 };
 struct SnArgs {
     int32_t begin[QG_MAX_BATCH];
     int32_t count;
+    int32_t ks;  // workgroups sharing the K range of each row block (1, 2 or 4)
     SnProb p[QG_MAX_BATCH];
 };
 
@@ -204,7 +206,10 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
         if (i < a.count && wg >= a.begin[i]) k = i;
     const SnProb P = a.p[k];
 
-    const int tile0 = (wg - P.wg_begin) * TW;
+    const int KS = a.ks;
+    const int local = wg - P.wg_begin;
+    const int ks = local % KS;  // the KS workgroups of a row block are neighbours in the grid
+    const int tile0 = (local / KS) * TW;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15, s = lane >> 4;
@@ -229,8 +234,10 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
         const int n = 16 * c + i;
         ln.x[c] = n < P.N ? (uint32_t)(((int64_t)n * P.ldx + 8 * s) * 4) : kOutOfRange;
     }
+    // this workgroup's share of the K units, split among its wavefronts round-robin
     const int units = P.nb * 4;
-    const int niter = (units - wave + W - 1) / W;  // units wave, wave + W, ...
+    const int ub = (int)((int64_t)ks * units / KS), ue = (int)((int64_t)(ks + 1) * units / KS);
+    const int niter = (ue - ub - wave + W - 1) / W;  // units ub + wave, ub + wave + W, ...
     qg_f4 acc[TW][C];
 #pragma unroll
     for (int t = 0; t < TW; ++t)
@@ -243,13 +250,13 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
     // is clamped to the wavefront's last unit) and the pair loop has a single exit,
     // so the loop-carried load state, and with it every wait count, is exact.
     if (niter > 0) {
-        const int ulast = wave + W * (niter - 1);
+        const int ufirst = ub + wave, ulast = ufirst + W * (niter - 1);
         SnIn<C, TW> b0, b1;
-        load_x<C, TW>(b0, xr, ln, wave);
-        load_w<C, TW>(b0, tl, ln, wave);
+        load_x<C, TW>(b0, xr, ln, ufirst);
+        load_w<C, TW>(b0, tl, ln, ufirst);
         int it = 0;
         for (; it + 2 <= niter; it += 2) {
-            const int u0 = wave + W * it;
+            const int u0 = ufirst + W * it;
             load_x<C, TW>(b1, xr, ln, u0 + W);
             load_w<C, TW>(b1, tl, ln, u0 + W);
             __builtin_amdgcn_sched_barrier(0);  // issue the loads before any wait
@@ -260,7 +267,7 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             unit_dot<C, TW>(acc, b1, u0 + W);
         }
-        if (it < niter) unit_dot<C, TW>(acc, b0, wave + W * it);
+        if (it < niter) unit_dot<C, TW>(acc, b0, ufirst + W * it);
     }
 
     if constexpr (W > 1) {
@@ -294,7 +301,10 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int n = 16 * c + 4 * s + e;
-                    if (n < P.N) P.Y[(int64_t)n * P.ldy + row] = acc[t][c][e];
+                    if (n >= P.N) continue;
+                    float v = acc[t][c][e];
+                    if (KS == 1 || qg_splitk_combine(v, P.slots + (int64_t)n * P.M + row, (int64_t)P.M * P.N, ks, KS))
+                        P.Y[(int64_t)n * P.ldy + row] = v;
                 }
         }
     }
@@ -330,14 +340,18 @@ SnProb make_sn(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy
     return P;
 }
 
-// Launch shape: W wavefronts per workgroup (up to 8, each with at least two
-// 64-weight K units to pipeline) and TW tiles per wavefront. Sharing one unit's
-// activations among TW tiles divides the activation traffic (which for 16-row
-// tiles exceeds the weight traffic once N > 2) by TW, at the price of TW times
-// fewer workgroups: one tile up to 256 tiles in the batch (about one workgroup
-// per CU), two above that, and for more than 16 columns four above 1024 tiles.
+// Launch shape. TW tiles per wavefront: sharing one unit's activations among TW
+// tiles divides the activation traffic (which for 16-row tiles exceeds the weight
+// traffic once N > 2) by TW, at the price of TW times fewer workgroups: one tile
+// up to 256 tiles in the batch (about one workgroup per CU), two above that, and
+// for more than 16 columns four above 1024 tiles. KS workgroups per row block may
+// split K (1, 2 or 4, through the exchange slots); measured on MI355X the extra
+// device-scope round trips at the end of every workgroup cost more than the
+// added parallelism gains on the 7B shapes, so KS stays 1 unless QG_SN_KS asks
+// for more. W wavefronts per workgroup (up to 8, 4 with four tiles), each with at
+// least two units.
 struct SnCfg {
-    int W, TW;
+    int W, TW, KS;
 };
 SnCfg choose_cfg(const SnArgs& a, int C) {
     int units = INT_MAX;
@@ -346,15 +360,19 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
         units = std::min(units, a.p[i].nb * 4);
         tiles += a.p[i].tiles;
     }
-    SnCfg c{1, tiles > 256 ? 2 : 1};
+    SnCfg c{1, tiles > 256 ? 2 : 1, 1};
     if (C == 2 && tiles > 1024) c.TW = 4;
+    int ew = 0, et = 0, ek = 0;
+    const bool env = qg::env_pair("QG_SN_CFG", &ew, &et);
+    if (env && (et == 1 || et == 2 || et == 4)) c.TW = et;
+    int64_t wgs = 0;
+    for (int i = 0; i < a.count; ++i) wgs += qg::ceil_div(a.p[i].tiles, c.TW);
+    (void)wgs;
+    int unused = 0;
+    if (qg::env_pair("QG_SN_KS", &ek, &unused) && (ek == 1 || ek == 2 || ek == 4)) c.KS = ek;
     const int wmax = c.TW == 4 ? 4 : 8;
-    while (c.W < wmax && 2 * c.W <= units / 2) c.W *= 2;
-    int ew = 0, et = 0;
-    if (qg::env_pair("QG_SN_CFG", &ew, &et)) {
-        if (ew == 1 || ew == 2 || ew == 4 || ew == 8) c.W = ew;
-        if (et == 1 || et == 2 || et == 4) c.TW = et;
-    }
+    while (c.W < wmax && 2 * c.W <= units / c.KS / 2) c.W *= 2;
+    if (env && (ew == 1 || ew == 2 || ew == 4 || ew == 8 || (ew == 16 && C == 1 && c.TW == 1))) c.W = ew;
     return c;
 }
 
@@ -364,34 +382,66 @@ void launch(const SnArgs& a, int grid, int W, hipStream_t s) {
         case 1: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 1>), dim3(grid), dim3(64), 0, s, a); break;
         case 2: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 2>), dim3(grid), dim3(128), 0, s, a); break;
         case 4: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 4>), dim3(grid), dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 8>), dim3(grid), dim3(512), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 8>), dim3(grid), dim3(512), 0, s, a); break;
+        default:
+            if constexpr (C == 1 && TW == 1) hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 16>), dim3(grid), dim3(1024), 0, s, a);
+            break;
     }
 }
 
-int run(const qg_gemm_problem* probs, int count, hipStream_t stream) {
+// Validates the problems and fills the kernel arguments and launch shape. With
+// ws_needed set, only the workspace size is computed (pointers are not checked).
+int plan(const qg_gemm_problem* probs, int count, bool size_only, SnArgs& a, SnCfg& cfg, int& C, int64_t& wgs,
+         size_t& ws_needed) {
     if (!probs) return qg::fail(QG_ERR_NULL, "NULL problem list");
     if (count < 1 || count > QG_MAX_BATCH)
         return qg::fail(QG_ERR_SHAPE, "count=%d not in [1, %d]", count, QG_MAX_BATCH);
-    SnArgs a{};
+    a = SnArgs{};
     a.count = count;
     int nmax = 0;
     for (int i = 0; i < count; ++i) {
         const qg_gemm_problem& q = probs[i];
-        int st = sn_validate(q.w_packed, q.X, q.ldx, q.Y, q.ldy, q.M, q.K, q.N);
+        static const float dummy[4] = {0, 0, 0, 0};
+        int st = size_only ? sn_validate(dummy, dummy, q.ldx, dummy, q.ldy, q.M, q.K, q.N)
+                           : sn_validate(q.w_packed, q.X, q.ldx, q.Y, q.ldy, q.M, q.K, q.N);
         if (st) return st;
         a.p[i] = make_sn(q.w_packed, q.X, q.ldx, q.Y, q.ldy, q.M, q.K, q.N);
         nmax = std::max(nmax, a.p[i].N);
     }
-    const int C = nmax > 16 ? 2 : 1;
-    const SnCfg cfg = choose_cfg(a, C);
-    int64_t wgs = 0;
+    C = nmax > 16 ? 2 : 1;
+    cfg = choose_cfg(a, C);
+    a.ks = cfg.KS;
+    wgs = 0;
+    ws_needed = 0;
     for (int i = 0; i < count; ++i) {
         a.p[i].wg_begin = (int32_t)wgs;
         a.begin[i] = (int32_t)wgs;
-        wgs += qg::ceil_div(a.p[i].tiles, cfg.TW);
+        wgs += qg::ceil_div(a.p[i].tiles, cfg.TW) * cfg.KS;
+        if (cfg.KS > 1) ws_needed += qg::align_up((size_t)(cfg.KS - 1) * a.p[i].M * a.p[i].N * 8, 256);
     }
     if (wgs > INT32_MAX) return qg::fail(QG_ERR_SHAPE, "too many tiles in one batch");
-    int st = qg::check_device();
+    return QG_OK;
+}
+
+int run(const qg_gemm_problem* probs, int count, void* ws, size_t ws_bytes, hipStream_t stream) {
+    SnArgs a;
+    SnCfg cfg;
+    int C;
+    int64_t wgs;
+    size_t need;
+    int st = plan(probs, count, false, a, cfg, C, wgs, need);
+    if (st) return st;
+    if (need > 0) {
+        if (!ws) return qg::fail(QG_ERR_WORKSPACE, "a workspace of %zu bytes is required", need);
+        if (ws_bytes < need) return qg::fail(QG_ERR_WORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+        if (!qg::aligned16(ws)) return qg::fail(QG_ERR_ALIGN, "workspace must be 16-byte aligned");
+        unsigned char* p = (unsigned char*)ws;
+        for (int i = 0; i < count; ++i) {
+            a.p[i].slots = (unsigned long long*)p;
+            p += qg::align_up((size_t)(cfg.KS - 1) * a.p[i].M * a.p[i].N * 8, 256);
+        }
+    }
+    st = qg::check_device();
     if (st) return st;
     const int key = 10 * C + cfg.TW;
     switch (key) {
@@ -405,38 +455,40 @@ int run(const qg_gemm_problem* probs, int count, hipStream_t stream) {
     return qg::launch_status("qgemm_q4k_smalln");
 }
 
+size_t ws_bytes_for(const qg_gemm_problem* probs, int count) {
+    SnArgs a;
+    SnCfg cfg;
+    int C;
+    int64_t wgs;
+    size_t need = 0;
+    if (plan(probs, count, true, a, cfg, C, wgs, need)) return 0;
+    return need;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t qgemm_q4k_smalln_workspace_bytes(int64_t M, int64_t K, int64_t N) {
-    (void)M;
-    (void)K;
-    (void)N;
-    return 0;  // each workgroup owns whole rows
+    const qg_gemm_problem p{nullptr, nullptr, K, nullptr, (M + 3) / 4 * 4, M, K, N};
+    return ws_bytes_for(&p, 1);
 }
 
 int qgemm_q4k_smalln(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy, int64_t M, int64_t K,
                      int64_t N, void* ws, size_t ws_bytes, qg_stream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
     qg::clear_error();
     const qg_gemm_problem p{w, X, ldx, Y, ldy, M, K, N};
-    return run(&p, 1, (hipStream_t)stream);
+    return run(&p, 1, ws, ws_bytes, (hipStream_t)stream);
 }
 
 size_t qgemm_q4k_smalln_batch_workspace_bytes(const qg_gemm_problem* problems, int count) {
-    (void)problems;
-    (void)count;
-    return 0;
+    return ws_bytes_for(problems, count);
 }
 
 int qgemm_q4k_smalln_batch(const qg_gemm_problem* problems, int count, void* ws, size_t ws_bytes,
                            qg_stream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
     qg::clear_error();
-    return run(problems, count, (hipStream_t)stream);
+    return run(problems, count, ws, ws_bytes, (hipStream_t)stream);
 }
 
 }  // extern "C"

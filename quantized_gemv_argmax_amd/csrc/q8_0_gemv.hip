@@ -220,12 +220,13 @@ __global__ __launch_bounds__(64 * W) void lmhead_tile_kernel(Q8Prob P, float2* _
 }
 
 // Stage 2: one workgroup reduces the partials in a fixed order.
-__global__ __launch_bounds__(1024) void lmhead_reduce_kernel(const float2* __restrict__ partials, int n,
+__global__ __launch_bounds__(1024) void lmhead_reduce_kernel(float2* __restrict__ partials, int n,
                                                               int32_t* out_index, float* out_value) {
     float bv = -__builtin_huge_valf();
     int bi = INT_MAX;
     for (int g = threadIdx.x; g < n; g += blockDim.x) {
         const float2 pg = partials[g];
+        partials[g] = make_float2(0.f, 0.f);  // workspaces are left all-zero
         const int gi = __builtin_bit_cast(int, pg.y);
         if (better(pg.x, gi, bv, bi)) {
             bv = pg.x;
@@ -387,7 +388,7 @@ int lmhead_argmax(const void* w, const float* x, int64_t M, int64_t K, void* ws,
     st = qg::launch_status("lmhead_argmax (tiles)");
     if (st) return st;
     const int threads = (int)std::min<int64_t>(1024, std::max<int64_t>(64, qg::ceil_div(P.tiles, 64) * 64));
-    hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(1), dim3(threads), 0, s, (const float2*)partials, P.tiles,
+    hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(1), dim3(threads), 0, s, (float2*)partials, P.tiles,
                        out_index, out_value);
     return qg::launch_status("lmhead_argmax (reduce)");
 }

@@ -56,9 +56,10 @@ bool env_pair(const char* name, int* a, int* b) {
     const char* s = getenv(name);
     if (!s || !*s) return false;
     int x = 0, y = 0;
-    if (sscanf(s, "%d,%d", &x, &y) != 2) return false;
+    const int got = sscanf(s, "%d,%d", &x, &y);
+    if (got < 1) return false;
     *a = x;
-    *b = y;
+    *b = got == 2 ? y : 0;  // a single number sets the first value only
     return true;
 }
 

@@ -226,3 +226,32 @@ QG_DEV float qg_sum_rows4(float v) {
     v += __shfl_xor(v, 32, 64);
     return v;
 }
+
+// ---------------------------------------------------------------------------
+// Split-K combination without fences or waiting. KS workgroups (KS a power of
+// two) each hold a partial sum of one output element; they meet pairwise in a
+// fixed tree, level by level: the partners of a pair each exchange
+// (1 << 32 | bits of their value) into the pair's 64-bit slot. The first to
+// arrive finds the slot idle (high word 0) and is done; the second finds its
+// partner's value in what the exchange returned, adds it (fp32 addition is
+// commutative, so the sum is the same whichever comes second), returns the slot
+// to idle and goes on to the next level. All communication is the value carried
+// by single atomic exchanges on one location each, so no fence is involved and
+// the sum has a fixed association ((p0 + p1) + (p2 + p3)): results do not depend
+// on arrival order. `slot` is this element's slot in the first of KS - 1 slot
+// arrays, `stride` the distance (in slots) between arrays; every slot is idle
+// (zero) before the call and is idle again after it. Returns true in the one
+// caller left holding the complete sum.
+QG_DEV bool qg_splitk_combine(float& v, unsigned long long* slot, int64_t stride, int ks, int KS) {
+    int base = 0;
+    for (int span = 1; span < KS; span <<= 1) {
+        unsigned long long* p = slot + (int64_t)(base + ks / (2 * span)) * stride;
+        const unsigned long long mine = (1ull << 32) | (unsigned long long)__builtin_bit_cast(uint32_t, v);
+        const unsigned long long old = __hip_atomic_exchange(p, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((old >> 32) == 0) return false;
+        v = v + __builtin_bit_cast(float, (uint32_t)old);
+        __hip_atomic_store(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        base += KS / (2 * span);
+    }
+    return true;
+}

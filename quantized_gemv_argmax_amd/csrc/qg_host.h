@@ -26,8 +26,8 @@ int launch_status(const char* what);
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Reads an optional "A,B" integer pair from an environment variable (tuning
-// sweeps); returns false when unset or malformed.
+// Reads an optional "A,B" (or "A", giving B = 0) integer pair from an environment
+// variable (tuning sweeps); returns false when unset or malformed.
 bool env_pair(const char* name, int* a, int* b);
 
 }  // namespace qg

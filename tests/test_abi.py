@@ -95,6 +95,18 @@ def test_smalln_validation(L):
     assert L.qgemm_q4k_smalln_workspace_bytes(3584, 3584, 5) == 0
 
 
+def test_smalln_split_k_workspace(L, monkeypatch):
+    # with K split between two workgroups per row block, their partial sums meet
+    # in one array of 8-byte slots per output element
+    monkeypatch.setenv("QG_SN_KS", "2")
+    f = L.qgemm_q4k_smalln
+    assert L.qgemm_q4k_smalln_workspace_bytes(3584, 3584, 5) == 3584 * 5 * 8
+    # a call that needs a workspace and gets none (or too little) is refused
+    # before any launch
+    assert f(C, A, 3584, B, 3584, 3584, 3584, 5, None, 0, None) == EWS
+    assert f(C, A, 3584, B, 3584, 3584, 3584, 5, A, 3584 * 5 * 8 - 8, None) == EWS
+
+
 def test_pack_validation(L):
     assert L.qg_pack_q4k(None, A, 64, 256, None) == ENULL
     assert L.qg_pack_q4k(A, B, 64, 100, None) == ESHAPE

@@ -13,7 +13,7 @@ import oracle
 import quantized_gemv_argmax_amd as qg
 import workloads
 from tests import blockenc as enc
-from tests.gpu_helpers import assert_within, case, packed_q8_0, to_dev
+from tests.gpu_helpers import DEV, assert_within, case, packed_q8_0, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -119,3 +119,22 @@ def test_lmhead_vocab_152064_with_resampling():
         assert abs(gv - yr[gi]) <= tol[gi]
         exact += gi == ri
     print(f"exact-match rate {exact}/{trials}")
+
+
+def test_lmhead_leaves_workspace_zero():
+    # the partial (max, index) pairs are cleared by the reduction, so a workspace
+    # shared with the small-N product (which needs idle, zero slots) stays valid
+    M, K = 5000, 512
+    W = workloads.q8_0_blocks(M, K, key=(23,))
+    x = workloads.x_vector(K, key=(23,))
+    ws = qg.Workspace(DEV)
+    case("lmhead_argmax workspace left zero")
+    wp = packed_q8_0(W, M, K)
+    for _ in range(2):
+        idx, _ = qg.lmhead_argmax(wp, to_dev(x), M, K, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.buf.count_nonzero()) == 0
+    yr, ar = oracle.gemv_q8_0(W, M, K, x)
+    gi, ri = int(idx.item()), oracle.argmax(yr)
+    tol = oracle.tolerance(ar)
+    assert gi == ri or yr[gi] >= yr[ri] - tol[gi] - tol[ri]

@@ -114,3 +114,36 @@ def test_launch_shapes(cfg, N, monkeypatch):
         Yc = Y.cpu().numpy()[:, :M]
         for n in range(N):
             assert_within(Yc[n], Yr[n], Ar[n], f"cfg {cfg} M={M} K={K} col {n}")
+
+
+@pytest.mark.parametrize("ks", ["2", "4"])
+@pytest.mark.parametrize("N", [5, 32])
+def test_split_k_exchange(ks, N, monkeypatch):
+    # K split among 2 or 4 workgroups per row block whose partial sums meet
+    # through 64-bit exchange slots: parity, bitwise determinism over repeated
+    # calls, and the workspace back to all-zero after every call
+    monkeypatch.setenv("QG_SN_KS", ks)
+    shapes = [(530, 4096), (77, 2048), (1000, 3584)]
+    probs, refs = [], []
+    for i, (M, K) in enumerate(shapes):
+        W = workloads.q4k_blocks(M, K, key=(35, i))
+        X = workloads.x_columns(K, N, key=(35, i, N))
+        Y = torch.full((N, (M + 3) // 4 * 4), float("nan"), device="cuda:0")
+        probs.append((packed_q4k(W, M, K), to_dev(X), Y, M, K))
+        refs.append(oracle.gemm_q4k(W, M, K, X, rows=np.arange(0, M, 3)))
+    ws = qg.Workspace("cuda:0")
+    case(f"qgemm_q4k_smalln_batch split-K ks={ks} N={N}")
+    qg.qgemm_q4k_smalln_batch(probs, ws=ws)
+    torch.cuda.synchronize()
+    assert ws.buf is not None and int(ws.buf.count_nonzero()) == 0
+    first = [p[2].clone() for p in probs]
+    for _ in range(2):
+        qg.qgemm_q4k_smalln_batch(probs, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.buf.count_nonzero()) == 0
+        for (w, X, Y, M, K), Y0 in zip(probs, first):
+            assert torch.equal(Y[:, :M], Y0[:, :M])  # the padding past M stays NaN
+    for (w, X, Y, M, K), (Yr, Ar) in zip(probs, refs):
+        Yc = Y.cpu().numpy()[:, :M][:, ::3]
+        for n in range(N):
+            assert_within(Yc[n], Yr[n], Ar[n], f"split-K {ks} M={M} K={K} col {n}")
