@@ -101,6 +101,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-ref", action="store_true",
                     help="end with one plain 256 MiB device copy (a reference dispatch for traffic counters)")
+    ap.add_argument("--counters", action="store_true",
+                    help="instead of the timed rows, run each other hot-path kernel a few times on distinct "
+                         "weight copies (a short program for rocprofv3 --pmc passes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -203,7 +206,9 @@ def main():
                 "avg_bytes_per_launch": int(avg_launch_bytes), "per_stage": per_stage}
 
     rows = {}
-    if not args.no_rows:
+    if args.counters:
+        counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers)
+    elif not args.no_rows:
         rows = other_rows(torch, np, qg, wl, dev, ws, layers, n_layers)
 
     cpu = None
@@ -247,6 +252,46 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+
+
+def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
+    """Each of the other hot-path kernels a few times, every call on its own weight
+    copy, in this order: 4096x4096 Q4_K GEMV (3 calls), Q8_0 11008x4096 and
+    4096x11008 (3 each), LM head + argmax 152064x3584 (2), small-N N=5 then N=32 over
+    the layers' stages (one grouped launch per stage)."""
+    M, K = 4096, 4096
+    W = wl.q4k_blocks(M, K, key=(1, 0))
+    wp = qg.pack_q4k(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
+    x = torch.from_numpy(wl.x_vector(K, key=(1, 0))).to(dev)
+    y = torch.empty(M, device=dev)
+    for c in [wp] + [wp.clone() for _ in range(2)]:
+        qg.qgemv_q4k(c, x, M, K, y=y, ws=ws)
+    for (M, K) in [(11008, 4096), (4096, 11008)]:
+        W = wl.q8_0_blocks(M, K, key=(2, M))
+        wp = qg.pack_q8_0(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
+        x = torch.from_numpy(wl.x_vector(K, key=(2, M))).to(dev)
+        y = torch.empty(M, device=dev)
+        for c in [wp] + [wp.clone() for _ in range(2)]:
+            qg.qgemv_q8_0(c, x, M, K, y=y, ws=ws)
+    M, K = wl.VOCAB, wl.HIDDEN
+    W = wl.q8_0_blocks(M, K, key=(4, 0))
+    wp = qg.pack_q8_0(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
+    del W
+    x = torch.from_numpy(wl.x_vector(K, key=(4, 0))).to(dev)
+    for c in (wp, wp.clone()):
+        qg.lmhead_argmax(c, x, M, K, ws=ws)
+    del wp
+    for N in (5, 32):
+        for L in range(n_layers):
+            for st in wl.LAYER_STAGES:
+                grp = []
+                for i in st:
+                    wp_, _, _, M_, K_ = layers[L][i]
+                    X_ = torch.from_numpy(wl.x_columns(K_, N, key=(5, L, i, N))).to(dev)
+                    grp.append((wp_, X_, torch.empty((N, (M_ + 3) // 4 * 4), device=dev), M_, K_))
+                qg.qgemm_q4k_smalln_batch(grp, ws=ws)
+    torch.cuda.synchronize()
+    log("counter rows done")
 
 
 def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
