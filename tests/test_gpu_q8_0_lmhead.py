@@ -99,7 +99,7 @@ def test_lmhead_vocab_152064_with_resampling():
     case("lmhead_argmax 152064x3584 pack")
     wp = packed_q8_0(W, M, K)
     exact = 0
-    trials = 4
+    trials = 16
     for t in range(trials):
         r = 0
         while True:
@@ -116,6 +116,8 @@ def test_lmhead_vocab_152064_with_resampling():
         tol = oracle.tolerance(ar)
         if s[-1] - s[-2] > tol[ri]:
             assert gi == ri
+        else:  # within the tolerance band any row that could be the maximum will do
+            assert yr[gi] >= yr[ri] - tol[gi] - tol[ri]
         assert abs(gv - yr[gi]) <= tol[gi]
         exact += gi == ri
     print(f"exact-match rate {exact}/{trials}")
