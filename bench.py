@@ -349,7 +349,7 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     ov = torch.empty(1, dtype=torch.float32, device=dev)
     ms = graph_ms(torch, lambda: [qg.lmhead_argmax(c, x, M, K, out_index=oi, out_value=ov, ws=ws) for c in copies],
                   20) / 2
-    b = wp.numel() + 4 * K + 8 * (-(-M // 64)) * 2 + 8
+    b = wp.numel() + 4 * K + 8 * (-(-M // 16)) * 2 + 8  # weights, x, partials written and read, result
     # unfused comparison: Q8_0 GEMV writing the 608,256-byte logit vector + torch argmax
     logits = torch.empty(M, device=dev)
     ms_unfused = graph_ms(torch, lambda: [(qg.qgemv_q8_0(c, x, M, K, y=logits, ws=ws), torch.argmax(logits))
@@ -370,6 +370,19 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
         "unfused_gemv_plus_torch_argmax_us": round(ms_unfused * 1e3, 3),
         "d2h_logits_608256B_us": round(d2h_us, 2), "d2h_index_4B_us": round(d2h4_us, 2)}
     log(f"row lmhead: {rows['lmhead_argmax_152064x3584']}")
+
+    # batched greedy verification on the same head: N = 5 columns in one pass
+    N = 5
+    X5 = torch.from_numpy(wl.x_columns(K, N, key=(4, 3))).to(dev)
+    oi5 = torch.empty(N, dtype=torch.int32, device=dev)
+    ov5 = torch.empty(N, dtype=torch.float32, device=dev)
+    ms = graph_ms(torch, lambda: [qg.lmhead_argmax_verify(c, X5, M, K, out_index=oi5, out_value=ov5, ws=ws)
+                                  for c in copies], 20) / 2
+    b = wp.numel() + 4 * K * N + 8 * (-(-M // 16)) * N * 2 + 8 * N
+    rows["lmhead_verify_N5_152064x3584"] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                                            "bytes": int(b), "us_per_single_column_argmax": round(
+                                                rows["lmhead_argmax_152064x3584"]["us"], 3)}
+    log(f"row lmhead verify N=5: {rows['lmhead_verify_N5_152064x3584']}")
     del copies, wp
 
     # small-N verify over the 196 decode matrices (weights read once per call), one

@@ -176,6 +176,23 @@ int lmhead_argmax(const void* w_packed_q8_0, const float* x, int64_t M, int64_t 
                   void* workspace, size_t workspace_bytes,
                   int32_t* out_index, float* out_value, qg_stream_t stream);
 
+/*
+ * Batched greedy verification on the LM head ("Why Local LLMs Don't Need C++ or
+ * Python", section 2: projection and argmax fused on the device, one int32 per
+ * decision; section 4: the candidate tokens are verified in one batched pass over
+ * the weights). For each column n < N of X (column-major K x N, ldx >= K, a
+ * multiple of 4): out_index[n] = min{ i : logit_{i,n} = max_j logit_{j,n} } and,
+ * if out_value is not NULL, out_value[n] = that logit, with logits = W X[:, n] and
+ * W an M x K Q8_0 matrix in packed layout. 1 <= N <= QG_SMALLN_MAX, K % 256 == 0.
+ * The weights are read once for all N columns and no logit reaches HBM. Needs
+ * lmhead_argmax_verify_workspace_bytes(M, K, N) bytes of workspace (8 bytes per
+ * 16-row tile and column, left zero). NaN logits never win.
+ */
+size_t lmhead_argmax_verify_workspace_bytes(int64_t M, int64_t K, int64_t N);
+int lmhead_argmax_verify(const void* w_packed_q8_0, const float* X, int64_t ldx, int64_t M, int64_t K, int64_t N,
+                         void* workspace, size_t workspace_bytes,
+                         int32_t* out_index, float* out_value, qg_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

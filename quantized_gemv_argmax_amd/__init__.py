@@ -60,6 +60,8 @@ _SIGS = {
     "qgemm_q4k_smalln": (_I, [_P, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
     "qgemm_q4k_smalln_batch_workspace_bytes": (_SZ, [ctypes.POINTER(_GemmProblem), _I]),
     "qgemm_q4k_smalln_batch": (_I, [ctypes.POINTER(_GemmProblem), _I, _P, _SZ, _P]),
+    "lmhead_argmax_verify_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "lmhead_argmax_verify": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P, _P, _P]),
     "lmhead_argmax_workspace_bytes": (_SZ, [_I64, _I64]),
     "lmhead_argmax": (_I, [_P, _P, _I64, _I64, _P, _SZ, _P, _P, _P]),
 }
@@ -271,3 +273,20 @@ def lmhead_argmax(w: torch.Tensor, x: torch.Tensor, M: int, K: int, out_index: t
     _check("lmhead_argmax", lib().lmhead_argmax(_ptr(w), _ptr(x), M, K, ws.ptr(), ws.nbytes(), _ptr(out_index),
                                                   _ptr(out_value), _stream(x.device)))
     return out_index, out_value
+
+
+def lmhead_argmax_verify(w: torch.Tensor, X: torch.Tensor, M: int, K: int, out_index: torch.Tensor | None = None,
+                         out_value: torch.Tensor | None = None, ws: Workspace | None = None):
+    """Batched greedy verification on a Q8_0 LM head. X: fp32 (N, ldx), row n = column n.
+    Returns (index int32[N], value float32[N]) device tensors."""
+    _need_cuda(w, X, out_index, out_value)
+    N, ldx = X.shape
+    if X.stride(1) != 1 or X.stride(0) != ldx:
+        raise ValueError("X must be a contiguous (N, ldx) tensor")
+    oi = out_index if out_index is not None else torch.empty(N, dtype=torch.int32, device=X.device)
+    ov = out_value if out_value is not None else torch.empty(N, dtype=torch.float32, device=X.device)
+    need = int(lib().lmhead_argmax_verify_workspace_bytes(M, K, N))
+    ws = _ws(ws, need, X.device)
+    _check("lmhead_argmax_verify", lib().lmhead_argmax_verify(_ptr(w), _ptr(X), ldx, M, K, N, ws.ptr(), ws.nbytes(),
+                                                              _ptr(oi), _ptr(ov), _stream(X.device)))
+    return oi, ov

@@ -44,10 +44,6 @@ namespace {
 
 constexpr int T = QG_TILE_ROWS;
 
-typedef _Float16 qg_h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 qg_h2 __attribute__((ext_vector_type(2)));
-typedef float qg_f4 __attribute__((ext_vector_type(4)));
-
 struct SnProb {
     const uint8_t* w;
     const float* X;
@@ -78,10 +74,8 @@ struct SnIn {
 // an offset beyond the resource's range: the hardware returns zeros for them
 // without a memory access (their products land in output columns that are not
 // stored).
-typedef unsigned int qg_u4v __attribute__((ext_vector_type(4)));
-typedef unsigned int qg_u2v __attribute__((ext_vector_type(2)));
-constexpr uint32_t kOutOfRange = 0x80000000u;  // >= every resource size used here
-constexpr int kNonTemporal = 2;                 // buffer-load cache policy: nt
+constexpr uint32_t kOutOfRange = kQgOutOfRange;
+constexpr int kNonTemporal = kQgNonTemporal;
 
 template <int C, int TW>
 struct SnLane {
@@ -123,36 +117,18 @@ QG_DEV void load_x(SnIn<C, TW>& d, __amdgpu_buffer_rsrc_t xr, const SnLane<C, TW
         }
 }
 
-QG_DEV uint32_t pk_rne(float a, float b) {
-    const qg_h2 h = {(_Float16)a, (_Float16)b};
-    return __builtin_bit_cast(uint32_t, h);
-}
-
-// Eight activations in the masked-dword order 0, 2, 1, 3, 4, 6, 5, 7, as fp16.
-QG_DEV qg_h8 a_operand(const float4 lo, const float4 hi) {
-    uint4 r;
-    r.x = pk_rne(lo.x, lo.z);
-    r.y = pk_rne(lo.y, lo.w);
-    r.z = pk_rne(hi.x, hi.z);
-    r.w = pk_rne(hi.y, hi.w);
-    return __builtin_bit_cast(qg_h8, r);
-}
-
-// Byte k of a packed word, as float.
-QG_DEV float byte_f(uint32_t v, int k) { return (float)((v >> (8 * k)) & 0xffu); }
-
 template <int C, int TW>
 QG_DEV void unit_dot(qg_f4 (&acc)[TW][C], const SnIn<C, TW>& d, int u) {
     const int g = u & 3;  // sub-blocks 2g (low nibbles) and 2g + 1 (high nibbles)
-    const qg_h8 ones = __builtin_bit_cast(qg_h8, make_uint4(0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u));
+    const qg_h8 ones = qg_ones_h8();
     const qg_f4 zero = {0.f, 0.f, 0.f, 0.f};
     // activations and their sub-block sums, shared by the TW tiles
     qg_h8 a_lo[C], a_hi[C];
     qg_f4 x_lo[C], x_hi[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        a_lo[c] = a_operand(d.x[0][c][0], d.x[0][c][1]);
-        a_hi[c] = a_operand(d.x[1][c][0], d.x[1][c][1]);
+        a_lo[c] = qg_a_operand(d.x[0][c][0], d.x[0][c][1]);
+        a_hi[c] = qg_a_operand(d.x[1][c][0], d.x[1][c][1]);
         x_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[c], ones, zero, 0, 0, 0);
         x_hi[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[c], ones, zero, 0, 0, 0);
     }
@@ -169,10 +145,10 @@ QG_DEV void unit_dot(qg_f4 (&acc)[TW][C], const SnIn<C, TW>& d, int u) {
         const uint32_t scw = qg_opaque(g < 2 ? sc03 : sc47);
         const uint32_t mw = qg_opaque(g < 2 ? m03 : m47);
         const int kb = 2 * (g & 1);
-        const float s_lo = dd * byte_f(scw, kb);
-        const float s_hi = dd * 0.0625f * byte_f(scw, kb + 1);
-        const float m_lo = dm * byte_f(mw, kb);
-        const float m_hi = dm * byte_f(mw, kb + 1);
+        const float s_lo = dd * qg_byte_f(scw, kb);
+        const float s_hi = dd * 0.0625f * qg_byte_f(scw, kb + 1);
+        const float m_lo = dm * qg_byte_f(mw, kb);
+        const float m_hi = dm * qg_byte_f(mw, kb + 1);
 
         const uint32_t w0 = d.q[t].x, w1 = d.q[t].y;
         const uint32_t w0s = w0 >> 8, w1s = w1 >> 8;
@@ -221,14 +197,14 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
         const int tc = min(tile0 + t, P.tiles - 1);
         tl.rt[t] = min(T, P.M - tc * T);
         tl.w[t] = __builtin_amdgcn_make_buffer_rsrc((void*)(P.w + (size_t)tc * T * P.nb * 144), (short)0,
-                                                    tl.rt[t] * P.nb * 144, 0x00020000);
+                                                    tl.rt[t] * P.nb * 144, kQgRawBufferFlags);
         const uint32_t r = (uint32_t)min(i, tl.rt[t] - 1);
         ln.hdr[t] = 16 * r;
         ln.q[t] = 16 * r + 8 * (s & 1) + (uint32_t)(s >> 1) * 16 * tl.rt[t];
     }
     // activations: column n = 16 c + i of X, this lane's 8-element K slice
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)P.X, (short)0, (int)(((int64_t)(P.N - 1) * P.ldx + (int64_t)P.nb * 256) * 4), 0x00020000);
+        (void*)P.X, (short)0, (int)(((int64_t)(P.N - 1) * P.ldx + (int64_t)P.nb * 256) * 4), kQgRawBufferFlags);
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int n = 16 * c + i;

@@ -255,3 +255,42 @@ QG_DEV bool qg_splitk_combine(float& v, unsigned long long* slot, int64_t stride
     }
     return true;
 }
+
+// ---------------------------------------------------------------------------
+// fp16 matrix-core operands (v_mfma_f32_16x16x32_f16: lane l holds
+// A[l % 16][8 (l / 16) + 0..7], B[8 (l / 16) + 0..7][l % 16] and
+// D[4 (l / 16) + e][l % 16], e = 0..3).
+typedef _Float16 qg_h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 qg_h2 __attribute__((ext_vector_type(2)));
+typedef float qg_f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int qg_u4v __attribute__((ext_vector_type(4)));
+typedef unsigned int qg_u2v __attribute__((ext_vector_type(2)));
+
+// Two floats as an fp16 pair, rounded to nearest even.
+QG_DEV uint32_t qg_pk_rne(float a, float b) {
+    const qg_h2 h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Eight consecutive activations as an fp16 matrix-core operand in the order the
+// masked quant dwords use: elements 0, 2, 1, 3, 4, 6, 5, 7 (bytes 0 and 2 of a
+// dword, then bytes 1 and 3, of each of two dwords).
+QG_DEV qg_h8 qg_a_operand(const float4 lo, const float4 hi) {
+    const uint4 r = make_uint4(qg_pk_rne(lo.x, lo.z), qg_pk_rne(lo.y, lo.w), qg_pk_rne(hi.x, hi.z),
+                               qg_pk_rne(hi.y, hi.w));
+    return __builtin_bit_cast(qg_h8, r);
+}
+
+// All-ones fp16 operand: a product with it sums the other operand over K.
+QG_DEV qg_h8 qg_ones_h8() {
+    return __builtin_bit_cast(qg_h8, make_uint4(0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u));
+}
+
+// Byte k of a packed word, as float.
+QG_DEV float qg_byte_f(uint32_t v, int k) { return (float)((v >> (8 * k)) & 0xffu); }
+
+// Buffer-resource constants: raw buffer loads past a resource's range return
+// zeros without a memory access; the cache policy bit marks streamed loads.
+constexpr uint32_t kQgOutOfRange = 0x80000000u;  // >= every resource size used here
+constexpr int kQgNonTemporal = 2;
+constexpr int kQgRawBufferFlags = 0x00020000;

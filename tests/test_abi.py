@@ -122,3 +122,17 @@ def test_valid_call_without_gpu_reports_device_error(L):
         pytest.skip("GPU present")
     st = L.qgemv_q4k(C, A, B, 64, 256, None, 0, None)
     assert st in (EDEV, EUNSUP)
+
+
+def test_verify_validation(L):
+    f = L.lmhead_argmax_verify
+    out = 0x40000
+    assert f(C, A, 512, 64, 500, 5, B, 1 << 20, out, None, None) == ESHAPE   # K % 256
+    assert f(C, A, 512, 64, 512, 0, B, 1 << 20, out, None, None) == ESHAPE   # N = 0
+    assert f(C, A, 512, 64, 512, 33, B, 1 << 20, out, None, None) == ESHAPE  # N > 32
+    assert f(C, A, 500, 64, 512, 5, B, 1 << 20, out, None, None) == ESHAPE   # ldx < K
+    assert f(C, A, 512, 64, 512, 5, None, 0, out, None, None) == EWS
+    assert f(C, A, 512, 64, 512, 5, B, 1 << 20, None, None, None) == ENULL
+    # 4 tiles x 5 columns x 8 bytes, rounded up to 256
+    assert L.lmhead_argmax_verify_workspace_bytes(64, 512, 5) == 256
+    assert L.lmhead_argmax_verify_workspace_bytes(152064, 3584, 5) == 152064 // 16 * 5 * 8

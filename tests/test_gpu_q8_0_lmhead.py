@@ -140,3 +140,71 @@ def test_lmhead_leaves_workspace_zero():
     gi, ri = int(idx.item()), oracle.argmax(yr)
     tol = oracle.tolerance(ar)
     assert gi == ri or yr[gi] >= yr[ri] - tol[gi] - tol[ri]
+
+
+def check_verify(W, M, K, X, what, ws=None):
+    """lmhead_argmax_verify against the oracle, column by column (same band rule
+    as the single-column LM head)."""
+    N = X.shape[0]
+    case(f"lmhead_argmax_verify {what} M={M} K={K} N={N}")
+    wp = packed_q8_0(W, M, K)
+    idx, val = qg.lmhead_argmax_verify(wp, to_dev(X), M, K, ws=ws)
+    torch.cuda.synchronize()
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    exact = 0
+    for n in range(N):
+        yr, ar = oracle.gemv_q8_0(W, M, K, X[n])
+        gi, ri = int(idx[n]), oracle.argmax(yr)
+        tol = oracle.tolerance(ar)
+        srt = np.sort(yr)
+        gap = srt[-1] - srt[-2] if M > 1 else np.inf
+        if gap > tol[ri]:
+            assert gi == ri, (what, n, gi, ri, gap)
+        else:
+            assert yr[gi] >= yr[ri] - tol[gi] - tol[ri], (what, n, gi, ri)
+        assert abs(float(val[n]) - yr[gi]) <= tol[gi], (what, n, float(val[n]), yr[gi])
+        exact += gi == ri
+    return exact
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 256, 1), (200, 256, 5), (1000, 3584, 5), (4097, 512, 17), (63, 1024, 32),
+                                   (3000, 768, 16)])
+def test_verify_small(M, K, N):
+    W = workloads.q8_0_blocks(M, K, key=(24, M, K))
+    X = workloads.x_columns(K, N, key=(24, M, K, N))
+    check_verify(W, M, K, X, "small")
+
+
+def test_verify_constructed_ties_per_column():
+    # constant-quant rows, column n = (n + 1) * ones: logit_{r,n} = d K c_r (n + 1);
+    # the maximum is tied between rows 1, 3, 4: every column must return 1
+    K, N = 256, 5
+    c = np.array([5, 9, -3, 9, 9, 0, 8] * 20)
+    M = len(c)
+    W = np.stack([np.concatenate([enc.q8_0_block(0x3400, [cr] * 32) for _ in range(K // 32)]) for cr in c])
+    X = np.stack([np.full(K, n + 1, np.float32) for n in range(N)])
+    case("lmhead_argmax_verify ties")
+    idx, val = qg.lmhead_argmax_verify(packed_q8_0(W, M, K), to_dev(X), M, K)
+    assert idx.cpu().tolist() == [1] * N
+    assert val.cpu().tolist() == [0.25 * K * 9 * (n + 1) for n in range(N)]
+
+
+def test_verify_vocab_152064_n5():
+    """Full LM-head shape, five columns in one pass; a column is redrawn while its
+    oracle top-2 gap is below 1e-3. The workspace is left zero."""
+    M, K, N = workloads.VOCAB, workloads.HIDDEN, 5
+    W = workloads.q8_0_blocks(M, K, key=(4, 0))
+    cols = []
+    for n in range(N):
+        r = 0
+        while True:
+            x = workloads.x_vector(K, key=(4, 2, n, r))
+            s = np.sort(oracle.gemv_q8_0(W, M, K, x)[0])
+            if s[-1] - s[-2] >= 1e-3:
+                break
+            r += 1
+        cols.append(x)
+    ws = qg.Workspace(DEV)
+    exact = check_verify(W, M, K, np.stack(cols), "vocab", ws=ws)
+    assert int(ws.buf.count_nonzero()) == 0
+    print(f"exact-match rate {exact}/{N}")
