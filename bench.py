@@ -257,7 +257,8 @@ def main():
 def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     """Each of the other hot-path kernels a few times, every call on its own weight
     copy, in this order: 4096x4096 Q4_K GEMV (3 calls), Q8_0 11008x4096 and
-    4096x11008 (3 each), LM head + argmax 152064x3584 (2), small-N N=5 then N=32 over
+    4096x11008 (3 each), LM head + argmax 152064x3584 (2), the same head verifying 5
+    columns (2), small-N N=5 then N=32 over
     the layers' stages (one grouped launch per stage)."""
     M, K = 4096, 4096
     W = wl.q4k_blocks(M, K, key=(1, 0))
@@ -278,9 +279,13 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     wp = qg.pack_q8_0(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
     del W
     x = torch.from_numpy(wl.x_vector(K, key=(4, 0))).to(dev)
-    for c in (wp, wp.clone()):
+    copies = (wp, wp.clone())
+    for c in copies:
         qg.lmhead_argmax(c, x, M, K, ws=ws)
-    del wp
+    X5 = torch.from_numpy(wl.x_columns(K, 5, key=(4, 3))).to(dev)
+    for c in copies:
+        qg.lmhead_argmax_verify(c, X5, M, K, ws=ws)
+    del wp, copies
     for N in (5, 32):
         for L in range(n_layers):
             for st in wl.LAYER_STAGES:
