@@ -39,24 +39,26 @@ struct VaProb {
     int32_t M, nmb, N, tiles;
 };
 
-// Inputs of one unit: blocks 2g and 2g + 1 of macro-block mb (u = 4 mb + g).
-template <int C>
+// Inputs of one unit: blocks 2g and 2g + 1 of macro-block mb (u = 4 mb + g) of
+// TW consecutive tiles, which share the unit's activations.
+template <int C, int TW>
 struct VaIn {
-    uint4 sc;            // the eight fp16 block scales of this lane's row
-    uint2 q[2];          // quants 8 (l / 16)..+7 of blocks 2g and 2g + 1
+    uint4 sc[TW];        // the eight fp16 block scales of this lane's row
+    uint2 q[TW][2];      // quants 8 (l / 16)..+7 of blocks 2g and 2g + 1
     float4 x[2][C][2];   // [block][column block][first / second 4 activations]
 };
 
+template <int C, int TW>
 struct VaLane {
-    uint32_t sc, q;  // byte offsets of this lane's scale segment / quant bytes
-    uint32_t x[2];   // per column block: byte offset of this lane's activations
+    __amdgpu_buffer_rsrc_t w[TW];  // one tile each
+    int32_t rt[TW];                // rows of the tile
+    uint32_t sc[TW], q[TW];        // byte offsets of this lane's scale segment / quant bytes
+    uint32_t x[C];                 // per column block: byte offset of this lane's activations
 };
 
-template <int C>
-QG_DEV void load_unit(VaIn<C>& d, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t xr, const VaLane& ln, int rt,
-                      int u) {
+template <int C, int TW>
+QG_DEV void load_unit(VaIn<C, TW>& d, __amdgpu_buffer_rsrc_t xr, const VaLane<C, TW>& ln, int u) {
     const int mb = u >> 2, g = u & 3;
-    const int base = mb * 17 * 16 * rt;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -65,38 +67,51 @@ QG_DEV void load_unit(VaIn<C>& d, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsr
             d.x[h][c][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, ln.x[c], so, 0));
             d.x[h][c][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, ln.x[c], so + 16, 0));
         }
-    // the scales serve the four units of the macro-block: a cached load
-    const qg_u4v s = __builtin_amdgcn_raw_buffer_load_b128(wr, ln.sc, base, 0);
-    d.sc = make_uint4(s.x, s.y, s.z, s.w);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        // block k = 2g + h: segment 1 + 2k + (l / 32)
-        const qg_u2v q =
-            __builtin_amdgcn_raw_buffer_load_b64(wr, ln.q, base + (1 + 2 * (2 * g + h)) * 16 * rt, kQgNonTemporal);
-        d.q[h] = make_uint2(q.x, q.y);
+    for (int t = 0; t < TW; ++t) {
+        const int base = mb * 17 * 16 * ln.rt[t];
+        // the scales serve the four units of the macro-block: a cached load
+        const qg_u4v s = __builtin_amdgcn_raw_buffer_load_b128(ln.w[t], ln.sc[t], base, 0);
+        d.sc[t] = make_uint4(s.x, s.y, s.z, s.w);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // block k = 2g + h: segment 1 + 2k + (l / 32)
+            const qg_u2v q = __builtin_amdgcn_raw_buffer_load_b64(
+                ln.w[t], ln.q[t], base + (1 + 2 * (2 * g + h)) * 16 * ln.rt[t], kQgNonTemporal);
+            d.q[t][h] = make_uint2(q.x, q.y);
+        }
     }
 }
 
-template <int C>
-QG_DEV void unit_dot(qg_f4 (&acc)[C], const VaIn<C>& d, int u) {
+template <int C, int TW>
+QG_DEV void unit_dot(qg_f4 (&acc)[TW][C], const VaIn<C, TW>& d, int u) {
     const int g = u & 3;
     const qg_h8 ones = qg_ones_h8();
     const qg_f4 zero = {0.f, 0.f, 0.f, 0.f};
-    const uint32_t dw = g == 0 ? d.sc.x : g == 1 ? d.sc.y : g == 2 ? d.sc.z : d.sc.w;  // scales of blocks 2g, 2g+1
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const float dk = h ? qg_half_hi(dw) : qg_half_lo(dw);
-        const float d24 = dk * 16777216.0f, dx = -128.0f * dk;
-        const uint32_t w0 = d.q[h].x ^ 0x80808080u, w1 = d.q[h].y ^ 0x80808080u;
-        const qg_h8 b = __builtin_bit_cast(
-            qg_h8, make_uint4(w0 & 0x00ff00ffu, (w0 >> 8) & 0x00ff00ffu, w1 & 0x00ff00ffu, (w1 >> 8) & 0x00ff00ffu));
+        qg_h8 a[C];
+        qg_f4 xs[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const qg_h8 a = qg_a_operand(d.x[h][c][0], d.x[h][c][1]);
-            const qg_f4 sp = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, zero, 0, 0, 0);
-            const qg_f4 xs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, zero, 0, 0, 0);
+            a[c] = qg_a_operand(d.x[h][c][0], d.x[h][c][1]);
+            xs[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[c], ones, zero, 0, 0, 0);
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[c][e] = fmaf(d24, sp[e], fmaf(dx, xs[e], acc[c][e]));
+        for (int t = 0; t < TW; ++t) {
+            // scales of blocks 2g, 2g + 1
+            const uint32_t dw = g == 0 ? d.sc[t].x : g == 1 ? d.sc[t].y : g == 2 ? d.sc[t].z : d.sc[t].w;
+            const float dk = h ? qg_half_hi(dw) : qg_half_lo(dw);
+            const float d24 = dk * 16777216.0f, dx = -128.0f * dk;
+            const uint32_t w0 = d.q[t][h].x ^ 0x80808080u, w1 = d.q[t][h].y ^ 0x80808080u;
+            const qg_h8 b = __builtin_bit_cast(qg_h8, make_uint4(w0 & 0x00ff00ffu, (w0 >> 8) & 0x00ff00ffu,
+                                                                 w1 & 0x00ff00ffu, (w1 >> 8) & 0x00ff00ffu));
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const qg_f4 sp = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[c], b, zero, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[t][c][e] = fmaf(d24, sp[e], fmaf(dx, xs[c][e], acc[t][c][e]));
+            }
         }
     }
 }
@@ -105,22 +120,28 @@ QG_DEV void unit_dot(qg_f4 (&acc)[C], const VaIn<C>& d, int u) {
 // lower index; NaN and missing rows carry -inf and INT_MAX and never win.
 QG_DEV bool va_better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 
-template <int C, int W>
+template <int C, int TW, int W>
 __global__ __launch_bounds__(64 * W) void lmhead_verify_tile_kernel(VaProb P) {
-    const int tile = blockIdx.x;
+    const int tile0 = blockIdx.x * TW;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15, s = lane >> 4;
-    const int rt = min(T, P.M - tile * T);
-    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(P.w + (size_t)tile * T * P.nmb * 8 * 34), (short)0, rt * P.nmb * 8 * 34, kQgRawBufferFlags);
     const int K = P.nmb * 256;
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)P.X, (short)0, (int)(((int64_t)(P.N - 1) * P.ldx + K) * 4), kQgRawBufferFlags);
-    VaLane ln;
-    const uint32_t r = (uint32_t)min(i, rt - 1);  // rows past a ragged tile re-read the last row
-    ln.sc = 16 * r;
-    ln.q = 16 * r + 8 * (s & 1) + (uint32_t)(s >> 1) * 16 * rt;
+    VaLane<C, TW> ln;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+        // a tile past the matrix end re-reads the last tile, rows past a ragged
+        // tile's end its last row; their results are dropped
+        const int tc = min(tile0 + t, P.tiles - 1);
+        ln.rt[t] = min(T, P.M - tc * T);
+        ln.w[t] = __builtin_amdgcn_make_buffer_rsrc((void*)(P.w + (size_t)tc * T * P.nmb * 8 * 34), (short)0,
+                                                    ln.rt[t] * P.nmb * 8 * 34, kQgRawBufferFlags);
+        const uint32_t r = (uint32_t)min(i, ln.rt[t] - 1);
+        ln.sc[t] = 16 * r;
+        ln.q[t] = 16 * r + 8 * (s & 1) + (uint32_t)(s >> 1) * 16 * ln.rt[t];
+    }
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int n = 16 * c + i;
@@ -129,69 +150,79 @@ __global__ __launch_bounds__(64 * W) void lmhead_verify_tile_kernel(VaProb P) {
 
     const int units = P.nmb * 4;
     const int niter = (units - wave + W - 1) / W;  // units wave, wave + W, ...
-    qg_f4 acc[C];
+    qg_f4 acc[TW][C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) acc[c] = qg_f4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[t][c] = qg_f4{0.f, 0.f, 0.f, 0.f};
     // ping-pong over pairs of units with unconditional, clamped loads and a
     // single-exit loop, so every wait count is exact
     if (niter > 0) {
         const int ulast = wave + W * (niter - 1);
-        VaIn<C> b0, b1;
-        load_unit<C>(b0, wr, xr, ln, rt, wave);
+        VaIn<C, TW> b0, b1;
+        load_unit<C, TW>(b0, xr, ln, wave);
         int it = 0;
         for (; it + 2 <= niter; it += 2) {
             const int u0 = wave + W * it;
-            load_unit<C>(b1, wr, xr, ln, rt, u0 + W);
+            load_unit<C, TW>(b1, xr, ln, u0 + W);
             __builtin_amdgcn_sched_barrier(0);
-            unit_dot<C>(acc, b0, u0);
-            load_unit<C>(b0, wr, xr, ln, rt, min(u0 + 2 * W, ulast));
+            unit_dot<C, TW>(acc, b0, u0);
+            load_unit<C, TW>(b0, xr, ln, min(u0 + 2 * W, ulast));
             __builtin_amdgcn_sched_barrier(0);
-            unit_dot<C>(acc, b1, u0 + W);
+            unit_dot<C, TW>(acc, b1, u0 + W);
         }
-        if (it < niter) unit_dot<C>(acc, b0, wave + W * it);
+        if (it < niter) unit_dot<C, TW>(acc, b0, wave + W * it);
     }
     if constexpr (W > 1) {
-        __shared__ float red[W][C * 4][64];
+        __shared__ float red[W][TW * C * 4][64];
 #pragma unroll
-        for (int c = 0; c < C; ++c)
+        for (int t = 0; t < TW; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) red[wave][4 * c + e][lane] = acc[c][e];
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) red[wave][(t * C + c) * 4 + e][lane] = acc[t][c][e];
         __syncthreads();
         if (wave != 0) return;
+#pragma unroll
+        for (int t = 0; t < TW; ++t)
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float v = red[0][(t * C + c) * 4 + e][lane];
+#pragma unroll
+                    for (int w = 1; w < W; ++w) v += red[w][(t * C + c) * 4 + e][lane];
+                    acc[t][c][e] = v;
+                }
+    }
+    // lane (i, s) holds row i of each tile, columns 16 c + 4 s + e: reduce over rows
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+        if (tile0 + t >= P.tiles) break;  // wavefront-uniform
 #pragma unroll
         for (int c = 0; c < C; ++c)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float v = red[0][4 * c + e][lane];
+                float v = acc[t][c][e];
+                int idx = (tile0 + t) * T + i;
+                if (i >= ln.rt[t] || !(v == v)) {
+                    v = -__builtin_huge_valf();
+                    idx = INT_MAX;
+                }
 #pragma unroll
-                for (int w = 1; w < W; ++w) v += red[w][4 * c + e][lane];
-                acc[c][e] = v;
+                for (int off = 8; off >= 1; off >>= 1) {
+                    const float ov = __shfl_xor(v, off, 64);
+                    const int oi = __shfl_xor(idx, off, 64);
+                    if (va_better(ov, oi, v, idx)) {
+                        v = ov;
+                        idx = oi;
+                    }
+                }
+                const int n = 16 * c + 4 * s + e;
+                if (i == 0 && n < P.N)
+                    P.partials[(int64_t)n * P.tiles + tile0 + t] = make_float2(v, __builtin_bit_cast(float, idx));
             }
     }
-    // lane (i, s) holds row i, columns 16 c + 4 s + e: reduce over the 16 rows
-#pragma unroll
-    for (int c = 0; c < C; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float v = acc[c][e];
-            int idx = tile * T + i;
-            if (i >= rt || !(v == v)) {
-                v = -__builtin_huge_valf();
-                idx = INT_MAX;
-            }
-#pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) {
-                const float ov = __shfl_xor(v, off, 64);
-                const int oi = __shfl_xor(idx, off, 64);
-                if (va_better(ov, oi, v, idx)) {
-                    v = ov;
-                    idx = oi;
-                }
-            }
-            const int n = 16 * c + 4 * s + e;
-            if (i == 0 && n < P.N)
-                P.partials[(int64_t)n * P.tiles + tile] = make_float2(v, __builtin_bit_cast(float, idx));
-        }
 }
 
 // Stage 2: workgroup n reduces column n's partials in a fixed order and clears them.
@@ -262,13 +293,13 @@ int va_validate(const void* w, const float* X, int64_t ldx, int64_t M, int64_t K
 
 size_t va_ws_bytes(int64_t M, int64_t N) { return qg::align_up((size_t)qg::ceil_div(M, T) * N * 8, 256); }
 
-template <int C>
+template <int C, int TW>
 void va_launch(const VaProb& P, int W, hipStream_t s) {
-    const dim3 grid(P.tiles);
+    const dim3 grid((unsigned)qg::ceil_div(P.tiles, TW));
     if (W == 8)
-        hipLaunchKernelGGL((lmhead_verify_tile_kernel<C, 8>), grid, dim3(512), 0, s, P);
+        hipLaunchKernelGGL((lmhead_verify_tile_kernel<C, TW, 8>), grid, dim3(512), 0, s, P);
     else
-        hipLaunchKernelGGL((lmhead_verify_tile_kernel<C, 4>), grid, dim3(256), 0, s, P);
+        hipLaunchKernelGGL((lmhead_verify_tile_kernel<C, TW, 4>), grid, dim3(256), 0, s, P);
 }
 
 }  // namespace
@@ -303,14 +334,25 @@ int lmhead_argmax_verify(const void* w, const float* X, int64_t ldx, int64_t M, 
     P.nmb = (int32_t)(K / 256);
     P.N = (int32_t)N;
     P.tiles = (int32_t)qg::ceil_div(M, T);
-    int W = P.nmb * 4 >= 16 ? 8 : 4;
-    int ew = 0, eu = 0;
-    if (qg::env_pair("QG_VA_CFG", &ew, &eu) && (ew == 4 || ew == 8)) W = ew;
+    // W wavefronts split K (four for two column blocks, whose registers allow fewer
+    // wavefronts per SIMD); TW tiles per workgroup share each unit's activations
+    // (two while that leaves at least 1024 workgroups)
+    int W = (P.nmb * 4 >= 16 && N <= 16) ? 8 : 4;
+    int TW = P.tiles >= 2048 ? 2 : 1;
+    int ew = 0, et = 0;
+    if (qg::env_pair("QG_VA_CFG", &ew, &et)) {
+        if (ew == 4 || ew == 8) W = ew;
+        if (et == 1 || et == 2 || (et == 4 && N <= 16)) TW = et;  // four tiles of two column blocks spill
+    }
     hipStream_t s = (hipStream_t)stream;
-    if (N > 16)
-        va_launch<2>(P, W, s);
-    else
-        va_launch<1>(P, W, s);
+    const int key = 10 * (N > 16 ? 2 : 1) + TW;
+    switch (key) {
+        case 11: va_launch<1, 1>(P, W, s); break;
+        case 12: va_launch<1, 2>(P, W, s); break;
+        case 14: va_launch<1, 4>(P, W, s); break;
+        case 21: va_launch<2, 1>(P, W, s); break;
+        default: va_launch<2, 2>(P, W, s); break;
+    }
     st = qg::launch_status("lmhead_argmax_verify (tiles)");
     if (st) return st;
     const int threads = (int)std::min<int64_t>(1024, std::max<int64_t>(64, qg::ceil_div(P.tiles, 8 * 64) * 64));

@@ -208,3 +208,15 @@ def test_verify_vocab_152064_n5():
     exact = check_verify(W, M, K, np.stack(cols), "vocab", ws=ws)
     assert int(ws.buf.count_nonzero()) == 0
     print(f"exact-match rate {exact}/{N}")
+
+
+@pytest.mark.parametrize("cfg", ["8,1", "8,2", "8,4", "4,2"])
+@pytest.mark.parametrize("N", [5, 20])
+def test_verify_launch_shapes(cfg, N, monkeypatch):
+    # every (wavefronts, tiles per workgroup) shape, with a tile count that is not a
+    # multiple of the tiles per workgroup and a ragged last tile
+    monkeypatch.setenv("QG_VA_CFG", cfg)
+    M, K = 1000, 1024
+    W = workloads.q8_0_blocks(M, K, key=(25, M))
+    X = workloads.x_columns(K, N, key=(25, N))
+    check_verify(W, M, K, X, f"shape {cfg}")
