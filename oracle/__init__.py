@@ -45,9 +45,11 @@ def lib():
         L.or_q4k_unpack_scales.argtypes = [_P, _P, _P]
         L.or_q4k_dequant_block.argtypes = [_P, _P]
         L.or_q8_0_dequant_block.argtypes = [_P, _P]
+        L.or_q6k_dequant_block.argtypes = [_P, _P]
         L.or_q4k_dequant_row.argtypes = [_P, _I64, _P]
         L.or_q8_0_dequant_row.argtypes = [_P, _I64, _P]
-        for name in ("or_gemv_q4k", "or_gemv_q8_0"):
+        L.or_q6k_dequant_row.argtypes = [_P, _I64, _P]
+        for name in ("or_gemv_q4k", "or_gemv_q8_0", "or_gemv_q6k"):
             getattr(L, name).argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P]
         L.or_gemv_q4k_factored.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
         L.or_gemm_q4k.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _P, _P]
@@ -107,6 +109,23 @@ def q8_0_dequant_block(blk) -> np.ndarray:
     return w
 
 
+def q6k_dequant_block(blk) -> np.ndarray:
+    b = np.ascontiguousarray(blk, dtype=np.uint8)
+    assert b.size == 210
+    w = np.zeros(256, np.float64)
+    lib().or_q6k_dequant_block(_ptr(b), _ptr(w))
+    return w
+
+
+def q6k_dequant(W, M: int, K: int) -> np.ndarray:
+    W = _u8(W)
+    assert W.size == M * (K // 256) * 210
+    out = np.zeros((M, K), np.float64)
+    for r in range(M):
+        lib().or_q6k_dequant_row(_ptr(W.reshape(M, -1)[r]), K, _ptr(out[r]))
+    return out
+
+
 def q4k_dequant(W, M: int, K: int) -> np.ndarray:
     W = _u8(W)
     assert W.size == M * (K // 256) * 144
@@ -146,6 +165,10 @@ def gemv_q4k(W, M: int, K: int, x, rows=None):
 
 def gemv_q8_0(W, M: int, K: int, x, rows=None):
     return _gemv(lib().or_gemv_q8_0, W, M, K, x, rows, (K // 32) * 34)
+
+
+def gemv_q6k(W, M: int, K: int, x, rows=None):
+    return _gemv(lib().or_gemv_q6k, W, M, K, x, rows, (K // 256) * 210)
 
 
 def gemv_q4k_factored(W, M: int, K: int, x, rows=None) -> np.ndarray:

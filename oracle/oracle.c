@@ -78,12 +78,35 @@ void or_q8_0_dequant_block(const uint8_t blk[34], double w[32]) {
     for (int i = 0; i < 32; ++i) w[i] = d * (double)(int8_t)blk[2 + i];
 }
 
+/* 6-bit quant (0..63) of weight i (0..255) of a Q6_K block. */
+static int q6k_quant(const uint8_t* ql, const uint8_t* qh, int i) {
+    int h = i / 128;         /* 128-weight half: ql + 64h, qh + 32h */
+    int p = (i % 128) / 32;  /* quarter of the half */
+    int l = i % 32;
+    uint8_t lo_byte = ql[64 * h + l + 32 * (p % 2)];
+    int lo = (p < 2) ? (lo_byte & 15) : (lo_byte >> 4);
+    int hi = (qh[32 * h + l] >> (2 * p)) & 3;
+    return lo | (hi << 4);
+}
+
+void or_q6k_dequant_block(const uint8_t blk[210], double w[256]) {
+    const uint8_t* ql = blk;
+    const uint8_t* qh = blk + 128;
+    const int8_t* sc = (const int8_t*)(blk + 192);
+    double d = or_half_to_double(rd16(blk + 208));
+    for (int i = 0; i < 256; ++i) w[i] = d * sc[i / 16] * (q6k_quant(ql, qh, i) - 32);
+}
+
 void or_q4k_dequant_row(const uint8_t* row, int64_t K, double* w) {
     for (int64_t b = 0; b < K / 256; ++b) or_q4k_dequant_block(row + 144 * b, w + 256 * b);
 }
 
 void or_q8_0_dequant_row(const uint8_t* row, int64_t K, double* w) {
     for (int64_t b = 0; b < K / 32; ++b) or_q8_0_dequant_block(row + 34 * b, w + 32 * b);
+}
+
+void or_q6k_dequant_row(const uint8_t* row, int64_t K, double* w) {
+    for (int64_t b = 0; b < K / 256; ++b) or_q6k_dequant_block(row + 210 * b, w + 256 * b);
 }
 
 /* Plain dot product, sequential in k, of a dequantized row with x. */
@@ -125,6 +148,12 @@ void or_gemv_q8_0(const uint8_t* W, int64_t M, int64_t K, const float* x,
                   const int64_t* rows, int64_t nrows, double* y, double* a) {
     (void)M;
     gemv_dense(or_q8_0_dequant_row, (K / 32) * 34, W, K, x, rows, nrows, y, a);
+}
+
+void or_gemv_q6k(const uint8_t* W, int64_t M, int64_t K, const float* x,
+                 const int64_t* rows, int64_t nrows, double* y, double* a) {
+    (void)M;
+    gemv_dense(or_q6k_dequant_row, (K / 256) * 210, W, K, x, rows, nrows, y, a);
 }
 
 void or_gemv_q4k_factored(const uint8_t* W, int64_t M, int64_t K, const float* x,

@@ -19,6 +19,14 @@
  *     holds weight 64*g + l in its low nibble and weight 64*g + 32 + l in its
  *     high nibble.
  *   Q8_0 (34 B / 32 weights): fp16 d, 32 int8 q; weight i is d*q[i].
+ *   Q6_K (210 B / 256 weights; the third K-quant of the dotLLM README's news
+ *     entries, which the pages name without a layout): 128 bytes ql (low four
+ *     bits of each quant), 64 bytes qh (high two bits), 16 int8 sub-block
+ *     scales, fp16 d. Weight i is d*sc[i/16]*(q_i - 32), q_i its 6-bit quant.
+ *     In each 128-weight half h (ql + 64h, qh + 32h), for l < 32 and p < 4,
+ *     weight 128h + 32p + l takes its low four bits from byte ql[l + 32(p%2)]
+ *     (low nibble for p < 2, high nibble for p >= 2) and its high two bits from
+ *     bits 2p, 2p+1 of qh[l].
  * Compatibility of this reading with real GGUF files is parity unpinned (no
  * file, decoder or format document is available); the pins in the tests fix the
  * oracle to the reading itself.
@@ -38,13 +46,15 @@ double or_half_to_double(uint16_t h);
 /* Unpack the twelve 6-bit-field bytes of a Q4_K block into sc[8], m[8]. */
 void or_q4k_unpack_scales(const uint8_t s[12], int sc[8], int m[8]);
 
-/* Dequantize one block. w receives 256 (Q4_K) or 32 (Q8_0) doubles. */
+/* Dequantize one block. w receives 256 (Q4_K, Q6_K) or 32 (Q8_0) doubles. */
 void or_q4k_dequant_block(const uint8_t blk[144], double w[256]);
 void or_q8_0_dequant_block(const uint8_t blk[34], double w[32]);
+void or_q6k_dequant_block(const uint8_t blk[210], double w[256]);
 
 /* Dequantize a whole row of K weights (K/256 Q4_K or K/32 Q8_0 blocks). */
 void or_q4k_dequant_row(const uint8_t* row, int64_t K, double* w);
 void or_q8_0_dequant_row(const uint8_t* row, int64_t K, double* w);
+void or_q6k_dequant_row(const uint8_t* row, int64_t K, double* w);
 
 /*
  * y = W x for the rows listed in rows[0..nrows) (rows == NULL: rows 0..nrows-1).
@@ -56,6 +66,8 @@ void or_gemv_q4k(const uint8_t* W, int64_t M, int64_t K, const float* x,
                  const int64_t* rows, int64_t nrows, double* y, double* a);
 void or_gemv_q8_0(const uint8_t* W, int64_t M, int64_t K, const float* x,
                   const int64_t* rows, int64_t nrows, double* y, double* a);
+void or_gemv_q6k(const uint8_t* W, int64_t M, int64_t K, const float* x,
+                 const int64_t* rows, int64_t nrows, double* y, double* a);
 
 /*
  * Factored Q4_K form: per 32-weight sub-block, S = sum q*x and X = sum x, then

@@ -12,6 +12,7 @@ import os
 import numpy as np
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "q4k_q8_0_blocks.txt")
+GOLDEN_Q6K = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "q6k_blocks.txt")
 
 
 def half_bits(v) -> np.ndarray:
@@ -58,6 +59,64 @@ def q8_0_block(d_bits: int, q) -> np.ndarray:
     blk[0:2] = np.array([d_bits], dtype=np.uint16).view(np.uint8)
     blk[2:] = q.astype(np.int8).view(np.uint8)
     return blk
+
+
+def q6k_block(d_bits: int, sc, q) -> np.ndarray:
+    """Q6_K block from 16 int8 scales and 256 six-bit quants, built byte by byte:
+    ql byte b of half h = b // 64 holds (low nibble) the low bits of the quant of
+    weight 128h + 32(r // 32) + r % 32 and (high nibble) those of the weight 64
+    further, r = b % 64; qh byte b of half h = b // 32 packs, two bits each from
+    bit 0 up, the high bits of weights 128h + l, +32, +64, +96, l = b % 32."""
+    sc = np.asarray(sc, dtype=np.int64)
+    q = np.asarray(q, dtype=np.int64)
+    assert sc.shape == (16,) and sc.min() >= -128 and sc.max() <= 127
+    assert q.shape == (256,) and q.min() >= 0 and q.max() <= 63
+    blk = np.zeros(210, dtype=np.uint8)
+    for b in range(128):
+        h, r = divmod(b, 64)
+        first = 128 * h + 32 * (r // 32) + r % 32
+        blk[b] = (q[first] & 15) | ((q[first + 64] & 15) << 4)
+    for b in range(64):
+        h, l = divmod(b, 32)
+        v = 0
+        for p in range(4):
+            v |= (q[128 * h + 32 * p + l] >> 4) << (2 * p)
+        blk[128 + b] = v
+    blk[192:208] = sc.astype(np.int8).view(np.uint8)
+    blk[208:210] = np.array([d_bits], dtype=np.uint16).view(np.uint8)
+    return blk
+
+
+def q6k_weights(d: float, sc, q) -> np.ndarray:
+    """Weights straight from the parameters (no bytes involved)."""
+    j = np.arange(256) // 16
+    return d * np.asarray(sc, np.float64)[j] * (np.asarray(q, np.float64) - 32)
+
+
+def golden_q6k() -> dict:
+    """name -> dict(block=uint8[210], sum=float, w={index: value})."""
+    fields: dict[str, dict[str, str]] = {}
+    with open(GOLDEN_Q6K) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = (t.strip() for t in line.split("=", 1))
+            name, attr = key.split(".")
+            fields.setdefault(name, {})[attr] = val
+    out = {}
+    for name, fl in fields.items():
+        ql = _rule(fl["ql_rule"], 128)
+        qh = _rule(fl["qh_rule"], 64)
+        assert ql.min() >= 0 and ql.max() <= 255 and qh.min() >= 0 and qh.max() <= 255
+        blk = np.concatenate([ql.astype(np.uint8), qh.astype(np.uint8), _hex(fl["scales"]), _hex(fl["d"])])
+        assert blk.size == 210
+        w = {}
+        for item in fl["w"].split():
+            i, v = item.split(":")
+            w[int(i)] = float(v)
+        out[name] = {"block": blk, "sum": float(fl["sum"]), "w": w}
+    return out
 
 
 def q4k_weights(d: float, dmin: float, sc, m, q) -> np.ndarray:

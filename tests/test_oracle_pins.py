@@ -261,6 +261,81 @@ def test_q8_0_zero_scale():
 
 
 # ---------------------------------------------------------------- rows subset, small N
+# ---------------------------------------------------------------- Q6_K
+
+def random_q6k_params(rng):
+    d = float(np.float16(rng.uniform(0.001, 0.02)))
+    sc = rng.integers(-128, 128, 16)
+    q = rng.integers(0, 64, 256)
+    return d, sc, q
+
+
+@pytest.mark.parametrize("name", ["Q6A", "Q6B"])
+def test_q6k_golden_blocks(name):
+    g = enc.golden_q6k()[name]
+    w = oracle.q6k_dequant_block(g["block"])
+    assert w.sum() == g["sum"]
+    for i, v in g["w"].items():
+        assert w[i] == v, (name, i)
+
+
+def test_q6k_encoder_reproduces_golden_bytes():
+    # the golden bytes (hand-written rules) equal the encoder's output for the
+    # parameters they were derived from
+    G = enc.golden_q6k()
+    i = np.arange(256)
+    a = enc.q6k_block(0x3C00, np.arange(16) - 8, i % 64)
+    assert np.array_equal(a, G["Q6A"]["block"])
+    p, l = (i % 128) // 32, i % 32
+    b = enc.q6k_block(0x3800, np.ones(16, int), 16 * p + (l & 15))
+    assert np.array_equal(b, G["Q6B"]["block"])
+
+
+def test_q6k_encode_decode_random_blocks():
+    rng = np.random.default_rng(41)
+    for _ in range(100):
+        d, sc, q = random_q6k_params(rng)
+        blk = enc.q6k_block(enc.half_bits(d), sc, q)
+        assert np.array_equal(oracle.q6k_dequant_block(blk), enc.q6k_weights(d, sc, q))
+
+
+def test_q6k_extreme_quants_and_scales():
+    # q = 0 -> -32, q = 63 -> +31; scale -128 and 127
+    sc = np.array([-128, 127] * 8)
+    q = np.array([0, 63] * 128)
+    blk = enc.q6k_block(0x3C00, sc, q)
+    w = oracle.q6k_dequant_block(blk)
+    j = np.arange(256) // 16
+    assert np.array_equal(w, sc[j] * np.where(np.arange(256) % 2 == 0, -32.0, 31.0))
+
+
+def test_q6k_zero_scale_gives_zero():
+    rng = np.random.default_rng(42)
+    _, sc, q = random_q6k_params(rng)
+    assert np.all(oracle.q6k_dequant_block(enc.q6k_block(0, sc, q)) == 0)
+
+
+def test_q6k_bruteforce_tiny_matrices():
+    rng = np.random.default_rng(43)
+    for M, K in [(1, 256), (3, 512), (4, 256)]:
+        nb = K // 256
+        blocks, Wd = [], np.zeros((M, K))
+        for r in range(M):
+            row = []
+            for b in range(nb):
+                d, sc, q = random_q6k_params(rng)
+                row.append(enc.q6k_block(enc.half_bits(d), sc, q))
+                Wd[r, 256 * b:256 * (b + 1)] = enc.q6k_weights(d, sc, q)
+            blocks.append(np.concatenate(row))
+        W = np.stack(blocks)
+        x = rng.standard_normal(K).astype(np.float32)
+        y, a = oracle.gemv_q6k(W, M, K, x)
+        ref = Wd @ x.astype(np.float64)
+        aref = np.abs(Wd * x.astype(np.float64)).sum(axis=1)
+        assert np.allclose(y, ref, rtol=0, atol=1e-12 * aref.max())
+        assert np.allclose(a, aref, rtol=1e-13, atol=0)
+
+
 def test_row_subset_matches_full():
     M, K = 40, 512
     W = workloads.q4k_blocks(M, K, key=(95, 1))

@@ -81,6 +81,21 @@ def q4k_blocks(M: int, K: int, key=(0,)) -> np.ndarray:
     return out.reshape(M, nb * Q4K_BLOCK_BYTES)
 
 
+def q6k_blocks(M: int, K: int, key=(0,)) -> np.ndarray:
+    """Random canonical Q6_K matrix: uint8 array of shape (M, K // 256 * 210), row-major.
+    The 128 + 64 quant bytes and the 16 scale bytes are uniform random bytes (so the
+    6-bit quants are i.i.d. U{0..63} and the int8 scales U{-128..127}); d is fp16
+    ~U(0.001, 0.02), stored in the block's last two bytes."""
+    if K % Q4K_BLOCK_WEIGHTS:
+        raise ValueError("K must be a multiple of 256 for Q6_K")
+    nb = K // Q4K_BLOCK_WEIGHTS
+    rng = rng_for(*key, ROLE_W)
+    out = rng.integers(0, 256, size=(M, nb, 210), dtype=np.uint8)
+    d = _fp16_bits(rng, M * nb).reshape(M, nb)
+    out[:, :, 208:210] = d.astype(np.uint16)[..., None].view(np.uint8)
+    return out.reshape(M, nb * 210)
+
+
 def q8_0_blocks(M: int, K: int, key=(0,)) -> np.ndarray:
     """Random canonical Q8_0 matrix: uint8 array of shape (M, K // 32 * 34), row-major."""
     if K % Q8_0_BLOCK_WEIGHTS:
