@@ -259,7 +259,8 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     copy, in this order: 4096x4096 Q4_K GEMV (3 calls), Q8_0 11008x4096 and
     4096x11008 (3 each), LM head + argmax 152064x3584 (2), the same head verifying 5
     columns (2), small-N N=5 then N=32 over
-    the layers' stages (one grouped launch per stage)."""
+    the layers' stages (one grouped launch per stage), Q6_K 3584x18944 (3) and
+    152064x3584 (2)."""
     M, K = 4096, 4096
     W = wl.q4k_blocks(M, K, key=(1, 0))
     wp = qg.pack_q4k(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
@@ -295,6 +296,15 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
                     X_ = torch.from_numpy(wl.x_columns(K_, N, key=(5, L, i, N))).to(dev)
                     grp.append((wp_, X_, torch.empty((N, (M_ + 3) // 4 * 4), device=dev), M_, K_))
                 qg.qgemm_q4k_smalln_batch(grp, ws=ws)
+    for (M, K), reps in [((wl.HIDDEN, wl.FFN), 3), ((wl.VOCAB, wl.HIDDEN), 2)]:
+        W = wl.q6k_blocks(M, K, key=(6, M))
+        wp = qg.pack_q6k(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
+        del W
+        x = torch.from_numpy(wl.x_vector(K, key=(6, M))).to(dev)
+        y = torch.empty(M, device=dev)
+        for c in [wp] + [wp.clone() for _ in range(reps - 1)]:
+            qg.qgemv_q6k(c, x, M, K, y=y, ws=ws)
+        del wp
     torch.cuda.synchronize()
     log("counter rows done")
 
@@ -342,6 +352,23 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
                                       "bytes": b, "copies_rotated": R}
         log(f"row q8_0 {M}x{K}: {rows[f'q8_0_gemv_{M}x{K}']}")
         del copies
+
+    # Q6_K GEMVs: the FFN down projection 3584x18944 (rotated copies) and the
+    # 152064x3584 output head (2 copies), the two Q6_K matrices of a Q4_K_M 7B file
+    for (M, K) in [(wl.HIDDEN, wl.FFN), (wl.VOCAB, wl.HIDDEN)]:
+        W = wl.q6k_blocks(M, K, key=(6, M))
+        wp = qg.pack_q6k(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
+        del W
+        R = max(2, -(-(1 << 30) // wp.numel()))
+        copies = rotated(wp, R)
+        x = torch.from_numpy(wl.x_vector(K, key=(6, M))).to(dev)
+        y = torch.empty(M, device=dev)
+        ms = graph_ms(torch, lambda: [qg.qgemv_q6k(c, x, M, K, y=y, ws=ws) for c in copies], 20) / R
+        b = wp.numel() + 4 * (M + K)
+        rows[f"q6k_gemv_{M}x{K}"] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                                     "bytes": b, "copies_rotated": R}
+        log(f"row q6k {M}x{K}: {rows[f'q6k_gemv_{M}x{K}']}")
+        del copies, wp
 
     # fused LM head + argmax 152064x3584 Q8_0, 2 copies
     M, K = wl.VOCAB, wl.HIDDEN

@@ -104,6 +104,26 @@ int qgemv_q4k(const void* w_packed, const float* x, float* y, int64_t M, int64_t
               void* workspace, size_t workspace_bytes, qg_stream_t stream);
 
 /*
+ * y[M] = W x[K], W an M x K Q6_K matrix in packed layout (qg_pack_q6k), x and y
+ * fp32. Q6_K is the third K-quant format the dotLLM README's CUDA decode GEMV
+ * covers (news entry on the CUDA backend; "Q4_K_M dequantization and vec_dot
+ * kernels"). Canonical block, 210 B per 256 weights (GGUF reading; the pages name
+ * the format but do not spell out its bytes): 128 bytes ql of low nibbles, 64
+ * bytes qh of two-bit high parts, 16 int8 sub-scales, fp16 d; weight k of
+ * sub-block j = k/16 is d * sc_j * (q_k - 32) with the six-bit q_k. Packed
+ * layout, tiles of 16 rows (rt in the last tile): segment s < 13 (16 bytes: the
+ * block's bytes 16s..16s+15) of super-block b of row i at
+ * tile_base + ((b*13 + s)*rt + i)*16, d at tile_base + nb*13*rt*16 + (b*rt + i)*2,
+ * tile_base = tile*16*nb*210. 1 <= M <= 2^31-17, K % 256 == 0, 256 <= K <= 2^24.
+ * Needs no workspace.
+ */
+size_t qg_q6k_bytes(int64_t M, int64_t K);
+int qg_pack_q6k(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t stream);
+size_t qgemv_q6k_workspace_bytes(int64_t M, int64_t K);
+int qgemv_q6k(const void* w_packed, const float* x, float* y, int64_t M, int64_t K,
+              void* workspace, size_t workspace_bytes, qg_stream_t stream);
+
+/*
  * Several independent Q4_K GEMVs in one launch (the dotLLM README's fused decode
  * dispatch of Q/K/V and of gate/up). Problems must not write overlapping outputs.
  * 1 <= count <= QG_MAX_BATCH. Each entry follows qgemv_q4k's rules.

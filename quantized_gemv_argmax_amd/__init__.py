@@ -47,8 +47,10 @@ _SIGS = {
     "qg_last_error": (ctypes.c_char_p, []),
     "qg_q4k_bytes": (_SZ, [_I64, _I64]),
     "qg_q8_0_bytes": (_SZ, [_I64, _I64]),
+    "qg_q6k_bytes": (_SZ, [_I64, _I64]),
     "qg_pack_q4k": (_I, [_P, _P, _I64, _I64, _P]),
     "qg_pack_q8_0": (_I, [_P, _P, _I64, _I64, _P]),
+    "qg_pack_q6k": (_I, [_P, _P, _I64, _I64, _P]),
     "qg_workspace_clear": (_I, [_P, _SZ, _P]),
     "qgemv_q4k_workspace_bytes": (_SZ, [_I64, _I64]),
     "qgemv_q4k": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
@@ -56,6 +58,8 @@ _SIGS = {
     "qgemv_q4k_batch": (_I, [ctypes.POINTER(_Problem), _I, _P, _SZ, _P]),
     "qgemv_q8_0_workspace_bytes": (_SZ, [_I64, _I64]),
     "qgemv_q8_0": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
+    "qgemv_q6k_workspace_bytes": (_SZ, [_I64, _I64]),
+    "qgemv_q6k": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "qgemm_q4k_smalln_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "qgemm_q4k_smalln": (_I, [_P, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
     "qgemm_q4k_smalln_batch_workspace_bytes": (_SZ, [ctypes.POINTER(_GemmProblem), _I]),
@@ -167,6 +171,10 @@ def q8_0_bytes(M: int, K: int) -> int:
     return int(lib().qg_q8_0_bytes(M, K))
 
 
+def q6k_bytes(M: int, K: int) -> int:
+    return int(lib().qg_q6k_bytes(M, K))
+
+
 def pack_q4k(canonical: torch.Tensor, M: int, K: int, out: torch.Tensor | None = None) -> torch.Tensor:
     """Repack canonical Q4_K bytes (uint8 device tensor) into the library's layout."""
     _need_cuda(canonical)
@@ -185,6 +193,17 @@ def pack_q8_0(canonical: torch.Tensor, M: int, K: int, out: torch.Tensor | None 
         raise ValueError(f"expected {n} uint8 bytes of Q8_0 blocks")
     out = out if out is not None else torch.empty(n, dtype=torch.uint8, device=canonical.device)
     _check("qg_pack_q8_0", lib().qg_pack_q8_0(_ptr(canonical), _ptr(out), M, K, _stream(canonical.device)))
+    return out
+
+
+def pack_q6k(canonical: torch.Tensor, M: int, K: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Repack canonical Q6_K bytes (uint8 device tensor) into the library's layout."""
+    _need_cuda(canonical)
+    n = q6k_bytes(M, K)
+    if canonical.numel() != n or canonical.dtype != torch.uint8:
+        raise ValueError(f"expected {n} uint8 bytes of Q6_K blocks")
+    out = out if out is not None else torch.empty(n, dtype=torch.uint8, device=canonical.device)
+    _check("qg_pack_q6k", lib().qg_pack_q6k(_ptr(canonical), _ptr(out), M, K, _stream(canonical.device)))
     return out
 
 
@@ -221,6 +240,17 @@ def qgemv_q8_0(w: torch.Tensor, x: torch.Tensor, M: int, K: int, y: torch.Tensor
     need = int(lib().qgemv_q8_0_workspace_bytes(M, K))
     ws = _ws(ws, need, x.device)
     _check("qgemv_q8_0", lib().qgemv_q8_0(_ptr(w), _ptr(x), _ptr(y), M, K, ws.ptr(), ws.nbytes(), _stream(x.device)))
+    return y
+
+
+def qgemv_q6k(w: torch.Tensor, x: torch.Tensor, M: int, K: int, y: torch.Tensor | None = None,
+              ws: Workspace | None = None) -> torch.Tensor:
+    """y[M] = W x for a packed Q6_K matrix (fp32 x, y)."""
+    _need_cuda(w, x, y)
+    y = y if y is not None else torch.empty(M, dtype=torch.float32, device=x.device)
+    need = int(lib().qgemv_q6k_workspace_bytes(M, K))
+    ws = _ws(ws, need, x.device)
+    _check("qgemv_q6k", lib().qgemv_q6k(_ptr(w), _ptr(x), _ptr(y), M, K, ws.ptr(), ws.nbytes(), _stream(x.device)))
     return y
 
 

@@ -294,3 +294,155 @@ QG_DEV float qg_byte_f(uint32_t v, int k) { return (float)((v >> (8 * k)) & 0xff
 constexpr uint32_t kQgOutOfRange = 0x80000000u;  // >= every resource size used here
 constexpr int kQgNonTemporal = 2;
 constexpr int kQgRawBufferFlags = 0x00020000;
+
+// ---------------------------------------------------------------------------
+// Q6_K: one 16-byte segment of low quant bits (ql: 4 dwords, 32 weights: the low
+// nibbles of run "lo", the high nibbles of run "hi", 64 weights further on) with
+// the matching 16 bytes of high bits (qh), against the activation pairs of lanes
+// LA (dwords 0, 1) and LB (dwords 2, 3). Each 6-bit quant is assembled in place
+// in its byte: low four bits from ql, bits 2PP..2PP+1 (run lo) or 2PP+4..2PP+5
+// (run hi) of qh as bits 4-5, by one bit-field insert with the 0x0F0F0F0F mask
+// `m4` (a scalar register: the insert has no literal form); masking bytes 0, 2 /
+// 1, 3 with 0x003F003F leaves two fp16 subnormals q * 2^-24. Accumulators: lo0 /
+// lo1 take bytes 0, 2 / 1, 3 of run lo (pairs x[r+0] / x[r+1]), hi0 / hi1 those
+// of run hi (pairs x[r+2] / x[r+3]), r = 0 for dwords 0 and 2, 4 for 1 and 3.
+// Hazards as for qg_q4_seg_dot: all sixteen masks are built before the first dot
+// product, accumulators rotate every four instructions, s_nop 4 at the end.
+template <int LA, int LB, int PP>
+QG_DEV void qg_q6_seg_dot(float& lo0, float& hi0, float& lo1, float& hi1, const uint4 ql, const uint4 qh,
+                          const uint32_t (&x)[8], uint32_t m4) {
+    uint32_t m[16], t0, t1, t2;
+    if constexpr (PP == 0) {
+        asm("v_lshlrev_b32 %20, 4, %27\n\t"
+            "v_bfi_b32 %21, %39, %23, %20\n\t"
+            "v_and_b32 %4, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %5, 0x3f003f, %22\n\t"
+            "v_lshrrev_b32 %20, 4, %23\n\t"
+            "v_bfi_b32 %21, %39, %20, %27\n\t"
+            "v_and_b32 %6, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %7, 0x3f003f, %22\n\t"
+            "v_lshlrev_b32 %20, 4, %28\n\t"
+            "v_bfi_b32 %21, %39, %24, %20\n\t"
+            "v_and_b32 %8, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %9, 0x3f003f, %22\n\t"
+            "v_lshrrev_b32 %20, 4, %24\n\t"
+            "v_bfi_b32 %21, %39, %20, %28\n\t"
+            "v_and_b32 %10, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %11, 0x3f003f, %22\n\t"
+            "v_lshlrev_b32 %20, 4, %29\n\t"
+            "v_bfi_b32 %21, %39, %25, %20\n\t"
+            "v_and_b32 %12, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %13, 0x3f003f, %22\n\t"
+            "v_lshrrev_b32 %20, 4, %25\n\t"
+            "v_bfi_b32 %21, %39, %20, %29\n\t"
+            "v_and_b32 %14, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %15, 0x3f003f, %22\n\t"
+            "v_lshlrev_b32 %20, 4, %30\n\t"
+            "v_bfi_b32 %21, %39, %26, %20\n\t"
+            "v_and_b32 %16, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %17, 0x3f003f, %22\n\t"
+            "v_lshrrev_b32 %20, 4, %26\n\t"
+            "v_bfi_b32 %21, %39, %20, %30\n\t"
+            "v_and_b32 %18, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %19, 0x3f003f, %22\n\t"
+            "v_dot2c_f32_f16_dpp %0, %31, %4 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %2, %32, %5 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %1, %33, %6 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %3, %34, %7 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %0, %35, %8 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %2, %36, %9 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %1, %37, %10 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %3, %38, %11 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %0, %31, %12 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %2, %32, %13 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %1, %33, %14 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %3, %34, %15 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %0, %35, %16 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %2, %36, %17 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %1, %37, %18 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %3, %38, %19 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "s_nop 4"
+            : "+v"(lo0), "+v"(hi0), "+v"(lo1), "+v"(hi1), "=&v"(m[0]), "=&v"(m[1]), "=&v"(m[2]), "=&v"(m[3]),
+              "=&v"(m[4]), "=&v"(m[5]), "=&v"(m[6]), "=&v"(m[7]), "=&v"(m[8]), "=&v"(m[9]), "=&v"(m[10]),
+              "=&v"(m[11]), "=&v"(m[12]), "=&v"(m[13]), "=&v"(m[14]), "=&v"(m[15]), "=&v"(t0), "=&v"(t1), "=&v"(t2)
+            : "v"(ql.x), "v"(ql.y), "v"(ql.z), "v"(ql.w), "v"(qh.x), "v"(qh.y), "v"(qh.z), "v"(qh.w), "v"(x[0]),
+              "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]), "s"(m4), "n"(LA),
+              "n"(LB));
+    } else {
+        asm("v_lshlrev_b32 %20, 2, %27\n\t"
+            "v_bfi_b32 %21, %39, %23, %20\n\t"
+            "v_and_b32 %4, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %5, 0x3f003f, %22\n\t"
+            "v_lshrrev_b32 %20, 4, %23\n\t"
+            "v_lshrrev_b32 %22, 2, %27\n\t"
+            "v_bfi_b32 %21, %39, %20, %22\n\t"
+            "v_and_b32 %6, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %7, 0x3f003f, %22\n\t"
+            "v_lshlrev_b32 %20, 2, %28\n\t"
+            "v_bfi_b32 %21, %39, %24, %20\n\t"
+            "v_and_b32 %8, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %9, 0x3f003f, %22\n\t"
+            "v_lshrrev_b32 %20, 4, %24\n\t"
+            "v_lshrrev_b32 %22, 2, %28\n\t"
+            "v_bfi_b32 %21, %39, %20, %22\n\t"
+            "v_and_b32 %10, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %11, 0x3f003f, %22\n\t"
+            "v_lshlrev_b32 %20, 2, %29\n\t"
+            "v_bfi_b32 %21, %39, %25, %20\n\t"
+            "v_and_b32 %12, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %13, 0x3f003f, %22\n\t"
+            "v_lshrrev_b32 %20, 4, %25\n\t"
+            "v_lshrrev_b32 %22, 2, %29\n\t"
+            "v_bfi_b32 %21, %39, %20, %22\n\t"
+            "v_and_b32 %14, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %15, 0x3f003f, %22\n\t"
+            "v_lshlrev_b32 %20, 2, %30\n\t"
+            "v_bfi_b32 %21, %39, %26, %20\n\t"
+            "v_and_b32 %16, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %17, 0x3f003f, %22\n\t"
+            "v_lshrrev_b32 %20, 4, %26\n\t"
+            "v_lshrrev_b32 %22, 2, %30\n\t"
+            "v_bfi_b32 %21, %39, %20, %22\n\t"
+            "v_and_b32 %18, 0x3f003f, %21\n\t"
+            "v_lshrrev_b32 %22, 8, %21\n\t"
+            "v_and_b32 %19, 0x3f003f, %22\n\t"
+            "v_dot2c_f32_f16_dpp %0, %31, %4 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %2, %32, %5 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %1, %33, %6 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %3, %34, %7 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %0, %35, %8 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %2, %36, %9 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %1, %37, %10 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %3, %38, %11 row_newbcast:%40 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %0, %31, %12 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %2, %32, %13 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %1, %33, %14 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %3, %34, %15 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %0, %35, %16 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %2, %36, %17 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %1, %37, %18 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "v_dot2c_f32_f16_dpp %3, %38, %19 row_newbcast:%41 row_mask:0xf bank_mask:0xf\n\t"
+            "s_nop 4"
+            : "+v"(lo0), "+v"(hi0), "+v"(lo1), "+v"(hi1), "=&v"(m[0]), "=&v"(m[1]), "=&v"(m[2]), "=&v"(m[3]),
+              "=&v"(m[4]), "=&v"(m[5]), "=&v"(m[6]), "=&v"(m[7]), "=&v"(m[8]), "=&v"(m[9]), "=&v"(m[10]),
+              "=&v"(m[11]), "=&v"(m[12]), "=&v"(m[13]), "=&v"(m[14]), "=&v"(m[15]), "=&v"(t0), "=&v"(t1), "=&v"(t2)
+            : "v"(ql.x), "v"(ql.y), "v"(ql.z), "v"(ql.w), "v"(qh.x), "v"(qh.y), "v"(qh.z), "v"(qh.w), "v"(x[0]),
+              "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]), "s"(m4), "n"(LA),
+              "n"(LB));
+    }
+}

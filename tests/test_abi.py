@@ -136,3 +136,23 @@ def test_verify_validation(L):
     # 4 tiles x 5 columns x 8 bytes, rounded up to 256
     assert L.lmhead_argmax_verify_workspace_bytes(64, 512, 5) == 256
     assert L.lmhead_argmax_verify_workspace_bytes(152064, 3584, 5) == 152064 // 16 * 5 * 8
+
+
+def test_q6k_sizes_and_validation(L):
+    assert L.qg_q6k_bytes(3584, 18944) == 3584 * 74 * 210
+    assert L.qg_q6k_bytes(152064, 3584) == 152064 * 14 * 210
+    assert L.qg_q6k_bytes(10, 300) == 0
+    assert L.qg_q6k_bytes(0, 256) == 0
+    f = L.qgemv_q6k
+    assert f(None, A, B, 64, 256, None, 0, None) == ENULL
+    assert f(C, A, B, 64, 300, None, 0, None) == ESHAPE
+    assert f(C, A, B, 0, 256, None, 0, None) == ESHAPE
+    assert f(C, A, B, 2**31 - 8, 256, None, 0, None) == ESHAPE
+    assert f(C, A, B, 64, 2**25, None, 0, None) == ESHAPE
+    assert f(C + 2, A, B, 64, 256, None, 0, None) == EALIGN
+    assert f(C, A, B + 4, 64, 256, None, 0, None) == EALIGN
+    assert L.qgemv_q6k_workspace_bytes(3584, 18944) == 0
+    assert L.qg_pack_q6k(None, A, 64, 256, None) == ENULL
+    assert L.qg_pack_q6k(A, B, 64, 100, None) == ESHAPE
+    assert L.qg_pack_q6k(A, A + 16, 64, 256, None) == ESHAPE  # overlap
+    assert L.qg_pack_q6k(A + 2, B, 64, 256, None) == EALIGN

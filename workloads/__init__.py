@@ -56,6 +56,7 @@ LAYER_STAGES = ((0, 1, 2), (3,), (4, 5), (6,))
 N_LAYERS = 28
 VOCAB = 152064
 HIDDEN = 3584
+FFN = 18944
 
 
 def rng_for(*key: int) -> np.random.Generator:
