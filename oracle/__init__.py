@@ -56,6 +56,11 @@ def lib():
         L.or_argmax.restype = _I64
         L.or_argmax.argtypes = [_P, _I64]
         L.or_num_threads.restype = ctypes.c_int
+        L.or_topk.argtypes = [_P, _I64, ctypes.c_int, _P]
+        L.or_logsumexp.restype = ctypes.c_double
+        L.or_logsumexp.argtypes = [_P, _I64]
+        L.or_sample_topk.restype = ctypes.c_int
+        L.or_sample_topk.argtypes = [_P, ctypes.c_int] + [ctypes.c_double] * 4
         _lib = L
     return _lib
 
@@ -196,6 +201,28 @@ def gemm_q4k(W, M: int, K: int, X_cols, rows=None):
 def argmax(y) -> int:
     y = np.ascontiguousarray(y, dtype=np.float64)
     return int(lib().or_argmax(_ptr(y), y.size))
+
+
+def topk(z, k: int) -> np.ndarray:
+    """Indices of the k best entries, best first (larger value, then lower index;
+    NaN counts as -inf)."""
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    if not 1 <= k <= z.size:
+        raise ValueError("need 1 <= k <= len(z)")
+    out = np.empty(k, np.int64)
+    lib().or_topk(_ptr(z), z.size, k, _ptr(out))
+    return out
+
+
+def logsumexp(z) -> float:
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    return float(lib().or_logsumexp(_ptr(z), z.size))
+
+
+def sample_topk(z_sorted, temperature: float, top_p: float, min_p: float, u: float) -> int:
+    """Position drawn by the sampler chain over the k best logits (best first)."""
+    z = np.ascontiguousarray(z_sorted, dtype=np.float64)
+    return int(lib().or_sample_topk(_ptr(z), z.size, temperature, top_p, min_p, u))
 
 
 def num_threads() -> int:

@@ -198,3 +198,70 @@ int64_t or_argmax(const double* y, int64_t n) {
         if (y[i] > y[best]) best = i;   /* strict: ties keep the lower index */
     return best;
 }
+
+/* ------------------------------------------------------------------ sampling */
+
+static double finite_or_neg_inf(double v) { return v != v ? -INFINITY : v; }
+
+void or_topk(const double* z, int64_t n, int k, int64_t* out_idx) {
+    unsigned char* taken = (unsigned char*)calloc((size_t)n, 1);
+    for (int r = 0; r < k; ++r) {
+        int64_t best = -1;
+        for (int64_t i = 0; i < n; ++i) {
+            if (taken[i]) continue;
+            /* strict comparison: among equal values the lower index stays */
+            if (best < 0 || finite_or_neg_inf(z[i]) > finite_or_neg_inf(z[best])) best = i;
+        }
+        out_idx[r] = best;
+        if (best >= 0) taken[best] = 1;
+    }
+    free(taken);
+}
+
+double or_logsumexp(const double* z, int64_t n) {
+    double m = -INFINITY;
+    for (int64_t i = 0; i < n; ++i)
+        if (finite_or_neg_inf(z[i]) > m) m = z[i];
+    if (m == -INFINITY) return -INFINITY;
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) s += exp(finite_or_neg_inf(z[i]) - m);
+    return m + log(s);
+}
+
+int or_sample_topk(const double* z, int k, double temperature, double top_p, double min_p, double u) {
+    if (temperature <= 0.0 || k == 1) return 0;
+    double* q = (double*)malloc(sizeof(double) * (size_t)k);
+    double total = 0.0;
+    for (int i = 0; i < k; ++i) {
+        q[i] = exp((finite_or_neg_inf(z[i]) - z[0]) / temperature);
+        total += q[i];
+    }
+    /* top-p: shortest prefix whose weight reaches top_p of the total */
+    int n = k;
+    if (top_p < 1.0) {
+        double c = 0.0;
+        for (n = 0; n < k;) {
+            c += q[n];
+            ++n;
+            if (c >= top_p * total) break;
+        }
+    }
+    /* min-p: entries whose weight is at least min_p times the largest (q[0] = 1) */
+    int m = 0;
+    for (int i = 0; i < n; ++i)
+        if (q[i] >= min_p * q[0]) m = i + 1;
+    double kept = 0.0;
+    for (int i = 0; i < m; ++i) kept += q[i];
+    const double target = u * kept;
+    double c = 0.0;
+    int j = m - 1;
+    for (int i = 0; i < m; ++i) {
+        c += q[i];
+        if (c > target) {
+            j = i;
+            break;
+        }
+    }
+    free(q);
+    return j;
+}

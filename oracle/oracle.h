@@ -90,6 +90,33 @@ int64_t or_argmax(const double* y, int64_t n);
 /* Number of OpenMP threads the row loops use (1 without OpenMP). */
 int or_num_threads(void);
 
+/*
+ * Sampling-side reductions over a logit vector (dotLLM README: the news entry on
+ * log-probabilities, top_logprobs 0..20 from the per-token log-softmax taken
+ * before sampling; Key Features, composable sampling: temperature -> top-k ->
+ * top-p -> min-p -> categorical draw). NaN logits count as -inf throughout.
+ */
+
+/* The k best entries of z[0..n), best first, in the order "larger value first,
+ * equal values by lower index": k rounds of a first-maximum search that skips
+ * the entries already taken. Requires 1 <= k <= n. */
+void or_topk(const double* z, int64_t n, int k, int64_t* out_idx);
+
+/* log(sum_i exp(z_i)) as max + log(sum exp(z_i - max)); -inf if every entry is
+ * -inf. */
+double or_logsumexp(const double* z, int64_t n);
+
+/*
+ * One draw from the sampler chain over the k best logits z[0..k), best first:
+ * temperature T (T <= 0: greedy, returns 0), weights q_i = exp((z_i - z_0) / T);
+ * top-p keeps the shortest prefix whose weight reaches top_p of the k-total
+ * (top_p >= 1 keeps all); min-p keeps, of those, the entries with
+ * q_i >= min_p * q_0; the draw returns the first position j whose cumulative
+ * weight exceeds u times the kept total (u in [0, 1) is the caller's uniform
+ * random number).
+ */
+int or_sample_topk(const double* z, int k, double temperature, double top_p, double min_p, double u);
+
 #ifdef __cplusplus
 }
 #endif

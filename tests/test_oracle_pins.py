@@ -9,6 +9,8 @@ sequential dot product of "Building a Fully Custom C# LLM Runtime", VectorMath
 sample, widened to fp64), the per-row bound sum|w*x|, and the greedy token choice
 (first maximum) of "Why Local LLMs Don't Need C++ or Python", section 2.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -381,3 +383,110 @@ def test_argmax_on_constructed_lm_head():
 def test_tolerance_formula():
     a = np.array([0.0, 1.0, 1000.0])
     assert np.allclose(oracle.tolerance(a), [1e-6, 1e-3 + 1e-6, 1.0 + 1e-6])
+
+
+# ---------------------------------------------------------------- sampling side
+GOLDEN_SAMPLING = os.path.join(os.path.dirname(__file__), "golden", "sampling_cases.txt")
+
+
+def _golden_sampling():
+    out = []
+    with open(GOLDEN_SAMPLING) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            lhs, rhs = (t.strip() for t in line.split("->"))
+            kind, *fields = lhs.split()
+            kv = dict(fl.split("=", 1) for fl in fields)
+            z = kv.pop("z")
+            if z.startswith("log:"):
+                zz = np.log(np.array([float(v) for v in z[4:].split(",")]))
+            else:
+                zz = np.array([float(v) for v in z.split(",")])
+            out.append((kind, zz, kv, rhs))
+    return out
+
+
+@pytest.mark.parametrize("case", _golden_sampling(), ids=lambda c: c[0])
+def test_sampling_golden(case):
+    kind, z, kv, rhs = case
+    if kind == "topk":
+        got = oracle.topk(z, int(kv["k"]))
+        assert got.tolist() == [int(v) for v in rhs.split(",")]
+    elif kind == "lse":
+        want = float(rhs)
+        got = oracle.logsumexp(z)
+        assert (got == want) if np.isinf(want) else abs(got - want) <= 1e-14 * max(1.0, abs(want))
+    else:
+        got = oracle.sample_topk(z, float(kv["T"]), float(kv["top_p"]), float(kv["min_p"]), float(kv["u"]))
+        assert got == int(rhs)
+
+
+def test_topk_matches_python_sort_with_ties():
+    rng = np.random.default_rng(40)
+    for n, k in [(1, 1), (7, 3), (50, 50), (300, 20), (1000, 64)]:
+        z = rng.integers(-5, 6, n).astype(np.float64)  # many ties
+        z[rng.integers(0, n, max(1, n // 20))] = -np.inf
+        want = sorted(range(n), key=lambda i: (-z[i], i))[:k]
+        assert oracle.topk(z, k).tolist() == want
+
+
+def test_logsumexp_against_scipy_and_shift():
+    from scipy.special import logsumexp as sp_lse
+    rng = np.random.default_rng(41)
+    for n, s in [(1, 1.0), (10, 0.1), (1000, 3.0), (152064, 50.0)]:
+        z = rng.standard_normal(n) * s
+        a = oracle.logsumexp(z)
+        assert abs(a - sp_lse(z)) <= 1e-12 * max(1.0, abs(a))
+        # log-sum-exp commutes with a constant shift
+        assert abs(oracle.logsumexp(z + 7.25) - (a + 7.25)) <= 1e-12 * max(1.0, abs(a))
+        # the log-softmax exponentiates to a distribution
+        assert abs(np.exp(z - a).sum() - 1.0) <= 1e-12 * n
+
+
+def _sample_vectorized(z, T, top_p, min_p, u):
+    """A second formulation: softmax probabilities, cumulative sums, searchsorted."""
+    if T <= 0:
+        return 0
+    p = np.exp((z - z.max()) / T)
+    p = p / p.sum()
+    n = len(p) if top_p >= 1 else int(np.searchsorted(np.cumsum(p), top_p, side="left")) + 1
+    n = min(n, len(p))
+    keep = np.flatnonzero(p[:n] >= min_p * p[0])
+    m = keep[-1] + 1
+    c = np.cumsum(p[:m])
+    return int(min(np.searchsorted(c, u * c[-1], side="right"), m - 1)), c / c[-1]
+
+
+def test_sampler_matches_second_formulation():
+    rng = np.random.default_rng(42)
+    checked = 0
+    for _ in range(400):
+        k = int(rng.integers(1, 65))
+        z = np.sort(rng.standard_normal(k) * rng.choice([0.3, 1.0, 4.0]))[::-1].copy()
+        T = float(rng.choice([0.0, 0.5, 1.0, 1.7]))
+        top_p = float(rng.choice([1.0, 0.9, 0.5, 0.05]))
+        min_p = float(rng.choice([0.0, 0.05, 0.3]))
+        u = float(rng.random())
+        r = _sample_vectorized(z, T, top_p, min_p, u)
+        if T <= 0:
+            assert oracle.sample_topk(z, T, top_p, min_p, u) == 0
+            continue
+        j, cdf = r
+        if np.min(np.abs(cdf - u)) < 1e-9:  # too close to a boundary to be a fair test
+            continue
+        assert oracle.sample_topk(z, T, top_p, min_p, u) == j
+        checked += 1
+    assert checked > 250
+
+
+def test_sampler_inverse_cdf_counts_are_exact():
+    # u on a uniform grid: each token is drawn exactly N * p times
+    p = np.array([0.5, 0.25, 0.125, 0.125])
+    z = np.log(p)
+    N = 800
+    counts = np.zeros(4, int)
+    for i in range(N):
+        counts[oracle.sample_topk(z, 1.0, 1.0, 0.0, (i + 0.5) / N)] += 1
+    assert counts.tolist() == [400, 200, 100, 100]
