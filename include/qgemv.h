@@ -213,6 +213,63 @@ int lmhead_argmax_verify(const void* w_packed_q8_0, const float* X, int64_t ldx,
                          void* workspace, size_t workspace_bytes,
                          int32_t* out_index, float* out_value, qg_stream_t stream);
 
+/*
+ * Top-k, log-softmax and the top-k sampler over a logit vector, on the device
+ * (dotLLM README: the news entry on log-probabilities, top_logprobs 0..20 from
+ * the per-token log-softmax taken before sampling; Key Features, composable
+ * sampling: temperature -> top-k -> top-p -> min-p -> categorical draw). The k
+ * best rows are ranked by logit, equal logits by lower row; NaN logits count as
+ * -inf. Results (device pointers in qg_topk_out; NULL skips an optional one):
+ *   index[k]   row ids, best first (required)
+ *   logit[k]   their logits
+ *   logprob[k] logit - lse
+ *   lse[1]     log(sum_r exp(logit_r)) over all M rows, fp32
+ *   token[1]   with a sampler: one draw from the chain over the k best, at
+ *              temperature T (T <= 0: index[0]); top-p keeps the shortest prefix
+ *              whose weight exp((z_i - z_0)/T) reaches top_p of the k-total, min-p
+ *              the entries whose weight is at least min_p times the largest, and
+ *              the draw returns the first kept position whose cumulative weight
+ *              exceeds u times the kept total. u is one uniform number in [0, 1)
+ *              that the caller draws and passes in device memory.
+ * 1 <= k <= QG_TOPK_MAX, k <= M <= QG_TOPK_MAX_ROWS; 0 < top_p <= 1, 0 <= min_p <= 1.
+ * Workspace: 16 bytes per 16 rows (per-tile maxima and exponential sums), cleared
+ * again by the call.
+ */
+#define QG_TOPK_MAX 64
+#define QG_TOPK_MAX_ROWS 262144
+
+typedef struct {
+    int32_t* index;
+    float* logit;
+    float* logprob;
+    float* lse;
+    int32_t* token;
+} qg_topk_out;
+
+typedef struct {
+    float temperature;
+    float top_p;
+    float min_p;
+    const float* u; /* device pointer to one float */
+} qg_sampler;
+
+/* Over an fp32 logit vector already in device memory. */
+size_t logits_topk_workspace_bytes(int64_t M);
+int logits_topk(const float* logits, int64_t M, int k, const qg_sampler* sampler /* host, or NULL */,
+                void* workspace, size_t workspace_bytes, const qg_topk_out* out /* host */,
+                qg_stream_t stream);
+
+/*
+ * Fused with the Q8_0 LM head: logits = W x (W packed, M x K, K % 32 == 0) are
+ * computed tile by tile and left in the caller's device buffer logits[M] (they
+ * never cross to the host); the per-tile statistics come out of the same kernel,
+ * and one more launch selects, normalizes and samples.
+ */
+size_t lmhead_topk_workspace_bytes(int64_t M, int64_t K);
+int lmhead_topk(const void* w_packed, const float* x, int64_t M, int64_t K, int k, float* logits,
+                const qg_sampler* sampler /* host, or NULL */, void* workspace, size_t workspace_bytes,
+                const qg_topk_out* out /* host */, qg_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,6 +39,16 @@ class _GemmProblem(ctypes.Structure):
                 ("N", ctypes.c_int64)]
 
 
+class _TopkOut(ctypes.Structure):
+    _fields_ = [("index", ctypes.c_void_p), ("logit", ctypes.c_void_p), ("logprob", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p), ("token", ctypes.c_void_p)]
+
+
+class _Sampler(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_p", ctypes.c_float), ("min_p", ctypes.c_float),
+                ("u", ctypes.c_void_p)]
+
+
 _P, _I64, _SZ, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
 
 _SIGS = {
@@ -67,6 +77,11 @@ _SIGS = {
     "lmhead_argmax_verify_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "lmhead_argmax_verify": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P, _P, _P]),
     "lmhead_argmax_workspace_bytes": (_SZ, [_I64, _I64]),
+    "logits_topk_workspace_bytes": (_SZ, [_I64]),
+    "logits_topk": (_I, [_P, _I64, _I, ctypes.POINTER(_Sampler), _P, _SZ, ctypes.POINTER(_TopkOut), _P]),
+    "lmhead_topk_workspace_bytes": (_SZ, [_I64, _I64]),
+    "lmhead_topk": (_I, [_P, _P, _I64, _I64, _I, _P, ctypes.POINTER(_Sampler), _P, _SZ, ctypes.POINTER(_TopkOut),
+                         _P]),
     "lmhead_argmax": (_I, [_P, _P, _I64, _I64, _P, _SZ, _P, _P, _P]),
 }
 
@@ -320,3 +335,60 @@ def lmhead_argmax_verify(w: torch.Tensor, X: torch.Tensor, M: int, K: int, out_i
     _check("lmhead_argmax_verify", lib().lmhead_argmax_verify(_ptr(w), _ptr(X), ldx, M, K, N, ws.ptr(), ws.nbytes(),
                                                               _ptr(oi), _ptr(ov), _stream(X.device)))
     return oi, ov
+
+
+# ------------------------------------------------------------------ top-k / log-softmax / sampling
+class TopK:
+    """Device outputs of a top-k call: index[k] (int32), logit[k], logprob[k], lse[1]
+    and, when a sampler was given, token[1] (int32)."""
+
+    def __init__(self, k: int, device, sample: bool):
+        self.index = torch.empty(k, dtype=torch.int32, device=device)
+        self.logit = torch.empty(k, dtype=torch.float32, device=device)
+        self.logprob = torch.empty(k, dtype=torch.float32, device=device)
+        self.lse = torch.empty(1, dtype=torch.float32, device=device)
+        self.token = torch.empty(1, dtype=torch.int32, device=device) if sample else None
+
+    def _c(self) -> _TopkOut:
+        return _TopkOut(_ptr(self.index), _ptr(self.logit), _ptr(self.logprob), _ptr(self.lse), _ptr(self.token))
+
+
+def _sampler(sampler):
+    """sampler: None or (temperature, top_p, min_p, u) with u a 1-element fp32 device tensor."""
+    if sampler is None:
+        return None
+    T, top_p, min_p, u = sampler
+    _need_cuda(u)
+    if u.dtype != torch.float32 or u.numel() < 1:
+        raise ValueError("u must be a float32 device tensor holding one uniform number")
+    return ctypes.pointer(_Sampler(T, top_p, min_p, _ptr(u)))
+
+
+def logits_topk(logits: torch.Tensor, k: int, sampler=None, ws: Workspace | None = None,
+                out: TopK | None = None) -> TopK:
+    """Top-k rows, log-softmax and (optionally) one sampled token of an fp32 logit
+    vector on the device."""
+    _need_cuda(logits)
+    M = logits.numel()
+    out = out if out is not None else TopK(k, logits.device, sampler is not None)
+    need = int(lib().logits_topk_workspace_bytes(M))
+    ws = _ws(ws, need, logits.device)
+    oc = out._c()
+    _check("logits_topk", lib().logits_topk(_ptr(logits), M, k, _sampler(sampler), ws.ptr(), ws.nbytes(),
+                                            ctypes.byref(oc), _stream(logits.device)))
+    return out
+
+
+def lmhead_topk(w: torch.Tensor, x: torch.Tensor, M: int, K: int, k: int, logits: torch.Tensor | None = None,
+                sampler=None, ws: Workspace | None = None, out: TopK | None = None):
+    """Q8_0 LM head fused with top-k, log-softmax and sampling. Returns (TopK, logits);
+    the logits stay in device memory."""
+    _need_cuda(w, x, logits)
+    logits = logits if logits is not None else torch.empty(M, dtype=torch.float32, device=x.device)
+    out = out if out is not None else TopK(k, x.device, sampler is not None)
+    need = int(lib().lmhead_topk_workspace_bytes(M, K))
+    ws = _ws(ws, need, x.device)
+    oc = out._c()
+    _check("lmhead_topk", lib().lmhead_topk(_ptr(w), _ptr(x), M, K, k, _ptr(logits), _sampler(sampler), ws.ptr(),
+                                            ws.nbytes(), ctypes.byref(oc), _stream(x.device)))
+    return out, logits

@@ -219,6 +219,22 @@ __global__ __launch_bounds__(64 * W) void lmhead_tile_kernel(Q8Prob P, float2* _
     if (lane == 0) partials[tile] = make_float2(v, __builtin_bit_cast(float, idx));
 }
 
+// Top-k stage 1: logits of one tile, written to the caller's logit vector, and
+// the tile's (first maximum, row, sum of exp(z - max)) partial.
+template <int W>
+__global__ __launch_bounds__(64 * W) void lmhead_topk_tile_kernel(Q8Prob P, float* __restrict__ logits,
+                                                                  float4* __restrict__ partials) {
+    const int tile = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const float v = tile_rows<W>(P, tile, lane, wave);
+    if (wave != 0 || lane >= 16) return;
+    const int rt = min(T, P.M - tile * T);
+    if (lane < rt) logits[tile * T + lane] = v;
+    const float4 st = qg_group16_stats(v, tile * T + lane, lane < rt);
+    if (lane == 0) partials[tile] = st;
+}
+
 // Stage 2: one workgroup reduces the partials in a fixed order.
 __global__ __launch_bounds__(1024) void lmhead_reduce_kernel(float2* __restrict__ partials, int n,
                                                               int32_t* out_index, float* out_value) {
@@ -418,6 +434,41 @@ int lmhead_argmax(const void* w, const float* x, int64_t M, int64_t K, void* ws,
     hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(1), dim3(threads), 0, s, (float2*)partials, P.tiles,
                        out_index, out_value);
     return qg::launch_status("lmhead_argmax (reduce)");
+}
+
+size_t lmhead_topk_workspace_bytes(int64_t M, int64_t K) {
+    if (K < 32 || K % 32 || K > (1 << 24)) return 0;
+    return qg::topk_ws_bytes(M);
+}
+
+int lmhead_topk(const void* w, const float* x, int64_t M, int64_t K, int k, float* logits, const qg_sampler* sampler,
+                void* ws, size_t ws_bytes, const qg_topk_out* out, qg_stream_t stream) {
+    qg::clear_error();
+    int st = validate(w, x, M, K);
+    if (st) return st;
+    st = qg::validate_topk(M, k, sampler, out);
+    if (st) return st;
+    if (!logits) return qg::fail(QG_ERR_NULL, "logits is NULL");
+    if (!qg::aligned16(logits)) return qg::fail(QG_ERR_ALIGN, "logits not 16-byte aligned");
+    const size_t need = qg::topk_ws_bytes(M);
+    if (!ws || ws_bytes < need)
+        return qg::fail(QG_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws ? ws_bytes : 0);
+    if (!qg::aligned16(ws)) return qg::fail(QG_ERR_ALIGN, "workspace not 16-byte aligned");
+    st = qg::check_device();
+    if (st) return st;
+    Q8Prob P = make_prob(w, x, nullptr, M, K);
+    float4* partials = (float4*)ws;
+    const dim3 grid(P.tiles);
+    hipStream_t s = (hipStream_t)stream;
+    switch (choose_w(P, "QG_LM_CFG")) {
+        case 1: hipLaunchKernelGGL(lmhead_topk_tile_kernel<1>, grid, dim3(64), 0, s, P, logits, partials); break;
+        case 2: hipLaunchKernelGGL(lmhead_topk_tile_kernel<2>, grid, dim3(128), 0, s, P, logits, partials); break;
+        case 4: hipLaunchKernelGGL(lmhead_topk_tile_kernel<4>, grid, dim3(256), 0, s, P, logits, partials); break;
+        default: hipLaunchKernelGGL(lmhead_topk_tile_kernel<8>, grid, dim3(512), 0, s, P, logits, partials); break;
+    }
+    st = qg::launch_status("lmhead_topk (tiles)");
+    if (st) return st;
+    return qg::launch_topk_select(partials, P.tiles, logits, M, k, sampler, *out, s);
 }
 
 int qg_pack_q8_0(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t stream) {

@@ -446,3 +446,41 @@ QG_DEV void qg_q6_seg_dot(float& lo0, float& hi0, float& lo1, float& hi1, const 
               "n"(LB));
     }
 }
+
+// ---------------------------------------------------------------------------
+// Top-k support. Per 16-lane group (one 16-row tile, one value per lane): the
+// first maximum (larger value, then lower index) and sum over the group of
+// exp(v - max), returned in every lane as (max, index bits, sum, 0). NaN counts
+// as -inf; a lane with valid == false takes part as (-inf, INT_MAX) and adds
+// nothing. A group whose maximum is -inf has sum 0.
+QG_DEV bool qg_better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
+QG_DEV float4 qg_group16_stats(float v, int idx, bool valid) {
+    if (!valid || v != v) v = -__builtin_huge_valf();
+    if (!valid) idx = 0x7fffffff;
+    float m = v;
+    int mi = idx;
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+        const float om = __shfl_xor(m, off, 64);
+        const int oi = __shfl_xor(mi, off, 64);
+        if (qg_better(om, oi, m, mi)) {
+            m = om;
+            mi = oi;
+        }
+    }
+    float e = (m == -__builtin_huge_valf()) ? 0.f : __expf(v - m);
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) e += __shfl_xor(e, off, 64);
+    return make_float4(m, __builtin_bit_cast(float, mi), e, 0.f);
+}
+
+// Order-preserving map of a float to an unsigned key (larger float, larger key;
+// -0 as +0, NaN as -inf) and its inverse.
+QG_DEV uint32_t qg_ord(float v) {
+    if (v != v) v = -__builtin_huge_valf();
+    v = v + 0.0f;  // -0 -> +0
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+QG_DEV float qg_unord(uint32_t o) { return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o); }

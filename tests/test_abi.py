@@ -156,3 +156,36 @@ def test_q6k_sizes_and_validation(L):
     assert L.qg_pack_q6k(A, B, 64, 100, None) == ESHAPE
     assert L.qg_pack_q6k(A, A + 16, 64, 256, None) == ESHAPE  # overlap
     assert L.qg_pack_q6k(A + 2, B, 64, 256, None) == EALIGN
+
+
+def test_topk_validation(L):
+    O, S = qg._TopkOut, qg._Sampler
+    D = 0x50000
+    out = O(D, D + 256, D + 512, D + 768, D + 1024)
+    ok_ws = 1 << 20
+    f = L.logits_topk
+    assert L.logits_topk_workspace_bytes(152064) == 152064 // 16 * 16
+    assert L.logits_topk_workspace_bytes(262145) == 0
+    assert L.lmhead_topk_workspace_bytes(152064, 3584) == 152064 // 16 * 16
+    assert L.lmhead_topk_workspace_bytes(152064, 3500) == 0
+    assert f(None, 1000, 5, None, B, ok_ws, ctypes.byref(out), None) == ENULL
+    assert f(A, 1000, 5, None, B, ok_ws, None, None) == ENULL
+    assert f(A, 1000, 0, None, B, ok_ws, ctypes.byref(out), None) == ESHAPE
+    assert f(A, 1000, 65, None, B, ok_ws, ctypes.byref(out), None) == ESHAPE
+    assert f(A, 4, 5, None, B, ok_ws, ctypes.byref(out), None) == ESHAPE          # k > M
+    assert f(A, 262145, 5, None, B, ok_ws, ctypes.byref(out), None) == ESHAPE     # M too large
+    assert f(A, 1000, 5, None, None, 0, ctypes.byref(out), None) == EWS
+    assert f(A, 1000, 5, None, B, 16, ctypes.byref(out), None) == EWS
+    assert f(A + 4, 1000, 5, None, B, ok_ws, ctypes.byref(out), None) == EALIGN
+    bad = O(D + 2, None, None, None, None)
+    assert f(A, 1000, 5, None, B, ok_ws, ctypes.byref(bad), None) == EALIGN
+    # a sampler needs u, a token output and sane parameters
+    assert f(A, 1000, 5, ctypes.byref(S(1.0, 0.9, 0.0, None)), B, ok_ws, ctypes.byref(out), None) == ENULL
+    no_tok = O(D, None, None, None, None)
+    assert f(A, 1000, 5, ctypes.byref(S(1.0, 0.9, 0.0, C)), B, ok_ws, ctypes.byref(no_tok), None) == ENULL
+    for T, p, m in [(1.0, 0.0, 0.0), (1.0, 1.5, 0.0), (1.0, 0.9, -0.1), (1.0, 0.9, 1.5), (float("nan"), 0.9, 0.0)]:
+        assert f(A, 1000, 5, ctypes.byref(S(T, p, m, C)), B, ok_ws, ctypes.byref(out), None) == ESHAPE
+    g = L.lmhead_topk
+    assert g(C, A, 1000, 3584, 5, None, None, B, ok_ws, ctypes.byref(out), None) == ENULL   # logits
+    assert g(C, A, 1000, 3500, 5, D, None, B, ok_ws, ctypes.byref(out), None) == ESHAPE
+    assert g(C, A, 1000, 3584, 5, D + 4, None, B, ok_ws, ctypes.byref(out), None) == EALIGN
