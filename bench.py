@@ -258,7 +258,7 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     """Each of the other hot-path kernels a few times, every call on its own weight
     copy, in this order: 4096x4096 Q4_K GEMV (3 calls), Q8_0 11008x4096 and
     4096x11008 (3 each), LM head + argmax 152064x3584 (2), the same head verifying 5
-    columns (2), small-N N=5 then N=32 over
+    columns (2), top-20 + sampling on that head (2), small-N N=5 then N=32 over
     the layers' stages (one grouped launch per stage), Q6_K 3584x18944 (3) and
     152064x3584 (2)."""
     M, K = 4096, 4096
@@ -286,6 +286,9 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     X5 = torch.from_numpy(wl.x_columns(K, 5, key=(4, 3))).to(dev)
     for c in copies:
         qg.lmhead_argmax_verify(c, X5, M, K, ws=ws)
+    u_dev = torch.full((1,), 0.5, device=dev)
+    for c in copies:
+        qg.lmhead_topk(c, x, M, K, 20, sampler=(0.8, 0.95, 0.05, u_dev), ws=ws)
     del wp, copies
     for N in (5, 32):
         for L in range(n_layers):
@@ -415,6 +418,24 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
                                             "bytes": int(b), "us_per_single_column_argmax": round(
                                                 rows["lmhead_argmax_152064x3584"]["us"], 3)}
     log(f"row lmhead verify N=5: {rows['lmhead_verify_N5_152064x3584']}")
+
+    # top-20 log-probabilities and one sampled token on the same head (T 0.8,
+    # top-p 0.95, min-p 0.05); the logits stay in a device buffer
+    kk = 20
+    u_dev = torch.full((1,), 0.5, device=dev)
+    logits_buf = torch.empty(M, device=dev)
+    tk = qg.TopK(kk, dev, True)
+    smp = (0.8, 0.95, 0.05, u_dev)
+    ms = graph_ms(torch, lambda: [qg.lmhead_topk(c, x, M, K, kk, logits=logits_buf, sampler=smp, ws=ws, out=tk)
+                                  for c in copies], 20) / 2
+    tiles = -(-M // 16)
+    b = wp.numel() + 4 * K + 4 * M + 16 * tiles * 2 + 16 * kk * 4 + 4 * (3 * kk + 2)
+    ms_sel = graph_ms(torch, lambda: qg.logits_topk(logits_buf, kk, sampler=smp, ws=ws, out=tk), 50)
+    rows[f"lmhead_top{kk}_sample_152064x3584"] = {
+        "us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": int(b),
+        "us_argmax_same_head": rows["lmhead_argmax_152064x3584"]["us"],
+        "us_logits_topk_on_resident_logits": round(ms_sel * 1e3, 3)}
+    log(f"row lmhead top-{kk} + sample: {rows[f'lmhead_top{kk}_sample_152064x3584']}")
     del copies, wp
 
     # small-N verify over the 196 decode matrices (weights read once per call), one

@@ -468,7 +468,7 @@ int lmhead_topk(const void* w, const float* x, int64_t M, int64_t K, int k, floa
     }
     st = qg::launch_status("lmhead_topk (tiles)");
     if (st) return st;
-    return qg::launch_topk_select(partials, P.tiles, logits, M, k, sampler, *out, s);
+    return qg::launch_topk_select(ws, P.tiles, logits, M, k, sampler, *out, s);
 }
 
 int qg_pack_q8_0(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t stream) {

@@ -31,12 +31,13 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 bool env_pair(const char* name, int* a, int* b);
 
 // Top-k selection stage shared by logits_topk and lmhead_topk (topk_logprobs.hip).
-// validate_topk checks k, M, the sampler and the outputs; launch_topk_select
-// reduces `tiles` per-tile partials (float4: max, index bits, exponential sum) and
-// the logits to the outputs and clears the partials.
+// validate_topk checks k, M, the sampler and the outputs. The workspace starts
+// with `tiles` per-tile partials (float4: max, row bits, exponential sum);
+// launch_topk_select reduces them and the logits to the outputs and leaves the
+// workspace all-zero.
 int validate_topk(int64_t M, int k, const qg_sampler* sampler, const qg_topk_out* out);
 size_t topk_ws_bytes(int64_t M);
-int launch_topk_select(float4* partials, int tiles, const float* logits, int64_t M, int k,
-                       const qg_sampler* sampler, const qg_topk_out& out, hipStream_t s);
+int launch_topk_select(void* ws, int tiles, const float* logits, int64_t M, int k, const qg_sampler* sampler,
+                       const qg_topk_out& out, hipStream_t s);
 
 }  // namespace qg

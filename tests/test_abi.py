@@ -164,9 +164,17 @@ def test_topk_validation(L):
     out = O(D, D + 256, D + 512, D + 768, D + 1024)
     ok_ws = 1 << 20
     f = L.logits_topk
-    assert L.logits_topk_workspace_bytes(152064) == 152064 // 16 * 16
+    # 16 bytes per 16-row tile, then per group of 1024 tiles 64 eight-byte keys
+    # and one (max, sum) pair, each part 256-byte aligned at its end
+    def ws(M):
+        tiles = -(-M // 16)
+        groups = -(-tiles // 1024)
+        up = lambda v: -(-v // 256) * 256
+        return up(up(tiles * 16) + groups * 64 * 8 + groups * 8)
+    assert L.logits_topk_workspace_bytes(152064) == ws(152064) == 157440
+    assert L.logits_topk_workspace_bytes(262144) == ws(262144)
     assert L.logits_topk_workspace_bytes(262145) == 0
-    assert L.lmhead_topk_workspace_bytes(152064, 3584) == 152064 // 16 * 16
+    assert L.lmhead_topk_workspace_bytes(152064, 3584) == ws(152064)
     assert L.lmhead_topk_workspace_bytes(152064, 3500) == 0
     assert f(None, 1000, 5, None, B, ok_ws, ctypes.byref(out), None) == ENULL
     assert f(A, 1000, 5, None, B, ok_ws, None, None) == ENULL
