@@ -490,3 +490,103 @@ def test_sampler_inverse_cdf_counts_are_exact():
     for i in range(N):
         counts[oracle.sample_topk(z, 1.0, 1.0, 0.0, (i + 0.5) / N)] += 1
     assert counts.tolist() == [400, 200, 100, 100]
+
+
+# ---------------------------------------------------------------- int8 activations
+GOLDEN_Q8K = os.path.join(os.path.dirname(__file__), "golden", "q8k_activation_cases.txt")
+
+
+def _golden_q8k():
+    f = {}
+    for line in open(GOLDEN_Q8K):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        k, v = (t.strip() for t in line.split("=", 1))
+        name, attr = k.split(".")
+        f.setdefault(name, {})[attr] = v
+    out = {}
+    i = np.arange(256)
+    for name, fl in f.items():
+        if "x_rule" in fl:
+            x = eval(fl["x_rule"], {"i": i}).astype(np.float32)
+            q = eval(fl["q_rule"], {"i": i}).astype(np.int64)
+        else:
+            x = np.zeros(256, np.float32)
+            vals = [float(v) for v in fl["x_list"].split()]
+            x[:len(vals)] = vals
+            q = np.zeros(256, np.int64)
+            qs = [int(v) for v in fl["q_list"].split()]
+            q[:len(qs)] = qs
+        out[name] = dict(x=x, d=float(fl["d"]), q=q, bsums=[int(v) for v in fl["bsums"].split()])
+    return out
+
+
+@pytest.mark.parametrize("name", ["A", "B", "C"])
+def test_q8k_golden_blocks(name):
+    g = _golden_q8k()[name]
+    d, q, bs = oracle.quantize_q8k(g["x"])
+    assert float(d[0]) == g["d"]
+    assert q.astype(np.int64).tolist() == g["q"].tolist()
+    assert bs.astype(np.int64).tolist() == g["bsums"]
+
+
+def test_q8k_error_bound_and_extremes():
+    rng = np.random.default_rng(50)
+    x = (rng.standard_normal(256 * 40) * rng.choice([1e-3, 1.0, 300.0], 256 * 40)).astype(np.float32)
+    d, q, bs = oracle.quantize_q8k(x)
+    xb = x.reshape(-1, 256).astype(np.float64)
+    qb = q.reshape(-1, 256).astype(np.float64)
+    db = d.astype(np.float64)[:, None]
+    # the largest magnitude of each block maps to +-127, every element within half a step
+    assert np.all(np.abs(qb).max(axis=1) == 127)
+    assert np.all(np.abs(xb - db * qb) <= db * (0.5 + 1e-5))
+    assert np.array_equal(bs.reshape(-1, 16).astype(np.int64), qb.reshape(-1, 16, 16).sum(axis=2).astype(np.int64))
+
+
+def test_q8k_gemv_exact_when_quantization_is_exact():
+    # activations that are multiples of 1/8 with max 127/8 quantize without error,
+    # so the integer-activation product equals the fp32-activation product exactly
+    M, K = 33, 768
+    W = workloads.q4k_blocks(M, K, key=(51,))
+    k = np.random.default_rng(51).integers(-127, 128, K)
+    k[::256] = 127
+    x = (k / 8).astype(np.float32)
+    d, q, _ = oracle.quantize_q8k(x)
+    assert np.array_equal(q.astype(np.int64), k)
+    y8, a8 = oracle.gemv_q4k_q8k(W, M, K, d, q)
+    y, a = oracle.gemv_q4k(W, M, K, x)
+    assert np.array_equal(y8, y) and np.array_equal(a8, a)
+
+
+def test_q8k_gemv_integer_case_against_int64_matmul():
+    # d = 1, dmin = 0, every sub-scale 1: weights are the 4-bit quants; activations
+    # k/8: y = (Q @ k) / 8 exactly
+    M, K = 9, 512
+    rng = np.random.default_rng(52)
+    rows = []
+    Q = rng.integers(0, 16, (M, K))
+    for r in range(M):
+        blks = []
+        for b in range(K // 256):
+            blks.append(enc.q4k_block(0x3C00, 0, [1] * 8, [0] * 8, Q[r, 256 * b:256 * b + 256]))
+        rows.append(np.concatenate(blks))
+    W = np.stack(rows)
+    k = rng.integers(-127, 128, K)
+    k[0] = 127
+    k[256] = -127
+    d, q, _ = oracle.quantize_q8k((k / 8).astype(np.float32))
+    y, _ = oracle.gemv_q4k_q8k(W, M, K, d, q)
+    assert np.array_equal(y * 8, (Q @ k).astype(np.float64))
+
+
+def test_q8k_gemv_within_the_parity_tolerance_of_fp32_activations():
+    # the quantization error (at most half a step per activation) keeps the product
+    # inside 1e-3 * sum|w x| of the fp32-activation product at the 7B shapes
+    for M, K in [(64, 3584), (16, 18944)]:
+        W = workloads.q4k_blocks(M, K, key=(53, K))
+        x = workloads.x_vector(K, key=(53, K))
+        d, q, _ = oracle.quantize_q8k(x)
+        y8, _ = oracle.gemv_q4k_q8k(W, M, K, d, q)
+        y, a = oracle.gemv_q4k(W, M, K, x)
+        assert np.all(np.abs(y8 - y) <= oracle.tolerance(a))
