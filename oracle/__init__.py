@@ -56,8 +56,8 @@ def lib():
         L.or_argmax.restype = _I64
         L.or_argmax.argtypes = [_P, _I64]
         L.or_num_threads.restype = ctypes.c_int
-        L.or_quantize_q8k.argtypes = [_P, _I64, _P, _P, _P]
-        L.or_gemv_q4k_q8k.argtypes = [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P]
+        L.or_quantize_q8_1.argtypes = [_P, _I64, _P, _P, _P]
+        L.or_gemv_q4k_q8_1.argtypes = [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P]
         L.or_topk.argtypes = [_P, _I64, ctypes.c_int, _P]
         L.or_logsumexp.restype = ctypes.c_double
         L.or_logsumexp.argtypes = [_P, _I64]
@@ -205,28 +205,28 @@ def argmax(y) -> int:
     return int(lib().or_argmax(_ptr(y), y.size))
 
 
-def quantize_q8k(x):
-    """Q8_K-style activations: (d float32[K/256], q int8[K], bsums int16[K/16])."""
+def quantize_q8_1(x):
+    """Q8_1-style activations: (d float32[K/32], q int8[K], s int16[K/32])."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     K = x.size
-    if K % 256:
-        raise ValueError("K must be a multiple of 256")
-    d = np.empty(K // 256, np.float32)
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    d = np.empty(K // 32, np.float32)
     q = np.empty(K, np.int8)
-    bs = np.empty(K // 16, np.int16)
-    lib().or_quantize_q8k(_ptr(x), K, _ptr(d), _ptr(q), _ptr(bs))
-    return d, q, bs
+    s = np.empty(K // 32, np.int16)
+    lib().or_quantize_q8_1(_ptr(x), K, _ptr(d), _ptr(q), _ptr(s))
+    return d, q, s
 
 
-def gemv_q4k_q8k(W, M: int, K: int, d, q, rows=None):
-    """y = W xq with xq = d[k/256] * q[k]; returns (y, sum|w*xq|) in fp64."""
+def gemv_q4k_q8_1(W, M: int, K: int, d, q, rows=None):
+    """y = W xq with xq = d[k/32] * q[k]; returns (y, sum|w*xq|) in fp64."""
     W = _u8(W)
     d = np.ascontiguousarray(d, dtype=np.float32)
     q = np.ascontiguousarray(q, dtype=np.int8)
     r, n = _rows(rows, M)
     y = np.zeros(n, np.float64)
     a = np.zeros(n, np.float64)
-    lib().or_gemv_q4k_q8k(_ptr(W), M, K, _ptr(d), _ptr(q), _ptr(r), n, _ptr(y), _ptr(a))
+    lib().or_gemv_q4k_q8_1(_ptr(W), M, K, _ptr(d), _ptr(q), _ptr(r), n, _ptr(y), _ptr(a))
     return y, a
 
 

@@ -201,33 +201,31 @@ int64_t or_argmax(const double* y, int64_t n) {
 
 /* ------------------------------------------------------------------ int8 activations */
 
-void or_quantize_q8k(const float* x, int64_t K, float* d, int8_t* q, int16_t* bsums) {
-    for (int64_t b = 0; b < K / 256; ++b) {
-        const float* xb = x + 256 * b;
+void or_quantize_q8_1(const float* x, int64_t K, float* d, int8_t* q, int16_t* s) {
+    for (int64_t b = 0; b < K / 32; ++b) {
+        const float* xb = x + 32 * b;
         float amax = 0.0f;
-        for (int i = 0; i < 256; ++i)
+        for (int i = 0; i < 32; ++i)
             if (fabsf(xb[i]) > amax) amax = fabsf(xb[i]);
         const float db = amax / 127.0f;
         d[b] = db;
-        for (int i = 0; i < 256; ++i) {
+        int sum = 0;
+        for (int i = 0; i < 32; ++i) {
             float v = 0.0f;
             if (db != 0.0f) {
                 v = rintf(xb[i] / db);
                 if (v > 127.0f) v = 127.0f;
                 if (v < -127.0f) v = -127.0f;
             }
-            q[256 * b + i] = (int8_t)v;
+            q[32 * b + i] = (int8_t)v;
+            sum += (int)v;
         }
-        for (int g = 0; g < 16; ++g) {
-            int s = 0;
-            for (int i = 0; i < 16; ++i) s += q[256 * b + 16 * g + i];
-            bsums[16 * b + g] = (int16_t)s;
-        }
+        s[b] = (int16_t)sum;
     }
 }
 
-void or_gemv_q4k_q8k(const uint8_t* W, int64_t M, int64_t K, const float* d, const int8_t* q,
-                     const int64_t* rows, int64_t nrows, double* y, double* a) {
+void or_gemv_q4k_q8_1(const uint8_t* W, int64_t M, int64_t K, const float* d, const int8_t* q,
+                      const int64_t* rows, int64_t nrows, double* y, double* a) {
     (void)M;
 #pragma omp parallel
     {
@@ -236,13 +234,13 @@ void or_gemv_q4k_q8k(const uint8_t* W, int64_t M, int64_t K, const float* d, con
         for (int64_t i = 0; i < nrows; ++i) {
             const int64_t r = rows ? rows[i] : i;
             or_q4k_dequant_row(W + r * (K / 256) * 144, K, w);
-            double s = 0.0, t = 0.0;
+            double sum = 0.0, t = 0.0;
             for (int64_t k = 0; k < K; ++k) {
-                const double p = w[k] * ((double)d[k / 256] * (double)q[k]);
-                s += p;
+                const double p = w[k] * ((double)d[k / 32] * (double)q[k]);
+                sum += p;
                 t += fabs(p);
             }
-            y[i] = s;
+            y[i] = sum;
             if (a) a[i] = t;
         }
         free(w);

@@ -91,21 +91,23 @@ int64_t or_argmax(const double* y, int64_t n);
 int or_num_threads(void);
 
 /*
- * Integer-activation form (dotLLM README news: Q8_K input quantization with a
- * float32 scale per 256-element block and precomputed block sums, feeding fused
- * K-quant dot products). Reading: per block of 256 activations, amax = max |x|,
+ * Integer-activation form (dotLLM README news: Q8_1 / Q8_K input quantization,
+ * a float32 scale per block of activations with precomputed block sums, feeding
+ * fused K-quant dot products). Reading, with the Q8_1 block of 32 (one block per
+ * Q4_K sub-block; a scale per 256 was measured to exceed the product tolerance on
+ * some rows at K = 3584): per block of 32 activations, amax = max |x|,
  * d = amax / 127 and q = round-half-even(x / d) clamped to [-127, 127], both in
- * float32 as written (q = 0 when d = 0); bsums[i] = sum of q over elements
- * 16i .. 16i+15. The quantization takes integer decisions, so it is done in the
- * float32 arithmetic a GPU kernel would use (one correctly rounded division and
- * one rounding per element) rather than in fp64.
+ * float32 as written (q = 0 when d = 0); s = the sum of the block's q. The
+ * quantization takes integer decisions, so it is done in the float32 arithmetic
+ * a GPU kernel would use (one correctly rounded division and one rounding per
+ * element) rather than in fp64.
  */
-void or_quantize_q8k(const float* x, int64_t K, float* d, int8_t* q, int16_t* bsums);
+void or_quantize_q8_1(const float* x, int64_t K, float* d, int8_t* q, int16_t* s);
 
-/* y = W xq for a Q4_K matrix W and the dequantized activations xq_k = d[k/256] * q[k]
+/* y = W xq for a Q4_K matrix W and the dequantized activations xq_k = d[k/32] * q[k]
  * (fp64, dense form; rows and a as for or_gemv_q4k). */
-void or_gemv_q4k_q8k(const uint8_t* W, int64_t M, int64_t K, const float* d, const int8_t* q,
-                     const int64_t* rows, int64_t nrows, double* y, double* a);
+void or_gemv_q4k_q8_1(const uint8_t* W, int64_t M, int64_t K, const float* d, const int8_t* q,
+                      const int64_t* rows, int64_t nrows, double* y, double* a);
 
 /*
  * Sampling-side reductions over a logit vector (dotLLM README: the news entry on

@@ -484,3 +484,42 @@ QG_DEV uint32_t qg_ord(float v) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 QG_DEV float qg_unord(uint32_t o) { return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o); }
+
+// ---------------------------------------------------------------------------
+// Q4_K against int8 activations: one 16-byte quant segment (4 dwords, 32 weights)
+// and this lane's activation dwords x = (low run bytes 0-3, 4-7, high run bytes
+// 0-3, 4-7), taken from lane LA for quant dwords 0, 1 and LB for 2, 3 by the DPP
+// row broadcast. Low nibbles masked with 0x0F0F0F0F are four unsigned bytes (the
+// quants of the low sub-block), the high nibbles likewise after a shift by 4;
+// v_dot4c_i32_i8 adds four byte products to an int32 accumulator: lo0 / lo1 take
+// dwords 0, 2 / 1, 3 of the low sub-block, hi0 / hi1 those of the high one. All
+// masks come first; each accumulator is re-read four instructions after its last
+// write; s_nop 4 at the end (as for qg_q4_seg_dot).
+template <int LA, int LB>
+QG_DEV void qg_q4_seg_dot_i8(int& lo0, int& hi0, int& lo1, int& hi1, const uint4 q, const uint32_t (&x)[4]) {
+    uint32_t m0, m1, m2, m3, m4, m5, m6, m7, t;
+    asm("v_and_b32 %4, 0x0f0f0f0f, %13\n\t"
+        "v_lshrrev_b32 %12, 4, %13\n\t"
+        "v_and_b32 %5, 0x0f0f0f0f, %12\n\t"
+        "v_and_b32 %6, 0x0f0f0f0f, %14\n\t"
+        "v_lshrrev_b32 %12, 4, %14\n\t"
+        "v_and_b32 %7, 0x0f0f0f0f, %12\n\t"
+        "v_and_b32 %8, 0x0f0f0f0f, %15\n\t"
+        "v_lshrrev_b32 %12, 4, %15\n\t"
+        "v_and_b32 %9, 0x0f0f0f0f, %12\n\t"
+        "v_and_b32 %10, 0x0f0f0f0f, %16\n\t"
+        "v_lshrrev_b32 %12, 4, %16\n\t"
+        "v_and_b32 %11, 0x0f0f0f0f, %12\n\t"
+        "v_dot4c_i32_i8_dpp %0, %17, %4 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %19, %5 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %18, %6 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %20, %7 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %17, %8 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %19, %9 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %18, %10 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %20, %11 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 4"
+        : "+v"(lo0), "+v"(hi0), "+v"(lo1), "+v"(hi1), "=&v"(m0), "=&v"(m1), "=&v"(m2), "=&v"(m3), "=&v"(m4),
+          "=&v"(m5), "=&v"(m6), "=&v"(m7), "=&v"(t)
+        : "v"(q.x), "v"(q.y), "v"(q.z), "v"(q.w), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "n"(LA), "n"(LB));
+}

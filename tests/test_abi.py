@@ -197,3 +197,18 @@ def test_topk_validation(L):
     assert g(C, A, 1000, 3584, 5, None, None, B, ok_ws, ctypes.byref(out), None) == ENULL   # logits
     assert g(C, A, 1000, 3500, 5, D, None, B, ok_ws, ctypes.byref(out), None) == ESHAPE
     assert g(C, A, 1000, 3584, 5, D + 4, None, B, ok_ws, ctypes.byref(out), None) == EALIGN
+
+
+def test_q8k_validation(L):
+    assert L.qg_q8k_bytes(3584) == 64 + 3584 + 448
+    assert L.qg_q8k_bytes(300) == 0
+    assert L.qg_quantize_q8k(None, 256, B, None) == ENULL
+    assert L.qg_quantize_q8k(A, 300, B, None) == ESHAPE
+    assert L.qg_quantize_q8k(A + 4, 256, B, None) == EALIGN
+    assert L.qg_quantize_q8k(A, 256, A + 512, None) == ESHAPE  # overlap
+    f = L.qgemv_q4k_q8k
+    assert f(C, None, B, 64, 256, None, 0, None) == ENULL
+    assert f(C, A, B, 64, 300, None, 0, None) == ESHAPE
+    assert f(C, A, B, 0, 256, None, 0, None) == ESHAPE
+    assert f(C, A + 8, B, 64, 256, None, 0, None) == EALIGN
+    assert L.qgemv_q4k_q8k_workspace_bytes(3584, 3584) == 0

@@ -493,12 +493,12 @@ def test_sampler_inverse_cdf_counts_are_exact():
 
 
 # ---------------------------------------------------------------- int8 activations
-GOLDEN_Q8K = os.path.join(os.path.dirname(__file__), "golden", "q8k_activation_cases.txt")
+GOLDEN_Q8_1 = os.path.join(os.path.dirname(__file__), "golden", "q8_1_activation_cases.txt")
 
 
-def _golden_q8k():
+def _golden_q8_1():
     f = {}
-    for line in open(GOLDEN_Q8K):
+    for line in open(GOLDEN_Q8_1):
         line = line.strip()
         if not line or line.startswith("#"):
             continue
@@ -518,75 +518,70 @@ def _golden_q8k():
             q = np.zeros(256, np.int64)
             qs = [int(v) for v in fl["q_list"].split()]
             q[:len(qs)] = qs
-        out[name] = dict(x=x, d=float(fl["d"]), q=q, bsums=[int(v) for v in fl["bsums"].split()])
+        out[name] = dict(x=x, d=[float(v) for v in fl["d"].split()], q=q, s=[int(v) for v in fl["s"].split()])
     return out
 
 
 @pytest.mark.parametrize("name", ["A", "B", "C"])
-def test_q8k_golden_blocks(name):
-    g = _golden_q8k()[name]
-    d, q, bs = oracle.quantize_q8k(g["x"])
-    assert float(d[0]) == g["d"]
+def test_q8_1_golden_blocks(name):
+    g = _golden_q8_1()[name]
+    d, q, s = oracle.quantize_q8_1(g["x"])
+    assert d.astype(np.float64).tolist() == g["d"]
     assert q.astype(np.int64).tolist() == g["q"].tolist()
-    assert bs.astype(np.int64).tolist() == g["bsums"]
+    assert s.astype(np.int64).tolist() == g["s"]
 
 
-def test_q8k_error_bound_and_extremes():
+def test_q8_1_error_bound_and_extremes():
     rng = np.random.default_rng(50)
-    x = (rng.standard_normal(256 * 40) * rng.choice([1e-3, 1.0, 300.0], 256 * 40)).astype(np.float32)
-    d, q, bs = oracle.quantize_q8k(x)
-    xb = x.reshape(-1, 256).astype(np.float64)
-    qb = q.reshape(-1, 256).astype(np.float64)
+    x = (rng.standard_normal(32 * 300) * rng.choice([1e-3, 1.0, 300.0], 32 * 300)).astype(np.float32)
+    d, q, s = oracle.quantize_q8_1(x)
+    xb = x.reshape(-1, 32).astype(np.float64)
+    qb = q.reshape(-1, 32).astype(np.float64)
     db = d.astype(np.float64)[:, None]
     # the largest magnitude of each block maps to +-127, every element within half a step
     assert np.all(np.abs(qb).max(axis=1) == 127)
     assert np.all(np.abs(xb - db * qb) <= db * (0.5 + 1e-5))
-    assert np.array_equal(bs.reshape(-1, 16).astype(np.int64), qb.reshape(-1, 16, 16).sum(axis=2).astype(np.int64))
+    assert np.array_equal(s.astype(np.int64), qb.sum(axis=1).astype(np.int64))
 
 
-def test_q8k_gemv_exact_when_quantization_is_exact():
-    # activations that are multiples of 1/8 with max 127/8 quantize without error,
-    # so the integer-activation product equals the fp32-activation product exactly
+def test_q8_1_gemv_exact_when_quantization_is_exact():
+    # activations that are multiples of 1/8 with 127/8 in every block quantize
+    # without error, so the integer-activation product equals the fp32 one exactly
     M, K = 33, 768
     W = workloads.q4k_blocks(M, K, key=(51,))
     k = np.random.default_rng(51).integers(-127, 128, K)
-    k[::256] = 127
+    k[::32] = 127
     x = (k / 8).astype(np.float32)
-    d, q, _ = oracle.quantize_q8k(x)
+    d, q, _ = oracle.quantize_q8_1(x)
     assert np.array_equal(q.astype(np.int64), k)
-    y8, a8 = oracle.gemv_q4k_q8k(W, M, K, d, q)
+    y8, a8 = oracle.gemv_q4k_q8_1(W, M, K, d, q)
     y, a = oracle.gemv_q4k(W, M, K, x)
     assert np.array_equal(y8, y) and np.array_equal(a8, a)
 
 
-def test_q8k_gemv_integer_case_against_int64_matmul():
+def test_q8_1_gemv_integer_case_against_int64_matmul():
     # d = 1, dmin = 0, every sub-scale 1: weights are the 4-bit quants; activations
-    # k/8: y = (Q @ k) / 8 exactly
+    # k/8 with 127/8 in every block: y = (Q @ k) / 8 exactly
     M, K = 9, 512
     rng = np.random.default_rng(52)
-    rows = []
     Q = rng.integers(0, 16, (M, K))
-    for r in range(M):
-        blks = []
-        for b in range(K // 256):
-            blks.append(enc.q4k_block(0x3C00, 0, [1] * 8, [0] * 8, Q[r, 256 * b:256 * b + 256]))
-        rows.append(np.concatenate(blks))
-    W = np.stack(rows)
+    W = np.stack([np.concatenate([enc.q4k_block(0x3C00, 0, [1] * 8, [0] * 8, Q[r, 256 * b:256 * b + 256])
+                                  for b in range(K // 256)]) for r in range(M)])
     k = rng.integers(-127, 128, K)
-    k[0] = 127
-    k[256] = -127
-    d, q, _ = oracle.quantize_q8k((k / 8).astype(np.float32))
-    y, _ = oracle.gemv_q4k_q8k(W, M, K, d, q)
+    k[::32] = -127
+    d, q, _ = oracle.quantize_q8_1((k / 8).astype(np.float32))
+    y, _ = oracle.gemv_q4k_q8_1(W, M, K, d, q)
     assert np.array_equal(y * 8, (Q @ k).astype(np.float64))
 
 
-def test_q8k_gemv_within_the_parity_tolerance_of_fp32_activations():
-    # the quantization error (at most half a step per activation) keeps the product
-    # inside 1e-3 * sum|w x| of the fp32-activation product at the 7B shapes
+def test_q8_1_gemv_within_the_parity_tolerance_of_fp32_activations():
+    # the quantization error (at most half a step per activation, the step set per
+    # 32 activations) keeps the product inside 1e-3 * sum|w x| of the
+    # fp32-activation product at the 7B decode shapes
     for M, K in [(64, 3584), (16, 18944)]:
         W = workloads.q4k_blocks(M, K, key=(53, K))
         x = workloads.x_vector(K, key=(53, K))
-        d, q, _ = oracle.quantize_q8k(x)
-        y8, _ = oracle.gemv_q4k_q8k(W, M, K, d, q)
+        d, q, _ = oracle.quantize_q8_1(x)
+        y8, _ = oracle.gemv_q4k_q8_1(W, M, K, d, q)
         y, a = oracle.gemv_q4k(W, M, K, x)
         assert np.all(np.abs(y8 - y) <= oracle.tolerance(a))
