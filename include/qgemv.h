@@ -125,23 +125,26 @@ int qgemv_q6k(const void* w_packed, const float* x, float* y, int64_t M, int64_t
 
 /*
  * Integer activations (dotLLM README, news entries on Q8_1 / Q8_K input
- * quantization: a float32 scale per 256-element block and precomputed block
- * sums, feeding the fused K-quant dot products). qg_quantize_q8k writes, for an
- * fp32 x[K] (K % 256 == 0), the buffer xq of qg_q8k_bytes(K) bytes:
- *   float d[K/256] at 0; int8 q[K] at q_off = align16(4*(K/256));
- *   int16 bsums[K/16] at align16(q_off + K);
- * with d_b = max|x| / 127 over block b and q = round-half-to-even(x / d_b) in
- * float32 (0 when d_b = 0), bsums[i] = the sum of q over elements 16i..16i+15.
- * qgemv_q4k_q8k computes y[M] = W xq for the packed Q4_K matrix W, with the
- * quantized activations xq_k = d[k/256] * q[k]: every per-sub-block dot product
- * is an exact int32 (v_dot4c_i32_i8), scaled by d, dmin and d_b in fp32. Needs
- * no workspace. Shape rules as for qgemv_q4k.
+ * quantization: a float32 scale per block of activations with precomputed block
+ * sums, feeding the fused K-quant dot products; the Q8_1 block of 32, one per
+ * Q4_K sub-block). qg_quantize_q8_1 writes, for an fp32 x[K] (K % 256 == 0), the
+ * buffer xq of qg_q8_1_bytes(K) bytes:
+ *   float d[K/32] at 0; int8 q[K] at q_off = align16(4*(K/32));
+ *   int16 s[K/32] at align16(q_off + K);
+ * with d_c = max|x| / 127 over block c and q = round-half-to-even(x / d_c) in
+ * float32 (0 when d_c = 0), s_c = the sum of the block's q. qgemv_q4k_q8_1
+ * computes y[M] = W xq for the packed Q4_K matrix W and the quantized activations
+ * xq_k = d[k/32] * q[k]: each 32-weight dot product is an exact int32
+ * (v_dot4c_i32_i8), scaled by d, dmin and d_c in fp32. The quantization error
+ * stays within the library's 1e-3 * sum|w x| bound at the 7B decode shapes
+ * (measured below 0.8 of it at K = 3584), with a smaller margin at small K.
+ * Needs no workspace. Shape rules as for qgemv_q4k.
  */
-size_t qg_q8k_bytes(int64_t K);
-int qg_quantize_q8k(const float* x, int64_t K, void* xq, qg_stream_t stream);
-size_t qgemv_q4k_q8k_workspace_bytes(int64_t M, int64_t K);
-int qgemv_q4k_q8k(const void* w_packed, const void* xq, float* y, int64_t M, int64_t K,
-                  void* workspace, size_t workspace_bytes, qg_stream_t stream);
+size_t qg_q8_1_bytes(int64_t K);
+int qg_quantize_q8_1(const float* x, int64_t K, void* xq, qg_stream_t stream);
+size_t qgemv_q4k_q8_1_workspace_bytes(int64_t M, int64_t K);
+int qgemv_q4k_q8_1(const void* w_packed, const void* xq, float* y, int64_t M, int64_t K,
+                   void* workspace, size_t workspace_bytes, qg_stream_t stream);
 
 /*
  * Several independent Q4_K GEMVs in one launch (the dotLLM README's fused decode

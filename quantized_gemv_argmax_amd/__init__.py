@@ -68,10 +68,10 @@ _SIGS = {
     "qgemv_q4k_batch": (_I, [ctypes.POINTER(_Problem), _I, _P, _SZ, _P]),
     "qgemv_q8_0_workspace_bytes": (_SZ, [_I64, _I64]),
     "qgemv_q8_0": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
-    "qg_q8k_bytes": (_SZ, [_I64]),
-    "qg_quantize_q8k": (_I, [_P, _I64, _P, _P]),
-    "qgemv_q4k_q8k_workspace_bytes": (_SZ, [_I64, _I64]),
-    "qgemv_q4k_q8k": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
+    "qg_q8_1_bytes": (_SZ, [_I64]),
+    "qg_quantize_q8_1": (_I, [_P, _I64, _P, _P]),
+    "qgemv_q4k_q8_1_workspace_bytes": (_SZ, [_I64, _I64]),
+    "qgemv_q4k_q8_1": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "qgemv_q6k_workspace_bytes": (_SZ, [_I64, _I64]),
     "qgemv_q6k": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "qgemm_q4k_smalln_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
@@ -262,38 +262,38 @@ def qgemv_q8_0(w: torch.Tensor, x: torch.Tensor, M: int, K: int, y: torch.Tensor
     return y
 
 
-def q8k_bytes(K: int) -> int:
-    return int(lib().qg_q8k_bytes(K))
+def q8_1_bytes(K: int) -> int:
+    return int(lib().qg_q8_1_bytes(K))
 
 
-def q8k_views(xq: torch.Tensor, K: int):
-    """(d float32[K/256], q int8[K], bsums int16[K/16]) views of a quantized-activation buffer."""
-    nb = K // 256
-    q_off = -(-4 * nb // 16) * 16
-    b_off = -(-(q_off + K) // 16) * 16
-    return (xq[:4 * nb].view(torch.float32), xq[q_off:q_off + K].view(torch.int8),
-            xq[b_off:b_off + 2 * (K // 16)].view(torch.int16))
+def q8_1_views(xq: torch.Tensor, K: int):
+    """(d float32[K/32], q int8[K], s int16[K/32]) views of a quantized-activation buffer."""
+    nc = K // 32
+    q_off = -(-4 * nc // 16) * 16
+    s_off = -(-(q_off + K) // 16) * 16
+    return (xq[:4 * nc].view(torch.float32), xq[q_off:q_off + K].view(torch.int8),
+            xq[s_off:s_off + 2 * nc].view(torch.int16))
 
 
-def quantize_q8k(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Int8 activations with a float32 scale per 256 and block sums (uint8 buffer)."""
+def quantize_q8_1(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Int8 activations with a float32 scale and a block sum per 32 (uint8 buffer)."""
     _need_cuda(x, out)
     K = x.numel()
-    n = q8k_bytes(K)
+    n = q8_1_bytes(K)
     out = out if out is not None else torch.empty(n, dtype=torch.uint8, device=x.device)
-    _check("qg_quantize_q8k", lib().qg_quantize_q8k(_ptr(x), K, _ptr(out), _stream(x.device)))
+    _check("qg_quantize_q8_1", lib().qg_quantize_q8_1(_ptr(x), K, _ptr(out), _stream(x.device)))
     return out
 
 
-def qgemv_q4k_q8k(w: torch.Tensor, xq: torch.Tensor, M: int, K: int, y: torch.Tensor | None = None,
-                  ws: Workspace | None = None) -> torch.Tensor:
+def qgemv_q4k_q8_1(w: torch.Tensor, xq: torch.Tensor, M: int, K: int, y: torch.Tensor | None = None,
+                   ws: Workspace | None = None) -> torch.Tensor:
     """y[M] = W xq for a packed Q4_K matrix and quantized activations."""
     _need_cuda(w, xq, y)
     y = y if y is not None else torch.empty(M, dtype=torch.float32, device=xq.device)
-    need = int(lib().qgemv_q4k_q8k_workspace_bytes(M, K))
+    need = int(lib().qgemv_q4k_q8_1_workspace_bytes(M, K))
     ws = _ws(ws, need, xq.device)
-    _check("qgemv_q4k_q8k", lib().qgemv_q4k_q8k(_ptr(w), _ptr(xq), _ptr(y), M, K, ws.ptr(), ws.nbytes(),
-                                                _stream(xq.device)))
+    _check("qgemv_q4k_q8_1", lib().qgemv_q4k_q8_1(_ptr(w), _ptr(xq), _ptr(y), M, K, ws.ptr(), ws.nbytes(),
+                                                  _stream(xq.device)))
     return y
 
 

@@ -199,16 +199,16 @@ def test_topk_validation(L):
     assert g(C, A, 1000, 3584, 5, D + 4, None, B, ok_ws, ctypes.byref(out), None) == EALIGN
 
 
-def test_q8k_validation(L):
-    assert L.qg_q8k_bytes(3584) == 64 + 3584 + 448
-    assert L.qg_q8k_bytes(300) == 0
-    assert L.qg_quantize_q8k(None, 256, B, None) == ENULL
-    assert L.qg_quantize_q8k(A, 300, B, None) == ESHAPE
-    assert L.qg_quantize_q8k(A + 4, 256, B, None) == EALIGN
-    assert L.qg_quantize_q8k(A, 256, A + 512, None) == ESHAPE  # overlap
-    f = L.qgemv_q4k_q8k
+def test_q8_1_validation(L):
+    assert L.qg_q8_1_bytes(3584) == 448 + 3584 + 224
+    assert L.qg_q8_1_bytes(300) == 0
+    assert L.qg_quantize_q8_1(None, 256, B, None) == ENULL
+    assert L.qg_quantize_q8_1(A, 300, B, None) == ESHAPE
+    assert L.qg_quantize_q8_1(A + 4, 256, B, None) == EALIGN
+    assert L.qg_quantize_q8_1(A, 256, A + 512, None) == ESHAPE  # overlap
+    f = L.qgemv_q4k_q8_1
     assert f(C, None, B, 64, 256, None, 0, None) == ENULL
     assert f(C, A, B, 64, 300, None, 0, None) == ESHAPE
     assert f(C, A, B, 0, 256, None, 0, None) == ESHAPE
     assert f(C, A + 8, B, 64, 256, None, 0, None) == EALIGN
-    assert L.qgemv_q4k_q8k_workspace_bytes(3584, 3584) == 0
+    assert L.qgemv_q4k_q8_1_workspace_bytes(3584, 3584) == 0
