@@ -470,6 +470,36 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
                                        "launches_per_step": len(sstages), "per_stage": per_stage}
         log(f"row smalln N={N}: {rows[f'smalln_verify_N{N}']}")
         del sstages, flat
+
+    # the decode step with int8 activations (Q8_1-style, scale and sum per 32):
+    # every x quantized once beforehand (in a model the quantization belongs to the
+    # op that produces x), then the same 112 grouped launches on the integer path
+    xqs = [[qg.quantize_q8_1(m[1]) for m in layer] for layer in layers]
+    qstages = [[(layers[L][i][0], xqs[L][i], layers[L][i][2], layers[L][i][3], layers[L][i][4]) for i in st]
+               for L in range(n_layers) for st in wl.LAYER_STAGES]
+
+    def qstep(sts=qstages):
+        for grp in sts:
+            qg.qgemv_q4k_q8_1_batch(grp, ws=ws)
+
+    ms = graph_ms(torch, qstep, 20)
+    wb = sum(m[0].numel() for grp in qstages for m in grp)
+    b = wb + sum(m[1].numel() + 4 * m[3] for grp in qstages for m in grp)
+    per_stage = {}
+    for k, name in enumerate(["qkv", "o", "gate_up", "down"]):
+        sts = qstages[k::4]
+        nb_ = sum(m[0].numel() + m[1].numel() + 4 * m[3] for m in sts[0])
+        us = graph_ms(torch, lambda sts=sts: qstep(sts), 10) * 1e3 / len(sts)
+        per_stage[name] = {"avg_us": round(us, 3), "GBps": round(nb_ / (us * 1e-6) / 1e9, 1)}
+    xk = layers[0][0][1]
+    xo = torch.empty(qg.q8_1_bytes(xk.numel()), dtype=torch.uint8, device=dev)
+    us_q = graph_ms(torch, lambda: [qg.quantize_q8_1(xk, out=xo) for _ in range(20)], 10) * 1e3 / 20
+    rows["decode_step_int8_activations"] = {
+        "ms_per_step": round(ms, 4), "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": int(b),
+        "launches_per_step": len(qstages), "per_stage": per_stage,
+        "us_quantize_3584": round(us_q, 3), "quantization": "not timed (done once per x beforehand)"}
+    log(f"row decode step, int8 activations: {rows['decode_step_int8_activations']}")
+    del xqs, qstages
     return rows
 
 

@@ -146,6 +146,18 @@ size_t qgemv_q4k_q8_1_workspace_bytes(int64_t M, int64_t K);
 int qgemv_q4k_q8_1(const void* w_packed, const void* xq, float* y, int64_t M, int64_t K,
                    void* workspace, size_t workspace_bytes, qg_stream_t stream);
 
+/* Several independent qgemv_q4k_q8_1 products in one launch (as qgemv_q4k_batch). */
+typedef struct {
+    const void* w_packed;
+    const void* xq;
+    float* y;
+    int64_t M;
+    int64_t K;
+} qg_gemv_q8_1_problem;
+size_t qgemv_q4k_q8_1_batch_workspace_bytes(const qg_gemv_q8_1_problem* problems /* host */, int count);
+int qgemv_q4k_q8_1_batch(const qg_gemv_q8_1_problem* problems /* host */, int count,
+                         void* workspace, size_t workspace_bytes, qg_stream_t stream);
+
 /*
  * Several independent Q4_K GEMVs in one launch (the dotLLM README's fused decode
  * dispatch of Q/K/V and of gate/up). Problems must not write overlapping outputs.

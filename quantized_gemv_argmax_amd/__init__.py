@@ -72,6 +72,8 @@ _SIGS = {
     "qg_quantize_q8_1": (_I, [_P, _I64, _P, _P]),
     "qgemv_q4k_q8_1_workspace_bytes": (_SZ, [_I64, _I64]),
     "qgemv_q4k_q8_1": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
+    "qgemv_q4k_q8_1_batch_workspace_bytes": (_SZ, [ctypes.POINTER(_Problem), _I]),
+    "qgemv_q4k_q8_1_batch": (_I, [ctypes.POINTER(_Problem), _I, _P, _SZ, _P]),
     "qgemv_q6k_workspace_bytes": (_SZ, [_I64, _I64]),
     "qgemv_q6k": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "qgemm_q4k_smalln_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
@@ -295,6 +297,21 @@ def qgemv_q4k_q8_1(w: torch.Tensor, xq: torch.Tensor, M: int, K: int, y: torch.T
     _check("qgemv_q4k_q8_1", lib().qgemv_q4k_q8_1(_ptr(w), _ptr(xq), _ptr(y), M, K, ws.ptr(), ws.nbytes(),
                                                   _stream(xq.device)))
     return y
+
+
+def qgemv_q4k_q8_1_batch(problems, ws: Workspace | None = None):
+    """problems: list of (w_packed, xq, y, M, K); one launch for all of them."""
+    arr = (_Problem * len(problems))()  # same field layout as qg_gemv_q8_1_problem
+    dev = None
+    for i, (w, xq, y, M, K) in enumerate(problems):
+        _need_cuda(w, xq, y)
+        dev = xq.device
+        arr[i] = _Problem(_ptr(w), _ptr(xq), _ptr(y), M, K)
+    need = int(lib().qgemv_q4k_q8_1_batch_workspace_bytes(arr, len(problems)))
+    ws = _ws(ws, need, dev)
+    _check("qgemv_q4k_q8_1_batch", lib().qgemv_q4k_q8_1_batch(arr, len(problems), ws.ptr(), ws.nbytes(),
+                                                              _stream(dev)))
+    return [p[2] for p in problems]
 
 
 def qgemv_q6k(w: torch.Tensor, x: torch.Tensor, M: int, K: int, y: torch.Tensor | None = None,

@@ -153,16 +153,29 @@ QG_DEV float sb_dot8(const SbIn8& v) {
     return fmaf(dd, t, -dm * u);
 }
 
-struct Q81Args {
+struct Q81Prob {
     const uint8_t* w;
     XqArgs xq;
     float* y;
-    int32_t M, nb;
+    int32_t M, nb, wg_begin;
+};
+
+// Up to QG_MAX_BATCH problems in one grid; a workgroup finds its problem from the
+// compact array of first tiles.
+struct Q81Args {
+    int32_t begin[QG_MAX_BATCH];
+    int32_t count;
+    Q81Prob p[QG_MAX_BATCH];
 };
 
 template <int W, int MODE>
-__global__ __launch_bounds__(64 * W) void q4k_q8_1_gemv_kernel(Q81Args P) {
-    const int tile = blockIdx.x;
+__global__ __launch_bounds__(64 * W) void q4k_q8_1_gemv_kernel(Q81Args A) {
+    int k = 0;
+#pragma unroll
+    for (int i = 1; i < QG_MAX_BATCH; ++i)
+        if (i < A.count && (int)blockIdx.x >= A.begin[i]) k = i;
+    const Q81Prob P = A.p[k];
+    const int tile = blockIdx.x - P.wg_begin;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nb = P.nb;
@@ -218,8 +231,8 @@ __global__ __launch_bounds__(64 * W) void q4k_q8_1_gemv_kernel(Q81Args P) {
 }
 
 template <int W>
-void launch(const Q81Args& a, int tiles, hipStream_t s) {
-    if (a.nb <= 4 * W)
+void launch(const Q81Args& a, int tiles, int nb_max, hipStream_t s) {
+    if (nb_max <= 4 * W)
         hipLaunchKernelGGL((q4k_q8_1_gemv_kernel<W, 0>), dim3(tiles), dim3(64 * W), 0, s, a);
     else
         hipLaunchKernelGGL((q4k_q8_1_gemv_kernel<W, 2>), dim3(tiles), dim3(64 * W), 0, s, a);
@@ -251,6 +264,61 @@ int qg_quantize_q8_1(const float* x, int64_t K, void* xq, qg_stream_t stream) {
     return qg::launch_status("qg_quantize_q8_1");
 }
 
+size_t qgemv_q4k_q8_1_batch_workspace_bytes(const qg_gemv_q8_1_problem* problems, int count) {
+    (void)problems;
+    (void)count;
+    return 0;
+}
+
+int qgemv_q4k_q8_1_batch(const qg_gemv_q8_1_problem* pr, int count, void* ws, size_t ws_bytes, qg_stream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    qg::clear_error();
+    if (!pr) return qg::fail(QG_ERR_NULL, "problem list is NULL");
+    if (count < 1 || count > QG_MAX_BATCH)
+        return qg::fail(QG_ERR_SHAPE, "batch count %d not in [1, %d]", count, QG_MAX_BATCH);
+    Q81Args a{};
+    int tiles = 0, nb_max = 1;
+    for (int i = 0; i < count; ++i) {
+        const qg_gemv_q8_1_problem& p = pr[i];
+        if (!p.w_packed || !p.xq || !p.y) return qg::fail(QG_ERR_NULL, "problem %d: NULL pointer", i);
+        if (p.M < 1 || p.M > INT32_MAX - T) return qg::fail(QG_ERR_SHAPE, "problem %d: M=%lld out of range", i, (long long)p.M);
+        if (!k_ok(p.K))
+            return qg::fail(QG_ERR_SHAPE, "problem %d: K=%lld must be a positive multiple of 256 (<= 2^24)", i, (long long)p.K);
+        if (!qg::aligned16(p.w_packed) || !qg::aligned16(p.xq) || !qg::aligned16(p.y))
+            return qg::fail(QG_ERR_ALIGN, "problem %d: pointers must be 16-byte aligned", i);
+        const Q81Layout L = q81_layout(p.K);
+        const uint8_t* b = (const uint8_t*)p.xq;
+        Q81Prob& P = a.p[i];
+        P.w = (const uint8_t*)p.w_packed;
+        P.xq = XqArgs{(const float*)b, (const int8_t*)(b + L.q_off), (const int16_t*)(b + L.s_off)};
+        P.y = p.y;
+        P.M = (int32_t)p.M;
+        P.nb = (int32_t)(p.K / 256);
+        P.wg_begin = tiles;
+        a.begin[i] = tiles;
+        const int64_t t = qg::ceil_div(p.M, T);
+        if ((int64_t)tiles + t > INT32_MAX / 2) return qg::fail(QG_ERR_SHAPE, "batch too large");
+        tiles += (int)t;
+        nb_max = std::max(nb_max, (int)P.nb);
+    }
+    a.count = count;
+    int st = qg::check_device();
+    if (st) return st;
+    int W = 1;
+    while (W < 4 && 4 * W < nb_max) W *= 2;
+    int ew = 0, eu = 0;
+    if (qg::env_pair("QG_Q4K8_CFG", &ew, &eu) && (ew == 1 || ew == 2 || ew == 4 || ew == 8)) W = ew;
+    hipStream_t s = (hipStream_t)stream;
+    switch (W) {
+        case 1: launch<1>(a, tiles, nb_max, s); break;
+        case 2: launch<2>(a, tiles, nb_max, s); break;
+        case 4: launch<4>(a, tiles, nb_max, s); break;
+        default: launch<8>(a, tiles, nb_max, s); break;
+    }
+    return qg::launch_status("qgemv_q4k_q8_1");
+}
+
 size_t qgemv_q4k_q8_1_workspace_bytes(int64_t M, int64_t K) {
     (void)M;
     (void)K;
@@ -259,33 +327,8 @@ size_t qgemv_q4k_q8_1_workspace_bytes(int64_t M, int64_t K) {
 
 int qgemv_q4k_q8_1(const void* w, const void* xq, float* y, int64_t M, int64_t K, void* ws, size_t ws_bytes,
                    qg_stream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
-    qg::clear_error();
-    if (!w || !xq || !y) return qg::fail(QG_ERR_NULL, "NULL pointer");
-    if (M < 1 || M > INT32_MAX - T) return qg::fail(QG_ERR_SHAPE, "M=%lld out of range", (long long)M);
-    if (!k_ok(K)) return qg::fail(QG_ERR_SHAPE, "K=%lld must be a positive multiple of 256 (<= 2^24)", (long long)K);
-    if (!qg::aligned16(w) || !qg::aligned16(xq) || !qg::aligned16(y))
-        return qg::fail(QG_ERR_ALIGN, "pointers must be 16-byte aligned");
-    int st = qg::check_device();
-    if (st) return st;
-    const Q81Layout L = q81_layout(K);
-    const uint8_t* b = (const uint8_t*)xq;
-    Q81Args a{(const uint8_t*)w, {(const float*)b, (const int8_t*)(b + L.q_off), (const int16_t*)(b + L.s_off)}, y,
-              (int32_t)M, (int32_t)(K / 256)};
-    int W = 1;
-    while (W < 4 && 4 * W < a.nb) W *= 2;
-    int ew = 0, eu = 0;
-    if (qg::env_pair("QG_Q4K8_CFG", &ew, &eu) && (ew == 1 || ew == 2 || ew == 4 || ew == 8)) W = ew;
-    const int tiles = (int)qg::ceil_div(M, T);
-    hipStream_t s = (hipStream_t)stream;
-    switch (W) {
-        case 1: launch<1>(a, tiles, s); break;
-        case 2: launch<2>(a, tiles, s); break;
-        case 4: launch<4>(a, tiles, s); break;
-        default: launch<8>(a, tiles, s); break;
-    }
-    return qg::launch_status("qgemv_q4k_q8_1");
+    qg_gemv_q8_1_problem p{w, xq, y, M, K};
+    return qgemv_q4k_q8_1_batch(&p, 1, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -212,3 +212,21 @@ def test_q8_1_validation(L):
     assert f(C, A, B, 0, 256, None, 0, None) == ESHAPE
     assert f(C, A + 8, B, 64, 256, None, 0, None) == EALIGN
     assert L.qgemv_q4k_q8_1_workspace_bytes(3584, 3584) == 0
+
+
+def test_q8_1_batch_validation(L):
+    P = qg._Problem
+    arr = (P * 9)()
+    for i in range(9):
+        arr[i] = P(C, A, B, 64, 256)
+    f = L.qgemv_q4k_q8_1_batch
+    assert f(arr, 0, None, 0, None) == ESHAPE
+    assert f(arr, 9, None, 0, None) == ESHAPE
+    assert f(None, 1, None, 0, None) == ENULL
+    arr[1] = P(C, None, B, 64, 256)
+    assert f(arr, 2, None, 0, None) == ENULL
+    arr[1] = P(C, A, B, 64, 1000)
+    assert f(arr, 2, None, 0, None) == ESHAPE
+    arr[1] = P(C, A + 4, B, 64, 256)
+    assert f(arr, 2, None, 0, None) == EALIGN
+    assert L.qgemv_q4k_q8_1_batch_workspace_bytes(arr, 2) == 0

@@ -120,3 +120,34 @@ def test_deterministic():
     y2 = qg.qgemv_q4k_q8_1(wp, xq, M, K).clone()
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+def test_batch_matches_single_calls():
+    # the attention-input stage (Wq, Wk, Wv on one quantized x) and a ragged problem
+    # with its own activations, in one launch; each output matches the oracle's
+    # quantized product, and the three 3584-column ones equal their single calls bit
+    # for bit (same launch shape, same per-row arithmetic)
+    shapes = [(3584, 3584), (512, 3584), (512, 3584), (77, 768)]
+    x0 = workloads.x_vector(3584, key=(67, 0))
+    xq0 = qg.quantize_q8_1(to_dev(x0))
+    probs, refs = [], []
+    for i, (M, K) in enumerate(shapes):
+        W = workloads.q4k_blocks(M, K, key=(67, i))
+        if K == 3584:
+            xq, x = xq0, x0
+        else:
+            x = workloads.x_vector(K, key=(67, i))
+            xq = qg.quantize_q8_1(to_dev(x))
+        probs.append((packed_q4k(W, M, K), xq, torch.full((M,), float("nan"), device=DEV), M, K))
+        refs.append((W, x))
+    case("qgemv_q4k_q8_1_batch")
+    qg.qgemv_q4k_q8_1_batch(probs)
+    torch.cuda.synchronize()
+    for (w, xq, y, M, K), (W, x) in zip(probs, refs):
+        if K == 3584:
+            single = qg.qgemv_q4k_q8_1(w, xq, M, K)
+            torch.cuda.synchronize()
+            assert torch.equal(y, single), f"M={M} K={K}"
+        d, q, _ = oracle.quantize_q8_1(x)
+        yq, aq = oracle.gemv_q4k_q8_1(W, M, K, d, q)
+        assert np.all(np.abs(y.cpu().numpy() - yq) <= 1e-5 * aq + 1e-6)
