@@ -260,7 +260,7 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     4096x11008 (3 each), LM head + argmax 152064x3584 (2), the same head verifying 5
     columns (2), top-20 + sampling on that head (2), small-N N=5 then N=32 over
     the layers' stages (one grouped launch per stage), Q6_K 3584x18944 (3) and
-    152064x3584 (2)."""
+    152064x3584 (2), int8-activation Q4_K 4096x4096 (3, after one quantization)."""
     M, K = 4096, 4096
     W = wl.q4k_blocks(M, K, key=(1, 0))
     wp = qg.pack_q4k(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
@@ -308,6 +308,14 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
         for c in [wp] + [wp.clone() for _ in range(reps - 1)]:
             qg.qgemv_q6k(c, x, M, K, y=y, ws=ws)
         del wp
+    M, K = 4096, 4096
+    W = wl.q4k_blocks(M, K, key=(1, 0))
+    wp = qg.pack_q4k(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
+    x = torch.from_numpy(wl.x_vector(K, key=(1, 0))).to(dev)
+    xq = qg.quantize_q8_1(x)
+    y = torch.empty(M, device=dev)
+    for c in [wp] + [wp.clone() for _ in range(2)]:
+        qg.qgemv_q4k_q8_1(c, xq, M, K, y=y, ws=ws)
     torch.cuda.synchronize()
     log("counter rows done")
 
