@@ -188,7 +188,8 @@ int qgemv_q8_0(const void* w_packed, const float* x, float* y, int64_t M, int64_
  *   Y[:, n] = W X[:, n] for 0 <= n < N, 1 <= N <= QG_SMALLN_MAX.
  * X is column-major K x N with leading dimension ldx >= K (column n starts at
  * X + n*ldx); Y is column-major M x N with ldy >= M. ldx and ldy must be
- * multiples of 4. Each 32-weight sub-block is a 16 x 16 x 32 fp16 matrix-core
+ * multiples of 4, and X must span less than 2^31 bytes ((N-1)*ldx + K <
+ * 2^29 elements; otherwise QG_ERR_SHAPE). Each 32-weight sub-block is a 16 x 16 x 32 fp16 matrix-core
  * product of the activations (rounded to fp16) with the quants, accumulated and
  * scaled in fp32. Only Y[0..M) of each column is written. When the launch
  * splits K among workgroups (small M), their partial sums meet in a fixed order

@@ -297,6 +297,9 @@ int sn_validate(const void* w, const float* X, int64_t ldx, const float* Y, int6
     if (ldx < K || ldy < M || ldx % 4 || ldy % 4)
         return qg::fail(QG_ERR_SHAPE, "ldx=%lld / ldy=%lld must be >= K / M and multiples of 4", (long long)ldx,
                         (long long)ldy);
+    // the activations are read through one buffer resource whose 32-bit range must
+    // stay below the out-of-range offset used for columns past N
+    if ((N - 1) * ldx + K > INT32_MAX / 4) return qg::fail(QG_ERR_SHAPE, "X extent exceeds 2^31 bytes");
     if (!qg::aligned16(w) || !qg::aligned16(X) || !qg::aligned16(Y))
         return qg::fail(QG_ERR_ALIGN, "pointers must be 16-byte aligned");
     return QG_OK;

@@ -92,6 +92,9 @@ def test_smalln_validation(L):
     assert f(C, A, 256, B, 60, 64, 256, 5, None, 0, None) == ESHAPE   # ldy < M
     assert f(C, A, 258, B, 64, 64, 256, 5, None, 0, None) == ESHAPE   # ldx % 4
     assert f(C, A + 4, 256, B, 64, 64, 256, 5, None, 0, None) == EALIGN
+    # the activations must fit one 2^31-byte buffer range
+    assert f(C, A, 1 << 26, B, 64, 64, 256, 32, None, 0, None) == ESHAPE
+    assert f(C, A, 1 << 26, B, 64, 64, 256, 1, None, 0, None) != ESHAPE or "X extent" not in qg.last_error()
     assert L.qgemm_q4k_smalln_workspace_bytes(3584, 3584, 5) == 0
 
 
