@@ -1,0 +1,83 @@
+"""Entry points captured in a HIP graph: every replay, with eager work and
+synchronizations in between, must reproduce the eager results bit for bit (the
+kernels are deterministic and every workspace is left all-zero, so replays see
+the same state as the eager call)."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_gemv_argmax_amd as qg
+import workloads
+from tests.gpu_helpers import DEV, case, packed_q4k, packed_q8_0, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_match_eager():
+    torch.cuda.set_device(0)
+    ws = qg.Workspace(DEV, 8 << 20)
+    # q/k/v stage of a 7B layer (grouped), LM head argmax, LM head top-k with a
+    # sampler, small-N verify N=5, int8-activation product
+    stage = []
+    for i, (M, K) in enumerate([(3584, 3584), (512, 3584), (512, 3584)]):
+        W = workloads.q4k_blocks(M, K, key=(80, i))
+        stage.append((packed_q4k(W, M, K), to_dev(workloads.x_vector(K, key=(80, i))),
+                      torch.empty(M, device=DEV), M, K))
+    Mh, Kh = 20000, 1024
+    wh = packed_q8_0(workloads.q8_0_blocks(Mh, Kh, key=(81,)), Mh, Kh)
+    xh = to_dev((workloads.x_vector(Kh, key=(81,)) * 0.05).astype(np.float32))
+    oi = torch.empty(1, dtype=torch.int32, device=DEV)
+    ov = torch.empty(1, device=DEV)
+    u = torch.full((1,), 0.3, device=DEV)
+    tk = qg.TopK(20, DEV, True)
+    lg = torch.empty(Mh, device=DEV)
+    M5, K5 = 3584, 3584
+    X5 = to_dev(workloads.x_columns(K5, 5, key=(82,)))
+    Y5 = torch.empty((5, M5), device=DEV)
+    xq = torch.empty(qg.q8_1_bytes(K5), dtype=torch.uint8, device=DEV)
+    y8 = torch.empty(M5, device=DEV)
+
+    def work():
+        qg.qgemv_q4k_batch(stage, ws=ws)
+        qg.lmhead_argmax(wh, xh, Mh, Kh, out_index=oi, out_value=ov, ws=ws)
+        qg.lmhead_topk(wh, xh, Mh, Kh, 20, logits=lg, sampler=(0.9, 0.95, 0.02, u), ws=ws, out=tk)
+        qg.qgemm_q4k_smalln(stage[0][0], X5, M5, K5, Y=Y5, ws=ws)
+        qg.quantize_q8_1(stage[0][1], out=xq)
+        qg.qgemv_q4k_q8_1(stage[0][0], xq, M5, K5, y=y8, ws=ws)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        outs = [p[2] for p in stage] + [oi, ov, tk.index, tk.logit, tk.logprob, tk.lse, tk.token, lg, Y5, xq, y8]
+        return [t.clone() for t in outs]
+
+    case("graph capture: eager reference")
+    work()
+    ref = snapshot()
+    assert int(ws.buf.count_nonzero()) == 0
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(4):
+        # scribble over the outputs, then replay and compare
+        for t in snapshot_targets(stage, oi, ov, tk, lg, Y5, xq, y8):
+            t.zero_()
+        case(f"graph replay {rep}")
+        g.replay()
+        got = snapshot()
+        for k, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), f"replay {rep}: output {k} differs from the eager result"
+        assert int(ws.buf.count_nonzero()) == 0
+        # eager work between replays on the same buffers
+        qg.qgemv_q4k(stage[1][0], stage[1][1], stage[1][3], stage[1][4], y=stage[1][2], ws=ws)
+        torch.cuda.synchronize()
+
+
+def snapshot_targets(stage, oi, ov, tk, lg, Y5, xq, y8):
+    return [p[2] for p in stage] + [oi, ov, tk.index, tk.logit, tk.logprob, tk.lse, tk.token, lg, Y5, xq, y8]
