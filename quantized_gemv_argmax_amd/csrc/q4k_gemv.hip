@@ -75,6 +75,25 @@ QG_DEV void load_sb(SbIn& d, const uint4* __restrict__ seg, const float* __restr
     for (int s = 0; s < 9; ++s) d.s[s] = qg_stream_load(sb + s * rt);
 }
 
+// The same loads as raw buffer loads: one resource per tile (weights) and one for
+// x, a per-lane byte offset and the segment / activation offsets as scalar
+// operands, so that a super-block costs one vector address operation instead of
+// one 64-bit address per load.
+QG_DEV void load_sb_buf(SbIn& d, __amdgpu_buffer_rsrc_t wr, uint32_t vrow, __amdgpu_buffer_rsrc_t xr, uint32_t vx,
+                        int b, int rt) {
+    const uint32_t vxb = vx + (uint32_t)b * 1024u;
+    d.xa = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, vxb, 0, 0));
+    d.xb = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, vxb, 16, 0));
+    d.xc = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, vxb, 128, 0));
+    d.xd = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, vxb, 144, 0));
+    const uint32_t vb = vrow + (uint32_t)b * 9u * (uint32_t)rt * 16u;
+#pragma unroll
+    for (int s = 0; s < 9; ++s) {
+        const qg_u4v v = __builtin_amdgcn_raw_buffer_load_b128(wr, vb, s * rt * 16, kQgNonTemporal);
+        d.s[s] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+}
+
 // Contribution of one super-block for this lane's row.
 QG_DEV float sb_dot(const SbIn& d) {
     // activation pairs in the order the dot products consume them
@@ -160,22 +179,25 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(Q4Args a) {
 
     // activation slot of this lane: quant segment p = i/2, dwords 2(i%2), +1
     const int p = i >> 1;
-    const float* xk = P.x + 64 * (p >> 1) + 16 * (p & 1) + 8 * (i & 1);
+    const uint32_t vx = 4u * (uint32_t)(64 * (p >> 1) + 16 * (p & 1) + 8 * (i & 1));
     // rows past a ragged tile's end re-read the last row; their results are dropped
-    const uint4* __restrict__ seg =
-        reinterpret_cast<const uint4*>(P.w + (size_t)tile * T * nb * 144) + min(i, rt - 1);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(P.w + (size_t)tile * T * nb * 144), (short)0, rt * nb * 144, kQgRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)P.x, (short)0, nb * 1024, kQgRawBufferFlags);
+    const uint32_t vrow = 16u * (uint32_t)min(i, rt - 1);
 
     float acc = 0.f;
     if constexpr (MODE == 0) {  // one super-block per K-group (4W >= K/256)
         SbIn b0;
-        load_sb(b0, seg, xk, min(kg, nb - 1), rt);
+        load_sb_buf(b0, wr, vrow, xr, vx, min(kg, nb - 1), rt);
         const float v0 = sb_dot(b0);
         acc = (kg < nb) ? v0 : 0.f;
     } else if constexpr (MODE == 1) {
         const int niter = (nb + G - 1) / G;
         for (int it = 0; it < niter; ++it) {
             SbIn b0;
-            load_sb(b0, seg, xk, min(kg + G * it, nb - 1), rt);
+            load_sb_buf(b0, wr, vrow, xr, vx, min(kg + G * it, nb - 1), rt);
             const float v0 = sb_dot(b0);
             acc += (kg + G * it < nb) ? v0 : 0.f;
         }
@@ -187,14 +209,14 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(Q4Args a) {
         // loop has a single exit, so the loop-carried load state, and with it every
         // wait count, is exact: waiting for one super-block never waits for the next.
         SbIn b0, b1;
-        load_sb(b0, seg, xk, min(kg, nb - 1), rt);
+        load_sb_buf(b0, wr, vrow, xr, vx, min(kg, nb - 1), rt);
         int it = 0;
         for (; it + 2 <= niter; it += 2) {
-            load_sb(b1, seg, xk, min(kg + G * (it + 1), nb - 1), rt);
+            load_sb_buf(b1, wr, vrow, xr, vx, min(kg + G * (it + 1), nb - 1), rt);
             __builtin_amdgcn_sched_barrier(0);  // issue the loads before any wait
             const float v0 = sb_dot(b0);
             acc += (kg + G * it < nb) ? v0 : 0.f;
-            load_sb(b0, seg, xk, min(kg + G * (it + 2), nb - 1), rt);
+            load_sb_buf(b0, wr, vrow, xr, vx, min(kg + G * (it + 2), nb - 1), rt);
             __builtin_amdgcn_sched_barrier(0);
             const float v1 = sb_dot(b1);
             acc += (kg + G * (it + 1) < nb) ? v1 : 0.f;
