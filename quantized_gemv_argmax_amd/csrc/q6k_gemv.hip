@@ -61,17 +61,26 @@ struct Q6In {
     float4 xa, xb, xc, xd;    // low run dwords 0, 1, then high run dwords 0, 1
 };
 
-QG_DEV void load_q6(Q6In& v, const uint4* __restrict__ seg, const uint16_t* __restrict__ dp,
-                    const float* __restrict__ xk, int b, int rt) {
-    const float* xb = xk + 256 * b;
-    v.xa = *reinterpret_cast<const float4*>(xb);
-    v.xb = *reinterpret_cast<const float4*>(xb + 4);
-    v.xc = *reinterpret_cast<const float4*>(xb + 64);
-    v.xd = *reinterpret_cast<const float4*>(xb + 68);
-    const uint4* sb = seg + (size_t)b * kSegs * rt;
+// Raw buffer loads: one resource for the tile and one for x, a per-lane byte
+// offset, the segment and activation offsets as scalar operands.
+struct Q6Src {
+    __amdgpu_buffer_rsrc_t w, x;
+    uint32_t vrow, vd, vx;  // this lane's row in the segments / in the d region, its x slot
+};
+
+QG_DEV void load_q6(Q6In& v, const Q6Src& q, int b, int rt) {
+    const uint32_t vxb = q.vx + (uint32_t)b * 1024u;
+    v.xa = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(q.x, vxb, 0, 0));
+    v.xb = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(q.x, vxb, 16, 0));
+    v.xc = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(q.x, vxb, 256, 0));
+    v.xd = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(q.x, vxb, 272, 0));
+    const uint32_t vb = q.vrow + (uint32_t)b * (uint32_t)kSegs * (uint32_t)rt * 16u;
 #pragma unroll
-    for (int s = 0; s < kSegs; ++s) v.s[s] = qg_stream_load(sb + s * rt);
-    v.d = __builtin_nontemporal_load(dp + (size_t)b * rt);
+    for (int s = 0; s < kSegs; ++s) {
+        const qg_u4v t = __builtin_amdgcn_raw_buffer_load_b128(q.w, vb, s * rt * 16, kQgNonTemporal);
+        v.s[s] = make_uint4(t.x, t.y, t.z, t.w);
+    }
+    v.d = __builtin_amdgcn_raw_buffer_load_b16(q.w, q.vd + (uint32_t)b * (uint32_t)rt * 2u, 0, kQgNonTemporal);
 }
 
 QG_DEV float sc_i8(const uint4& sc, int j) {
@@ -154,30 +163,33 @@ __global__ __launch_bounds__(64 * W) void q6k_gemv_kernel(Q6Args P) {
 
     // activation slot of this lane: ql segment s = i/2 = 4h + 2pp + c, dwords 2(i%2), +1
     const int s = i >> 1;
-    const float* xk = P.x + 128 * (s >> 2) + 32 * ((s >> 1) & 1) + 16 * (s & 1) + 8 * (i & 1);
+    Q6Src src;
+    src.vx = 4u * (uint32_t)(128 * (s >> 2) + 32 * ((s >> 1) & 1) + 16 * (s & 1) + 8 * (i & 1));
     // rows past a ragged tile's end re-read the last row; their results are dropped
-    const uint8_t* tb = P.w + (size_t)tile * T * nb * kBlockBytes;
-    const uint4* __restrict__ seg = reinterpret_cast<const uint4*>(tb) + min(i, rt - 1);
-    const uint16_t* __restrict__ dp =
-        reinterpret_cast<const uint16_t*>(tb + (size_t)nb * kSegs * rt * 16) + min(i, rt - 1);
+    const uint32_t r = (uint32_t)min(i, rt - 1);
+    src.w = __builtin_amdgcn_make_buffer_rsrc((void*)(P.w + (size_t)tile * T * nb * kBlockBytes), (short)0,
+                                              rt * nb * kBlockBytes, kQgRawBufferFlags);
+    src.x = __builtin_amdgcn_make_buffer_rsrc((void*)P.x, (short)0, nb * 1024, kQgRawBufferFlags);
+    src.vrow = 16u * r;
+    src.vd = (uint32_t)nb * kSegs * (uint32_t)rt * 16u + 2u * r;
 
     float acc = 0.f;
     if constexpr (MODE == 0) {
         Q6In b0;
-        load_q6(b0, seg, dp, xk, min(kg, nb - 1), rt);
+        load_q6(b0, src, min(kg, nb - 1), rt);
         const float v0 = q6_dot(b0);
         acc = (kg < nb) ? v0 : 0.f;
     } else {
         const int niter = (nb + G - 1) / G;
         Q6In b0, b1;
-        load_q6(b0, seg, dp, xk, min(kg, nb - 1), rt);
+        load_q6(b0, src, min(kg, nb - 1), rt);
         int it = 0;
         for (; it + 2 <= niter; it += 2) {
-            load_q6(b1, seg, dp, xk, min(kg + G * (it + 1), nb - 1), rt);
+            load_q6(b1, src, min(kg + G * (it + 1), nb - 1), rt);
             __builtin_amdgcn_sched_barrier(0);
             const float v0 = q6_dot(b0);
             acc += (kg + G * it < nb) ? v0 : 0.f;
-            load_q6(b0, seg, dp, xk, min(kg + G * (it + 2), nb - 1), rt);
+            load_q6(b0, src, min(kg + G * (it + 2), nb - 1), rt);
             __builtin_amdgcn_sched_barrier(0);
             const float v1 = q6_dot(b1);
             acc += (kg + G * (it + 1) < nb) ? v1 : 0.f;
