@@ -36,6 +36,8 @@
 // their results are dropped.
 #include <algorithm>
 #include <climits>
+#include <cstdlib>
+#include <string>
 
 #include "qg_device.h"
 #include "qg_host.h"
@@ -286,6 +288,273 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
     }
 }
 
+// ------------------------------------------------------------ LDS-staged form
+// The kernel above keeps each wavefront's activations in registers (16 per lane
+// and column block for every 64-weight unit), which leaves room for only two units
+// of weights in flight per wavefront: too few bytes per CU to cover the HBM
+// latency. Here the activations go through LDS instead, and the two kinds of work
+// are given to different wavefronts, since a wavefront's loads complete in issue
+// order and a wait for an activation load would also wait for every weight load
+// issued before it:
+//   - WP producer wavefronts stage the activations of a chunk of WC super-blocks
+//     (256 WC values per column, all columns) into LDS, already rounded to fp16 and
+//     in the element order of the A operand; two chunk buffers alternate;
+//   - WC consumer wavefronts each take one super-block of the chunk for the TW
+//     tiles; their weight loads run D chunks ahead in a ring of register buffers
+//     and never wait behind an activation load.
+// One s_barrier per chunk separates the staging of chunk q + 1 from the use of
+// chunk q; it does not wait for outstanding memory loads, so the weight queues
+// stay full across it. LDS row layout: buffer 0 holds columns 0..N-1, buffer 1
+// columns N..2N-1, then one row of zeros, which lanes of columns past N (and every
+// lane of a super-block past the end of K) read instead. Rows are padded by 16
+// bytes so that the sixteen rows read by one instruction start in different banks.
+template <int WC>
+struct SwGeom {
+    static constexpr int kRowBytes = (WC * 256 + 8) * 2;
+};
+
+template <int TW>
+struct SwItem {
+    uint4 hdr[TW];   // d, dmin, 12 scale bytes of this lane's row
+    uint2 q[TW][4];  // quant bytes 8 (l / 16)..+7 of units g = 0..3 (sub-blocks 2g, 2g + 1)
+};
+
+template <int C, int TW>
+QG_DEV void sw_load(SwItem<TW>& it, const SnTiles<TW>& tl, const SnLane<C, TW>& ln, int b) {
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+        const int sb = b * 9 * 16 * tl.rt[t];
+        const qg_u4v h = __builtin_amdgcn_raw_buffer_load_b128(tl.w[t], ln.hdr[t], sb, kNonTemporal);
+        it.hdr[t] = make_uint4(h.x, h.y, h.z, h.w);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const qg_u2v q =
+                __builtin_amdgcn_raw_buffer_load_b64(tl.w[t], ln.q[t], sb + (1 + 2 * g) * 16 * tl.rt[t], kNonTemporal);
+            it.q[t][g] = make_uint2(q.x, q.y);
+        }
+    }
+}
+
+// One super-block for the TW tiles: a[c] is the LDS byte address of this lane's
+// first A operand (column block c, sub-block 0).
+template <int C, int TW>
+QG_DEV void sw_dot(qg_f4 (&acc)[TW][C], const SwItem<TW>& it, const unsigned char* lds, const uint32_t (&a)[C]) {
+    const qg_h8 ones = qg_ones_h8();
+    const qg_f4 zero = {0.f, 0.f, 0.f, 0.f};
+    // per tile: d (x 2^24: the quants enter as q * 2^-24), dmin and the 6-bit
+    // scales and mins of the eight sub-blocks
+    float dd[TW], dm[TW];
+    uint32_t sc03[TW], m03[TW], sc47[TW], m47[TW];
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+        const uint4 hd = it.hdr[t];
+        dd[t] = qg_half_lo(hd.x) * 16777216.0f;
+        dm[t] = qg_half_hi(hd.x);
+        sc03[t] = hd.y & 0x3f3f3f3fu;
+        m03[t] = hd.z & 0x3f3f3f3fu;
+        sc47[t] = (hd.w & 0x0f0f0f0fu) | ((hd.y >> 2) & 0x30303030u);
+        m47[t] = ((hd.w >> 4) & 0x0f0f0f0fu) | ((hd.z >> 2) & 0x30303030u);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        qg_h8 a_lo[C], a_hi[C];
+        qg_f4 x_lo[C], x_hi[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            a_lo[c] = *reinterpret_cast<const qg_h8*>(lds + a[c] + 128 * g);
+            a_hi[c] = *reinterpret_cast<const qg_h8*>(lds + a[c] + 128 * g + 64);
+            x_lo[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[c], ones, zero, 0, 0, 0);
+            x_hi[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[c], ones, zero, 0, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
+            const uint32_t scw = g < 2 ? sc03[t] : sc47[t];
+            const uint32_t mw = g < 2 ? m03[t] : m47[t];
+            const int kb = 2 * (g & 1);
+            const float s_lo = dd[t] * qg_byte_f(scw, kb);
+            const float s_hi = dd[t] * 0.0625f * qg_byte_f(scw, kb + 1);
+            const float m_lo = dm[t] * qg_byte_f(mw, kb);
+            const float m_hi = dm[t] * qg_byte_f(mw, kb + 1);
+            const uint32_t w0 = it.q[t][g].x, w1 = it.q[t][g].y;
+            const uint32_t w0s = w0 >> 8, w1s = w1 >> 8;
+            const qg_h8 b_lo = __builtin_bit_cast(
+                qg_h8, make_uint4(w0 & 0x000f000fu, w0s & 0x000f000fu, w1 & 0x000f000fu, w1s & 0x000f000fu));
+            const qg_h8 b_hi = __builtin_bit_cast(
+                qg_h8, make_uint4(w0 & 0x00f000f0u, w0s & 0x00f000f0u, w1 & 0x00f000f0u, w1s & 0x00f000f0u));
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const qg_f4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[c], b_lo, zero, 0, 0, 0);
+                const qg_f4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[c], b_hi, zero, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float v = acc[t][c][e];
+                    v = fmaf(s_lo, s0[e], v);
+                    v = fmaf(s_hi, s1[e], v);
+                    v = fmaf(-m_lo, x_lo[c][e], v);
+                    v = fmaf(-m_hi, x_hi[c][e], v);
+                    acc[t][c][e] = v;
+                }
+            }
+        }
+    }
+}
+
+// Workgroup barrier for the chunk hand-over: LDS operations complete first; pending
+// global loads are not waited for.
+QG_DEV void sw_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Producer: activations of chunk q (super-blocks q WC .. q WC + WC - 1, the last
+// chunk possibly shorter) into the LDS rows starting at `row0`. A pass covers CPP
+// columns, lane pl taking 8-element group pl % LPC of column pl / LPC; PB passes
+// have their loads in flight together.
+template <int WC, int WP>
+QG_DEV void sw_stage(unsigned char* lds, uint32_t row0, __amdgpu_buffer_rsrc_t xr, const SnProb& P, int q, int pl) {
+    constexpr int RB = SwGeom<WC>::kRowBytes;
+    constexpr int LPC = 32 * WC;  // 8-element groups per column and chunk
+    static_assert((64 * WP) % LPC == 0, "producer lanes must cover whole chunk rows");
+    constexpr int CPP = 64 * WP / LPC;
+    constexpr int PB = 8;
+    const int k0 = q * WC * 256;
+    const int g8n = min(WC, P.nb - q * WC) * 32;
+    const int g = pl % LPC;
+    const int passes = (P.N + CPP - 1) / CPP;
+    for (int p0 = 0; p0 < passes; p0 += PB) {
+        float4 v[PB][2];
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const int n = (p0 + j) * CPP + pl / LPC;
+            const uint32_t off =
+                (n < P.N && g < g8n) ? (uint32_t)(((int64_t)n * P.ldx + k0 + 8 * g) * 4) : kOutOfRange;
+            v[j][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+            v[j][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 16, 0));
+        }
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const int n = (p0 + j) * CPP + pl / LPC;
+            if (n < P.N && g < g8n)
+                *reinterpret_cast<qg_h8*>(lds + row0 + n * RB + 16 * g) = qg_a_operand(v[j][0], v[j][1]);
+        }
+    }
+}
+
+template <int C, int TW, int WC, int WP, int D>
+__global__ __launch_bounds__(64 * (WC + WP)) void q4k_smalln_lds_kernel(SnArgs a) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    constexpr int RB = SwGeom<WC>::kRowBytes;
+    const int wg = blockIdx.x;
+    int k = 0;
+#pragma unroll
+    for (int i = 1; i < QG_MAX_BATCH; ++i)
+        if (i < a.count && wg >= a.begin[i]) k = i;
+    const SnProb P = a.p[k];
+    const int tile0 = (wg - P.wg_begin) * TW;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nq = (P.nb + WC - 1) / WC;
+    const uint32_t zrow = (uint32_t)(2 * P.N * RB);
+
+    qg_f4 acc[TW][C];
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[t][c] = qg_f4{0.f, 0.f, 0.f, 0.f};
+    const int i = lane & 15, s = lane >> 4;
+
+    if (wave >= WC) {
+        // ---------------- producer
+        const int pl = (wave - WC) * 64 + lane;
+        for (int o = 16 * pl; o < RB; o += 16 * 64 * WP)
+            *reinterpret_cast<uint4*>(lds + zrow + o) = make_uint4(0u, 0u, 0u, 0u);
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)P.X, (short)0, (int)(((int64_t)(P.N - 1) * P.ldx + (int64_t)P.nb * 256) * 4), kQgRawBufferFlags);
+        sw_stage<WC, WP>(lds, 0, xr, P, 0, pl);
+        sw_barrier();
+        for (int q = 0; q < nq; q += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                // during chunk q + j: stage chunk q + j + 1 into the other buffer
+                if (q + j + 1 < nq) sw_stage<WC, WP>(lds, ((q + j + 1) & 1) * P.N * RB, xr, P, q + j + 1, pl);
+                sw_barrier();
+            }
+        }
+    } else {
+        // ---------------- consumers: wavefront w takes super-block q WC + w of chunk q
+        const int w = wave;
+        SnTiles<TW> tl;
+        SnLane<C, TW> ln;
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
+            const int tc = min(tile0 + t, P.tiles - 1);
+            tl.rt[t] = min(T, P.M - tc * T);
+            tl.w[t] = __builtin_amdgcn_make_buffer_rsrc((void*)(P.w + (size_t)tc * T * P.nb * 144), (short)0,
+                                                        tl.rt[t] * P.nb * 144, kQgRawBufferFlags);
+            const uint32_t r = (uint32_t)min(i, tl.rt[t] - 1);
+            ln.hdr[t] = 16 * r;
+            ln.q[t] = 16 * r + 8 * (s & 1) + (uint32_t)(s >> 1) * 16 * tl.rt[t];
+        }
+        // this lane's A-operand byte offsets: column n = 16 c + i, elements
+        // 256 w + 8 s.. of the chunk (+ 64 g, + 32 for the high sub-block)
+        const uint32_t kw = (uint32_t)(256 * w + 8 * s) * 2;
+        uint32_t a0[C], a1[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int n = 16 * c + i;
+            a0[c] = (n < P.N ? (uint32_t)(n * RB) : zrow) + kw;
+            a1[c] = (n < P.N ? (uint32_t)((P.N + n) * RB) : zrow) + kw;
+        }
+        const uint32_t az = zrow + kw;
+        SwItem<TW> ring[D];
+#pragma unroll
+        for (int j = 0; j < D; ++j) sw_load<C, TW>(ring[j], tl, ln, min(j * WC + w, P.nb - 1));
+        sw_barrier();
+        for (int q = 0; q < nq; q += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                const int qq = q + j;
+                // a super-block past the end of K (or a chunk past the last) reads
+                // the zero row: its products are exact zeros
+                const bool valid = qq * WC + w < P.nb;
+                uint32_t ad[C];
+#pragma unroll
+                for (int c = 0; c < C; ++c) ad[c] = valid ? ((qq & 1) ? a1[c] : a0[c]) : az;
+                sw_dot<C, TW>(acc, ring[j], lds, ad);
+                sw_load<C, TW>(ring[j], tl, ln, min((qq + D) * WC + w, P.nb - 1));
+                sw_barrier();
+            }
+        }
+    }
+
+    // partial sums of the WC consumers meet in LDS (the chunk buffers are free now)
+    float* red = reinterpret_cast<float*>(lds);
+    if (wave < WC) {
+#pragma unroll
+        for (int t = 0; t < TW; ++t)
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) red[(wave * TW * C * 4 + (t * C + c) * 4 + e) * 64 + lane] = acc[t][c][e];
+    }
+    sw_barrier();
+    if (wave != 0) return;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+        if (tile0 + t < P.tiles && i < min(T, P.M - (tile0 + t) * T)) {
+            const int row = (tile0 + t) * T + i;
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int n = 16 * c + 4 * s + e;
+                    if (n >= P.N) continue;
+                    float v = red[((t * C + c) * 4 + e) * 64 + lane];
+#pragma unroll
+                    for (int w = 1; w < WC; ++w) v += red[(w * TW * C * 4 + (t * C + c) * 4 + e) * 64 + lane];
+                    P.Y[(int64_t)n * P.ldy + row] = v;
+                }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ host side
 int sn_validate(const void* w, const float* X, int64_t ldx, const float* Y, int64_t ldy, int64_t M, int64_t K,
                 int64_t N) {
@@ -331,6 +600,8 @@ SnProb make_sn(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy
 // least two units.
 struct SnCfg {
     int W, TW, KS;
+    bool lds;  // LDS-staged kernel (KS = 1 only)
+    int D;     // its weight-queue depth in chunks
 };
 SnCfg choose_cfg(const SnArgs& a, int C) {
     int units = INT_MAX;
@@ -339,7 +610,7 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
         units = std::min(units, a.p[i].nb * 4);
         tiles += a.p[i].tiles;
     }
-    SnCfg c{1, tiles > 256 ? 2 : 1, 1};
+    SnCfg c{1, tiles > 256 ? 2 : 1, 1, false, 3};
     if (C == 2 && tiles > 1024) c.TW = 4;
     int ew = 0, et = 0, ek = 0;
     const bool env = qg::env_pair("QG_SN_CFG", &ew, &et);
@@ -352,7 +623,69 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
     const int wmax = c.TW == 4 ? 4 : 8;
     while (c.W < wmax && 2 * c.W <= units / c.KS / 2) c.W *= 2;
     if (env && (ew == 1 || ew == 2 || ew == 4 || ew == 8 || (ew == 16 && C == 1 && c.TW == 1))) c.W = ew;
+    // The LDS-staged kernel pays off where a workgroup walks many chunks: it is the
+    // default when every problem has at least 32 super-blocks per row (K >= 8192;
+    // measured on the 7B shapes: the down projection, K = 18944, 23.9 -> 21.3 us at
+    // N = 5 and 72 -> 49 us at N = 32, while the K = 3584 stages were slower).
+    // QG_SN_IMPL=regs / lds forces one form; the register form's launch-shape
+    // variables select it too. Tiles per workgroup: one up to 1024 tiles, then two
+    // (four for more than 16 columns); QG_SNL_CFG=TW,D overrides.
+    const char* impl = getenv("QG_SN_IMPL");
+    const std::string im = impl ? impl : "";
+    c.lds = c.KS == 1 && !env && im != "regs" && (im == "lds" || units >= 32 * 4);
+    if (c.lds) {
+        c.TW = tiles > 1024 ? (C == 2 ? 4 : 2) : (C == 2 && tiles > 256 ? 2 : 1);
+        c.D = 2;
+        int et2 = 0, ed = 0;
+        if (qg::env_pair("QG_SNL_CFG", &et2, &ed)) {
+            if (et2 == 1 || et2 == 2 || (et2 == 4 && C == 2)) c.TW = et2;
+            if (ed >= 2 && ed <= (C == 2 ? 3 : 4)) c.D = ed;
+        }
+        if (C == 2 && c.TW == 4) c.D = 2;  // a deeper queue would not fit the registers
+    }
     return c;
+}
+
+constexpr int kSwProducers = 4;
+template <int C>
+constexpr int sw_consumers() {
+    return C == 1 ? 8 : 4;
+}
+
+// Dynamic LDS of the LDS-staged kernel: two chunk buffers of N rows and the zero
+// row, or the consumers' partial sums if larger.
+size_t sw_lds_bytes(int C, int TW, int nmax) {
+    const int WC = C == 1 ? sw_consumers<1>() : sw_consumers<2>();
+    const size_t rb = (size_t)(WC * 256 + 8) * 2;
+    return std::max((2 * (size_t)nmax + 1) * rb, (size_t)WC * TW * C * 4 * 64 * 4);
+}
+
+template <int C, int TW, int D>
+void launch_lds(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
+    constexpr int WC = sw_consumers<C>();
+    const auto kern = q4k_smalln_lds_kernel<C, TW, WC, kSwProducers, D>;
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * (WC + kSwProducers)), lds, s, a);
+}
+
+void launch_lds_any(const SnArgs& a, int grid, int C, int TW, int D, size_t lds, hipStream_t s) {
+    switch (100 * C + 10 * TW + D) {
+        case 112: launch_lds<1, 1, 2>(a, grid, lds, s); break;
+        case 113: launch_lds<1, 1, 3>(a, grid, lds, s); break;
+        case 114: launch_lds<1, 1, 4>(a, grid, lds, s); break;
+        case 122: launch_lds<1, 2, 2>(a, grid, lds, s); break;
+        case 123: launch_lds<1, 2, 3>(a, grid, lds, s); break;
+        case 124: launch_lds<1, 2, 4>(a, grid, lds, s); break;
+        case 212: launch_lds<2, 1, 2>(a, grid, lds, s); break;
+        case 213: launch_lds<2, 1, 3>(a, grid, lds, s); break;
+        case 222: launch_lds<2, 2, 2>(a, grid, lds, s); break;
+        case 223: launch_lds<2, 2, 3>(a, grid, lds, s); break;
+        default: launch_lds<2, 4, 2>(a, grid, lds, s); break;
+    }
 }
 
 template <int C, int TW>
@@ -371,7 +704,7 @@ void launch(const SnArgs& a, int grid, int W, hipStream_t s) {
 // Validates the problems and fills the kernel arguments and launch shape. With
 // ws_needed set, only the workspace size is computed (pointers are not checked).
 int plan(const qg_gemm_problem* probs, int count, bool size_only, SnArgs& a, SnCfg& cfg, int& C, int64_t& wgs,
-         size_t& ws_needed) {
+         size_t& ws_needed, int* nmax_out = nullptr) {
     if (!probs) return qg::fail(QG_ERR_NULL, "NULL problem list");
     if (count < 1 || count > QG_MAX_BATCH)
         return qg::fail(QG_ERR_SHAPE, "count=%d not in [1, %d]", count, QG_MAX_BATCH);
@@ -388,6 +721,7 @@ int plan(const qg_gemm_problem* probs, int count, bool size_only, SnArgs& a, SnC
         nmax = std::max(nmax, a.p[i].N);
     }
     C = nmax > 16 ? 2 : 1;
+    if (nmax_out) *nmax_out = nmax;
     cfg = choose_cfg(a, C);
     a.ks = cfg.KS;
     wgs = 0;
@@ -408,7 +742,8 @@ int run(const qg_gemm_problem* probs, int count, void* ws, size_t ws_bytes, hipS
     int C;
     int64_t wgs;
     size_t need;
-    int st = plan(probs, count, false, a, cfg, C, wgs, need);
+    int nmax = 0;
+    int st = plan(probs, count, false, a, cfg, C, wgs, need, &nmax);
     if (st) return st;
     if (need > 0) {
         if (!ws) return qg::fail(QG_ERR_WORKSPACE, "a workspace of %zu bytes is required", need);
@@ -422,6 +757,10 @@ int run(const qg_gemm_problem* probs, int count, void* ws, size_t ws_bytes, hipS
     }
     st = qg::check_device();
     if (st) return st;
+    if (cfg.lds) {
+        launch_lds_any(a, (int)wgs, C, cfg.TW, cfg.D, sw_lds_bytes(C, cfg.TW, nmax), stream);
+        return qg::launch_status("qgemm_q4k_smalln");
+    }
     const int key = 10 * C + cfg.TW;
     switch (key) {
         case 11: launch<1, 1>(a, (int)wgs, cfg.W, stream); break;

@@ -147,3 +147,71 @@ def test_split_k_exchange(ks, N, monkeypatch):
         Yc = Y.cpu().numpy()[:, :M][:, ::3]
         for n in range(N):
             assert_within(Yc[n], Yr[n], Ar[n], f"split-K {ks} M={M} K={K} col {n}")
+
+
+# LDS-staged form (producer wavefronts stage the activations per chunk of super-blocks,
+# consumer wavefronts keep their weight loads chunks ahead): forced on shapes whose
+# super-block counts leave a short last chunk (nb % 8, nb % 4 != 0), a single chunk
+# (nb = 1), ragged tiles, and column counts on both sides of 16.
+@pytest.mark.parametrize("N", [1, 3, 5, 16, 17, 32])
+@pytest.mark.parametrize("M,K", [(200, 512), (65, 3328), (16, 256), (530, 9984)])
+def test_lds_form_shapes(M, K, N, monkeypatch):
+    monkeypatch.setenv("QG_SN_IMPL", "lds")
+    rows = None if M * K <= 200 * 3328 else sample_rows(M, 96, seed=M + N)
+    _, _, _, Y, Yr, Ar = run_smalln(M, K, N, key=(36, M, K, N), rows=rows)
+    for n in range(N):
+        assert_within(Y[n], Yr[n], Ar[n], f"lds form M={M} K={K} N={N} col {n}")
+
+
+@pytest.mark.parametrize("cfg", ["1,2", "1,3", "1,4", "2,2", "2,3", "4,2"])
+@pytest.mark.parametrize("N", [5, 32])
+def test_lds_form_launch_shapes(cfg, N, monkeypatch):
+    # every (tiles per workgroup, queue depth) the launcher accepts, on a batch whose
+    # tile counts are not multiples of the tiles per workgroup
+    if cfg.startswith("4") and N <= 16:
+        pytest.skip("four tiles per workgroup only with more than 16 columns")
+    monkeypatch.setenv("QG_SN_IMPL", "lds")
+    monkeypatch.setenv("QG_SNL_CFG", cfg)
+    shapes = [(530, 2304), (77, 256), (16, 768), (1000, 1280)]
+    probs, refs = [], []
+    for i, (M, K) in enumerate(shapes):
+        W = workloads.q4k_blocks(M, K, key=(37, i))
+        X = workloads.x_columns(K, N, key=(37, i, N))
+        Y = torch.full((N, (M + 3) // 4 * 4), float("nan"), device="cuda:0")
+        probs.append((packed_q4k(W, M, K), to_dev(X), Y, M, K))
+        refs.append(oracle.gemm_q4k(W, M, K, X))
+    case(f"qgemm_q4k_smalln_batch lds cfg={cfg} N={N}")
+    qg.qgemm_q4k_smalln_batch(probs)
+    torch.cuda.synchronize()
+    first = [p[2].clone() for p in probs]
+    qg.qgemm_q4k_smalln_batch(probs)  # deterministic: the same bits on a second call
+    torch.cuda.synchronize()
+    for (w, X, Y, M, K), Y0, (Yr, Ar) in zip(probs, first, refs):
+        assert torch.equal(Y[:, :M], Y0[:, :M])
+        Yc = Y.cpu().numpy()[:, :M]
+        for n in range(N):
+            assert_within(Yc[n], Yr[n], Ar[n], f"lds cfg {cfg} M={M} K={K} col {n}")
+
+
+def test_lds_form_padded_and_mixed_columns(monkeypatch):
+    # padded leading dimensions and problems with different column counts in one
+    # launch (LDS rows sized for the widest)
+    monkeypatch.setenv("QG_SN_IMPL", "lds")
+    shapes = [(130, 2048, 5, 12, 10), (40, 1024, 2, 4, 8), (33, 512, 9, 0, 3)]
+    probs, refs = [], []
+    for i, (M, K, N, px, py) in enumerate(shapes):
+        W = workloads.q4k_blocks(M, K, key=(38, i))
+        X = workloads.x_columns(K, N, key=(38, i))
+        Xp = np.zeros((N, K + px), np.float32)
+        Xp[:, :K] = X
+        Y = torch.full((N, M + py), 123.0, device="cuda:0")
+        probs.append((packed_q4k(W, M, K), to_dev(Xp), Y, M, K))
+        refs.append(oracle.gemm_q4k(W, M, K, X))
+    case("qgemm_q4k_smalln_batch lds padded / mixed N")
+    qg.qgemm_q4k_smalln_batch(probs)
+    torch.cuda.synchronize()
+    for (w, X, Y, M, K), (Yr, Ar) in zip(probs, refs):
+        Yc = Y.cpu().numpy()
+        assert np.all(Yc[:, M:] == 123.0)
+        for n in range(X.shape[0]):
+            assert_within(Yc[n, :M], Yr[n], Ar[n], f"lds padded M={M} K={K} col {n}")
