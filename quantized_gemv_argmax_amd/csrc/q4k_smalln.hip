@@ -27,9 +27,12 @@
 // Within a lane's 8-element K slice the order is that of the masked dwords:
 // bytes 0, 2, 1, 3, 4, 6, 5, 7; the activations are packed in the same order.
 //
-// Grid: one workgroup per TW consecutive 16-row tiles of the packed layout
-// (q4k_gemv.hip); its W wavefronts split K in units of 64 weights (two
-// sub-blocks), each wavefront applying one unit's activations to all TW tiles.
+// Two forms share this arithmetic. The LDS-staged form (the default, further
+// down) stages the activations in LDS and streams the weights with deep queues.
+// The register-staged form, described here: one workgroup per TW consecutive
+// 16-row tiles of the packed layout (q4k_gemv.hip); its W wavefronts split K in
+// units of 64 weights (two sub-blocks), each wavefront applying one unit's
+// activations to all TW tiles.
 // Partial results meet in LDS in a fixed order, so results are deterministic. No
 // workspace, no cross-workgroup traffic. Rows past a ragged tile's end and tiles
 // past the matrix end re-read the last row / tile, columns past N read zeros;
@@ -610,7 +613,7 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
         units = std::min(units, a.p[i].nb * 4);
         tiles += a.p[i].tiles;
     }
-    SnCfg c{1, tiles > 256 ? 2 : 1, 1, false, 3};
+    SnCfg c{1, tiles > 256 ? 2 : 1, 1, false, 2};
     if (C == 2 && tiles > 1024) c.TW = 4;
     int ew = 0, et = 0, ek = 0;
     const bool env = qg::env_pair("QG_SN_CFG", &ew, &et);
@@ -624,12 +627,15 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
     while (c.W < wmax && 2 * c.W <= units / c.KS / 2) c.W *= 2;
     if (env && (ew == 1 || ew == 2 || ew == 4 || ew == 8 || (ew == 16 && C == 1 && c.TW == 1))) c.W = ew;
     // The LDS-staged kernel pays off where a workgroup walks many chunks: it is the
-    // default when every problem has at least 32 super-blocks per row (K >= 8192;
-    // measured on the 7B shapes: the down projection, K = 18944, 23.9 -> 21.3 us at
-    // N = 5 and 72 -> 49 us at N = 32, while the K = 3584 stages were slower).
-    // QG_SN_IMPL=regs / lds forces one form; the register form's launch-shape
-    // variables select it too. Tiles per workgroup: one up to 1024 tiles, then two
-    // (four for more than 16 columns); QG_SNL_CFG=TW,D overrides.
+    // default when every problem has at least 32 super-blocks per row (K >= 8192).
+    // Measured on the 7B shapes against the register form: the down projection,
+    // K = 18944, 23.9 -> 21.7 us at N = 5 and 72.4 -> 49.4 us at N = 32 on every
+    // run; on the K = 3584 stages its times varied from run to run (gate/up at N = 5:
+    // 27 to 37 us against a steady 29.5), so those keep the register form. The
+    // register form also runs for split-K (QG_SN_KS) and its own launch-shape
+    // variable (QG_SN_CFG); QG_SN_IMPL=regs / lds forces a form. Tiles per
+    // workgroup: one up to 1024 tiles, then two (four for more than 16 columns);
+    // QG_SNL_CFG=TW,D overrides.
     const char* impl = getenv("QG_SN_IMPL");
     const std::string im = impl ? impl : "";
     c.lds = c.KS == 1 && !env && im != "regs" && (im == "lds" || units >= 32 * 4);

@@ -215,3 +215,14 @@ def test_lds_form_padded_and_mixed_columns(monkeypatch):
         assert np.all(Yc[:, M:] == 123.0)
         for n in range(X.shape[0]):
             assert_within(Yc[n, :M], Yr[n], Ar[n], f"lds padded M={M} K={K} col {n}")
+
+
+@pytest.mark.parametrize("N", [1, 5, 17, 32])
+@pytest.mark.parametrize("M,K", [(200, 512), (65, 3328), (48, 9984)])
+def test_register_form_shapes(M, K, N, monkeypatch):
+    # the register-staged form (activations in registers, wavefronts splitting K in
+    # 64-weight units), which split-K and its own launch-shape variable also select
+    monkeypatch.setenv("QG_SN_IMPL", "regs")
+    _, _, _, Y, Yr, Ar = run_smalln(M, K, N, key=(40, M, K, N))
+    for n in range(N):
+        assert_within(Y[n], Yr[n], Ar[n], f"register form M={M} K={K} N={N} col {n}")
