@@ -14,9 +14,11 @@ Printed (one JSON line): whole-step throughput in GB/s of algorithmic bytes
 wall divides them), the roofline entry of the dominant kernel (Q4_K GEMV: bytes
 per launch / average launch duration from HIP events on the launch stream), the
 fp64 CPU oracle timed on a bounded sample, and the other hot-path rows (single
-4096x4096 Q4_K GEMV, Q8_0 11008x4096 / 4096x11008, fused 152064x3584 LM head +
-argmax, small-N verify N=5 and N=32 over the same 196 matrices), each timed with
-rotation over enough weight copies to defeat the Infinity Cache.
+4096x4096 Q4_K GEMV, Q8_0 11008x4096 / 4096x11008, Q6_K 3584x18944 / 152064x3584,
+fused 152064x3584 LM head + argmax, the same head verifying 5 columns, top-20 with
+log-probabilities and one sampled token, small-N verify N=5 and N=32 over the same
+196 matrices, the decode step with int8 activations), each timed with rotation over
+enough weight copies to defeat the Infinity Cache.
 """
 from __future__ import annotations
 
@@ -107,7 +109,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(the projections would shard by rows across GPUs). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -38,6 +38,7 @@
 // past the matrix end re-read the last row / tile, columns past N read zeros;
 // their results are dropped.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstdlib>
 #include <string>
@@ -670,10 +671,12 @@ template <int C, int TW, int D>
 void launch_lds(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
     constexpr int WC = sw_consumers<C>();
     const auto kern = q4k_smalln_lds_kernel<C, TW, WC, kSwProducers, D>;
-    static bool attr = false;
-    if (!attr) {
+    // the dynamic LDS limit is raised once per device (more than 64 KB are used)
+    static std::atomic<bool> attr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr[dev].load(std::memory_order_acquire)) {
         (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr = true;
+        attr[dev].store(true, std::memory_order_release);
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * (WC + kSwProducers)), lds, s, a);
 }
