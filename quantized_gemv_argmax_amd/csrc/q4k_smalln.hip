@@ -559,6 +559,120 @@ __global__ __launch_bounds__(64 * (WC + WP)) void q4k_smalln_lds_kernel(SnArgs a
     }
 }
 
+// Single-pass form for short K and few columns: when the activations of the whole
+// K range fit in LDS (fp16, N rows and the zero row), every wavefront first
+// requests its share of them, then the weights of all its super-blocks at once
+// (W wavefronts take super-blocks w, w + W, ...; at most IMAX each), waits for the
+// activations only, stores them converted to LDS, and after one barrier computes
+// as the weights arrive: one memory round trip per workgroup, as in the GEMV.
+constexpr int kS1Waves = 8, kS1Items = 2, kS1Cols = 8;
+
+template <int C, int TW, int W, int IMAX>
+__global__ __launch_bounds__(64 * W) void q4k_smalln_lds1_kernel(SnArgs a) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int wg = blockIdx.x;
+    int k = 0;
+#pragma unroll
+    for (int i = 1; i < QG_MAX_BATCH; ++i)
+        if (i < a.count && wg >= a.begin[i]) k = i;
+    const SnProb P = a.p[k];
+    const int tile0 = (wg - P.wg_begin) * TW;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i = lane & 15, s = lane >> 4;
+    const int K = P.nb * 256;
+    const int RB = (K + 8) * 2;  // bytes per LDS row
+    const uint32_t zrow = (uint32_t)(P.N * RB);
+
+    SnTiles<TW> tl;
+    SnLane<C, TW> ln;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+        const int tc = min(tile0 + t, P.tiles - 1);
+        tl.rt[t] = min(T, P.M - tc * T);
+        tl.w[t] = __builtin_amdgcn_make_buffer_rsrc((void*)(P.w + (size_t)tc * T * P.nb * 144), (short)0,
+                                                    tl.rt[t] * P.nb * 144, kQgRawBufferFlags);
+        const uint32_t r = (uint32_t)min(i, tl.rt[t] - 1);
+        ln.hdr[t] = 16 * r;
+        ln.q[t] = 16 * r + 8 * (s & 1) + (uint32_t)(s >> 1) * 16 * tl.rt[t];
+    }
+
+    // activation groups of 8 (column n, group g): thread tid takes group tid of every
+    // column (the launcher guarantees K <= 512 W and N <= kS1Cols: a single round).
+    // They are requested before the weights, so that waiting for them waits for
+    // nothing else.
+    const int tid = threadIdx.x;
+    const int g = tid;
+    const int gpr = K / 8;  // groups per column
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)P.X, (short)0, (int)(((int64_t)(P.N - 1) * P.ldx + K) * 4), kQgRawBufferFlags);
+    float4 v[kS1Cols][2];
+#pragma unroll
+    for (int n = 0; n < kS1Cols; ++n) {
+        const uint32_t off = (n < P.N && g < gpr) ? (uint32_t)(((int64_t)n * P.ldx + 8 * g) * 4) : kOutOfRange;
+        v[n][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+        v[n][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 16, 0));
+    }
+    SwItem<TW> items[IMAX];
+#pragma unroll
+    for (int j = 0; j < IMAX; ++j) sw_load<C, TW>(items[j], tl, ln, min(wave + j * W, P.nb - 1));
+#pragma unroll
+    for (int n = 0; n < kS1Cols; ++n)
+        if (n < P.N && g < gpr) *reinterpret_cast<qg_h8*>(lds + n * RB + 16 * g) = qg_a_operand(v[n][0], v[n][1]);
+    for (int o = 16 * tid; o < RB; o += 16 * 64 * W)
+        *reinterpret_cast<uint4*>(lds + zrow + o) = make_uint4(0u, 0u, 0u, 0u);
+    sw_barrier();
+
+    qg_f4 acc[TW][C];
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[t][c] = qg_f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < IMAX; ++j) {
+        // a super-block past the end of K reads the zero row: exact zeros
+        const int b = wave + j * W;
+        const uint32_t kb = (uint32_t)(256 * b + 8 * s) * 2;
+        uint32_t ad[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int n = 16 * c + i;
+            ad[c] = (b < P.nb && n < P.N) ? (uint32_t)(n * RB) + kb : zrow + (uint32_t)(16 * s);
+        }
+        sw_dot<C, TW>(acc, items[j], lds, ad);
+    }
+
+    // the W partial sums meet in LDS, after every wavefront is done with the
+    // activations
+    sw_barrier();
+    float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[(wave * TW * C * 4 + (t * C + c) * 4 + e) * 64 + lane] = acc[t][c][e];
+    sw_barrier();
+    if (wave != 0) return;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+        if (tile0 + t < P.tiles && i < min(T, P.M - (tile0 + t) * T)) {
+            const int row = (tile0 + t) * T + i;
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int n = 16 * c + 4 * s + e;
+                    if (n >= P.N) continue;
+                    float v = red[((t * C + c) * 4 + e) * 64 + lane];
+#pragma unroll
+                    for (int w = 1; w < W; ++w) v += red[(w * TW * C * 4 + (t * C + c) * 4 + e) * 64 + lane];
+                    P.Y[(int64_t)n * P.ldy + row] = v;
+                }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ host side
 int sn_validate(const void* w, const float* X, int64_t ldx, const float* Y, int64_t ldy, int64_t M, int64_t K,
                 int64_t N) {
@@ -604,8 +718,9 @@ SnProb make_sn(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy
 // least two units.
 struct SnCfg {
     int W, TW, KS;
-    bool lds;  // LDS-staged kernel (KS = 1 only)
-    int D;     // its weight-queue depth in chunks
+    bool lds;   // LDS-staged kernel (KS = 1 only)
+    int D;      // its weight-queue depth in chunks
+    bool lds1;  // single-pass LDS kernel (short K, N <= 8)
 };
 SnCfg choose_cfg(const SnArgs& a, int C) {
     int units = INT_MAX;
@@ -614,7 +729,7 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
         units = std::min(units, a.p[i].nb * 4);
         tiles += a.p[i].tiles;
     }
-    SnCfg c{1, tiles > 256 ? 2 : 1, 1, false, 2};
+    SnCfg c{1, tiles > 256 ? 2 : 1, 1, false, 2, false};
     if (C == 2 && tiles > 1024) c.TW = 4;
     int ew = 0, et = 0, ek = 0;
     const bool env = qg::env_pair("QG_SN_CFG", &ew, &et);
@@ -626,37 +741,58 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
     if (qg::env_pair("QG_SN_KS", &ek, &unused) && (ek == 1 || ek == 2 || ek == 4)) c.KS = ek;
     const int wmax = c.TW == 4 ? 4 : 8;
     while (c.W < wmax && 2 * c.W <= units / c.KS / 2) c.W *= 2;
-    if (env && (ew == 1 || ew == 2 || ew == 4 || ew == 8 || (ew == 16 && C == 1 && c.TW == 1))) c.W = ew;
-    // The LDS-staged kernel pays off where a workgroup walks many chunks: it is the
-    // default when every problem has at least 32 super-blocks per row (K >= 8192).
-    // Measured on the 7B shapes against the register form: the down projection,
-    // K = 18944, 23.9 -> 21.7 us at N = 5 and 72.4 -> 49.4 us at N = 32 on every
-    // run; on the K = 3584 stages its times varied from run to run (gate/up at N = 5:
-    // 27 to 37 us against a steady 29.5), so those keep the register form. The
-    // register form also runs for split-K (QG_SN_KS) and its own launch-shape
-    // variable (QG_SN_CFG); QG_SN_IMPL=regs / lds forces a form. Tiles per
-    // workgroup: one up to 1024 tiles, then two (four for more than 16 columns);
-    // QG_SNL_CFG=TW,D overrides.
+    if (env && (ew == 1 || ew == 2 || ew == 4 || (ew == 8 && c.TW < 4) || (ew == 16 && C == 1 && c.TW == 1))) c.W = ew;
+    // Form selection, from measurements on the 7B shapes (stage times in us, register
+    // form -> chosen form):
+    //   - the single-pass LDS form for K <= 4096 and N <= 8 (N = 5: q/k/v 9.05 ->
+    //     8.75, o 6.85 -> 6.44, gate/up 29.7 -> 26.6);
+    //   - the chunked LDS form for K >= 8192 (down projection: N = 5 23.6 -> 21.6,
+    //     N = 32 72.3 -> 44.7) and for more than 16 columns over at most 1024 tiles
+    //     (N = 32: q/k/v 18.2 -> 14.2, o 16.6 -> 12.0);
+    //   - the register form otherwise (N = 32 gate/up, 2368 tiles: 57.7 against 62.6
+    //     for the chunked LDS form; N = 5 short K: 29.7 against 37.0).
+    // The register form also runs for split-K (QG_SN_KS) and its own launch-shape
+    // variable (QG_SN_CFG); QG_SN_IMPL=regs / lds / lds1 forces a form. Tiles per
+    // workgroup for the LDS forms: one, or two above 1024 tiles (chunked form: above
+    // 256 for more than 16 columns); QG_SNL_CFG=TW,D and QG_SN1_TW override.
     const char* impl = getenv("QG_SN_IMPL");
     const std::string im = impl ? impl : "";
-    c.lds = c.KS == 1 && !env && im != "regs" && (im == "lds" || units >= 32 * 4);
+    // Single-pass form: every problem with K <= 512 * 8 and N <= 8 (one round of
+    // activation loads per lane, all super-blocks of a row in flight at once).
+    bool s1 = c.KS == 1 && !env && C == 1;
+    for (int i = 0; i < a.count; ++i)
+        s1 = s1 && a.p[i].N <= kS1Cols && a.p[i].nb * 32 <= 64 * kS1Waves && a.p[i].nb <= kS1Items * kS1Waves;
+    c.lds1 = s1 && (im == "" || im == "lds1");
+    if (c.lds1) {
+        c.TW = tiles > 1024 ? 2 : 1;
+        int et1 = 0, unused1 = 0;
+        if (qg::env_pair("QG_SN1_TW", &et1, &unused1) && (et1 == 1 || et1 == 2)) c.TW = et1;
+        return c;
+    }
+    c.lds = c.KS == 1 && !env && im != "regs" && (im == "lds" || units >= 32 * 4 || (C == 2 && tiles <= 1024));
     if (c.lds) {
-        c.TW = tiles > 1024 ? (C == 2 ? 4 : 2) : (C == 2 && tiles > 256 ? 2 : 1);
+        c.TW = tiles > 1024 || (C == 2 && tiles > 256) ? 2 : 1;
         c.D = 2;
         int et2 = 0, ed = 0;
         if (qg::env_pair("QG_SNL_CFG", &et2, &ed)) {
-            if (et2 == 1 || et2 == 2 || (et2 == 4 && C == 2)) c.TW = et2;
+            if (et2 == 1 || et2 == 2) c.TW = et2;
             if (ed >= 2 && ed <= (C == 2 ? 3 : 4)) c.D = ed;
         }
-        if (C == 2 && c.TW == 4) c.D = 2;  // a deeper queue would not fit the registers
     }
     return c;
 }
 
-constexpr int kSwProducers = 4;
+// Consumer and producer wavefronts per workgroup: eight consumers for up to 16
+// columns, four above (the chunk buffers of 32 columns fill the LDS with four
+// super-blocks per chunk); as many producers as stage a chunk of up to 16 / 32
+// columns with one round of loads per lane.
 template <int C>
 constexpr int sw_consumers() {
     return C == 1 ? 8 : 4;
+}
+template <int C>
+constexpr int sw_producers() {
+    return C == 1 ? 4 : 8;
 }
 
 // Dynamic LDS of the LDS-staged kernel: two chunk buffers of N rows and the zero
@@ -670,7 +806,8 @@ size_t sw_lds_bytes(int C, int TW, int nmax) {
 template <int C, int TW, int D>
 void launch_lds(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
     constexpr int WC = sw_consumers<C>();
-    const auto kern = q4k_smalln_lds_kernel<C, TW, WC, kSwProducers, D>;
+    constexpr int WP = sw_producers<C>();
+    const auto kern = q4k_smalln_lds_kernel<C, TW, WC, WP, D>;
     // the dynamic LDS limit is raised once per device (more than 64 KB are used)
     static std::atomic<bool> attr[64];
     int dev = 0;
@@ -678,7 +815,19 @@ void launch_lds(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
         (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr[dev].store(true, std::memory_order_release);
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * (WC + kSwProducers)), lds, s, a);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * (WC + WP)), lds, s, a);
+}
+
+template <int TW>
+void launch_s1(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
+    const auto kern = q4k_smalln_lds1_kernel<1, TW, kS1Waves, kS1Items>;
+    static std::atomic<bool> attr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr[dev].load(std::memory_order_acquire)) {
+        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr[dev].store(true, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kS1Waves), lds, s, a);
 }
 
 void launch_lds_any(const SnArgs& a, int grid, int C, int TW, int D, size_t lds, hipStream_t s) {
@@ -692,8 +841,7 @@ void launch_lds_any(const SnArgs& a, int grid, int C, int TW, int D, size_t lds,
         case 212: launch_lds<2, 1, 2>(a, grid, lds, s); break;
         case 213: launch_lds<2, 1, 3>(a, grid, lds, s); break;
         case 222: launch_lds<2, 2, 2>(a, grid, lds, s); break;
-        case 223: launch_lds<2, 2, 3>(a, grid, lds, s); break;
-        default: launch_lds<2, 4, 2>(a, grid, lds, s); break;
+        default: launch_lds<2, 2, 3>(a, grid, lds, s); break;
     }
 }
 
@@ -703,7 +851,9 @@ void launch(const SnArgs& a, int grid, int W, hipStream_t s) {
         case 1: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 1>), dim3(grid), dim3(64), 0, s, a); break;
         case 2: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 2>), dim3(grid), dim3(128), 0, s, a); break;
         case 4: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 4>), dim3(grid), dim3(256), 0, s, a); break;
-        case 8: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 8>), dim3(grid), dim3(512), 0, s, a); break;
+        case 8:
+            if constexpr (TW < 4) hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 8>), dim3(grid), dim3(512), 0, s, a);
+            break;
         default:
             if constexpr (C == 1 && TW == 1) hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 16>), dim3(grid), dim3(1024), 0, s, a);
             break;
@@ -768,6 +918,16 @@ int run(const qg_gemm_problem* probs, int count, void* ws, size_t ws_bytes, hipS
     if (st) return st;
     if (cfg.lds) {
         launch_lds_any(a, (int)wgs, C, cfg.TW, cfg.D, sw_lds_bytes(C, cfg.TW, nmax), stream);
+        return qg::launch_status("qgemm_q4k_smalln");
+    }
+    if (cfg.lds1) {
+        int kmax = 0;
+        for (int i = 0; i < count; ++i) kmax = std::max(kmax, a.p[i].nb * 256);
+        const size_t lds = std::max((size_t)(nmax + 1) * (kmax + 8) * 2, (size_t)kS1Waves * cfg.TW * 4 * 64 * 4);
+        if (cfg.TW == 2)
+            launch_s1<2>(a, (int)wgs, lds, stream);
+        else
+            launch_s1<1>(a, (int)wgs, lds, stream);
         return qg::launch_status("qgemm_q4k_smalln");
     }
     const int key = 10 * C + cfg.TW;

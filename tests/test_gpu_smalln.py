@@ -163,13 +163,12 @@ def test_lds_form_shapes(M, K, N, monkeypatch):
         assert_within(Y[n], Yr[n], Ar[n], f"lds form M={M} K={K} N={N} col {n}")
 
 
-@pytest.mark.parametrize("cfg", ["1,2", "1,3", "1,4", "2,2", "2,3", "4,2"])
+@pytest.mark.parametrize("cfg", ["1,2", "1,3", "1,4", "2,2", "2,3", "2,4"])
 @pytest.mark.parametrize("N", [5, 32])
 def test_lds_form_launch_shapes(cfg, N, monkeypatch):
     # every (tiles per workgroup, queue depth) the launcher accepts, on a batch whose
-    # tile counts are not multiples of the tiles per workgroup
-    if cfg.startswith("4") and N <= 16:
-        pytest.skip("four tiles per workgroup only with more than 16 columns")
+    # tile counts are not multiples of the tiles per workgroup (a depth of 4 is taken
+    # up to 16 columns only; above, the launcher keeps its default depth)
     monkeypatch.setenv("QG_SN_IMPL", "lds")
     monkeypatch.setenv("QG_SNL_CFG", cfg)
     shapes = [(530, 2304), (77, 256), (16, 768), (1000, 1280)]
@@ -226,3 +225,32 @@ def test_register_form_shapes(M, K, N, monkeypatch):
     _, _, _, Y, Yr, Ar = run_smalln(M, K, N, key=(40, M, K, N))
     for n in range(N):
         assert_within(Y[n], Yr[n], Ar[n], f"register form M={M} K={K} N={N} col {n}")
+
+
+@pytest.mark.parametrize("tw", ["1", "2"])
+def test_single_pass_form(tw, monkeypatch):
+    # short-K single-pass form (all activations in LDS, every super-block of a row
+    # in flight at once): the largest K it takes (4096: sixteen super-blocks, two
+    # per wavefront), one super-block, N from 1 to its limit of 8 in one launch,
+    # ragged tiles and tile counts not a multiple of the tiles per workgroup
+    monkeypatch.setenv("QG_SN_IMPL", "lds1")
+    monkeypatch.setenv("QG_SN1_TW", tw)
+    shapes = [(530, 4096, 8), (77, 256, 1), (16, 3584, 5), (1000, 1280, 3), (33, 768, 2)]
+    probs, refs = [], []
+    for i, (M, K, N) in enumerate(shapes):
+        W = workloads.q4k_blocks(M, K, key=(39, i))
+        X = workloads.x_columns(K, N, key=(39, i, N))
+        Y = torch.full((N, (M + 3) // 4 * 4), float("nan"), device="cuda:0")
+        probs.append((packed_q4k(W, M, K), to_dev(X), Y, M, K))
+        refs.append(oracle.gemm_q4k(W, M, K, X))
+    case(f"qgemm_q4k_smalln_batch single-pass TW={tw}")
+    qg.qgemm_q4k_smalln_batch(probs)
+    torch.cuda.synchronize()
+    first = [p[2].clone() for p in probs]
+    qg.qgemm_q4k_smalln_batch(probs)
+    torch.cuda.synchronize()
+    for (w, X, Y, M, K), Y0, (Yr, Ar) in zip(probs, first, refs):
+        assert torch.equal(Y[:, :M], Y0[:, :M])
+        Yc = Y.cpu().numpy()[:, :M]
+        for n in range(X.shape[0]):
+            assert_within(Yc[n], Yr[n], Ar[n], f"single-pass TW={tw} M={M} K={K} col {n}")
