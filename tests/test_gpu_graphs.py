@@ -17,7 +17,7 @@ def test_graph_replays_match_eager():
     torch.cuda.set_device(0)
     ws = qg.Workspace(DEV, 8 << 20)
     # q/k/v stage of a 7B layer (grouped), LM head argmax, LM head top-k with a
-    # sampler, small-N verify N=5, int8-activation product
+    # sampler, small-N verify (N=5 short and long K, N=32), int8-activation product
     stage = []
     for i, (M, K) in enumerate([(3584, 3584), (512, 3584), (512, 3584)]):
         W = workloads.q4k_blocks(M, K, key=(80, i))
@@ -36,18 +36,29 @@ def test_graph_replays_match_eager():
     Y5 = torch.empty((5, M5), device=DEV)
     xq = torch.empty(qg.q8_1_bytes(K5), dtype=torch.uint8, device=DEV)
     y8 = torch.empty(M5, device=DEV)
+    # the chunked LDS form of the small-N product: a long-K down projection at N=5
+    # and the attention output at N=32
+    Md, Kd = 3584, 18944
+    wd = packed_q4k(workloads.q4k_blocks(Md, Kd, key=(83,)), Md, Kd)
+    Xd = to_dev(workloads.x_columns(Kd, 5, key=(83,)))
+    Yd = torch.empty((5, Md), device=DEV)
+    X32 = to_dev(workloads.x_columns(K5, 32, key=(84,)))
+    Y32 = torch.empty((32, M5), device=DEV)
 
     def work():
         qg.qgemv_q4k_batch(stage, ws=ws)
         qg.lmhead_argmax(wh, xh, Mh, Kh, out_index=oi, out_value=ov, ws=ws)
         qg.lmhead_topk(wh, xh, Mh, Kh, 20, logits=lg, sampler=(0.9, 0.95, 0.02, u), ws=ws, out=tk)
         qg.qgemm_q4k_smalln(stage[0][0], X5, M5, K5, Y=Y5, ws=ws)
+        qg.qgemm_q4k_smalln(wd, Xd, Md, Kd, Y=Yd, ws=ws)
+        qg.qgemm_q4k_smalln(stage[0][0], X32, M5, K5, Y=Y32, ws=ws)
         qg.quantize_q8_1(stage[0][1], out=xq)
         qg.qgemv_q4k_q8_1(stage[0][0], xq, M5, K5, y=y8, ws=ws)
 
     def snapshot():
         torch.cuda.synchronize()
-        outs = [p[2] for p in stage] + [oi, ov, tk.index, tk.logit, tk.logprob, tk.lse, tk.token, lg, Y5, xq, y8]
+        outs = [p[2] for p in stage] + [oi, ov, tk.index, tk.logit, tk.logprob, tk.lse, tk.token, lg, Y5, Yd, Y32, xq,
+                                        y8]
         return [t.clone() for t in outs]
 
     case("graph capture: eager reference")
@@ -66,7 +77,7 @@ def test_graph_replays_match_eager():
         work()
     for rep in range(4):
         # scribble over the outputs, then replay and compare
-        for t in snapshot_targets(stage, oi, ov, tk, lg, Y5, xq, y8):
+        for t in snapshot_targets(stage, oi, ov, tk, lg, Y5, Yd, Y32, xq, y8):
             t.zero_()
         case(f"graph replay {rep}")
         g.replay()
@@ -79,5 +90,5 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
 
 
-def snapshot_targets(stage, oi, ov, tk, lg, Y5, xq, y8):
-    return [p[2] for p in stage] + [oi, ov, tk.index, tk.logit, tk.logprob, tk.lse, tk.token, lg, Y5, xq, y8]
+def snapshot_targets(stage, oi, ov, tk, lg, Y5, Yd, Y32, xq, y8):
+    return [p[2] for p in stage] + [oi, ov, tk.index, tk.logit, tk.logprob, tk.lse, tk.token, lg, Y5, Yd, Y32, xq, y8]
