@@ -441,6 +441,46 @@ QG_DEV void sw_stage(unsigned char* lds, uint32_t row0, __amdgpu_buffer_rsrc_t x
     }
 }
 
+// The same staging split in two, for chunks that take a single round of PB passes
+// (N <= PB * CPP): sw_issue requests chunk q's activations into registers,
+// sw_write waits for them and stores them. The producer issues chunk q + 2 right
+// after writing chunk q + 1, so the loads have a whole chunk interval to arrive.
+template <int WC, int WP>
+struct SwRegs {
+    static constexpr int kPB = 8;
+    float4 v[kPB][2];
+};
+
+template <int WC, int WP>
+QG_DEV void sw_issue(SwRegs<WC, WP>& r, __amdgpu_buffer_rsrc_t xr, const SnProb& P, int q, int pl) {
+    constexpr int LPC = 32 * WC;
+    constexpr int CPP = 64 * WP / LPC;
+    const int k0 = q * WC * 256;
+    const int g8n = min(WC, P.nb - q * WC) * 32;
+    const int g = pl % LPC;
+#pragma unroll
+    for (int j = 0; j < SwRegs<WC, WP>::kPB; ++j) {
+        const int n = j * CPP + pl / LPC;
+        const uint32_t off = (n < P.N && g < g8n) ? (uint32_t)(((int64_t)n * P.ldx + k0 + 8 * g) * 4) : kOutOfRange;
+        r.v[j][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+        r.v[j][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 16, 0));
+    }
+}
+
+template <int WC, int WP>
+QG_DEV void sw_write(const SwRegs<WC, WP>& r, unsigned char* lds, uint32_t row0, const SnProb& P, int q, int pl) {
+    constexpr int RB = SwGeom<WC>::kRowBytes;
+    constexpr int LPC = 32 * WC;
+    constexpr int CPP = 64 * WP / LPC;
+    const int g8n = min(WC, P.nb - q * WC) * 32;
+    const int g = pl % LPC;
+#pragma unroll
+    for (int j = 0; j < SwRegs<WC, WP>::kPB; ++j) {
+        const int n = j * CPP + pl / LPC;
+        if (n < P.N && g < g8n) *reinterpret_cast<qg_h8*>(lds + row0 + n * RB + 16 * g) = qg_a_operand(r.v[j][0], r.v[j][1]);
+    }
+}
+
 template <int C, int TW, int WC, int WP, int D>
 __global__ __launch_bounds__(64 * (WC + WP)) void q4k_smalln_lds_kernel(SnArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -471,14 +511,37 @@ __global__ __launch_bounds__(64 * (WC + WP)) void q4k_smalln_lds_kernel(SnArgs a
             *reinterpret_cast<uint4*>(lds + zrow + o) = make_uint4(0u, 0u, 0u, 0u);
         const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
             (void*)P.X, (short)0, (int)(((int64_t)(P.N - 1) * P.ldx + (int64_t)P.nb * 256) * 4), kQgRawBufferFlags);
-        sw_stage<WC, WP>(lds, 0, xr, P, 0, pl);
-        sw_barrier();
-        for (int q = 0; q < nq; q += D) {
+        constexpr int CPP = 64 * WP / (32 * WC);
+        if (P.N <= SwRegs<WC, WP>::kPB * CPP) {
+            // one round per chunk: software-pipelined, loads one interval ahead
+            SwRegs<WC, WP> r;
+            sw_issue<WC, WP>(r, xr, P, 0, pl);
+            sw_write<WC, WP>(r, lds, 0, P, 0, pl);
+            if (1 < nq) sw_issue<WC, WP>(r, xr, P, 1, pl);
+            sw_barrier();
+            for (int q = 0; q < nq; q += D) {
 #pragma unroll
-            for (int j = 0; j < D; ++j) {
-                // during chunk q + j: stage chunk q + j + 1 into the other buffer
-                if (q + j + 1 < nq) sw_stage<WC, WP>(lds, ((q + j + 1) & 1) * P.N * RB, xr, P, q + j + 1, pl);
-                sw_barrier();
+                for (int j = 0; j < D; ++j) {
+                    // during chunk q + j: store chunk q + j + 1 (requested during the
+                    // previous interval) into the other buffer, request chunk q + j + 2
+                    const int qs = q + j + 1;
+                    if (qs < nq) {
+                        sw_write<WC, WP>(r, lds, (qs & 1) * P.N * RB, P, qs, pl);
+                        if (qs + 1 < nq) sw_issue<WC, WP>(r, xr, P, qs + 1, pl);
+                    }
+                    sw_barrier();
+                }
+            }
+        } else {
+            sw_stage<WC, WP>(lds, 0, xr, P, 0, pl);
+            sw_barrier();
+            for (int q = 0; q < nq; q += D) {
+#pragma unroll
+                for (int j = 0; j < D; ++j) {
+                    // during chunk q + j: stage chunk q + j + 1 into the other buffer
+                    if (q + j + 1 < nq) sw_stage<WC, WP>(lds, ((q + j + 1) & 1) * P.N * RB, xr, P, q + j + 1, pl);
+                    sw_barrier();
+                }
             }
         }
     } else {
