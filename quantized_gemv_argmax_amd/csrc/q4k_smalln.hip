@@ -27,6 +27,11 @@
 // Within a lane's 8-element K slice the order is that of the masked dwords:
 // bytes 0, 2, 1, 3, 4, 6, 5, 7; the activations are packed in the same order.
 //
+// For up to four columns the vector-ALU dot-product form (q4k_smalln_dot.hip)
+// runs instead: per 8 weights it costs 5 bit operations and 4 dot2 operations per
+// column, which stays below the matrix-core forms' per-sub-block scaling work
+// while N is small.
+//
 // Two forms share this arithmetic. The LDS-staged form (the default, further
 // down) stages the activations in LDS and streams the weights with deep queues.
 // The register-staged form, described here: one workgroup per TW consecutive
@@ -784,6 +789,7 @@ struct SnCfg {
     bool lds;   // LDS-staged kernel (KS = 1 only)
     int D;      // its weight-queue depth in chunks
     bool lds1;  // single-pass LDS kernel (short K, N <= 8)
+    bool dot;   // vector-ALU dot-product kernel (N <= 8, q4k_smalln_dot.hip)
 };
 SnCfg choose_cfg(const SnArgs& a, int C) {
     int units = INT_MAX;
@@ -792,7 +798,7 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
         units = std::min(units, a.p[i].nb * 4);
         tiles += a.p[i].tiles;
     }
-    SnCfg c{1, tiles > 256 ? 2 : 1, 1, false, 2, false};
+    SnCfg c{1, tiles > 256 ? 2 : 1, 1, false, 2, false, false};
     if (C == 2 && tiles > 1024) c.TW = 4;
     int ew = 0, et = 0, ek = 0;
     const bool env = qg::env_pair("QG_SN_CFG", &ew, &et);
@@ -820,6 +826,13 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
     // 256 for more than 16 columns); QG_SNL_CFG=TW,D and QG_SN1_TW override.
     const char* impl = getenv("QG_SN_IMPL");
     const std::string im = impl ? impl : "";
+    int ncol = 0;
+    for (int i = 0; i < a.count; ++i) ncol = std::max(ncol, (int)a.p[i].N);
+    // Vector-ALU dot-product form for up to four columns (196 decode matrices, ms
+    // per step against the matrix-core forms: N = 1 0.93 / 1.57, 2 1.13 / 1.58,
+    // 3 1.29 / 1.63, 4 1.52 / 1.67, 5 1.83 / 1.74); QG_SN_IMPL=dot forces it up to 8.
+    c.dot = c.KS == 1 && !env && ((ncol <= 4 && im == "") || (ncol <= 8 && im == "dot"));
+    if (c.dot) return c;
     // Single-pass form: every problem with K <= 512 * 8 and N <= 8 (one round of
     // activation loads per lane, all super-blocks of a row in flight at once).
     bool s1 = c.KS == 1 && !env && C == 1;
@@ -979,6 +992,7 @@ int run(const qg_gemm_problem* probs, int count, void* ws, size_t ws_bytes, hipS
     }
     st = qg::check_device();
     if (st) return st;
+    if (cfg.dot) return qg::smalln_dot_launch(probs, count, stream);
     if (cfg.lds) {
         launch_lds_any(a, (int)wgs, C, cfg.TW, cfg.D, sw_lds_bytes(C, cfg.TW, nmax), stream);
         return qg::launch_status("qgemm_q4k_smalln");

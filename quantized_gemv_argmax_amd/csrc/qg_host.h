@@ -40,4 +40,8 @@ size_t topk_ws_bytes(int64_t M);
 int launch_topk_select(void* ws, int tiles, const float* logits, int64_t M, int k, const qg_sampler* sampler,
                        const qg_topk_out& out, hipStream_t s);
 
+// Vector-ALU dot-product form of the small-N product (q4k_smalln_dot.hip), for
+// problems the small-N entry points have validated, each with N <= 8.
+int smalln_dot_launch(const qg_gemm_problem* probs, int count, hipStream_t s);
+
 }  // namespace qg

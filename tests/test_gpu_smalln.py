@@ -254,3 +254,66 @@ def test_single_pass_form(tw, monkeypatch):
         Yc = Y.cpu().numpy()[:, :M]
         for n in range(X.shape[0]):
             assert_within(Yc[n], Yr[n], Ar[n], f"single-pass TW={tw} M={M} K={K} col {n}")
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("M,K", [(200, 512), (65, 3328), (48, 9984), (1, 256)])
+def test_dot_form_shapes(M, K, N, monkeypatch):
+    # the vector-ALU dot-product form (N <= 8): one super-block per K-group (K up to
+    # 4096) and the pipelined walk over several (K = 9984: 39 super-blocks, a
+    # ragged last round), ragged tiles, a single row
+    monkeypatch.setenv("QG_SN_IMPL", "dot")
+    _, _, _, Y, Yr, Ar = run_smalln(M, K, N, key=(41, M, K, N))
+    for n in range(N):
+        assert_within(Y[n], Yr[n], Ar[n], f"dot form M={M} K={K} N={N} col {n}")
+
+
+@pytest.mark.parametrize("M,K", [(3584, 3584), (3584, 18944), (700, 2304)])
+def test_dot_form_columns_bit_exact_with_gemv(M, K, monkeypatch):
+    # each column of the dot-product form repeats the single-column kernel's
+    # arithmetic in the same order (four wavefronts per tile once K >= 2304), so it
+    # equals qgemv_q4k of that column bit for bit
+    monkeypatch.setenv("QG_SN_IMPL", "dot")
+    N = 5
+    W = workloads.q4k_blocks(M, K, key=(42, M, K))
+    X = workloads.x_columns(K, N, key=(42, M, K))
+    case(f"dot form vs qgemv_q4k M={M} K={K} N={N}")
+    wp = packed_q4k(W, M, K)
+    Y = qg.qgemm_q4k_smalln(wp, to_dev(X), M, K)
+    torch.cuda.synchronize()
+    for n in range(N):
+        y = qg.qgemv_q4k(wp, to_dev(X[n]), M, K)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y[n, :M].cpu().numpy(), y.cpu().numpy()), f"column {n}"
+    rows = sample_rows(M, 64, seed=K)
+    Yr, Ar = oracle.gemm_q4k(W, M, K, X, rows=rows)
+    Yc = Y.cpu().numpy()[:, :M]
+    for n in range(N):
+        assert_within(Yc[n, rows], Yr[n], Ar[n], f"dot form M={M} K={K} col {n}")
+
+
+def test_dot_form_batch_mixed_columns(monkeypatch):
+    # one launch over problems with different N (the kernel is built for the largest;
+    # smaller problems read zeros past their N and store only their own columns) and
+    # padded leading dimensions; padding and columns past N stay untouched
+    monkeypatch.setenv("QG_SN_IMPL", "dot")
+    shapes = [(530, 4096, 8), (77, 256, 1), (16, 3584, 5), (1000, 1280, 3), (33, 18944, 2)]
+    probs, refs, Xs = [], [], []
+    for i, (M, K, N) in enumerate(shapes):
+        W = workloads.q4k_blocks(M, K, key=(43, i))
+        X = workloads.x_columns(K, N, key=(43, i, N))
+        ldx = K + 256
+        Xp = np.full((N, ldx), np.nan, np.float32)
+        Xp[:, :K] = X
+        Y = torch.full((N, (M + 3) // 4 * 4 + 4), float("nan"), device="cuda:0")
+        probs.append((packed_q4k(W, M, K), to_dev(Xp), Y, M, K))
+        refs.append(oracle.gemm_q4k(W, M, K, X))
+    case("qgemm_q4k_smalln_batch dot form, mixed N")
+    # X rows are K + 256 long (NaN past K), Y rows longer than M: ldx > K, ldy > M
+    qg.qgemm_q4k_smalln_batch(probs)
+    torch.cuda.synchronize()
+    for (w, Xd, Y, M, K), (Yr, Ar) in zip(probs, refs):
+        Yc = Y.cpu().numpy()
+        assert np.all(np.isnan(Yc[:, M:])), "padding rows were written"
+        for n in range(Yc.shape[0]):
+            assert_within(Yc[n, :M], Yr[n], Ar[n], f"dot batch M={M} K={K} col {n}")
