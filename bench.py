@@ -16,8 +16,8 @@ per launch / average launch duration from HIP events on the launch stream), the
 fp64 CPU oracle timed on a bounded sample, and the other hot-path rows (single
 4096x4096 Q4_K GEMV, Q8_0 11008x4096 / 4096x11008, Q6_K 3584x18944 / 152064x3584,
 fused 152064x3584 LM head + argmax, the same head verifying 5 columns, top-20 with
-log-probabilities and one sampled token, small-N verify N=5 and N=32 over the same
-196 matrices, the decode step with int8 activations), each timed with rotation over
+log-probabilities and one sampled token, small-N verify N=5, N=32 and N=2 over the
+same 196 matrices, the decode step with int8 activations), each timed with rotation over
 enough weight copies to defeat the Infinity Cache.
 """
 from __future__ import annotations
@@ -292,7 +292,7 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     for c in copies:
         qg.lmhead_topk(c, x, M, K, 20, sampler=(0.8, 0.95, 0.05, u_dev), ws=ws)
     del wp, copies
-    for N in (5, 32):
+    for N in (5, 32, 2):
         for L in range(n_layers):
             for st in wl.LAYER_STAGES:
                 grp = []
@@ -450,7 +450,7 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
 
     # small-N verify over the 196 decode matrices (weights read once per call), one
     # grouped launch per dependency stage as in the decode step
-    for N in (5, 32):
+    for N in (5, 32, 2):
         sstages = []
         for L in range(n_layers):
             for st in wl.LAYER_STAGES:

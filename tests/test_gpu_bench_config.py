@@ -2,7 +2,7 @@
 step with the benchmark's seeded weights and activations, launched as the benchmark
 launches it (one grouped launch per dependency stage: {q,k,v}, {o}, {gate,up},
 {down}), for the fp32-activation GEMV (every row of all seven matrices), the int8-
-activation GEMV, and the small-N verify product at N = 5 and N = 32 (sampled rows)."""
+activation GEMV, and the small-N verify product at N = 5, N = 32 and N = 2 (sampled rows)."""
 import numpy as np
 import pytest
 import torch
@@ -59,7 +59,7 @@ def test_int8_decode_step_layer_as_timed():
         assert np.all(np.abs(y - yr) <= 1e-5 * ar + 1e-6), f"int8 layer 0 {name}"
 
 
-@pytest.mark.parametrize("N", [5, 32])
+@pytest.mark.parametrize("N", [5, 32, 2])
 def test_verify_step_layer_as_timed(N):
     L = 0
     mats = _layer(L)
