@@ -25,6 +25,7 @@
 // waits for those weights. Columns past a problem's N read zeros through an
 // out-of-range buffer offset and are not stored.
 #include <algorithm>
+#include <cstdlib>
 
 #include "qg_device.h"
 #include "qg_host.h"
@@ -199,7 +200,10 @@ QG_DEV void sb_dot_n(float (&out)[NC], const uint4 (&s)[9], const XIn<NC>& x) {
 }
 
 // MODE 0: one super-block per K-group (K <= 4096); 1: several, weights of the next
-// one in flight.
+// one in flight; 2: several, weights and activations of the next one in flight
+// (two full register buffers; used for one column, where it measured faster on
+// the 3584 x 18944 down projection, 10.4 -> 9.8 us, and slower for two, 13.5 ->
+// 14.2 us; QG_SND_XPP=0/1 overrides).
 template <int MODE, int NC>
 __global__ __launch_bounds__(64 * W) void q4k_smalln_dot_kernel(SdArgs a) {
     const int wg = blockIdx.x;
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_dot_kernel(SdArgs a) {
         sb_dot_n<NC>(v, w0, x);
 #pragma unroll
         for (int n = 0; n < NC; ++n) acc[n] = (kg < nb) ? v[n] : 0.f;
-    } else {
+    } else if constexpr (MODE == 1) {
         const int niter = (nb + G - 1) / G;
         // Two weight buffers over pairs of super-blocks; each super-block's
         // activations are requested before the next weights, so every wait is for
@@ -274,6 +278,35 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_dot_kernel(SdArgs a) {
             for (int n = 0; n < NC; ++n) acc[n] += (kg + G * it < nb) ? v[n] : 0.f;
         }
     }
+    if constexpr (MODE == 2) {
+        const int niter = (nb + G - 1) / G;
+        uint4 w0[9], w1[9];
+        XIn<NC> x0, x1;
+        load_w(w0, wr, vrow, min(kg, nb - 1), rt);
+        load_x<NC>(x0, xr, vx, min(kg, nb - 1), coff);
+        int it = 0;
+        for (; it + 2 <= niter; it += 2) {
+            load_w(w1, wr, vrow, min(kg + G * (it + 1), nb - 1), rt);
+            load_x<NC>(x1, xr, vx, min(kg + G * (it + 1), nb - 1), coff);
+            __builtin_amdgcn_sched_barrier(0);
+            float v[NC];
+            sb_dot_n<NC>(v, w0, x0);
+#pragma unroll
+            for (int n = 0; n < NC; ++n) acc[n] += (kg + G * it < nb) ? v[n] : 0.f;
+            load_w(w0, wr, vrow, min(kg + G * (it + 2), nb - 1), rt);
+            load_x<NC>(x0, xr, vx, min(kg + G * (it + 2), nb - 1), coff);
+            __builtin_amdgcn_sched_barrier(0);
+            sb_dot_n<NC>(v, w1, x1);
+#pragma unroll
+            for (int n = 0; n < NC; ++n) acc[n] += (kg + G * (it + 1) < nb) ? v[n] : 0.f;
+        }
+        if (it < niter) {
+            float v[NC];
+            sb_dot_n<NC>(v, w0, x0);
+#pragma unroll
+            for (int n = 0; n < NC; ++n) acc[n] += (kg + G * it < nb) ? v[n] : 0.f;
+        }
+    }
 
     __shared__ float red[W][NC][T];
 #pragma unroll
@@ -299,6 +332,14 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_dot_kernel(SdArgs a) {
 
 template <int NC>
 void launch_nc(const SdArgs& a, int grid, bool multi, hipStream_t s) {
+    const char* e = getenv("QG_SND_XPP");
+    const bool xpp = (e && *e) ? atoi(e) != 0 : NC == 1;
+    if constexpr (NC <= 2) {
+        if (multi && xpp) {
+            hipLaunchKernelGGL((q4k_smalln_dot_kernel<2, NC>), dim3(grid), dim3(64 * W), 0, s, a);
+            return;
+        }
+    }
     if (multi)
         hipLaunchKernelGGL((q4k_smalln_dot_kernel<1, NC>), dim3(grid), dim3(64 * W), 0, s, a);
     else

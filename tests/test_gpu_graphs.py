@@ -17,7 +17,7 @@ def test_graph_replays_match_eager():
     torch.cuda.set_device(0)
     ws = qg.Workspace(DEV, 8 << 20)
     # q/k/v stage of a 7B layer (grouped), LM head argmax, LM head top-k with a
-    # sampler, small-N verify (N=5 short and long K, N=32), int8-activation product
+    # sampler, small-N verify (N=5 short and long K, N=32, N=2 and 3), int8-activation product
     stage = []
     for i, (M, K) in enumerate([(3584, 3584), (512, 3584), (512, 3584)]):
         W = workloads.q4k_blocks(M, K, key=(80, i))
@@ -44,6 +44,12 @@ def test_graph_replays_match_eager():
     Yd = torch.empty((5, Md), device=DEV)
     X32 = to_dev(workloads.x_columns(K5, 32, key=(84,)))
     Y32 = torch.empty((32, M5), device=DEV)
+    # the vector-ALU dot form (N <= 4): one super-block per K-group at N=2, the
+    # pipelined walk over the long-K down projection at N=3
+    X2 = to_dev(workloads.x_columns(K5, 2, key=(85,)))
+    Y2 = torch.empty((2, M5), device=DEV)
+    Xd3 = to_dev(workloads.x_columns(Kd, 3, key=(86,)))
+    Yd3 = torch.empty((3, Md), device=DEV)
 
     def work():
         qg.qgemv_q4k_batch(stage, ws=ws)
@@ -52,13 +58,15 @@ def test_graph_replays_match_eager():
         qg.qgemm_q4k_smalln(stage[0][0], X5, M5, K5, Y=Y5, ws=ws)
         qg.qgemm_q4k_smalln(wd, Xd, Md, Kd, Y=Yd, ws=ws)
         qg.qgemm_q4k_smalln(stage[0][0], X32, M5, K5, Y=Y32, ws=ws)
+        qg.qgemm_q4k_smalln(stage[0][0], X2, M5, K5, Y=Y2, ws=ws)
+        qg.qgemm_q4k_smalln(wd, Xd3, Md, Kd, Y=Yd3, ws=ws)
         qg.quantize_q8_1(stage[0][1], out=xq)
         qg.qgemv_q4k_q8_1(stage[0][0], xq, M5, K5, y=y8, ws=ws)
 
     def snapshot():
         torch.cuda.synchronize()
         outs = [p[2] for p in stage] + [oi, ov, tk.index, tk.logit, tk.logprob, tk.lse, tk.token, lg, Y5, Yd, Y32, xq,
-                                        y8]
+                                        y8, Y2, Yd3]
         return [t.clone() for t in outs]
 
     case("graph capture: eager reference")
@@ -77,7 +85,7 @@ def test_graph_replays_match_eager():
         work()
     for rep in range(4):
         # scribble over the outputs, then replay and compare
-        for t in snapshot_targets(stage, oi, ov, tk, lg, Y5, Yd, Y32, xq, y8):
+        for t in snapshot_targets(stage, oi, ov, tk, lg, Y5, Yd, Y32, xq, y8) + [Y2, Yd3]:
             t.zero_()
         case(f"graph replay {rep}")
         g.replay()
