@@ -17,7 +17,7 @@ fp64 CPU oracle timed on a bounded sample, and the other hot-path rows (single
 4096x4096 Q4_K GEMV, Q8_0 11008x4096 / 4096x11008, Q6_K 3584x18944 / 152064x3584,
 fused 152064x3584 LM head + argmax, the same head verifying 5 columns, top-20 with
 log-probabilities and one sampled token, small-N verify N=5, N=32 and N=2 over the
-same 196 matrices, the decode step with int8 activations), each timed with rotation over
+same 196 matrices, the N=5 verify step and the decode step with int8 activations), each timed with rotation over
 enough weight copies to defeat the Infinity Cache.
 """
 from __future__ import annotations
@@ -480,6 +480,39 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
                                        "launches_per_step": len(sstages), "per_stage": per_stage}
         log(f"row smalln N={N}: {rows[f'smalln_verify_N{N}']}")
         del sstages, flat
+
+    # the verify step on int8 activations (each column quantized beforehand, as in
+    # the int8 decode row), N = 5: the same 112 grouped launches
+    N = 5
+    qv = []
+    for L in range(n_layers):
+        for st in wl.LAYER_STAGES:
+            grp = []
+            for i in st:
+                wp_, _, _, M_, K_ = layers[L][i]
+                X_ = torch.from_numpy(wl.x_columns(K_, N, key=(5, L, i, N))).to(dev)
+                grp.append((wp_, qg.quantize_q8_1_columns(X_), torch.empty((N, (M_ + 3) // 4 * 4), device=dev), M_, K_))
+            qv.append(grp)
+
+    def ivstep(sts=qv):
+        for grp in sts:
+            qg.qgemm_q4k_q8_1_smalln_batch(grp, ws=ws)
+
+    ms = graph_ms(torch, ivstep, 5)
+    flat = [m for grp in qv for m in grp]
+    b = sum(m[0].numel() + m[1].numel() + 4 * N * m[3] for m in flat)
+    per_stage = {}
+    for k, name in enumerate(["qkv", "o", "gate_up", "down"]):
+        sts = qv[k::4]
+        nb_ = sum(m[0].numel() + m[1].numel() + 4 * N * m[3] for m in sts[0])
+        us = graph_ms(torch, lambda sts=sts: ivstep(sts), 5) * 1e3 / len(sts)
+        per_stage[name] = {"avg_us": round(us, 3), "GBps": round(nb_ / (us * 1e-6) / 1e9, 1)}
+    rows["smalln_verify_N5_int8_activations"] = {
+        "ms_per_step": round(ms, 4), "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": int(b),
+        "verified_tokens_per_s": round(N * 1e3 / ms, 1), "launches_per_step": len(qv), "per_stage": per_stage,
+        "quantization": "not timed (done once per column beforehand)"}
+    log(f"row smalln N=5, int8 activations: {rows['smalln_verify_N5_int8_activations']}")
+    del qv, flat
 
     # the decode step with int8 activations (Q8_1-style, scale and sum per 32):
     # every x quantized once beforehand (in a model the quantization belongs to the

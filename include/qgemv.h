@@ -159,6 +159,32 @@ int qgemv_q4k_q8_1_batch(const qg_gemv_q8_1_problem* problems /* host */, int co
                          void* workspace, size_t workspace_bytes, qg_stream_t stream);
 
 /*
+ * Y = W Xq for N <= 8 int8-quantized activation columns in one pass over the
+ * packed Q4_K matrix W (batched verification, "Why Local LLMs Don't Need C++ or
+ * Python", section 4, on the integer path of the dotLLM README's Q8_1 input
+ * quantization). xq holds N consecutive buffers of qg_q8_1_bytes(K) bytes, column n
+ * at xq + n * qg_q8_1_bytes(K), each written by qg_quantize_q8_1. Y is column-major
+ * (column n at Y + n * ldy, ldy >= M, a multiple of 4). Column n equals
+ * qgemv_q4k_q8_1 of buffer n (bit for bit when K >= 2304). 1 <= N <= 8; other shape
+ * rules as for qgemv_q4k_q8_1. Needs no workspace.
+ */
+typedef struct {
+    const void* w_packed;
+    const void* xq;
+    float* Y;
+    int64_t ldy;
+    int64_t M;
+    int64_t K;
+    int64_t N;
+} qg_gemm_q8_1_problem;
+size_t qgemm_q4k_q8_1_smalln_workspace_bytes(int64_t M, int64_t K, int64_t N);
+int qgemm_q4k_q8_1_smalln(const void* w_packed, const void* xq, float* Y, int64_t ldy, int64_t M, int64_t K,
+                          int64_t N, void* workspace, size_t workspace_bytes, qg_stream_t stream);
+size_t qgemm_q4k_q8_1_smalln_batch_workspace_bytes(const qg_gemm_q8_1_problem* problems /* host */, int count);
+int qgemm_q4k_q8_1_smalln_batch(const qg_gemm_q8_1_problem* problems /* host */, int count,
+                                void* workspace, size_t workspace_bytes, qg_stream_t stream);
+
+/*
  * Several independent Q4_K GEMVs in one launch (the dotLLM README's fused decode
  * dispatch of Q/K/V and of gate/up). Problems must not write overlapping outputs.
  * 1 <= count <= QG_MAX_BATCH. Each entry follows qgemv_q4k's rules.

@@ -39,6 +39,11 @@ class _GemmProblem(ctypes.Structure):
                 ("N", ctypes.c_int64)]
 
 
+class _GemmQ81Problem(ctypes.Structure):
+    _fields_ = [("w_packed", ctypes.c_void_p), ("xq", ctypes.c_void_p), ("Y", ctypes.c_void_p),
+                ("ldy", ctypes.c_int64), ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64)]
+
+
 class _TopkOut(ctypes.Structure):
     _fields_ = [("index", ctypes.c_void_p), ("logit", ctypes.c_void_p), ("logprob", ctypes.c_void_p),
                 ("lse", ctypes.c_void_p), ("token", ctypes.c_void_p)]
@@ -74,6 +79,10 @@ _SIGS = {
     "qgemv_q4k_q8_1": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "qgemv_q4k_q8_1_batch_workspace_bytes": (_SZ, [ctypes.POINTER(_Problem), _I]),
     "qgemv_q4k_q8_1_batch": (_I, [ctypes.POINTER(_Problem), _I, _P, _SZ, _P]),
+    "qgemm_q4k_q8_1_smalln_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "qgemm_q4k_q8_1_smalln": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
+    "qgemm_q4k_q8_1_smalln_batch_workspace_bytes": (_SZ, [ctypes.POINTER(_GemmQ81Problem), _I]),
+    "qgemm_q4k_q8_1_smalln_batch": (_I, [ctypes.POINTER(_GemmQ81Problem), _I, _P, _SZ, _P]),
     "qgemv_q6k_workspace_bytes": (_SZ, [_I64, _I64]),
     "qgemv_q6k": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "qgemm_q4k_smalln_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
@@ -311,6 +320,50 @@ def qgemv_q4k_q8_1_batch(problems, ws: Workspace | None = None):
     ws = _ws(ws, need, dev)
     _check("qgemv_q4k_q8_1_batch", lib().qgemv_q4k_q8_1_batch(arr, len(problems), ws.ptr(), ws.nbytes(),
                                                               _stream(dev)))
+    return [p[2] for p in problems]
+
+
+def quantize_q8_1_columns(X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """X (N, ldx) fp32 rows of K = ldx activations each -> N consecutive Q8_1 buffers
+    of q8_1_bytes(K) bytes (one qg_quantize_q8_1 call per column)."""
+    _need_cuda(X, out)
+    N, K = X.shape
+    nb = q8_1_bytes(K)
+    out = out if out is not None else torch.empty(N * nb, dtype=torch.uint8, device=X.device)
+    for n in range(N):
+        quantize_q8_1(X[n], out=out[n * nb:(n + 1) * nb])
+    return out
+
+
+def qgemm_q4k_q8_1_smalln(w: torch.Tensor, xq: torch.Tensor, M: int, K: int, N: int, Y: torch.Tensor | None = None,
+                          ws: Workspace | None = None) -> torch.Tensor:
+    """Y (N, ldy) = W Xq for N <= 8 quantized columns (quantize_q8_1_columns)."""
+    _need_cuda(w, xq, Y)
+    Y = Y if Y is not None else torch.empty((N, (M + 3) // 4 * 4), dtype=torch.float32, device=xq.device)
+    if Y.shape[0] != N or Y.stride(1) != 1:
+        raise ValueError("Y must be a contiguous (N, ldy) tensor")
+    need = int(lib().qgemm_q4k_q8_1_smalln_workspace_bytes(M, K, N))
+    ws = _ws(ws, need, xq.device)
+    _check("qgemm_q4k_q8_1_smalln", lib().qgemm_q4k_q8_1_smalln(_ptr(w), _ptr(xq), _ptr(Y), Y.stride(0), M, K, N,
+                                                                ws.ptr(), ws.nbytes(), _stream(xq.device)))
+    return Y
+
+
+def qgemm_q4k_q8_1_smalln_batch(problems, ws: Workspace | None = None):
+    """problems: list of (w_packed, xq, Y, M, K) with Y (N, ldy) and xq holding N
+    quantized columns; one launch for all of them."""
+    arr = (_GemmQ81Problem * len(problems))()
+    dev = None
+    for i, (w, xq, Y, M, K) in enumerate(problems):
+        _need_cuda(w, xq, Y)
+        dev = xq.device
+        if Y.stride(1) != 1:
+            raise ValueError("Y must be a contiguous (N, ldy) tensor")
+        arr[i] = _GemmQ81Problem(_ptr(w), _ptr(xq), _ptr(Y), Y.stride(0), M, K, Y.shape[0])
+    need = int(lib().qgemm_q4k_q8_1_smalln_batch_workspace_bytes(arr, len(problems)))
+    ws = _ws(ws, need, dev)
+    _check("qgemm_q4k_q8_1_smalln_batch",
+           lib().qgemm_q4k_q8_1_smalln_batch(arr, len(problems), ws.ptr(), ws.nbytes(), _stream(dev)))
     return [p[2] for p in problems]
 
 

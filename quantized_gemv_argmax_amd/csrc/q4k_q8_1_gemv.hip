@@ -242,6 +242,12 @@ bool k_ok(int64_t K) { return K >= 256 && K % 256 == 0 && K <= (1 << 24); }
 
 }  // namespace
 
+void qg::q8_1_offsets(int64_t K, size_t* q_off, size_t* s_off) {
+    const Q81Layout L = q81_layout(K);
+    *q_off = L.q_off;
+    *s_off = L.s_off;
+}
+
 extern "C" {
 
 size_t qg_q8_1_bytes(int64_t K) { return k_ok(K) ? q81_layout(K).total : 0; }

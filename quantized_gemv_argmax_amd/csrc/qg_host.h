@@ -40,6 +40,10 @@ size_t topk_ws_bytes(int64_t M);
 int launch_topk_select(void* ws, int tiles, const float* logits, int64_t M, int k, const qg_sampler* sampler,
                        const qg_topk_out& out, hipStream_t s);
 
+// Byte offsets of the int8 quants and of the block sums in a Q8_1 activation
+// buffer of qg_q8_1_bytes(K) bytes (the block scales start at 0).
+void q8_1_offsets(int64_t K, size_t* q_off, size_t* s_off);
+
 // Vector-ALU dot-product form of the small-N product (q4k_smalln_dot.hip), for
 // problems the small-N entry points have validated, each with N <= 8.
 int smalln_dot_launch(const qg_gemm_problem* probs, int count, hipStream_t s);

@@ -2,7 +2,8 @@
 step with the benchmark's seeded weights and activations, launched as the benchmark
 launches it (one grouped launch per dependency stage: {q,k,v}, {o}, {gate,up},
 {down}), for the fp32-activation GEMV (every row of all seven matrices), the int8-
-activation GEMV, and the small-N verify product at N = 5, N = 32 and N = 2 (sampled rows)."""
+activation GEMV and N = 5 verify product, and the small-N verify product at N = 5, N = 32
+and N = 2 (sampled rows)."""
 import numpy as np
 import pytest
 import torch
@@ -57,6 +58,34 @@ def test_int8_decode_step_layer_as_timed():
         rows, (yr, ar) = refs[i]
         y = ys[i].cpu().numpy()[rows]
         assert np.all(np.abs(y - yr) <= 1e-5 * ar + 1e-6), f"int8 layer 0 {name}"
+
+
+def test_int8_verify_step_layer_as_timed():
+    # the N = 5 verify step on int8 activations, as the benchmark launches it
+    L, N = 0, 5
+    mats = _layer(L)
+    xqs, refs = [], []
+    for i, (name, W, _, M, K) in enumerate(mats):
+        X = workloads.x_columns(K, N, key=(5, L, i, N))
+        xq = qg.quantize_q8_1_columns(to_dev(X))
+        nb = qg.q8_1_bytes(K)
+        rows = sample_rows(M, 96, seed=M + K + i)
+        cols = []
+        for n in range(N):
+            d, q, _ = (t.cpu().numpy() for t in qg.q8_1_views(xq[n * nb:(n + 1) * nb], K))
+            cols.append(oracle.gemv_q4k_q8_1(W, M, K, d, q, rows=rows))
+        refs.append((rows, cols))
+        xqs.append(xq)
+    Ys = [torch.full((N, (M + 3) // 4 * 4), float("nan"), device=DEV) for (_, _, _, M, _) in mats]
+    case("qgemm_q4k_q8_1_smalln_batch N=5, layer 0 of the verify step, stage by stage")
+    for st in workloads.LAYER_STAGES:
+        qg.qgemm_q4k_q8_1_smalln_batch([(mats[i][2], xqs[i], Ys[i], mats[i][3], mats[i][4]) for i in st])
+    torch.cuda.synchronize()
+    for i, (name, W, _, M, K) in enumerate(mats):
+        rows, cols = refs[i]
+        Y = Ys[i].cpu().numpy()[:, :M][:, rows]
+        for n, (yr, ar) in enumerate(cols):
+            assert np.all(np.abs(Y[n] - yr) <= 1e-5 * ar + 1e-6), f"int8 verify layer 0 {name} col {n}"
 
 
 @pytest.mark.parametrize("N", [5, 32, 2])
