@@ -301,6 +301,14 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
                     X_ = torch.from_numpy(wl.x_columns(K_, N, key=(5, L, i, N))).to(dev)
                     grp.append((wp_, X_, torch.empty((N, (M_ + 3) // 4 * 4), device=dev), M_, K_))
                 qg.qgemm_q4k_smalln_batch(grp, ws=ws)
+    for L in range(n_layers):  # N = 5 on int8 activations
+        for st in wl.LAYER_STAGES:
+            grp = []
+            for i in st:
+                wp_, _, _, M_, K_ = layers[L][i]
+                X_ = torch.from_numpy(wl.x_columns(K_, 5, key=(5, L, i, 5))).to(dev)
+                grp.append((wp_, qg.quantize_q8_1_columns(X_), torch.empty((5, (M_ + 3) // 4 * 4), device=dev), M_, K_))
+            qg.qgemm_q4k_q8_1_smalln_batch(grp, ws=ws)
     for (M, K), reps in [((wl.HIDDEN, wl.FFN), 3), ((wl.VOCAB, wl.HIDDEN), 2)]:
         W = wl.q6k_blocks(M, K, key=(6, M))
         wp = qg.pack_q6k(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
