@@ -233,3 +233,37 @@ def test_q8_1_batch_validation(L):
     arr[1] = P(C, A + 4, B, 64, 256)
     assert f(arr, 2, None, 0, None) == EALIGN
     assert L.qgemv_q4k_q8_1_batch_workspace_bytes(arr, 2) == 0
+
+
+def test_q8_1_smalln_validation(L):
+    f = L.qgemm_q4k_q8_1_smalln
+    #  w, xq, Y, ldy, M, K, N
+    assert f(C, None, B, 64, 64, 256, 5, None, 0, None) == ENULL
+    assert f(C, A, B, 64, 64, 256, 0, None, 0, None) == ESHAPE    # N < 1
+    assert f(C, A, B, 64, 64, 256, 9, None, 0, None) == ESHAPE    # N > 8
+    assert f(C, A, B, 64, 64, 300, 5, None, 0, None) == ESHAPE    # K % 256
+    assert f(C, A, B, 60, 64, 256, 5, None, 0, None) == ESHAPE    # ldy < M
+    assert f(C, A, B, 66, 64, 256, 5, None, 0, None) == ESHAPE    # ldy % 4
+    assert f(C, A, B, 64, 0, 256, 5, None, 0, None) == ESHAPE     # M < 1
+    assert f(C, A + 8, B, 64, 64, 256, 5, None, 0, None) == EALIGN
+    assert L.qgemm_q4k_q8_1_smalln_workspace_bytes(3584, 3584, 5) == 0
+    P = qg._GemmQ81Problem
+    arr = (P * 9)()
+    for i in range(9):
+        arr[i] = P(C, A, B, 64, 64, 256, 5)
+    g = L.qgemm_q4k_q8_1_smalln_batch
+    assert g(arr, 0, None, 0, None) == ESHAPE
+    assert g(arr, 9, None, 0, None) == ESHAPE
+    assert g(None, 1, None, 0, None) == ENULL
+    arr[1] = P(C, A, None, 64, 64, 256, 5)
+    assert g(arr, 2, None, 0, None) == ENULL
+    assert L.qgemm_q4k_q8_1_smalln_batch_workspace_bytes(arr, 2) == 0
+
+
+def test_smalln_dot_form_validation_unchanged(L, monkeypatch):
+    # forcing the dot form does not relax the small-N argument checks
+    monkeypatch.setenv("QG_SN_IMPL", "dot")
+    f = L.qgemm_q4k_smalln
+    assert f(C, A, 256, B, 64, 64, 256, 0, None, 0, None) == ESHAPE
+    assert f(C, A, 128, B, 64, 64, 256, 3, None, 0, None) == ESHAPE   # ldx < K
+    assert f(C, A + 4, 256, B, 64, 64, 256, 3, None, 0, None) == EALIGN
