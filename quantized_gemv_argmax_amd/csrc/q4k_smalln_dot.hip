@@ -40,7 +40,8 @@ struct SdProb {
     const uint8_t* w;
     const float* X;
     float* Y;
-    int32_t ldx, ldy, M, nb, N, wg_begin;
+    int64_t ldy;
+    int32_t ldx, M, nb, N, wg_begin;  // (N - 1) * ldx + K < 2^29 (checked by the entry points)
 };
 struct SdArgs {
     int32_t begin[QG_MAX_BATCH];
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_dot_kernel(SdArgs a) {
             float v = red[0][n][r];
 #pragma unroll
             for (int w = 1; w < W; ++w) v += red[w][n][r];
-            P.Y[(size_t)n * P.ldy + tile * T + r] = v;
+            P.Y[n * P.ldy + tile * T + r] = v;
         }
     }
 }
@@ -363,8 +364,8 @@ int smalln_dot_launch(const qg_gemm_problem* probs, int count, hipStream_t s) {
         P.w = (const uint8_t*)q.w_packed;
         P.X = q.X;
         P.Y = q.Y;
-        P.ldx = (int32_t)q.ldx;
-        P.ldy = (int32_t)q.ldy;
+        P.ldx = q.N > 1 ? (int32_t)q.ldx : 0;  // the first column needs no stride
+        P.ldy = q.ldy;
         P.M = (int32_t)q.M;
         P.nb = (int32_t)(q.K / 256);
         P.N = (int32_t)q.N;
