@@ -210,7 +210,7 @@ def test_verify_vocab_152064_n5():
     print(f"exact-match rate {exact}/{N}")
 
 
-@pytest.mark.parametrize("cfg", ["8,1", "8,2", "8,4", "4,2"])
+@pytest.mark.parametrize("cfg", ["8,1", "8,2", "8,4", "4,2", "4,4"])
 @pytest.mark.parametrize("N", [5, 20])
 def test_verify_launch_shapes(cfg, N, monkeypatch):
     # every (wavefronts, tiles per workgroup) shape, with a tile count that is not a
