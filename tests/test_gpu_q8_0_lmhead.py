@@ -100,6 +100,7 @@ def test_lmhead_vocab_152064_with_resampling():
     wp = packed_q8_0(W, M, K)
     exact = 0
     trials = 16
+    worst = 0.0  # largest |out_value - y_ref[id]| / tol over the trials
     for t in range(trials):
         r = 0
         while True:
@@ -119,8 +120,9 @@ def test_lmhead_vocab_152064_with_resampling():
         else:  # within the tolerance band any row that could be the maximum will do
             assert yr[gi] >= yr[ri] - tol[gi] - tol[ri]
         assert abs(gv - yr[gi]) <= tol[gi]
+        worst = max(worst, abs(gv - yr[gi]) / tol[gi])
         exact += gi == ri
-    print(f"exact-match rate {exact}/{trials}")
+    print(f"exact-match rate {exact}/{trials}, largest out_value error {worst:.4f} of the tolerance")
 
 
 def test_lmhead_leaves_workspace_zero():
