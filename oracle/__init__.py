@@ -58,6 +58,7 @@ def lib():
         L.or_num_threads.restype = ctypes.c_int
         L.or_quantize_q8_1.argtypes = [_P, _I64, _P, _P, _P]
         L.or_gemv_q4k_q8_1.argtypes = [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P]
+        L.or_gemv_q8_0_q8_1.argtypes = [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P]
         L.or_topk.argtypes = [_P, _I64, ctypes.c_int, _P]
         L.or_logsumexp.restype = ctypes.c_double
         L.or_logsumexp.argtypes = [_P, _I64]
@@ -227,6 +228,20 @@ def gemv_q4k_q8_1(W, M: int, K: int, d, q, rows=None):
     y = np.zeros(n, np.float64)
     a = np.zeros(n, np.float64)
     lib().or_gemv_q4k_q8_1(_ptr(W), M, K, _ptr(d), _ptr(q), _ptr(r), n, _ptr(y), _ptr(a))
+    return y, a
+
+
+def gemv_q8_0_q8_1(W, M: int, K: int, d, q, rows=None):
+    """y = W xq for a Q8_0 matrix W and xq = d[k/32] * q[k]; returns (y, sum|w*xq|) in fp64."""
+    W = _u8(W)
+    if W.size != M * (K // 32) * 34:
+        raise ValueError("weight bytes do not match M x K")
+    d = np.ascontiguousarray(d, dtype=np.float32)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    r, n = _rows(rows, M)
+    y = np.zeros(n, np.float64)
+    a = np.zeros(n, np.float64)
+    lib().or_gemv_q8_0_q8_1(_ptr(W), M, K, _ptr(d), _ptr(q), _ptr(r), n, _ptr(y), _ptr(a))
     return y, a
 
 

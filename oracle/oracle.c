@@ -247,6 +247,29 @@ void or_gemv_q4k_q8_1(const uint8_t* W, int64_t M, int64_t K, const float* d, co
     }
 }
 
+void or_gemv_q8_0_q8_1(const uint8_t* W, int64_t M, int64_t K, const float* d, const int8_t* q,
+                      const int64_t* rows, int64_t nrows, double* y, double* a) {
+    (void)M;
+#pragma omp parallel
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < nrows; ++i) {
+            const int64_t r = rows ? rows[i] : i;
+            or_q8_0_dequant_row(W + r * (K / 32) * 34, K, w);
+            double sum = 0.0, t = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double p = w[k] * ((double)d[k / 32] * (double)q[k]);
+                sum += p;
+                t += fabs(p);
+            }
+            y[i] = sum;
+            if (a) a[i] = t;
+        }
+        free(w);
+    }
+}
+
 /* ------------------------------------------------------------------ sampling */
 
 static double finite_or_neg_inf(double v) { return v != v ? -INFINITY : v; }

@@ -109,6 +109,11 @@ void or_quantize_q8_1(const float* x, int64_t K, float* d, int8_t* q, int16_t* s
 void or_gemv_q4k_q8_1(const uint8_t* W, int64_t M, int64_t K, const float* d, const int8_t* q,
                       const int64_t* rows, int64_t nrows, double* y, double* a);
 
+/* y = W xq for a Q8_0 matrix W (the LM head) and the same dequantized activations
+ * xq_k = d[k/32] * q[k] (fp64, dense form; rows and a as for or_gemv_q8_0). */
+void or_gemv_q8_0_q8_1(const uint8_t* W, int64_t M, int64_t K, const float* d, const int8_t* q,
+                       const int64_t* rows, int64_t nrows, double* y, double* a);
+
 /*
  * Sampling-side reductions over a logit vector (dotLLM README: the news entry on
  * log-probabilities, top_logprobs 0..20 from the per-token log-softmax taken

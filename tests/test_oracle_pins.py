@@ -585,3 +585,49 @@ def test_q8_1_gemv_within_the_parity_tolerance_of_fp32_activations():
         y8, _ = oracle.gemv_q4k_q8_1(W, M, K, d, q)
         y, a = oracle.gemv_q4k(W, M, K, x)
         assert np.all(np.abs(y8 - y) <= oracle.tolerance(a))
+
+
+def test_q8_0_q8_1_gemv_exact_when_quantization_is_exact():
+    # LM head with integer activations: multiples of 1/8 with 127/8 in every block
+    # quantize without error, so the product equals the fp32-activation Q8_0 product
+    M, K = 41, 1024
+    W = workloads.q8_0_blocks(M, K, key=(54,))
+    k = np.random.default_rng(54).integers(-127, 128, K)
+    k[5::32] = -127
+    x = (k / 8).astype(np.float32)
+    d, q, _ = oracle.quantize_q8_1(x)
+    assert np.array_equal(q.astype(np.int64), k)
+    y8, a8 = oracle.gemv_q8_0_q8_1(W, M, K, d, q)
+    y, a = oracle.gemv_q8_0(W, M, K, x)
+    assert np.array_equal(y8, y) and np.array_equal(a8, a)
+    rows = np.array([40, 0, 17])
+    yr, ar = oracle.gemv_q8_0_q8_1(W, M, K, d, q, rows=rows)
+    assert np.array_equal(yr, y[rows]) and np.array_equal(ar, a[rows])
+
+
+def test_q8_0_q8_1_gemv_integer_case_against_int64_matmul():
+    # fp16 scale 1.0 in every weight block: weights are the int8 quants; activations
+    # k/4 with 127/4 in every block: y = (Q @ k) / 4 exactly, signs of both kept
+    M, K = 7, 320
+    rng = np.random.default_rng(55)
+    Q = rng.integers(-128, 128, (M, K))
+    W = np.stack([np.concatenate([enc.q8_0_block(0x3C00, Q[r, 32 * b:32 * b + 32]) for b in range(K // 32)])
+                  for r in range(M)])
+    k = rng.integers(-127, 128, K)
+    k[::32] = 127
+    d, q, _ = oracle.quantize_q8_1((k / 4).astype(np.float32))
+    y, a = oracle.gemv_q8_0_q8_1(W, M, K, d, q)
+    assert np.array_equal(y * 4, (Q @ k).astype(np.float64))
+    assert np.array_equal(a * 4, (np.abs(Q) @ np.abs(k)).astype(np.float64))
+
+
+def test_q8_0_q8_1_gemv_within_the_parity_tolerance_of_fp32_activations():
+    # at the LM-head width the activation quantization keeps the logits inside
+    # 1e-3 * sum|w x| of the fp32-activation logits
+    M, K = 96, 3584
+    W = workloads.q8_0_blocks(M, K, key=(56,))
+    x = workloads.x_vector(K, key=(56,))
+    d, q, _ = oracle.quantize_q8_1(x)
+    y8, _ = oracle.gemv_q8_0_q8_1(W, M, K, d, q)
+    y, a = oracle.gemv_q8_0(W, M, K, x)
+    assert np.all(np.abs(y8 - y) <= oracle.tolerance(a))
