@@ -15,7 +15,8 @@ wall divides them), the roofline entry of the dominant kernel (Q4_K GEMV: bytes
 per launch / average launch duration from HIP events on the launch stream), the
 fp64 CPU oracle timed on a bounded sample, and the other hot-path rows (single
 4096x4096 Q4_K GEMV, Q8_0 11008x4096 / 4096x11008, Q6_K 3584x18944 / 152064x3584,
-fused 152064x3584 LM head + argmax, the same head verifying 5 columns, top-20 with
+fused 152064x3584 LM head + argmax, the same head verifying 5 columns (fp32 and int8
+activations), top-20 with
 log-probabilities and one sampled token, small-N verify N=5, N=32 and N=2 over the
 same 196 matrices, the N=5 verify step and the decode step with int8 activations), each timed with rotation over
 enough weight copies to defeat the Infinity Cache.
@@ -260,7 +261,7 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     """Each of the other hot-path kernels a few times, every call on its own weight
     copy, in this order: 4096x4096 Q4_K GEMV (3 calls), Q8_0 11008x4096 and
     4096x11008 (3 each), LM head + argmax 152064x3584 (2), the same head verifying 5
-    columns (2), top-20 + sampling on that head (2), small-N N=5 then N=32 over
+    columns (2) and 5 int8 columns (2), top-20 + sampling on that head (2), small-N N=5 then N=32 over
     the layers' stages (one grouped launch per stage), Q6_K 3584x18944 (3) and
     152064x3584 (2), int8-activation Q4_K 4096x4096 (3, after one quantization)."""
     M, K = 4096, 4096
@@ -288,6 +289,9 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     X5 = torch.from_numpy(wl.x_columns(K, 5, key=(4, 3))).to(dev)
     for c in copies:
         qg.lmhead_argmax_verify(c, X5, M, K, ws=ws)
+    X5q = qg.quantize_q8_1_columns(X5)
+    for c in copies:
+        qg.lmhead_argmax_verify_q8_1(c, X5q, M, K, 5, ws=ws)
     u_dev = torch.full((1,), 0.5, device=dev)
     for c in copies:
         qg.lmhead_topk(c, x, M, K, 20, sampler=(0.8, 0.95, 0.05, u_dev), ws=ws)
@@ -436,6 +440,17 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
                                             "bytes": int(b), "us_per_single_column_argmax": round(
                                                 rows["lmhead_argmax_152064x3584"]["us"], 3)}
     log(f"row lmhead verify N=5: {rows['lmhead_verify_N5_152064x3584']}")
+
+    # the same verification on int8 activations (the columns quantized beforehand,
+    # as in the int8 decode row)
+    X5q = qg.quantize_q8_1_columns(X5)
+    ms = graph_ms(torch, lambda: [qg.lmhead_argmax_verify_q8_1(c, X5q, M, K, N, out_index=oi5, out_value=ov5, ws=ws)
+                                  for c in copies], 20) / 2
+    b = wp.numel() + X5q.numel() + 8 * (-(-M // 16)) * N * 2 + 8 * N
+    rows["lmhead_verify_N5_int8_activations"] = {
+        "us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": int(b),
+        "us_fp32_activations": rows["lmhead_verify_N5_152064x3584"]["us"]}
+    log(f"row lmhead verify N=5, int8 activations: {rows['lmhead_verify_N5_int8_activations']}")
 
     # top-20 log-probabilities and one sampled token on the same head (T 0.8,
     # top-p 0.95, min-p 0.05); the logits stay in a device buffer

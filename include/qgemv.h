@@ -276,6 +276,21 @@ int lmhead_argmax_verify(const void* w_packed_q8_0, const float* X, int64_t ldx,
                          int32_t* out_index, float* out_value, qg_stream_t stream);
 
 /*
+ * The same batched verification with int8 activations (the dotLLM README's Q8_1
+ * input quantization on the integer path): xq holds N consecutive buffers of
+ * qg_q8_1_bytes(K) bytes, column n at xq + n * qg_q8_1_bytes(K), each written by
+ * qg_quantize_q8_1. logit_{i,n} = sum_k w_ik d_n[k/32] q_n[k]; both quant operands
+ * are int8, the integer block products are exact and each block's term is scaled in
+ * fp32. 1 <= N <= 8, K % 256 == 0; outputs, workspace
+ * (lmhead_argmax_verify_q8_1_workspace_bytes(M, K, N), left zero) and the argmax
+ * rule as for lmhead_argmax_verify.
+ */
+size_t lmhead_argmax_verify_q8_1_workspace_bytes(int64_t M, int64_t K, int64_t N);
+int lmhead_argmax_verify_q8_1(const void* w_packed_q8_0, const void* xq, int64_t M, int64_t K, int64_t N,
+                              void* workspace, size_t workspace_bytes,
+                              int32_t* out_index, float* out_value, qg_stream_t stream);
+
+/*
  * Top-k, log-softmax and the top-k sampler over a logit vector, on the device
  * (dotLLM README: the news entry on log-probabilities, top_logprobs 0..20 from
  * the per-token log-softmax taken before sampling; Key Features, composable

@@ -91,6 +91,8 @@ _SIGS = {
     "qgemm_q4k_smalln_batch": (_I, [ctypes.POINTER(_GemmProblem), _I, _P, _SZ, _P]),
     "lmhead_argmax_verify_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "lmhead_argmax_verify": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P, _P, _P]),
+    "lmhead_argmax_verify_q8_1_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "lmhead_argmax_verify_q8_1": (_I, [_P, _P, _I64, _I64, _I64, _P, _SZ, _P, _P, _P]),
     "lmhead_argmax_workspace_bytes": (_SZ, [_I64, _I64]),
     "logits_topk_workspace_bytes": (_SZ, [_I64]),
     "logits_topk": (_I, [_P, _I64, _I, ctypes.POINTER(_Sampler), _P, _SZ, ctypes.POINTER(_TopkOut), _P]),
@@ -443,6 +445,22 @@ def lmhead_argmax_verify(w: torch.Tensor, X: torch.Tensor, M: int, K: int, out_i
     ws = _ws(ws, need, X.device)
     _check("lmhead_argmax_verify", lib().lmhead_argmax_verify(_ptr(w), _ptr(X), ldx, M, K, N, ws.ptr(), ws.nbytes(),
                                                               _ptr(oi), _ptr(ov), _stream(X.device)))
+    return oi, ov
+
+
+def lmhead_argmax_verify_q8_1(w: torch.Tensor, xq: torch.Tensor, M: int, K: int, N: int,
+                              out_index: torch.Tensor | None = None, out_value: torch.Tensor | None = None,
+                              ws: Workspace | None = None):
+    """Batched greedy verification on a Q8_0 LM head against N <= 8 quantized columns
+    (quantize_q8_1_columns). Returns (index int32[N], value float32[N]) device tensors."""
+    _need_cuda(w, xq, out_index, out_value)
+    oi = out_index if out_index is not None else torch.empty(N, dtype=torch.int32, device=xq.device)
+    ov = out_value if out_value is not None else torch.empty(N, dtype=torch.float32, device=xq.device)
+    need = int(lib().lmhead_argmax_verify_q8_1_workspace_bytes(M, K, N))
+    ws = _ws(ws, need, xq.device)
+    _check("lmhead_argmax_verify_q8_1",
+           lib().lmhead_argmax_verify_q8_1(_ptr(w), _ptr(xq), M, K, N, ws.ptr(), ws.nbytes(), _ptr(oi), _ptr(ov),
+                                           _stream(xq.device)))
     return oi, ov
 
 

@@ -302,6 +302,208 @@ void va_launch(const VaProb& P, int W, hipStream_t s) {
         hipLaunchKernelGGL((lmhead_verify_tile_kernel<C, TW, 4>), grid, dim3(256), 0, s, P);
 }
 
+// ---------------------------------------------------------------------------
+// Int8 activations: each column quantized Q8_1-style (qg_quantize_q8_1: a float32
+// scale d_x and 32 int8 quants per block). Both operands are then signed int8, so
+// a block's integer product S = sum_l q_w,l q_x,l comes straight from
+// v_dot4c_i32_i8 with no bias term, and logit += d_w (d_x S). Work decomposition
+// of the single-column LM head (q8_0_gemv.hip): lane = weight row, each DPP row a
+// K-group walking half macro-blocks (4 blocks, 128 weights); the lane of slot i
+// holds activation dwords 2i, 2i + 1 of the half for every column, and DPP row
+// broadcasts feed them to the 16 rows. Per column and block: 8 v_dot4c_i32_i8,
+// 4 integer additions and 3 float operations; the quant segments are used as
+// loaded. Stage 2 is lmhead_verify_reduce_kernel, on the same partials layout.
+
+struct VqProb {
+    const uint8_t* w;
+    const uint8_t* xq;  // N buffers of xb bytes
+    float2* partials;   // [N][tiles]
+    int32_t xb, q_off, M, nmb, N, tiles;
+};
+
+template <int NC>
+struct VqIn {
+    uint4 s[9];   // scale segment, then the 8 quant segments of the half macro-block
+    uint2 x[NC];  // activation dwords 2i, 2i + 1 of the half (i = lane % 16), per column
+    float dx[NC]; // scale of block i % 4 of the half, per column
+};
+
+// One block of one column: quant segments q0, q1 (weights 0..15, 16..31) against
+// the activation dwords of lanes L, L + 1, L + 2, L + 3 (L = 4k). Four accumulators
+// rotate, so none is re-read within two instructions of its last write; the block
+// opens with two wait states (the accumulators may come from ordinary VALU code)
+// and ends with s_nop 4 before ordinary VALU code reads them.
+template <int L>
+QG_DEV void blk_dot4(int (&a)[4], const uint4 q0, const uint4 q1, const uint2 x) {
+    asm("s_nop 1\n\t"
+        "v_dot4c_i32_i8_dpp %0, %12, %4 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %13, %5 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %12, %6 row_newbcast:%15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %13, %7 row_newbcast:%15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %12, %8 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %13, %9 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %2, %12, %10 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %3, %13, %11 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 4"
+        : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+        : "v"(q0.x), "v"(q0.y), "v"(q0.z), "v"(q0.w), "v"(q1.x), "v"(q1.y), "v"(q1.z), "v"(q1.w), "v"(x.x),
+          "v"(x.y), "n"(L), "n"(L + 1), "n"(L + 2), "n"(L + 3));
+}
+
+// Half macro-block u (macro-block u / 2, blocks 4 (u % 2) .. + 3) of this lane's
+// row: `vrow` = 16 * row, `vx[n]` = column n's quant offset of this lane (out of
+// range past N), `vd[n]` its scale offset.
+template <int NC>
+QG_DEV void load_half_q(VqIn<NC>& d, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t xr, uint32_t vrow, int rt,
+                        const uint32_t (&vx)[NC], const uint32_t (&vd)[NC], int u) {
+    const int mb = u >> 1, h = u & 1;
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const qg_u2v a = __builtin_amdgcn_raw_buffer_load_b64(xr, vx[n] + 128u * (uint32_t)u, 0, 0);
+        d.x[n] = make_uint2(a.x, a.y);
+        d.dx[n] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(xr, vd[n] + 16u * (uint32_t)u, 0, 0));
+    }
+    const uint32_t vs = vrow + (uint32_t)mb * 17u * 16u * (uint32_t)rt;
+    // the scales serve both halves: a cached load
+    const qg_u4v sv = __builtin_amdgcn_raw_buffer_load_b128(wr, vs, 0, 0);
+    d.s[0] = make_uint4(sv.x, sv.y, sv.z, sv.w);
+    const uint32_t vq = vs + (uint32_t)(8 * h) * 16u * (uint32_t)rt;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const qg_u4v v = __builtin_amdgcn_raw_buffer_load_b128(wr, vq, (1 + j) * 16 * rt, kQgNonTemporal);
+        d.s[1 + j] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+}
+
+template <int NC>
+QG_DEV void half_dot_q(float (&acc)[NC], const VqIn<NC>& d, int h, bool live) {
+    const uint32_t dw0 = h ? d.s[0].z : d.s[0].x;
+    const uint32_t dw1 = h ? d.s[0].w : d.s[0].y;
+    const float dk[4] = {qg_half_lo(dw0), qg_half_hi(dw0), qg_half_lo(dw1), qg_half_hi(dw1)};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int a[NC][4];
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            a[n][0] = a[n][1] = a[n][2] = a[n][3] = 0;
+            switch (k) {
+                case 0: blk_dot4<0>(a[n], d.s[1], d.s[2], d.x[n]); break;
+                case 1: blk_dot4<4>(a[n], d.s[3], d.s[4], d.x[n]); break;
+                case 2: blk_dot4<8>(a[n], d.s[5], d.s[6], d.x[n]); break;
+                default: blk_dot4<12>(a[n], d.s[7], d.s[8], d.x[n]); break;
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            const int S = (a[n][0] + a[n][1]) + (a[n][2] + a[n][3]);  // |S| <= 32 * 128 * 127
+            float dxk;
+            switch (k) {
+                case 0: dxk = qg_bcast<0>(d.dx[n]); break;
+                case 1: dxk = qg_bcast<1>(d.dx[n]); break;
+                case 2: dxk = qg_bcast<2>(d.dx[n]); break;
+                default: dxk = qg_bcast<3>(d.dx[n]); break;
+            }
+            const float t = fmaf(dk[k], dxk * (float)S, acc[n]);
+            acc[n] = live ? t : acc[n];
+        }
+    }
+}
+
+template <int NC, int W>
+__global__ __launch_bounds__(64 * W) void lmhead_verify_q8_1_tile_kernel(VqProb P) {
+    const int tile = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i = lane & 15;
+    const int kg = 4 * wave + (lane >> 4);
+    constexpr int G = 4 * W;
+    const int rt = min(T, P.M - tile * T);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(P.w + (size_t)tile * T * P.nmb * 272), (short)0, rt * P.nmb * 272, kQgRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)P.xq, (short)0, P.N * P.xb, kQgRawBufferFlags);
+    const uint32_t vrow = 16u * (uint32_t)min(i, rt - 1);
+    uint32_t vx[NC], vd[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const bool in = n < P.N;
+        vx[n] = in ? (uint32_t)(n * P.xb + P.q_off + 8 * i) : kQgOutOfRange;
+        vd[n] = in ? (uint32_t)(n * P.xb + 4 * (i & 3)) : kQgOutOfRange;
+    }
+    const int nu = 2 * P.nmb;
+    float acc[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) acc[n] = 0.f;
+    // ping-pong over pairs of half macro-blocks with unconditional, clamped loads
+    // and a single-exit loop, so every wait count is exact
+    const int niter = (nu + G - 1) / G;
+    VqIn<NC> b0, b1;
+    load_half_q<NC>(b0, wr, xr, vrow, rt, vx, vd, min(kg, nu - 1));
+    int it = 0;
+    for (; it + 2 <= niter; it += 2) {
+        const int u = kg + G * it;
+        load_half_q<NC>(b1, wr, xr, vrow, rt, vx, vd, min(u + G, nu - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        half_dot_q<NC>(acc, b0, u & 1, u < nu);
+        load_half_q<NC>(b0, wr, xr, vrow, rt, vx, vd, min(u + 2 * G, nu - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        half_dot_q<NC>(acc, b1, (u + G) & 1, u + G < nu);
+    }
+    if (it < niter) {
+        const int u = kg + G * it;
+        half_dot_q<NC>(acc, b0, u & 1, u < nu);
+    }
+#pragma unroll
+    for (int n = 0; n < NC; ++n) acc[n] = qg_sum_rows4(acc[n]);
+    if constexpr (W > 1) {
+        __shared__ float red[W][NC][T];
+#pragma unroll
+        for (int n = 0; n < NC; ++n)
+            if (lane < T) red[wave][n][lane] = acc[n];
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            float v = red[0][n][i];
+#pragma unroll
+            for (int w = 1; w < W; ++w) v += red[w][n][i];
+            acc[n] = v;
+        }
+    }
+    // lanes i of each DPP row hold row i's logits: reduce over the 16 rows
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        float v = acc[n];
+        int idx = tile * T + i;
+        if (i >= rt || !(v == v)) {
+            v = -__builtin_huge_valf();
+            idx = INT_MAX;
+        }
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(v, off, 64);
+            const int oi = __shfl_xor(idx, off, 64);
+            if (va_better(ov, oi, v, idx)) {
+                v = ov;
+                idx = oi;
+            }
+        }
+        if (lane == 0 && n < P.N) P.partials[(int64_t)n * P.tiles + tile] = make_float2(v, __builtin_bit_cast(float, idx));
+    }
+}
+
+constexpr int kVqMaxCols = 8;
+
+template <int NC>
+void vq_launch(const VqProb& P, int W, hipStream_t s) {
+    const dim3 grid((unsigned)P.tiles);
+    if (W == 4)
+        hipLaunchKernelGGL((lmhead_verify_q8_1_tile_kernel<NC, 4>), grid, dim3(256), 0, s, P);
+    else
+        hipLaunchKernelGGL((lmhead_verify_q8_1_tile_kernel<NC, 1>), grid, dim3(64), 0, s, P);
+}
+
 }  // namespace
 
 extern "C" {
@@ -365,6 +567,68 @@ int lmhead_argmax_verify(const void* w, const float* X, int64_t ldx, int64_t M, 
     hipLaunchKernelGGL(lmhead_verify_reduce_kernel, dim3((unsigned)N), dim3(threads), 0, s, P.partials, P.tiles,
                        out_index, out_value);
     return qg::launch_status("lmhead_argmax_verify (reduce)");
+}
+
+size_t lmhead_argmax_verify_q8_1_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M < 1 || M > INT32_MAX || K < 256 || K % 256 || K > (1 << 24) || N < 1 || N > kVqMaxCols) return 0;
+    return va_ws_bytes(M, N);
+}
+
+int lmhead_argmax_verify_q8_1(const void* w, const void* xq, int64_t M, int64_t K, int64_t N, void* ws,
+                              size_t ws_bytes, int32_t* out_index, float* out_value, qg_stream_t stream) {
+    qg::clear_error();
+    if (!w || !xq) return qg::fail(QG_ERR_NULL, "NULL pointer");
+    if (M < 1 || M > INT32_MAX - T) return qg::fail(QG_ERR_SHAPE, "M=%lld out of range", (long long)M);
+    if (K < 256 || K % 256 || K > (1 << 24))
+        return qg::fail(QG_ERR_SHAPE, "K=%lld must be a positive multiple of 256 (<= 2^24)", (long long)K);
+    if (N < 1 || N > kVqMaxCols) return qg::fail(QG_ERR_SHAPE, "N=%lld not in [1, %d]", (long long)N, kVqMaxCols);
+    if (!qg::aligned16(w) || !qg::aligned16(xq)) return qg::fail(QG_ERR_ALIGN, "pointers must be 16-byte aligned");
+    const size_t xb = qg_q8_1_bytes(K);
+    if ((int64_t)N * (int64_t)xb >= (int64_t)kQgOutOfRange)
+        return qg::fail(QG_ERR_SHAPE, "activation buffers exceed 2^31 bytes");
+    if (!out_index) return qg::fail(QG_ERR_NULL, "out_index is NULL");
+    if ((reinterpret_cast<uintptr_t>(out_index) & 3) || (reinterpret_cast<uintptr_t>(out_value) & 3))
+        return qg::fail(QG_ERR_ALIGN, "outputs must be 4-byte aligned");
+    const size_t need = va_ws_bytes(M, N);
+    if (!ws) return qg::fail(QG_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+    if (ws_bytes < need) return qg::fail(QG_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws_bytes);
+    if (!qg::aligned16(ws)) return qg::fail(QG_ERR_ALIGN, "workspace not 16-byte aligned");
+    int st = qg::check_device();
+    if (st) return st;
+    size_t q_off = 0, s_off = 0;
+    qg::q8_1_offsets(K, &q_off, &s_off);
+    VqProb P{};
+    P.w = (const uint8_t*)w;
+    P.xq = (const uint8_t*)xq;
+    P.partials = (float2*)ws;
+    P.xb = (int32_t)xb;
+    P.q_off = (int32_t)q_off;
+    P.M = (int32_t)M;
+    P.nmb = (int32_t)(K / 256);
+    P.N = (int32_t)N;
+    P.tiles = (int32_t)qg::ceil_div(M, T);
+    // one wavefront per tile on grids that fill the chip (vocabulary-sized heads),
+    // four that split K otherwise
+    int W = P.tiles >= 1024 ? 1 : 4;
+    int ew = 0, eu = 0;
+    if (qg::env_pair("QG_VQ_CFG", &ew, &eu) && (ew == 1 || ew == 4)) W = ew;
+    hipStream_t s = (hipStream_t)stream;
+    switch (N) {
+        case 1: vq_launch<1>(P, W, s); break;
+        case 2: vq_launch<2>(P, W, s); break;
+        case 3: vq_launch<3>(P, W, s); break;
+        case 4: vq_launch<4>(P, W, s); break;
+        case 5: vq_launch<5>(P, W, s); break;
+        case 6: vq_launch<6>(P, W, s); break;
+        case 7: vq_launch<7>(P, W, s); break;
+        default: vq_launch<8>(P, W, s); break;
+    }
+    st = qg::launch_status("lmhead_argmax_verify_q8_1 (tiles)");
+    if (st) return st;
+    const int threads = (int)std::min<int64_t>(1024, std::max<int64_t>(64, qg::ceil_div(P.tiles, 8 * 64) * 64));
+    hipLaunchKernelGGL(lmhead_verify_reduce_kernel, dim3((unsigned)N), dim3(threads), 0, s, P.partials, P.tiles,
+                       out_index, out_value);
+    return qg::launch_status("lmhead_argmax_verify_q8_1 (reduce)");
 }
 
 }  // extern "C"

@@ -267,3 +267,22 @@ def test_smalln_dot_form_validation_unchanged(L, monkeypatch):
     assert f(C, A, 256, B, 64, 64, 256, 0, None, 0, None) == ESHAPE
     assert f(C, A, 128, B, 64, 64, 256, 3, None, 0, None) == ESHAPE   # ldx < K
     assert f(C, A + 4, 256, B, 64, 64, 256, 3, None, 0, None) == EALIGN
+
+
+def test_verify_q8_1_validation(L):
+    f = L.lmhead_argmax_verify_q8_1
+    out = 0x40000
+    #  w, xq, M, K, N, ws, ws_bytes, out_index, out_value, stream
+    assert f(C, None, 64, 512, 5, B, 1 << 20, out, None, None) == ENULL
+    assert f(C, A, 64, 500, 5, B, 1 << 20, out, None, None) == ESHAPE   # K % 256
+    assert f(C, A, 64, 512, 0, B, 1 << 20, out, None, None) == ESHAPE   # N = 0
+    assert f(C, A, 64, 512, 9, B, 1 << 20, out, None, None) == ESHAPE   # N > 8
+    assert f(C, A, 0, 512, 5, B, 1 << 20, out, None, None) == ESHAPE    # M < 1
+    assert f(C + 8, A, 64, 512, 5, B, 1 << 20, out, None, None) == EALIGN
+    assert f(C, A, 64, 512, 5, None, 0, out, None, None) == EWS
+    assert f(C, A, 64, 512, 5, B, 255, out, None, None) == EWS
+    assert f(C, A, 64, 512, 5, B, 1 << 20, None, None, None) == ENULL
+    assert f(C, A, 64, 512, 5, B, 1 << 20, out + 2, None, None) == EALIGN
+    assert L.lmhead_argmax_verify_q8_1_workspace_bytes(64, 512, 5) == 256
+    assert L.lmhead_argmax_verify_q8_1_workspace_bytes(152064, 3584, 5) == 152064 // 16 * 5 * 8
+    assert L.lmhead_argmax_verify_q8_1_workspace_bytes(64, 512, 9) == 0
