@@ -311,8 +311,7 @@ void va_launch(const VaProb& P, int W, hipStream_t s) {
 // K-group walking half macro-blocks (4 blocks, 128 weights); the lane of slot i
 // holds activation dwords 2i, 2i + 1 of the half for every column, and DPP row
 // broadcasts feed them to the 16 rows. Per column and block: 8 v_dot4c_i32_i8,
-// 4 integer additions and 3 float operations; the quant segments are used as
-// loaded. Stage 2 is lmhead_verify_reduce_kernel, on the same partials layout.
+// 7 integer and 4 float operations; the quant segments are used as loaded. Stage 2 is lmhead_verify_reduce_kernel, on the same partials layout.
 
 struct VqProb {
     const uint8_t* w;
@@ -351,18 +350,18 @@ QG_DEV void blk_dot4(int (&a)[4], const uint4 q0, const uint4 q1, const uint2 x)
 }
 
 // Half macro-block u (macro-block u / 2, blocks 4 (u % 2) .. + 3) of this lane's
-// row: `vrow` = 16 * row, `vx[n]` = column n's quant offset of this lane (out of
-// range past N), `vd[n]` its scale offset.
+// row: `vrow` = 16 * row, `vx` / `vd` this lane's quant / scale offset within a
+// column's buffer, `xb` the (uniform) distance between column buffers.
 template <int NC>
 QG_DEV void load_half_q(VqIn<NC>& d, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t xr, uint32_t vrow, int rt,
-                        const uint32_t (&vx)[NC], const uint32_t (&vd)[NC], int u) {
+                        uint32_t vx, uint32_t vd, int xb, int u) {
     const int mb = u >> 1, h = u & 1;
+    const uint32_t ox = vx + 128u * (uint32_t)u, od = vd + 16u * (uint32_t)u;
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
-        const qg_u2v a = __builtin_amdgcn_raw_buffer_load_b64(xr, vx[n] + 128u * (uint32_t)u, 0, 0);
+        const qg_u2v a = __builtin_amdgcn_raw_buffer_load_b64(xr, ox, n * xb, 0);
         d.x[n] = make_uint2(a.x, a.y);
-        d.dx[n] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(xr, vd[n] + 16u * (uint32_t)u, 0, 0));
+        d.dx[n] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xr, od, n * xb, 0));
     }
     const uint32_t vs = vrow + (uint32_t)mb * 17u * 16u * (uint32_t)rt;
     // the scales serve both halves: a cached load
@@ -376,27 +375,28 @@ QG_DEV void load_half_q(VqIn<NC>& d, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_
     }
 }
 
+// Column by column within each block (four integer accumulators live at a time).
+// A half that is only a clamped re-read (live false) is scaled by zero: it adds
+// nothing unless its activation scales are not finite, and then the same half's
+// live pass has made the row's logit NaN already.
 template <int NC>
 QG_DEV void half_dot_q(float (&acc)[NC], const VqIn<NC>& d, int h, bool live) {
     const uint32_t dw0 = h ? d.s[0].z : d.s[0].x;
     const uint32_t dw1 = h ? d.s[0].w : d.s[0].y;
-    const float dk[4] = {qg_half_lo(dw0), qg_half_hi(dw0), qg_half_lo(dw1), qg_half_hi(dw1)};
+    const float dk[4] = {live ? qg_half_lo(dw0) : 0.f, live ? qg_half_hi(dw0) : 0.f, live ? qg_half_lo(dw1) : 0.f,
+                         live ? qg_half_hi(dw1) : 0.f};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        int a[NC][4];
 #pragma unroll
         for (int n = 0; n < NC; ++n) {
-            a[n][0] = a[n][1] = a[n][2] = a[n][3] = 0;
+            int a[4] = {0, 0, 0, 0};
             switch (k) {
-                case 0: blk_dot4<0>(a[n], d.s[1], d.s[2], d.x[n]); break;
-                case 1: blk_dot4<4>(a[n], d.s[3], d.s[4], d.x[n]); break;
-                case 2: blk_dot4<8>(a[n], d.s[5], d.s[6], d.x[n]); break;
-                default: blk_dot4<12>(a[n], d.s[7], d.s[8], d.x[n]); break;
+                case 0: blk_dot4<0>(a, d.s[1], d.s[2], d.x[n]); break;
+                case 1: blk_dot4<4>(a, d.s[3], d.s[4], d.x[n]); break;
+                case 2: blk_dot4<8>(a, d.s[5], d.s[6], d.x[n]); break;
+                default: blk_dot4<12>(a, d.s[7], d.s[8], d.x[n]); break;
             }
-        }
-#pragma unroll
-        for (int n = 0; n < NC; ++n) {
-            const int S = (a[n][0] + a[n][1]) + (a[n][2] + a[n][3]);  // |S| <= 32 * 128 * 127
+            const int S = (a[0] + a[1]) + (a[2] + a[3]);  // |S| <= 32 * 128 * 127
             float dxk;
             switch (k) {
                 case 0: dxk = qg_bcast<0>(d.dx[n]); break;
@@ -404,8 +404,7 @@ QG_DEV void half_dot_q(float (&acc)[NC], const VqIn<NC>& d, int h, bool live) {
                 case 2: dxk = qg_bcast<2>(d.dx[n]); break;
                 default: dxk = qg_bcast<3>(d.dx[n]); break;
             }
-            const float t = fmaf(dk[k], dxk * (float)S, acc[n]);
-            acc[n] = live ? t : acc[n];
+            acc[n] = fmaf(dk[k], dxk * (float)S, acc[n]);
         }
     }
 }
@@ -424,13 +423,8 @@ __global__ __launch_bounds__(64 * W) void lmhead_verify_q8_1_tile_kernel(VqProb 
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc((void*)P.xq, (short)0, P.N * P.xb, kQgRawBufferFlags);
     const uint32_t vrow = 16u * (uint32_t)min(i, rt - 1);
-    uint32_t vx[NC], vd[NC];
-#pragma unroll
-    for (int n = 0; n < NC; ++n) {
-        const bool in = n < P.N;
-        vx[n] = in ? (uint32_t)(n * P.xb + P.q_off + 8 * i) : kQgOutOfRange;
-        vd[n] = in ? (uint32_t)(n * P.xb + 4 * (i & 3)) : kQgOutOfRange;
-    }
+    // the launch instantiates NC = N: every column is in range
+    const uint32_t vx = (uint32_t)(P.q_off + 8 * i), vd = (uint32_t)(4 * (i & 3));
     const int nu = 2 * P.nmb;
     float acc[NC];
 #pragma unroll
@@ -439,14 +433,14 @@ __global__ __launch_bounds__(64 * W) void lmhead_verify_q8_1_tile_kernel(VqProb 
     // and a single-exit loop, so every wait count is exact
     const int niter = (nu + G - 1) / G;
     VqIn<NC> b0, b1;
-    load_half_q<NC>(b0, wr, xr, vrow, rt, vx, vd, min(kg, nu - 1));
+    load_half_q<NC>(b0, wr, xr, vrow, rt, vx, vd, P.xb, min(kg, nu - 1));
     int it = 0;
     for (; it + 2 <= niter; it += 2) {
         const int u = kg + G * it;
-        load_half_q<NC>(b1, wr, xr, vrow, rt, vx, vd, min(u + G, nu - 1));
+        load_half_q<NC>(b1, wr, xr, vrow, rt, vx, vd, P.xb, min(u + G, nu - 1));
         __builtin_amdgcn_sched_barrier(0);
         half_dot_q<NC>(acc, b0, u & 1, u < nu);
-        load_half_q<NC>(b0, wr, xr, vrow, rt, vx, vd, min(u + 2 * G, nu - 1));
+        load_half_q<NC>(b0, wr, xr, vrow, rt, vx, vd, P.xb, min(u + 2 * G, nu - 1));
         __builtin_amdgcn_sched_barrier(0);
         half_dot_q<NC>(acc, b1, (u + G) & 1, u + G < nu);
     }
