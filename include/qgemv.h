@@ -268,7 +268,9 @@ int lmhead_argmax(const void* w_packed_q8_0, const float* x, int64_t M, int64_t 
  * W an M x K Q8_0 matrix in packed layout. 1 <= N <= QG_SMALLN_MAX, K % 256 == 0.
  * The weights are read once for all N columns and no logit reaches HBM. Needs
  * lmhead_argmax_verify_workspace_bytes(M, K, N) bytes of workspace (8 bytes per
- * 16-row tile and column, left zero). NaN logits never win.
+ * 16-row tile and column, and for N <= 6 another 2.125 K bytes per column for the
+ * columns rounded to fp16 and their block sums; left zero). The activations are
+ * rounded to fp16 for the products in either case. NaN logits never win.
  */
 size_t lmhead_argmax_verify_workspace_bytes(int64_t M, int64_t K, int64_t N);
 int lmhead_argmax_verify(const void* w_packed_q8_0, const float* X, int64_t ldx, int64_t M, int64_t K, int64_t N,

@@ -20,9 +20,12 @@
 // the tile then reduce per column to (max, lowest index) and one 8-byte partial
 // per (column, tile) goes to the workspace. Stage 2 (one workgroup per column)
 // reduces a column's partials in a fixed order, clears them and writes the id and
-// its logit. K must be a multiple of 256 (whole macro-blocks of 8 blocks).
+// its logit. K must be a multiple of 256 (whole macro-blocks of 8 blocks). This
+// matrix-core stage 1 serves N > 6; up to 6 columns take the vector-ALU form below.
 #include <algorithm>
 #include <climits>
+#include <cstdlib>
+#include <cstring>
 
 #include "qg_device.h"
 #include "qg_host.h"
@@ -225,10 +228,14 @@ __global__ __launch_bounds__(64 * W) void lmhead_verify_tile_kernel(VaProb P) {
     }
 }
 
-// Stage 2: workgroup n reduces column n's partials in a fixed order and clears them.
+// Stage 2: workgroup n reduces column n's partials in a fixed order and clears them;
+// the workgroups also clear `clr16` 16-byte words at `clr` (the vector-ALU form's
+// activation pairs and sums, read by stage 1 only).
 __global__ __launch_bounds__(1024) void lmhead_verify_reduce_kernel(float2* __restrict__ partials, int tiles,
-                                                                    int32_t* out_index, float* out_value) {
+                                                                    int32_t* out_index, float* out_value,
+                                                                    uint4* __restrict__ clr, int clr16) {
     const int n = blockIdx.x;
+    for (int w = n * blockDim.x + threadIdx.x; w < clr16; w += gridDim.x * blockDim.x) clr[w] = make_uint4(0, 0, 0, 0);
     float2* col = partials + (int64_t)n * tiles;
     float bv = -__builtin_huge_valf();
     int bi = INT_MAX;
@@ -300,6 +307,237 @@ void va_launch(const VaProb& P, int W, hipStream_t s) {
         hipLaunchKernelGGL((lmhead_verify_tile_kernel<C, TW, 8>), grid, dim3(512), 0, s, P);
     else
         hipLaunchKernelGGL((lmhead_verify_tile_kernel<C, TW, 4>), grid, dim3(256), 0, s, P);
+}
+
+// ---------------------------------------------------------------------------
+// Vector-ALU form for N <= 6 fp32 columns (the default there): the work
+// decomposition of the single-column LM head (lane = weight row, each DPP row a
+// K-group over half macro-blocks of 128 weights), with the quants biased to bytes
+// and read in place as fp16 subnormals as in q8_0_gemv.hip, and the masked words
+// of a segment shared by all columns. A first launch rounds each column to fp16
+// once, already in the pair order the masked words need ((x0, x2), (x1, x3),
+// (x4, x6), (x5, x7) per 8 activations), and sums every 32-weight block's rounded
+// activations in fp32 (X, which removes the bias exactly: logit += d (2^24 S' -
+// 128 X)); both go to the workspace after the partials. Per column and block:
+// 16 v_dot2c_f32_f16 with DPP row broadcasts, 3 additions and 2 fma.
+
+__global__ __launch_bounds__(256) void lmhead_verify_prep_kernel(const float* __restrict__ X, int64_t ldx, int K,
+                                                                 int N, uint4* __restrict__ pairs,
+                                                                 float* __restrict__ xsum) {
+    const int g8 = K / 8;
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= N * g8) return;  // whole quads only: N * g8 is a multiple of 32
+    const int n = t / g8, g = t - n * g8;
+    const float4* src = reinterpret_cast<const float4*>(X + (int64_t)n * ldx + 8 * g);
+    const QgPairs4 p = qg_cvt_pairs4(src[0], src[1]);
+    pairs[t] = make_uint4(p.p[0], p.p[1], p.p[2], p.p[3]);
+    // the eight rounded values, in a fixed order: (x0 + x2) + (x1 + x3) + ...
+    float v = ((qg_half_lo(p.p[0]) + qg_half_hi(p.p[0])) + (qg_half_lo(p.p[1]) + qg_half_hi(p.p[1]))) +
+              ((qg_half_lo(p.p[2]) + qg_half_hi(p.p[2])) + (qg_half_lo(p.p[3]) + qg_half_hi(p.p[3])));
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    if ((g & 3) == 0) xsum[(int64_t)n * (K / 32) + g / 4] = v;
+}
+
+struct VdProb {
+    const uint8_t* w;
+    const uint8_t* xp;  // N pair arrays of 2K bytes, then N block-sum arrays of K/8 bytes
+    float2* partials;   // [N][tiles]
+    int32_t xpb, xs_off, xsb, M, nmb, N, tiles;  // pair bytes per column, offset of the sums, sum bytes per column
+};
+
+template <int NC>
+struct VdIn {
+    uint4 s[9];    // scale segment, then the 8 quant segments of the half macro-block
+    uint4 xp[NC];  // activations 8i .. 8i + 7 of the half as fp16 pairs (i = lane % 16), per column
+    float xs[NC];  // rounded-activation sum of block i % 4 of the half, per column
+};
+
+// One quant segment of one column: masked words m (2d: bytes 0, 2 of dword d;
+// 2d + 1: bytes 1, 3) against the activation pairs of lane LA (dwords 0, 1) and LB
+// (dwords 2, 3). Opens with two wait states (masks and accumulators come from
+// ordinary VALU code); TAIL blocks end with s_nop 4 before ordinary VALU code
+// reads the accumulators.
+#define QG_SEG8H_TEXT \
+    "s_nop 1\n\t" \
+    "v_dot2c_f32_f16_dpp %0, %12, %4 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t" \
+    "v_dot2c_f32_f16_dpp %1, %13, %5 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t" \
+    "v_dot2c_f32_f16_dpp %2, %14, %6 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t" \
+    "v_dot2c_f32_f16_dpp %3, %15, %7 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t" \
+    "v_dot2c_f32_f16_dpp %0, %12, %8 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t" \
+    "v_dot2c_f32_f16_dpp %1, %13, %9 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t" \
+    "v_dot2c_f32_f16_dpp %2, %14, %10 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t" \
+    "v_dot2c_f32_f16_dpp %3, %15, %11 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
+template <int LA, bool TAIL>
+QG_DEV void seg8h_dot(float (&a)[4], const uint32_t (&m)[8], const uint4 x) {
+    if constexpr (TAIL)
+        asm(QG_SEG8H_TEXT "s_nop 4"
+            : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+            : "v"(m[0]), "v"(m[1]), "v"(m[2]), "v"(m[3]), "v"(m[4]), "v"(m[5]), "v"(m[6]), "v"(m[7]), "v"(x.x),
+              "v"(x.y), "v"(x.z), "v"(x.w), "n"(LA), "n"(LA + 1));
+    else
+        asm(QG_SEG8H_TEXT ""
+            : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+            : "v"(m[0]), "v"(m[1]), "v"(m[2]), "v"(m[3]), "v"(m[4]), "v"(m[5]), "v"(m[6]), "v"(m[7]), "v"(x.x),
+              "v"(x.y), "v"(x.z), "v"(x.w), "n"(LA), "n"(LA + 1));
+}
+
+// The biased bytes of a quant segment, masked in place: per dword, bytes 0, 2
+// then bytes 1, 3, each as two fp16 subnormals.
+QG_DEV void seg8h_masks(uint32_t (&m)[8], const uint4 q) {
+    const uint32_t w[4] = {q.x ^ 0x80808080u, q.y ^ 0x80808080u, q.z ^ 0x80808080u, q.w ^ 0x80808080u};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        m[2 * d] = w[d] & 0x00ff00ffu;
+        m[2 * d + 1] = (w[d] >> 8) & 0x00ff00ffu;
+    }
+}
+
+template <int NC>
+QG_DEV void load_half_d(VdIn<NC>& d, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t xr, uint32_t vrow, int rt,
+                        uint32_t vx, uint32_t vd, const VdProb& P, int u) {
+    const int mb = u >> 1, h = u & 1;
+    const uint32_t ox = vx + 256u * (uint32_t)u, od = vd + 16u * (uint32_t)u;
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const qg_u4v a = __builtin_amdgcn_raw_buffer_load_b128(xr, ox, n * P.xpb, 0);
+        d.xp[n] = make_uint4(a.x, a.y, a.z, a.w);
+        d.xs[n] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xr, od, P.xs_off + n * P.xsb, 0));
+    }
+    const uint32_t vs = vrow + (uint32_t)mb * 17u * 16u * (uint32_t)rt;
+    const qg_u4v sv = __builtin_amdgcn_raw_buffer_load_b128(wr, vs, 0, 0);  // scales: a cached load
+    d.s[0] = make_uint4(sv.x, sv.y, sv.z, sv.w);
+    const uint32_t vq = vs + (uint32_t)(8 * h) * 16u * (uint32_t)rt;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const qg_u4v v = __builtin_amdgcn_raw_buffer_load_b128(wr, vq, (1 + j) * 16 * rt, kQgNonTemporal);
+        d.s[1 + j] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+}
+
+template <int NC>
+QG_DEV void half_dot_d(float (&acc)[NC], const VdIn<NC>& d, int h, bool live) {
+    const uint32_t dw0 = h ? d.s[0].z : d.s[0].x;
+    const uint32_t dw1 = h ? d.s[0].w : d.s[0].y;
+    // a clamped re-read (live false) is scaled by zero
+    const float dk[4] = {live ? qg_half_lo(dw0) : 0.f, live ? qg_half_hi(dw0) : 0.f, live ? qg_half_lo(dw1) : 0.f,
+                         live ? qg_half_hi(dw1) : 0.f};
+    constexpr float two24 = 16777216.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t m0[8], m1[8];
+        seg8h_masks(m0, d.s[1 + 2 * k]);
+        seg8h_masks(m1, d.s[2 + 2 * k]);
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            float a[4] = {0.f, 0.f, 0.f, 0.f};
+            switch (k) {
+                case 0: seg8h_dot<0, false>(a, m0, d.xp[n]); seg8h_dot<2, true>(a, m1, d.xp[n]); break;
+                case 1: seg8h_dot<4, false>(a, m0, d.xp[n]); seg8h_dot<6, true>(a, m1, d.xp[n]); break;
+                case 2: seg8h_dot<8, false>(a, m0, d.xp[n]); seg8h_dot<10, true>(a, m1, d.xp[n]); break;
+                default: seg8h_dot<12, false>(a, m0, d.xp[n]); seg8h_dot<14, true>(a, m1, d.xp[n]); break;
+            }
+            const float S = (a[0] + a[1]) + (a[2] + a[3]);
+            float X;
+            switch (k) {
+                case 0: X = qg_bcast<0>(d.xs[n]); break;
+                case 1: X = qg_bcast<1>(d.xs[n]); break;
+                case 2: X = qg_bcast<2>(d.xs[n]); break;
+                default: X = qg_bcast<3>(d.xs[n]); break;
+            }
+            acc[n] = fmaf(dk[k], fmaf(two24, S, -128.f * X), acc[n]);
+        }
+    }
+}
+
+template <int NC, int W>
+__global__ __launch_bounds__(64 * W) void lmhead_verify_dot_kernel(VdProb P) {
+    const int tile = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i = lane & 15;
+    const int kg = 4 * wave + (lane >> 4);
+    constexpr int G = 4 * W;
+    const int rt = min(T, P.M - tile * T);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(P.w + (size_t)tile * T * P.nmb * 272), (short)0, rt * P.nmb * 272, kQgRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)P.xp, (short)0, P.xs_off + P.N * P.xsb, kQgRawBufferFlags);
+    const uint32_t vrow = 16u * (uint32_t)min(i, rt - 1);
+    // the launch instantiates NC = N: every column is in range
+    const uint32_t vx = (uint32_t)(16 * i), vd = (uint32_t)(4 * (i & 3));
+    const int nu = 2 * P.nmb;
+    float acc[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) acc[n] = 0.f;
+    const int niter = (nu + G - 1) / G;
+    VdIn<NC> b0, b1;
+    load_half_d<NC>(b0, wr, xr, vrow, rt, vx, vd, P, min(kg, nu - 1));
+    int it = 0;
+    for (; it + 2 <= niter; it += 2) {
+        const int u = kg + G * it;
+        load_half_d<NC>(b1, wr, xr, vrow, rt, vx, vd, P, min(u + G, nu - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        half_dot_d<NC>(acc, b0, u & 1, u < nu);
+        load_half_d<NC>(b0, wr, xr, vrow, rt, vx, vd, P, min(u + 2 * G, nu - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        half_dot_d<NC>(acc, b1, (u + G) & 1, u + G < nu);
+    }
+    if (it < niter) {
+        const int u = kg + G * it;
+        half_dot_d<NC>(acc, b0, u & 1, u < nu);
+    }
+#pragma unroll
+    for (int n = 0; n < NC; ++n) acc[n] = qg_sum_rows4(acc[n]);
+    if constexpr (W > 1) {
+        __shared__ float red[W][NC][T];
+#pragma unroll
+        for (int n = 0; n < NC; ++n)
+            if (lane < T) red[wave][n][lane] = acc[n];
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            float v = red[0][n][i];
+#pragma unroll
+            for (int w = 1; w < W; ++w) v += red[w][n][i];
+            acc[n] = v;
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        float v = acc[n];
+        int idx = tile * T + i;
+        if (i >= rt || !(v == v)) {
+            v = -__builtin_huge_valf();
+            idx = INT_MAX;
+        }
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(v, off, 64);
+            const int oi = __shfl_xor(idx, off, 64);
+            if (va_better(ov, oi, v, idx)) {
+                v = ov;
+                idx = oi;
+            }
+        }
+        if (lane == 0) P.partials[(int64_t)n * P.tiles + tile] = make_float2(v, __builtin_bit_cast(float, idx));
+    }
+}
+
+constexpr int kVdMaxCols = 6;  // above six columns the matrix-core form is faster
+
+// Workspace of the vector-ALU form past the partials: 2K bytes of pairs and K/8
+// bytes of block sums per column.
+size_t vd_extra_bytes(int64_t K, int64_t N) { return qg::align_up((size_t)N * (size_t)(2 * K + K / 8), 256); }
+
+template <int NC>
+void vd_launch(const VdProb& P, int W, hipStream_t s) {
+    const dim3 grid((unsigned)P.tiles);
+    if (W == 4)
+        hipLaunchKernelGGL((lmhead_verify_dot_kernel<NC, 4>), grid, dim3(256), 0, s, P);
+    else
+        hipLaunchKernelGGL((lmhead_verify_dot_kernel<NC, 1>), grid, dim3(64), 0, s, P);
 }
 
 // ---------------------------------------------------------------------------
@@ -504,7 +742,7 @@ extern "C" {
 
 size_t lmhead_argmax_verify_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     if (M < 1 || M > INT32_MAX || K < 256 || K % 256 || N < 1 || N > QG_SMALLN_MAX) return 0;
-    return va_ws_bytes(M, N);
+    return va_ws_bytes(M, N) + (N <= kVdMaxCols ? vd_extra_bytes(K, N) : 0);
 }
 
 int lmhead_argmax_verify(const void* w, const float* X, int64_t ldx, int64_t M, int64_t K, int64_t N, void* ws,
@@ -515,12 +753,56 @@ int lmhead_argmax_verify(const void* w, const float* X, int64_t ldx, int64_t M, 
     if (!out_index) return qg::fail(QG_ERR_NULL, "out_index is NULL");
     if ((reinterpret_cast<uintptr_t>(out_index) & 3) || (reinterpret_cast<uintptr_t>(out_value) & 3))
         return qg::fail(QG_ERR_ALIGN, "outputs must be 4-byte aligned");
-    const size_t need = va_ws_bytes(M, N);
+    const size_t need = lmhead_argmax_verify_workspace_bytes(M, K, N);
     if (!ws) return qg::fail(QG_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
     if (ws_bytes < need) return qg::fail(QG_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws_bytes);
     if (!qg::aligned16(ws)) return qg::fail(QG_ERR_ALIGN, "workspace not 16-byte aligned");
     st = qg::check_device();
     if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const char* impl = getenv("QG_VA_IMPL");
+    const bool mfma = N > kVdMaxCols || (impl && std::strcmp(impl, "mfma") == 0);
+    if (!mfma) {
+        // vector-ALU form: fp16 pairs and block sums, then one wavefront per tile on
+        // grids that fill the chip, four that split K otherwise (152064 x 3584, us:
+        // N = 1 95.5, 2 97.2, 4 111.3, 5 123.2, 6 133.7, 8 166.4 against 144.1, 135.9,
+        // 138.6, 139.7, 141.3, 142.9 for the matrix-core form)
+        const size_t pb = va_ws_bytes(M, N);
+        uint8_t* xp = (uint8_t*)ws + pb;
+        const int g8 = (int)(K / 8);
+        hipLaunchKernelGGL(lmhead_verify_prep_kernel, dim3((unsigned)qg::ceil_div((int64_t)N * g8, 256)), dim3(256),
+                           0, s, X, ldx, (int)K, (int)N, (uint4*)xp, (float*)(xp + (size_t)N * 2 * K));
+        st = qg::launch_status("lmhead_argmax_verify (prep)");
+        if (st) return st;
+        VdProb D{};
+        D.w = (const uint8_t*)w;
+        D.xp = xp;
+        D.partials = (float2*)ws;
+        D.xpb = (int32_t)(2 * K);
+        D.xs_off = (int32_t)(N * 2 * K);
+        D.xsb = (int32_t)(K / 8);
+        D.M = (int32_t)M;
+        D.nmb = (int32_t)(K / 256);
+        D.N = (int32_t)N;
+        D.tiles = (int32_t)qg::ceil_div(M, T);
+        int W = D.tiles >= 1024 ? 1 : 4;
+        int ew = 0, eu = 0;
+        if (qg::env_pair("QG_VD_CFG", &ew, &eu) && (ew == 1 || ew == 4)) W = ew;
+        switch (N) {
+            case 1: vd_launch<1>(D, W, s); break;
+            case 2: vd_launch<2>(D, W, s); break;
+            case 3: vd_launch<3>(D, W, s); break;
+            case 4: vd_launch<4>(D, W, s); break;
+            case 5: vd_launch<5>(D, W, s); break;
+            default: vd_launch<6>(D, W, s); break;
+        }
+        st = qg::launch_status("lmhead_argmax_verify (tiles)");
+        if (st) return st;
+        const int threads = (int)std::min<int64_t>(1024, std::max<int64_t>(64, qg::ceil_div(D.tiles, 8 * 64) * 64));
+        hipLaunchKernelGGL(lmhead_verify_reduce_kernel, dim3((unsigned)N), dim3(threads), 0, s, D.partials, D.tiles,
+                           out_index, out_value, (uint4*)xp, (int)(N * (2 * K + K / 8) / 16));
+        return qg::launch_status("lmhead_argmax_verify (reduce)");
+    }
     VaProb P{};
     P.w = (const uint8_t*)w;
     P.X = X;
@@ -546,7 +828,6 @@ int lmhead_argmax_verify(const void* w, const float* X, int64_t ldx, int64_t M, 
         if (ew == 4 || ew == 8) W = ew;
         if (et == 1 || et == 2 || (et == 4 && N <= 16)) TW = et;  // four tiles of two column blocks spill
     }
-    hipStream_t s = (hipStream_t)stream;
     const int key = 10 * (N > 16 ? 2 : 1) + TW;
     switch (key) {
         case 11: va_launch<1, 1>(P, W, s); break;
@@ -559,7 +840,7 @@ int lmhead_argmax_verify(const void* w, const float* X, int64_t ldx, int64_t M, 
     if (st) return st;
     const int threads = (int)std::min<int64_t>(1024, std::max<int64_t>(64, qg::ceil_div(P.tiles, 8 * 64) * 64));
     hipLaunchKernelGGL(lmhead_verify_reduce_kernel, dim3((unsigned)N), dim3(threads), 0, s, P.partials, P.tiles,
-                       out_index, out_value);
+                       out_index, out_value, (uint4*)nullptr, 0);
     return qg::launch_status("lmhead_argmax_verify (reduce)");
 }
 
@@ -621,7 +902,7 @@ int lmhead_argmax_verify_q8_1(const void* w, const void* xq, int64_t M, int64_t 
     if (st) return st;
     const int threads = (int)std::min<int64_t>(1024, std::max<int64_t>(64, qg::ceil_div(P.tiles, 8 * 64) * 64));
     hipLaunchKernelGGL(lmhead_verify_reduce_kernel, dim3((unsigned)N), dim3(threads), 0, s, P.partials, P.tiles,
-                       out_index, out_value);
+                       out_index, out_value, (uint4*)nullptr, 0);
     return qg::launch_status("lmhead_argmax_verify_q8_1 (reduce)");
 }
 

@@ -136,9 +136,11 @@ def test_verify_validation(L):
     assert f(C, A, 500, 64, 512, 5, B, 1 << 20, out, None, None) == ESHAPE   # ldx < K
     assert f(C, A, 512, 64, 512, 5, None, 0, out, None, None) == EWS
     assert f(C, A, 512, 64, 512, 5, B, 1 << 20, None, None, None) == ENULL
-    # 4 tiles x 5 columns x 8 bytes, rounded up to 256
-    assert L.lmhead_argmax_verify_workspace_bytes(64, 512, 5) == 256
-    assert L.lmhead_argmax_verify_workspace_bytes(152064, 3584, 5) == 152064 // 16 * 5 * 8
+    # 4 tiles x 5 columns x 8 bytes, rounded up to 256; for N <= 6 also the fp16
+    # pairs (2K bytes) and block sums (K/8 bytes) of every column, rounded up to 256
+    assert L.lmhead_argmax_verify_workspace_bytes(64, 512, 5) == 256 + 5632
+    assert L.lmhead_argmax_verify_workspace_bytes(152064, 3584, 5) == 152064 // 16 * 5 * 8 + 38144
+    assert L.lmhead_argmax_verify_workspace_bytes(152064, 3584, 7) == 152064 // 16 * 7 * 8
 
 
 def test_q6k_sizes_and_validation(L):

@@ -215,10 +215,54 @@ def test_verify_vocab_152064_n5():
 @pytest.mark.parametrize("cfg", ["8,1", "8,2", "8,4", "4,2", "4,4"])
 @pytest.mark.parametrize("N", [5, 20])
 def test_verify_launch_shapes(cfg, N, monkeypatch):
-    # every (wavefronts, tiles per workgroup) shape, with a tile count that is not a
-    # multiple of the tiles per workgroup and a ragged last tile
+    # every (wavefronts, tiles per workgroup) shape of the matrix-core form, with a
+    # tile count that is not a multiple of the tiles per workgroup and a ragged last
+    # tile
+    monkeypatch.setenv("QG_VA_IMPL", "mfma")
     monkeypatch.setenv("QG_VA_CFG", cfg)
     M, K = 1000, 1024
     W = workloads.q8_0_blocks(M, K, key=(25, M))
     X = workloads.x_columns(K, N, key=(25, N))
     check_verify(W, M, K, X, f"shape {cfg}")
+
+
+@pytest.mark.parametrize("cfg", ["1,0", "4,0"])
+@pytest.mark.parametrize("N", [1, 3, 6])
+def test_verify_vector_alu_form_shapes(cfg, N, monkeypatch):
+    # the vector-ALU form (N <= 6): one and four wavefronts per tile, half
+    # macro-block counts that do not divide among the K-groups (K = 2816: 22
+    # halves), a ragged last tile; the workspace (partials, fp16 pairs and block
+    # sums) is left zero
+    monkeypatch.setenv("QG_VD_CFG", cfg)
+    M, K = 1000, 2816
+    W = workloads.q8_0_blocks(M, K, key=(26, M))
+    X = workloads.x_columns(K, N, key=(26, N))
+    ws = qg.Workspace(DEV)
+    check_verify(W, M, K, X, f"vector-ALU form {cfg}", ws=ws)
+    assert int(ws.buf.count_nonzero()) == 0
+
+
+def test_verify_forms_agree_on_ldx_padding():
+    # X with ldx > K (padding columns of NaN never read) through both forms
+    M, K, N, ldx = 500, 1024, 4, 1100
+    W = workloads.q8_0_blocks(M, K, key=(27,))
+    X = workloads.x_columns(K, N, key=(27,))
+    Xp = np.full((N, ldx), np.nan, np.float32)
+    Xp[:, :K] = X
+    wp = packed_q8_0(W, M, K)
+    case("lmhead_argmax_verify ldx padding, both forms")
+    i_dot, v_dot = qg.lmhead_argmax_verify(wp, to_dev(Xp), M, K)
+    import os
+    os.environ["QG_VA_IMPL"] = "mfma"
+    try:
+        i_mma, v_mma = qg.lmhead_argmax_verify(wp, to_dev(Xp), M, K)
+    finally:
+        del os.environ["QG_VA_IMPL"]
+    torch.cuda.synchronize()
+    for n in range(N):
+        yr, ar = oracle.gemv_q8_0(W, M, K, X[n])
+        tol = oracle.tolerance(ar)
+        for gi, gv in ((int(i_dot[n]), float(v_dot[n])), (int(i_mma[n]), float(v_mma[n]))):
+            ri = oracle.argmax(yr)
+            assert yr[gi] >= yr[ri] - tol[gi] - tol[ri], n
+            assert abs(gv - yr[gi]) <= tol[gi], n
