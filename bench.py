@@ -261,7 +261,7 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     """Each of the other hot-path kernels a few times, every call on its own weight
     copy, in this order: 4096x4096 Q4_K GEMV (3 calls), Q8_0 11008x4096 and
     4096x11008 (3 each), LM head + argmax 152064x3584 (2), the same head verifying 5
-    columns (2) and 5 int8 columns (2), top-20 + sampling on that head (2), small-N N=5 then N=32 over
+    columns (2, vector-ALU form) and 5 int8 columns (2), top-20 + sampling on that head (2), small-N N=5 then N=32 over
     the layers' stages (one grouped launch per stage), Q6_K 3584x18944 (3) and
     152064x3584 (2), int8-activation Q4_K 4096x4096 (3, after one quantization)."""
     M, K = 4096, 4096
