@@ -318,8 +318,9 @@ void va_launch(const VaProb& P, int W, hipStream_t s) {
 // once, already in the pair order the masked words need ((x0, x2), (x1, x3),
 // (x4, x6), (x5, x7) per 8 activations), and sums every 32-weight block's rounded
 // activations in fp32 (X, which removes the bias exactly: logit += d (2^24 S' -
-// 128 X)); both go to the workspace after the partials. Per column and block:
-// 16 v_dot2c_f32_f16 with DPP row broadcasts, 3 additions and 2 fma.
+// 128 X)), stored as -128 * 2^-24 * X so that it can seed a product accumulator;
+// both go to the workspace after the partials. Per column and block: 16
+// v_dot2c_f32_f16 with DPP row broadcasts, 3 additions and 1 fma.
 
 __global__ __launch_bounds__(256) void lmhead_verify_prep_kernel(const float* __restrict__ X, int64_t ldx, int K,
                                                                  int N, uint4* __restrict__ pairs,
@@ -336,7 +337,8 @@ __global__ __launch_bounds__(256) void lmhead_verify_prep_kernel(const float* __
               ((qg_half_lo(p.p[2]) + qg_half_hi(p.p[2])) + (qg_half_lo(p.p[3]) + qg_half_hi(p.p[3])));
     v += __shfl_xor(v, 1, 64);
     v += __shfl_xor(v, 2, 64);
-    if ((g & 3) == 0) xsum[(int64_t)n * (K / 32) + g / 4] = v;
+    // stored as the bias term in the products' scale: -128 * 2^-24 * X
+    if ((g & 3) == 0) xsum[(int64_t)n * (K / 32) + g / 4] = v * -7.62939453125e-06f;
 }
 
 struct VdProb {
@@ -350,7 +352,7 @@ template <int NC>
 struct VdIn {
     uint4 s[9];    // scale segment, then the 8 quant segments of the half macro-block
     uint4 xp[NC];  // activations 8i .. 8i + 7 of the half as fp16 pairs (i = lane % 16), per column
-    float xs[NC];  // rounded-activation sum of block i % 4 of the half, per column
+    float xs[NC];  // bias term -128 * 2^-24 * X of block i % 4 of the half, per column
 };
 
 // One quant segment of one column: masked words m (2d: bytes 0, 2 of dword d;
@@ -419,10 +421,10 @@ template <int NC>
 QG_DEV void half_dot_d(float (&acc)[NC], const VdIn<NC>& d, int h, bool live) {
     const uint32_t dw0 = h ? d.s[0].z : d.s[0].x;
     const uint32_t dw1 = h ? d.s[0].w : d.s[0].y;
-    // a clamped re-read (live false) is scaled by zero
-    const float dk[4] = {live ? qg_half_lo(dw0) : 0.f, live ? qg_half_hi(dw0) : 0.f, live ? qg_half_lo(dw1) : 0.f,
-                         live ? qg_half_hi(dw1) : 0.f};
+    // a clamped re-read (live false) is scaled by zero; 2^24 undoes the subnormal scale
     constexpr float two24 = 16777216.0f;
+    const float dk[4] = {live ? two24 * qg_half_lo(dw0) : 0.f, live ? two24 * qg_half_hi(dw0) : 0.f,
+                         live ? two24 * qg_half_lo(dw1) : 0.f, live ? two24 * qg_half_hi(dw1) : 0.f};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         uint32_t m0[8], m1[8];
@@ -430,22 +432,23 @@ QG_DEV void half_dot_d(float (&acc)[NC], const VdIn<NC>& d, int h, bool live) {
         seg8h_masks(m1, d.s[2 + 2 * k]);
 #pragma unroll
         for (int n = 0; n < NC; ++n) {
-            float a[4] = {0.f, 0.f, 0.f, 0.f};
+            // the first accumulator starts at the block's bias term, so the sum is
+            // 2^-24 (S' - 128 * 2^24 X)
+            float a[4];
+            switch (k) {
+                case 0: a[0] = qg_bcast<0>(d.xs[n]); break;
+                case 1: a[0] = qg_bcast<1>(d.xs[n]); break;
+                case 2: a[0] = qg_bcast<2>(d.xs[n]); break;
+                default: a[0] = qg_bcast<3>(d.xs[n]); break;
+            }
+            a[1] = a[2] = a[3] = 0.f;
             switch (k) {
                 case 0: seg8h_dot<0, false>(a, m0, d.xp[n]); seg8h_dot<2, true>(a, m1, d.xp[n]); break;
                 case 1: seg8h_dot<4, false>(a, m0, d.xp[n]); seg8h_dot<6, true>(a, m1, d.xp[n]); break;
                 case 2: seg8h_dot<8, false>(a, m0, d.xp[n]); seg8h_dot<10, true>(a, m1, d.xp[n]); break;
                 default: seg8h_dot<12, false>(a, m0, d.xp[n]); seg8h_dot<14, true>(a, m1, d.xp[n]); break;
             }
-            const float S = (a[0] + a[1]) + (a[2] + a[3]);
-            float X;
-            switch (k) {
-                case 0: X = qg_bcast<0>(d.xs[n]); break;
-                case 1: X = qg_bcast<1>(d.xs[n]); break;
-                case 2: X = qg_bcast<2>(d.xs[n]); break;
-                default: X = qg_bcast<3>(d.xs[n]); break;
-            }
-            acc[n] = fmaf(dk[k], fmaf(two24, S, -128.f * X), acc[n]);
+            acc[n] = fmaf(dk[k], (a[0] + a[1]) + (a[2] + a[3]), acc[n]);
         }
     }
 }
