@@ -385,13 +385,14 @@ QG_DEV void seg8h_dot(float (&a)[4], const uint32_t (&m)[8], const uint4 x) {
 }
 
 // The biased bytes of a quant segment, masked in place: per dword, bytes 0, 2
-// then bytes 1, 3, each as two fp16 subnormals.
+// then bytes 1, 3, each as two fp16 subnormals. One byte permutation each
+// (selector byte 0x0c gives a zero byte): 3 operations per dword.
 QG_DEV void seg8h_masks(uint32_t (&m)[8], const uint4 q) {
     const uint32_t w[4] = {q.x ^ 0x80808080u, q.y ^ 0x80808080u, q.z ^ 0x80808080u, q.w ^ 0x80808080u};
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        m[2 * d] = w[d] & 0x00ff00ffu;
-        m[2 * d + 1] = (w[d] >> 8) & 0x00ff00ffu;
+        m[2 * d] = __builtin_amdgcn_perm(w[d], w[d], 0x0c020c00u);
+        m[2 * d + 1] = __builtin_amdgcn_perm(w[d], w[d], 0x0c030c01u);
     }
 }
 
