@@ -100,3 +100,53 @@ def test_graph_replays_match_eager():
 
 def snapshot_targets(stage, oi, ov, tk, lg, Y5, Yd, Y32, xq, y8):
     return [p[2] for p in stage] + [oi, ov, tk.index, tk.logit, tk.logprob, tk.lse, tk.token, lg, Y5, Yd, Y32, xq, y8]
+
+
+def test_lmhead_verify_forms_in_a_graph():
+    # both verification forms on fp32 columns (vector-ALU N = 5, matrix-core N = 9)
+    # and the int8-column form, captured once and replayed three times with eager
+    # work in between; every replay must equal the eager result, and the shared
+    # workspace (cleared by the kernels themselves, no memset nodes) stays zero
+    import numpy as np
+    import workloads
+    from tests.gpu_helpers import DEV, case, packed_q8_0
+    import quantized_gemv_argmax_amd as qg
+    M, K = 5000, 1536
+    W = workloads.q8_0_blocks(M, K, key=(70,))
+    wp = packed_q8_0(W, M, K)
+    X5 = torch.from_numpy(workloads.x_columns(K, 5, key=(70, 5))).to(DEV)
+    X9 = torch.from_numpy(workloads.x_columns(K, 9, key=(70, 9))).to(DEV)
+    xq = qg.quantize_q8_1_columns(X5)
+    ws = qg.Workspace(DEV)
+    outs = [(torch.empty(n, dtype=torch.int32, device=DEV), torch.empty(n, device=DEV)) for n in (5, 9, 5)]
+
+    def run():
+        qg.lmhead_argmax_verify(wp, X5, M, K, out_index=outs[0][0], out_value=outs[0][1], ws=ws)
+        qg.lmhead_argmax_verify(wp, X9, M, K, out_index=outs[1][0], out_value=outs[1][1], ws=ws)
+        qg.lmhead_argmax_verify_q8_1(wp, xq, M, K, 5, out_index=outs[2][0], out_value=outs[2][1], ws=ws)
+
+    case("LM-head verification forms in a HIP graph")
+    run()
+    torch.cuda.synchronize()
+    ref = [(i.clone(), v.clone()) for i, v in outs]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, v in outs:
+            i.fill_(-7)
+            v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (i, v), (ri, rv) in zip(outs, ref):
+            assert torch.equal(i, ri) and torch.equal(v, rv), rep
+        assert int(ws.buf.count_nonzero()) == 0, rep
+        run()  # eager work between replays
+        torch.cuda.synchronize()
+    assert np.all(ref[0][0].cpu().numpy() >= 0)
