@@ -154,7 +154,7 @@ def main():
 
     def step():
         for st in stages:
-            qg.qgemv_q4k_batch(st, ws=ws)
+            qg.qgemv_q4k_batch(st)
 
     for _ in range(max(1, args.warmup)):
         step()
@@ -197,7 +197,7 @@ def main():
 
         def stage_fn(sts=sts):
             for st in sts:
-                qg.qgemv_q4k_batch(st, ws=ws)
+                qg.qgemv_q4k_batch(st)
         us = graph_ms(torch, stage_fn, reps=max(10, args.steps // 2)) * 1e3 / len(sts)
         per_stage[name] = {"avg_us": round(us, 3), "bytes": int(nb), "GBps": round(nb / (us * 1e-6) / 1e9, 1)}
     log(f"dominant kernel: {achieved:.1f} GB/s, {avg_launch_ms * 1e3:.3f} us per launch; per stage {per_stage}")
@@ -270,14 +270,14 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     x = torch.from_numpy(wl.x_vector(K, key=(1, 0))).to(dev)
     y = torch.empty(M, device=dev)
     for c in [wp] + [wp.clone() for _ in range(2)]:
-        qg.qgemv_q4k(c, x, M, K, y=y, ws=ws)
+        qg.qgemv_q4k(c, x, M, K, y=y)
     for (M, K) in [(11008, 4096), (4096, 11008)]:
         W = wl.q8_0_blocks(M, K, key=(2, M))
         wp = qg.pack_q8_0(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
         x = torch.from_numpy(wl.x_vector(K, key=(2, M))).to(dev)
         y = torch.empty(M, device=dev)
         for c in [wp] + [wp.clone() for _ in range(2)]:
-            qg.qgemv_q8_0(c, x, M, K, y=y, ws=ws)
+            qg.qgemv_q8_0(c, x, M, K, y=y)
     M, K = wl.VOCAB, wl.HIDDEN
     W = wl.q8_0_blocks(M, K, key=(4, 0))
     wp = qg.pack_q8_0(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
@@ -304,7 +304,7 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
                     wp_, _, _, M_, K_ = layers[L][i]
                     X_ = torch.from_numpy(wl.x_columns(K_, N, key=(5, L, i, N))).to(dev)
                     grp.append((wp_, X_, torch.empty((N, (M_ + 3) // 4 * 4), device=dev), M_, K_))
-                qg.qgemm_q4k_smalln_batch(grp, ws=ws)
+                qg.qgemm_q4k_smalln_batch(grp)
     for L in range(n_layers):  # N = 5 on int8 activations
         for st in wl.LAYER_STAGES:
             grp = []
@@ -312,7 +312,7 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
                 wp_, _, _, M_, K_ = layers[L][i]
                 X_ = torch.from_numpy(wl.x_columns(K_, 5, key=(5, L, i, 5))).to(dev)
                 grp.append((wp_, qg.quantize_q8_1_columns(X_), torch.empty((5, (M_ + 3) // 4 * 4), device=dev), M_, K_))
-            qg.qgemm_q4k_q8_1_smalln_batch(grp, ws=ws)
+            qg.qgemm_q4k_q8_1_smalln_batch(grp)
     for (M, K), reps in [((wl.HIDDEN, wl.FFN), 3), ((wl.VOCAB, wl.HIDDEN), 2)]:
         W = wl.q6k_blocks(M, K, key=(6, M))
         wp = qg.pack_q6k(torch.from_numpy(W.reshape(-1)).to(dev), M, K)
@@ -320,7 +320,7 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
         x = torch.from_numpy(wl.x_vector(K, key=(6, M))).to(dev)
         y = torch.empty(M, device=dev)
         for c in [wp] + [wp.clone() for _ in range(reps - 1)]:
-            qg.qgemv_q6k(c, x, M, K, y=y, ws=ws)
+            qg.qgemv_q6k(c, x, M, K, y=y)
         del wp
     M, K = 4096, 4096
     W = wl.q4k_blocks(M, K, key=(1, 0))
@@ -329,7 +329,7 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     xq = qg.quantize_q8_1(x)
     y = torch.empty(M, device=dev)
     for c in [wp] + [wp.clone() for _ in range(2)]:
-        qg.qgemv_q4k_q8_1(c, xq, M, K, y=y, ws=ws)
+        qg.qgemv_q4k_q8_1(c, xq, M, K, y=y)
     torch.cuda.synchronize()
     log("counter rows done")
 
@@ -356,7 +356,7 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     copies = rotated(wp, R)
     x = torch.from_numpy(wl.x_vector(K, key=(1, 0))).to(dev)
     y = torch.empty(M, device=dev)
-    ms = graph_ms(torch, lambda: [qg.qgemv_q4k(c, x, M, K, y=y, ws=ws) for c in copies], 20) / R
+    ms = graph_ms(torch, lambda: [qg.qgemv_q4k(c, x, M, K, y=y) for c in copies], 20) / R
     b = W.size + 4 * (M + K)
     rows["q4k_gemv_4096x4096"] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
                                   "bytes": b, "copies_rotated": R}
@@ -371,7 +371,7 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
         copies = rotated(wp, R)
         x = torch.from_numpy(wl.x_vector(K, key=(2, M))).to(dev)
         y = torch.empty(M, device=dev)
-        ms = graph_ms(torch, lambda: [qg.qgemv_q8_0(c, x, M, K, y=y, ws=ws) for c in copies], 20) / R
+        ms = graph_ms(torch, lambda: [qg.qgemv_q8_0(c, x, M, K, y=y) for c in copies], 20) / R
         b = W.size + 4 * (M + K)
         rows[f"q8_0_gemv_{M}x{K}"] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
                                       "bytes": b, "copies_rotated": R}
@@ -388,7 +388,7 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
         copies = rotated(wp, R)
         x = torch.from_numpy(wl.x_vector(K, key=(6, M))).to(dev)
         y = torch.empty(M, device=dev)
-        ms = graph_ms(torch, lambda: [qg.qgemv_q6k(c, x, M, K, y=y, ws=ws) for c in copies], 20) / R
+        ms = graph_ms(torch, lambda: [qg.qgemv_q6k(c, x, M, K, y=y) for c in copies], 20) / R
         b = wp.numel() + 4 * (M + K)
         rows[f"q6k_gemv_{M}x{K}"] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
                                      "bytes": b, "copies_rotated": R}
@@ -409,7 +409,7 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
     b = wp.numel() + 4 * K + 8 * (-(-M // 16)) * 2 + 8  # weights, x, partials written and read, result
     # unfused comparison: Q8_0 GEMV writing the 608,256-byte logit vector + torch argmax
     logits = torch.empty(M, device=dev)
-    ms_unfused = graph_ms(torch, lambda: [(qg.qgemv_q8_0(c, x, M, K, y=logits, ws=ws), torch.argmax(logits))
+    ms_unfused = graph_ms(torch, lambda: [(qg.qgemv_q8_0(c, x, M, K, y=logits), torch.argmax(logits))
                                           for c in copies], 20) / 2
     h = torch.empty(M, dtype=torch.float32, pin_memory=True)
     torch.cuda.synchronize()
@@ -486,7 +486,7 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
 
         def vstep(sts=sstages):
             for grp in sts:
-                qg.qgemm_q4k_smalln_batch(grp, ws=ws)
+                qg.qgemm_q4k_smalln_batch(grp)
 
         ms = graph_ms(torch, vstep, 5)
         flat = [m for grp in sstages for m in grp]
@@ -519,7 +519,7 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
 
     def ivstep(sts=qv):
         for grp in sts:
-            qg.qgemm_q4k_q8_1_smalln_batch(grp, ws=ws)
+            qg.qgemm_q4k_q8_1_smalln_batch(grp)
 
     ms = graph_ms(torch, ivstep, 5)
     flat = [m for grp in qv for m in grp]
@@ -546,7 +546,7 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
 
     def qstep(sts=qstages):
         for grp in sts:
-            qg.qgemv_q4k_q8_1_batch(grp, ws=ws)
+            qg.qgemv_q4k_q8_1_batch(grp)
 
     ms = graph_ms(torch, qstep, 20)
     wb = sum(m[0].numel() for grp in qstages for m in grp)

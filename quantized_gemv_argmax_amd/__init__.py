@@ -44,6 +44,17 @@ class _GemmQ81Problem(ctypes.Structure):
                 ("ldy", ctypes.c_int64), ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64)]
 
 
+class _LaunchOverride(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("gemv_waves", "smalln_form", "smalln_waves", "smalln_tiles",
+                                            "smalln_depth", "verify_form", "verify_waves", "verify_tiles")]
+
+
+# kernel forms a launch override can force (include/qgemv.h)
+FORM_AUTO = 0
+FORM_SMALLN_REGS, FORM_SMALLN_LDS, FORM_SMALLN_LDS1, FORM_SMALLN_DOT = 1, 2, 3, 4
+FORM_VERIFY_MFMA, FORM_VERIFY_DOT = 1, 2
+
+
 class _TopkOut(ctypes.Structure):
     _fields_ = [("index", ctypes.c_void_p), ("logit", ctypes.c_void_p), ("logprob", ctypes.c_void_p),
                 ("lse", ctypes.c_void_p), ("token", ctypes.c_void_p)]
@@ -67,28 +78,21 @@ _SIGS = {
     "qg_pack_q8_0": (_I, [_P, _P, _I64, _I64, _P]),
     "qg_pack_q6k": (_I, [_P, _P, _I64, _I64, _P]),
     "qg_workspace_clear": (_I, [_P, _SZ, _P]),
-    "qgemv_q4k_workspace_bytes": (_SZ, [_I64, _I64]),
-    "qgemv_q4k": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
-    "qgemv_q4k_batch_workspace_bytes": (_SZ, [ctypes.POINTER(_Problem), _I]),
-    "qgemv_q4k_batch": (_I, [ctypes.POINTER(_Problem), _I, _P, _SZ, _P]),
-    "qgemv_q8_0_workspace_bytes": (_SZ, [_I64, _I64]),
-    "qgemv_q8_0": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
+    "qgemv_q4k": (_I, [_P, _P, _P, _I64, _I64, _P]),
+    "qgemv_q4k_batch": (_I, [ctypes.POINTER(_Problem), _I, _P]),
+    "qgemv_q8_0": (_I, [_P, _P, _P, _I64, _I64, _P]),
     "qg_q8_1_bytes": (_SZ, [_I64]),
     "qg_quantize_q8_1": (_I, [_P, _I64, _P, _P]),
-    "qgemv_q4k_q8_1_workspace_bytes": (_SZ, [_I64, _I64]),
-    "qgemv_q4k_q8_1": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
-    "qgemv_q4k_q8_1_batch_workspace_bytes": (_SZ, [ctypes.POINTER(_Problem), _I]),
-    "qgemv_q4k_q8_1_batch": (_I, [ctypes.POINTER(_Problem), _I, _P, _SZ, _P]),
-    "qgemm_q4k_q8_1_smalln_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
-    "qgemm_q4k_q8_1_smalln": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
-    "qgemm_q4k_q8_1_smalln_batch_workspace_bytes": (_SZ, [ctypes.POINTER(_GemmQ81Problem), _I]),
-    "qgemm_q4k_q8_1_smalln_batch": (_I, [ctypes.POINTER(_GemmQ81Problem), _I, _P, _SZ, _P]),
-    "qgemv_q6k_workspace_bytes": (_SZ, [_I64, _I64]),
-    "qgemv_q6k": (_I, [_P, _P, _P, _I64, _I64, _P, _SZ, _P]),
-    "qgemm_q4k_smalln_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
-    "qgemm_q4k_smalln": (_I, [_P, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
-    "qgemm_q4k_smalln_batch_workspace_bytes": (_SZ, [ctypes.POINTER(_GemmProblem), _I]),
-    "qgemm_q4k_smalln_batch": (_I, [ctypes.POINTER(_GemmProblem), _I, _P, _SZ, _P]),
+    "qg_quantize_q8_1_columns": (_I, [_P, _I64, _I64, _I64, _P, _P]),
+    "qgemv_q4k_q8_1": (_I, [_P, _P, _P, _I64, _I64, _P]),
+    "qgemv_q4k_q8_1_batch": (_I, [ctypes.POINTER(_Problem), _I, _P]),
+    "qgemm_q4k_q8_1_smalln": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    "qgemm_q4k_q8_1_smalln_batch": (_I, [ctypes.POINTER(_GemmQ81Problem), _I, _P]),
+    "qgemv_q6k": (_I, [_P, _P, _P, _I64, _I64, _P]),
+    "qgemm_q4k_smalln": (_I, [_P, _P, _I64, _P, _I64, _I64, _I64, _I64, _P]),
+    "qgemm_q4k_smalln_batch": (_I, [ctypes.POINTER(_GemmProblem), _I, _P]),
+    "qg_set_launch_override": (_I, [ctypes.c_void_p]),
+    "qg_get_launch_override": (_I, [ctypes.c_void_p]),
     "lmhead_argmax_verify_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "lmhead_argmax_verify": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P, _P, _P]),
     "lmhead_argmax_verify_q8_1_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
@@ -239,19 +243,51 @@ def pack_q6k(canonical: torch.Tensor, M: int, K: int, out: torch.Tensor | None =
     return out
 
 
+# ------------------------------------------------------------------ launch override
+class launch_override:
+    """Context manager (or plain call through .set()) that forces kernel forms or
+    launch shapes on this host thread for tests and measurements, through
+    qg_set_launch_override; fields not given keep the automatic choice. Example:
+    `with qg.launch_override(smalln_form=qg.FORM_SMALLN_LDS, smalln_tiles=2): ...`"""
+
+    def __init__(self, **fields):
+        self.o = _LaunchOverride()
+        for k, v in fields.items():
+            if k not in dict(_LaunchOverride._fields_):
+                raise TypeError(f"unknown launch override field {k!r}")
+            setattr(self.o, k, int(v))
+        self._prev = None
+
+    def set(self):
+        _check("qg_set_launch_override", lib().qg_set_launch_override(ctypes.byref(self.o)))
+
+    def __enter__(self):
+        self._prev = _LaunchOverride()
+        _check("qg_get_launch_override", lib().qg_get_launch_override(ctypes.byref(self._prev)))
+        self.set()
+        return self
+
+    def __exit__(self, *exc):
+        _check("qg_set_launch_override", lib().qg_set_launch_override(ctypes.byref(self._prev)))
+        return False
+
+
+def get_launch_override() -> dict:
+    o = _LaunchOverride()
+    _check("qg_get_launch_override", lib().qg_get_launch_override(ctypes.byref(o)))
+    return {n: getattr(o, n) for n, _ in _LaunchOverride._fields_}
+
+
 # ------------------------------------------------------------------ products
-def qgemv_q4k(w: torch.Tensor, x: torch.Tensor, M: int, K: int, y: torch.Tensor | None = None,
-              ws: Workspace | None = None) -> torch.Tensor:
+def qgemv_q4k(w: torch.Tensor, x: torch.Tensor, M: int, K: int, y: torch.Tensor | None = None) -> torch.Tensor:
     """y[M] = W x for a packed Q4_K matrix (fp32 x, y)."""
     _need_cuda(w, x, y)
     y = y if y is not None else torch.empty(M, dtype=torch.float32, device=x.device)
-    need = int(lib().qgemv_q4k_workspace_bytes(M, K))
-    ws = _ws(ws, need, x.device)
-    _check("qgemv_q4k", lib().qgemv_q4k(_ptr(w), _ptr(x), _ptr(y), M, K, ws.ptr(), ws.nbytes(), _stream(x.device)))
+    _check("qgemv_q4k", lib().qgemv_q4k(_ptr(w), _ptr(x), _ptr(y), M, K, _stream(x.device)))
     return y
 
 
-def qgemv_q4k_batch(problems, ws: Workspace | None = None):
+def qgemv_q4k_batch(problems):
     """problems: list of (w_packed, x, y, M, K); one launch for all of them."""
     arr = (_Problem * len(problems))()
     dev = None
@@ -259,19 +295,14 @@ def qgemv_q4k_batch(problems, ws: Workspace | None = None):
         _need_cuda(w, x, y)
         dev = x.device
         arr[i] = _Problem(_ptr(w), _ptr(x), _ptr(y), M, K)
-    need = int(lib().qgemv_q4k_batch_workspace_bytes(arr, len(problems)))
-    ws = _ws(ws, need, dev)
-    _check("qgemv_q4k_batch", lib().qgemv_q4k_batch(arr, len(problems), ws.ptr(), ws.nbytes(), _stream(dev)))
+    _check("qgemv_q4k_batch", lib().qgemv_q4k_batch(arr, len(problems), _stream(dev)))
     return [p[2] for p in problems]
 
 
-def qgemv_q8_0(w: torch.Tensor, x: torch.Tensor, M: int, K: int, y: torch.Tensor | None = None,
-               ws: Workspace | None = None) -> torch.Tensor:
+def qgemv_q8_0(w: torch.Tensor, x: torch.Tensor, M: int, K: int, y: torch.Tensor | None = None) -> torch.Tensor:
     _need_cuda(w, x, y)
     y = y if y is not None else torch.empty(M, dtype=torch.float32, device=x.device)
-    need = int(lib().qgemv_q8_0_workspace_bytes(M, K))
-    ws = _ws(ws, need, x.device)
-    _check("qgemv_q8_0", lib().qgemv_q8_0(_ptr(w), _ptr(x), _ptr(y), M, K, ws.ptr(), ws.nbytes(), _stream(x.device)))
+    _check("qgemv_q8_0", lib().qgemv_q8_0(_ptr(w), _ptr(x), _ptr(y), M, K, _stream(x.device)))
     return y
 
 
@@ -298,19 +329,15 @@ def quantize_q8_1(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Ten
     return out
 
 
-def qgemv_q4k_q8_1(w: torch.Tensor, xq: torch.Tensor, M: int, K: int, y: torch.Tensor | None = None,
-                   ws: Workspace | None = None) -> torch.Tensor:
+def qgemv_q4k_q8_1(w: torch.Tensor, xq: torch.Tensor, M: int, K: int, y: torch.Tensor | None = None) -> torch.Tensor:
     """y[M] = W xq for a packed Q4_K matrix and quantized activations."""
     _need_cuda(w, xq, y)
     y = y if y is not None else torch.empty(M, dtype=torch.float32, device=xq.device)
-    need = int(lib().qgemv_q4k_q8_1_workspace_bytes(M, K))
-    ws = _ws(ws, need, xq.device)
-    _check("qgemv_q4k_q8_1", lib().qgemv_q4k_q8_1(_ptr(w), _ptr(xq), _ptr(y), M, K, ws.ptr(), ws.nbytes(),
-                                                  _stream(xq.device)))
+    _check("qgemv_q4k_q8_1", lib().qgemv_q4k_q8_1(_ptr(w), _ptr(xq), _ptr(y), M, K, _stream(xq.device)))
     return y
 
 
-def qgemv_q4k_q8_1_batch(problems, ws: Workspace | None = None):
+def qgemv_q4k_q8_1_batch(problems):
     """problems: list of (w_packed, xq, y, M, K); one launch for all of them."""
     arr = (_Problem * len(problems))()  # same field layout as qg_gemv_q8_1_problem
     dev = None
@@ -318,40 +345,38 @@ def qgemv_q4k_q8_1_batch(problems, ws: Workspace | None = None):
         _need_cuda(w, xq, y)
         dev = xq.device
         arr[i] = _Problem(_ptr(w), _ptr(xq), _ptr(y), M, K)
-    need = int(lib().qgemv_q4k_q8_1_batch_workspace_bytes(arr, len(problems)))
-    ws = _ws(ws, need, dev)
-    _check("qgemv_q4k_q8_1_batch", lib().qgemv_q4k_q8_1_batch(arr, len(problems), ws.ptr(), ws.nbytes(),
-                                                              _stream(dev)))
+    _check("qgemv_q4k_q8_1_batch", lib().qgemv_q4k_q8_1_batch(arr, len(problems), _stream(dev)))
     return [p[2] for p in problems]
 
 
-def quantize_q8_1_columns(X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """X (N, ldx) fp32 rows of K = ldx activations each -> N consecutive Q8_1 buffers
-    of q8_1_bytes(K) bytes (one qg_quantize_q8_1 call per column)."""
+def quantize_q8_1_columns(X: torch.Tensor, out: torch.Tensor | None = None, K: int | None = None) -> torch.Tensor:
+    """X (N, ldx) fp32, row n = column n (its first K = ldx entries unless K is
+    given) -> N consecutive Q8_1 buffers of q8_1_bytes(K) bytes, in one launch."""
     _need_cuda(X, out)
-    N, K = X.shape
+    N, ldx = X.shape
+    if X.stride(1) != 1 or X.stride(0) != ldx:
+        raise ValueError("X must be a contiguous (N, ldx) tensor")
+    K = ldx if K is None else K
     nb = q8_1_bytes(K)
     out = out if out is not None else torch.empty(N * nb, dtype=torch.uint8, device=X.device)
-    for n in range(N):
-        quantize_q8_1(X[n], out=out[n * nb:(n + 1) * nb])
+    _check("qg_quantize_q8_1_columns",
+           lib().qg_quantize_q8_1_columns(_ptr(X), ldx, K, N, _ptr(out), _stream(X.device)))
     return out
 
 
-def qgemm_q4k_q8_1_smalln(w: torch.Tensor, xq: torch.Tensor, M: int, K: int, N: int, Y: torch.Tensor | None = None,
-                          ws: Workspace | None = None) -> torch.Tensor:
+def qgemm_q4k_q8_1_smalln(w: torch.Tensor, xq: torch.Tensor, M: int, K: int, N: int,
+                          Y: torch.Tensor | None = None) -> torch.Tensor:
     """Y (N, ldy) = W Xq for N <= 8 quantized columns (quantize_q8_1_columns)."""
     _need_cuda(w, xq, Y)
     Y = Y if Y is not None else torch.empty((N, (M + 3) // 4 * 4), dtype=torch.float32, device=xq.device)
     if Y.shape[0] != N or Y.stride(1) != 1:
         raise ValueError("Y must be a contiguous (N, ldy) tensor")
-    need = int(lib().qgemm_q4k_q8_1_smalln_workspace_bytes(M, K, N))
-    ws = _ws(ws, need, xq.device)
     _check("qgemm_q4k_q8_1_smalln", lib().qgemm_q4k_q8_1_smalln(_ptr(w), _ptr(xq), _ptr(Y), Y.stride(0), M, K, N,
-                                                                ws.ptr(), ws.nbytes(), _stream(xq.device)))
+                                                                _stream(xq.device)))
     return Y
 
 
-def qgemm_q4k_q8_1_smalln_batch(problems, ws: Workspace | None = None):
+def qgemm_q4k_q8_1_smalln_batch(problems):
     """problems: list of (w_packed, xq, Y, M, K) with Y (N, ldy) and xq holding N
     quantized columns; one launch for all of them."""
     arr = (_GemmQ81Problem * len(problems))()
@@ -362,26 +387,19 @@ def qgemm_q4k_q8_1_smalln_batch(problems, ws: Workspace | None = None):
         if Y.stride(1) != 1:
             raise ValueError("Y must be a contiguous (N, ldy) tensor")
         arr[i] = _GemmQ81Problem(_ptr(w), _ptr(xq), _ptr(Y), Y.stride(0), M, K, Y.shape[0])
-    need = int(lib().qgemm_q4k_q8_1_smalln_batch_workspace_bytes(arr, len(problems)))
-    ws = _ws(ws, need, dev)
-    _check("qgemm_q4k_q8_1_smalln_batch",
-           lib().qgemm_q4k_q8_1_smalln_batch(arr, len(problems), ws.ptr(), ws.nbytes(), _stream(dev)))
+    _check("qgemm_q4k_q8_1_smalln_batch", lib().qgemm_q4k_q8_1_smalln_batch(arr, len(problems), _stream(dev)))
     return [p[2] for p in problems]
 
 
-def qgemv_q6k(w: torch.Tensor, x: torch.Tensor, M: int, K: int, y: torch.Tensor | None = None,
-              ws: Workspace | None = None) -> torch.Tensor:
+def qgemv_q6k(w: torch.Tensor, x: torch.Tensor, M: int, K: int, y: torch.Tensor | None = None) -> torch.Tensor:
     """y[M] = W x for a packed Q6_K matrix (fp32 x, y)."""
     _need_cuda(w, x, y)
     y = y if y is not None else torch.empty(M, dtype=torch.float32, device=x.device)
-    need = int(lib().qgemv_q6k_workspace_bytes(M, K))
-    ws = _ws(ws, need, x.device)
-    _check("qgemv_q6k", lib().qgemv_q6k(_ptr(w), _ptr(x), _ptr(y), M, K, ws.ptr(), ws.nbytes(), _stream(x.device)))
+    _check("qgemv_q6k", lib().qgemv_q6k(_ptr(w), _ptr(x), _ptr(y), M, K, _stream(x.device)))
     return y
 
 
-def qgemm_q4k_smalln(w: torch.Tensor, X: torch.Tensor, M: int, K: int, Y: torch.Tensor | None = None,
-                     ws: Workspace | None = None) -> torch.Tensor:
+def qgemm_q4k_smalln(w: torch.Tensor, X: torch.Tensor, M: int, K: int, Y: torch.Tensor | None = None) -> torch.Tensor:
     """X: (N, ldx) fp32, row n = column n of the K x N operand (ldx >= K, ldx % 4 == 0).
     Returns Y as (N, ldy) with Y[n, :M] = W X[n, :K]."""
     _need_cuda(w, X, Y)
@@ -392,14 +410,12 @@ def qgemm_q4k_smalln(w: torch.Tensor, X: torch.Tensor, M: int, K: int, Y: torch.
         ldy = (M + 3) // 4 * 4
         Y = torch.empty((N, ldy), dtype=torch.float32, device=X.device)
     ldy = Y.shape[1]
-    need = int(lib().qgemm_q4k_smalln_workspace_bytes(M, K, N))
-    ws = _ws(ws, need, X.device)
     _check("qgemm_q4k_smalln", lib().qgemm_q4k_smalln(_ptr(w), _ptr(X), ldx, _ptr(Y), ldy, M, K, N,
-                                                        ws.ptr(), ws.nbytes(), _stream(X.device)))
+                                                        _stream(X.device)))
     return Y
 
 
-def qgemm_q4k_smalln_batch(problems, ws: Workspace | None = None):
+def qgemm_q4k_smalln_batch(problems):
     """problems: list of (w_packed, X, Y, M, K) with X (N, ldx) and Y (N, ldy) as in
     qgemm_q4k_smalln; one launch for all of them. Returns the Y tensors."""
     arr = (_GemmProblem * len(problems))()
@@ -411,10 +427,7 @@ def qgemm_q4k_smalln_batch(problems, ws: Workspace | None = None):
         if X.stride(1) != 1 or X.stride(0) != ldx or Y.stride(1) != 1 or Y.shape[0] != N:
             raise ValueError("X and Y must be contiguous (N, ld) tensors with the same N")
         arr[i] = _GemmProblem(_ptr(w), _ptr(X), ldx, _ptr(Y), Y.stride(0), M, K, N)
-    need = int(lib().qgemm_q4k_smalln_batch_workspace_bytes(arr, len(problems)))
-    ws = _ws(ws, need, dev)
-    _check("qgemm_q4k_smalln_batch",
-           lib().qgemm_q4k_smalln_batch(arr, len(problems), ws.ptr(), ws.nbytes(), _stream(dev)))
+    _check("qgemm_q4k_smalln_batch", lib().qgemm_q4k_smalln_batch(arr, len(problems), _stream(dev)))
     return [p[2] for p in problems]
 
 

@@ -32,10 +32,11 @@
 // 0x000F000F leaves two quants q as the binary16 values q * 2^-24, with
 // 0x00F000F0 two high nibbles as 16q * 2^-24; the 2^24 and 1/16 factors go into
 // the sub-block scales. Per 8 weights: 5 bit operations and 4 dot2 operations.
-// Rounding x to fp16 changes each product by at most 2^-11 relative, well inside
-// the 1e-3 * sum|w*x| bound; accumulation is fp32.
+// The sub-block sums X_j are taken over the same fp16 values, so the result is the
+// exact product of W with the rounded x up to fp32 accumulation: rounding x to
+// fp16 changes each product by at most 2^-11 relative (x in the fp16 normal
+// range), well inside the 1e-3 * sum|w*x| bound.
 #include <algorithm>
-#include <cstdlib>
 
 #include "qg_device.h"
 #include "qg_host.h"
@@ -64,17 +65,6 @@ struct SbIn {
     float4 xa, xb, xc, xd;  // activations: low-nibble dwords i0, i0+1, then high-nibble ones
 };
 
-QG_DEV void load_sb(SbIn& d, const uint4* __restrict__ seg, const float* __restrict__ xk, int b, int rt) {
-    const float* xb = xk + 256 * b;
-    d.xa = *reinterpret_cast<const float4*>(xb);
-    d.xb = *reinterpret_cast<const float4*>(xb + 4);
-    d.xc = *reinterpret_cast<const float4*>(xb + 32);
-    d.xd = *reinterpret_cast<const float4*>(xb + 36);
-    const uint4* sb = seg + (size_t)b * 9 * rt;
-#pragma unroll
-    for (int s = 0; s < 9; ++s) d.s[s] = qg_stream_load(sb + s * rt);
-}
-
 // The same loads as raw buffer loads: one resource per tile (weights) and one for
 // x, a per-lane byte offset and the segment / activation offsets as scalar
 // operands, so that a super-block costs one vector address operation instead of
@@ -98,12 +88,11 @@ QG_DEV void load_sb_buf(SbIn& d, __amdgpu_buffer_rsrc_t wr, uint32_t vrow, __amd
 QG_DEV float sb_dot(const SbIn& d) {
     // activation pairs in the order the dot products consume them
     const QgPairs8 xp = qg_cvt_pairs(d.xa, d.xc, d.xb, d.xd);
-    // sub-block sums: this lane holds 8 values of sub-block 2g and 8 of 2g+1,
-    // g = (lane % 16) / 4, so a quad reduction gives X_{2g}, X_{2g+1}
-    const float slo_x = ((d.xa.x + d.xa.y) + (d.xa.z + d.xa.w)) + ((d.xb.x + d.xb.y) + (d.xb.z + d.xb.w));
-    const float shi_x = ((d.xc.x + d.xc.y) + (d.xc.z + d.xc.w)) + ((d.xd.x + d.xd.y) + (d.xd.z + d.xd.w));
-    const float Xlo = qg_quad_sum(slo_x);
-    const float Xhi = qg_quad_sum(shi_x);
+    // sub-block sums of the same fp16 values: this lane holds 8 of sub-block 2g
+    // (pairs 0, 1, 4, 5) and 8 of 2g+1 (pairs 2, 3, 6, 7), g = (lane % 16) / 4, so a
+    // quad reduction gives X_{2g}, X_{2g+1}
+    const float Xlo = qg_quad_sum(qg_sum_pairs4(xp.p[0], xp.p[1], xp.p[4], xp.p[5]));
+    const float Xhi = qg_quad_sum(qg_sum_pairs4(xp.p[2], xp.p[3], xp.p[6], xp.p[7]));
 
     // S_{2g} (low nibbles) and S_{2g+1} (high nibbles, x16) from quant segments 2g, 2g+1
     float S[8];
@@ -157,8 +146,8 @@ QG_DEV float sb_dot(const SbIn& d) {
     return fmaf(dd * 16777216.0f, t, -dm * mn);
 }
 
-// MODE 0: one super-block per K-group; 1: several, one register buffer (load,
-// compute, load, ...); 2: several, two register buffers (ping-pong prefetch).
+// MODE 0: one super-block per K-group; 2: several, two register buffers
+// (ping-pong prefetch).
 template <int W, int MODE>
 __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(Q4Args a) {
     const int wg = blockIdx.x;
@@ -193,14 +182,6 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(Q4Args a) {
         load_sb_buf(b0, wr, vrow, xr, vx, min(kg, nb - 1), rt);
         const float v0 = sb_dot(b0);
         acc = (kg < nb) ? v0 : 0.f;
-    } else if constexpr (MODE == 1) {
-        const int niter = (nb + G - 1) / G;
-        for (int it = 0; it < niter; ++it) {
-            SbIn b0;
-            load_sb_buf(b0, wr, vrow, xr, vx, min(kg + G * it, nb - 1), rt);
-            const float v0 = sb_dot(b0);
-            acc += (kg + G * it < nb) ? v0 : 0.f;
-        }
     } else {
         const int niter = (nb + G - 1) / G;
         // Ping-pong between two register buffers over pairs of super-blocks: the
@@ -242,122 +223,6 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(Q4Args a) {
     if (lane < rt) P.y[tile * T + lane] = v;
 }
 
-// Persistent form: a fixed grid of workgroups walks the tiles of all problems
-// (tile = blockIdx.x, + gridDim.x, ...). Each K-group keeps the loads of its next
-// work item (next super-block, or the first super-block of the next tile) in flight
-// while it computes the current one, so a wavefront streams continuously and no
-// workgroup is launched or retired per tile.
-QG_DEV int find_prob(const Q4Args& a, int gt) {
-    int k = 0;
-#pragma unroll
-    for (int i = 1; i < QG_MAX_BATCH; ++i)
-        if (i < a.count && gt >= a.begin[i]) k = i;
-    return k;
-}
-
-template <int W>
-QG_DEV void load_item(SbIn& d, const Q4Prob& P, int tile, int it, int kg, int i, int xoff) {
-    constexpr int G = 4 * W;
-    const int rt = min(T, P.M - tile * T);
-    const uint4* seg = reinterpret_cast<const uint4*>(P.w + (size_t)tile * T * P.nb * 144) + min(i, rt - 1);
-    load_sb(d, seg, P.x + xoff, min(kg + G * it, P.nb - 1), rt);
-}
-
-// Work item of a workgroup: super-block iteration `it` of global tile `gt`
-// (problem k). `valid` is false past the end of the workgroup's tile sequence.
-struct Item {
-    int gt, it, k;
-    bool valid;
-};
-
-// The item after c in this workgroup's sequence. Past the end, the result keeps
-// c's address (its load is re-issued and unused) and is marked invalid; every call
-// advances (it + 1, or gt + gridDim.x), so the sequence ends after at most
-// total_tiles * iterations steps.
-template <int W>
-QG_DEV Item next_item(const Q4Args& a, const Item c, int total_tiles) {
-    constexpr int G = 4 * W;
-    Item n = c;
-    bool ok = true;
-    n.it = c.it + 1;
-    if (n.it == (a.p[c.k].nb + G - 1) / G) {
-        n.gt = c.gt + gridDim.x;
-        n.it = 0;
-        ok = n.gt < total_tiles;
-        if (ok) n.k = find_prob(a, n.gt);
-    }
-    if (!ok) {
-        n.gt = c.gt;
-        n.it = c.it;
-        n.k = c.k;
-    }
-    n.valid = ok && c.valid;
-    return n;
-}
-
-template <int W>
-struct PersistState {
-    float acc = 0.f;
-    int parity = 0;
-};
-
-// Compute item c from buffer d; on the last super-block of a tile, reduce over the
-// K-groups and wavefronts and store the tile's 16 outputs.
-template <int W>
-QG_DEV void process(PersistState<W>& st, float (&red)[2][W][T], const Q4Args& a, const SbIn& d, const Item c, int lane,
-                    int wave, int kg) {
-    constexpr int G = 4 * W;
-    const Q4Prob& P = a.p[c.k];
-    const float v = sb_dot(d);
-    st.acc += (kg + G * c.it < P.nb) ? v : 0.f;
-    if (c.it == (P.nb + G - 1) / G - 1) {
-        const int tile = c.gt - P.wg_begin;
-        const int rt = min(T, P.M - tile * T);
-        float r = qg_sum_rows4(st.acc);
-        if constexpr (W > 1) {
-            if (lane < T) red[st.parity][wave][lane] = r;
-            __syncthreads();
-            if (wave == 0 && lane < T) {
-                r = red[st.parity][0][lane];
-#pragma unroll
-                for (int w = 1; w < W; ++w) r += red[st.parity][w][lane];
-            }
-            st.parity ^= 1;
-        }
-        if (wave == 0 && lane < rt) P.y[tile * T + lane] = r;
-        st.acc = 0.f;
-    }
-}
-
-template <int W>
-__global__ __launch_bounds__(64 * W) void q4k_gemv_persist_kernel(Q4Args a, int total_tiles) {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int i = lane & 15;
-    const int kg = 4 * wave + (lane >> 4);
-    const int p = i >> 1;
-    const int xoff = 64 * (p >> 1) + 16 * (p & 1) + 8 * (i & 1);
-    __shared__ float red[2][W][T];
-
-    PersistState<W> st;
-    Item c0{(int)blockIdx.x, 0, find_prob(a, blockIdx.x), true};
-    SbIn b0, b1;
-    load_item<W>(b0, a.p[c0.k], c0.gt - a.p[c0.k].wg_begin, c0.it, kg, i, xoff);
-    // ping-pong between two register buffers: the loads of one item stay in
-    // flight while the other is computed, with no register copies in between
-    while (true) {
-        const Item c1 = next_item<W>(a, c0, total_tiles);
-        load_item<W>(b1, a.p[c1.k], c1.gt - a.p[c1.k].wg_begin, c1.it, kg, i, xoff);
-        process<W>(st, red, a, b0, c0, lane, wave, kg);
-        if (!c1.valid) break;
-        const Item c2 = next_item<W>(a, c1, total_tiles);
-        load_item<W>(b0, a.p[c2.k], c2.gt - a.p[c2.k].wg_begin, c2.it, kg, i, xoff);
-        process<W>(st, red, a, b1, c1, lane, wave, kg);
-        if (!c2.valid) break;
-        c0 = c2;
-    }
-}
-
 __global__ void q4k_pack_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t M, int nb) {
     const int64_t units = M * nb * 9;
     const int64_t tile_units = (int64_t)T * nb * 9;
@@ -379,18 +244,6 @@ struct Plan {
     int total_wg = 0;  // tiles over all problems
 };
 
-int cu_count() {
-    static int cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 void plan_batch(const qg_gemv_problem* pr, int count, Q4Args* args, Plan* plan) {
     int64_t tiles_total = 0;
     int nb_max = 1;
@@ -404,8 +257,7 @@ void plan_batch(const qg_gemv_problem* pr, int count, Q4Args* args, Plan* plan) 
     (void)tiles_total;
     int W = 1;
     while (W < 4 && 4 * W < nb_max) W *= 2;
-    int ew = 0, eu = 0;
-    if (qg::env_pair("QG_Q4K_CFG", &ew, &eu) && (ew == 1 || ew == 2 || ew == 4 || ew == 8 || ew == 16)) W = ew;
+    if (qg::launch_override().gemv_waves) W = qg::launch_override().gemv_waves;
     plan->W = W;
     int wg = 0;
     for (int i = 0; i < count; ++i) {
@@ -424,7 +276,7 @@ void plan_batch(const qg_gemv_problem* pr, int count, Q4Args* args, Plan* plan) 
     plan->total_wg = wg;
 }
 
-int validate(const qg_gemv_problem* pr, int count) {
+qg_status validate(const qg_gemv_problem* pr, int count) {
     if (!pr) return qg::fail(QG_ERR_NULL, "problem list is NULL");
     if (count < 1 || count > QG_MAX_BATCH) return qg::fail(QG_ERR_SHAPE, "batch count %d not in [1, %d]", count, QG_MAX_BATCH);
     int64_t tiles = 0;
@@ -446,18 +298,8 @@ template <int W>
 void launch(const Q4Args& a, int tiles, hipStream_t s) {
     bool multi = false;  // some K-group walks more than one super-block
     for (int i = 0; i < a.count; ++i) multi = multi || a.p[i].nb > 4 * W;
-    // A grid of one workgroup per tile measured faster than a persistent grid on
-    // the 7B decode shapes; QG_Q4K_PERSIST=n selects a persistent grid of n
-    // workgroups per CU.
-    const char* e = getenv("QG_Q4K_PERSIST");
-    const int per_cu = (e && *e) ? atoi(e) : 0;
-    const int grid = per_cu > 0 ? std::min(tiles, per_cu * cu_count()) : tiles;
-    if (grid < tiles)
-        hipLaunchKernelGGL(q4k_gemv_persist_kernel<W>, dim3(grid), dim3(64 * W), 0, s, a, tiles);
-    else if (!multi)
+    if (!multi)
         hipLaunchKernelGGL((q4k_gemv_kernel<W, 0>), dim3(tiles), dim3(64 * W), 0, s, a);
-    else if constexpr (W >= 16)
-        hipLaunchKernelGGL((q4k_gemv_kernel<W, 1>), dim3(tiles), dim3(64 * W), 0, s, a);
     else
         hipLaunchKernelGGL((q4k_gemv_kernel<W, 2>), dim3(tiles), dim3(64 * W), 0, s, a);
 }
@@ -466,17 +308,10 @@ void launch(const Q4Args& a, int tiles, hipStream_t s) {
 
 extern "C" {
 
-size_t qgemv_q4k_batch_workspace_bytes(const qg_gemv_problem* problems, int count) {
-    (void)problems;
-    (void)count;
-    return 0;  // every workgroup owns whole rows: no cross-workgroup reduction
-}
-
-int qgemv_q4k_batch(const qg_gemv_problem* problems, int count, void* ws, size_t ws_bytes, qg_stream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
+// Every workgroup owns whole rows: no cross-workgroup reduction, no workspace.
+qg_status qgemv_q4k_batch(const qg_gemv_problem* problems, int count, qg_stream_t stream) {
     qg::clear_error();
-    int st = validate(problems, count);
+    qg_status st = validate(problems, count);
     if (st) return st;
     Q4Args a{};
     Plan p;
@@ -488,25 +323,17 @@ int qgemv_q4k_batch(const qg_gemv_problem* problems, int count, void* ws, size_t
         case 1: launch<1>(a, p.total_wg, s); break;
         case 2: launch<2>(a, p.total_wg, s); break;
         case 4: launch<4>(a, p.total_wg, s); break;
-        case 8: launch<8>(a, p.total_wg, s); break;
-        default: launch<16>(a, p.total_wg, s); break;
+        default: launch<8>(a, p.total_wg, s); break;
     }
     return qg::launch_status("qgemv_q4k");
 }
 
-size_t qgemv_q4k_workspace_bytes(int64_t M, int64_t K) {
-    (void)M;
-    (void)K;
-    return 0;
-}
-
-int qgemv_q4k(const void* w, const float* x, float* y, int64_t M, int64_t K, void* ws, size_t ws_bytes,
-              qg_stream_t stream) {
+qg_status qgemv_q4k(const void* w, const float* x, float* y, int64_t M, int64_t K, qg_stream_t stream) {
     qg_gemv_problem p{w, x, y, M, K};
-    return qgemv_q4k_batch(&p, 1, ws, ws_bytes, stream);
+    return qgemv_q4k_batch(&p, 1, stream);
 }
 
-int qg_pack_q4k(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t stream) {
+qg_status qg_pack_q4k(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t stream) {
     qg::clear_error();
     if (!src || !dst) return qg::fail(QG_ERR_NULL, "NULL pointer");
     if (M < 1 || M > INT32_MAX || K < 256 || K % 256 || K > (1 << 24))
@@ -516,7 +343,7 @@ int qg_pack_q4k(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t st
     const uint8_t* s8 = (const uint8_t*)src;
     const uint8_t* d8 = (const uint8_t*)dst;
     if (s8 < d8 + bytes && d8 < s8 + bytes) return qg::fail(QG_ERR_SHAPE, "src and dst overlap");
-    int st = qg::check_device();
+    qg_status st = qg::check_device();
     if (st) return st;
     const int64_t units = (int64_t)(bytes / 16);
     const int blocks = (int)std::min<int64_t>(qg::ceil_div(units, 256), 65536);

@@ -51,15 +51,21 @@ struct XqArgs {
     const int16_t* s;
 };
 
-// One wavefront per 256 activations (eight blocks: lanes 8c .. 8c+7 hold block c),
-// four per workgroup.
-__global__ __launch_bounds__(256) void q8_1_quantize_kernel(const float* __restrict__ x, int n256,
-                                                            float* __restrict__ d, int8_t* __restrict__ q,
-                                                            int16_t* __restrict__ s) {
-    const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+// One wavefront per 256 activations of one column (eight blocks: lanes 8c ..
+// 8c+7 hold block c), four per workgroup; column n reads x + n * ldx and writes
+// the buffer at xq + n * xqb (q at q_off, sums at s_off within it).
+__global__ __launch_bounds__(256) void q8_1_quantize_kernel(const float* __restrict__ x, int64_t ldx, int n256,
+                                                            int N, uint8_t* __restrict__ xq, int64_t xqb,
+                                                            int32_t q_off, int32_t s_off) {
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (b >= n256) return;  // whole wavefronts
-    const float4 v = reinterpret_cast<const float4*>(x + 256 * (size_t)b)[lane];
+    if (gw >= n256 * N) return;  // whole wavefronts
+    const int n = gw / n256, b = gw - n * n256;
+    uint8_t* out = xq + (int64_t)n * xqb;
+    float* d = reinterpret_cast<float*>(out);
+    int8_t* q = reinterpret_cast<int8_t*>(out + q_off);
+    int16_t* s = reinterpret_cast<int16_t*>(out + s_off);
+    const float4 v = reinterpret_cast<const float4*>(x + (int64_t)n * ldx + 256 * (int64_t)b)[lane];
     float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     // maximum over the eight lanes of the block: quad swaps, then the 8-lane mirror
     am = fmaxf(am, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, am), 0xb1, 0xf, 0xf, true)));
@@ -252,33 +258,34 @@ extern "C" {
 
 size_t qg_q8_1_bytes(int64_t K) { return k_ok(K) ? q81_layout(K).total : 0; }
 
-int qg_quantize_q8_1(const float* x, int64_t K, void* xq, qg_stream_t stream) {
+qg_status qg_quantize_q8_1_columns(const float* X, int64_t ldx, int64_t K, int64_t N, void* xq, qg_stream_t stream) {
     qg::clear_error();
-    if (!x || !xq) return qg::fail(QG_ERR_NULL, "NULL pointer");
+    if (!X || !xq) return qg::fail(QG_ERR_NULL, "NULL pointer");
     if (!k_ok(K)) return qg::fail(QG_ERR_SHAPE, "K=%lld must be a positive multiple of 256 (<= 2^24)", (long long)K);
-    if (!qg::aligned16(x) || !qg::aligned16(xq)) return qg::fail(QG_ERR_ALIGN, "pointers must be 16-byte aligned");
+    if (N < 1 || N > QG_SMALLN_MAX) return qg::fail(QG_ERR_SHAPE, "N=%lld not in [1, %d]", (long long)N, QG_SMALLN_MAX);
+    if (N > 1 && (ldx < K || ldx % 4 || (N - 1) * ldx + K > (int64_t)1 << 29))
+        return qg::fail(QG_ERR_SHAPE, "ldx=%lld must be a multiple of 4, >= K, with (N-1)*ldx + K < 2^29",
+                        (long long)ldx);
+    if (!qg::aligned16(X) || !qg::aligned16(xq)) return qg::fail(QG_ERR_ALIGN, "pointers must be 16-byte aligned");
     const Q81Layout L = q81_layout(K);
-    const uint8_t* x8 = (const uint8_t*)x;
+    const uint8_t* x8 = (const uint8_t*)X;
     const uint8_t* q8 = (const uint8_t*)xq;
-    if (x8 < q8 + L.total && q8 < x8 + 4 * K) return qg::fail(QG_ERR_SHAPE, "x and xq overlap");
-    int st = qg::check_device();
+    const int64_t xspan = 4 * ((N - 1) * (N > 1 ? ldx : 0) + K);
+    if (x8 < q8 + N * L.total && q8 < x8 + xspan) return qg::fail(QG_ERR_SHAPE, "X and xq overlap");
+    qg_status st = qg::check_device();
     if (st) return st;
     const int n256 = (int)(K / 256);
-    uint8_t* b = (uint8_t*)xq;
-    hipLaunchKernelGGL(q8_1_quantize_kernel, dim3((unsigned)qg::ceil_div(n256, 4)), dim3(256), 0, (hipStream_t)stream,
-                       x, n256, (float*)b, (int8_t*)(b + L.q_off), (int16_t*)(b + L.s_off));
+    hipLaunchKernelGGL(q8_1_quantize_kernel, dim3((unsigned)qg::ceil_div((int64_t)n256 * N, 4)), dim3(256), 0,
+                       (hipStream_t)stream, X, N > 1 ? ldx : 0, n256, (int)N, (uint8_t*)xq, (int64_t)L.total,
+                       (int32_t)L.q_off, (int32_t)L.s_off);
     return qg::launch_status("qg_quantize_q8_1");
 }
 
-size_t qgemv_q4k_q8_1_batch_workspace_bytes(const qg_gemv_q8_1_problem* problems, int count) {
-    (void)problems;
-    (void)count;
-    return 0;
+qg_status qg_quantize_q8_1(const float* x, int64_t K, void* xq, qg_stream_t stream) {
+    return qg_quantize_q8_1_columns(x, K, K, 1, xq, stream);
 }
 
-int qgemv_q4k_q8_1_batch(const qg_gemv_q8_1_problem* pr, int count, void* ws, size_t ws_bytes, qg_stream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
+qg_status qgemv_q4k_q8_1_batch(const qg_gemv_q8_1_problem* pr, int count, qg_stream_t stream) {
     qg::clear_error();
     if (!pr) return qg::fail(QG_ERR_NULL, "problem list is NULL");
     if (count < 1 || count > QG_MAX_BATCH)
@@ -309,12 +316,11 @@ int qgemv_q4k_q8_1_batch(const qg_gemv_q8_1_problem* pr, int count, void* ws, si
         nb_max = std::max(nb_max, (int)P.nb);
     }
     a.count = count;
-    int st = qg::check_device();
+    qg_status st = qg::check_device();
     if (st) return st;
     int W = 1;
     while (W < 4 && 4 * W < nb_max) W *= 2;
-    int ew = 0, eu = 0;
-    if (qg::env_pair("QG_Q4K8_CFG", &ew, &eu) && (ew == 1 || ew == 2 || ew == 4 || ew == 8)) W = ew;
+    if (qg::launch_override().gemv_waves) W = qg::launch_override().gemv_waves;
     hipStream_t s = (hipStream_t)stream;
     switch (W) {
         case 1: launch<1>(a, tiles, nb_max, s); break;
@@ -325,16 +331,9 @@ int qgemv_q4k_q8_1_batch(const qg_gemv_q8_1_problem* pr, int count, void* ws, si
     return qg::launch_status("qgemv_q4k_q8_1");
 }
 
-size_t qgemv_q4k_q8_1_workspace_bytes(int64_t M, int64_t K) {
-    (void)M;
-    (void)K;
-    return 0;
-}
-
-int qgemv_q4k_q8_1(const void* w, const void* xq, float* y, int64_t M, int64_t K, void* ws, size_t ws_bytes,
-                   qg_stream_t stream) {
+qg_status qgemv_q4k_q8_1(const void* w, const void* xq, float* y, int64_t M, int64_t K, qg_stream_t stream) {
     qg_gemv_q8_1_problem p{w, xq, y, M, K};
-    return qgemv_q4k_q8_1_batch(&p, 1, ws, ws_bytes, stream);
+    return qgemv_q4k_q8_1_batch(&p, 1, stream);
 }
 
 }  // extern "C"

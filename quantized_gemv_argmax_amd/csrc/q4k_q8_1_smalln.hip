@@ -302,16 +302,7 @@ constexpr int kMaxCols = 8;
 
 extern "C" {
 
-size_t qgemm_q4k_q8_1_smalln_batch_workspace_bytes(const qg_gemm_q8_1_problem* problems, int count) {
-    (void)problems;
-    (void)count;
-    return 0;
-}
-
-int qgemm_q4k_q8_1_smalln_batch(const qg_gemm_q8_1_problem* pr, int count, void* ws, size_t ws_bytes,
-                                qg_stream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
+qg_status qgemm_q4k_q8_1_smalln_batch(const qg_gemm_q8_1_problem* pr, int count, qg_stream_t stream) {
     qg::clear_error();
     if (!pr) return qg::fail(QG_ERR_NULL, "problem list is NULL");
     if (count < 1 || count > QG_MAX_BATCH)
@@ -358,7 +349,7 @@ int qgemm_q4k_q8_1_smalln_batch(const qg_gemm_q8_1_problem* pr, int count, void*
         multi = multi || P.nb > G;
     }
     a.count = count;
-    int st = qg::check_device();
+    qg_status st = qg::check_device();
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
     switch (nmax) {
@@ -374,17 +365,10 @@ int qgemm_q4k_q8_1_smalln_batch(const qg_gemm_q8_1_problem* pr, int count, void*
     return qg::launch_status("qgemm_q4k_q8_1_smalln");
 }
 
-size_t qgemm_q4k_q8_1_smalln_workspace_bytes(int64_t M, int64_t K, int64_t N) {
-    (void)M;
-    (void)K;
-    (void)N;
-    return 0;
-}
-
-int qgemm_q4k_q8_1_smalln(const void* w_packed, const void* xq, float* Y, int64_t ldy, int64_t M, int64_t K,
-                          int64_t N, void* ws, size_t ws_bytes, qg_stream_t stream) {
+qg_status qgemm_q4k_q8_1_smalln(const void* w_packed, const void* xq, float* Y, int64_t ldy, int64_t M, int64_t K,
+                                int64_t N, qg_stream_t stream) {
     const qg_gemm_q8_1_problem p{w_packed, xq, Y, ldy, M, K, N};
-    return qgemm_q4k_q8_1_smalln_batch(&p, 1, ws, ws_bytes, stream);
+    return qgemm_q4k_q8_1_smalln_batch(&p, 1, stream);
 }
 
 }  // extern "C"

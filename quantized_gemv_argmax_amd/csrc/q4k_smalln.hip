@@ -59,14 +59,12 @@ struct SnProb {
     const uint8_t* w;
     const float* X;
     float* Y;
-    unsigned long long* slots;  // split-K exchange slots: KS - 1 arrays of M * N (KS > 1)
     int64_t ldx, ldy;
     int32_t M, nb, N, tiles, wg_begin;
 };
 struct SnArgs {
     int32_t begin[QG_MAX_BATCH];
     int32_t count;
-    int32_t ks;  // workgroups sharing the K range of each row block (1, 2 or 4)
     SnProb p[QG_MAX_BATCH];
 };
 
@@ -193,10 +191,7 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
         if (i < a.count && wg >= a.begin[i]) k = i;
     const SnProb P = a.p[k];
 
-    const int KS = a.ks;
-    const int local = wg - P.wg_begin;
-    const int ks = local % KS;  // the KS workgroups of a row block are neighbours in the grid
-    const int tile0 = (local / KS) * TW;
+    const int tile0 = (wg - P.wg_begin) * TW;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15, s = lane >> 4;
@@ -221,10 +216,9 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
         const int n = 16 * c + i;
         ln.x[c] = n < P.N ? (uint32_t)(((int64_t)n * P.ldx + 8 * s) * 4) : kOutOfRange;
     }
-    // this workgroup's share of the K units, split among its wavefronts round-robin
+    // the K units, split among the wavefronts round-robin
     const int units = P.nb * 4;
-    const int ub = (int)((int64_t)ks * units / KS), ue = (int)((int64_t)(ks + 1) * units / KS);
-    const int niter = (ue - ub - wave + W - 1) / W;  // units ub + wave, ub + wave + W, ...
+    const int niter = (units - wave + W - 1) / W;  // units wave, wave + W, ...
     qg_f4 acc[TW][C];
 #pragma unroll
     for (int t = 0; t < TW; ++t)
@@ -237,7 +231,7 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
     // is clamped to the wavefront's last unit) and the pair loop has a single exit,
     // so the loop-carried load state, and with it every wait count, is exact.
     if (niter > 0) {
-        const int ufirst = ub + wave, ulast = ufirst + W * (niter - 1);
+        const int ufirst = wave, ulast = ufirst + W * (niter - 1);
         SnIn<C, TW> b0, b1;
         load_x<C, TW>(b0, xr, ln, ufirst);
         load_w<C, TW>(b0, tl, ln, ufirst);
@@ -289,9 +283,7 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_kernel(SnArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     const int n = 16 * c + 4 * s + e;
                     if (n >= P.N) continue;
-                    float v = acc[t][c][e];
-                    if (KS == 1 || qg_splitk_combine(v, P.slots + (int64_t)n * P.M + row, (int64_t)P.M * P.N, ks, KS))
-                        P.Y[(int64_t)n * P.ldy + row] = v;
+                    P.Y[(int64_t)n * P.ldy + row] = acc[t][c][e];
                 }
         }
     }
@@ -742,7 +734,7 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_lds1_kernel(SnArgs a) {
 }
 
 // ------------------------------------------------------------------ host side
-int sn_validate(const void* w, const float* X, int64_t ldx, const float* Y, int64_t ldy, int64_t M, int64_t K,
+qg_status sn_validate(const void* w, const float* X, int64_t ldx, const float* Y, int64_t ldy, int64_t M, int64_t K,
                 int64_t N) {
     if (!w || !X || !Y) return qg::fail(QG_ERR_NULL, "NULL pointer");
     if (M < 1 || M > INT32_MAX) return qg::fail(QG_ERR_SHAPE, "M=%lld out of range", (long long)M);
@@ -778,41 +770,36 @@ SnProb make_sn(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy
 // tiles divides the activation traffic (which for 16-row tiles exceeds the weight
 // traffic once N > 2) by TW, at the price of TW times fewer workgroups: one tile
 // up to 256 tiles in the batch (about one workgroup per CU), two above that, and
-// for more than 16 columns four above 1024 tiles. KS workgroups per row block may
-// split K (1, 2 or 4, through the exchange slots); measured on MI355X the extra
-// device-scope round trips at the end of every workgroup cost more than the
-// added parallelism gains on the 7B shapes, so KS stays 1 unless QG_SN_KS asks
-// for more. W wavefronts per workgroup (up to 8, 4 with four tiles), each with at
-// least two units.
+// for more than 16 columns four above 1024 tiles. W wavefronts per workgroup (up
+// to 8, 4 with four tiles), each with at least two units. (Splitting K among
+// workgroups, their partial sums meeting through atomic exchanges, was measured
+// slower at every 7B shape: the device-scope round trips at the end of every
+// workgroup cost more than the added parallelism gains.)
 struct SnCfg {
-    int W, TW, KS;
-    bool lds;   // LDS-staged kernel (KS = 1 only)
+    int W, TW;
+    bool lds;   // chunked LDS-staged kernel
     int D;      // its weight-queue depth in chunks
     bool lds1;  // single-pass LDS kernel (short K, N <= 8)
     bool dot;   // vector-ALU dot-product kernel (N <= 8, q4k_smalln_dot.hip)
 };
 SnCfg choose_cfg(const SnArgs& a, int C) {
+    const qg_launch_override& ov = qg::launch_override();
+    const int form = ov.smalln_form;
     int units = INT_MAX;
     int64_t tiles = 0;
+    int ncol = 0;
     for (int i = 0; i < a.count; ++i) {
         units = std::min(units, a.p[i].nb * 4);
         tiles += a.p[i].tiles;
+        ncol = std::max(ncol, (int)a.p[i].N);
     }
-    SnCfg c{1, tiles > 256 ? 2 : 1, 1, false, 2, false, false};
+    SnCfg c{1, tiles > 256 ? 2 : 1, false, 2, false, false};
     if (C == 2 && tiles > 1024) c.TW = 4;
-    int ew = 0, et = 0, ek = 0;
-    const bool env = qg::env_pair("QG_SN_CFG", &ew, &et);
-    if (env && (et == 1 || et == 2 || et == 4)) c.TW = et;
-    int64_t wgs = 0;
-    for (int i = 0; i < a.count; ++i) wgs += qg::ceil_div(a.p[i].tiles, c.TW);
-    (void)wgs;
-    int unused = 0;
-    if (qg::env_pair("QG_SN_KS", &ek, &unused) && (ek == 1 || ek == 2 || ek == 4)) c.KS = ek;
-    const int wmax = c.TW == 4 ? 4 : 8;
-    while (c.W < wmax && 2 * c.W <= units / c.KS / 2) c.W *= 2;
-    if (env && (ew == 1 || ew == 2 || ew == 4 || (ew == 8 && c.TW < 4) || (ew == 16 && C == 1 && c.TW == 1))) c.W = ew;
     // Form selection, from measurements on the 7B shapes (stage times in us, register
     // form -> chosen form):
+    //   - the vector-ALU dot-product form for up to four columns (196 decode
+    //     matrices, ms per step against the matrix-core forms: N = 1 0.93 / 1.57,
+    //     2 1.13 / 1.58, 3 1.29 / 1.63, 4 1.52 / 1.67, 5 1.83 / 1.74);
     //   - the single-pass LDS form for K <= 4096 and N <= 8 (N = 5: q/k/v 9.05 ->
     //     8.75, o 6.85 -> 6.44, gate/up 29.7 -> 26.6);
     //   - the chunked LDS form for K >= 8192 (down projection: N = 5 23.6 -> 21.6,
@@ -820,41 +807,35 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
     //     (N = 32: q/k/v 18.2 -> 14.2, o 16.6 -> 12.0);
     //   - the register form otherwise (N = 32 gate/up, 2368 tiles: 57.7 against 62.6
     //     for the chunked LDS form; N = 5 short K: 29.7 against 37.0).
-    // The register form also runs for split-K (QG_SN_KS) and its own launch-shape
-    // variable (QG_SN_CFG); QG_SN_IMPL=regs / lds / lds1 forces a form. Tiles per
-    // workgroup for the LDS forms: one, or two above 1024 tiles (chunked form: above
-    // 256 for more than 16 columns); QG_SNL_CFG=TW,D and QG_SN1_TW override.
-    const char* impl = getenv("QG_SN_IMPL");
-    const std::string im = impl ? impl : "";
-    int ncol = 0;
-    for (int i = 0; i < a.count; ++i) ncol = std::max(ncol, (int)a.p[i].N);
-    // Vector-ALU dot-product form for up to four columns (196 decode matrices, ms
-    // per step against the matrix-core forms: N = 1 0.93 / 1.57, 2 1.13 / 1.58,
-    // 3 1.29 / 1.63, 4 1.52 / 1.67, 5 1.83 / 1.74); QG_SN_IMPL=dot forces it up to 8.
-    c.dot = c.KS == 1 && !env && ((ncol <= 4 && im == "") || (ncol <= 8 && im == "dot"));
+    // A launch override (qg_set_launch_override) can force a form within the range
+    // it supports, and the launch shape.
+    c.dot = (form == QG_FORM_AUTO && ncol <= 4) || (form == QG_FORM_SMALLN_DOT && ncol <= 8);
     if (c.dot) return c;
     // Single-pass form: every problem with K <= 512 * 8 and N <= 8 (one round of
     // activation loads per lane, all super-blocks of a row in flight at once).
-    bool s1 = c.KS == 1 && !env && C == 1;
+    bool s1 = C == 1;
     for (int i = 0; i < a.count; ++i)
         s1 = s1 && a.p[i].N <= kS1Cols && a.p[i].nb * 32 <= 64 * kS1Waves && a.p[i].nb <= kS1Items * kS1Waves;
-    c.lds1 = s1 && (im == "" || im == "lds1");
+    c.lds1 = s1 && (form == QG_FORM_AUTO || form == QG_FORM_SMALLN_LDS1);
     if (c.lds1) {
         c.TW = tiles > 1024 ? 2 : 1;
-        int et1 = 0, unused1 = 0;
-        if (qg::env_pair("QG_SN1_TW", &et1, &unused1) && (et1 == 1 || et1 == 2)) c.TW = et1;
+        if (ov.smalln_tiles == 1 || ov.smalln_tiles == 2) c.TW = ov.smalln_tiles;
         return c;
     }
-    c.lds = c.KS == 1 && !env && im != "regs" && (im == "lds" || units >= 32 * 4 || (C == 2 && tiles <= 1024));
+    c.lds = form == QG_FORM_SMALLN_LDS ||
+            (form != QG_FORM_SMALLN_REGS && (units >= 32 * 4 || (C == 2 && tiles <= 1024)));
     if (c.lds) {
         c.TW = tiles > 1024 || (C == 2 && tiles > 256) ? 2 : 1;
         c.D = 2;
-        int et2 = 0, ed = 0;
-        if (qg::env_pair("QG_SNL_CFG", &et2, &ed)) {
-            if (et2 == 1 || et2 == 2) c.TW = et2;
-            if (ed >= 2 && ed <= (C == 2 ? 3 : 4)) c.D = ed;
-        }
+        if (ov.smalln_tiles == 1 || ov.smalln_tiles == 2) c.TW = ov.smalln_tiles;
+        if (ov.smalln_depth >= 2 && ov.smalln_depth <= (C == 2 ? 3 : 4)) c.D = ov.smalln_depth;
+        return c;
     }
+    // register form
+    if (ov.smalln_tiles) c.TW = ov.smalln_tiles;
+    const int wmax = c.TW == 4 ? 4 : 8;
+    while (c.W < wmax && 2 * c.W <= units / 2) c.W *= 2;
+    if (ov.smalln_waves && (ov.smalln_waves < 8 || c.TW < 4)) c.W = ov.smalln_waves;
     return c;
 }
 
@@ -927,69 +908,46 @@ void launch(const SnArgs& a, int grid, int W, hipStream_t s) {
         case 1: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 1>), dim3(grid), dim3(64), 0, s, a); break;
         case 2: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 2>), dim3(grid), dim3(128), 0, s, a); break;
         case 4: hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 4>), dim3(grid), dim3(256), 0, s, a); break;
-        case 8:
-            if constexpr (TW < 4) hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 8>), dim3(grid), dim3(512), 0, s, a);
-            break;
         default:
-            if constexpr (C == 1 && TW == 1) hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 16>), dim3(grid), dim3(1024), 0, s, a);
+            if constexpr (TW < 4) hipLaunchKernelGGL((q4k_smalln_kernel<C, TW, 8>), dim3(grid), dim3(512), 0, s, a);
             break;
     }
 }
 
-// Validates the problems and fills the kernel arguments and launch shape. With
-// ws_needed set, only the workspace size is computed (pointers are not checked).
-int plan(const qg_gemm_problem* probs, int count, bool size_only, SnArgs& a, SnCfg& cfg, int& C, int64_t& wgs,
-         size_t& ws_needed, int* nmax_out = nullptr) {
+// Validates the problems and fills the kernel arguments and launch shape.
+qg_status plan(const qg_gemm_problem* probs, int count, SnArgs& a, SnCfg& cfg, int& C, int64_t& wgs, int& nmax) {
     if (!probs) return qg::fail(QG_ERR_NULL, "NULL problem list");
     if (count < 1 || count > QG_MAX_BATCH)
         return qg::fail(QG_ERR_SHAPE, "count=%d not in [1, %d]", count, QG_MAX_BATCH);
     a = SnArgs{};
     a.count = count;
-    int nmax = 0;
+    nmax = 0;
     for (int i = 0; i < count; ++i) {
         const qg_gemm_problem& q = probs[i];
-        static const float dummy[4] = {0, 0, 0, 0};
-        int st = size_only ? sn_validate(dummy, dummy, q.ldx, dummy, q.ldy, q.M, q.K, q.N)
-                           : sn_validate(q.w_packed, q.X, q.ldx, q.Y, q.ldy, q.M, q.K, q.N);
+        qg_status st = sn_validate(q.w_packed, q.X, q.ldx, q.Y, q.ldy, q.M, q.K, q.N);
         if (st) return st;
         a.p[i] = make_sn(q.w_packed, q.X, q.ldx, q.Y, q.ldy, q.M, q.K, q.N);
         nmax = std::max(nmax, a.p[i].N);
     }
     C = nmax > 16 ? 2 : 1;
-    if (nmax_out) *nmax_out = nmax;
     cfg = choose_cfg(a, C);
-    a.ks = cfg.KS;
     wgs = 0;
-    ws_needed = 0;
     for (int i = 0; i < count; ++i) {
         a.p[i].wg_begin = (int32_t)wgs;
         a.begin[i] = (int32_t)wgs;
-        wgs += qg::ceil_div(a.p[i].tiles, cfg.TW) * cfg.KS;
-        if (cfg.KS > 1) ws_needed += qg::align_up((size_t)(cfg.KS - 1) * a.p[i].M * a.p[i].N * 8, 256);
+        wgs += qg::ceil_div(a.p[i].tiles, cfg.TW);
     }
     if (wgs > INT32_MAX) return qg::fail(QG_ERR_SHAPE, "too many tiles in one batch");
     return QG_OK;
 }
 
-int run(const qg_gemm_problem* probs, int count, void* ws, size_t ws_bytes, hipStream_t stream) {
+qg_status run(const qg_gemm_problem* probs, int count, hipStream_t stream) {
     SnArgs a;
     SnCfg cfg;
-    int C;
+    int C, nmax;
     int64_t wgs;
-    size_t need;
-    int nmax = 0;
-    int st = plan(probs, count, false, a, cfg, C, wgs, need, &nmax);
+    qg_status st = plan(probs, count, a, cfg, C, wgs, nmax);
     if (st) return st;
-    if (need > 0) {
-        if (!ws) return qg::fail(QG_ERR_WORKSPACE, "a workspace of %zu bytes is required", need);
-        if (ws_bytes < need) return qg::fail(QG_ERR_WORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
-        if (!qg::aligned16(ws)) return qg::fail(QG_ERR_ALIGN, "workspace must be 16-byte aligned");
-        unsigned char* p = (unsigned char*)ws;
-        for (int i = 0; i < count; ++i) {
-            a.p[i].slots = (unsigned long long*)p;
-            p += qg::align_up((size_t)(cfg.KS - 1) * a.p[i].M * a.p[i].N * 8, 256);
-        }
-    }
     st = qg::check_device();
     if (st) return st;
     if (cfg.dot) return qg::smalln_dot_launch(probs, count, stream);
@@ -1019,40 +977,20 @@ int run(const qg_gemm_problem* probs, int count, void* ws, size_t ws_bytes, hipS
     return qg::launch_status("qgemm_q4k_smalln");
 }
 
-size_t ws_bytes_for(const qg_gemm_problem* probs, int count) {
-    SnArgs a;
-    SnCfg cfg;
-    int C;
-    int64_t wgs;
-    size_t need = 0;
-    if (plan(probs, count, true, a, cfg, C, wgs, need)) return 0;
-    return need;
-}
-
 }  // namespace
 
 extern "C" {
 
-size_t qgemm_q4k_smalln_workspace_bytes(int64_t M, int64_t K, int64_t N) {
-    const qg_gemm_problem p{nullptr, nullptr, K, nullptr, (M + 3) / 4 * 4, M, K, N};
-    return ws_bytes_for(&p, 1);
-}
-
-int qgemm_q4k_smalln(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy, int64_t M, int64_t K,
-                     int64_t N, void* ws, size_t ws_bytes, qg_stream_t stream) {
+qg_status qgemm_q4k_smalln(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy, int64_t M, int64_t K,
+                           int64_t N, qg_stream_t stream) {
     qg::clear_error();
     const qg_gemm_problem p{w, X, ldx, Y, ldy, M, K, N};
-    return run(&p, 1, ws, ws_bytes, (hipStream_t)stream);
+    return run(&p, 1, (hipStream_t)stream);
 }
 
-size_t qgemm_q4k_smalln_batch_workspace_bytes(const qg_gemm_problem* problems, int count) {
-    return ws_bytes_for(problems, count);
-}
-
-int qgemm_q4k_smalln_batch(const qg_gemm_problem* problems, int count, void* ws, size_t ws_bytes,
-                           qg_stream_t stream) {
+qg_status qgemm_q4k_smalln_batch(const qg_gemm_problem* problems, int count, qg_stream_t stream) {
     qg::clear_error();
-    return run(problems, count, ws, ws_bytes, (hipStream_t)stream);
+    return run(problems, count, (hipStream_t)stream);
 }
 
 }  // extern "C"

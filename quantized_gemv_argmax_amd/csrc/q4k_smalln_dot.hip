@@ -25,7 +25,6 @@
 // waits for those weights. Columns past a problem's N read zeros through an
 // out-of-range buffer offset and are not stored.
 #include <algorithm>
-#include <cstdlib>
 
 #include "qg_device.h"
 #include "qg_host.h"
@@ -138,10 +137,10 @@ QG_DEV void sb_dot_n(float (&out)[NC], const uint4 (&s)[9], const XIn<NC>& x) {
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
         xp[n] = qg_cvt_pairs(x.a[n], x.c[n], x.b[n], x.d[n]);
-        const float slo = ((x.a[n].x + x.a[n].y) + (x.a[n].z + x.a[n].w)) + ((x.b[n].x + x.b[n].y) + (x.b[n].z + x.b[n].w));
-        const float shi = ((x.c[n].x + x.c[n].y) + (x.c[n].z + x.c[n].w)) + ((x.d[n].x + x.d[n].y) + (x.d[n].z + x.d[n].w));
-        Xlo[n] = qg_quad_sum(slo);
-        Xhi[n] = qg_quad_sum(shi);
+        // sub-block sums over the same fp16 values (low run pairs 0, 1, 4, 5;
+        // high run pairs 2, 3, 6, 7), as in the single-column kernel
+        Xlo[n] = qg_quad_sum(qg_sum_pairs4(xp[n].p[0], xp[n].p[1], xp[n].p[4], xp[n].p[5]));
+        Xhi[n] = qg_quad_sum(qg_sum_pairs4(xp[n].p[2], xp[n].p[3], xp[n].p[6], xp[n].p[7]));
     }
     const uint4 hd = s[0];
     const QgScales sc = qg_q4k_scales(hd.y, hd.z, hd.w);
@@ -204,7 +203,7 @@ QG_DEV void sb_dot_n(float (&out)[NC], const uint4 (&s)[9], const XIn<NC>& x) {
 // one in flight; 2: several, weights and activations of the next one in flight
 // (two full register buffers; used for one column, where it measured faster on
 // the 3584 x 18944 down projection, 10.4 -> 9.8 us, and slower for two, 13.5 ->
-// 14.2 us; QG_SND_XPP=0/1 overrides).
+// 14.2 us).
 template <int MODE, int NC>
 __global__ __launch_bounds__(64 * W) void q4k_smalln_dot_kernel(SdArgs a) {
     const int wg = blockIdx.x;
@@ -333,10 +332,8 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_dot_kernel(SdArgs a) {
 
 template <int NC>
 void launch_nc(const SdArgs& a, int grid, bool multi, hipStream_t s) {
-    const char* e = getenv("QG_SND_XPP");
-    const bool xpp = (e && *e) ? atoi(e) != 0 : NC == 1;
-    if constexpr (NC <= 2) {
-        if (multi && xpp) {
+    if constexpr (NC == 1) {
+        if (multi) {
             hipLaunchKernelGGL((q4k_smalln_dot_kernel<2, NC>), dim3(grid), dim3(64 * W), 0, s, a);
             return;
         }
@@ -353,7 +350,7 @@ namespace qg {
 
 // Launches the dot-product form for problems already validated by the small-N
 // entry points (N <= 8 each; ldx, ldy and the activation extent checked there).
-int smalln_dot_launch(const qg_gemm_problem* probs, int count, hipStream_t s) {
+qg_status smalln_dot_launch(const qg_gemm_problem* probs, int count, hipStream_t s) {
     SdArgs a{};
     a.count = count;
     int wg = 0, nmax = 0;

@@ -34,10 +34,10 @@
 // quants are assembled in place with one bit-field insert per four weights and
 // masked to fp16 subnormals q * 2^-24 (qg_q6_seg_dot); one segment call yields
 // S_j of two sub-blocks. The 2^24 factor and the -32 offset are applied per
-// super-block. fp16 rounding of x changes each product by at most 2^-11 relative;
-// accumulation is fp32.
+// super-block, with activation sums taken over the same fp16 values, so fp16
+// rounding of x changes each product by at most 2^-11 relative (x in the fp16
+// normal range); accumulation is fp32.
 #include <algorithm>
-#include <cstdlib>
 
 #include "qg_device.h"
 #include "qg_host.h"
@@ -106,8 +106,10 @@ QG_DEV float q6_dot(const Q6In& v) {
     const QgPairs8 xp = qg_cvt_pairs(v.xa, v.xc, v.xb, v.xd);
     // this lane holds 8 values of sub-block j_lo(s) and 8 of j_lo(s) + 4; the
     // lane pair 2s, 2s+1 holds all 16 of both
-    float slo = ((v.xa.x + v.xa.y) + (v.xa.z + v.xa.w)) + ((v.xb.x + v.xb.y) + (v.xb.z + v.xb.w));
-    float shi = ((v.xc.x + v.xc.y) + (v.xc.z + v.xc.w)) + ((v.xd.x + v.xd.y) + (v.xd.z + v.xd.w));
+    // (the sums are taken over the same fp16 values the dot products use: low run
+    // pairs 0, 1, 4, 5, high run pairs 2, 3, 6, 7)
+    float slo = qg_sum_pairs4(xp.p[0], xp.p[1], xp.p[4], xp.p[5]);
+    float shi = qg_sum_pairs4(xp.p[2], xp.p[3], xp.p[6], xp.p[7]);
     slo += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, slo), 0xb1, 0xf, 0xf, true));
     shi += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, shi), 0xb1, 0xf, 0xf, true));
 
@@ -250,8 +252,7 @@ int choose_w(int nb) {
     // enough K-groups that every super-block of a row has its own, up to 4 wavefronts
     int W = 1;
     while (W < 4 && 4 * W < nb) W *= 2;
-    int ew = 0, eu = 0;
-    if (qg::env_pair("QG_Q6K_CFG", &ew, &eu) && (ew == 1 || ew == 2 || ew == 4 || ew == 8)) W = ew;
+    if (qg::launch_override().gemv_waves) W = qg::launch_override().gemv_waves;
     return W;
 }
 
@@ -272,16 +273,8 @@ size_t qg_q6k_bytes(int64_t M, int64_t K) {
     return (size_t)M * (size_t)(K / 256) * (size_t)kBlockBytes;
 }
 
-size_t qgemv_q6k_workspace_bytes(int64_t M, int64_t K) {
-    (void)M;
-    (void)K;
-    return 0;  // every workgroup owns whole rows
-}
-
-int qgemv_q6k(const void* w, const float* x, float* y, int64_t M, int64_t K, void* ws, size_t ws_bytes,
-              qg_stream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
+// Every workgroup owns whole rows: no workspace.
+qg_status qgemv_q6k(const void* w, const float* x, float* y, int64_t M, int64_t K, qg_stream_t stream) {
     qg::clear_error();
     if (!w || !x || !y) return qg::fail(QG_ERR_NULL, "NULL pointer");
     if (M < 1 || M > INT32_MAX - T) return qg::fail(QG_ERR_SHAPE, "M=%lld out of range", (long long)M);
@@ -289,7 +282,7 @@ int qgemv_q6k(const void* w, const float* x, float* y, int64_t M, int64_t K, voi
         return qg::fail(QG_ERR_SHAPE, "K=%lld must be a positive multiple of 256 (<= 2^24)", (long long)K);
     if (!qg::aligned16(w) || !qg::aligned16(x) || !qg::aligned16(y))
         return qg::fail(QG_ERR_ALIGN, "pointers must be 16-byte aligned");
-    int st = qg::check_device();
+    qg_status st = qg::check_device();
     if (st) return st;
     Q6Args a{(const uint8_t*)w, x, y, (int32_t)M, (int32_t)(K / 256)};
     const int tiles = (int)qg::ceil_div(M, T);
@@ -303,7 +296,7 @@ int qgemv_q6k(const void* w, const float* x, float* y, int64_t M, int64_t K, voi
     return qg::launch_status("qgemv_q6k");
 }
 
-int qg_pack_q6k(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t stream) {
+qg_status qg_pack_q6k(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t stream) {
     qg::clear_error();
     if (!src || !dst) return qg::fail(QG_ERR_NULL, "NULL pointer");
     if (M < 1 || M > INT32_MAX || K < 256 || K % 256 || K > (1 << 24))
@@ -313,7 +306,7 @@ int qg_pack_q6k(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t st
     const uint8_t* s8 = (const uint8_t*)src;
     const uint8_t* d8 = (const uint8_t*)dst;
     if (s8 < d8 + bytes && d8 < s8 + bytes) return qg::fail(QG_ERR_SHAPE, "src and dst overlap");
-    int st = qg::check_device();
+    qg_status st = qg::check_device();
     if (st) return st;
     const int64_t items = M * (K / 256) * (kSegs + 1);
     const int blocks = (int)std::min<int64_t>(qg::ceil_div(items, 256), 65536);

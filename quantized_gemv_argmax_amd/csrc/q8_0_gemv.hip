@@ -21,12 +21,14 @@
 //
 // Inner product, as in the Q4_K GEMV: a wavefront is four 16-lane DPP rows
 // ("K-groups", lane = weight row); each K-group walks half macro-blocks (4 blocks,
-// 128 weights) of its own. The int8 quants are biased to bytes (q ^ 0x80 = q + 128)
-// and used in place as fp16 subnormals ((q + 128) * 2^-24, two per masked word);
-// v_dot2c_f32_f16 with a DPP row broadcast feeds each lane the fp16 activation pair
-// it needs from the lane that holds it. The bias is removed per block with the
-// block's activation sum: d * (2^24 * S' - 128 * X). Per 4 weights: 4 bit
-// operations and 2 dot2 operations.
+// 128 weights) of its own. The int8 quants become signed fp16 subnormals
+// q * 2^-24 in place (a byte bias, one byte permutation and one exact packed fp16
+// addition per two quants: qg_q8_signed_masks), and v_dot2c_f32_f16 with a DPP
+// row broadcast feeds each lane the fp16 activation pair it needs from the lane
+// that holds it: per 4 weights 5 bit and fp16 operations and 2 dot2 operations.
+// The products are exact and every partial sum is bounded by sum |q x|, so the
+// result is within 2^-11 * sum|w x| plus fp32 accumulation error of the exact
+// product (x rounded to fp16), also for rows whose quants are all zero.
 #include <algorithm>
 #include <climits>
 
@@ -62,44 +64,32 @@ QG_DEV void load_half(HalfIn& d, const uint4* __restrict__ seg, const float* __r
     for (int s = 0; s < 8; ++s) d.s[1 + s] = qg_stream_load(base + (size_t)(1 + 8 * h + s) * rt);
 }
 
-// Contribution of half macro-block h for this lane's row.
+// Contribution of half macro-block h for this lane's row: the signed quants as
+// fp16 subnormals (qg_q8_signed_masks), so a block's product needs no activation
+// sum and the block's term is d * 2^24 * S.
 QG_DEV float half_dot(const HalfIn& d, int h) {
     const QgPairs4 xp = qg_cvt_pairs4(d.xa, d.xb);
-    // this lane holds 8 activations of block (lane % 16) / 4: quad sums give X_k
-    const float part = ((d.xa.x + d.xa.y) + (d.xa.z + d.xa.w)) + ((d.xb.x + d.xb.y) + (d.xb.z + d.xb.w));
-    const float Xq = qg_quad_sum(part);
-    float S[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-        switch (k) {
-            case 0:
-                qg_q8_seg_dot<0, 1>(a0, a1, a2, a3, d.s[1], xp.p);
-                qg_q8_seg_dot<2, 3>(a0, a1, a2, a3, d.s[2], xp.p);
-                break;
-            case 1:
-                qg_q8_seg_dot<4, 5>(a0, a1, a2, a3, d.s[3], xp.p);
-                qg_q8_seg_dot<6, 7>(a0, a1, a2, a3, d.s[4], xp.p);
-                break;
-            case 2:
-                qg_q8_seg_dot<8, 9>(a0, a1, a2, a3, d.s[5], xp.p);
-                qg_q8_seg_dot<10, 11>(a0, a1, a2, a3, d.s[6], xp.p);
-                break;
-            default:
-                qg_q8_seg_dot<12, 13>(a0, a1, a2, a3, d.s[7], xp.p);
-                qg_q8_seg_dot<14, 15>(a0, a1, a2, a3, d.s[8], xp.p);
-                break;
-        }
-        S[k] = (a0 + a1) + (a2 + a3);
-    }
+    const uint4 x = make_uint4(xp.p[0], xp.p[1], xp.p[2], xp.p[3]);
     const uint32_t dw0 = h ? d.s[0].z : d.s[0].x;
     const uint32_t dw1 = h ? d.s[0].w : d.s[0].y;
-    const float dk[4] = {qg_half_lo(dw0), qg_half_hi(dw0), qg_half_lo(dw1), qg_half_hi(dw1)};
-    const float X[4] = {qg_bcast<0>(Xq), qg_bcast<4>(Xq), qg_bcast<8>(Xq), qg_bcast<12>(Xq)};
     constexpr float two24 = 16777216.0f;
+    const float dk[4] = {two24 * qg_half_lo(dw0), two24 * qg_half_hi(dw0), two24 * qg_half_lo(dw1),
+                         two24 * qg_half_hi(dw1)};
     float acc = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc = fmaf(dk[k], fmaf(two24, S[k], -128.f * X[k]), acc);
+    for (int k = 0; k < 4; ++k) {
+        uint32_t m0[8], m1[8];
+        qg_q8_signed_masks(m0, d.s[1 + 2 * k]);
+        qg_q8_signed_masks(m1, d.s[2 + 2 * k]);
+        float a[4] = {0.f, 0.f, 0.f, 0.f};
+        switch (k) {
+            case 0: qg_q8_seg8h_dot<0, false>(a, m0, x); qg_q8_seg8h_dot<2, true>(a, m1, x); break;
+            case 1: qg_q8_seg8h_dot<4, false>(a, m0, x); qg_q8_seg8h_dot<6, true>(a, m1, x); break;
+            case 2: qg_q8_seg8h_dot<8, false>(a, m0, x); qg_q8_seg8h_dot<10, true>(a, m1, x); break;
+            default: qg_q8_seg8h_dot<12, false>(a, m0, x); qg_q8_seg8h_dot<14, true>(a, m1, x); break;
+        }
+        acc = fmaf(dk[k], (a[0] + a[1]) + (a[2] + a[3]), acc);
+    }
     return acc;
 }
 
@@ -334,7 +324,7 @@ __global__ void q8_0_pack_kernel(const uint8_t* __restrict__ src, uint8_t* __res
     }
 }
 
-int validate(const void* w, const float* x, int64_t M, int64_t K) {
+qg_status validate(const void* w, const float* x, int64_t M, int64_t K) {
     if (!w || !x) return qg::fail(QG_ERR_NULL, "NULL pointer");
     if (M < 1 || M > INT32_MAX) return qg::fail(QG_ERR_SHAPE, "M=%lld out of range", (long long)M);
     if (K < 32 || K % 32 || K > (1 << 24))
@@ -360,11 +350,10 @@ Q8Prob make_prob(const void* w, const float* x, float* y, int64_t M, int64_t K) 
 // (measured, us per call: 11008 x 4096, 688 tiles: W = 1 9.43, 2 10.46, 8 9.71;
 // 4096 x 11008, 256 tiles: W = 2 10.20, 4 10.04, 8 9.95) and each K-group keeps at
 // least two half macro-blocks.
-int choose_w(const Q8Prob& P, const char* env) {
+int choose_w(const Q8Prob& P) {
     int W = 1;
     while (W < 8 && (int64_t)P.tiles * W < 640 && 4 * (2 * W) <= 2 * P.nmb + 3) W *= 2;
-    int ew = 0, eu = 0;
-    if (qg::env_pair(env, &ew, &eu) && (ew == 1 || ew == 2 || ew == 4 || ew == 8)) W = ew;
+    if (qg::launch_override().gemv_waves) W = qg::launch_override().gemv_waves;
     return W;
 }
 
@@ -374,18 +363,9 @@ size_t lm_ws_bytes(const Q8Prob& P) { return qg::align_up((size_t)P.tiles * 8, 2
 
 extern "C" {
 
-size_t qgemv_q8_0_workspace_bytes(int64_t M, int64_t K) {
-    (void)M;
-    (void)K;
-    return 0;
-}
-
-int qgemv_q8_0(const void* w, const float* x, float* y, int64_t M, int64_t K, void* ws, size_t ws_bytes,
-               qg_stream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
+qg_status qgemv_q8_0(const void* w, const float* x, float* y, int64_t M, int64_t K, qg_stream_t stream) {
     qg::clear_error();
-    int st = validate(w, x, M, K);
+    qg_status st = validate(w, x, M, K);
     if (st) return st;
     if (!y) return qg::fail(QG_ERR_NULL, "y is NULL");
     if (!qg::aligned16(y)) return qg::fail(QG_ERR_ALIGN, "y not 16-byte aligned");
@@ -394,7 +374,7 @@ int qgemv_q8_0(const void* w, const float* x, float* y, int64_t M, int64_t K, vo
     if (st) return st;
     const dim3 grid(P.tiles);
     hipStream_t s = (hipStream_t)stream;
-    switch (choose_w(P, "QG_Q8_CFG")) {
+    switch (choose_w(P)) {
         case 1: hipLaunchKernelGGL(q8_0_gemv_kernel<1>, grid, dim3(64), 0, s, P); break;
         case 2: hipLaunchKernelGGL(q8_0_gemv_kernel<2>, grid, dim3(128), 0, s, P); break;
         case 4: hipLaunchKernelGGL(q8_0_gemv_kernel<4>, grid, dim3(256), 0, s, P); break;
@@ -408,10 +388,10 @@ size_t lmhead_argmax_workspace_bytes(int64_t M, int64_t K) {
     return lm_ws_bytes(make_prob(nullptr, nullptr, nullptr, M, K));
 }
 
-int lmhead_argmax(const void* w, const float* x, int64_t M, int64_t K, void* ws, size_t ws_bytes,
+qg_status lmhead_argmax(const void* w, const float* x, int64_t M, int64_t K, void* ws, size_t ws_bytes,
                   int32_t* out_index, float* out_value, qg_stream_t stream) {
     qg::clear_error();
-    int st = validate(w, x, M, K);
+    qg_status st = validate(w, x, M, K);
     if (st) return st;
     if (!out_index) return qg::fail(QG_ERR_NULL, "out_index is NULL");
     if ((reinterpret_cast<uintptr_t>(out_index) & 3) || (reinterpret_cast<uintptr_t>(out_value) & 3))
@@ -426,7 +406,7 @@ int lmhead_argmax(const void* w, const float* x, int64_t M, int64_t K, void* ws,
     float2* partials = (float2*)ws;
     const dim3 grid(P.tiles);
     hipStream_t s = (hipStream_t)stream;
-    switch (choose_w(P, "QG_LM_CFG")) {
+    switch (choose_w(P)) {
         case 1: hipLaunchKernelGGL(lmhead_tile_kernel<1>, grid, dim3(64), 0, s, P, partials); break;
         case 2: hipLaunchKernelGGL(lmhead_tile_kernel<2>, grid, dim3(128), 0, s, P, partials); break;
         case 4: hipLaunchKernelGGL(lmhead_tile_kernel<4>, grid, dim3(256), 0, s, P, partials); break;
@@ -445,10 +425,10 @@ size_t lmhead_topk_workspace_bytes(int64_t M, int64_t K) {
     return qg::topk_ws_bytes(M);
 }
 
-int lmhead_topk(const void* w, const float* x, int64_t M, int64_t K, int k, float* logits, const qg_sampler* sampler,
+qg_status lmhead_topk(const void* w, const float* x, int64_t M, int64_t K, int k, float* logits, const qg_sampler* sampler,
                 void* ws, size_t ws_bytes, const qg_topk_out* out, qg_stream_t stream) {
     qg::clear_error();
-    int st = validate(w, x, M, K);
+    qg_status st = validate(w, x, M, K);
     if (st) return st;
     st = qg::validate_topk(M, k, sampler, out);
     if (st) return st;
@@ -464,7 +444,7 @@ int lmhead_topk(const void* w, const float* x, int64_t M, int64_t K, int k, floa
     float4* partials = (float4*)ws;
     const dim3 grid(P.tiles);
     hipStream_t s = (hipStream_t)stream;
-    switch (choose_w(P, "QG_LM_CFG")) {
+    switch (choose_w(P)) {
         case 1: hipLaunchKernelGGL(lmhead_topk_tile_kernel<1>, grid, dim3(64), 0, s, P, logits, partials); break;
         case 2: hipLaunchKernelGGL(lmhead_topk_tile_kernel<2>, grid, dim3(128), 0, s, P, logits, partials); break;
         case 4: hipLaunchKernelGGL(lmhead_topk_tile_kernel<4>, grid, dim3(256), 0, s, P, logits, partials); break;
@@ -475,7 +455,7 @@ int lmhead_topk(const void* w, const float* x, int64_t M, int64_t K, int k, floa
     return qg::launch_topk_select(ws, P.tiles, logits, M, k, sampler, *out, s);
 }
 
-int qg_pack_q8_0(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t stream) {
+qg_status qg_pack_q8_0(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t stream) {
     qg::clear_error();
     if (!src || !dst) return qg::fail(QG_ERR_NULL, "NULL pointer");
     if (M < 1 || M > INT32_MAX || K < 32 || K % 32 || K > (1 << 24))
@@ -485,7 +465,7 @@ int qg_pack_q8_0(const void* src, void* dst, int64_t M, int64_t K, qg_stream_t s
     const uint8_t* s8 = (const uint8_t*)src;
     const uint8_t* d8 = (const uint8_t*)dst;
     if (s8 < d8 + bytes && d8 < s8 + bytes) return qg::fail(QG_ERR_SHAPE, "src and dst overlap");
-    int st = qg::check_device();
+    qg_status st = qg::check_device();
     if (st) return st;
     const int blocks = (int)std::min<int64_t>(qg::ceil_div((int64_t)bytes, 256), 65536);
     hipLaunchKernelGGL(q8_0_pack_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint8_t*)src,

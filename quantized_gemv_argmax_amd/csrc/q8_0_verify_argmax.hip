@@ -286,7 +286,7 @@ __global__ __launch_bounds__(1024) void lmhead_verify_reduce_kernel(float2* __re
     }
 }
 
-int va_validate(const void* w, const float* X, int64_t ldx, int64_t M, int64_t K, int64_t N) {
+qg_status va_validate(const void* w, const float* X, int64_t ldx, int64_t M, int64_t K, int64_t N) {
     if (!w || !X) return qg::fail(QG_ERR_NULL, "NULL pointer");
     if (M < 1 || M > INT32_MAX) return qg::fail(QG_ERR_SHAPE, "M=%lld out of range", (long long)M);
     if (K < 256 || K % 256 || K > (1 << 24))
@@ -355,35 +355,6 @@ struct VdIn {
     float xs[NC];  // bias term -128 * 2^-24 * X of block i % 4 of the half, per column
 };
 
-// One quant segment of one column: masked words m (2d: bytes 0, 2 of dword d;
-// 2d + 1: bytes 1, 3) against the activation pairs of lane LA (dwords 0, 1) and LB
-// (dwords 2, 3). Opens with two wait states (masks and accumulators come from
-// ordinary VALU code); TAIL blocks end with s_nop 4 before ordinary VALU code
-// reads the accumulators.
-#define QG_SEG8H_TEXT \
-    "s_nop 1\n\t" \
-    "v_dot2c_f32_f16_dpp %0, %12, %4 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t" \
-    "v_dot2c_f32_f16_dpp %1, %13, %5 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t" \
-    "v_dot2c_f32_f16_dpp %2, %14, %6 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t" \
-    "v_dot2c_f32_f16_dpp %3, %15, %7 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t" \
-    "v_dot2c_f32_f16_dpp %0, %12, %8 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t" \
-    "v_dot2c_f32_f16_dpp %1, %13, %9 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t" \
-    "v_dot2c_f32_f16_dpp %2, %14, %10 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t" \
-    "v_dot2c_f32_f16_dpp %3, %15, %11 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
-template <int LA, bool TAIL>
-QG_DEV void seg8h_dot(float (&a)[4], const uint32_t (&m)[8], const uint4 x) {
-    if constexpr (TAIL)
-        asm(QG_SEG8H_TEXT "s_nop 4"
-            : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
-            : "v"(m[0]), "v"(m[1]), "v"(m[2]), "v"(m[3]), "v"(m[4]), "v"(m[5]), "v"(m[6]), "v"(m[7]), "v"(x.x),
-              "v"(x.y), "v"(x.z), "v"(x.w), "n"(LA), "n"(LA + 1));
-    else
-        asm(QG_SEG8H_TEXT ""
-            : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
-            : "v"(m[0]), "v"(m[1]), "v"(m[2]), "v"(m[3]), "v"(m[4]), "v"(m[5]), "v"(m[6]), "v"(m[7]), "v"(x.x),
-              "v"(x.y), "v"(x.z), "v"(x.w), "n"(LA), "n"(LA + 1));
-}
-
 // The biased bytes of a quant segment, masked in place: per dword, bytes 0, 2
 // then bytes 1, 3, each as two fp16 subnormals. One byte permutation each
 // (selector byte 0x0c gives a zero byte): 3 operations per dword.
@@ -444,10 +415,10 @@ QG_DEV void half_dot_d(float (&acc)[NC], const VdIn<NC>& d, int h, bool live) {
             }
             a[1] = a[2] = a[3] = 0.f;
             switch (k) {
-                case 0: seg8h_dot<0, false>(a, m0, d.xp[n]); seg8h_dot<2, true>(a, m1, d.xp[n]); break;
-                case 1: seg8h_dot<4, false>(a, m0, d.xp[n]); seg8h_dot<6, true>(a, m1, d.xp[n]); break;
-                case 2: seg8h_dot<8, false>(a, m0, d.xp[n]); seg8h_dot<10, true>(a, m1, d.xp[n]); break;
-                default: seg8h_dot<12, false>(a, m0, d.xp[n]); seg8h_dot<14, true>(a, m1, d.xp[n]); break;
+                case 0: qg_q8_seg8h_dot<0, false>(a, m0, d.xp[n]); qg_q8_seg8h_dot<2, true>(a, m1, d.xp[n]); break;
+                case 1: qg_q8_seg8h_dot<4, false>(a, m0, d.xp[n]); qg_q8_seg8h_dot<6, true>(a, m1, d.xp[n]); break;
+                case 2: qg_q8_seg8h_dot<8, false>(a, m0, d.xp[n]); qg_q8_seg8h_dot<10, true>(a, m1, d.xp[n]); break;
+                default: qg_q8_seg8h_dot<12, false>(a, m0, d.xp[n]); qg_q8_seg8h_dot<14, true>(a, m1, d.xp[n]); break;
             }
             acc[n] = fmaf(dk[k], (a[0] + a[1]) + (a[2] + a[3]), acc[n]);
         }
@@ -749,10 +720,10 @@ size_t lmhead_argmax_verify_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     return va_ws_bytes(M, N) + (N <= kVdMaxCols ? vd_extra_bytes(K, N) : 0);
 }
 
-int lmhead_argmax_verify(const void* w, const float* X, int64_t ldx, int64_t M, int64_t K, int64_t N, void* ws,
+qg_status lmhead_argmax_verify(const void* w, const float* X, int64_t ldx, int64_t M, int64_t K, int64_t N, void* ws,
                          size_t ws_bytes, int32_t* out_index, float* out_value, qg_stream_t stream) {
     qg::clear_error();
-    int st = va_validate(w, X, ldx, M, K, N);
+    qg_status st = va_validate(w, X, ldx, M, K, N);
     if (st) return st;
     if (!out_index) return qg::fail(QG_ERR_NULL, "out_index is NULL");
     if ((reinterpret_cast<uintptr_t>(out_index) & 3) || (reinterpret_cast<uintptr_t>(out_value) & 3))
@@ -764,8 +735,8 @@ int lmhead_argmax_verify(const void* w, const float* X, int64_t ldx, int64_t M, 
     st = qg::check_device();
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    const char* impl = getenv("QG_VA_IMPL");
-    const bool mfma = N > kVdMaxCols || (impl && std::strcmp(impl, "mfma") == 0);
+    const qg_launch_override& ov = qg::launch_override();
+    const bool mfma = N > kVdMaxCols || ov.verify_form == QG_FORM_VERIFY_MFMA;
     if (!mfma) {
         // vector-ALU form: fp16 pairs and block sums, then one wavefront per tile on
         // grids that fill the chip, four that split K otherwise (152064 x 3584, us:
@@ -790,8 +761,7 @@ int lmhead_argmax_verify(const void* w, const float* X, int64_t ldx, int64_t M, 
         D.N = (int32_t)N;
         D.tiles = (int32_t)qg::ceil_div(M, T);
         int W = D.tiles >= 1024 ? 1 : 4;
-        int ew = 0, eu = 0;
-        if (qg::env_pair("QG_VD_CFG", &ew, &eu) && (ew == 1 || ew == 4)) W = ew;
+        if (ov.verify_waves == 1 || ov.verify_waves == 4) W = ov.verify_waves;
         switch (N) {
             case 1: vd_launch<1>(D, W, s); break;
             case 2: vd_launch<2>(D, W, s); break;
@@ -827,11 +797,9 @@ int lmhead_argmax_verify(const void* w, const float* X, int64_t ldx, int64_t M, 
         W = 4;
         TW = 4;
     }
-    int ew = 0, et = 0;
-    if (qg::env_pair("QG_VA_CFG", &ew, &et)) {
-        if (ew == 4 || ew == 8) W = ew;
-        if (et == 1 || et == 2 || (et == 4 && N <= 16)) TW = et;  // four tiles of two column blocks spill
-    }
+    if (ov.verify_waves == 4 || ov.verify_waves == 8) W = ov.verify_waves;
+    const int et = ov.verify_tiles;
+    if (et == 1 || et == 2 || (et == 4 && N <= 16)) TW = et;  // four tiles of two column blocks spill
     const int key = 10 * (N > 16 ? 2 : 1) + TW;
     switch (key) {
         case 11: va_launch<1, 1>(P, W, s); break;
@@ -853,7 +821,7 @@ size_t lmhead_argmax_verify_q8_1_workspace_bytes(int64_t M, int64_t K, int64_t N
     return va_ws_bytes(M, N);
 }
 
-int lmhead_argmax_verify_q8_1(const void* w, const void* xq, int64_t M, int64_t K, int64_t N, void* ws,
+qg_status lmhead_argmax_verify_q8_1(const void* w, const void* xq, int64_t M, int64_t K, int64_t N, void* ws,
                               size_t ws_bytes, int32_t* out_index, float* out_value, qg_stream_t stream) {
     qg::clear_error();
     if (!w || !xq) return qg::fail(QG_ERR_NULL, "NULL pointer");
@@ -872,7 +840,7 @@ int lmhead_argmax_verify_q8_1(const void* w, const void* xq, int64_t M, int64_t 
     if (!ws) return qg::fail(QG_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
     if (ws_bytes < need) return qg::fail(QG_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws_bytes);
     if (!qg::aligned16(ws)) return qg::fail(QG_ERR_ALIGN, "workspace not 16-byte aligned");
-    int st = qg::check_device();
+    qg_status st = qg::check_device();
     if (st) return st;
     size_t q_off = 0, s_off = 0;
     qg::q8_1_offsets(K, &q_off, &s_off);
@@ -889,8 +857,8 @@ int lmhead_argmax_verify_q8_1(const void* w, const void* xq, int64_t M, int64_t 
     // one wavefront per tile on grids that fill the chip (vocabulary-sized heads),
     // four that split K otherwise
     int W = P.tiles >= 1024 ? 1 : 4;
-    int ew = 0, eu = 0;
-    if (qg::env_pair("QG_VQ_CFG", &ew, &eu) && (ew == 1 || ew == 4)) W = ew;
+    const qg_launch_override& ov = qg::launch_override();
+    if (ov.verify_waves == 1 || ov.verify_waves == 4) W = ov.verify_waves;
     hipStream_t s = (hipStream_t)stream;
     switch (N) {
         case 1: vq_launch<1>(P, W, s); break;

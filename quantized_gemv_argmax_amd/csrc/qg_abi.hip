@@ -1,6 +1,7 @@
 // C ABI plumbing: status strings, per-thread error text, device check, workspace
 // clearing.
 #include <algorithm>
+#include <initializer_list>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -12,12 +13,12 @@ namespace qg {
 
 static thread_local char g_err[512] = "";
 
-int fail(int status, const char* fmt, ...) {
+qg_status fail(int status, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
     vsnprintf(g_err, sizeof(g_err), fmt, ap);
     va_end(ap);
-    return status;
+    return (qg_status)status;
 }
 
 void clear_error() { g_err[0] = 0; }
@@ -28,7 +29,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 static int g_dev_ok[64];
 static std::mutex g_dev_mu;
 
-int check_device() {
+qg_status check_device() {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(QG_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
@@ -46,22 +47,15 @@ int check_device() {
     return QG_OK;
 }
 
-int launch_status(const char* what) {
+qg_status launch_status(const char* what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_ERR_DEVICE, "%s launch failed: %s", what, hipGetErrorString(e));
     return QG_OK;
 }
 
-bool env_pair(const char* name, int* a, int* b) {
-    const char* s = getenv(name);
-    if (!s || !*s) return false;
-    int x = 0, y = 0;
-    const int got = sscanf(s, "%d,%d", &x, &y);
-    if (got < 1) return false;
-    *a = x;
-    *b = got == 2 ? y : 0;  // a single number sets the first value only
-    return true;
-}
+static thread_local qg_launch_override g_override = {};
+
+const qg_launch_override& launch_override() { return g_override; }
 
 }  // namespace qg
 
@@ -91,6 +85,46 @@ const char* qg_status_string(int s) {
 
 const char* qg_last_error(void) { return qg::g_err; }
 
+qg_status qg_set_launch_override(const qg_launch_override* o) {
+    qg::clear_error();
+    if (!o) {
+        qg::g_override = qg_launch_override{};
+        return QG_OK;
+    }
+    const qg_launch_override& v = *o;
+    auto in = [](int x, std::initializer_list<int> ok) {
+        if (x == 0) return true;
+        for (int k : ok)
+            if (x == k) return true;
+        return false;
+    };
+    if (!in(v.gemv_waves, {1, 2, 4, 8}))
+        return (qg_status)qg::fail(QG_ERR_SHAPE, "gemv_waves=%d not in {0, 1, 2, 4, 8}", v.gemv_waves);
+    if (!in(v.smalln_form, {QG_FORM_SMALLN_REGS, QG_FORM_SMALLN_LDS, QG_FORM_SMALLN_LDS1, QG_FORM_SMALLN_DOT}))
+        return (qg_status)qg::fail(QG_ERR_SHAPE, "smalln_form=%d unknown", v.smalln_form);
+    if (!in(v.smalln_waves, {1, 2, 4, 8}))
+        return (qg_status)qg::fail(QG_ERR_SHAPE, "smalln_waves=%d not in {0, 1, 2, 4, 8}", v.smalln_waves);
+    if (!in(v.smalln_tiles, {1, 2, 4}))
+        return (qg_status)qg::fail(QG_ERR_SHAPE, "smalln_tiles=%d not in {0, 1, 2, 4}", v.smalln_tiles);
+    if (!in(v.smalln_depth, {2, 3, 4}))
+        return (qg_status)qg::fail(QG_ERR_SHAPE, "smalln_depth=%d not in {0, 2, 3, 4}", v.smalln_depth);
+    if (!in(v.verify_form, {QG_FORM_VERIFY_MFMA, QG_FORM_VERIFY_DOT}))
+        return (qg_status)qg::fail(QG_ERR_SHAPE, "verify_form=%d unknown", v.verify_form);
+    if (!in(v.verify_waves, {1, 4, 8}))
+        return (qg_status)qg::fail(QG_ERR_SHAPE, "verify_waves=%d not in {0, 1, 4, 8}", v.verify_waves);
+    if (!in(v.verify_tiles, {1, 2, 4}))
+        return (qg_status)qg::fail(QG_ERR_SHAPE, "verify_tiles=%d not in {0, 1, 2, 4}", v.verify_tiles);
+    qg::g_override = v;
+    return QG_OK;
+}
+
+qg_status qg_get_launch_override(qg_launch_override* o) {
+    qg::clear_error();
+    if (!o) return (qg_status)qg::fail(QG_ERR_NULL, "NULL pointer");
+    *o = qg::g_override;
+    return QG_OK;
+}
+
 size_t qg_q4k_bytes(int64_t M, int64_t K) {
     if (M < 1 || K < 256 || K % 256) return 0;
     return (size_t)M * (size_t)(K / 256) * 144u;
@@ -101,12 +135,12 @@ size_t qg_q8_0_bytes(int64_t M, int64_t K) {
     return (size_t)M * (size_t)(K / 32) * 34u;
 }
 
-int qg_workspace_clear(void* ws, size_t bytes, qg_stream_t stream) {
+qg_status qg_workspace_clear(void* ws, size_t bytes, qg_stream_t stream) {
     qg::clear_error();
     if (bytes == 0) return QG_OK;
     if (!ws) return qg::fail(QG_ERR_NULL, "workspace is NULL");
     if (!qg::aligned16(ws)) return qg::fail(QG_ERR_ALIGN, "workspace not 16-byte aligned");
-    int st = qg::check_device();
+    qg_status st = qg::check_device();
     if (st) return st;
     size_t n16 = bytes / 16;
     int ntail = (int)(bytes % 16);

@@ -118,44 +118,6 @@ QG_DEV void qg_q4_seg_dot(float& lo0, float& hi0, float& lo1, float& hi1, const 
           "v"(x[6]), "v"(x[7]), "n"(LA), "n"(LB));
 }
 
-// Q8_0: one 16-byte quant segment (16 int8) against the activation pairs of lanes
-// LA (dwords 0, 1: pairs x[0..3]) and LB (dwords 2, 3: pairs x[0..3]). The quants
-// are biased to bytes (q ^ 0x80 = q + 128), bytes 0,2 and 1,3 of each dword masked
-// in place and read as fp16 subnormals ((q + 128) * 2^-24). Dwords 0 and 2 feed
-// a0 / a1, dwords 1 and 3 feed a2 / a3.
-template <int LA, int LB>
-QG_DEV void qg_q8_seg_dot(float& a0, float& a1, float& a2, float& a3, const uint4 q, const uint32_t (&x)[4]) {
-    uint32_t u0, m0, t0, n0, u1, m1, t1, n1;
-    asm("v_xor_b32 %4, 0x80808080, %12\n\t"
-        "v_and_b32 %5, 0xff00ff, %4\n\t"
-        "v_lshrrev_b32 %6, 8, %4\n\t"
-        "v_and_b32 %7, 0xff00ff, %6\n\t"
-        "v_xor_b32 %8, 0x80808080, %13\n\t"
-        "v_and_b32 %9, 0xff00ff, %8\n\t"
-        "v_lshrrev_b32 %10, 8, %8\n\t"
-        "v_and_b32 %11, 0xff00ff, %10\n\t"
-        "v_dot2c_f32_f16_dpp %0, %16, %5 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %1, %17, %7 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
-        "v_xor_b32 %4, 0x80808080, %14\n\t"
-        "v_and_b32 %5, 0xff00ff, %4\n\t"
-        "v_lshrrev_b32 %6, 8, %4\n\t"
-        "v_and_b32 %7, 0xff00ff, %6\n\t"
-        "v_dot2c_f32_f16_dpp %2, %18, %9 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %3, %19, %11 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
-        "v_xor_b32 %8, 0x80808080, %15\n\t"
-        "v_and_b32 %9, 0xff00ff, %8\n\t"
-        "v_lshrrev_b32 %10, 8, %8\n\t"
-        "v_and_b32 %11, 0xff00ff, %10\n\t"
-        "v_dot2c_f32_f16_dpp %0, %16, %5 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %1, %17, %7 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %2, %18, %9 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %3, %19, %11 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 4"
-        : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "=&v"(u0), "=&v"(m0), "=&v"(t0), "=&v"(n0), "=&v"(u1), "=&v"(m1),
-          "=&v"(t1), "=&v"(n1)
-        : "v"(q.x), "v"(q.y), "v"(q.z), "v"(q.w), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "n"(LA), "n"(LB));
-}
-
 // Eight fp16x2 pairs (round to nearest even) from four float4, in the order
 // (a.x,a.z) (a.y,a.w) (b.x,b.z) (b.y,b.w) (c...) (d...), then two wait states.
 struct QgPairs8 {
@@ -228,35 +190,6 @@ QG_DEV float qg_sum_rows4(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K combination without fences or waiting. KS workgroups (KS a power of
-// two) each hold a partial sum of one output element; they meet pairwise in a
-// fixed tree, level by level: the partners of a pair each exchange
-// (1 << 32 | bits of their value) into the pair's 64-bit slot. The first to
-// arrive finds the slot idle (high word 0) and is done; the second finds its
-// partner's value in what the exchange returned, adds it (fp32 addition is
-// commutative, so the sum is the same whichever comes second), returns the slot
-// to idle and goes on to the next level. All communication is the value carried
-// by single atomic exchanges on one location each, so no fence is involved and
-// the sum has a fixed association ((p0 + p1) + (p2 + p3)): results do not depend
-// on arrival order. `slot` is this element's slot in the first of KS - 1 slot
-// arrays, `stride` the distance (in slots) between arrays; every slot is idle
-// (zero) before the call and is idle again after it. Returns true in the one
-// caller left holding the complete sum.
-QG_DEV bool qg_splitk_combine(float& v, unsigned long long* slot, int64_t stride, int ks, int KS) {
-    int base = 0;
-    for (int span = 1; span < KS; span <<= 1) {
-        unsigned long long* p = slot + (int64_t)(base + ks / (2 * span)) * stride;
-        const unsigned long long mine = (1ull << 32) | (unsigned long long)__builtin_bit_cast(uint32_t, v);
-        const unsigned long long old = __hip_atomic_exchange(p, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((old >> 32) == 0) return false;
-        v = v + __builtin_bit_cast(float, (uint32_t)old);
-        __hip_atomic_store(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        base += KS / (2 * span);
-    }
-    return true;
-}
-
-// ---------------------------------------------------------------------------
 // fp16 matrix-core operands (v_mfma_f32_16x16x32_f16: lane l holds
 // A[l % 16][8 (l / 16) + 0..7], B[8 (l / 16) + 0..7][l % 16] and
 // D[4 (l / 16) + e][l % 16], e = 0..3).
@@ -265,6 +198,69 @@ typedef _Float16 qg_h2 __attribute__((ext_vector_type(2)));
 typedef float qg_f4 __attribute__((ext_vector_type(4)));
 typedef unsigned int qg_u4v __attribute__((ext_vector_type(4)));
 typedef unsigned int qg_u2v __attribute__((ext_vector_type(2)));
+
+// Sum of the eight fp16 values held in four packed pairs, in fp32 and a fixed
+// order (a, b, c, d): each step is one v_dot2_f32_f16 against (1, 1), which adds
+// both halves of a pair to the running sum. Used for the per-block activation
+// sums, so that they are taken over exactly the values the dot products use.
+QG_DEV float qg_sum_pairs4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const qg_h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    float s = __builtin_amdgcn_fdot2(__builtin_bit_cast(qg_h2, a), one, 0.0f, false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(qg_h2, b), one, s, false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(qg_h2, c), one, s, false);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(qg_h2, d), one, s, false);
+}
+
+// Q8_0 quant segments (16 int8 quants q) as signed fp16 subnormals q * 2^-24,
+// two per word: per dword, the quants are biased to bytes (q ^ 0x80 = q + 128),
+// bytes 0, 2 and then 1, 3 are moved into the low bytes of the two halves by one
+// byte permutation each (selector byte 0x0c gives a zero byte), and one packed
+// fp16 addition of -128 * 2^-24 (bits 0x8080) to both halves takes the bias off
+// exactly, (q + 128) * 2^-24 - 128 * 2^-24 = q * 2^-24 being representable. So
+// no activation sum is needed to remove a bias, and a product of the signed
+// quants with the fp16 activations is exact: per dword 5 operations for 4
+// weights. m[2d] holds bytes 0, 2 of dword d, m[2d + 1] bytes 1, 3.
+QG_DEV uint32_t qg_f16x2_add(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(qg_h2, a) + __builtin_bit_cast(qg_h2, b));
+}
+QG_DEV void qg_q8_signed_masks(uint32_t (&m)[8], const uint4 q) {
+    const uint32_t w[4] = {q.x ^ 0x80808080u, q.y ^ 0x80808080u, q.z ^ 0x80808080u, q.w ^ 0x80808080u};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        m[2 * d] = qg_f16x2_add(__builtin_amdgcn_perm(w[d], w[d], 0x0c020c00u), 0x80808080u);
+        m[2 * d + 1] = qg_f16x2_add(__builtin_amdgcn_perm(w[d], w[d], 0x0c030c01u), 0x80808080u);
+    }
+}
+
+// One Q8_0 quant segment of 16 weights: masked words m (2d: bytes 0, 2 of dword
+// d; 2d + 1: bytes 1, 3) against the activation pairs x = ((x0, x2), (x1, x3),
+// (x4, x6), (x5, x7)) of lane LA (dwords 0, 1) and lane LA + 1 (dwords 2, 3) of
+// this DPP row. Opens with two wait states (masks and accumulators come from
+// ordinary VALU code); TAIL blocks end with s_nop 4 before ordinary VALU code
+// reads the accumulators.
+#define QG_SEG8H_TEXT \
+    "s_nop 1\n\t" \
+    "v_dot2c_f32_f16_dpp %0, %12, %4 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t" \
+    "v_dot2c_f32_f16_dpp %1, %13, %5 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t" \
+    "v_dot2c_f32_f16_dpp %2, %14, %6 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t" \
+    "v_dot2c_f32_f16_dpp %3, %15, %7 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n\t" \
+    "v_dot2c_f32_f16_dpp %0, %12, %8 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t" \
+    "v_dot2c_f32_f16_dpp %1, %13, %9 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t" \
+    "v_dot2c_f32_f16_dpp %2, %14, %10 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t" \
+    "v_dot2c_f32_f16_dpp %3, %15, %11 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
+template <int LA, bool TAIL>
+QG_DEV void qg_q8_seg8h_dot(float (&a)[4], const uint32_t (&m)[8], const uint4 x) {
+    if constexpr (TAIL)
+        asm(QG_SEG8H_TEXT "s_nop 4"
+            : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+            : "v"(m[0]), "v"(m[1]), "v"(m[2]), "v"(m[3]), "v"(m[4]), "v"(m[5]), "v"(m[6]), "v"(m[7]), "v"(x.x),
+              "v"(x.y), "v"(x.z), "v"(x.w), "n"(LA), "n"(LA + 1));
+    else
+        asm(QG_SEG8H_TEXT ""
+            : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+            : "v"(m[0]), "v"(m[1]), "v"(m[2]), "v"(m[3]), "v"(m[4]), "v"(m[5]), "v"(m[6]), "v"(m[7]), "v"(x.x),
+              "v"(x.y), "v"(x.z), "v"(x.w), "n"(LA), "n"(LA + 1));
+}
 
 // Two floats as an fp16 pair, rounded to nearest even.
 QG_DEV uint32_t qg_pk_rne(float a, float b) {

@@ -435,7 +435,7 @@ size_t topk_ws_bytes(int64_t M) {
     return ws_layout(M).total;
 }
 
-int validate_topk(int64_t M, int k, const qg_sampler* sampler, const qg_topk_out* out) {
+qg_status validate_topk(int64_t M, int k, const qg_sampler* sampler, const qg_topk_out* out) {
     if (!out) return fail(QG_ERR_NULL, "output descriptor is NULL");
     if (!out->index) return fail(QG_ERR_NULL, "out->index is NULL");
     if (M < 1 || M > QG_TOPK_MAX_ROWS)
@@ -455,7 +455,7 @@ int validate_topk(int64_t M, int k, const qg_sampler* sampler, const qg_topk_out
     return QG_OK;
 }
 
-int launch_topk_select(void* ws, int tiles, const float* logits, int64_t M, int k, const qg_sampler* sampler,
+qg_status launch_topk_select(void* ws, int tiles, const float* logits, int64_t M, int k, const qg_sampler* sampler,
                        const qg_topk_out& out, hipStream_t s) {
     const WsLayout L = ws_layout(M);
     uint8_t* w8 = (uint8_t*)ws;
@@ -464,7 +464,7 @@ int launch_topk_select(void* ws, int tiles, const float* logits, int64_t M, int 
     float2* glse = (float2*)(w8 + L.glse);
     hipLaunchKernelGGL(topk_group_kernel, dim3(groups), dim3(kWG), 0, s, (float4*)(w8 + L.partials), tiles, k, gkeys,
                        glse);
-    int st = launch_status("top-k selection (groups)");
+    qg_status st = launch_status("top-k selection (groups)");
     if (st) return st;
     FinArgs a{};
     a.gkeys = gkeys;
@@ -494,11 +494,11 @@ extern "C" {
 
 size_t logits_topk_workspace_bytes(int64_t M) { return qg::topk_ws_bytes(M); }
 
-int logits_topk(const float* logits, int64_t M, int k, const qg_sampler* sampler, void* ws, size_t ws_bytes,
+qg_status logits_topk(const float* logits, int64_t M, int k, const qg_sampler* sampler, void* ws, size_t ws_bytes,
                 const qg_topk_out* out, qg_stream_t stream) {
     qg::clear_error();
     if (!logits) return qg::fail(QG_ERR_NULL, "logits is NULL");
-    int st = qg::validate_topk(M, k, sampler, out);
+    qg_status st = qg::validate_topk(M, k, sampler, out);
     if (st) return st;
     if (!qg::aligned16(logits)) return qg::fail(QG_ERR_ALIGN, "logits not 16-byte aligned");
     const size_t need = qg::topk_ws_bytes(M);

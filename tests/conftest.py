@@ -27,3 +27,16 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _reset_launch_override():
+    """Every test starts and ends with the library's automatic launch choices (a
+    test may force forms with quantized_gemv_argmax_amd.launch_override(...).set())."""
+    yield
+    try:
+        import quantized_gemv_argmax_amd as qg
+        if qg._lib is not None:
+            qg.lib().qg_set_launch_override(None)
+    except Exception:
+        pass

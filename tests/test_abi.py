@@ -2,6 +2,7 @@
 header declares, and its host-side validation returns the documented status
 codes without launching anything (no GPU needed)."""
 import ctypes
+import re
 
 import pytest
 
@@ -18,7 +19,83 @@ def L():
 
 
 def test_loads_and_version(L):
-    assert L.qg_abi_version() == 1
+    assert L.qg_abi_version() == 2
+
+
+def _declarations():
+    """(return type, name, parameter list) of every function include/qgemv.h declares,
+    parsed from the header text (comments stripped)."""
+    text = open(qg.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    out = {}
+    for m in re.finditer(r"(?:(?<=[;}])|^)\s*((?:const\s+)?[A-Za-z_][A-Za-z_0-9]*\s*\**)\s*([a-z_][a-z_0-9]*)\s*"
+                         r"\(([^;{]*?)\)\s*;", text, flags=re.S | re.M):
+        ret, name, params = m.group(1).strip(), m.group(2), " ".join(m.group(3).split())
+        if name in ("if", "while", "return", "sizeof", "defined"):
+            continue
+        plist = [] if params in ("", "void") else [p.strip() for p in params.split(",")]
+        out[name] = (ret, plist)
+    return out
+
+
+# The boundary the survey's scope table fixes (names, return types and argument
+# counts); the library may export more.
+SCOPE_BOUNDARY = {
+    "qg_abi_version": ("int", 0),
+    "qg_status_string": ("const char*", 1),
+    "qg_last_error": ("const char*", 0),
+    "qg_q4k_bytes": ("size_t", 2),
+    "qg_q8_0_bytes": ("size_t", 2),
+    "qg_pack_q4k": ("qg_status", 5),
+    "qg_pack_q8_0": ("qg_status", 5),
+    "qgemv_q4k": ("qg_status", 6),
+    "qgemv_q8_0": ("qg_status", 6),
+    "qgemm_q4k_smalln": ("qg_status", 9),
+    "lmhead_argmax_workspace_bytes": ("size_t", 2),
+    "lmhead_argmax": ("qg_status", 9),
+}
+
+
+def test_scope_boundary_signatures():
+    decl = _declarations()
+    for name, (ret, nargs) in SCOPE_BOUNDARY.items():
+        assert name in decl, name
+        r, params = decl[name]
+        assert r.replace(" ", "") == ret.replace(" ", ""), (name, r)
+        assert len(params) == nargs, (name, params)
+    # the products that need no workspace take none
+    for name in ("qgemv_q4k", "qgemv_q8_0", "qgemm_q4k_smalln", "qgemv_q6k", "qgemv_q4k_q8_1",
+                 "qgemm_q4k_q8_1_smalln", "qgemv_q4k_batch", "qgemm_q4k_smalln_batch"):
+        assert not any("workspace" in p for p in decl[name][1]), name
+        assert decl[name][1][-1].startswith("qg_stream_t"), name
+    assert decl["qgemv_q4k"][1] == ["const void* w_packed", "const float* x", "float* y", "int64_t M", "int64_t K",
+                                    "qg_stream_t stream"]
+    assert decl["qgemm_q4k_smalln"][1][:3] == ["const void* w_packed", "const float* X", "int64_t ldx"]
+    assert decl["lmhead_argmax"][1][6:8] == ["int32_t* out_index", "float* out_value"]
+    # every entry point that launches work returns a status
+    for name, (r, params) in decl.items():
+        if params and params[-1].startswith("qg_stream_t"):
+            assert r == "qg_status", name
+
+
+def test_every_declaration_cites_its_passage():
+    # each function declaration is preceded, within its block comment, by a
+    # citation of the page section that defines it (or is a helper / override)
+    text = open(qg.HEADER).read()
+    blocks = re.split(r"\n(?=/\*)", text)
+    cited = set()
+    for b in blocks:
+        m = re.match(r"/\*(.*?)\*/(.*)", b, flags=re.S)
+        if not m:
+            continue
+        comment, body = m.group(1), m.group(2)
+        names = re.findall(r"\b([a-z_][a-z_0-9]*)\s*\(", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+        if re.search(r"README|Why Local LLMs|Building a Fully Custom|tests and measurements|cannot allocate|"
+                     r"host only|Size in bytes|Zero-fill", comment):
+            cited.update(names)
+    for name in _declarations():
+        assert name in cited, name
 
 
 def test_every_header_function_is_exported(L):
@@ -47,16 +124,13 @@ def test_sizes(L):
 
 def test_gemv_validation(L):
     f = L.qgemv_q4k
-    assert f(None, A, B, 64, 256, None, 0, None) == ENULL
+    assert f(None, A, B, 64, 256, None) == ENULL
     assert "NULL" in qg.last_error()
-    assert f(C, A, B, 64, 300, None, 0, None) == ESHAPE
-    assert f(C, A, B, 0, 256, None, 0, None) == ESHAPE
-    assert f(C, A, B, 2**31, 256, None, 0, None) == ESHAPE
-    assert f(C + 4, A, B, 64, 256, None, 0, None) == EALIGN
-    assert f(C, A + 8, B, 64, 256, None, 0, None) == EALIGN
-    # no workspace is needed by the GEMV entry points
-    assert L.qgemv_q4k_workspace_bytes(3584, 3584) == 0
-    assert L.qgemv_q8_0_workspace_bytes(11008, 4096) == 0
+    assert f(C, A, B, 64, 300, None) == ESHAPE
+    assert f(C, A, B, 0, 256, None) == ESHAPE
+    assert f(C, A, B, 2**31, 256, None) == ESHAPE
+    assert f(C + 4, A, B, 64, 256, None) == EALIGN
+    assert f(C, A + 8, B, 64, 256, None) == EALIGN
 
 
 def test_batch_validation(L):
@@ -64,18 +138,18 @@ def test_batch_validation(L):
     arr = (P * 9)()
     for i in range(9):
         arr[i] = P(C, A, B, 64, 256)
-    assert L.qgemv_q4k_batch(arr, 0, None, 0, None) == ESHAPE
-    assert L.qgemv_q4k_batch(arr, 9, None, 0, None) == ESHAPE
+    assert L.qgemv_q4k_batch(arr, 0, None) == ESHAPE
+    assert L.qgemv_q4k_batch(arr, 9, None) == ESHAPE
     arr[1] = P(C, None, B, 64, 256)
-    assert L.qgemv_q4k_batch(arr, 2, None, 0, None) == ENULL
-    assert L.qgemv_q4k_batch(None, 1, None, 0, None) == ENULL
+    assert L.qgemv_q4k_batch(arr, 2, None) == ENULL
+    assert L.qgemv_q4k_batch(None, 1, None) == ENULL
     arr[1] = P(C, A, B, 64, 1000)
-    assert L.qgemv_q4k_batch(arr, 2, None, 0, None) == ESHAPE
+    assert L.qgemv_q4k_batch(arr, 2, None) == ESHAPE
 
 
 def test_q8_0_and_lmhead_validation(L):
-    assert L.qgemv_q8_0(C, A, B, 10, 33, None, 0, None) == ESHAPE
-    assert L.qgemv_q8_0(C, A, None, 10, 64, None, 0, None) == ENULL
+    assert L.qgemv_q8_0(C, A, B, 10, 33, None) == ESHAPE
+    assert L.qgemv_q8_0(C, A, None, 10, 64, None) == ENULL
     assert L.lmhead_argmax(C, A, 1000, 3584, 0x40000, 1 << 20, None, None, None) == ENULL
     assert L.lmhead_argmax(C, A, 1000, 3584, None, 0, B, None, None) == EWS
     assert L.lmhead_argmax(C, A, 1000, 3584, 0x40000, 16, B, None, None) == EWS
@@ -86,28 +160,15 @@ def test_q8_0_and_lmhead_validation(L):
 
 def test_smalln_validation(L):
     f = L.qgemm_q4k_smalln
-    assert f(C, A, 256, B, 64, 64, 256, 0, None, 0, None) == ESHAPE
-    assert f(C, A, 256, B, 64, 64, 256, 33, None, 0, None) == ESHAPE
-    assert f(C, A, 128, B, 64, 64, 256, 5, None, 0, None) == ESHAPE   # ldx < K
-    assert f(C, A, 256, B, 60, 64, 256, 5, None, 0, None) == ESHAPE   # ldy < M
-    assert f(C, A, 258, B, 64, 64, 256, 5, None, 0, None) == ESHAPE   # ldx % 4
-    assert f(C, A + 4, 256, B, 64, 64, 256, 5, None, 0, None) == EALIGN
+    assert f(C, A, 256, B, 64, 64, 256, 0, None) == ESHAPE
+    assert f(C, A, 256, B, 64, 64, 256, 33, None) == ESHAPE
+    assert f(C, A, 128, B, 64, 64, 256, 5, None) == ESHAPE   # ldx < K
+    assert f(C, A, 256, B, 60, 64, 256, 5, None) == ESHAPE   # ldy < M
+    assert f(C, A, 258, B, 64, 64, 256, 5, None) == ESHAPE   # ldx % 4
+    assert f(C, A + 4, 256, B, 64, 64, 256, 5, None) == EALIGN
     # the activations must fit one 2^31-byte buffer range
-    assert f(C, A, 1 << 26, B, 64, 64, 256, 32, None, 0, None) == ESHAPE
-    assert f(C, A, 1 << 26, B, 64, 64, 256, 1, None, 0, None) != ESHAPE or "X extent" not in qg.last_error()
-    assert L.qgemm_q4k_smalln_workspace_bytes(3584, 3584, 5) == 0
-
-
-def test_smalln_split_k_workspace(L, monkeypatch):
-    # with K split between two workgroups per row block, their partial sums meet
-    # in one array of 8-byte slots per output element
-    monkeypatch.setenv("QG_SN_KS", "2")
-    f = L.qgemm_q4k_smalln
-    assert L.qgemm_q4k_smalln_workspace_bytes(3584, 3584, 5) == 3584 * 5 * 8
-    # a call that needs a workspace and gets none (or too little) is refused
-    # before any launch
-    assert f(C, A, 3584, B, 3584, 3584, 3584, 5, None, 0, None) == EWS
-    assert f(C, A, 3584, B, 3584, 3584, 3584, 5, A, 3584 * 5 * 8 - 8, None) == EWS
+    assert f(C, A, 1 << 26, B, 64, 64, 256, 32, None) == ESHAPE
+    assert f(C, A, 1 << 26, B, 64, 64, 256, 1, None) != ESHAPE or "X extent" not in qg.last_error()
 
 
 def test_pack_validation(L):
@@ -123,7 +184,7 @@ def test_valid_call_without_gpu_reports_device_error(L):
     import torch
     if torch.cuda.is_available():
         pytest.skip("GPU present")
-    st = L.qgemv_q4k(C, A, B, 64, 256, None, 0, None)
+    st = L.qgemv_q4k(C, A, B, 64, 256, None)
     assert st in (EDEV, EUNSUP)
 
 
@@ -149,14 +210,13 @@ def test_q6k_sizes_and_validation(L):
     assert L.qg_q6k_bytes(10, 300) == 0
     assert L.qg_q6k_bytes(0, 256) == 0
     f = L.qgemv_q6k
-    assert f(None, A, B, 64, 256, None, 0, None) == ENULL
-    assert f(C, A, B, 64, 300, None, 0, None) == ESHAPE
-    assert f(C, A, B, 0, 256, None, 0, None) == ESHAPE
-    assert f(C, A, B, 2**31 - 8, 256, None, 0, None) == ESHAPE
-    assert f(C, A, B, 64, 2**25, None, 0, None) == ESHAPE
-    assert f(C + 2, A, B, 64, 256, None, 0, None) == EALIGN
-    assert f(C, A, B + 4, 64, 256, None, 0, None) == EALIGN
-    assert L.qgemv_q6k_workspace_bytes(3584, 18944) == 0
+    assert f(None, A, B, 64, 256, None) == ENULL
+    assert f(C, A, B, 64, 300, None) == ESHAPE
+    assert f(C, A, B, 0, 256, None) == ESHAPE
+    assert f(C, A, B, 2**31 - 8, 256, None) == ESHAPE
+    assert f(C, A, B, 64, 2**25, None) == ESHAPE
+    assert f(C + 2, A, B, 64, 256, None) == EALIGN
+    assert f(C, A, B + 4, 64, 256, None) == EALIGN
     assert L.qg_pack_q6k(None, A, 64, 256, None) == ENULL
     assert L.qg_pack_q6k(A, B, 64, 100, None) == ESHAPE
     assert L.qg_pack_q6k(A, A + 16, 64, 256, None) == ESHAPE  # overlap
@@ -212,11 +272,10 @@ def test_q8_1_validation(L):
     assert L.qg_quantize_q8_1(A + 4, 256, B, None) == EALIGN
     assert L.qg_quantize_q8_1(A, 256, A + 512, None) == ESHAPE  # overlap
     f = L.qgemv_q4k_q8_1
-    assert f(C, None, B, 64, 256, None, 0, None) == ENULL
-    assert f(C, A, B, 64, 300, None, 0, None) == ESHAPE
-    assert f(C, A, B, 0, 256, None, 0, None) == ESHAPE
-    assert f(C, A + 8, B, 64, 256, None, 0, None) == EALIGN
-    assert L.qgemv_q4k_q8_1_workspace_bytes(3584, 3584) == 0
+    assert f(C, None, B, 64, 256, None) == ENULL
+    assert f(C, A, B, 64, 300, None) == ESHAPE
+    assert f(C, A, B, 0, 256, None) == ESHAPE
+    assert f(C, A + 8, B, 64, 256, None) == EALIGN
 
 
 def test_q8_1_batch_validation(L):
@@ -225,50 +284,83 @@ def test_q8_1_batch_validation(L):
     for i in range(9):
         arr[i] = P(C, A, B, 64, 256)
     f = L.qgemv_q4k_q8_1_batch
-    assert f(arr, 0, None, 0, None) == ESHAPE
-    assert f(arr, 9, None, 0, None) == ESHAPE
-    assert f(None, 1, None, 0, None) == ENULL
+    assert f(arr, 0, None) == ESHAPE
+    assert f(arr, 9, None) == ESHAPE
+    assert f(None, 1, None) == ENULL
     arr[1] = P(C, None, B, 64, 256)
-    assert f(arr, 2, None, 0, None) == ENULL
+    assert f(arr, 2, None) == ENULL
     arr[1] = P(C, A, B, 64, 1000)
-    assert f(arr, 2, None, 0, None) == ESHAPE
+    assert f(arr, 2, None) == ESHAPE
     arr[1] = P(C, A + 4, B, 64, 256)
-    assert f(arr, 2, None, 0, None) == EALIGN
-    assert L.qgemv_q4k_q8_1_batch_workspace_bytes(arr, 2) == 0
+    assert f(arr, 2, None) == EALIGN
 
 
 def test_q8_1_smalln_validation(L):
     f = L.qgemm_q4k_q8_1_smalln
     #  w, xq, Y, ldy, M, K, N
-    assert f(C, None, B, 64, 64, 256, 5, None, 0, None) == ENULL
-    assert f(C, A, B, 64, 64, 256, 0, None, 0, None) == ESHAPE    # N < 1
-    assert f(C, A, B, 64, 64, 256, 9, None, 0, None) == ESHAPE    # N > 8
-    assert f(C, A, B, 64, 64, 300, 5, None, 0, None) == ESHAPE    # K % 256
-    assert f(C, A, B, 60, 64, 256, 5, None, 0, None) == ESHAPE    # ldy < M
-    assert f(C, A, B, 66, 64, 256, 5, None, 0, None) == ESHAPE    # ldy % 4
-    assert f(C, A, B, 64, 0, 256, 5, None, 0, None) == ESHAPE     # M < 1
-    assert f(C, A + 8, B, 64, 64, 256, 5, None, 0, None) == EALIGN
-    assert L.qgemm_q4k_q8_1_smalln_workspace_bytes(3584, 3584, 5) == 0
+    assert f(C, None, B, 64, 64, 256, 5, None) == ENULL
+    assert f(C, A, B, 64, 64, 256, 0, None) == ESHAPE    # N < 1
+    assert f(C, A, B, 64, 64, 256, 9, None) == ESHAPE    # N > 8
+    assert f(C, A, B, 64, 64, 300, 5, None) == ESHAPE    # K % 256
+    assert f(C, A, B, 60, 64, 256, 5, None) == ESHAPE    # ldy < M
+    assert f(C, A, B, 66, 64, 256, 5, None) == ESHAPE    # ldy % 4
+    assert f(C, A, B, 64, 0, 256, 5, None) == ESHAPE     # M < 1
+    assert f(C, A + 8, B, 64, 64, 256, 5, None) == EALIGN
     P = qg._GemmQ81Problem
     arr = (P * 9)()
     for i in range(9):
         arr[i] = P(C, A, B, 64, 64, 256, 5)
     g = L.qgemm_q4k_q8_1_smalln_batch
-    assert g(arr, 0, None, 0, None) == ESHAPE
-    assert g(arr, 9, None, 0, None) == ESHAPE
-    assert g(None, 1, None, 0, None) == ENULL
+    assert g(arr, 0, None) == ESHAPE
+    assert g(arr, 9, None) == ESHAPE
+    assert g(None, 1, None) == ENULL
     arr[1] = P(C, A, None, 64, 64, 256, 5)
-    assert g(arr, 2, None, 0, None) == ENULL
-    assert L.qgemm_q4k_q8_1_smalln_batch_workspace_bytes(arr, 2) == 0
+    assert g(arr, 2, None) == ENULL
 
 
-def test_smalln_dot_form_validation_unchanged(L, monkeypatch):
-    # forcing the dot form does not relax the small-N argument checks
-    monkeypatch.setenv("QG_SN_IMPL", "dot")
+def test_smalln_forced_forms_keep_validation(L):
+    # forcing a form does not relax the small-N argument checks
     f = L.qgemm_q4k_smalln
-    assert f(C, A, 256, B, 64, 64, 256, 0, None, 0, None) == ESHAPE
-    assert f(C, A, 128, B, 64, 64, 256, 3, None, 0, None) == ESHAPE   # ldx < K
-    assert f(C, A + 4, 256, B, 64, 64, 256, 3, None, 0, None) == EALIGN
+    for form in (qg.FORM_SMALLN_DOT, qg.FORM_SMALLN_REGS, qg.FORM_SMALLN_LDS, qg.FORM_SMALLN_LDS1):
+        with qg.launch_override(smalln_form=form):
+            assert f(C, A, 256, B, 64, 64, 256, 0, None) == ESHAPE
+            assert f(C, A, 128, B, 64, 64, 256, 3, None) == ESHAPE   # ldx < K
+            assert f(C, A + 4, 256, B, 64, 64, 256, 3, None) == EALIGN
+    assert qg.get_launch_override()["smalln_form"] == 0
+
+
+def test_launch_override_validation(L):
+    O = qg._LaunchOverride
+    assert L.qg_set_launch_override(None) == OK
+    for field, bad in [("gemv_waves", 3), ("gemv_waves", 16), ("smalln_form", 5), ("smalln_waves", 16),
+                       ("smalln_tiles", 3), ("smalln_depth", 1), ("verify_form", 3), ("verify_waves", 2),
+                       ("verify_tiles", 8)]:
+        o = O()
+        setattr(o, field, bad)
+        assert L.qg_set_launch_override(ctypes.byref(o)) == ESHAPE, field
+        assert field in qg.last_error()
+    assert all(v == 0 for v in qg.get_launch_override().values())
+    with qg.launch_override(gemv_waves=2, verify_form=qg.FORM_VERIFY_MFMA):
+        got = qg.get_launch_override()
+        assert got["gemv_waves"] == 2 and got["verify_form"] == qg.FORM_VERIFY_MFMA
+        with qg.launch_override(smalln_tiles=4):
+            assert qg.get_launch_override()["gemv_waves"] == 0
+        assert qg.get_launch_override()["gemv_waves"] == 2
+    assert all(v == 0 for v in qg.get_launch_override().values())
+    assert L.qg_get_launch_override(None) == ENULL
+
+
+def test_quantize_columns_validation(L):
+    f = L.qg_quantize_q8_1_columns
+    #  X, ldx, K, N, xq, stream
+    assert f(None, 256, 256, 2, B, None) == ENULL
+    assert f(A, 256, 300, 2, B, None) == ESHAPE     # K % 256
+    assert f(A, 256, 256, 0, B, None) == ESHAPE     # N < 1
+    assert f(A, 256, 256, 33, B, None) == ESHAPE    # N > 32
+    assert f(A, 128, 256, 2, B, None) == ESHAPE     # ldx < K
+    assert f(A, 258, 256, 2, B, None) == ESHAPE     # ldx % 4
+    assert f(A + 4, 256, 256, 2, B, None) == EALIGN
+    assert f(A, 256, 256, 2, A + 1024, None) == ESHAPE  # overlap
 
 
 def test_verify_q8_1_validation(L):

@@ -52,16 +52,16 @@ def test_graph_replays_match_eager():
     Yd3 = torch.empty((3, Md), device=DEV)
 
     def work():
-        qg.qgemv_q4k_batch(stage, ws=ws)
+        qg.qgemv_q4k_batch(stage)
         qg.lmhead_argmax(wh, xh, Mh, Kh, out_index=oi, out_value=ov, ws=ws)
         qg.lmhead_topk(wh, xh, Mh, Kh, 20, logits=lg, sampler=(0.9, 0.95, 0.02, u), ws=ws, out=tk)
-        qg.qgemm_q4k_smalln(stage[0][0], X5, M5, K5, Y=Y5, ws=ws)
-        qg.qgemm_q4k_smalln(wd, Xd, Md, Kd, Y=Yd, ws=ws)
-        qg.qgemm_q4k_smalln(stage[0][0], X32, M5, K5, Y=Y32, ws=ws)
-        qg.qgemm_q4k_smalln(stage[0][0], X2, M5, K5, Y=Y2, ws=ws)
-        qg.qgemm_q4k_smalln(wd, Xd3, Md, Kd, Y=Yd3, ws=ws)
+        qg.qgemm_q4k_smalln(stage[0][0], X5, M5, K5, Y=Y5)
+        qg.qgemm_q4k_smalln(wd, Xd, Md, Kd, Y=Yd)
+        qg.qgemm_q4k_smalln(stage[0][0], X32, M5, K5, Y=Y32)
+        qg.qgemm_q4k_smalln(stage[0][0], X2, M5, K5, Y=Y2)
+        qg.qgemm_q4k_smalln(wd, Xd3, Md, Kd, Y=Yd3)
         qg.quantize_q8_1(stage[0][1], out=xq)
-        qg.qgemv_q4k_q8_1(stage[0][0], xq, M5, K5, y=y8, ws=ws)
+        qg.qgemv_q4k_q8_1(stage[0][0], xq, M5, K5, y=y8)
 
     def snapshot():
         torch.cuda.synchronize()
@@ -94,7 +94,7 @@ def test_graph_replays_match_eager():
             assert torch.equal(a, b), f"replay {rep}: output {k} differs from the eager result"
         assert int(ws.buf.count_nonzero()) == 0
         # eager work between replays on the same buffers
-        qg.qgemv_q4k(stage[1][0], stage[1][1], stage[1][3], stage[1][4], y=stage[1][2], ws=ws)
+        qg.qgemv_q4k(stage[1][0], stage[1][1], stage[1][3], stage[1][4], y=stage[1][2])
         torch.cuda.synchronize()
 
 

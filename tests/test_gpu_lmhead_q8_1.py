@@ -68,10 +68,10 @@ def test_verify_q8_1_small(M, K, N):
 
 @pytest.mark.parametrize("cfg", ["1,0", "4,0"])
 @pytest.mark.parametrize("N", [1, 5, 8])
-def test_verify_q8_1_launch_shapes(cfg, N, monkeypatch):
+def test_verify_q8_1_launch_shapes(cfg, N):
     # one and four wavefronts per tile, with half macro-block counts that do not
     # divide evenly among the K-groups (K = 2816: 22 halves) and a ragged last tile
-    monkeypatch.setenv("QG_VQ_CFG", cfg)
+    qg.launch_override(verify_waves=int(cfg.split(",")[0])).set()
     M, K = 1000, 2816
     W = workloads.q8_0_blocks(M, K, key=(61, M))
     X = workloads.x_columns(K, N, key=(61, N))

@@ -83,9 +83,8 @@ def test_deterministic():
     x = to_dev(workloads.x_vector(K, key=(12,)))
     case("qgemv_q4k determinism")
     wp = packed_q4k(W, M, K)
-    ws = qg.Workspace(DEV)
-    y1 = qg.qgemv_q4k(wp, x, M, K, ws=ws).clone()
-    y2 = qg.qgemv_q4k(wp, x, M, K, ws=ws).clone()
+    y1 = qg.qgemv_q4k(wp, x, M, K).clone()
+    y2 = qg.qgemv_q4k(wp, x, M, K).clone()
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
 
@@ -117,22 +116,3 @@ def test_batch_matches_oracle_per_problem():
     torch.cuda.synchronize()
     for (w, x, y, M, K), (yr, ar) in zip(probs, refs):
         assert_within(y.cpu().numpy(), yr, ar, f"batch M={M} K={K}")
-
-
-@pytest.mark.parametrize("per_cu", ["1", "2"])
-def test_persistent_grid_walks_every_tile(per_cu, monkeypatch):
-    # a grid smaller than the tile count: each workgroup walks several tiles
-    # (of several problems, with ragged last tiles)
-    monkeypatch.setenv("QG_Q4K_PERSIST", per_cu)
-    shapes = [(4100, 3584), (517, 512), (16, 18944), (9000, 768)]
-    probs, refs = [], []
-    for i, (M, K) in enumerate(shapes):
-        W = workloads.q4k_blocks(M, K, key=(15, i))
-        x = workloads.x_vector(K, key=(15, i))
-        probs.append((packed_q4k(W, M, K), to_dev(x), torch.full((M,), float("nan"), device=DEV), M, K))
-        refs.append(oracle.gemv_q4k(W, M, K, x))
-    case(f"qgemv_q4k_batch persistent per_cu={per_cu}")
-    qg.qgemv_q4k_batch(probs)
-    torch.cuda.synchronize()
-    for (w, x, y, M, K), (yr, ar) in zip(probs, refs):
-        assert_within(y.cpu().numpy(), yr, ar, f"persistent M={M} K={K}")

@@ -104,8 +104,8 @@ def test_zero_activations_give_zero():
 
 
 @pytest.mark.parametrize("cfg", ["1", "2", "4", "8"])
-def test_launch_shapes(cfg, monkeypatch):
-    monkeypatch.setenv("QG_Q4K8_CFG", cfg)
+def test_launch_shapes(cfg):
+    qg.launch_override(gemv_waves=int(cfg)).set()
     for M, K in [(35, 1024), (33, 9472)]:
         run(M, K, key=(65, M, int(cfg)))
 

@@ -143,10 +143,10 @@ def test_deterministic():
 
 
 @pytest.mark.parametrize("cfg", ["1", "2", "4", "8"])
-def test_launch_shapes(cfg, monkeypatch):
+def test_launch_shapes(cfg):
     # every wavefront count per workgroup, in both the single-super-block and
     # the pair-loop forms
-    monkeypatch.setenv("QG_Q6K_CFG", cfg)
+    qg.launch_override(gemv_waves=int(cfg)).set()
     for M, K in [(35, 1024), (33, 9472)]:
         y, yr, ar = run_q6k(M, K, key=(27, M, int(cfg)))
         assert_within(y, yr, ar, f"q6k cfg={cfg} M={M} K={K}")

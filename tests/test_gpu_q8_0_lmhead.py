@@ -214,12 +214,12 @@ def test_verify_vocab_152064_n5():
 
 @pytest.mark.parametrize("cfg", ["8,1", "8,2", "8,4", "4,2", "4,4"])
 @pytest.mark.parametrize("N", [5, 20])
-def test_verify_launch_shapes(cfg, N, monkeypatch):
+def test_verify_launch_shapes(cfg, N):
     # every (wavefronts, tiles per workgroup) shape of the matrix-core form, with a
     # tile count that is not a multiple of the tiles per workgroup and a ragged last
     # tile
-    monkeypatch.setenv("QG_VA_IMPL", "mfma")
-    monkeypatch.setenv("QG_VA_CFG", cfg)
+    w, tw = (int(v) for v in cfg.split(","))
+    qg.launch_override(verify_form=qg.FORM_VERIFY_MFMA, verify_waves=w, verify_tiles=tw).set()
     M, K = 1000, 1024
     W = workloads.q8_0_blocks(M, K, key=(25, M))
     X = workloads.x_columns(K, N, key=(25, N))
@@ -228,12 +228,12 @@ def test_verify_launch_shapes(cfg, N, monkeypatch):
 
 @pytest.mark.parametrize("cfg", ["1,0", "4,0"])
 @pytest.mark.parametrize("N", [1, 3, 6])
-def test_verify_vector_alu_form_shapes(cfg, N, monkeypatch):
+def test_verify_vector_alu_form_shapes(cfg, N):
     # the vector-ALU form (N <= 6): one and four wavefronts per tile, half
     # macro-block counts that do not divide among the K-groups (K = 2816: 22
     # halves), a ragged last tile; the workspace (partials, fp16 pairs and block
     # sums) is left zero
-    monkeypatch.setenv("QG_VD_CFG", cfg)
+    qg.launch_override(verify_form=qg.FORM_VERIFY_DOT, verify_waves=int(cfg.split(",")[0])).set()
     M, K = 1000, 2816
     W = workloads.q8_0_blocks(M, K, key=(26, M))
     X = workloads.x_columns(K, N, key=(26, N))
@@ -252,12 +252,8 @@ def test_verify_forms_agree_on_ldx_padding():
     wp = packed_q8_0(W, M, K)
     case("lmhead_argmax_verify ldx padding, both forms")
     i_dot, v_dot = qg.lmhead_argmax_verify(wp, to_dev(Xp), M, K)
-    import os
-    os.environ["QG_VA_IMPL"] = "mfma"
-    try:
+    with qg.launch_override(verify_form=qg.FORM_VERIFY_MFMA):
         i_mma, v_mma = qg.lmhead_argmax_verify(wp, to_dev(Xp), M, K)
-    finally:
-        del os.environ["QG_VA_IMPL"]
     torch.cuda.synchronize()
     for n in range(N):
         yr, ar = oracle.gemv_q8_0(W, M, K, X[n])

@@ -94,11 +94,12 @@ def test_batch_mixed_problems():
 
 @pytest.mark.parametrize("cfg", ["1,1", "2,2", "4,4", "8,1", "8,2", "4,2"])
 @pytest.mark.parametrize("N", [5, 32])
-def test_launch_shapes(cfg, N, monkeypatch):
-    # every (wavefronts, tiles per wavefront) shape the launcher can pick, on a batch
-    # whose tile counts are not multiples of the tiles per wavefront and whose K
+def test_launch_shapes(cfg, N):
+    # every (wavefronts, tiles per wavefront) shape of the register-staged form, on a
+    # batch whose tile counts are not multiples of the tiles per wavefront and whose K
     # ranges leave some wavefronts with an odd number of units (or none)
-    monkeypatch.setenv("QG_SN_CFG", cfg)
+    w, tw = (int(v) for v in cfg.split(","))
+    qg.launch_override(smalln_form=qg.FORM_SMALLN_REGS, smalln_waves=w, smalln_tiles=tw).set()
     shapes = [(530, 1024), (77, 256), (16, 768), (1000, 512)]
     probs, refs = [], []
     for i, (M, K) in enumerate(shapes):
@@ -116,47 +117,14 @@ def test_launch_shapes(cfg, N, monkeypatch):
             assert_within(Yc[n], Yr[n], Ar[n], f"cfg {cfg} M={M} K={K} col {n}")
 
 
-@pytest.mark.parametrize("ks", ["2", "4"])
-@pytest.mark.parametrize("N", [5, 32])
-def test_split_k_exchange(ks, N, monkeypatch):
-    # K split among 2 or 4 workgroups per row block whose partial sums meet
-    # through 64-bit exchange slots: parity, bitwise determinism over repeated
-    # calls, and the workspace back to all-zero after every call
-    monkeypatch.setenv("QG_SN_KS", ks)
-    shapes = [(530, 4096), (77, 2048), (1000, 3584)]
-    probs, refs = [], []
-    for i, (M, K) in enumerate(shapes):
-        W = workloads.q4k_blocks(M, K, key=(35, i))
-        X = workloads.x_columns(K, N, key=(35, i, N))
-        Y = torch.full((N, (M + 3) // 4 * 4), float("nan"), device="cuda:0")
-        probs.append((packed_q4k(W, M, K), to_dev(X), Y, M, K))
-        refs.append(oracle.gemm_q4k(W, M, K, X, rows=np.arange(0, M, 3)))
-    ws = qg.Workspace("cuda:0")
-    case(f"qgemm_q4k_smalln_batch split-K ks={ks} N={N}")
-    qg.qgemm_q4k_smalln_batch(probs, ws=ws)
-    torch.cuda.synchronize()
-    assert ws.buf is not None and int(ws.buf.count_nonzero()) == 0
-    first = [p[2].clone() for p in probs]
-    for _ in range(2):
-        qg.qgemm_q4k_smalln_batch(probs, ws=ws)
-        torch.cuda.synchronize()
-        assert int(ws.buf.count_nonzero()) == 0
-        for (w, X, Y, M, K), Y0 in zip(probs, first):
-            assert torch.equal(Y[:, :M], Y0[:, :M])  # the padding past M stays NaN
-    for (w, X, Y, M, K), (Yr, Ar) in zip(probs, refs):
-        Yc = Y.cpu().numpy()[:, :M][:, ::3]
-        for n in range(N):
-            assert_within(Yc[n], Yr[n], Ar[n], f"split-K {ks} M={M} K={K} col {n}")
-
-
 # LDS-staged form (producer wavefronts stage the activations per chunk of super-blocks,
 # consumer wavefronts keep their weight loads chunks ahead): forced on shapes whose
 # super-block counts leave a short last chunk (nb % 8, nb % 4 != 0), a single chunk
 # (nb = 1), ragged tiles, and column counts on both sides of 16.
 @pytest.mark.parametrize("N", [1, 3, 5, 16, 17, 32])
 @pytest.mark.parametrize("M,K", [(200, 512), (65, 3328), (16, 256), (530, 9984)])
-def test_lds_form_shapes(M, K, N, monkeypatch):
-    monkeypatch.setenv("QG_SN_IMPL", "lds")
+def test_lds_form_shapes(M, K, N):
+    qg.launch_override(smalln_form=qg.FORM_SMALLN_LDS).set()
     rows = None if M * K <= 200 * 3328 else sample_rows(M, 96, seed=M + N)
     _, _, _, Y, Yr, Ar = run_smalln(M, K, N, key=(36, M, K, N), rows=rows)
     for n in range(N):
@@ -165,12 +133,12 @@ def test_lds_form_shapes(M, K, N, monkeypatch):
 
 @pytest.mark.parametrize("cfg", ["1,2", "1,3", "1,4", "2,2", "2,3", "2,4"])
 @pytest.mark.parametrize("N", [5, 32])
-def test_lds_form_launch_shapes(cfg, N, monkeypatch):
+def test_lds_form_launch_shapes(cfg, N):
     # every (tiles per workgroup, queue depth) the launcher accepts, on a batch whose
     # tile counts are not multiples of the tiles per workgroup (a depth of 4 is taken
     # up to 16 columns only; above, the launcher keeps its default depth)
-    monkeypatch.setenv("QG_SN_IMPL", "lds")
-    monkeypatch.setenv("QG_SNL_CFG", cfg)
+    tw, depth = (int(v) for v in cfg.split(","))
+    qg.launch_override(smalln_form=qg.FORM_SMALLN_LDS, smalln_tiles=tw, smalln_depth=depth).set()
     shapes = [(530, 2304), (77, 256), (16, 768), (1000, 1280)]
     probs, refs = [], []
     for i, (M, K) in enumerate(shapes):
@@ -192,10 +160,10 @@ def test_lds_form_launch_shapes(cfg, N, monkeypatch):
             assert_within(Yc[n], Yr[n], Ar[n], f"lds cfg {cfg} M={M} K={K} col {n}")
 
 
-def test_lds_form_padded_and_mixed_columns(monkeypatch):
+def test_lds_form_padded_and_mixed_columns():
     # padded leading dimensions and problems with different column counts in one
     # launch (LDS rows sized for the widest)
-    monkeypatch.setenv("QG_SN_IMPL", "lds")
+    qg.launch_override(smalln_form=qg.FORM_SMALLN_LDS).set()
     shapes = [(130, 2048, 5, 12, 10), (40, 1024, 2, 4, 8), (33, 512, 9, 0, 3)]
     probs, refs = [], []
     for i, (M, K, N, px, py) in enumerate(shapes):
@@ -218,23 +186,22 @@ def test_lds_form_padded_and_mixed_columns(monkeypatch):
 
 @pytest.mark.parametrize("N", [1, 5, 17, 32])
 @pytest.mark.parametrize("M,K", [(200, 512), (65, 3328), (48, 9984)])
-def test_register_form_shapes(M, K, N, monkeypatch):
+def test_register_form_shapes(M, K, N):
     # the register-staged form (activations in registers, wavefronts splitting K in
-    # 64-weight units), which split-K and its own launch-shape variable also select
-    monkeypatch.setenv("QG_SN_IMPL", "regs")
+    # 64-weight units)
+    qg.launch_override(smalln_form=qg.FORM_SMALLN_REGS).set()
     _, _, _, Y, Yr, Ar = run_smalln(M, K, N, key=(40, M, K, N))
     for n in range(N):
         assert_within(Y[n], Yr[n], Ar[n], f"register form M={M} K={K} N={N} col {n}")
 
 
 @pytest.mark.parametrize("tw", ["1", "2"])
-def test_single_pass_form(tw, monkeypatch):
+def test_single_pass_form(tw):
     # short-K single-pass form (all activations in LDS, every super-block of a row
     # in flight at once): the largest K it takes (4096: sixteen super-blocks, two
     # per wavefront), one super-block, N from 1 to its limit of 8 in one launch,
     # ragged tiles and tile counts not a multiple of the tiles per workgroup
-    monkeypatch.setenv("QG_SN_IMPL", "lds1")
-    monkeypatch.setenv("QG_SN1_TW", tw)
+    qg.launch_override(smalln_form=qg.FORM_SMALLN_LDS1, smalln_tiles=int(tw)).set()
     shapes = [(530, 4096, 8), (77, 256, 1), (16, 3584, 5), (1000, 1280, 3), (33, 768, 2)]
     probs, refs = [], []
     for i, (M, K, N) in enumerate(shapes):
@@ -258,22 +225,22 @@ def test_single_pass_form(tw, monkeypatch):
 
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("M,K", [(200, 512), (65, 3328), (48, 9984), (1, 256)])
-def test_dot_form_shapes(M, K, N, monkeypatch):
+def test_dot_form_shapes(M, K, N):
     # the vector-ALU dot-product form (N <= 8): one super-block per K-group (K up to
     # 4096) and the pipelined walk over several (K = 9984: 39 super-blocks, a
     # ragged last round), ragged tiles, a single row
-    monkeypatch.setenv("QG_SN_IMPL", "dot")
+    qg.launch_override(smalln_form=qg.FORM_SMALLN_DOT).set()
     _, _, _, Y, Yr, Ar = run_smalln(M, K, N, key=(41, M, K, N))
     for n in range(N):
         assert_within(Y[n], Yr[n], Ar[n], f"dot form M={M} K={K} N={N} col {n}")
 
 
 @pytest.mark.parametrize("M,K", [(3584, 3584), (3584, 18944), (700, 2304)])
-def test_dot_form_columns_bit_exact_with_gemv(M, K, monkeypatch):
+def test_dot_form_columns_bit_exact_with_gemv(M, K):
     # each column of the dot-product form repeats the single-column kernel's
     # arithmetic in the same order (four wavefronts per tile once K >= 2304), so it
     # equals qgemv_q4k of that column bit for bit
-    monkeypatch.setenv("QG_SN_IMPL", "dot")
+    qg.launch_override(smalln_form=qg.FORM_SMALLN_DOT).set()
     N = 5
     W = workloads.q4k_blocks(M, K, key=(42, M, K))
     X = workloads.x_columns(K, N, key=(42, M, K))
@@ -292,11 +259,11 @@ def test_dot_form_columns_bit_exact_with_gemv(M, K, monkeypatch):
         assert_within(Yc[n, rows], Yr[n], Ar[n], f"dot form M={M} K={K} col {n}")
 
 
-def test_dot_form_batch_mixed_columns(monkeypatch):
+def test_dot_form_batch_mixed_columns():
     # one launch over problems with different N (the kernel is built for the largest;
     # smaller problems read zeros past their N and store only their own columns) and
     # padded leading dimensions; padding and columns past N stay untouched
-    monkeypatch.setenv("QG_SN_IMPL", "dot")
+    qg.launch_override(smalln_form=qg.FORM_SMALLN_DOT).set()
     shapes = [(530, 4096, 8), (77, 256, 1), (16, 3584, 5), (1000, 1280, 3), (33, 18944, 2)]
     probs, refs, Xs = [], [], []
     for i, (M, K, N) in enumerate(shapes):
