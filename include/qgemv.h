@@ -293,6 +293,20 @@ qg_status lmhead_argmax(const void* w_packed_q8_0, const float* x, int64_t M, in
                         int32_t* out_index, float* out_value, qg_stream_t stream);
 
 /*
+ * lmhead_argmax for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and the same result as lmhead_argmax, bit for bit, with the per-tile
+ * partials in a fixed array inside the library instead of a caller workspace:
+ * 256 KiB per GPU, present from library load until the process ends, so
+ * M <= 524288 (QG_ERR_SHAPE above). The call allocates nothing. Every call on one
+ * GPU uses that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race and give wrong results; order them on one stream. The array needs
+ * no clearing between calls (every partial is written before it is read).
+ */
+qg_status lmhead_argmax_noalloc(const void* w_packed_q8_0, const float* x, int64_t M, int64_t K,
+                                int32_t* out_index, float* out_value, qg_stream_t stream);
+
+/*
  * Batched greedy verification on the LM head ("Why Local LLMs Don't Need C++ or
  * Python", section 2: projection and argmax fused on the device, one int32 per
  * decision; section 4: the candidate tokens are verified in one batched pass over

@@ -104,6 +104,7 @@ _SIGS = {
     "lmhead_topk": (_I, [_P, _P, _I64, _I64, _I, _P, ctypes.POINTER(_Sampler), _P, _SZ, ctypes.POINTER(_TopkOut),
                          _P]),
     "lmhead_argmax": (_I, [_P, _P, _I64, _I64, _P, _SZ, _P, _P, _P]),
+    "lmhead_argmax_noalloc": (_I, [_P, _P, _I64, _I64, _P, _P, _P]),
 }
 
 
@@ -441,6 +442,18 @@ def lmhead_argmax(w: torch.Tensor, x: torch.Tensor, M: int, K: int, out_index: t
     ws = _ws(ws, need, x.device)
     _check("lmhead_argmax", lib().lmhead_argmax(_ptr(w), _ptr(x), M, K, ws.ptr(), ws.nbytes(), _ptr(out_index),
                                                   _ptr(out_value), _stream(x.device)))
+    return out_index, out_value
+
+
+def lmhead_argmax_noalloc(w: torch.Tensor, x: torch.Tensor, M: int, K: int, out_index: torch.Tensor | None = None,
+                          out_value: torch.Tensor | None = None):
+    """lmhead_argmax with the partials in the library's own per-GPU array (no
+    workspace; calls on one GPU must not overlap). Returns (index, value) tensors."""
+    _need_cuda(w, x, out_index, out_value)
+    out_index = out_index if out_index is not None else torch.empty(1, dtype=torch.int32, device=x.device)
+    out_value = out_value if out_value is not None else torch.empty(1, dtype=torch.float32, device=x.device)
+    _check("lmhead_argmax_noalloc", lib().lmhead_argmax_noalloc(_ptr(w), _ptr(x), M, K, _ptr(out_index),
+                                                                _ptr(out_value), _stream(x.device)))
     return out_index, out_value
 
 

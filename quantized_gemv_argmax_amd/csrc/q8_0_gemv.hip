@@ -31,6 +31,7 @@
 // product (x rounded to fp16), also for rows whose quants are all zero.
 #include <algorithm>
 #include <climits>
+#include <mutex>
 
 #include "qg_device.h"
 #include "qg_host.h"
@@ -359,6 +360,56 @@ int choose_w(const Q8Prob& P) {
 
 size_t lm_ws_bytes(const Q8Prob& P) { return qg::align_up((size_t)P.tiles * 8, 256); }
 
+// Launches both stages of the LM-head argmax with its partials at `partials`.
+qg_status lmhead_launch(const Q8Prob& P, float2* partials, int32_t* out_index, float* out_value, hipStream_t s) {
+    const dim3 grid(P.tiles);
+    switch (choose_w(P)) {
+        case 1: hipLaunchKernelGGL(lmhead_tile_kernel<1>, grid, dim3(64), 0, s, P, partials); break;
+        case 2: hipLaunchKernelGGL(lmhead_tile_kernel<2>, grid, dim3(128), 0, s, P, partials); break;
+        case 4: hipLaunchKernelGGL(lmhead_tile_kernel<4>, grid, dim3(256), 0, s, P, partials); break;
+        default: hipLaunchKernelGGL(lmhead_tile_kernel<8>, grid, dim3(512), 0, s, P, partials); break;
+    }
+    qg_status st = qg::launch_status("lmhead_argmax (tiles)");
+    if (st) return st;
+    const int threads = (int)std::min<int64_t>(1024, std::max<int64_t>(64, qg::ceil_div(P.tiles, 64) * 64));
+    hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(1), dim3(threads), 0, s, partials, P.tiles, out_index, out_value);
+    return qg::launch_status("lmhead_argmax (reduce)");
+}
+
+}  // namespace
+
+// Scratch of lmhead_argmax_noalloc: the per-tile (max, index) partials, 8 bytes
+// per 16-row tile, in a device array of the library itself (one copy per GPU,
+// held until the process ends). In host code `scratch` only names the symbol (a
+// host-side stand-in, not a device address); its device address comes from
+// hipGetSymbolAddress, once per device, and only that address reaches kernels.
+constexpr size_t kLmScratchBytes = 256 * 1024;  // 32768 tiles: M <= 524288
+static __device__ __align__(256) uint8_t scratch[kLmScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // per device: the device address of `scratch`
+
+// Device address of the current device's scratch array, looked up on the first
+// call on that device (with it current), or an error.
+qg_status scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return qg::fail(QG_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return qg::fail(QG_ERR_DEVICE, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return qg::fail(QG_ERR_DEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -403,21 +454,27 @@ qg_status lmhead_argmax(const void* w, const float* x, int64_t M, int64_t K, voi
     if (!qg::aligned16(ws)) return qg::fail(QG_ERR_ALIGN, "workspace not 16-byte aligned");
     st = qg::check_device();
     if (st) return st;
-    float2* partials = (float2*)ws;
-    const dim3 grid(P.tiles);
-    hipStream_t s = (hipStream_t)stream;
-    switch (choose_w(P)) {
-        case 1: hipLaunchKernelGGL(lmhead_tile_kernel<1>, grid, dim3(64), 0, s, P, partials); break;
-        case 2: hipLaunchKernelGGL(lmhead_tile_kernel<2>, grid, dim3(128), 0, s, P, partials); break;
-        case 4: hipLaunchKernelGGL(lmhead_tile_kernel<4>, grid, dim3(256), 0, s, P, partials); break;
-        default: hipLaunchKernelGGL(lmhead_tile_kernel<8>, grid, dim3(512), 0, s, P, partials); break;
-    }
-    st = qg::launch_status("lmhead_argmax (tiles)");
+    return lmhead_launch(P, (float2*)ws, out_index, out_value, (hipStream_t)stream);
+}
+
+qg_status lmhead_argmax_noalloc(const void* w, const float* x, int64_t M, int64_t K, int32_t* out_index,
+                                float* out_value, qg_stream_t stream) {
+    qg::clear_error();
+    qg_status st = validate(w, x, M, K);
     if (st) return st;
-    const int threads = (int)std::min<int64_t>(1024, std::max<int64_t>(64, qg::ceil_div(P.tiles, 64) * 64));
-    hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(1), dim3(threads), 0, s, (float2*)partials, P.tiles,
-                       out_index, out_value);
-    return qg::launch_status("lmhead_argmax (reduce)");
+    if (!out_index) return qg::fail(QG_ERR_NULL, "out_index is NULL");
+    if ((reinterpret_cast<uintptr_t>(out_index) & 3) || (reinterpret_cast<uintptr_t>(out_value) & 3))
+        return qg::fail(QG_ERR_ALIGN, "outputs must be 4-byte aligned");
+    Q8Prob P = make_prob(w, x, nullptr, M, K);
+    if (lm_ws_bytes(P) > kLmScratchBytes)
+        return qg::fail(QG_ERR_SHAPE, "M=%lld needs %zu bytes of partials; lmhead_argmax_noalloc holds %zu (M <= %zu)",
+                        (long long)M, lm_ws_bytes(P), kLmScratchBytes, kLmScratchBytes / 8 * 16);
+    st = qg::check_device();
+    if (st) return st;
+    void* ptr = nullptr;
+    st = scratch_address(&ptr);
+    if (st) return st;
+    return lmhead_launch(P, (float2*)ptr, out_index, out_value, (hipStream_t)stream);
 }
 
 size_t lmhead_topk_workspace_bytes(int64_t M, int64_t K) {

@@ -158,6 +158,21 @@ def test_q8_0_and_lmhead_validation(L):
     assert L.lmhead_argmax_workspace_bytes(152064, 3584) == 152064 // 16 * 8
 
 
+def test_noalloc_validation(L):
+    f = L.lmhead_argmax_noalloc
+    #  w, x, M, K, out_index, out_value, stream
+    assert f(None, A, 1000, 3584, B, None, None) == ENULL
+    assert f(C, A, 1000, 3584, None, None, None) == ENULL
+    assert f(C, A, 1000, 3500, B, None, None) == ESHAPE
+    assert f(C, A, 524289, 3584, B, None, None) == ESHAPE      # beyond the fixed partial array
+    assert "524288" in qg.last_error()
+    assert f(C, A, 1000, 3584, B + 2, None, None) == EALIGN
+    assert f(C + 8, A, 1000, 3584, B, None, None) == EALIGN
+    import torch
+    if not torch.cuda.is_available():
+        assert f(C, A, 524288, 3584, B, None, None) in (EDEV, EUNSUP)
+
+
 def test_smalln_validation(L):
     f = L.qgemm_q4k_smalln
     assert f(C, A, 256, B, 64, 64, 256, 0, None) == ESHAPE
