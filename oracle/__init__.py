@@ -56,6 +56,7 @@ def lib():
         L.or_argmax.restype = _I64
         L.or_argmax.argtypes = [_P, _I64]
         L.or_num_threads.restype = ctypes.c_int
+        L.or_set_num_threads.argtypes = [ctypes.c_int]
         L.or_quantize_q8_1.argtypes = [_P, _I64, _P, _P, _P]
         L.or_gemv_q4k_q8_1.argtypes = [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P]
         L.or_gemv_q8_0_q8_1.argtypes = [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P]
@@ -269,6 +270,12 @@ def sample_topk(z_sorted, temperature: float, top_p: float, min_p: float, u: flo
 
 def num_threads() -> int:
     return int(lib().or_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the OpenMP loops over rows in later calls (the results do not
+    depend on it: each row is computed by one thread, in the same order)."""
+    lib().or_set_num_threads(int(n))
 
 
 def tolerance(a: np.ndarray) -> np.ndarray:

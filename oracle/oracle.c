@@ -18,6 +18,15 @@ int or_num_threads(void) {
 #endif
 }
 
+/* Threads used by later parallel loops (n >= 1); scheduling only, no arithmetic. */
+void or_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 static uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 
 /* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */

@@ -89,6 +89,7 @@ int64_t or_argmax(const double* y, int64_t n);
 
 /* Number of OpenMP threads the row loops use (1 without OpenMP). */
 int or_num_threads(void);
+void or_set_num_threads(int n); /* threads for later calls (scheduling only) */
 
 /*
  * Integer-activation form (dotLLM README news: Q8_1 / Q8_K input quantization,

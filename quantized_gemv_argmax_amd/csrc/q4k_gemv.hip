@@ -65,18 +65,20 @@ struct SbIn {
     float4 xa, xb, xc, xd;  // activations: low-nibble dwords i0, i0+1, then high-nibble ones
 };
 
-// The same loads as raw buffer loads: one resource per tile (weights) and one for
-// x, a per-lane byte offset and the segment / activation offsets as scalar
-// operands, so that a super-block costs one vector address operation instead of
-// one 64-bit address per load.
+// Loads of super-block b: raw buffer loads with one resource per tile (weights)
+// and one for x, a per-lane byte offset and the segment / activation offsets as
+// scalar operands, so that a super-block costs one vector address operation
+// instead of one 64-bit address per load. A K-group past the end of K (valid
+// false) gets an offset beyond both resources: the loads return zeros without a
+// memory access, and every load is still issued, so the wait counts stay exact.
 QG_DEV void load_sb_buf(SbIn& d, __amdgpu_buffer_rsrc_t wr, uint32_t vrow, __amdgpu_buffer_rsrc_t xr, uint32_t vx,
-                        int b, int rt) {
-    const uint32_t vxb = vx + (uint32_t)b * 1024u;
+                        int b, int rt, bool valid) {
+    const uint32_t vxb = valid ? vx + (uint32_t)b * 1024u : kQgOutOfRange;
     d.xa = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, vxb, 0, 0));
     d.xb = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, vxb, 16, 0));
     d.xc = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, vxb, 128, 0));
     d.xd = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, vxb, 144, 0));
-    const uint32_t vb = vrow + (uint32_t)b * 9u * (uint32_t)rt * 16u;
+    const uint32_t vb = valid ? vrow + (uint32_t)b * 9u * (uint32_t)rt * 16u : kQgOutOfRange;
 #pragma unroll
     for (int s = 0; s < 9; ++s) {
         const qg_u4v v = __builtin_amdgcn_raw_buffer_load_b128(wr, vb, s * rt * 16, kQgNonTemporal);
@@ -179,25 +181,26 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(Q4Args a) {
     float acc = 0.f;
     if constexpr (MODE == 0) {  // one super-block per K-group (4W >= K/256)
         SbIn b0;
-        load_sb_buf(b0, wr, vrow, xr, vx, min(kg, nb - 1), rt);
+        load_sb_buf(b0, wr, vrow, xr, vx, kg, rt, kg < nb);
         const float v0 = sb_dot(b0);
         acc = (kg < nb) ? v0 : 0.f;
     } else {
         const int niter = (nb + G - 1) / G;
         // Ping-pong between two register buffers over pairs of super-blocks: the
         // loads of one stay in flight while the other is computed. The loads are
-        // unconditional (the index is clamped to the last super-block) and the pair
-        // loop has a single exit, so the loop-carried load state, and with it every
-        // wait count, is exact: waiting for one super-block never waits for the next.
+        // unconditional (past the end of K they read zeros without a memory access)
+        // and the pair loop has a single exit, so the loop-carried load state, and
+        // with it every wait count, is exact: waiting for one super-block never
+        // waits for the next.
         SbIn b0, b1;
-        load_sb_buf(b0, wr, vrow, xr, vx, min(kg, nb - 1), rt);
+        load_sb_buf(b0, wr, vrow, xr, vx, kg, rt, kg < nb);
         int it = 0;
         for (; it + 2 <= niter; it += 2) {
-            load_sb_buf(b1, wr, vrow, xr, vx, min(kg + G * (it + 1), nb - 1), rt);
+            load_sb_buf(b1, wr, vrow, xr, vx, kg + G * (it + 1), rt, kg + G * (it + 1) < nb);
             __builtin_amdgcn_sched_barrier(0);  // issue the loads before any wait
             const float v0 = sb_dot(b0);
             acc += (kg + G * it < nb) ? v0 : 0.f;
-            load_sb_buf(b0, wr, vrow, xr, vx, min(kg + G * (it + 2), nb - 1), rt);
+            load_sb_buf(b0, wr, vrow, xr, vx, kg + G * (it + 2), rt, kg + G * (it + 2) < nb);
             __builtin_amdgcn_sched_barrier(0);
             const float v1 = sb_dot(b1);
             acc += (kg + G * (it + 1) < nb) ? v1 : 0.f;
