@@ -413,7 +413,9 @@ qg_status lmhead_topk(const void* w_packed, const float* x, int64_t M, int64_t K
  *                 (qgemv_q4k*, qgemv_q4k_q8_1*, qgemv_q6k, qgemv_q8_0, the LM-head
  *                 tile kernels): 1, 2, 4, 8.
  *   smalln_form   qgemm_q4k_smalln*: register-staged matrix-core, chunked-LDS
- *                 matrix-core, single-pass-LDS matrix-core or vector-ALU dot form.
+ *                 matrix-core, single-pass-LDS matrix-core, vector-ALU dot form,
+ *                 or the streamed single-pass form (workgroups walk several tiles;
+ *                 the single-pass shapes, the weights of each matrix < 2 GiB).
  *   smalln_waves  wavefronts per workgroup of the register-staged form: 1..8.
  *   smalln_tiles  16-row tiles per workgroup (matrix-core forms): 1, 2, 4.
  *   smalln_depth  weight-queue depth in chunks of the chunked-LDS form: 2..4.
@@ -427,6 +429,7 @@ qg_status lmhead_topk(const void* w_packed, const float* x, int64_t M, int64_t K
 #define QG_FORM_SMALLN_LDS 2
 #define QG_FORM_SMALLN_LDS1 3
 #define QG_FORM_SMALLN_DOT 4
+#define QG_FORM_SMALLN_STREAM 5
 #define QG_FORM_VERIFY_MFMA 1
 #define QG_FORM_VERIFY_DOT 2
 typedef struct {

@@ -61,6 +61,7 @@ struct SnProb {
     float* Y;
     int64_t ldx, ldy;
     int32_t M, nb, N, tiles, wg_begin;
+    int32_t wgs;  // workgroups of this problem (streamed form)
 };
 struct SnArgs {
     int32_t begin[QG_MAX_BATCH];
@@ -733,6 +734,276 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_lds1_kernel(SnArgs a) {
     }
 }
 
+// Streamed single-pass form, for the same shapes as the single-pass form when the
+// batch has more tiles than the chip holds workgroups: the grid is sized to the
+// resident workgroup slots, and workgroup j of a problem with G workgroups walks
+// tiles j, j + G, j + 2G, ... (at most kStTiles). The activations of the whole K
+// range go to LDS once per workgroup, as in the single-pass form; the W
+// wavefronts then take the (tile, super-block) units of the walk in turn, each
+// with the next unit's loads in flight while one is computed, so a CU's weight
+// stream does not stop between tiles and no partly filled last generation of
+// workgroups is left at the end. A wavefront accumulates the units of one tile in
+// registers and parks the sum in LDS when its walk moves to the next tile; the
+// parked sums of the W wavefronts meet once, at the end, in a fixed order.
+// LDS: the N activation rows (lanes of columns past N read column 0: their
+// products only reach output columns that are not stored), the sub-block sums of
+// the activations (K / 32 entries of 8 columns), then one parked sum per tile
+// slot and wavefront, for the 32 lanes that hold columns 0..7 (N <= 8).
+#ifndef QG_ST_WAVES
+#define QG_ST_WAVES 8
+#endif
+constexpr int kStWaves = QG_ST_WAVES;               // wavefronts per workgroup
+constexpr int kStPerCu = kStWaves >= 16 ? 1 : 2;    // resident workgroups per CU
+constexpr int kStTiles = kStWaves >= 16 ? 10 : 5;
+#ifndef QG_ST_RING
+#define QG_ST_RING 2
+#endif
+
+// Loads of unit (tile t, super-block b); valid false: offsets past the resource,
+// zeros without a memory access (so every load is still issued and the wait
+// counts stay exact). The caller passes a tile inside the matrix either way.
+QG_DEV void st_load(SwItem<1>& it, __amdgpu_buffer_rsrc_t wr, const SnProb& P, int t, int b, int i, int s,
+                    bool valid) {
+    const int rt = min(T, P.M - t * T);
+    const uint32_t r = (uint32_t)min(i, rt - 1);
+    const uint32_t vh = valid ? 16u * r : kOutOfRange;
+    const uint32_t vq = valid ? 16u * r + 8u * (uint32_t)(s & 1) + (uint32_t)(s >> 1) * 16u * (uint32_t)rt : kOutOfRange;
+    const int so = valid ? t * T * P.nb * 144 + b * 9 * 16 * rt : 0;
+    const qg_u4v h = __builtin_amdgcn_raw_buffer_load_b128(wr, vh, so, kNonTemporal);
+    it.hdr[0] = make_uint4(h.x, h.y, h.z, h.w);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const qg_u2v q = __builtin_amdgcn_raw_buffer_load_b64(wr, vq, so + (1 + 2 * g) * 16 * rt, kNonTemporal);
+        it.q[0][g] = make_uint2(q.x, q.y);
+    }
+}
+
+// One super-block of one tile for the streamed form: as sw_dot, but the
+// sub-block sums X_j of the activations come from the table the workgroup built
+// once while staging them (xs: byte address of this lane's entry for sub-block 0
+// of the super-block), instead of a matrix-core product per sub-block.
+QG_DEV void st_dot(qg_f4& acc, const SwItem<1>& it, const unsigned char* lds, uint32_t a, uint32_t xs) {
+    const qg_f4 zero = {0.f, 0.f, 0.f, 0.f};
+    const uint4 hd = it.hdr[0];
+    const float dd = qg_half_lo(hd.x) * 16777216.0f;  // quants enter as q * 2^-24
+    const float dm = qg_half_hi(hd.x);
+    const uint32_t sc03 = hd.y & 0x3f3f3f3fu, m03 = hd.z & 0x3f3f3f3fu;
+    const uint32_t sc47 = (hd.w & 0x0f0f0f0fu) | ((hd.y >> 2) & 0x30303030u);
+    const uint32_t m47 = ((hd.w >> 4) & 0x0f0f0f0fu) | ((hd.z >> 2) & 0x30303030u);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const qg_h8 a_lo = *reinterpret_cast<const qg_h8*>(lds + a + 128 * g);
+        const qg_h8 a_hi = *reinterpret_cast<const qg_h8*>(lds + a + 128 * g + 64);
+        const qg_f4 x_lo = *reinterpret_cast<const qg_f4*>(lds + xs + 64 * g);
+        const qg_f4 x_hi = *reinterpret_cast<const qg_f4*>(lds + xs + 64 * g + 32);
+        const uint32_t scw = g < 2 ? sc03 : sc47;
+        const uint32_t mw = g < 2 ? m03 : m47;
+        const int kb = 2 * (g & 1);
+        const float s_lo = dd * qg_byte_f(scw, kb);
+        const float s_hi = dd * 0.0625f * qg_byte_f(scw, kb + 1);
+        const float m_lo = dm * qg_byte_f(mw, kb);
+        const float m_hi = dm * qg_byte_f(mw, kb + 1);
+        const uint32_t w0 = it.q[0][g].x, w1 = it.q[0][g].y;
+        const uint32_t w0s = w0 >> 8, w1s = w1 >> 8;
+        const qg_h8 b_lo = __builtin_bit_cast(
+            qg_h8, make_uint4(w0 & 0x000f000fu, w0s & 0x000f000fu, w1 & 0x000f000fu, w1s & 0x000f000fu));
+        const qg_h8 b_hi = __builtin_bit_cast(
+            qg_h8, make_uint4(w0 & 0x00f000f0u, w0s & 0x00f000f0u, w1 & 0x00f000f0u, w1s & 0x00f000f0u));
+        const qg_f4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, zero, 0, 0, 0);
+        const qg_f4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, zero, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = acc[e];
+            v = fmaf(s_lo, s0[e], v);
+            v = fmaf(s_hi, s1[e], v);
+            v = fmaf(-m_lo, x_lo[e], v);
+            v = fmaf(-m_hi, x_hi[e], v);
+            acc[e] = v;
+        }
+    }
+}
+
+// The same super-block with the sub-block scales inside the matrix-core operands:
+//   - B carries q * sc_j instead of q (at most 15 * 63 = 945, still an exact fp16
+//     subnormal, one packed 16-bit multiply per dword), so the eight products of
+//     the super-block accumulate in the matrix core and d is applied once;
+//   - the min term sum_j (dmin m_j) X_j[n] is a 16 x 16 x 8 product in fp32, two
+//     v_mfma_f32_16x16x4_f32 with A = -X_j[n] from the workgroup's table (xt: byte
+//     address of this lane's entry, column l % 16, sub-block l / 16) and B = dmin m_j
+//     of this lane's row, accumulated across units in `accm`.
+typedef unsigned short qg_u16x2 __attribute__((ext_vector_type(2)));
+
+QG_DEV uint32_t st_mul16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(qg_u16x2, a) * __builtin_bit_cast(qg_u16x2, b));
+}
+
+QG_DEV void st_dot2(qg_f4& acc, qg_f4& accm, const SwItem<1>& it, const unsigned char* lds, uint32_t a, uint32_t xt,
+                    uint32_t sh) {
+    const uint4 hd = it.hdr[0];
+    const float dd = qg_half_lo(hd.x) * 16777216.0f;  // quants enter as q * 2^-24
+    const float dm = qg_half_hi(hd.x);
+    const uint32_t sc03 = hd.y & 0x3f3f3f3fu, m03 = hd.z & 0x3f3f3f3fu;
+    const uint32_t sc47 = (hd.w & 0x0f0f0f0fu) | ((hd.y >> 2) & 0x30303030u);
+    const uint32_t m47 = ((hd.w >> 4) & 0x0f0f0f0fu) | ((hd.z >> 2) & 0x30303030u);
+    // min term: B = dmin m_j, j = l / 16 (first product) and 4 + l / 16 (second)
+    const float bm0 = dm * (float)((m03 >> sh) & 0xffu);
+    const float bm1 = dm * (float)((m47 >> sh) & 0xffu);
+    const float xa0 = *reinterpret_cast<const float*>(lds + xt);
+    const float xa1 = *reinterpret_cast<const float*>(lds + xt + 256);
+    accm = __builtin_amdgcn_mfma_f32_16x16x4f32(xa0, bm0, accm, 0, 0, 0);
+    accm = __builtin_amdgcn_mfma_f32_16x16x4f32(xa1, bm1, accm, 0, 0, 0);
+
+    qg_f4 p = {0.f, 0.f, 0.f, 0.f};
+    constexpr uint32_t M = 0x000f000fu;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const qg_h8 a_lo = *reinterpret_cast<const qg_h8*>(lds + a + 128 * g);
+        const qg_h8 a_hi = *reinterpret_cast<const qg_h8*>(lds + a + 128 * g + 64);
+        const uint32_t scw = g < 2 ? sc03 : sc47;
+        const uint32_t kb = 2 * (g & 1);
+        // sc_j in both 16-bit halves
+        const uint32_t s_lo = __builtin_amdgcn_perm(0u, scw, 0x0c000c00u | (kb << 16) | kb);
+        const uint32_t s_hi = __builtin_amdgcn_perm(0u, scw, 0x0c000c00u | ((kb + 1) << 16) | (kb + 1));
+        const uint32_t w0 = it.q[0][g].x, w1 = it.q[0][g].y;
+        const qg_h8 b_lo = __builtin_bit_cast(
+            qg_h8, make_uint4(st_mul16(w0 & M, s_lo), st_mul16((w0 >> 8) & M, s_lo), st_mul16(w1 & M, s_lo),
+                              st_mul16((w1 >> 8) & M, s_lo)));
+        const qg_h8 b_hi = __builtin_bit_cast(
+            qg_h8, make_uint4(st_mul16((w0 >> 4) & M, s_hi), st_mul16((w0 >> 12) & M, s_hi),
+                              st_mul16((w1 >> 4) & M, s_hi), st_mul16((w1 >> 12) & M, s_hi)));
+        p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, p, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, p, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(dd, p[e], acc[e]);
+}
+
+template <int W, int R>
+__global__ __launch_bounds__(64 * W, 4) void q4k_smalln_stream_kernel(SnArgs a) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int wg = blockIdx.x;
+    int k = 0;
+#pragma unroll
+    for (int i = 1; i < QG_MAX_BATCH; ++i)
+        if (i < a.count && wg >= a.begin[i]) k = i;
+    const SnProb P = a.p[k];
+    const int j = wg - P.wg_begin;
+    const int G = P.wgs;
+    const int nt = (P.tiles - j + G - 1) / G;  // tiles of this walk, 1..kStTiles
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i = lane & 15, s = lane >> 4;
+    const int nb = P.nb;
+    const int K = nb * 256;
+    const int RB = (K + 8) * 2;  // bytes per LDS row
+    const uint32_t xsb = (uint32_t)(P.N * RB);  // sub-block sums -X_j[n], 16 columns per j
+    qg_f4* park = reinterpret_cast<qg_f4*>(lds + xsb + 2 * K);
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)P.w, (short)0, P.M * nb * 144, kQgRawBufferFlags);
+
+    // activations: thread tid takes 8-element group tid of every column (K <= 512 W)
+    const int tid = threadIdx.x;
+    const int gpr = K / 8;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)P.X, (short)0, (int)(((int64_t)(P.N - 1) * P.ldx + K) * 4), kQgRawBufferFlags);
+    float4 v[kS1Cols][2];
+#pragma unroll
+    for (int n = 0; n < kS1Cols; ++n) {
+        const uint32_t off = (n < P.N && tid < gpr) ? (uint32_t)(((int64_t)n * P.ldx + 8 * tid) * 4) : kOutOfRange;
+        v[n][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+        v[n][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 16, 0));
+    }
+
+    // this wavefront's units: wave, wave + W, ... of the nt * nb units of the walk;
+    // (lt, lb) is the tile slot and super-block of the unit being loaded
+    const int U = nt * nb;
+    const int niter = (U - wave + W - 1) / W;
+    int lt = wave / nb, lb = wave - (wave / nb) * nb;
+    auto advance = [&](int& t_, int& b_) {
+        b_ += W;
+        while (b_ >= nb) {
+            b_ -= nb;
+            ++t_;
+        }
+    };
+    // a ring of R unit buffers: units 0..R-2 are requested before the activations
+    // are stored
+    const int t_first = lt, b_first = lb;
+    SwItem<1> ring[R];
+#pragma unroll
+    for (int r = 0; r + 1 < R; ++r) {
+        st_load(ring[r], wr, P, j + min(lt, nt - 1) * G, lb, i, s, r < niter);
+        advance(lt, lb);
+    }
+
+    // parked sums start at zero (a wavefront may have no unit in some tile)
+    for (int o = tid; o < kStTiles * W * 32; o += 64 * W) park[o] = qg_f4{0.f, 0.f, 0.f, 0.f};
+    // fp16 activations, and the sums of each 32-element sub-block over the same
+    // fp16 values (a quad of threads holds one sub-block of a column)
+#pragma unroll
+    for (int n = 0; n < kS1Cols; ++n) {
+        const qg_h8 h = qg_a_operand(v[n][0], v[n][1]);
+        if (n < P.N && tid < gpr) *reinterpret_cast<qg_h8*>(lds + n * RB + 16 * tid) = h;
+        const uint4 hw = __builtin_bit_cast(uint4, h);
+        const float xsum = qg_quad_sum(qg_sum_pairs4(hw.x, hw.y, hw.z, hw.w));
+        if ((tid & 3) == 0 && tid < gpr) *reinterpret_cast<float*>(lds + xsb + ((tid >> 2) * 16 + n) * 4) = -xsum;
+    }
+    if ((tid & 3) == 0 && tid < gpr) {  // columns 8..15 of the table: zeros
+        *reinterpret_cast<uint4*>(lds + xsb + ((tid >> 2) * 16 + 8) * 4) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(lds + xsb + ((tid >> 2) * 16 + 12) * 4) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    sw_barrier();
+
+    const uint32_t an = (uint32_t)((i < P.N ? i : 0) * RB + 16 * s);
+    const uint32_t xtl = xsb + (uint32_t)(s * 16 + i) * 4;  // sub-block s of a super-block, column i
+    const uint32_t msh = 8u * (uint32_t)s;
+    qg_f4 cur[1][1] = {{qg_f4{0.f, 0.f, 0.f, 0.f}}};
+    qg_f4 curm = {0.f, 0.f, 0.f, 0.f};
+    int ct = t_first, cb = b_first;  // unit being computed
+    auto unit = [&](const SwItem<1>& it) {
+        st_dot2(cur[0][0], curm, it, lds, an + (uint32_t)(512 * cb), xtl + (uint32_t)(512 * cb), msh);
+        const int pt = ct;
+        advance(ct, cb);
+        if (ct != pt) {  // the walk moves to the next tile: park this one's sum
+            if (lane < 32) park[(pt * W + wave) * 32 + lane] = cur[0][0] + curm;
+            cur[0][0] = qg_f4{0.f, 0.f, 0.f, 0.f};
+            curm = qg_f4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+
+    // Each step requests unit it + R - 1 and computes unit it. The loads are
+    // unconditional (past the wavefront's last unit they read zeros) and the loop
+    // has a single exit, so the loop-carried load state, and with it every wait
+    // count, is exact: waiting for one unit never waits for a later one.
+    for (int it = 0; it < niter; it += R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            st_load(ring[(r + R - 1) % R], wr, P, j + min(lt, nt - 1) * G, lb, i, s, it + r + R - 1 < niter);
+            advance(lt, lb);
+            __builtin_amdgcn_sched_barrier(0);
+            if (it + r < niter) unit(ring[r]);
+        }
+    }
+    // (the position after a wavefront's last unit lies past the walk's last tile,
+    // so every tile's sum has been parked)
+    sw_barrier();
+    if (wave >= nt) return;
+    const int t = j + wave * G;
+    const int rt = min(T, P.M - t * T);
+    if (lane >= 32) return;
+    qg_f4 sum = park[(wave * W) * 32 + lane];
+#pragma unroll
+    for (int w = 1; w < W; ++w) sum += park[(wave * W + w) * 32 + lane];
+    if (i < rt) {
+        const int row = t * T + i;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int n = 4 * s + e;
+            if (n < P.N) P.Y[(int64_t)n * P.ldy + row] = sum[e];
+        }
+    }
+}
+
 // ------------------------------------------------------------------ host side
 qg_status sn_validate(const void* w, const float* X, int64_t ldx, const float* Y, int64_t ldy, int64_t M, int64_t K,
                 int64_t N) {
@@ -775,12 +1046,18 @@ SnProb make_sn(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy
 // workgroups, their partial sums meeting through atomic exchanges, was measured
 // slower at every 7B shape: the device-scope round trips at the end of every
 // workgroup cost more than the added parallelism gains.)
+// Dynamic LDS of the streamed form: nmax activation rows and the parked sums.
+size_t stream_lds_bytes(int nmax, int kmax) {
+    return (size_t)nmax * (kmax + 8) * 2 + 2 * (size_t)kmax + (size_t)kStTiles * kStWaves * 32 * 16;
+}
+
 struct SnCfg {
     int W, TW;
     bool lds;   // chunked LDS-staged kernel
     int D;      // its weight-queue depth in chunks
     bool lds1;  // single-pass LDS kernel (short K, N <= 8)
     bool dot;   // vector-ALU dot-product kernel (N <= 8, q4k_smalln_dot.hip)
+    bool stream;  // streamed single-pass kernel (single-pass shapes, many tiles)
 };
 SnCfg choose_cfg(const SnArgs& a, int C) {
     const qg_launch_override& ov = qg::launch_override();
@@ -793,7 +1070,7 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
         tiles += a.p[i].tiles;
         ncol = std::max(ncol, (int)a.p[i].N);
     }
-    SnCfg c{1, tiles > 256 ? 2 : 1, false, 2, false, false};
+    SnCfg c{1, tiles > 256 ? 2 : 1, false, 2, false, false, false};
     if (C == 2 && tiles > 1024) c.TW = 4;
     // Form selection, from measurements on the 7B shapes (stage times in us, register
     // form -> chosen form):
@@ -801,7 +1078,9 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
     //     matrices, ms per step against the matrix-core forms: N = 1 0.93 / 1.57,
     //     2 1.13 / 1.58, 3 1.29 / 1.63, 4 1.52 / 1.67, 5 1.83 / 1.74);
     //   - the single-pass LDS form for K <= 4096 and N <= 8 (N = 5: q/k/v 9.05 ->
-    //     8.75, o 6.85 -> 6.44, gate/up 29.7 -> 26.6);
+    //     8.75, o 6.85 -> 6.44, gate/up 29.7 -> 26.6), in its streamed variant
+    //     where two workgroups fit a CU's LDS (N = 5: q/k/v 8.86 -> 8.49, o 6.36 ->
+    //     5.48, gate/up 27.2 -> 21.1; N = 8 gate/up 28.4 -> 23.4);
     //   - the chunked LDS form for K >= 8192 (down projection: N = 5 23.6 -> 21.6,
     //     N = 32 72.3 -> 44.7) and for more than 16 columns over at most 1024 tiles
     //     (N = 32: q/k/v 18.2 -> 14.2, o 16.6 -> 12.0);
@@ -816,7 +1095,22 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
     bool s1 = C == 1;
     for (int i = 0; i < a.count; ++i)
         s1 = s1 && a.p[i].N <= kS1Cols && a.p[i].nb * 32 <= 64 * kS1Waves && a.p[i].nb <= kS1Items * kS1Waves;
-    c.lds1 = s1 && (form == QG_FORM_AUTO || form == QG_FORM_SMALLN_LDS1);
+    // the streamed form reads the weights through one buffer resource per matrix,
+    // and its LDS must fit (automatic choice: two workgroups per CU)
+    bool st = s1;
+    int kmax = 0;
+    for (int i = 0; i < a.count; ++i) {
+        st = st && (int64_t)a.p[i].M * a.p[i].nb * 144 < (int64_t)INT32_MAX;
+        kmax = std::max(kmax, a.p[i].nb * 256);
+    }
+    const size_t st_lds = stream_lds_bytes(ncol, kmax);
+    // automatic choice: where the workgroups fit the CUs' LDS as planned, or where a
+    // batch of many tiles runs one workgroup per CU (N = 8 gate/up: 28.4 -> 23.4 us)
+    c.stream = st && ((form == QG_FORM_AUTO && (st_lds <= 160 * 1024 / kStPerCu ||
+                                                (tiles >= 1024 && st_lds <= 160 * 1024))) ||
+                      (form == QG_FORM_SMALLN_STREAM && st_lds <= 160 * 1024));
+    if (c.stream) return c;
+    c.lds1 = s1 && (form == QG_FORM_AUTO || form == QG_FORM_SMALLN_LDS1 || form == QG_FORM_SMALLN_STREAM);
     if (c.lds1) {
         c.TW = tiles > 1024 ? 2 : 1;
         if (ov.smalln_tiles == 1 || ov.smalln_tiles == 2) c.TW = ov.smalln_tiles;
@@ -887,6 +1181,38 @@ void launch_s1(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kS1Waves), lds, s, a);
 }
 
+void launch_stream(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
+    const auto kern = q4k_smalln_stream_kernel<kStWaves, QG_ST_RING>;
+    static std::atomic<bool> attr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr[dev].load(std::memory_order_acquire)) {
+        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr[dev].store(true, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kStWaves), lds, s, a);
+}
+
+// Workgroups per problem for the streamed form: the resident slots (two
+// workgroups per CU) shared in proportion to the tiles, at most kStTiles tiles
+// per workgroup. Fills wg_begin, wgs and the compact begin array; returns the grid.
+int64_t stream_grid(SnArgs& a, int cus) {
+    int64_t tiles = 0;
+    for (int i = 0; i < a.count; ++i) tiles += a.p[i].tiles;
+    const int64_t slots = kStPerCu * (int64_t)std::max(cus, 1);
+    int64_t wgs = 0;
+    for (int i = 0; i < a.count; ++i) {
+        const int64_t t = a.p[i].tiles;
+        int64_t g = (slots * t + tiles - 1) / tiles;
+        g = std::max<int64_t>(g, qg::ceil_div(t, kStTiles));
+        g = std::min<int64_t>(std::max<int64_t>(g, 1), t);
+        a.p[i].wg_begin = (int32_t)wgs;
+        a.p[i].wgs = (int32_t)g;
+        a.begin[i] = (int32_t)wgs;
+        wgs += g;
+    }
+    return wgs;
+}
+
 void launch_lds_any(const SnArgs& a, int grid, int C, int TW, int D, size_t lds, hipStream_t s) {
     switch (100 * C + 10 * TW + D) {
         case 112: launch_lds<1, 1, 2>(a, grid, lds, s); break;
@@ -953,6 +1279,13 @@ qg_status run(const qg_gemm_problem* probs, int count, hipStream_t stream) {
     if (cfg.dot) return qg::smalln_dot_launch(probs, count, stream);
     if (cfg.lds) {
         launch_lds_any(a, (int)wgs, C, cfg.TW, cfg.D, sw_lds_bytes(C, cfg.TW, nmax), stream);
+        return qg::launch_status("qgemm_q4k_smalln");
+    }
+    if (cfg.stream) {
+        const int64_t grid = stream_grid(a, qg::device_cus());
+        int kmax = 0;
+        for (int i = 0; i < count; ++i) kmax = std::max(kmax, a.p[i].nb * 256);
+        launch_stream(a, (int)grid, stream_lds_bytes(nmax, kmax), stream);
         return qg::launch_status("qgemm_q4k_smalln");
     }
     if (cfg.lds1) {

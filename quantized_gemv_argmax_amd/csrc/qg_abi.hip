@@ -27,6 +27,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Per-device verdict cache: 0 unknown, 1 gfx950, 2 other.
 static int g_dev_ok[64];
+static int g_dev_cus[64];
 static std::mutex g_dev_mu;
 
 qg_status check_device() {
@@ -41,10 +42,18 @@ qg_status check_device() {
             e = hipGetDeviceProperties(&prop, dev);
             if (e != hipSuccess) return fail(QG_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
             g_dev_ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+            g_dev_cus[dev] = prop.multiProcessorCount;
         }
         if (g_dev_ok[dev] != 1) return fail(QG_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
     }
     return QG_OK;
+}
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    return g_dev_cus[dev] > 0 ? g_dev_cus[dev] : 1;
 }
 
 qg_status launch_status(const char* what) {
@@ -100,7 +109,8 @@ qg_status qg_set_launch_override(const qg_launch_override* o) {
     };
     if (!in(v.gemv_waves, {1, 2, 4, 8}))
         return (qg_status)qg::fail(QG_ERR_SHAPE, "gemv_waves=%d not in {0, 1, 2, 4, 8}", v.gemv_waves);
-    if (!in(v.smalln_form, {QG_FORM_SMALLN_REGS, QG_FORM_SMALLN_LDS, QG_FORM_SMALLN_LDS1, QG_FORM_SMALLN_DOT}))
+    if (!in(v.smalln_form,
+            {QG_FORM_SMALLN_REGS, QG_FORM_SMALLN_LDS, QG_FORM_SMALLN_LDS1, QG_FORM_SMALLN_DOT, QG_FORM_SMALLN_STREAM}))
         return (qg_status)qg::fail(QG_ERR_SHAPE, "smalln_form=%d unknown", v.smalln_form);
     if (!in(v.smalln_waves, {1, 2, 4, 8}))
         return (qg_status)qg::fail(QG_ERR_SHAPE, "smalln_waves=%d not in {0, 1, 2, 4, 8}", v.smalln_waves);

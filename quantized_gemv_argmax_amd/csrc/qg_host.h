@@ -20,6 +20,9 @@ bool aligned16(const void* p);
 // Returns QG_OK if the current device is gfx950, else an error status.
 qg_status check_device();
 
+// Compute units of the current device (after a successful check_device()).
+int device_cus();
+
 // Translate a launch error into QG_ERR_DEVICE (records the HIP message).
 qg_status launch_status(const char* what);
 

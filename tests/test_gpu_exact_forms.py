@@ -32,7 +32,7 @@ from tests.gpu_helpers import DEV, case, packed_q4k, packed_q8_0, to_dev
 pytestmark = pytest.mark.gpu
 
 FORMS = {"auto": qg.FORM_AUTO, "regs": qg.FORM_SMALLN_REGS, "lds": qg.FORM_SMALLN_LDS,
-         "lds1": qg.FORM_SMALLN_LDS1, "dot": qg.FORM_SMALLN_DOT}
+         "lds1": qg.FORM_SMALLN_LDS1, "dot": qg.FORM_SMALLN_DOT, "stream": qg.FORM_SMALLN_STREAM}
 
 
 @functools.lru_cache(maxsize=None)
@@ -115,14 +115,15 @@ def check_exact(Y, W, M, K, X, what):
 
 SMALLN_CASES = [("auto", N) for N in (1, 2, 3, 4, 5, 8, 9, 16, 17, 32)] + \
                [("regs", N) for N in (5, 17, 32)] + [("lds", N) for N in (5, 17, 32)] + \
-               [("lds1", N) for N in (5, 8)] + [("dot", N) for N in (1, 5, 8)]
+               [("lds1", N) for N in (5, 8)] + [("dot", N) for N in (1, 5, 8)] + \
+               [("stream", N) for N in (1, 5, 8)]
 
 
 @pytest.mark.parametrize("form,N", SMALLN_CASES)
 @pytest.mark.parametrize("M,K", [(70, 768), (37, 9984), (300, 3840)])
 def test_smalln_exact(form, N, M, K):
-    if form == "lds1" and K > 4096:
-        pytest.skip("the single-pass form takes K <= 4096")
+    if form in ("lds1", "stream") and K > 4096:
+        pytest.skip("the single-pass forms take K <= 4096")
     W = exact_q4k_rows(M, K, seed=M + K)
     X = exact_columns(K, N)
     wp = packed_q4k(W, M, K)
@@ -134,7 +135,7 @@ def test_smalln_exact(form, N, M, K):
 
 
 @pytest.mark.parametrize("form,N", [("auto", 5), ("auto", 32), ("regs", 5), ("regs", 32), ("lds", 5),
-                                    ("lds", 32), ("lds1", 5), ("dot", 5)])
+                                    ("lds", 32), ("lds1", 5), ("dot", 5), ("stream", 5)])
 def test_smalln_zero_scales_exact_zero_random_x(form, N):
     # d = dmin = 0 in every block: exactly 0 whatever the activations
     M, K = 100, 3584

@@ -223,6 +223,41 @@ def test_single_pass_form(tw):
             assert_within(Yc[n], Yr[n], Ar[n], f"single-pass TW={tw} M={M} K={K} col {n}")
 
 
+def test_streamed_form():
+    # streamed single-pass form (workgroups walk up to five tiles each, per-tile
+    # sums parked in LDS): ragged tiles, one super-block, K = 4096, N from 1 to 8,
+    # and batches of more tiles than the grid has workgroups, so that walks of one
+    # to five tiles occur (3125 tiles of one super-block; 1250 + 20 tiles of two)
+    qg.launch_override(smalln_form=qg.FORM_SMALLN_STREAM).set()
+    batches = [[(530, 4096, 8), (77, 256, 1), (16, 3584, 5), (1000, 1280, 3), (33, 768, 2)],
+               [(50000, 256, 5)],
+               [(20000, 512, 5), (317, 512, 5)],
+               [(18944, 3584, 5), (18944, 3584, 5)]]
+    for bi, shapes in enumerate(batches):
+        probs, refs = [], []
+        for i, (M, K, N) in enumerate(shapes):
+            W = workloads.q4k_blocks(M, K, key=(43, bi, i))
+            X = workloads.x_columns(K, N, key=(43, bi, i, N))
+            Y = torch.full((N, (M + 3) // 4 * 4), float("nan"), device="cuda:0")
+            rows = sample_rows(M, 256, seed=M + i) if M * K > 1 << 24 else None
+            probs.append((packed_q4k(W, M, K), to_dev(X), Y, M, K))
+            refs.append((rows, oracle.gemm_q4k(W, M, K, X, rows=rows)))
+        case(f"qgemm_q4k_smalln_batch streamed batch {bi}: {shapes}")
+        qg.qgemm_q4k_smalln_batch(probs)
+        torch.cuda.synchronize()
+        first = [p[2].clone() for p in probs]
+        qg.qgemm_q4k_smalln_batch(probs)
+        torch.cuda.synchronize()
+        for (w, X, Y, M, K), Y0, (rows, (Yr, Ar)) in zip(probs, first, refs):
+            assert torch.equal(Y[:, :M], Y0[:, :M]), "streamed form not deterministic"
+            assert not torch.isnan(Y[:, :M]).any(), "streamed form left outputs unwritten"
+            Yc = Y.cpu().numpy()[:, :M]
+            if rows is not None:
+                Yc = Yc[:, rows]
+            for n in range(X.shape[0]):
+                assert_within(Yc[n], Yr[n], Ar[n], f"streamed M={M} K={K} col {n}")
+
+
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("M,K", [(200, 512), (65, 3328), (48, 9984), (1, 256)])
 def test_dot_form_shapes(M, K, N):
