@@ -414,8 +414,10 @@ qg_status lmhead_topk(const void* w_packed, const float* x, int64_t M, int64_t K
  *                 tile kernels): 1, 2, 4, 8.
  *   smalln_form   qgemm_q4k_smalln*: register-staged matrix-core, chunked-LDS
  *                 matrix-core, single-pass-LDS matrix-core, vector-ALU dot form,
- *                 or the streamed single-pass form (workgroups walk several tiles;
- *                 the single-pass shapes, the weights of each matrix < 2 GiB).
+ *                 the streamed single-pass form (workgroups walk several tiles;
+ *                 the single-pass shapes, the weights of each matrix < 2 GiB), or
+ *                 the chunked walk form (one workgroup per CU walks several tiles
+ *                 chunk by chunk along K; any K, the weights of each matrix < 2 GiB).
  *   smalln_waves  wavefronts per workgroup of the register-staged form: 1..8.
  *   smalln_tiles  16-row tiles per workgroup (matrix-core forms): 1, 2, 4.
  *   smalln_depth  weight-queue depth in chunks of the chunked-LDS form: 2..4.
@@ -430,6 +432,7 @@ qg_status lmhead_topk(const void* w_packed, const float* x, int64_t M, int64_t K
 #define QG_FORM_SMALLN_LDS1 3
 #define QG_FORM_SMALLN_DOT 4
 #define QG_FORM_SMALLN_STREAM 5
+#define QG_FORM_SMALLN_WALK 6
 #define QG_FORM_VERIFY_MFMA 1
 #define QG_FORM_VERIFY_DOT 2
 typedef struct {

@@ -51,7 +51,8 @@ class _LaunchOverride(ctypes.Structure):
 
 # kernel forms a launch override can force (include/qgemv.h)
 FORM_AUTO = 0
-FORM_SMALLN_REGS, FORM_SMALLN_LDS, FORM_SMALLN_LDS1, FORM_SMALLN_DOT, FORM_SMALLN_STREAM = 1, 2, 3, 4, 5
+FORM_SMALLN_REGS, FORM_SMALLN_LDS, FORM_SMALLN_LDS1, FORM_SMALLN_DOT, FORM_SMALLN_STREAM, FORM_SMALLN_WALK = \
+    1, 2, 3, 4, 5, 6
 FORM_VERIFY_MFMA, FORM_VERIFY_DOT = 1, 2
 
 

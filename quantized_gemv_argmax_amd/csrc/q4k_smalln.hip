@@ -1004,6 +1004,216 @@ __global__ __launch_bounds__(64 * W, 4) void q4k_smalln_stream_kernel(SnArgs a) 
     }
 }
 
+// Chunked walk form, for batches of many tiles with up to 32 columns: one
+// workgroup of 16 wavefronts per CU walks up to kWkTiles tiles (j, j + G, j + 2G,
+// ...) chunk by chunk along K. The activations of a chunk of KC super-blocks (all N
+// columns) are staged into LDS as fp16 once per workgroup, with the sums of their
+// 32-element sub-blocks, one chunk ahead in two buffers, and serve every tile of
+// the walk: a workgroup reads X once, not once per tile. In each chunk, wavefront w
+// computes super-block w % KC of the chunk for the tile slots (w + 16 m) / KC, m =
+// 0, 1, ...: the same tile slots in every chunk, so its per-tile sums stay in
+// registers until the end, and with KC C = 4 the four SIMDs get equal work for any
+// number of tiles. The weights of a wavefront's units in the next chunk are
+// requested right after the same units of this chunk are computed. Products as in
+// the streamed form (scales inside the matrix-core operands, the min term as an
+// fp32 matrix-core product); every column block c of 16 columns reuses one B.
+constexpr int kWkWaves = 16, kWkTiles = 10;
+constexpr int64_t kWkAutoTiles = 1024;
+
+template <int C>
+struct WkGeom {
+    static constexpr int KC = 4 / C;                                       // super-blocks per chunk
+    static constexpr int MU = (kWkTiles * KC + kWkWaves - 1) / kWkWaves;  // units per wavefront and chunk
+    static constexpr int RB = (KC * 256 + 8) * 2;                          // bytes per activation row
+    static constexpr int TB = KC * 8 * 16 * C * 4;                          // sub-block sum table bytes
+    static constexpr int GC = KC * 32;                                      // 8-element groups per column
+};
+
+// Activations of chunk q into registers: thread tid takes groups tid and tid + 1024
+// of the chunk (group g: column g / GC, elements 8 (g % GC)..+7 of the chunk; N GC
+// <= 2048). Groups past N or past K read zeros without a memory access.
+template <int C>
+QG_DEV void wk_issue(float4 (&v)[2][2], __amdgpu_buffer_rsrc_t xr, const SnProb& P, int q, int tid) {
+    constexpr int KC = WkGeom<C>::KC, GC = WkGeom<C>::GC;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int g = tid + 1024 * r;
+        const int n = g / GC, k8 = g % GC;
+        const int kk = q * KC * 256 + 8 * k8;
+        const uint32_t off =
+            (n < P.N && kk < P.nb * 256) ? (uint32_t)(((int64_t)n * P.ldx + kk) * 4) : kOutOfRange;
+        v[r][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+        v[r][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 16, 0));
+    }
+}
+
+// ... and from registers into a chunk buffer: fp16 rows of RB bytes per column,
+// then the table of -X_j[n] (16 C columns per sub-block j of the chunk, from the
+// same fp16 values; a quad of threads holds one sub-block of a column).
+template <int C>
+QG_DEV void wk_write(const float4 (&v)[2][2], unsigned char* buf, const SnProb& P, int tid) {
+    constexpr int RB = WkGeom<C>::RB, GC = WkGeom<C>::GC;
+    float* table = reinterpret_cast<float*>(buf + P.N * RB);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int g = tid + 1024 * r;
+        const int n = g / GC, k8 = g % GC;
+        const qg_h8 h = qg_a_operand(v[r][0], v[r][1]);
+        if (n < P.N) *reinterpret_cast<qg_h8*>(buf + n * RB + 16 * k8) = h;
+        const uint4 hw = __builtin_bit_cast(uint4, h);
+        const float xs = qg_quad_sum(qg_sum_pairs4(hw.x, hw.y, hw.z, hw.w));
+        if ((k8 & 3) == 0) table[(k8 >> 2) * 16 * C + n] = -xs;
+    }
+}
+
+// One super-block of one tile for C column blocks (a[c]: LDS byte address of this
+// lane's A operand for sub-block 0; xt: this lane's table entry, sub-block l / 16
+// of the super-block, column l % 16 of block 0).
+template <int C>
+QG_DEV void wk_dot(qg_f4 (&acc)[C], const SwItem<1>& it, const unsigned char* buf, const uint32_t (&a)[C],
+                   uint32_t xt, uint32_t sh) {
+    const uint4 hd = it.hdr[0];
+    const float dd = qg_half_lo(hd.x) * 16777216.0f;  // quants enter as q * 2^-24
+    const float dm = qg_half_hi(hd.x);
+    const uint32_t sc03 = hd.y & 0x3f3f3f3fu, m03 = hd.z & 0x3f3f3f3fu;
+    const uint32_t sc47 = (hd.w & 0x0f0f0f0fu) | ((hd.y >> 2) & 0x30303030u);
+    const uint32_t m47 = ((hd.w >> 4) & 0x0f0f0f0fu) | ((hd.z >> 2) & 0x30303030u);
+    const float bm0 = dm * (float)((m03 >> sh) & 0xffu);
+    const float bm1 = dm * (float)((m47 >> sh) & 0xffu);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const float xa0 = *reinterpret_cast<const float*>(buf + xt + 64 * c);
+        const float xa1 = *reinterpret_cast<const float*>(buf + xt + 64 * c + 256 * C);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa0, bm0, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa1, bm1, acc[c], 0, 0, 0);
+    }
+    qg_f4 p[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) p[c] = qg_f4{0.f, 0.f, 0.f, 0.f};
+    constexpr uint32_t M = 0x000f000fu;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint32_t scw = g < 2 ? sc03 : sc47;
+        const uint32_t kb = 2 * (g & 1);
+        const uint32_t s_lo = __builtin_amdgcn_perm(0u, scw, 0x0c000c00u | (kb << 16) | kb);
+        const uint32_t s_hi = __builtin_amdgcn_perm(0u, scw, 0x0c000c00u | ((kb + 1) << 16) | (kb + 1));
+        const uint32_t w0 = it.q[0][g].x, w1 = it.q[0][g].y;
+        const qg_h8 b_lo = __builtin_bit_cast(
+            qg_h8, make_uint4(st_mul16(w0 & M, s_lo), st_mul16((w0 >> 8) & M, s_lo), st_mul16(w1 & M, s_lo),
+                              st_mul16((w1 >> 8) & M, s_lo)));
+        const qg_h8 b_hi = __builtin_bit_cast(
+            qg_h8, make_uint4(st_mul16((w0 >> 4) & M, s_hi), st_mul16((w0 >> 12) & M, s_hi),
+                              st_mul16((w1 >> 4) & M, s_hi), st_mul16((w1 >> 12) & M, s_hi)));
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const qg_h8 a_lo = *reinterpret_cast<const qg_h8*>(buf + a[c] + 128 * g);
+            const qg_h8 a_hi = *reinterpret_cast<const qg_h8*>(buf + a[c] + 128 * g + 64);
+            p[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, p[c], 0, 0, 0);
+            p[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, p[c], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[c][e] = fmaf(dd, p[c][e], acc[c][e]);
+}
+
+template <int C>
+__global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_walk_kernel(SnArgs a) {
+    using Gm = WkGeom<C>;
+    constexpr int KC = Gm::KC, MU = Gm::MU, RB = Gm::RB, TB = Gm::TB;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int wg = blockIdx.x;
+    int k = 0;
+#pragma unroll
+    for (int i = 1; i < QG_MAX_BATCH; ++i)
+        if (i < a.count && wg >= a.begin[i]) k = i;
+    const SnProb P = a.p[k];
+    const int j = wg - P.wg_begin;
+    const int G = P.wgs;
+    const int nt = (P.tiles - j + G - 1) / G;  // tiles of this walk, 1..kWkTiles
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = threadIdx.x;
+    const int i = lane & 15, s = lane >> 4;
+    const int nb = P.nb;
+    const int nq = (nb + KC - 1) / KC;
+    const uint32_t BS = ((uint32_t)(P.N * RB + TB) + 15u) & ~15u;  // bytes per chunk buffer
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)P.w, (short)0, P.M * nb * 144, kQgRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)P.X, (short)0, (int)(((int64_t)(P.N - 1) * P.ldx + (int64_t)nb * 256) * 4), kQgRawBufferFlags);
+    const int sb = wave % KC;  // this wavefront's super-block within every chunk
+
+    // chunk 0: activations, and the weights of this wavefront's units
+    float4 vx[2][2];
+    wk_issue<C>(vx, xr, P, 0, tid);
+    SwItem<1> ring[MU];
+#pragma unroll
+    for (int m = 0; m < MU; ++m) {
+        const int ts = (wave + kWkWaves * m) / KC;
+        st_load(ring[m], wr, P, j + min(ts, nt - 1) * G, min(sb, nb - 1), i, s, ts < nt && sb < nb);
+    }
+    wk_write<C>(vx, lds, P, tid);
+    sw_barrier();
+
+    uint32_t an[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int n = 16 * c + i;
+        an[c] = (uint32_t)((n < P.N ? n : 0) * RB + 16 * s + 512 * sb);
+    }
+    const uint32_t xt = (uint32_t)(P.N * RB) + (uint32_t)(((sb * 8 + s) * 16 * C + i) * 4);
+    const uint32_t sh = 8u * (uint32_t)s;
+    qg_f4 acc[MU][C];
+#pragma unroll
+    for (int m = 0; m < MU; ++m)
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[m][c] = qg_f4{0.f, 0.f, 0.f, 0.f};
+
+    for (int q = 0; q < nq; ++q) {
+        const unsigned char* cur = lds + (q & 1) * BS;
+        wk_issue<C>(vx, xr, P, q + 1, tid);  // past the last chunk: zeros, no memory access
+        const int b = q * KC + sb;
+#pragma unroll
+        for (int m = 0; m < MU; ++m) {
+            const int ts = (wave + kWkWaves * m) / KC;
+            if (ts < nt && b < nb) wk_dot<C>(acc[m], ring[m], cur, an, xt, sh);
+            st_load(ring[m], wr, P, j + min(ts, nt - 1) * G, min(b + KC, nb - 1), i, s, ts < nt && b + KC < nb);
+        }
+        wk_write<C>(vx, lds + ((q + 1) & 1) * BS, P, tid);
+        sw_barrier();
+    }
+
+    // per-tile partial sums of the KC wavefronts of each tile meet in LDS
+    qg_f4* park = reinterpret_cast<qg_f4*>(lds);
+#pragma unroll
+    for (int m = 0; m < MU; ++m) {
+        const int u = wave + kWkWaves * m;
+        if (u / KC < nt)
+#pragma unroll
+            for (int c = 0; c < C; ++c) park[(u * C + c) * 64 + lane] = acc[m][c];
+    }
+    sw_barrier();
+    if (wave >= nt) return;
+    const int t = j + wave * G;
+    const int rt = min(T, P.M - t * T);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        qg_f4 sum = park[((wave * KC) * C + c) * 64 + lane];
+#pragma unroll
+        for (int b2 = 1; b2 < KC; ++b2) sum += park[((wave * KC + b2) * C + c) * 64 + lane];
+        if (i < rt) {
+            const int row = t * T + i;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int n = 16 * c + 4 * s + e;
+                if (n < P.N) P.Y[(int64_t)n * P.ldy + row] = sum[e];
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ host side
 qg_status sn_validate(const void* w, const float* X, int64_t ldx, const float* Y, int64_t ldy, int64_t M, int64_t K,
                 int64_t N) {
@@ -1058,6 +1268,7 @@ struct SnCfg {
     bool lds1;  // single-pass LDS kernel (short K, N <= 8)
     bool dot;   // vector-ALU dot-product kernel (N <= 8, q4k_smalln_dot.hip)
     bool stream;  // streamed single-pass kernel (single-pass shapes, many tiles)
+    bool walk;    // chunked walk kernel (many tiles, up to 32 columns)
 };
 SnCfg choose_cfg(const SnArgs& a, int C) {
     const qg_launch_override& ov = qg::launch_override();
@@ -1070,7 +1281,7 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
         tiles += a.p[i].tiles;
         ncol = std::max(ncol, (int)a.p[i].N);
     }
-    SnCfg c{1, tiles > 256 ? 2 : 1, false, 2, false, false, false};
+    SnCfg c{1, tiles > 256 ? 2 : 1, false, 2, false, false, false, false};
     if (C == 2 && tiles > 1024) c.TW = 4;
     // Form selection, from measurements on the 7B shapes (stage times in us, register
     // form -> chosen form):
@@ -1084,12 +1295,20 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
     //   - the chunked LDS form for K >= 8192 (down projection: N = 5 23.6 -> 21.6,
     //     N = 32 72.3 -> 44.7) and for more than 16 columns over at most 1024 tiles
     //     (N = 32: q/k/v 18.2 -> 14.2, o 16.6 -> 12.0);
-    //   - the register form otherwise (N = 32 gate/up, 2368 tiles: 57.7 against 62.6
-    //     for the chunked LDS form; N = 5 short K: 29.7 against 37.0).
+    //   - the chunked walk form for more columns over at least kWkAutoTiles tiles
+    //     (N = 32 gate/up, 2368 tiles: 56.7 -> 28.3; with few tiles per CU it idles
+    //     most of its wavefronts: N = 32 q/k/v 15.5 -> 32.9);
+    //   - the register form otherwise (N = 5 short K: 29.7 against 37.0 for the
+    //     chunked LDS form).
     // A launch override (qg_set_launch_override) can force a form within the range
     // it supports, and the launch shape.
     c.dot = (form == QG_FORM_AUTO && ncol <= 4) || (form == QG_FORM_SMALLN_DOT && ncol <= 8);
     if (c.dot) return c;
+    // the walk form reads the weights through one buffer resource per matrix
+    bool wk = true;
+    for (int i = 0; i < a.count; ++i) wk = wk && (int64_t)a.p[i].M * a.p[i].nb * 144 < (int64_t)INT32_MAX;
+    c.walk = wk && form == QG_FORM_SMALLN_WALK;
+    if (c.walk) return c;
     // Single-pass form: every problem with K <= 512 * 8 and N <= 8 (one round of
     // activation loads per lane, all super-blocks of a row in flight at once).
     bool s1 = C == 1;
@@ -1116,6 +1335,9 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
         if (ov.smalln_tiles == 1 || ov.smalln_tiles == 2) c.TW = ov.smalln_tiles;
         return c;
     }
+    // many tiles, more columns than the single-pass forms take: the chunked walk
+    c.walk = wk && form == QG_FORM_AUTO && tiles >= kWkAutoTiles;
+    if (c.walk) return c;
     c.lds = form == QG_FORM_SMALLN_LDS ||
             (form != QG_FORM_SMALLN_REGS && (units >= 32 * 4 || (C == 2 && tiles <= 1024)));
     if (c.lds) {
@@ -1195,15 +1417,15 @@ void launch_stream(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
 // Workgroups per problem for the streamed form: the resident slots (two
 // workgroups per CU) shared in proportion to the tiles, at most kStTiles tiles
 // per workgroup. Fills wg_begin, wgs and the compact begin array; returns the grid.
-int64_t stream_grid(SnArgs& a, int cus) {
+int64_t stream_grid(SnArgs& a, int cus, int per_cu = kStPerCu, int tmax = kStTiles) {
     int64_t tiles = 0;
     for (int i = 0; i < a.count; ++i) tiles += a.p[i].tiles;
-    const int64_t slots = kStPerCu * (int64_t)std::max(cus, 1);
+    const int64_t slots = per_cu * (int64_t)std::max(cus, 1);
     int64_t wgs = 0;
     for (int i = 0; i < a.count; ++i) {
         const int64_t t = a.p[i].tiles;
         int64_t g = (slots * t + tiles - 1) / tiles;
-        g = std::max<int64_t>(g, qg::ceil_div(t, kStTiles));
+        g = std::max<int64_t>(g, qg::ceil_div(t, tmax));
         g = std::min<int64_t>(std::max<int64_t>(g, 1), t);
         a.p[i].wg_begin = (int32_t)wgs;
         a.p[i].wgs = (int32_t)g;
@@ -1211,6 +1433,26 @@ int64_t stream_grid(SnArgs& a, int cus) {
         wgs += g;
     }
     return wgs;
+}
+
+template <int C>
+void launch_walk(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
+    const auto kern = q4k_smalln_walk_kernel<C>;
+    static std::atomic<bool> attr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr[dev].load(std::memory_order_acquire)) {
+        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr[dev].store(true, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWkWaves), lds, s, a);
+}
+
+// Dynamic LDS of the walk form: two chunk buffers, or the parked sums if larger.
+size_t walk_lds_bytes(int C, int nmax) {
+    const size_t rb = C == 1 ? WkGeom<1>::RB : WkGeom<2>::RB;
+    const size_t tb = C == 1 ? WkGeom<1>::TB : WkGeom<2>::TB;
+    const size_t bs = (nmax * rb + tb + 15) / 16 * 16;
+    return std::max(2 * bs, (size_t)kWkTiles * 4 * 1024);
 }
 
 void launch_lds_any(const SnArgs& a, int grid, int C, int TW, int D, size_t lds, hipStream_t s) {
@@ -1279,6 +1521,14 @@ qg_status run(const qg_gemm_problem* probs, int count, hipStream_t stream) {
     if (cfg.dot) return qg::smalln_dot_launch(probs, count, stream);
     if (cfg.lds) {
         launch_lds_any(a, (int)wgs, C, cfg.TW, cfg.D, sw_lds_bytes(C, cfg.TW, nmax), stream);
+        return qg::launch_status("qgemm_q4k_smalln");
+    }
+    if (cfg.walk) {
+        const int64_t grid = stream_grid(a, qg::device_cus(), 1, kWkTiles);
+        if (C == 1)
+            launch_walk<1>(a, (int)grid, walk_lds_bytes(1, nmax), stream);
+        else
+            launch_walk<2>(a, (int)grid, walk_lds_bytes(2, nmax), stream);
         return qg::launch_status("qgemm_q4k_smalln");
     }
     if (cfg.stream) {

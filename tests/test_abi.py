@@ -337,7 +337,7 @@ def test_smalln_forced_forms_keep_validation(L):
     # forcing a form does not relax the small-N argument checks
     f = L.qgemm_q4k_smalln
     for form in (qg.FORM_SMALLN_DOT, qg.FORM_SMALLN_REGS, qg.FORM_SMALLN_LDS, qg.FORM_SMALLN_LDS1,
-                 qg.FORM_SMALLN_STREAM):
+                 qg.FORM_SMALLN_STREAM, qg.FORM_SMALLN_WALK):
         with qg.launch_override(smalln_form=form):
             assert f(C, A, 256, B, 64, 64, 256, 0, None) == ESHAPE
             assert f(C, A, 128, B, 64, 64, 256, 3, None) == ESHAPE   # ldx < K
@@ -348,7 +348,7 @@ def test_smalln_forced_forms_keep_validation(L):
 def test_launch_override_validation(L):
     O = qg._LaunchOverride
     assert L.qg_set_launch_override(None) == OK
-    for field, bad in [("gemv_waves", 3), ("gemv_waves", 16), ("smalln_form", 6), ("smalln_waves", 16),
+    for field, bad in [("gemv_waves", 3), ("gemv_waves", 16), ("smalln_form", 7), ("smalln_waves", 16),
                        ("smalln_tiles", 3), ("smalln_depth", 1), ("verify_form", 3), ("verify_waves", 2),
                        ("verify_tiles", 8)]:
         o = O()

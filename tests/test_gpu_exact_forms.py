@@ -32,7 +32,8 @@ from tests.gpu_helpers import DEV, case, packed_q4k, packed_q8_0, to_dev
 pytestmark = pytest.mark.gpu
 
 FORMS = {"auto": qg.FORM_AUTO, "regs": qg.FORM_SMALLN_REGS, "lds": qg.FORM_SMALLN_LDS,
-         "lds1": qg.FORM_SMALLN_LDS1, "dot": qg.FORM_SMALLN_DOT, "stream": qg.FORM_SMALLN_STREAM}
+         "lds1": qg.FORM_SMALLN_LDS1, "dot": qg.FORM_SMALLN_DOT, "stream": qg.FORM_SMALLN_STREAM,
+         "walk": qg.FORM_SMALLN_WALK}
 
 
 @functools.lru_cache(maxsize=None)
@@ -116,7 +117,7 @@ def check_exact(Y, W, M, K, X, what):
 SMALLN_CASES = [("auto", N) for N in (1, 2, 3, 4, 5, 8, 9, 16, 17, 32)] + \
                [("regs", N) for N in (5, 17, 32)] + [("lds", N) for N in (5, 17, 32)] + \
                [("lds1", N) for N in (5, 8)] + [("dot", N) for N in (1, 5, 8)] + \
-               [("stream", N) for N in (1, 5, 8)]
+               [("stream", N) for N in (1, 5, 8)] + [("walk", N) for N in (1, 5, 16, 17, 32)]
 
 
 @pytest.mark.parametrize("form,N", SMALLN_CASES)
@@ -135,7 +136,8 @@ def test_smalln_exact(form, N, M, K):
 
 
 @pytest.mark.parametrize("form,N", [("auto", 5), ("auto", 32), ("regs", 5), ("regs", 32), ("lds", 5),
-                                    ("lds", 32), ("lds1", 5), ("dot", 5), ("stream", 5)])
+                                    ("lds", 32), ("lds1", 5), ("dot", 5), ("stream", 5),
+                                    ("walk", 5), ("walk", 32)])
 def test_smalln_zero_scales_exact_zero_random_x(form, N):
     # d = dmin = 0 in every block: exactly 0 whatever the activations
     M, K = 100, 3584

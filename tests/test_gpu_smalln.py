@@ -258,6 +258,41 @@ def test_streamed_form():
                 assert_within(Yc[n], Yr[n], Ar[n], f"streamed M={M} K={K} col {n}")
 
 
+@pytest.mark.parametrize("N", [1, 5, 16, 17, 32])
+def test_walk_form(N):
+    # chunked walk form (one workgroup per CU walking up to ten tiles, K in chunks
+    # of four super-blocks for N <= 16, two above): chunk counts with a ragged last
+    # chunk (K = 768, 3328, 9984), one super-block, ragged tiles, walks of one to
+    # ten tiles (30000 rows: 1875 tiles), two problems of different K in one batch
+    qg.launch_override(smalln_form=qg.FORM_SMALLN_WALK).set()
+    batches = [[(530, 768, N), (77, 256, N), (1000, 3328, N)],
+               [(30000, 512, N)],
+               [(4000, 9984, N), (3001, 1280, N)]]
+    for bi, shapes in enumerate(batches):
+        probs, refs = [], []
+        for i, (M, K, n_) in enumerate(shapes):
+            W = workloads.q4k_blocks(M, K, key=(44, bi, i))
+            X = workloads.x_columns(K, n_, key=(44, bi, i, n_))
+            Y = torch.full((n_, (M + 3) // 4 * 4), float("nan"), device="cuda:0")
+            rows = sample_rows(M, 192, seed=M + i) if M * K * n_ > 1 << 26 else None
+            probs.append((packed_q4k(W, M, K), to_dev(X), Y, M, K))
+            refs.append((rows, oracle.gemm_q4k(W, M, K, X, rows=rows)))
+        case(f"qgemm_q4k_smalln_batch walk N={N} batch {bi}: {shapes}")
+        qg.qgemm_q4k_smalln_batch(probs)
+        torch.cuda.synchronize()
+        first = [p[2].clone() for p in probs]
+        qg.qgemm_q4k_smalln_batch(probs)
+        torch.cuda.synchronize()
+        for (w, X, Y, M, K), Y0, (rows, (Yr, Ar)) in zip(probs, first, refs):
+            assert torch.equal(Y[:, :M], Y0[:, :M]), "walk form not deterministic"
+            assert not torch.isnan(Y[:, :M]).any(), "walk form left outputs unwritten"
+            Yc = Y.cpu().numpy()[:, :M]
+            if rows is not None:
+                Yc = Yc[:, rows]
+            for n in range(X.shape[0]):
+                assert_within(Yc[n], Yr[n], Ar[n], f"walk M={M} K={K} col {n}")
+
+
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("M,K", [(200, 512), (65, 3328), (48, 9984), (1, 256)])
 def test_dot_form_shapes(M, K, N):
