@@ -310,7 +310,7 @@ def counter_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
                     wp_, _, _, M_, K_ = layers[L][i]
                     X_ = torch.from_numpy(wl.x_columns(K_, N, key=(5, L, i, N))).to(dev)
                     grp.append((wp_, X_, torch.empty((N, (M_ + 3) // 4 * 4), device=dev), M_, K_))
-                qg.qgemm_q4k_smalln_batch(grp)
+                qg.qgemm_q4k_smalln_batch_ws(grp)
     for L in range(n_layers):  # N = 5 on int8 activations
         for st in wl.LAYER_STAGES:
             grp = []
@@ -501,9 +501,15 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
                     grp.append((wp_, X_, torch.empty((N, (M_ + 3) // 4 * 4), device=dev), M_, K_))
                 sstages.append(grp)
 
+        # the workspace entry point, which may split few-tile stages over K slices
+        # (its second, summing launch is part of the step); one scratch buffer serves
+        # every stage, allocated before the timed region
+        needs = [qg.qgemm_q4k_smalln_batch_workspace_bytes(grp) for grp in sstages]
+        sws = qg.Workspace(dev, max(max(needs), 1))
+
         def vstep(sts=sstages):
             for grp in sts:
-                qg.qgemm_q4k_smalln_batch(grp)
+                qg.qgemm_q4k_smalln_batch_ws(grp, sws)
 
         ms = graph_ms(torch, vstep, 5)
         flat = [m for grp in sstages for m in grp]
@@ -517,7 +523,9 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
             per_stage[name] = {"avg_us": round(us, 3), "GBps": round(nb_ / (us * 1e-6) / 1e9, 1)}
         rows[f"smalln_verify_N{N}"] = {"ms_per_step": round(ms, 4), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
                                        "bytes": int(b), "verified_tokens_per_s": round(N * 1e3 / ms, 1),
-                                       "launches_per_step": len(sstages), "per_stage": per_stage}
+                                       "launches_per_step": len(sstages) + sum(1 for n_ in needs if n_ > 0),
+                                       "entry_point": "qgemm_q4k_smalln_batch_ws",
+                                       "workspace_bytes": int(max(needs)), "per_stage": per_stage}
         log(f"row smalln N={N}: {rows[f'smalln_verify_N{N}']}")
         del sstages, flat
 

@@ -275,6 +275,26 @@ typedef struct {
 qg_status qgemm_q4k_smalln_batch(const qg_gemm_problem* problems /* host */, int count, qg_stream_t stream);
 
 /*
+ * The same batch with a caller-owned workspace ("Why Local LLMs Don't Need C++ or
+ * Python", section 4: the batched verification pass, here for batches of few
+ * tiles and many columns, where the activations outweigh the weights). With a
+ * workspace the library may split each product over groups of tiles that share
+ * one staging of the activations and over slices of K; the slices' partial sums go
+ * to the workspace and a second launch adds them in slice order, so results stay
+ * deterministic and equal, to the bound in Arithmetic above, those of
+ * qgemm_q4k_smalln_batch (with other rounding order). _workspace_bytes gives the
+ * bytes the batch needs on the current device (0: none; invalid problems: 0);
+ * any 16-byte-aligned device buffer of at least that size serves. It needs no
+ * clearing and is left with undefined contents, so a buffer shared with the
+ * LM-head calls (whose workspaces must stay all-zero) has to be cleared again
+ * (qg_workspace_clear) before they use it. A smaller or NULL workspace where one
+ * is needed: QG_ERR_WORKSPACE. Calls that share a workspace must not overlap.
+ */
+size_t qgemm_q4k_smalln_batch_workspace_bytes(const qg_gemm_problem* problems /* host */, int count);
+qg_status qgemm_q4k_smalln_batch_ws(const qg_gemm_problem* problems /* host */, int count, void* workspace,
+                                    size_t workspace_bytes, qg_stream_t stream);
+
+/*
  * Fused LM head ("Why Local LLMs Don't Need C++ or Python", section 2: the final
  * projection and the argmax reduction stay on the device and a single int32 token
  * id crosses to the host instead of the logit vector): logits = W x (W an M x K
@@ -417,7 +437,9 @@ qg_status lmhead_topk(const void* w_packed, const float* x, int64_t M, int64_t K
  *                 the streamed single-pass form (workgroups walk several tiles;
  *                 the single-pass shapes, the weights of each matrix < 2 GiB), or
  *                 the chunked walk form (one workgroup per CU walks several tiles
- *                 chunk by chunk along K; any K, the weights of each matrix < 2 GiB).
+ *                 chunk by chunk along K; any K, the weights of each matrix < 2 GiB),
+ *                 or that form over tile groups and K slices (the _ws entry point
+ *                 with a workspace only).
  *   smalln_waves  wavefronts per workgroup of the register-staged form: 1..8.
  *   smalln_tiles  16-row tiles per workgroup (matrix-core forms): 1, 2, 4.
  *   smalln_depth  weight-queue depth in chunks of the chunked-LDS form: 2..4.
@@ -433,6 +455,7 @@ qg_status lmhead_topk(const void* w_packed, const float* x, int64_t M, int64_t K
 #define QG_FORM_SMALLN_DOT 4
 #define QG_FORM_SMALLN_STREAM 5
 #define QG_FORM_SMALLN_WALK 6
+#define QG_FORM_SMALLN_SPLIT 7
 #define QG_FORM_VERIFY_MFMA 1
 #define QG_FORM_VERIFY_DOT 2
 typedef struct {

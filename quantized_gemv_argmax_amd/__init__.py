@@ -51,8 +51,8 @@ class _LaunchOverride(ctypes.Structure):
 
 # kernel forms a launch override can force (include/qgemv.h)
 FORM_AUTO = 0
-FORM_SMALLN_REGS, FORM_SMALLN_LDS, FORM_SMALLN_LDS1, FORM_SMALLN_DOT, FORM_SMALLN_STREAM, FORM_SMALLN_WALK = \
-    1, 2, 3, 4, 5, 6
+FORM_SMALLN_REGS, FORM_SMALLN_LDS, FORM_SMALLN_LDS1, FORM_SMALLN_DOT, FORM_SMALLN_STREAM, FORM_SMALLN_WALK, \
+    FORM_SMALLN_SPLIT = 1, 2, 3, 4, 5, 6, 7
 FORM_VERIFY_MFMA, FORM_VERIFY_DOT = 1, 2
 
 
@@ -92,6 +92,8 @@ _SIGS = {
     "qgemv_q6k": (_I, [_P, _P, _P, _I64, _I64, _P]),
     "qgemm_q4k_smalln": (_I, [_P, _P, _I64, _P, _I64, _I64, _I64, _I64, _P]),
     "qgemm_q4k_smalln_batch": (_I, [ctypes.POINTER(_GemmProblem), _I, _P]),
+    "qgemm_q4k_smalln_batch_workspace_bytes": (_SZ, [ctypes.POINTER(_GemmProblem), _I]),
+    "qgemm_q4k_smalln_batch_ws": (_I, [ctypes.POINTER(_GemmProblem), _I, _P, _SZ, _P]),
     "qg_set_launch_override": (_I, [ctypes.c_void_p]),
     "qg_get_launch_override": (_I, [ctypes.c_void_p]),
     "lmhead_argmax_verify_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
@@ -417,9 +419,7 @@ def qgemm_q4k_smalln(w: torch.Tensor, X: torch.Tensor, M: int, K: int, Y: torch.
     return Y
 
 
-def qgemm_q4k_smalln_batch(problems):
-    """problems: list of (w_packed, X, Y, M, K) with X (N, ldx) and Y (N, ldy) as in
-    qgemm_q4k_smalln; one launch for all of them. Returns the Y tensors."""
+def _gemm_problems(problems):
     arr = (_GemmProblem * len(problems))()
     dev = None
     for i, (w, X, Y, M, K) in enumerate(problems):
@@ -429,7 +429,35 @@ def qgemm_q4k_smalln_batch(problems):
         if X.stride(1) != 1 or X.stride(0) != ldx or Y.stride(1) != 1 or Y.shape[0] != N:
             raise ValueError("X and Y must be contiguous (N, ld) tensors with the same N")
         arr[i] = _GemmProblem(_ptr(w), _ptr(X), ldx, _ptr(Y), Y.stride(0), M, K, N)
+    return arr, dev
+
+
+def qgemm_q4k_smalln_batch(problems):
+    """problems: list of (w_packed, X, Y, M, K) with X (N, ldx) and Y (N, ldy) as in
+    qgemm_q4k_smalln; one launch for all of them. Returns the Y tensors."""
+    arr, dev = _gemm_problems(problems)
     _check("qgemm_q4k_smalln_batch", lib().qgemm_q4k_smalln_batch(arr, len(problems), _stream(dev)))
+    return [p[2] for p in problems]
+
+
+def qgemm_q4k_smalln_batch_workspace_bytes(problems) -> int:
+    arr, _ = _gemm_problems(problems)
+    return lib().qgemm_q4k_smalln_batch_workspace_bytes(arr, len(problems))
+
+
+def qgemm_q4k_smalln_batch_ws(problems, ws: Workspace | None = None):
+    """qgemm_q4k_smalln_batch with a workspace (sized by
+    qgemm_q4k_smalln_batch_workspace_bytes; a per-device scratch buffer if None),
+    which lets the library split few-tile, many-column products over K slices. The
+    workspace's contents are left undefined."""
+    arr, dev = _gemm_problems(problems)
+    need = lib().qgemm_q4k_smalln_batch_workspace_bytes(arr, len(problems))
+    if ws is None:  # scratch contents: never the zero-kept workspace of the LM-head calls
+        key = ("scratch", str(dev))
+        ws = _default_ws.setdefault(key, Workspace(dev))
+    ws.ensure(need)
+    _check("qgemm_q4k_smalln_batch_ws",
+           lib().qgemm_q4k_smalln_batch_ws(arr, len(problems), ws.ptr(), ws.nbytes(), _stream(dev)))
     return [p[2] for p in problems]
 
 

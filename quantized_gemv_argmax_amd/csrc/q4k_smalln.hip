@@ -61,7 +61,10 @@ struct SnProb {
     float* Y;
     int64_t ldx, ldy;
     int32_t M, nb, N, tiles, wg_begin;
-    int32_t wgs;  // workgroups of this problem (streamed form)
+    int32_t wgs;        // streamed and walk forms: workgroups (walk: tile groups) of this problem
+    int32_t slices;     // walk form: K slices (workgroups = wgs * slices)
+    int32_t slice_sbs;  // super-blocks per K slice
+    float* part;        // walk form with K slices: partial sums (qg_f4 per lane) instead of Y
 };
 struct SnArgs {
     int32_t begin[QG_MAX_BATCH];
@@ -1019,29 +1022,33 @@ __global__ __launch_bounds__(64 * W, 4) void q4k_smalln_stream_kernel(SnArgs a) 
 // fp32 matrix-core product); every column block c of 16 columns reuses one B.
 constexpr int kWkWaves = 16, kWkTiles = 10;
 constexpr int64_t kWkAutoTiles = 1024;
+constexpr int kSpMaxSlices = 16, kSpAutoCols = 5;
 
-template <int C>
+
+template <int C, int KC_, int TMAX>
 struct WkGeom {
-    static constexpr int KC = 4 / C;                                       // super-blocks per chunk
-    static constexpr int MU = (kWkTiles * KC + kWkWaves - 1) / kWkWaves;  // units per wavefront and chunk
+    static constexpr int KC = KC_;                                     // super-blocks per chunk
+    static constexpr int MU = (TMAX * KC + kWkWaves - 1) / kWkWaves;  // units per wavefront and chunk
     static constexpr int RB = (KC * 256 + 8) * 2;                          // bytes per activation row
     static constexpr int TB = KC * 8 * 16 * C * 4;                          // sub-block sum table bytes
     static constexpr int GC = KC * 32;                                      // 8-element groups per column
 };
 
-// Activations of chunk q into registers: thread tid takes groups tid and tid + 1024
-// of the chunk (group g: column g / GC, elements 8 (g % GC)..+7 of the chunk; N GC
-// <= 2048). Groups past N or past K read zeros without a memory access.
-template <int C>
-QG_DEV void wk_issue(float4 (&v)[2][2], __amdgpu_buffer_rsrc_t xr, const SnProb& P, int q, int tid) {
-    constexpr int KC = WkGeom<C>::KC, GC = WkGeom<C>::GC;
+// Activations of chunk q of the K slice [kb0, kb1) (super-blocks) into registers:
+// thread tid takes groups tid and tid + 1024 of the chunk (group g: column g / GC,
+// elements 8 (g % GC)..+7 of the chunk; the launcher keeps N GC <= 2048). Groups past N or past the
+// slice read zeros without a memory access.
+template <int C, int KC_>
+QG_DEV void wk_issue(float4 (&v)[2][2], __amdgpu_buffer_rsrc_t xr, const SnProb& P, int kb0, int kb1, int q,
+                     int tid) {
+    constexpr int KC = WkGeom<C, KC_, 1>::KC, GC = WkGeom<C, KC_, 1>::GC;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int g = tid + 1024 * r;
         const int n = g / GC, k8 = g % GC;
-        const int kk = q * KC * 256 + 8 * k8;
+        const int kk = (kb0 + q * KC) * 256 + 8 * k8;
         const uint32_t off =
-            (n < P.N && kk < P.nb * 256) ? (uint32_t)(((int64_t)n * P.ldx + kk) * 4) : kOutOfRange;
+            (n < P.N && kk < kb1 * 256) ? (uint32_t)(((int64_t)n * P.ldx + kk) * 4) : kOutOfRange;
         v[r][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
         v[r][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 16, 0));
     }
@@ -1050,9 +1057,9 @@ QG_DEV void wk_issue(float4 (&v)[2][2], __amdgpu_buffer_rsrc_t xr, const SnProb&
 // ... and from registers into a chunk buffer: fp16 rows of RB bytes per column,
 // then the table of -X_j[n] (16 C columns per sub-block j of the chunk, from the
 // same fp16 values; a quad of threads holds one sub-block of a column).
-template <int C>
+template <int C, int KC_>
 QG_DEV void wk_write(const float4 (&v)[2][2], unsigned char* buf, const SnProb& P, int tid) {
-    constexpr int RB = WkGeom<C>::RB, GC = WkGeom<C>::GC;
+    constexpr int RB = WkGeom<C, KC_, 1>::RB, GC = WkGeom<C, KC_, 1>::GC;
     float* table = reinterpret_cast<float*>(buf + P.N * RB);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -1118,9 +1125,9 @@ QG_DEV void wk_dot(qg_f4 (&acc)[C], const SwItem<1>& it, const unsigned char* bu
         for (int e = 0; e < 4; ++e) acc[c][e] = fmaf(dd, p[c][e], acc[c][e]);
 }
 
-template <int C>
+template <int C, int KC_, int TMAX>
 __global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_walk_kernel(SnArgs a) {
-    using Gm = WkGeom<C>;
+    using Gm = WkGeom<C, KC_, TMAX>;
     constexpr int KC = Gm::KC, MU = Gm::MU, RB = Gm::RB, TB = Gm::TB;
     extern __shared__ __align__(16) unsigned char lds[];
     const int wg = blockIdx.x;
@@ -1129,15 +1136,17 @@ __global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_walk_kernel(SnArg
     for (int i = 1; i < QG_MAX_BATCH; ++i)
         if (i < a.count && wg >= a.begin[i]) k = i;
     const SnProb P = a.p[k];
-    const int j = wg - P.wg_begin;
     const int G = P.wgs;
-    const int nt = (P.tiles - j + G - 1) / G;  // tiles of this walk, 1..kWkTiles
+    const int j = (wg - P.wg_begin) % G;  // tile group: tiles j, j + G, ...
+    const int h = (wg - P.wg_begin) / G;  // K slice
+    const int nt = (P.tiles - j + G - 1) / G;  // tiles of this walk, 1..TMAX
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tid = threadIdx.x;
     const int i = lane & 15, s = lane >> 4;
     const int nb = P.nb;
-    const int nq = (nb + KC - 1) / KC;
+    const int kb0 = h * P.slice_sbs, kb1 = min(nb, kb0 + P.slice_sbs);  // super-blocks of the slice
+    const int nq = (kb1 - kb0 + KC - 1) / KC;
     const uint32_t BS = ((uint32_t)(P.N * RB + TB) + 15u) & ~15u;  // bytes per chunk buffer
     const __amdgpu_buffer_rsrc_t wr =
         __builtin_amdgcn_make_buffer_rsrc((void*)P.w, (short)0, P.M * nb * 144, kQgRawBufferFlags);
@@ -1147,14 +1156,14 @@ __global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_walk_kernel(SnArg
 
     // chunk 0: activations, and the weights of this wavefront's units
     float4 vx[2][2];
-    wk_issue<C>(vx, xr, P, 0, tid);
+    wk_issue<C, KC>(vx, xr, P, kb0, kb1, 0, tid);
     SwItem<1> ring[MU];
 #pragma unroll
     for (int m = 0; m < MU; ++m) {
         const int ts = (wave + kWkWaves * m) / KC;
-        st_load(ring[m], wr, P, j + min(ts, nt - 1) * G, min(sb, nb - 1), i, s, ts < nt && sb < nb);
+        st_load(ring[m], wr, P, j + min(ts, nt - 1) * G, min(kb0 + sb, nb - 1), i, s, ts < nt && kb0 + sb < kb1);
     }
-    wk_write<C>(vx, lds, P, tid);
+    wk_write<C, KC>(vx, lds, P, tid);
     sw_barrier();
 
     uint32_t an[C];
@@ -1173,15 +1182,15 @@ __global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_walk_kernel(SnArg
 
     for (int q = 0; q < nq; ++q) {
         const unsigned char* cur = lds + (q & 1) * BS;
-        wk_issue<C>(vx, xr, P, q + 1, tid);  // past the last chunk: zeros, no memory access
-        const int b = q * KC + sb;
+        wk_issue<C, KC>(vx, xr, P, kb0, kb1, q + 1, tid);  // past the last chunk: zeros, no memory access
+        const int b = kb0 + q * KC + sb;
 #pragma unroll
         for (int m = 0; m < MU; ++m) {
             const int ts = (wave + kWkWaves * m) / KC;
-            if (ts < nt && b < nb) wk_dot<C>(acc[m], ring[m], cur, an, xt, sh);
-            st_load(ring[m], wr, P, j + min(ts, nt - 1) * G, min(b + KC, nb - 1), i, s, ts < nt && b + KC < nb);
+            if (ts < nt && b < kb1) wk_dot<C>(acc[m], ring[m], cur, an, xt, sh);
+            st_load(ring[m], wr, P, j + min(ts, nt - 1) * G, min(b + KC, nb - 1), i, s, ts < nt && b + KC < kb1);
         }
-        wk_write<C>(vx, lds + ((q + 1) & 1) * BS, P, tid);
+        wk_write<C, KC>(vx, lds + ((q + 1) & 1) * BS, P, tid);
         sw_barrier();
     }
 
@@ -1203,6 +1212,10 @@ __global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_walk_kernel(SnArg
         qg_f4 sum = park[((wave * KC) * C + c) * 64 + lane];
 #pragma unroll
         for (int b2 = 1; b2 < KC; ++b2) sum += park[((wave * KC + b2) * C + c) * 64 + lane];
+        if (P.part) {  // one of several K slices: the partial sums go to the workspace
+            reinterpret_cast<qg_f4*>(P.part)[(((int64_t)h * P.tiles + t) * C + c) * 64 + lane] = sum;
+            continue;
+        }
         if (i < rt) {
             const int row = t * T + i;
 #pragma unroll
@@ -1210,6 +1223,43 @@ __global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_walk_kernel(SnArg
                 const int n = 16 * c + 4 * s + e;
                 if (n < P.N) P.Y[(int64_t)n * P.ldy + row] = sum[e];
             }
+        }
+    }
+}
+
+// Sum of the K slices' partial sums of the walk form, in slice order (so results
+// are deterministic): one 64-lane workgroup per tile and column block.
+struct RdProb {
+    const qg_f4* part;
+    float* Y;
+    int64_t ldy;
+    int32_t M, N, tiles, slices, C, wg_begin;
+};
+struct RdArgs {
+    int32_t begin[QG_MAX_BATCH];
+    int32_t count;
+    RdProb p[QG_MAX_BATCH];
+};
+
+__global__ __launch_bounds__(64) void q4k_smalln_reduce_kernel(RdArgs a) {
+    const int wg = blockIdx.x;
+    int k = 0;
+#pragma unroll
+    for (int i = 1; i < QG_MAX_BATCH; ++i)
+        if (i < a.count && wg >= a.begin[i]) k = i;
+    const RdProb P = a.p[k];
+    const int l = wg - P.wg_begin;
+    const int t = l / P.C, c = l % P.C;
+    const int lane = threadIdx.x;
+    const int i = lane & 15, s = lane >> 4;
+    qg_f4 sum = P.part[((int64_t)t * P.C + c) * 64 + lane];
+    for (int h = 1; h < P.slices; ++h) sum += P.part[(((int64_t)h * P.tiles + t) * P.C + c) * 64 + lane];
+    const int rt = min(T, P.M - t * T);
+    if (i < rt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int n = 16 * c + 4 * s + e;
+            if (n < P.N) P.Y[(int64_t)n * P.ldy + t * T + i] = sum[e];
         }
     }
 }
@@ -1244,6 +1294,9 @@ SnProb make_sn(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy
     P.nb = (int32_t)(K / 256);
     P.N = (int32_t)N;
     P.tiles = (int32_t)qg::ceil_div(M, T);
+    P.slices = 1;
+    P.slice_sbs = P.nb;
+    P.part = nullptr;
     return P;
 }
 
@@ -1269,8 +1322,9 @@ struct SnCfg {
     bool dot;   // vector-ALU dot-product kernel (N <= 8, q4k_smalln_dot.hip)
     bool stream;  // streamed single-pass kernel (single-pass shapes, many tiles)
     bool walk;    // chunked walk kernel (many tiles, up to 32 columns)
+    bool split;   // the walk kernel over groups of tiles and K slices, summed by a second kernel
 };
-SnCfg choose_cfg(const SnArgs& a, int C) {
+SnCfg choose_cfg(const SnArgs& a, int C, bool ws) {
     const qg_launch_override& ov = qg::launch_override();
     const int form = ov.smalln_form;
     int units = INT_MAX;
@@ -1281,7 +1335,7 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
         tiles += a.p[i].tiles;
         ncol = std::max(ncol, (int)a.p[i].N);
     }
-    SnCfg c{1, tiles > 256 ? 2 : 1, false, 2, false, false, false, false};
+    SnCfg c{1, tiles > 256 ? 2 : 1, false, 2, false, false, false, false, false};
     if (C == 2 && tiles > 1024) c.TW = 4;
     // Form selection, from measurements on the 7B shapes (stage times in us, register
     // form -> chosen form):
@@ -1308,6 +1362,9 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
     bool wk = true;
     for (int i = 0; i < a.count; ++i) wk = wk && (int64_t)a.p[i].M * a.p[i].nb * 144 < (int64_t)INT32_MAX;
     c.walk = wk && form == QG_FORM_SMALLN_WALK;
+    if (c.walk) return c;
+    // K slices need a workspace for their partial sums
+    c.split = c.walk = ws && wk && form == QG_FORM_SMALLN_SPLIT;
     if (c.walk) return c;
     // Single-pass form: every problem with K <= 512 * 8 and N <= 8 (one round of
     // activation loads per lane, all super-blocks of a row in flight at once).
@@ -1337,6 +1394,11 @@ SnCfg choose_cfg(const SnArgs& a, int C) {
     }
     // many tiles, more columns than the single-pass forms take: the chunked walk
     c.walk = wk && form == QG_FORM_AUTO && tiles >= kWkAutoTiles;
+    if (c.walk) return c;
+    // fewer tiles, with a workspace: the walk over tile groups and K slices, where
+    // the activations outweigh the weights (every workgroup of the other forms
+    // reads all of X for its one or two tiles)
+    c.split = c.walk = ws && wk && form == QG_FORM_AUTO && ncol >= kSpAutoCols;
     if (c.walk) return c;
     c.lds = form == QG_FORM_SMALLN_LDS ||
             (form != QG_FORM_SMALLN_REGS && (units >= 32 * 4 || (C == 2 && tiles <= 1024)));
@@ -1435,9 +1497,9 @@ int64_t stream_grid(SnArgs& a, int cus, int per_cu = kStPerCu, int tmax = kStTil
     return wgs;
 }
 
-template <int C>
+template <int C, int KC, int TMAX>
 void launch_walk(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
-    const auto kern = q4k_smalln_walk_kernel<C>;
+    const auto kern = q4k_smalln_walk_kernel<C, KC, TMAX>;
     static std::atomic<bool> attr[64];
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr[dev].load(std::memory_order_acquire)) {
@@ -1447,12 +1509,71 @@ void launch_walk(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWkWaves), lds, s, a);
 }
 
+// Walk-form shapes: column blocks, super-blocks per chunk, most tiles per
+// workgroup, and tiles per group when K is sliced (KC C = 4 for up to 32 columns;
+// KC = 8 for up to 8 columns, where groups of four tiles give every wavefront two
+// units per chunk: N = 5 down projection 19.7 -> 16.7 us, against 18.9 with
+// groups of two).
+struct WkShape {
+    int C, KC, TMAX, T;
+};
+
 // Dynamic LDS of the walk form: two chunk buffers, or the parked sums if larger.
-size_t walk_lds_bytes(int C, int nmax) {
-    const size_t rb = C == 1 ? WkGeom<1>::RB : WkGeom<2>::RB;
-    const size_t tb = C == 1 ? WkGeom<1>::TB : WkGeom<2>::TB;
+size_t walk_lds_bytes(const WkShape& w, int nmax) {
+    const size_t rb = (size_t)(w.KC * 256 + 8) * 2;
+    const size_t tb = (size_t)w.KC * 8 * 16 * w.C * 4;
     const size_t bs = (nmax * rb + tb + 15) / 16 * 16;
-    return std::max(2 * bs, (size_t)kWkTiles * 4 * 1024);
+    return std::max(2 * bs, (size_t)w.TMAX * w.KC * w.C * 1024);
+}
+
+WkShape walk_shape(int C, int nmax, bool split) {
+    if (C == 2) return WkShape{2, 2, kWkTiles, 8};
+    if (split && nmax <= 8) return WkShape{1, 8, 4, 4};
+    return WkShape{1, 4, kWkTiles, 4};
+}
+
+void launch_walk_any(const WkShape& w, const SnArgs& a, int grid, int nmax, hipStream_t s) {
+    const size_t lds = walk_lds_bytes(w, nmax);
+    if (w.C == 2)
+        launch_walk<2, 2, kWkTiles>(a, grid, lds, s);
+    else if (w.KC == 8)
+        launch_walk<1, 8, 4>(a, grid, lds, s);
+    else
+        launch_walk<1, 4, kWkTiles>(a, grid, lds, s);
+}
+
+// Tile groups and K slices of the walk form with a workspace: per problem, groups
+// of w.T tiles (enough units per chunk for the 16 wavefronts), and as
+// many K slices as give the problem its share of one workgroup per CU (at most
+// kSpMaxSlices). Slices of one super-block-range each write partial sums to the
+// workspace (problems left with one slice write Y). Fills wgs, slices,
+// slice_sbs, part, wg_begin and begin; returns the grid and the workspace bytes.
+int64_t split_grid(SnArgs& a, int cus, const WkShape& w, float* ws, size_t* need) {
+    const int C = w.C;
+    int64_t tiles = 0;
+    for (int i = 0; i < a.count; ++i) tiles += a.p[i].tiles;
+    int64_t wgs = 0;
+    size_t off = 0;
+    for (int i = 0; i < a.count; ++i) {
+        SnProb& P = a.p[i];
+        const int64_t G = qg::ceil_div(P.tiles, w.T);
+        const int64_t share = std::max<int64_t>(1, (int64_t)std::max(cus, 1) * P.tiles / tiles);
+        int64_t H = std::min<int64_t>({std::max<int64_t>(share / G, 1), kSpMaxSlices, P.nb});
+        P.slice_sbs = (int32_t)qg::ceil_div(P.nb, H);
+        H = qg::ceil_div(P.nb, P.slice_sbs);
+        P.wgs = (int32_t)G;
+        P.slices = (int32_t)H;
+        P.part = nullptr;
+        if (H > 1) {
+            P.part = ws ? ws + off / sizeof(float) : nullptr;
+            off += (size_t)H * P.tiles * C * 1024;
+        }
+        P.wg_begin = (int32_t)wgs;
+        a.begin[i] = (int32_t)wgs;
+        wgs += G * H;
+    }
+    *need = off;
+    return wgs;
 }
 
 void launch_lds_any(const SnArgs& a, int grid, int C, int TW, int D, size_t lds, hipStream_t s) {
@@ -1483,7 +1604,8 @@ void launch(const SnArgs& a, int grid, int W, hipStream_t s) {
 }
 
 // Validates the problems and fills the kernel arguments and launch shape.
-qg_status plan(const qg_gemm_problem* probs, int count, SnArgs& a, SnCfg& cfg, int& C, int64_t& wgs, int& nmax) {
+qg_status plan(const qg_gemm_problem* probs, int count, SnArgs& a, SnCfg& cfg, int& C, int64_t& wgs, int& nmax,
+               bool ws = false) {
     if (!probs) return qg::fail(QG_ERR_NULL, "NULL problem list");
     if (count < 1 || count > QG_MAX_BATCH)
         return qg::fail(QG_ERR_SHAPE, "count=%d not in [1, %d]", count, QG_MAX_BATCH);
@@ -1498,7 +1620,7 @@ qg_status plan(const qg_gemm_problem* probs, int count, SnArgs& a, SnCfg& cfg, i
         nmax = std::max(nmax, a.p[i].N);
     }
     C = nmax > 16 ? 2 : 1;
-    cfg = choose_cfg(a, C);
+    cfg = choose_cfg(a, C, ws);
     wgs = 0;
     for (int i = 0; i < count; ++i) {
         a.p[i].wg_begin = (int32_t)wgs;
@@ -1509,26 +1631,64 @@ qg_status plan(const qg_gemm_problem* probs, int count, SnArgs& a, SnCfg& cfg, i
     return QG_OK;
 }
 
-qg_status run(const qg_gemm_problem* probs, int count, hipStream_t stream) {
+// Workspace bytes the batch needs on the current device (0: none).
+size_t split_bytes(const qg_gemm_problem* probs, int count) {
     SnArgs a;
     SnCfg cfg;
     int C, nmax;
     int64_t wgs;
-    qg_status st = plan(probs, count, a, cfg, C, wgs, nmax);
+    if (plan(probs, count, a, cfg, C, wgs, nmax, true) || !cfg.split) return 0;
+    qg::clear_error();
+    const int cus = qg::check_device() == QG_OK ? qg::device_cus() : 256;
+    qg::clear_error();
+    size_t need = 0;
+    split_grid(a, cus, walk_shape(C, nmax, true), nullptr, &need);
+    return need;
+}
+
+qg_status run(const qg_gemm_problem* probs, int count, hipStream_t stream, void* ws = nullptr, size_t ws_bytes = 0,
+              bool ws_mode = false) {
+    SnArgs a;
+    SnCfg cfg;
+    int C, nmax;
+    int64_t wgs;
+    qg_status st = plan(probs, count, a, cfg, C, wgs, nmax, ws_mode);
     if (st) return st;
     st = qg::check_device();
     if (st) return st;
+    if (cfg.split) {
+        size_t need = 0;
+        const WkShape ws_shape = walk_shape(C, nmax, true);
+        const int64_t grid = split_grid(a, qg::device_cus(), ws_shape, (float*)ws, &need);
+        if (need > 0 && (!ws || ws_bytes < need))
+            return qg::fail(QG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+        if (need > 0 && !qg::aligned16(ws)) return qg::fail(QG_ERR_ALIGN, "workspace not 16-byte aligned");
+        launch_walk_any(ws_shape, a, (int)grid, nmax, stream);
+        st = qg::launch_status("qgemm_q4k_smalln_batch_ws");
+        if (st || need == 0) return st;
+        RdArgs r{};
+        int64_t rw = 0;
+        for (int i = 0; i < a.count; ++i) {
+            const SnProb& P = a.p[i];
+            if (!P.part) continue;
+            RdProb& q = r.p[r.count];
+            q = RdProb{(const qg_f4*)P.part, P.Y, P.ldy, P.M, P.N, P.tiles, P.slices, C, (int32_t)rw};
+            r.begin[r.count] = (int32_t)rw;
+            ++r.count;
+            rw += (int64_t)P.tiles * C;
+        }
+        hipLaunchKernelGGL(q4k_smalln_reduce_kernel, dim3((unsigned)rw), dim3(64), 0, stream, r);
+        return qg::launch_status("qgemm_q4k_smalln_batch_ws");
+    }
     if (cfg.dot) return qg::smalln_dot_launch(probs, count, stream);
     if (cfg.lds) {
         launch_lds_any(a, (int)wgs, C, cfg.TW, cfg.D, sw_lds_bytes(C, cfg.TW, nmax), stream);
         return qg::launch_status("qgemm_q4k_smalln");
     }
     if (cfg.walk) {
-        const int64_t grid = stream_grid(a, qg::device_cus(), 1, kWkTiles);
-        if (C == 1)
-            launch_walk<1>(a, (int)grid, walk_lds_bytes(1, nmax), stream);
-        else
-            launch_walk<2>(a, (int)grid, walk_lds_bytes(2, nmax), stream);
+        const WkShape w = walk_shape(C, nmax, false);
+        const int64_t grid = stream_grid(a, qg::device_cus(), 1, w.TMAX);
+        launch_walk_any(w, a, (int)grid, nmax, stream);
         return qg::launch_status("qgemm_q4k_smalln");
     }
     if (cfg.stream) {
@@ -1574,6 +1734,17 @@ qg_status qgemm_q4k_smalln(const void* w, const float* X, int64_t ldx, float* Y,
 qg_status qgemm_q4k_smalln_batch(const qg_gemm_problem* problems, int count, qg_stream_t stream) {
     qg::clear_error();
     return run(problems, count, (hipStream_t)stream);
+}
+
+size_t qgemm_q4k_smalln_batch_workspace_bytes(const qg_gemm_problem* problems, int count) {
+    qg::clear_error();
+    return split_bytes(problems, count);
+}
+
+qg_status qgemm_q4k_smalln_batch_ws(const qg_gemm_problem* problems, int count, void* workspace,
+                                    size_t workspace_bytes, qg_stream_t stream) {
+    qg::clear_error();
+    return run(problems, count, (hipStream_t)stream, workspace, workspace_bytes, true);
 }
 
 }  // extern "C"

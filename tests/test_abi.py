@@ -337,7 +337,7 @@ def test_smalln_forced_forms_keep_validation(L):
     # forcing a form does not relax the small-N argument checks
     f = L.qgemm_q4k_smalln
     for form in (qg.FORM_SMALLN_DOT, qg.FORM_SMALLN_REGS, qg.FORM_SMALLN_LDS, qg.FORM_SMALLN_LDS1,
-                 qg.FORM_SMALLN_STREAM, qg.FORM_SMALLN_WALK):
+                 qg.FORM_SMALLN_STREAM, qg.FORM_SMALLN_WALK, qg.FORM_SMALLN_SPLIT):
         with qg.launch_override(smalln_form=form):
             assert f(C, A, 256, B, 64, 64, 256, 0, None) == ESHAPE
             assert f(C, A, 128, B, 64, 64, 256, 3, None) == ESHAPE   # ldx < K
@@ -345,10 +345,25 @@ def test_smalln_forced_forms_keep_validation(L):
     assert qg.get_launch_override()["smalln_form"] == 0
 
 
+def test_smalln_ws_sizes_and_validation(L):
+    P = qg._GemmProblem
+    arr = (P * 2)(P(C, A, 18944, B, 3584, 3584, 18944, 32), P(C, A, 3584, B, 4608, 4608, 3584, 32))
+    assert L.qgemm_q4k_smalln_batch_workspace_bytes(arr, 0) == 0            # invalid count
+    bad = (P * 1)(P(C, A, 100, B, 3584, 3584, 18944, 32))                    # ldx < K
+    assert L.qgemm_q4k_smalln_batch_workspace_bytes(bad, 1) == 0
+    with qg.launch_override(smalln_form=qg.FORM_SMALLN_SPLIT):
+        need = L.qgemm_q4k_smalln_batch_workspace_bytes(arr, 2)
+        assert need > 0 and need % 1024 == 0
+        # a partial sum per K slice, tile and 16-column block, at most 16 slices
+        assert need <= 16 * (224 + 288) * 2 * 1024
+    assert L.qgemm_q4k_smalln_batch_ws(None, 1, None, 0, None) == ENULL
+    assert L.qgemm_q4k_smalln_batch_ws(bad, 1, None, 0, None) == ESHAPE
+
+
 def test_launch_override_validation(L):
     O = qg._LaunchOverride
     assert L.qg_set_launch_override(None) == OK
-    for field, bad in [("gemv_waves", 3), ("gemv_waves", 16), ("smalln_form", 7), ("smalln_waves", 16),
+    for field, bad in [("gemv_waves", 3), ("gemv_waves", 16), ("smalln_form", 8), ("smalln_waves", 16),
                        ("smalln_tiles", 3), ("smalln_depth", 1), ("verify_form", 3), ("verify_waves", 2),
                        ("verify_tiles", 8)]:
         o = O()

@@ -293,6 +293,68 @@ def test_walk_form(N):
                 assert_within(Yc[n], Yr[n], Ar[n], f"walk M={M} K={K} col {n}")
 
 
+@pytest.mark.parametrize("N", [1, 5, 16, 17, 32])
+def test_split_walk_form(N):
+    # the walk form over tile groups and K slices (with a workspace): slices of one
+    # to many super-blocks, a ragged last slice, problems left with one slice next
+    # to sliced ones in one batch, ragged tiles; partial sums added in slice order
+    qg.launch_override(smalln_form=qg.FORM_SMALLN_SPLIT).set()
+    batches = [[(530, 768, N), (77, 256, N), (1000, 3328, N)],
+               [(3584, 18944, N)],
+               [(33, 9984, N), (3001, 1280, N)]]
+    for bi, shapes in enumerate(batches):
+        probs, refs = [], []
+        for i, (M, K, n_) in enumerate(shapes):
+            W = workloads.q4k_blocks(M, K, key=(45, bi, i))
+            X = workloads.x_columns(K, n_, key=(45, bi, i, n_))
+            Y = torch.full((n_, (M + 3) // 4 * 4), float("nan"), device="cuda:0")
+            rows = sample_rows(M, 192, seed=M + i) if M * K * n_ > 1 << 26 else None
+            probs.append((packed_q4k(W, M, K), to_dev(X), Y, M, K))
+            refs.append((rows, oracle.gemm_q4k(W, M, K, X, rows=rows)))
+        need = qg.qgemm_q4k_smalln_batch_workspace_bytes(probs)
+        case(f"qgemm_q4k_smalln_batch_ws split N={N} batch {bi}: {shapes}, workspace {need}")
+        assert need > 0
+        # scratch contents do not matter: fill the workspace with NaN bytes first
+        ws = qg.Workspace("cuda:0", need)
+        ws.buf.fill_(0xff)
+        qg.qgemm_q4k_smalln_batch_ws(probs, ws)
+        torch.cuda.synchronize()
+        first = [p[2].clone() for p in probs]
+        qg.qgemm_q4k_smalln_batch_ws(probs, ws)
+        torch.cuda.synchronize()
+        for (w, X, Y, M, K), Y0, (rows, (Yr, Ar)) in zip(probs, first, refs):
+            assert torch.equal(Y[:, :M], Y0[:, :M]), "split walk form not deterministic"
+            assert not torch.isnan(Y[:, :M]).any(), "split walk form left outputs unwritten"
+            Yc = Y.cpu().numpy()[:, :M]
+            if rows is not None:
+                Yc = Yc[:, rows]
+            for n in range(X.shape[0]):
+                assert_within(Yc[n], Yr[n], Ar[n], f"split M={M} K={K} col {n}")
+
+
+@pytest.mark.parametrize("N", [5, 32])
+def test_batch_ws_7b_stages(N):
+    # the workspace entry point with the automatic choice on the 7B decode stages
+    # (the q/k/v, o and down stages take the K-sliced walk): sampled rows
+    for si, stage in enumerate(workloads.LAYER_STAGES):
+        probs, refs = [], []
+        for mi in stage:
+            name, M, K = workloads.LAYER_MATRICES[mi]
+            W = workloads.q4k_blocks(M, K, key=(46, mi, N))
+            X = workloads.x_columns(K, N, key=(46, mi, N, 1))
+            rows = sample_rows(M, 96, seed=M + K + N)
+            probs.append((packed_q4k(W, M, K), to_dev(X), torch.full((N, (M + 3) // 4 * 4), float("nan"),
+                                                                     device="cuda:0"), M, K))
+            refs.append((rows, oracle.gemm_q4k(W, M, K, X, rows=rows)))
+        case(f"qgemm_q4k_smalln_batch_ws 7B stage {si} N={N}")
+        qg.qgemm_q4k_smalln_batch_ws(probs)
+        torch.cuda.synchronize()
+        for (w, X, Y, M, K), (rows, (Yr, Ar)) in zip(probs, refs):
+            Yc = Y.cpu().numpy()[:, :M][:, rows]
+            for n in range(N):
+                assert_within(Yc[n], Yr[n], Ar[n], f"ws stage {si} M={M} K={K} col {n}")
+
+
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("M,K", [(200, 512), (65, 3328), (48, 9984), (1, 256)])
 def test_dot_form_shapes(M, K, N):
