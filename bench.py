@@ -502,8 +502,8 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
                 sstages.append(grp)
 
         # the workspace entry point, which may split few-tile stages over K slices
-        # (its second, summing launch is part of the step); one scratch buffer serves
-        # every stage, allocated before the timed region
+        # (the slices' sums are added by the last workgroup of each tile group); one
+        # workspace serves every stage, allocated and zeroed before the timed region
         needs = [qg.qgemm_q4k_smalln_batch_workspace_bytes(grp) for grp in sstages]
         sws = qg.Workspace(dev, max(max(needs), 1))
 
@@ -523,7 +523,7 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
             per_stage[name] = {"avg_us": round(us, 3), "GBps": round(nb_ / (us * 1e-6) / 1e9, 1)}
         rows[f"smalln_verify_N{N}"] = {"ms_per_step": round(ms, 4), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
                                        "bytes": int(b), "verified_tokens_per_s": round(N * 1e3 / ms, 1),
-                                       "launches_per_step": len(sstages) + sum(1 for n_ in needs if n_ > 0),
+                                       "launches_per_step": len(sstages),
                                        "entry_point": "qgemm_q4k_smalln_batch_ws",
                                        "workspace_bytes": int(max(needs)), "per_stage": per_stage}
         log(f"row smalln N={N}: {rows[f'smalln_verify_N{N}']}")

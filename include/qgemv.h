@@ -280,15 +280,17 @@ qg_status qgemm_q4k_smalln_batch(const qg_gemm_problem* problems /* host */, int
  * tiles and many columns, where the activations outweigh the weights). With a
  * workspace the library may split each product over groups of tiles that share
  * one staging of the activations and over slices of K; the slices' partial sums go
- * to the workspace and a second launch adds them in slice order, so results stay
- * deterministic and equal, to the bound in Arithmetic above, those of
- * qgemm_q4k_smalln_batch (with other rounding order). _workspace_bytes gives the
- * bytes the batch needs on the current device (0: none; invalid problems: 0);
- * any 16-byte-aligned device buffer of at least that size serves. It needs no
- * clearing and is left with undefined contents, so a buffer shared with the
- * LM-head calls (whose workspaces must stay all-zero) has to be cleared again
- * (qg_workspace_clear) before they use it. A smaller or NULL workspace where one
- * is needed: QG_ERR_WORKSPACE. Calls that share a workspace must not overlap.
+ * to the workspace, and the last workgroup of each tile group to finish (counted
+ * on a per-group counter in the workspace) adds them in slice order, so results
+ * stay deterministic and equal, to the bound in Arithmetic above, those of
+ * qgemm_q4k_smalln_batch (with another rounding order). _workspace_bytes gives
+ * the bytes the batch needs on the current device (0: none; invalid problems:
+ * 0). The workspace (16-byte aligned, at least that size) must be zero-filled
+ * before its first use (qg_workspace_clear); every call leaves its counters zero
+ * and the rest of it with undefined contents, so a buffer shared with the LM-head
+ * calls (whose workspaces must stay all-zero) has to be cleared again before they
+ * use it. A smaller or NULL workspace where one is needed: QG_ERR_WORKSPACE.
+ * Calls that share a workspace must not overlap.
  */
 size_t qgemm_q4k_smalln_batch_workspace_bytes(const qg_gemm_problem* problems /* host */, int count);
 qg_status qgemm_q4k_smalln_batch_ws(const qg_gemm_problem* problems /* host */, int count, void* workspace,

@@ -65,6 +65,7 @@ struct SnProb {
     int32_t slices;     // walk form: K slices (workgroups = wgs * slices)
     int32_t slice_sbs;  // super-blocks per K slice
     float* part;        // walk form with K slices: partial sums (qg_f4 per lane) instead of Y
+    uint32_t* ctr;      // and one arrival counter per tile group (zero between calls)
 };
 struct SnArgs {
     int32_t begin[QG_MAX_BATCH];
@@ -1204,62 +1205,73 @@ __global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_walk_kernel(SnArg
             for (int c = 0; c < C; ++c) park[(u * C + c) * 64 + lane] = acc[m][c];
     }
     sw_barrier();
-    if (wave >= nt) return;
-    const int t = j + wave * G;
+    // wavefront w < nt owns tile slot w from here on
+    const int t = j + min(wave, nt - 1) * G;
     const int rt = min(T, P.M - t * T);
+    qg_f4 sum[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        qg_f4 sum = park[((wave * KC) * C + c) * 64 + lane];
+        sum[c] = park[((min(wave, nt - 1) * KC) * C + c) * 64 + lane];
 #pragma unroll
-        for (int b2 = 1; b2 < KC; ++b2) sum += park[((wave * KC + b2) * C + c) * 64 + lane];
-        if (P.part) {  // one of several K slices: the partial sums go to the workspace
-            reinterpret_cast<qg_f4*>(P.part)[(((int64_t)h * P.tiles + t) * C + c) * 64 + lane] = sum;
-            continue;
+        for (int b2 = 1; b2 < KC; ++b2) sum[c] += park[((min(wave, nt - 1) * KC + b2) * C + c) * 64 + lane];
+    }
+    if (P.part) {
+        // One of several K slices. Its partial sums go to the workspace with
+        // device-coherent stores; after every wavefront's stores have completed, one
+        // lane counts the workgroup in on its tile group's counter, and the group's
+        // last workgroup (which saw the others' arrivals, hence their completed
+        // stores) adds the slices' partial sums in slice order with device-coherent
+        // loads and writes Y, then returns the counter to zero. No workgroup waits
+        // for another.
+        // partial sums: one buffer resource over the problem's slices; cache policy
+        // sc1 makes the stores and loads device-coherent (other XCDs' L2 caches are
+        // not consulted)
+        constexpr int kCoherent = 0x10;
+        const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)P.part, (short)0, P.slices * P.tiles * C * 1024, kQgRawBufferFlags);
+        if (wave < nt)
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(qg_u4v, sum[c]), pr,
+                                                       (uint32_t)lane * 16u,
+                                                       ((h * P.tiles + t) * C + c) * 1024, kCoherent);
+        __builtin_amdgcn_s_waitcnt(0);
+        int* last = reinterpret_cast<int*>(lds);  // the parked sums have all been read
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t old = __hip_atomic_fetch_add(P.ctr + j, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *last = old == (uint32_t)(P.slices - 1);
+            if (*last) __hip_atomic_store(P.ctr + j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        __syncthreads();
+        if (!*last || wave >= nt) return;
+        // per column block, all slices' loads in flight at once, then added in
+        // slice order
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            qg_u4v pv[kSpMaxSlices];
+#pragma unroll
+            for (int h2 = 0; h2 < kSpMaxSlices; ++h2)
+                pv[h2] = __builtin_amdgcn_raw_buffer_load_b128(
+                    pr, h2 < P.slices ? (uint32_t)lane * 16u : kOutOfRange,
+                    h2 < P.slices ? ((h2 * P.tiles + t) * C + c) * 1024 : 0, kCoherent);
+            qg_f4 v = __builtin_bit_cast(qg_f4, pv[0]);
+#pragma unroll
+            for (int h2 = 1; h2 < kSpMaxSlices; ++h2)
+                if (h2 < P.slices) v += __builtin_bit_cast(qg_f4, pv[h2]);
+            sum[c] = v;
+        }
+    }
+    if (wave >= nt) return;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
         if (i < rt) {
             const int row = t * T + i;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int n = 16 * c + 4 * s + e;
-                if (n < P.N) P.Y[(int64_t)n * P.ldy + row] = sum[e];
+                if (n < P.N) P.Y[(int64_t)n * P.ldy + row] = sum[c][e];
             }
-        }
-    }
-}
-
-// Sum of the K slices' partial sums of the walk form, in slice order (so results
-// are deterministic): one 64-lane workgroup per tile and column block.
-struct RdProb {
-    const qg_f4* part;
-    float* Y;
-    int64_t ldy;
-    int32_t M, N, tiles, slices, C, wg_begin;
-};
-struct RdArgs {
-    int32_t begin[QG_MAX_BATCH];
-    int32_t count;
-    RdProb p[QG_MAX_BATCH];
-};
-
-__global__ __launch_bounds__(64) void q4k_smalln_reduce_kernel(RdArgs a) {
-    const int wg = blockIdx.x;
-    int k = 0;
-#pragma unroll
-    for (int i = 1; i < QG_MAX_BATCH; ++i)
-        if (i < a.count && wg >= a.begin[i]) k = i;
-    const RdProb P = a.p[k];
-    const int l = wg - P.wg_begin;
-    const int t = l / P.C, c = l % P.C;
-    const int lane = threadIdx.x;
-    const int i = lane & 15, s = lane >> 4;
-    qg_f4 sum = P.part[((int64_t)t * P.C + c) * 64 + lane];
-    for (int h = 1; h < P.slices; ++h) sum += P.part[(((int64_t)h * P.tiles + t) * P.C + c) * 64 + lane];
-    const int rt = min(T, P.M - t * T);
-    if (i < rt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int n = 16 * c + 4 * s + e;
-            if (n < P.N) P.Y[(int64_t)n * P.ldy + t * T + i] = sum[e];
         }
     }
 }
@@ -1297,6 +1309,7 @@ SnProb make_sn(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy
     P.slices = 1;
     P.slice_sbs = P.nb;
     P.part = nullptr;
+    P.ctr = nullptr;
     return P;
 }
 
@@ -1543,17 +1556,18 @@ void launch_walk_any(const WkShape& w, const SnArgs& a, int grid, int nmax, hipS
 }
 
 // Tile groups and K slices of the walk form with a workspace: per problem, groups
-// of w.T tiles (enough units per chunk for the 16 wavefronts), and as
-// many K slices as give the problem its share of one workgroup per CU (at most
-// kSpMaxSlices). Slices of one super-block-range each write partial sums to the
-// workspace (problems left with one slice write Y). Fills wgs, slices,
-// slice_sbs, part, wg_begin and begin; returns the grid and the workspace bytes.
-int64_t split_grid(SnArgs& a, int cus, const WkShape& w, float* ws, size_t* need) {
+// of w.T tiles (enough units per chunk for the 16 wavefronts), and as many K slices
+// as give the problem its share of one workgroup per CU (at most kSpMaxSlices).
+// Problems left with one slice write Y directly. Workspace: one counter per tile
+// group of the sliced problems (256-byte aligned block), then their partial sums.
+// Fills wgs, slices, slice_sbs, part, ctr, wg_begin and begin; returns the grid and
+// the workspace bytes.
+int64_t split_grid(SnArgs& a, int cus, const WkShape& w, void* ws, size_t* need) {
     const int C = w.C;
     int64_t tiles = 0;
     for (int i = 0; i < a.count; ++i) tiles += a.p[i].tiles;
     int64_t wgs = 0;
-    size_t off = 0;
+    size_t nctr = 0, npart = 0;
     for (int i = 0; i < a.count; ++i) {
         SnProb& P = a.p[i];
         const int64_t G = qg::ceil_div(P.tiles, w.T);
@@ -1563,16 +1577,30 @@ int64_t split_grid(SnArgs& a, int cus, const WkShape& w, float* ws, size_t* need
         H = qg::ceil_div(P.nb, P.slice_sbs);
         P.wgs = (int32_t)G;
         P.slices = (int32_t)H;
-        P.part = nullptr;
-        if (H > 1) {
-            P.part = ws ? ws + off / sizeof(float) : nullptr;
-            off += (size_t)H * P.tiles * C * 1024;
-        }
         P.wg_begin = (int32_t)wgs;
         a.begin[i] = (int32_t)wgs;
         wgs += G * H;
+        if (H > 1) {
+            nctr += (size_t)G;
+            npart += (size_t)H * P.tiles * C * 1024;
+        }
     }
-    *need = off;
+    const size_t ctr_bytes = qg::align_up(nctr * 4, 256);
+    size_t co = 0, po = ctr_bytes;
+    for (int i = 0; i < a.count; ++i) {
+        SnProb& P = a.p[i];
+        P.part = nullptr;
+        P.ctr = nullptr;
+        if (P.slices > 1 && ws) {
+            P.ctr = (uint32_t*)ws + co;
+            P.part = (float*)((char*)ws + po);
+        }
+        if (P.slices > 1) {
+            co += (size_t)P.wgs;
+            po += (size_t)P.slices * P.tiles * C * 1024;
+        }
+    }
+    *need = npart ? ctr_bytes + npart : 0;
     return wgs;
 }
 
@@ -1659,25 +1687,11 @@ qg_status run(const qg_gemm_problem* probs, int count, hipStream_t stream, void*
     if (cfg.split) {
         size_t need = 0;
         const WkShape ws_shape = walk_shape(C, nmax, true);
-        const int64_t grid = split_grid(a, qg::device_cus(), ws_shape, (float*)ws, &need);
+        const int64_t grid = split_grid(a, qg::device_cus(), ws_shape, ws, &need);
         if (need > 0 && (!ws || ws_bytes < need))
             return qg::fail(QG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
         if (need > 0 && !qg::aligned16(ws)) return qg::fail(QG_ERR_ALIGN, "workspace not 16-byte aligned");
         launch_walk_any(ws_shape, a, (int)grid, nmax, stream);
-        st = qg::launch_status("qgemm_q4k_smalln_batch_ws");
-        if (st || need == 0) return st;
-        RdArgs r{};
-        int64_t rw = 0;
-        for (int i = 0; i < a.count; ++i) {
-            const SnProb& P = a.p[i];
-            if (!P.part) continue;
-            RdProb& q = r.p[r.count];
-            q = RdProb{(const qg_f4*)P.part, P.Y, P.ldy, P.M, P.N, P.tiles, P.slices, C, (int32_t)rw};
-            r.begin[r.count] = (int32_t)rw;
-            ++r.count;
-            rw += (int64_t)P.tiles * C;
-        }
-        hipLaunchKernelGGL(q4k_smalln_reduce_kernel, dim3((unsigned)rw), dim3(64), 0, stream, r);
         return qg::launch_status("qgemm_q4k_smalln_batch_ws");
     }
     if (cfg.dot) return qg::smalln_dot_launch(probs, count, stream);

@@ -353,9 +353,10 @@ def test_smalln_ws_sizes_and_validation(L):
     assert L.qgemm_q4k_smalln_batch_workspace_bytes(bad, 1) == 0
     with qg.launch_override(smalln_form=qg.FORM_SMALLN_SPLIT):
         need = L.qgemm_q4k_smalln_batch_workspace_bytes(arr, 2)
-        assert need > 0 and need % 1024 == 0
-        # a partial sum per K slice, tile and 16-column block, at most 16 slices
-        assert need <= 16 * (224 + 288) * 2 * 1024
+        assert need > 0 and need % 256 == 0
+        # one counter per tile group (a 256-byte aligned block), then a partial sum
+        # per K slice, tile and 16-column block, at most 16 slices
+        assert need <= 4 * (224 + 288) + 256 + 16 * (224 + 288) * 2 * 1024
     assert L.qgemm_q4k_smalln_batch_ws(None, 1, None, 0, None) == ENULL
     assert L.qgemm_q4k_smalln_batch_ws(bad, 1, None, 0, None) == ESHAPE
 

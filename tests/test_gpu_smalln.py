@@ -314,14 +314,20 @@ def test_split_walk_form(N):
         need = qg.qgemm_q4k_smalln_batch_workspace_bytes(probs)
         case(f"qgemm_q4k_smalln_batch_ws split N={N} batch {bi}: {shapes}, workspace {need}")
         assert need > 0
-        # scratch contents do not matter: fill the workspace with NaN bytes first
-        ws = qg.Workspace("cuda:0", need)
-        ws.buf.fill_(0xff)
+        ws = qg.Workspace("cuda:0", need)  # zero-filled: the arrival counters start at 0
         qg.qgemm_q4k_smalln_batch_ws(probs, ws)
         torch.cuda.synchronize()
         first = [p[2].clone() for p in probs]
-        qg.qgemm_q4k_smalln_batch_ws(probs, ws)
-        torch.cuda.synchronize()
+        # repeated calls on the same workspace: the counters return to zero and the
+        # slice sums never read a stale partial (bit-identical results every time)
+        for rep in range(8):
+            for p_ in probs:
+                p_[2].fill_(float("nan"))
+            qg.qgemm_q4k_smalln_batch_ws(probs, ws)
+            torch.cuda.synchronize()
+            for p_, Y0 in zip(probs, first):
+                assert torch.equal(p_[2][:, :p_[3]], Y0[:, :p_[3]]), f"split walk form differs on call {rep + 2}"
+        assert int(ws.buf[:64].ne(0).sum()) == 0, "arrival counters not returned to zero"
         for (w, X, Y, M, K), Y0, (rows, (Yr, Ar)) in zip(probs, first, refs):
             assert torch.equal(Y[:, :M], Y0[:, :M]), "split walk form not deterministic"
             assert not torch.isnan(Y[:, :M]).any(), "split walk form left outputs unwritten"
