@@ -53,7 +53,7 @@ class _LaunchOverride(ctypes.Structure):
 FORM_AUTO = 0
 FORM_SMALLN_REGS, FORM_SMALLN_LDS, FORM_SMALLN_LDS1, FORM_SMALLN_DOT, FORM_SMALLN_STREAM, FORM_SMALLN_WALK, \
     FORM_SMALLN_SPLIT = 1, 2, 3, 4, 5, 6, 7
-FORM_VERIFY_MFMA, FORM_VERIFY_DOT = 1, 2
+FORM_VERIFY_MFMA, FORM_VERIFY_DOT, FORM_VERIFY_STREAM = 1, 2, 3
 
 
 class _TopkOut(ctypes.Structure):

@@ -21,7 +21,8 @@
 // per (column, tile) goes to the workspace. Stage 2 (one workgroup per column)
 // reduces a column's partials in a fixed order, clears them and writes the id and
 // its logit. K must be a multiple of 256 (whole macro-blocks of 8 blocks). This
-// matrix-core stage 1 serves N > 6; up to 6 columns take the vector-ALU form below.
+// matrix-core stage 1 serves N > 8 (and K > 4096 above 6 columns); the streamed
+// form below takes N <= 8 with K <= 4096, the vector-ALU form the rest.
 #include <algorithm>
 #include <climits>
 #include <cstdlib>
@@ -122,6 +123,10 @@ QG_DEV void unit_dot(qg_f4 (&acc)[TW][C], const VaIn<C, TW>& d, int u) {
 // (value, index) order of the argmax: larger value wins, equal values go to the
 // lower index; NaN and missing rows carry -inf and INT_MAX and never win.
 QG_DEV bool va_better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
+// Workgroup barrier: LDS operations complete first; pending global loads are not
+// waited for.
+QG_DEV void sw_vs_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int C, int TW, int W>
 __global__ __launch_bounds__(64 * W) void lmhead_verify_tile_kernel(VaProb P) {
@@ -516,6 +521,276 @@ void vd_launch(const VdProb& P, int W, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Streamed form (N <= 8, 2048 <= K <= 4096): the grid is sized to the resident
+// workgroup slots, and workgroup j walks tiles j, j + G, j + 2G, ... The columns
+// are staged into LDS once per workgroup (fp16, and the negated sums of every
+// 32-weight block over the same fp16 values); the eight wavefronts take the (tile,
+// macro-block) units of the walk in turn, with the next unit's loads in flight
+// while one is computed, so the weight stream does not stop between tiles. The
+// walk runs in rounds of two tiles: a wavefront keeps one accumulator per tile of
+// the round, parks both at the round's end, and after the round's barrier two
+// wavefronts (rotating with the round) add a tile's parked sums in a fixed order
+// and fold the tile's rows into their running (max, lowest index) per column.
+// At the end the running results meet in LDS and one 8-byte partial per (column,
+// workgroup) goes to the workspace; stage 2 is lmhead_verify_reduce_kernel.
+// Per block: S' = sum_k x[k][n] (q[r][k] + 128) as one 16 x 16 x 32 fp16
+// matrix-core product (the biased quants as fp16 subnormals, one byte permutation
+// per dword), logit += d 2^24 S' in fp32; the bias -128 d X[n] of four blocks is
+// one v_mfma_f32_16x16x4_f32 (A the table entries -X, B 128 d of the lane's row),
+// accumulated across the tile's units.
+constexpr int kVsWaves = 8, kVsCols = 8;
+// The automatic choice for every N it takes (152064 x 3584, us, streamed / vector-ALU
+// dot / matrix-core forms: N = 1 93.3 / 95.0 / 134.5, 2 92.2 / 96.4 / 135.7,
+// 4 92.6 / 105.2 / 138.5, 5 93.2 / 115.8 / 139.2, 6 93.1 / 125.9 / 141.3,
+// 8 94.4 / - / 142.9; the single-column argmax 94.7).
+constexpr int kVsMinCols = 1;
+
+struct VsProb {
+    const uint8_t* w;
+    const float* X;
+    int64_t ldx;
+    float2* partials;  // [N][G]
+    int32_t M, nmb, N, tiles, G;
+};
+
+struct VsItem {
+    uint4 sc;     // the eight fp16 block scales of this lane's row
+    uint2 q[8];   // quant bytes 8 (l / 16)..+7 of blocks 0..7
+};
+
+// Loads of unit (tile t, macro-block mb); valid false: offsets past the resource,
+// zeros without a memory access (every load is still issued: exact wait counts).
+QG_DEV void vs_load(VsItem& it, __amdgpu_buffer_rsrc_t wr, const VsProb& P, int t, int mb, int i, int s,
+                    bool valid) {
+    const int rt = min(T, P.M - t * T);
+    const uint32_t r = (uint32_t)min(i, rt - 1);
+    const uint32_t vh = valid ? 16u * r : kQgOutOfRange;
+    const uint32_t vq =
+        valid ? 16u * r + 8u * (uint32_t)(s & 1) + (uint32_t)(s >> 1) * 16u * (uint32_t)rt : kQgOutOfRange;
+    const int so = valid ? t * T * P.nmb * 272 + mb * 17 * 16 * rt : 0;
+    const qg_u4v h = __builtin_amdgcn_raw_buffer_load_b128(wr, vh, so, 0);  // scales: a cached load
+    it.sc = make_uint4(h.x, h.y, h.z, h.w);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const qg_u2v q = __builtin_amdgcn_raw_buffer_load_b64(wr, vq, so + (1 + 2 * k) * 16 * rt, kQgNonTemporal);
+        it.q[k] = make_uint2(q.x, q.y);
+    }
+}
+
+// One unit: a = LDS byte address of this lane's A operand for block 0 of the
+// macro-block, xt = its table entry (block l / 16, column l % 16).
+QG_DEV void vs_dot(qg_f4& acc, qg_f4& accm, const VsItem& it, const unsigned char* lds, uint32_t a, uint32_t xt,
+                   int s) {
+    const qg_f4 zero = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t dws[4] = {it.sc.x, it.sc.y, it.sc.z, it.sc.w};
+    // bias: blocks s and 4 + s of the lane's row, 128 d each
+    const uint32_t b0 = (s >> 1) ? it.sc.y : it.sc.x, b1 = (s >> 1) ? it.sc.w : it.sc.z;
+    const float bm0 = 128.0f * ((s & 1) ? qg_half_hi(b0) : qg_half_lo(b0));
+    const float bm1 = 128.0f * ((s & 1) ? qg_half_hi(b1) : qg_half_lo(b1));
+    const float xa0 = *reinterpret_cast<const float*>(lds + xt);
+    const float xa1 = *reinterpret_cast<const float*>(lds + xt + 256);
+    accm = __builtin_amdgcn_mfma_f32_16x16x4f32(xa0, bm0, accm, 0, 0, 0);
+    accm = __builtin_amdgcn_mfma_f32_16x16x4f32(xa1, bm1, accm, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t dw = dws[k >> 1];
+        const float d24 = ((k & 1) ? qg_half_hi(dw) : qg_half_lo(dw)) * 16777216.0f;
+        const qg_h8 av = *reinterpret_cast<const qg_h8*>(lds + a + 64 * k);
+        const uint32_t w0 = it.q[k].x ^ 0x80808080u, w1 = it.q[k].y ^ 0x80808080u;
+        const qg_h8 b = __builtin_bit_cast(
+            qg_h8, make_uint4(__builtin_amdgcn_perm(w0, w0, 0x0c020c00u), __builtin_amdgcn_perm(w0, w0, 0x0c030c01u),
+                              __builtin_amdgcn_perm(w1, w1, 0x0c020c00u), __builtin_amdgcn_perm(w1, w1, 0x0c030c01u)));
+        const qg_f4 sp = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b, zero, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(d24, sp[e], acc[e]);
+    }
+}
+
+template <int W>
+__global__ __launch_bounds__(64 * W, 4) void lmhead_verify_stream_kernel(VsProb P) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int j = blockIdx.x;
+    const int G = P.G;
+    const int nt = (P.tiles - j + G - 1) / G;  // tiles of this walk
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i = lane & 15, s = lane >> 4;
+    const int nmb = P.nmb;
+    const int K = nmb * 256;
+    const int RB = (K + 8) * 2;
+    const uint32_t xsb = (uint32_t)(P.N * RB);          // table of -X per block, 16 columns
+    qg_f4* park = reinterpret_cast<qg_f4*>(lds + xsb + 2 * K);  // [2 buffers][2 slots][W][32 lanes]
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)P.w, (short)0, P.M * nmb * 272, kQgRawBufferFlags);
+
+    // columns: thread tid takes 8-element group tid of every column (K <= 512 W)
+    const int tid = threadIdx.x;
+    const int gpr = K / 8;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)P.X, (short)0, (int)(((int64_t)(P.N - 1) * P.ldx + K) * 4), kQgRawBufferFlags);
+    float4 v[kVsCols][2];
+#pragma unroll
+    for (int n = 0; n < kVsCols; ++n) {
+        const uint32_t off = (n < P.N && tid < gpr) ? (uint32_t)(((int64_t)n * P.ldx + 8 * tid) * 4) : kQgOutOfRange;
+        v[n][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+        v[n][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 16, 0));
+    }
+
+    // this wavefront's units: wave, wave + W, ... of the nt * nmb units of the walk;
+    // (lt, lb) is the tile slot and macro-block of the unit being loaded
+    const int U = nt * nmb;
+    const int niter = (U - wave + W - 1) / W;
+    int lt = wave / nmb, lb = wave - (wave / nmb) * nmb;
+    auto advance = [&](int& t_, int& b_) {
+        b_ += W;
+        while (b_ >= nmb) {
+            b_ -= nmb;
+            ++t_;
+        }
+    };
+    const int t_first = lt, b_first = lb;
+    VsItem b0, b1;
+    vs_load(b0, wr, P, j + min(lt, nt - 1) * G, lb, i, s, niter > 0);
+    advance(lt, lb);
+
+#pragma unroll
+    for (int n = 0; n < kVsCols; ++n) {
+        const qg_h8 h = qg_a_operand(v[n][0], v[n][1]);
+        if (n < P.N && tid < gpr) *reinterpret_cast<qg_h8*>(lds + n * RB + 16 * tid) = h;
+        const uint4 hw = __builtin_bit_cast(uint4, h);
+        const float xsum = qg_quad_sum(qg_sum_pairs4(hw.x, hw.y, hw.z, hw.w));
+        if ((tid & 3) == 0 && tid < gpr) *reinterpret_cast<float*>(lds + xsb + ((tid >> 2) * 16 + n) * 4) = -xsum;
+    }
+    if ((tid & 3) == 0 && tid < gpr) {  // columns 8..15 of the table: zeros
+        *reinterpret_cast<uint4*>(lds + xsb + ((tid >> 2) * 16 + 8) * 4) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(lds + xsb + ((tid >> 2) * 16 + 12) * 4) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    sw_vs_barrier();
+
+    const uint32_t an = (uint32_t)((i < P.N ? i : 0) * RB + 16 * s);
+    const uint32_t xtl = xsb + (uint32_t)(s * 16 + i) * 4;
+    // round accumulators (tile slots 2r and 2r + 1), running best per column of the
+    // tiles this wavefront reduces
+    qg_f4 acc[2] = {qg_f4{0.f, 0.f, 0.f, 0.f}, qg_f4{0.f, 0.f, 0.f, 0.f}};
+    qg_f4 accm[2] = {qg_f4{0.f, 0.f, 0.f, 0.f}, qg_f4{0.f, 0.f, 0.f, 0.f}};
+    float bv[4];
+    int bi[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bv[e] = -__builtin_huge_valf();
+        bi[e] = INT_MAX;
+    }
+    int round = 0;
+    // end of round `round`: park, barrier, reduce its tiles (wavefronts 2 round % W
+    // and 2 round % W + 1), start the next
+    auto end_round = [&]() {
+        qg_f4* pb = park + (size_t)(round & 1) * 2 * W * 32;
+        if (lane < 32) {
+            pb[(0 * W + wave) * 32 + lane] = acc[0] + accm[0];
+            pb[(1 * W + wave) * 32 + lane] = acc[1] + accm[1];
+        }
+        acc[0] = acc[1] = accm[0] = accm[1] = qg_f4{0.f, 0.f, 0.f, 0.f};
+        sw_vs_barrier();
+        const int q = wave - (2 * round) % W;  // this wavefront's slot in the round, if 0 or 1
+        const int ts = 2 * round + q;
+        if ((q == 0 || q == 1) && ts < nt && lane < 32) {
+            qg_f4 sum = pb[(q * W) * 32 + lane];
+#pragma unroll
+            for (int w = 1; w < W; ++w) sum += pb[(q * W + w) * 32 + lane];
+            const int t = j + ts * G;
+            const int rt = min(T, P.M - t * T);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float vv = sum[e];
+                int idx = t * T + i;
+                if (i >= rt || !(vv == vv)) {
+                    vv = -__builtin_huge_valf();
+                    idx = INT_MAX;
+                }
+                if (va_better(vv, idx, bv[e], bi[e])) {
+                    bv[e] = vv;
+                    bi[e] = idx;
+                }
+            }
+        }
+        ++round;
+    };
+
+    int ct = t_first, cb = b_first;  // unit being computed
+    auto unit = [&](const VsItem& it) {
+        while (ct >= 2 * (round + 1)) end_round();  // the walk enters a later round
+        if (ct & 1)
+            vs_dot(acc[1], accm[1], it, lds, an + (uint32_t)(512 * cb), xtl + (uint32_t)(512 * cb), s);
+        else
+            vs_dot(acc[0], accm[0], it, lds, an + (uint32_t)(512 * cb), xtl + (uint32_t)(512 * cb), s);
+        advance(ct, cb);
+    };
+
+    // ping-pong: unconditional loads, single-exit loop, exact wait counts
+    int it = 0;
+    for (; it + 2 <= niter; it += 2) {
+        vs_load(b1, wr, P, j + min(lt, nt - 1) * G, lb, i, s, true);
+        advance(lt, lb);
+        __builtin_amdgcn_sched_barrier(0);
+        unit(b0);
+        vs_load(b0, wr, P, j + min(lt, nt - 1) * G, lb, i, s, it + 2 < niter);
+        advance(lt, lb);
+        __builtin_amdgcn_sched_barrier(0);
+        unit(b1);
+    }
+    if (it < niter) unit(b0);
+    // every wavefront ends every round, with or without units in it, so all meet
+    // the same barriers
+    const int nrounds = (nt + 1) / 2;
+    while (round < nrounds) end_round();
+
+    // the wavefronts' running results meet in LDS (the columns are no longer read)
+    float* bvs = reinterpret_cast<float*>(lds);
+    int* bis = reinterpret_cast<int*>(lds + W * 32 * 4 * 4);
+    if (lane < 32)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // rows first: the lanes i = 0..15 of column 4 s + e
+            float vv = bv[e];
+            int idx = bi[e];
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) {
+                const float ov = __shfl_xor(vv, off, 64);
+                const int oi = __shfl_xor(idx, off, 64);
+                if (va_better(ov, oi, vv, idx)) {
+                    vv = ov;
+                    idx = oi;
+                }
+            }
+            bvs[(wave * 32 + lane) * 4 + e] = vv;
+            bis[(wave * 32 + lane) * 4 + e] = idx;
+        }
+    sw_vs_barrier();
+    if (wave != 0 || i != 0 || lane >= 32) return;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float vv = bvs[lane * 4 + e];
+        int idx = bis[lane * 4 + e];
+#pragma unroll
+        for (int w = 1; w < W; ++w) {
+            const float ov = bvs[(w * 32 + lane) * 4 + e];
+            const int oi = bis[(w * 32 + lane) * 4 + e];
+            if (va_better(ov, oi, vv, idx)) {
+                vv = ov;
+                idx = oi;
+            }
+        }
+        const int n = 4 * s + e;
+        if (n < P.N) P.partials[(int64_t)n * G + j] = make_float2(vv, __builtin_bit_cast(float, idx));
+    }
+}
+
+// Dynamic LDS of the streamed form: the columns, their block sums, the parked sums.
+size_t vs_lds_bytes(int64_t K, int64_t N) {
+    return (size_t)N * (K + 8) * 2 + 2 * (size_t)K + 2 * 2 * kVsWaves * 32 * 16;
+}
+
+// ---------------------------------------------------------------------------
 // Int8 activations: each column quantized Q8_1-style (qg_quantize_q8_1: a float32
 // scale d_x and 32 int8 quants per block). Both operands are then signed int8, so
 // a block's integer product S = sum_l q_w,l q_x,l comes straight from
@@ -736,6 +1011,40 @@ qg_status lmhead_argmax_verify(const void* w, const float* X, int64_t ldx, int64
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
     const qg_launch_override& ov = qg::launch_override();
+    // streamed form: up to 8 columns, K <= 4096 (one round of column loads), weights
+    // under 2 GiB (one buffer resource)
+    const bool vs_ok = N <= kVsCols && K <= 512 * kVsWaves && M * (K / 256) * 272 < (int64_t)INT32_MAX &&
+                       vs_lds_bytes(K, N) <= 160 * 1024;
+    const bool stream_form =
+        vs_ok && (ov.verify_form == QG_FORM_VERIFY_STREAM || (ov.verify_form == QG_FORM_AUTO && N >= kVsMinCols));
+    if (stream_form) {
+        VsProb V{};
+        V.w = (const uint8_t*)w;
+        V.X = X;
+        V.ldx = ldx;
+        V.partials = (float2*)ws;
+        V.M = (int32_t)M;
+        V.nmb = (int32_t)(K / 256);
+        V.N = (int32_t)N;
+        V.tiles = (int32_t)qg::ceil_div(M, T);
+        const size_t lds = vs_lds_bytes(K, N);
+        const int per_cu = lds <= 80 * 1024 ? 2 : 1;
+        V.G = (int32_t)std::min<int64_t>(V.tiles, (int64_t)per_cu * qg::device_cus());
+        const auto kern = lmhead_verify_stream_kernel<kVsWaves>;
+        static bool attr_set[64];
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr_set[dev]) {
+            (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+            attr_set[dev] = true;
+        }
+        hipLaunchKernelGGL(kern, dim3((unsigned)V.G), dim3(64 * kVsWaves), lds, s, V);
+        st = qg::launch_status("lmhead_argmax_verify (tiles)");
+        if (st) return st;
+        const int threads = (int)std::min<int64_t>(1024, std::max<int64_t>(64, qg::ceil_div(V.G, 8 * 64) * 64));
+        hipLaunchKernelGGL(lmhead_verify_reduce_kernel, dim3((unsigned)N), dim3(threads), 0, s, V.partials, V.G,
+                           out_index, out_value, (uint4*)nullptr, 0);
+        return qg::launch_status("lmhead_argmax_verify (reduce)");
+    }
     const bool mfma = N > kVdMaxCols || ov.verify_form == QG_FORM_VERIFY_MFMA;
     if (!mfma) {
         // vector-ALU form: fp16 pairs and block sums, then one wavefront per tile on

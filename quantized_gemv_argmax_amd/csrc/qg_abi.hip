@@ -119,7 +119,7 @@ qg_status qg_set_launch_override(const qg_launch_override* o) {
         return (qg_status)qg::fail(QG_ERR_SHAPE, "smalln_tiles=%d not in {0, 1, 2, 4}", v.smalln_tiles);
     if (!in(v.smalln_depth, {2, 3, 4}))
         return (qg_status)qg::fail(QG_ERR_SHAPE, "smalln_depth=%d not in {0, 2, 3, 4}", v.smalln_depth);
-    if (!in(v.verify_form, {QG_FORM_VERIFY_MFMA, QG_FORM_VERIFY_DOT}))
+    if (!in(v.verify_form, {QG_FORM_VERIFY_MFMA, QG_FORM_VERIFY_DOT, QG_FORM_VERIFY_STREAM}))
         return (qg_status)qg::fail(QG_ERR_SHAPE, "verify_form=%d unknown", v.verify_form);
     if (!in(v.verify_waves, {1, 4, 8}))
         return (qg_status)qg::fail(QG_ERR_SHAPE, "verify_waves=%d not in {0, 1, 4, 8}", v.verify_waves);

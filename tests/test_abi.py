@@ -365,7 +365,7 @@ def test_launch_override_validation(L):
     O = qg._LaunchOverride
     assert L.qg_set_launch_override(None) == OK
     for field, bad in [("gemv_waves", 3), ("gemv_waves", 16), ("smalln_form", 8), ("smalln_waves", 16),
-                       ("smalln_tiles", 3), ("smalln_depth", 1), ("verify_form", 3), ("verify_waves", 2),
+                       ("smalln_tiles", 3), ("smalln_depth", 1), ("verify_form", 4), ("verify_waves", 2),
                        ("verify_tiles", 8)]:
         o = O()
         setattr(o, field, bad)

@@ -227,7 +227,8 @@ def expected_ids(W, M, K, X):
 @pytest.mark.parametrize("form,N,W_,TW", [("mfma", 5, 4, 4), ("mfma", 5, 8, 1), ("mfma", 9, 8, 2),
                                           ("mfma", 20, 4, 1), ("mfma", 32, 4, 2), ("dot", 1, 1, 0),
                                           ("dot", 5, 1, 0), ("dot", 6, 4, 0), ("auto", 5, 0, 0),
-                                          ("auto", 17, 0, 0)])
+                                          ("auto", 17, 0, 0), ("stream", 1, 0, 0), ("stream", 5, 0, 0),
+                                          ("stream", 8, 0, 0)])
 def test_verify_integer_exact(form, N, W_, TW):
     M, K = 5000, 1536
     rng = np.random.default_rng(N)
@@ -236,7 +237,8 @@ def test_verify_integer_exact(form, N, W_, TW):
     ids, vals, L = expected_ids(W, M, K, X)
     assert np.sum(L[:, 0] == vals[0]) >= 2  # the planted tie
     wp = packed_q8_0(W, M, K)
-    ov = {"verify_form": {"mfma": qg.FORM_VERIFY_MFMA, "dot": qg.FORM_VERIFY_DOT, "auto": 0}[form],
+    ov = {"verify_form": {"mfma": qg.FORM_VERIFY_MFMA, "dot": qg.FORM_VERIFY_DOT, "auto": 0,
+                          "stream": qg.FORM_VERIFY_STREAM}[form],
           "verify_waves": W_, "verify_tiles": TW}
     ws = qg.Workspace(DEV)
     case(f"lmhead_argmax_verify integer form={form} N={N} W={W_} TW={TW}")

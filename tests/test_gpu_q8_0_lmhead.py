@@ -242,6 +242,21 @@ def test_verify_vector_alu_form_shapes(cfg, N):
     assert int(ws.buf.count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("N", [1, 2, 5, 8])
+def test_verify_streamed_form_shapes(N):
+    # the streamed form (grid of resident workgroups walking tiles in rounds of
+    # two): one tile (a single round of one tile), one macro-block, a ragged last
+    # tile, walks of many tiles with K = 4096 (its largest); the workspace is left
+    # zero
+    qg.launch_override(verify_form=qg.FORM_VERIFY_STREAM).set()
+    for key, (M, K) in enumerate([(16, 256), (33, 768), (1000, 2816), (20000, 4096)]):
+        W = workloads.q8_0_blocks(M, K, key=(28, M))
+        X = workloads.x_columns(K, N, key=(28, N, key))
+        ws = qg.Workspace(DEV)
+        check_verify(W, M, K, X, f"streamed form M={M} K={K} N={N}", ws=ws)
+        assert int(ws.buf.count_nonzero()) == 0
+
+
 def test_verify_forms_agree_on_ldx_padding():
     # X with ldx > K (padding columns of NaN never read) through both forms
     M, K, N, ldx = 500, 1024, 4, 1100
@@ -254,11 +269,14 @@ def test_verify_forms_agree_on_ldx_padding():
     i_dot, v_dot = qg.lmhead_argmax_verify(wp, to_dev(Xp), M, K)
     with qg.launch_override(verify_form=qg.FORM_VERIFY_MFMA):
         i_mma, v_mma = qg.lmhead_argmax_verify(wp, to_dev(Xp), M, K)
+    with qg.launch_override(verify_form=qg.FORM_VERIFY_DOT):
+        i_vd, v_vd = qg.lmhead_argmax_verify(wp, to_dev(Xp), M, K)
     torch.cuda.synchronize()
     for n in range(N):
         yr, ar = oracle.gemv_q8_0(W, M, K, X[n])
         tol = oracle.tolerance(ar)
-        for gi, gv in ((int(i_dot[n]), float(v_dot[n])), (int(i_mma[n]), float(v_mma[n]))):
+        for gi, gv in ((int(i_dot[n]), float(v_dot[n])), (int(i_mma[n]), float(v_mma[n])),
+                       (int(i_vd[n]), float(v_vd[n]))):
             ri = oracle.argmax(yr)
             assert yr[gi] >= yr[ri] - tol[gi] - tol[ri], n
             assert abs(gv - yr[gi]) <= tol[gi], n
