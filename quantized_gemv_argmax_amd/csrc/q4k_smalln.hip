@@ -1023,7 +1023,7 @@ __global__ __launch_bounds__(64 * W, 4) void q4k_smalln_stream_kernel(SnArgs a) 
 // fp32 matrix-core product); every column block c of 16 columns reuses one B.
 constexpr int kWkWaves = 16, kWkTiles = 10;
 constexpr int64_t kWkAutoTiles = 1024;
-constexpr int kSpMaxSlices = 16, kSpAutoCols = 5;
+constexpr int kSpMaxSlices = 16, kSpAutoCols = 5, kSpAutoK1 = 8192;
 
 
 template <int C, int KC_, int TMAX>
@@ -1411,7 +1411,13 @@ SnCfg choose_cfg(const SnArgs& a, int C, bool ws) {
     // fewer tiles, with a workspace: the walk over tile groups and K slices, where
     // the activations outweigh the weights (every workgroup of the other forms
     // reads all of X for its one or two tiles)
-    c.split = c.walk = ws && wk && form == QG_FORM_AUTO && ncol >= kSpAutoCols;
+    // (measured on the 7B stages: N = 32 down 41.7 -> 22.2, q/k/v 15.3 -> 12.2; N = 16
+    // down 30.2 -> 22.9, N = 8 down 20.1 -> 17.1, N = 5 down 19.6 -> 16.3; but N = 16
+    // q/k/v 11.2 -> 13.1 and o 9.9 -> 10.6: with one column block, only long K gains)
+    int kmin = INT_MAX;
+    for (int i = 0; i < a.count; ++i) kmin = std::min(kmin, a.p[i].nb * 256);
+    c.split = c.walk =
+        ws && wk && form == QG_FORM_AUTO && ncol >= kSpAutoCols && (C == 2 || kmin >= kSpAutoK1);
     if (c.walk) return c;
     c.lds = form == QG_FORM_SMALLN_LDS ||
             (form != QG_FORM_SMALLN_REGS && (units >= 32 * 4 || (C == 2 && tiles <= 1024)));
