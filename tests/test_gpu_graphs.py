@@ -50,6 +50,16 @@ def test_graph_replays_match_eager():
     Y2 = torch.empty((2, M5), device=DEV)
     Xd3 = to_dev(workloads.x_columns(Kd, 3, key=(86,)))
     Yd3 = torch.empty((3, Md), device=DEV)
+    # the walk forms: K slices with a workspace (down projection, N=32; its arrival
+    # counters must come back to zero on every replay) and a many-tile walk (N=32
+    # over 18944 rows)
+    Xd32 = to_dev(workloads.x_columns(Kd, 32, key=(87,)))
+    Yd32 = torch.empty((32, Md), device=DEV)
+    Mg, Kg = 18944, 3584
+    wg = packed_q4k(workloads.q4k_blocks(Mg, Kg, key=(88,)), Mg, Kg)
+    Xg32 = to_dev(workloads.x_columns(Kg, 32, key=(88,)))
+    Yg32 = torch.empty((32, Mg), device=DEV)
+    wss = qg.Workspace(DEV, qg.qgemm_q4k_smalln_batch_workspace_bytes([(wd, Xd32, Yd32, Md, Kd)]))
 
     def work():
         qg.qgemv_q4k_batch(stage)
@@ -62,11 +72,13 @@ def test_graph_replays_match_eager():
         qg.qgemm_q4k_smalln(wd, Xd3, Md, Kd, Y=Yd3)
         qg.quantize_q8_1(stage[0][1], out=xq)
         qg.qgemv_q4k_q8_1(stage[0][0], xq, M5, K5, y=y8)
+        qg.qgemm_q4k_smalln_batch_ws([(wd, Xd32, Yd32, Md, Kd)], wss)
+        qg.qgemm_q4k_smalln(wg, Xg32, Mg, Kg, Y=Yg32)
 
     def snapshot():
         torch.cuda.synchronize()
         outs = [p[2] for p in stage] + [oi, ov, tk.index, tk.logit, tk.logprob, tk.lse, tk.token, lg, Y5, Yd, Y32, xq,
-                                        y8, Y2, Yd3]
+                                        y8, Y2, Yd3, Yd32, Yg32]
         return [t.clone() for t in outs]
 
     case("graph capture: eager reference")
@@ -85,7 +97,7 @@ def test_graph_replays_match_eager():
         work()
     for rep in range(4):
         # scribble over the outputs, then replay and compare
-        for t in snapshot_targets(stage, oi, ov, tk, lg, Y5, Yd, Y32, xq, y8) + [Y2, Yd3]:
+        for t in snapshot_targets(stage, oi, ov, tk, lg, Y5, Yd, Y32, xq, y8) + [Y2, Yd3, Yd32, Yg32]:
             t.zero_()
         case(f"graph replay {rep}")
         g.replay()
@@ -93,6 +105,7 @@ def test_graph_replays_match_eager():
         for k, (a, b) in enumerate(zip(got, ref)):
             assert torch.equal(a, b), f"replay {rep}: output {k} differs from the eager result"
         assert int(ws.buf.count_nonzero()) == 0
+        assert int(wss.buf[:256].count_nonzero()) == 0, "walk-form arrival counters not back to zero"
         # eager work between replays on the same buffers
         qg.qgemv_q4k(stage[1][0], stage[1][1], stage[1][3], stage[1][4], y=stage[1][2])
         torch.cuda.synchronize()
