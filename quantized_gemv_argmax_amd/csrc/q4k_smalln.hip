@@ -1023,7 +1023,7 @@ __global__ __launch_bounds__(64 * W, 4) void q4k_smalln_stream_kernel(SnArgs a) 
 // fp32 matrix-core product); every column block c of 16 columns reuses one B.
 constexpr int kWkWaves = 16, kWkTiles = 10;
 constexpr int64_t kWkAutoTiles = 1024;
-constexpr int kSpMaxSlices = 16, kSpAutoCols = 5, kSpAutoK1 = 8192;
+constexpr int kSpMaxSlices = 16, kSpAutoCols = 4, kSpAutoK1 = 8192;
 
 
 template <int C, int KC_, int TMAX>
@@ -1322,6 +1322,9 @@ SnProb make_sn(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy
 // workgroups, their partial sums meeting through atomic exchanges, was measured
 // slower at every 7B shape: the device-scope round trips at the end of every
 // workgroup cost more than the added parallelism gains.)
+// Batches of at least this many tiles take the streamed form from three columns.
+constexpr int64_t kStAutoTiles = 1024;
+
 // Dynamic LDS of the streamed form: nmax activation rows and the parked sums.
 size_t stream_lds_bytes(int nmax, int kmax) {
     return (size_t)nmax * (kmax + 8) * 2 + 2 * (size_t)kmax + (size_t)kStTiles * kStWaves * 32 * 16;
@@ -1369,15 +1372,30 @@ SnCfg choose_cfg(const SnArgs& a, int C, bool ws) {
     //     chunked LDS form).
     // A launch override (qg_set_launch_override) can force a form within the range
     // it supports, and the launch shape.
-    c.dot = (form == QG_FORM_AUTO && ncol <= 4) || (form == QG_FORM_SMALLN_DOT && ncol <= 8);
-    if (c.dot) return c;
     // the walk form reads the weights through one buffer resource per matrix
     bool wk = true;
-    for (int i = 0; i < a.count; ++i) wk = wk && (int64_t)a.p[i].M * a.p[i].nb * 144 < (int64_t)INT32_MAX;
-    c.walk = wk && form == QG_FORM_SMALLN_WALK;
+    int kmin = INT_MAX;
+    for (int i = 0; i < a.count; ++i) {
+        wk = wk && (int64_t)a.p[i].M * a.p[i].nb * 144 < (int64_t)INT32_MAX;
+        kmin = std::min(kmin, a.p[i].nb * 256);
+    }
+    // K slices need a workspace for their partial sums. Automatic choice: fewer
+    // tiles than the many-tile walk takes, and two column blocks or long K
+    // (measured on the 7B stages: N = 32 down 41.7 -> 22.2, q/k/v 15.3 -> 12.2; N = 16
+    // down 30.2 -> 22.9, N = 8 down 20.1 -> 17.1, N = 5 down 19.6 -> 16.3, N = 4 down
+    // 17.7 (dot form) -> 16.0; but N = 3 down 15.4 (dot) -> 16.0, N = 16 q/k/v 11.2 ->
+    // 13.1 and o 9.9 -> 10.6: with one column block, only long K gains)
+    c.split = c.walk = ws && wk &&
+                       (form == QG_FORM_SMALLN_SPLIT ||
+                        (form == QG_FORM_AUTO && tiles < kWkAutoTiles && ncol >= kSpAutoCols &&
+                         (C == 2 || kmin >= kSpAutoK1)));
     if (c.walk) return c;
-    // K slices need a workspace for their partial sums
-    c.split = c.walk = ws && wk && form == QG_FORM_SMALLN_SPLIT;
+    // (three and four columns over many tiles go to the streamed form below: gate/up,
+    // 2368 tiles, N = 3 23.6 -> 20.7 us, N = 4 26.6 -> 20.1)
+    const bool many_short = tiles >= kStAutoTiles && ncol >= 3;
+    c.dot = (form == QG_FORM_AUTO && ncol <= 4 && !many_short) || (form == QG_FORM_SMALLN_DOT && ncol <= 8);
+    if (c.dot) return c;
+    c.walk = wk && form == QG_FORM_SMALLN_WALK;
     if (c.walk) return c;
     // Single-pass form: every problem with K <= 512 * 8 and N <= 8 (one round of
     // activation loads per lane, all super-blocks of a row in flight at once).
@@ -1407,17 +1425,6 @@ SnCfg choose_cfg(const SnArgs& a, int C, bool ws) {
     }
     // many tiles, more columns than the single-pass forms take: the chunked walk
     c.walk = wk && form == QG_FORM_AUTO && tiles >= kWkAutoTiles;
-    if (c.walk) return c;
-    // fewer tiles, with a workspace: the walk over tile groups and K slices, where
-    // the activations outweigh the weights (every workgroup of the other forms
-    // reads all of X for its one or two tiles)
-    // (measured on the 7B stages: N = 32 down 41.7 -> 22.2, q/k/v 15.3 -> 12.2; N = 16
-    // down 30.2 -> 22.9, N = 8 down 20.1 -> 17.1, N = 5 down 19.6 -> 16.3; but N = 16
-    // q/k/v 11.2 -> 13.1 and o 9.9 -> 10.6: with one column block, only long K gains)
-    int kmin = INT_MAX;
-    for (int i = 0; i < a.count; ++i) kmin = std::min(kmin, a.p[i].nb * 256);
-    c.split = c.walk =
-        ws && wk && form == QG_FORM_AUTO && ncol >= kSpAutoCols && (C == 2 || kmin >= kSpAutoK1);
     if (c.walk) return c;
     c.lds = form == QG_FORM_SMALLN_LDS ||
             (form != QG_FORM_SMALLN_REGS && (units >= 32 * 4 || (C == 2 && tiles <= 1024)));
