@@ -441,7 +441,10 @@ qg_status lmhead_topk(const void* w_packed, const float* x, int64_t M, int64_t K
  *                 the chunked walk form (one workgroup per CU walks several tiles
  *                 chunk by chunk along K; any K, the weights of each matrix < 2 GiB),
  *                 or that form over tile groups and K slices (the _ws entry point
- *                 with a workspace only).
+ *                 with a workspace only), or tile groups and K slices whose
+ *                 activations are staged whole before the weights are walked (the
+ *                 _ws entry point, up to 16 columns and N times the slice's
+ *                 super-blocks at most 160; else as the previous value).
  *   smalln_waves  wavefronts per workgroup of the register-staged form: 1..8.
  *   smalln_tiles  16-row tiles per workgroup (matrix-core forms): 1, 2, 4.
  *   smalln_depth  weight-queue depth in chunks of the chunked-LDS form: 2..4.
@@ -459,6 +462,7 @@ qg_status lmhead_topk(const void* w_packed, const float* x, int64_t M, int64_t K
 #define QG_FORM_SMALLN_STREAM 5
 #define QG_FORM_SMALLN_WALK 6
 #define QG_FORM_SMALLN_SPLIT 7
+#define QG_FORM_SMALLN_SLICE 8
 #define QG_FORM_VERIFY_MFMA 1
 #define QG_FORM_VERIFY_DOT 2
 #define QG_FORM_VERIFY_STREAM 3

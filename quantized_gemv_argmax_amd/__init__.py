@@ -52,7 +52,7 @@ class _LaunchOverride(ctypes.Structure):
 # kernel forms a launch override can force (include/qgemv.h)
 FORM_AUTO = 0
 FORM_SMALLN_REGS, FORM_SMALLN_LDS, FORM_SMALLN_LDS1, FORM_SMALLN_DOT, FORM_SMALLN_STREAM, FORM_SMALLN_WALK, \
-    FORM_SMALLN_SPLIT = 1, 2, 3, 4, 5, 6, 7
+    FORM_SMALLN_SPLIT, FORM_SMALLN_SLICE = 1, 2, 3, 4, 5, 6, 7, 8
 FORM_VERIFY_MFMA, FORM_VERIFY_DOT, FORM_VERIFY_STREAM = 1, 2, 3
 
 

@@ -1023,7 +1023,7 @@ __global__ __launch_bounds__(64 * W, 4) void q4k_smalln_stream_kernel(SnArgs a) 
 // fp32 matrix-core product); every column block c of 16 columns reuses one B.
 constexpr int kWkWaves = 16, kWkTiles = 10;
 constexpr int64_t kWkAutoTiles = 1024;
-constexpr int kSpMaxSlices = 16, kSpAutoCols = 4, kSpAutoK1 = 8192;
+constexpr int kSpMaxSlices = 16, kSpAutoCols = 3, kSpAutoK1 = 8192;
 
 
 template <int C, int KC_, int TMAX>
@@ -1126,6 +1126,109 @@ QG_DEV void wk_dot(qg_f4 (&acc)[C], const SwItem<1>& it, const unsigned char* bu
         for (int e = 0; e < 4; ++e) acc[c][e] = fmaf(dd, p[c][e], acc[c][e]);
 }
 
+template <int C>
+QG_DEV void wk_finish(qg_f4 (&sum)[C], unsigned char* lds, const SnProb& P, int j, int h, int nt, int G, int wave,
+                      int lane);
+
+// End of the walk and slice forms: the per-tile partial sums of the KC
+// wavefronts of each tile meet in LDS (every wavefront has finished reading the
+// activations), wavefront w < nt adds those of tile slot w, and the sums go to Y,
+// or, for one of several K slices, to the workspace for the slices' last
+// workgroup to add.
+template <int C, int KC, int MU>
+QG_DEV void wk_tail(const qg_f4 (&acc)[MU][C], unsigned char* lds, const SnProb& P, int j, int h, int nt, int G,
+                    int wave, int lane) {
+    qg_f4* park = reinterpret_cast<qg_f4*>(lds);
+#pragma unroll
+    for (int m = 0; m < MU; ++m) {
+        const int u = wave + kWkWaves * m;
+        if (u / KC < nt)
+#pragma unroll
+            for (int c = 0; c < C; ++c) park[(u * C + c) * 64 + lane] = acc[m][c];
+    }
+    sw_barrier();
+    // wavefront w < nt owns tile slot w from here on
+    qg_f4 sum[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        sum[c] = park[((min(wave, nt - 1) * KC) * C + c) * 64 + lane];
+#pragma unroll
+        for (int b2 = 1; b2 < KC; ++b2) sum[c] += park[((min(wave, nt - 1) * KC + b2) * C + c) * 64 + lane];
+    }
+    wk_finish<C>(sum, lds, P, j, h, nt, G, wave, lane);
+}
+
+// Sums of tile slot w < nt (wavefront w) to Y, or, for one of several K slices,
+// to the workspace for the slices' last workgroup to add.
+template <int C>
+QG_DEV void wk_finish(qg_f4 (&sum)[C], unsigned char* lds, const SnProb& P, int j, int h, int nt, int G, int wave,
+                      int lane) {
+    const int i = lane & 15, s = lane >> 4;
+    const int t = j + min(wave, nt - 1) * G;
+    const int rt = min(T, P.M - t * T);
+    if (P.part) {
+        // One of several K slices. Its partial sums go to the workspace with
+        // device-coherent stores; after every wavefront's stores have completed, one
+        // lane counts the workgroup in on its tile group's counter, and the group's
+        // last workgroup (which saw the others' arrivals, hence their completed
+        // stores) adds the slices' partial sums in slice order with device-coherent
+        // loads and writes Y, then returns the counter to zero. No workgroup waits
+        // for another.
+        // partial sums: one buffer resource over the problem's slices; cache policy
+        // sc1 makes the stores and loads device-coherent (other XCDs' L2 caches are
+        // not consulted)
+        constexpr int kCoherent = 0x10;
+        const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)P.part, (short)0, P.slices * P.tiles * C * 1024, kQgRawBufferFlags);
+        // (only lanes holding real columns store and load)
+        if (wave < nt)
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                if (16 * c + 4 * s < P.N)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(qg_u4v, sum[c]), pr,
+                                                       (uint32_t)lane * 16u,
+                                                       ((h * P.tiles + t) * C + c) * 1024, kCoherent);
+        __builtin_amdgcn_s_waitcnt(0);
+        int* last = reinterpret_cast<int*>(lds);  // the parked sums have all been read
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t old = __hip_atomic_fetch_add(P.ctr + j, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *last = old == (uint32_t)(P.slices - 1);
+            if (*last) __hip_atomic_store(P.ctr + j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!*last || wave >= nt) return;
+        // per column block, all slices' loads in flight at once, then added in
+        // slice order
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            qg_u4v pv[kSpMaxSlices];
+#pragma unroll
+            for (int h2 = 0; h2 < kSpMaxSlices; ++h2)
+                pv[h2] = __builtin_amdgcn_raw_buffer_load_b128(
+                    pr, h2 < P.slices && 16 * c + 4 * s < P.N ? (uint32_t)lane * 16u : kOutOfRange,
+                    h2 < P.slices ? ((h2 * P.tiles + t) * C + c) * 1024 : 0, kCoherent);
+            qg_f4 v = __builtin_bit_cast(qg_f4, pv[0]);
+#pragma unroll
+            for (int h2 = 1; h2 < kSpMaxSlices; ++h2)
+                if (h2 < P.slices) v += __builtin_bit_cast(qg_f4, pv[h2]);
+            sum[c] = v;
+        }
+    }
+    if (wave >= nt) return;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        if (i < rt) {
+            const int row = t * T + i;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int n = 16 * c + 4 * s + e;
+                if (n < P.N) P.Y[(int64_t)n * P.ldy + row] = sum[c][e];
+            }
+        }
+    }
+}
+
 template <int C, int KC_, int TMAX>
 __global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_walk_kernel(SnArgs a) {
     using Gm = WkGeom<C, KC_, TMAX>;
@@ -1195,85 +1298,119 @@ __global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_walk_kernel(SnArg
         sw_barrier();
     }
 
-    // per-tile partial sums of the KC wavefronts of each tile meet in LDS
-    qg_f4* park = reinterpret_cast<qg_f4*>(lds);
+    wk_tail<C, KC, MU>(acc, lds, P, j, h, nt, G, wave, lane);
+}
+
+// K-slice form for up to 16 columns (one column block): tile groups of TMAX
+// tiles and K slices as in the walk form, but the activations of the whole slice
+// (at most NG 8-element groups per thread: N times the slice's super-blocks at
+// most 32 NG) are staged into LDS once, before any weight is requested, so that
+// they arrive first, and the walk over the weights has no staging and no
+// barrier. Wavefront w keeps tile slot w % TMAX and takes super-blocks w / TMAX,
+// w / TMAX + 16 / TMAX, ... of the slice into one accumulator, the next
+// super-block's weights in flight while it computes one. Slice h covers
+// super-blocks [h nb / H, (h + 1) nb / H) of the H slices. Measured on the 7B
+// down projection (N = 5): weights requested before the activations delay them
+// (staged at 3.7 us instead of 2.2), and deeper weight queues (two to four units
+// ahead) or units claimed through an LDS counter were slower (14.1 us against
+// 15.0, 16.0, 16.7 and 15.2).
+constexpr int kSlGroups = 5, kSlTiles = 4;
+
+template <int TMAX, int NG>
+__global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_slice_kernel(SnArgs a) {
+    constexpr int R = 2;  // units in the ring: one computed, one in flight
+    static_assert(kWkWaves % TMAX == 0, "tile slots must divide the wavefronts");
+    constexpr int SS = kWkWaves / TMAX;  // super-block stride of a wavefront
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int wg = blockIdx.x;
+    int k = 0;
 #pragma unroll
-    for (int m = 0; m < MU; ++m) {
-        const int u = wave + kWkWaves * m;
-        if (u / KC < nt)
+    for (int i = 1; i < QG_MAX_BATCH; ++i)
+        if (i < a.count && wg >= a.begin[i]) k = i;
+    const SnProb P = a.p[k];
+    const int G = P.wgs;
+    const int j = (wg - P.wg_begin) % G;  // tile group: tiles j, j + G, ...
+    const int h = (wg - P.wg_begin) / G;  // K slice
+    const int nt = (P.tiles - j + G - 1) / G;  // tiles of this walk, 1..TMAX
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = threadIdx.x;
+    const int i = lane & 15, s = lane >> 4;
+    const int nb = P.nb;
+    const int kb0 = (int)((int64_t)h * nb / P.slices), kb1 = (int)((int64_t)(h + 1) * nb / P.slices);
+    const int ns = kb1 - kb0;                            // super-blocks of the slice
+    const int GS = 32 * ns;                              // 8-element groups per column of the slice
+    const uint32_t RB = (uint32_t)(ns * 256 + 8) * 2;    // bytes per activation row
+    const uint32_t XT = (uint32_t)P.N * RB;              // table of -X_j[n], 16 columns per sub-block
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)P.w, (short)0, P.M * nb * 144, kQgRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)P.X, (short)0, (int)(((int64_t)(P.N - 1) * P.ldx + (int64_t)nb * 256) * 4), kQgRawBufferFlags);
+    const int ts = wave % TMAX, s0 = wave / TMAX;
+    const int nu = ts < nt && s0 < ns ? (ns - s0 + SS - 1) / SS : 0;  // this wavefront's units
+    const int t = j + min(ts, nt - 1) * G;
+
+    // the slice's activations (group g: column g / GS, elements 8 (g % GS)..+7 of
+    // the slice; groups past N columns read zeros without a memory access)
+    float4 v[NG][2];
 #pragma unroll
-            for (int c = 0; c < C; ++c) park[(u * C + c) * 64 + lane] = acc[m][c];
+    for (int r = 0; r < NG; ++r) {
+        const int g = tid + 64 * kWkWaves * r;
+        const int n = g / GS, k8 = g - n * GS;
+        const uint32_t off = n < P.N ? (uint32_t)(((int64_t)n * P.ldx + kb0 * 256 + 8 * k8) * 4) : kOutOfRange;
+        v[r][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+        v[r][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 16, 0));
+    }
+    SwItem<1> ring[R];
+    // fp16 activations, and the sums of each 32-element sub-block over the same
+    // fp16 values (a quad of threads holds one sub-block of a column)
+    float* table = reinterpret_cast<float*>(lds + XT);
+#pragma unroll
+    for (int r = 0; r < NG; ++r) {
+        const int g = tid + 64 * kWkWaves * r;
+        const int n = g / GS, k8 = g - n * GS;
+        const qg_h8 hx = qg_a_operand(v[r][0], v[r][1]);
+        if (n < P.N) *reinterpret_cast<qg_h8*>(lds + n * RB + 16 * k8) = hx;
+        const uint4 hw = __builtin_bit_cast(uint4, hx);
+        const float xs = qg_quad_sum(qg_sum_pairs4(hw.x, hw.y, hw.z, hw.w));
+        if (n < P.N && (k8 & 3) == 0) table[(k8 >> 2) * 16 + n] = -xs;
     }
     sw_barrier();
-    // wavefront w < nt owns tile slot w from here on
-    const int t = j + min(wave, nt - 1) * G;
-    const int rt = min(T, P.M - t * T);
-    qg_f4 sum[C];
+    // then the weights of this wavefront's first R - 1 units
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-        sum[c] = park[((min(wave, nt - 1) * KC) * C + c) * 64 + lane];
+    for (int r = 0; r + 1 < R; ++r)
+        st_load(ring[r], wr, P, t, min(kb0 + s0 + SS * r, nb - 1), i, s, r < nu);
+
+    const uint32_t an0 = (uint32_t)((i < P.N ? i : 0) * RB + 16 * s);
+    const uint32_t xt0 = XT + (uint32_t)(s * 16 + i) * 4;
+    const uint32_t sh = 8u * (uint32_t)s;
+    qg_f4 acc[1] = {qg_f4{0.f, 0.f, 0.f, 0.f}};
+    // Each step requests unit it + R - 1 and computes unit it. The loads are
+    // unconditional (past the wavefront's last unit they read zeros without a
+    // memory access), so every wait count is exact.
+    for (int it = 0; it < nu; it += R) {
 #pragma unroll
-        for (int b2 = 1; b2 < KC; ++b2) sum[c] += park[((min(wave, nt - 1) * KC + b2) * C + c) * 64 + lane];
-    }
-    if (P.part) {
-        // One of several K slices. Its partial sums go to the workspace with
-        // device-coherent stores; after every wavefront's stores have completed, one
-        // lane counts the workgroup in on its tile group's counter, and the group's
-        // last workgroup (which saw the others' arrivals, hence their completed
-        // stores) adds the slices' partial sums in slice order with device-coherent
-        // loads and writes Y, then returns the counter to zero. No workgroup waits
-        // for another.
-        // partial sums: one buffer resource over the problem's slices; cache policy
-        // sc1 makes the stores and loads device-coherent (other XCDs' L2 caches are
-        // not consulted)
-        constexpr int kCoherent = 0x10;
-        const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)P.part, (short)0, P.slices * P.tiles * C * 1024, kQgRawBufferFlags);
-        if (wave < nt)
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(qg_u4v, sum[c]), pr,
-                                                       (uint32_t)lane * 16u,
-                                                       ((h * P.tiles + t) * C + c) * 1024, kCoherent);
-        __builtin_amdgcn_s_waitcnt(0);
-        int* last = reinterpret_cast<int*>(lds);  // the parked sums have all been read
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t old = __hip_atomic_fetch_add(P.ctr + j, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            *last = old == (uint32_t)(P.slices - 1);
-            if (*last) __hip_atomic_store(P.ctr + j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        if (!*last || wave >= nt) return;
-        // per column block, all slices' loads in flight at once, then added in
-        // slice order
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            qg_u4v pv[kSpMaxSlices];
-#pragma unroll
-            for (int h2 = 0; h2 < kSpMaxSlices; ++h2)
-                pv[h2] = __builtin_amdgcn_raw_buffer_load_b128(
-                    pr, h2 < P.slices ? (uint32_t)lane * 16u : kOutOfRange,
-                    h2 < P.slices ? ((h2 * P.tiles + t) * C + c) * 1024 : 0, kCoherent);
-            qg_f4 v = __builtin_bit_cast(qg_f4, pv[0]);
-#pragma unroll
-            for (int h2 = 1; h2 < kSpMaxSlices; ++h2)
-                if (h2 < P.slices) v += __builtin_bit_cast(qg_f4, pv[h2]);
-            sum[c] = v;
-        }
-    }
-    if (wave >= nt) return;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-        if (i < rt) {
-            const int row = t * T + i;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int n = 16 * c + 4 * s + e;
-                if (n < P.N) P.Y[(int64_t)n * P.ldy + row] = sum[c][e];
+        for (int r = 0; r < R; ++r) {
+            const int u = it + r;
+            st_load(ring[(r + R - 1) % R], wr, P, t, min(kb0 + s0 + SS * (u + R - 1), nb - 1), i, s, u + R - 1 < nu);
+            __builtin_amdgcn_sched_barrier(0);
+            if (u < nu) {
+                const uint32_t sl = (uint32_t)(s0 + SS * u);  // super-block within the slice
+                const uint32_t an[1] = {an0 + 512u * sl};
+                wk_dot<1>(acc, ring[r], lds, an, xt0 + 512u * sl, sh);
             }
         }
     }
+    // wavefronts of one tile slot meet in LDS (every wavefront has finished
+    // reading the activations)
+    sw_barrier();
+    qg_f4* park = reinterpret_cast<qg_f4*>(lds);
+    park[wave * 64 + lane] = acc[0];
+    sw_barrier();
+    qg_f4 sum[1] = {park[min(wave, TMAX - 1) * 64 + lane]};
+#pragma unroll
+    for (int w2 = 1; w2 < SS; ++w2) sum[0] += park[(min(wave, TMAX - 1) + TMAX * w2) * 64 + lane];
+    wk_finish<1>(sum, lds, P, j, h, nt, G, wave, lane);
 }
 
 // ------------------------------------------------------------------ host side
@@ -1338,7 +1475,8 @@ struct SnCfg {
     bool dot;   // vector-ALU dot-product kernel (N <= 8, q4k_smalln_dot.hip)
     bool stream;  // streamed single-pass kernel (single-pass shapes, many tiles)
     bool walk;    // chunked walk kernel (many tiles, up to 32 columns)
-    bool split;   // the walk kernel over groups of tiles and K slices, summed by a second kernel
+    bool split;   // groups of tiles and K slices (workspace), the last workgroup of a group adding them
+    bool slice;   // ... in the slice kernel where it fits, else in the walk kernel
 };
 SnCfg choose_cfg(const SnArgs& a, int C, bool ws) {
     const qg_launch_override& ov = qg::launch_override();
@@ -1351,7 +1489,7 @@ SnCfg choose_cfg(const SnArgs& a, int C, bool ws) {
         tiles += a.p[i].tiles;
         ncol = std::max(ncol, (int)a.p[i].N);
     }
-    SnCfg c{1, tiles > 256 ? 2 : 1, false, 2, false, false, false, false, false};
+    SnCfg c{1, tiles > 256 ? 2 : 1, false, 2, false, false, false, false, false, false};
     if (C == 2 && tiles > 1024) c.TW = 4;
     // Form selection, from measurements on the 7B shapes (stage times in us, register
     // form -> chosen form):
@@ -1386,9 +1524,10 @@ SnCfg choose_cfg(const SnArgs& a, int C, bool ws) {
     // 17.7 (dot form) -> 16.0; but N = 3 down 15.4 (dot) -> 16.0, N = 16 q/k/v 11.2 ->
     // 13.1 and o 9.9 -> 10.6: with one column block, only long K gains)
     c.split = c.walk = ws && wk &&
-                       (form == QG_FORM_SMALLN_SPLIT ||
+                       (form == QG_FORM_SMALLN_SPLIT || form == QG_FORM_SMALLN_SLICE ||
                         (form == QG_FORM_AUTO && tiles < kWkAutoTiles && ncol >= kSpAutoCols &&
                          (C == 2 || kmin >= kSpAutoK1)));
+    c.slice = c.split && form != QG_FORM_SMALLN_SPLIT;
     if (c.walk) return c;
     // (three and four columns over many tiles go to the streamed form below: gate/up,
     // 2368 tiles, N = 3 23.6 -> 20.7 us, N = 4 26.6 -> 20.1)
@@ -1558,6 +1697,49 @@ WkShape walk_shape(int C, int nmax, bool split) {
     return WkShape{1, 4, kWkTiles, 4};
 }
 
+// The slice form serves a batch whose every slice fits its activation staging
+// and LDS.
+size_t slice_lds_bytes(const SnArgs& a);
+bool slice_fits(const SnArgs& a) {
+    for (int i = 0; i < a.count; ++i)
+        if ((int64_t)a.p[i].N * a.p[i].slice_sbs * 32 > (int64_t)kSlGroups * 64 * kWkWaves) return false;
+    return slice_lds_bytes(a) <= 160 * 1024;
+}
+
+// Dynamic LDS of the slice form: the slice's activation rows and sub-block sums,
+// or the parked sums if larger.
+size_t slice_lds_bytes(const SnArgs& a) {
+    size_t b = (size_t)kWkWaves * 1024;
+    for (int i = 0; i < a.count; ++i) {
+        const size_t ns = (size_t)a.p[i].slice_sbs;
+        b = std::max(b, (size_t)a.p[i].N * (ns * 256 + 8) * 2 + ns * 512);
+    }
+    return b;
+}
+
+template <int NG>
+void launch_slice(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
+    const auto kern = q4k_smalln_slice_kernel<kSlTiles, NG>;
+    static std::atomic<bool> attr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr[dev].load(std::memory_order_acquire)) {
+        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr[dev].store(true, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWkWaves), lds, s, a);
+}
+
+// Activation groups per thread the batch's slices need: three (the smaller
+// instance, the only one at N <= 5 on the 7B down projection) or kSlGroups.
+void launch_slice_any(const SnArgs& a, int grid, hipStream_t s) {
+    int64_t g = 0;
+    for (int i = 0; i < a.count; ++i) g = std::max<int64_t>(g, (int64_t)a.p[i].N * a.p[i].slice_sbs * 32);
+    if (g <= 3 * 64 * kWkWaves)
+        launch_slice<3>(a, grid, slice_lds_bytes(a), s);
+    else
+        launch_slice<kSlGroups>(a, grid, slice_lds_bytes(a), s);
+}
+
 void launch_walk_any(const WkShape& w, const SnArgs& a, int grid, int nmax, hipStream_t s) {
     const size_t lds = walk_lds_bytes(w, nmax);
     if (w.C == 2)
@@ -1615,6 +1797,23 @@ int64_t split_grid(SnArgs& a, int cus, const WkShape& w, void* ws, size_t* need)
     }
     *need = npart ? ctr_bytes + npart : 0;
     return wgs;
+}
+
+// Plan of a batch with a workspace: tile groups and K slices for the slice form
+// where it may serve (one column block, every slice's activations within its
+// staging), else for the walk form. Returns the grid; *slice tells which form.
+int64_t split_plan(SnArgs& a, int cus, int C, int nmax, bool slice_ok, void* ws, size_t* need, bool* slice) {
+    if (slice_ok && C == 1) {
+        SnArgs b = a;
+        const int64_t grid = split_grid(b, cus, WkShape{1, 8, kSlTiles, kSlTiles}, ws, need);
+        if (slice_fits(b)) {
+            a = b;
+            *slice = true;
+            return grid;
+        }
+    }
+    *slice = false;
+    return split_grid(a, cus, walk_shape(C, nmax, true), ws, need);
 }
 
 void launch_lds_any(const SnArgs& a, int grid, int C, int TW, int D, size_t lds, hipStream_t s) {
@@ -1683,7 +1882,8 @@ size_t split_bytes(const qg_gemm_problem* probs, int count) {
     const int cus = qg::check_device() == QG_OK ? qg::device_cus() : 256;
     qg::clear_error();
     size_t need = 0;
-    split_grid(a, cus, walk_shape(C, nmax, true), nullptr, &need);
+    bool slice = false;
+    split_plan(a, cus, C, nmax, cfg.slice, nullptr, &need, &slice);
     return need;
 }
 
@@ -1699,12 +1899,15 @@ qg_status run(const qg_gemm_problem* probs, int count, hipStream_t stream, void*
     if (st) return st;
     if (cfg.split) {
         size_t need = 0;
-        const WkShape ws_shape = walk_shape(C, nmax, true);
-        const int64_t grid = split_grid(a, qg::device_cus(), ws_shape, ws, &need);
+        bool slice = false;
+        const int64_t grid = split_plan(a, qg::device_cus(), C, nmax, cfg.slice, ws, &need, &slice);
         if (need > 0 && (!ws || ws_bytes < need))
             return qg::fail(QG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
         if (need > 0 && !qg::aligned16(ws)) return qg::fail(QG_ERR_ALIGN, "workspace not 16-byte aligned");
-        launch_walk_any(ws_shape, a, (int)grid, nmax, stream);
+        if (slice)
+            launch_slice_any(a, (int)grid, stream);
+        else
+            launch_walk_any(walk_shape(C, nmax, true), a, (int)grid, nmax, stream);
         return qg::launch_status("qgemm_q4k_smalln_batch_ws");
     }
     if (cfg.dot) return qg::smalln_dot_launch(probs, count, stream);

@@ -111,7 +111,7 @@ qg_status qg_set_launch_override(const qg_launch_override* o) {
         return (qg_status)qg::fail(QG_ERR_SHAPE, "gemv_waves=%d not in {0, 1, 2, 4, 8}", v.gemv_waves);
     if (!in(v.smalln_form,
             {QG_FORM_SMALLN_REGS, QG_FORM_SMALLN_LDS, QG_FORM_SMALLN_LDS1, QG_FORM_SMALLN_DOT, QG_FORM_SMALLN_STREAM,
-             QG_FORM_SMALLN_WALK, QG_FORM_SMALLN_SPLIT}))
+             QG_FORM_SMALLN_WALK, QG_FORM_SMALLN_SPLIT, QG_FORM_SMALLN_SLICE}))
         return (qg_status)qg::fail(QG_ERR_SHAPE, "smalln_form=%d unknown", v.smalln_form);
     if (!in(v.smalln_waves, {1, 2, 4, 8}))
         return (qg_status)qg::fail(QG_ERR_SHAPE, "smalln_waves=%d not in {0, 1, 2, 4, 8}", v.smalln_waves);

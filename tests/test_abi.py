@@ -337,7 +337,7 @@ def test_smalln_forced_forms_keep_validation(L):
     # forcing a form does not relax the small-N argument checks
     f = L.qgemm_q4k_smalln
     for form in (qg.FORM_SMALLN_DOT, qg.FORM_SMALLN_REGS, qg.FORM_SMALLN_LDS, qg.FORM_SMALLN_LDS1,
-                 qg.FORM_SMALLN_STREAM, qg.FORM_SMALLN_WALK, qg.FORM_SMALLN_SPLIT):
+                 qg.FORM_SMALLN_STREAM, qg.FORM_SMALLN_WALK, qg.FORM_SMALLN_SPLIT, qg.FORM_SMALLN_SLICE):
         with qg.launch_override(smalln_form=form):
             assert f(C, A, 256, B, 64, 64, 256, 0, None) == ESHAPE
             assert f(C, A, 128, B, 64, 64, 256, 3, None) == ESHAPE   # ldx < K
@@ -357,6 +357,11 @@ def test_smalln_ws_sizes_and_validation(L):
         # one counter per tile group (a 256-byte aligned block), then a partial sum
         # per K slice, tile and 16-column block, at most 16 slices
         assert need <= 4 * (224 + 288) + 256 + 16 * (224 + 288) * 2 * 1024
+    # the slice form's plan for the 7B down projection at N = 5: 56 groups of four
+    # tiles, four K slices (18 or 19 super-blocks: 5 x 19 <= 160 staged groups)
+    one = (P * 1)(P(C, A, 18944, B, 3584, 3584, 18944, 5))
+    with qg.launch_override(smalln_form=qg.FORM_SMALLN_SLICE):
+        assert L.qgemm_q4k_smalln_batch_workspace_bytes(one, 1) == 256 + 4 * 224 * 1024
     assert L.qgemm_q4k_smalln_batch_ws(None, 1, None, 0, None) == ENULL
     assert L.qgemm_q4k_smalln_batch_ws(bad, 1, None, 0, None) == ESHAPE
 
@@ -364,7 +369,7 @@ def test_smalln_ws_sizes_and_validation(L):
 def test_launch_override_validation(L):
     O = qg._LaunchOverride
     assert L.qg_set_launch_override(None) == OK
-    for field, bad in [("gemv_waves", 3), ("gemv_waves", 16), ("smalln_form", 8), ("smalln_waves", 16),
+    for field, bad in [("gemv_waves", 3), ("gemv_waves", 16), ("smalln_form", 9), ("smalln_waves", 16),
                        ("smalln_tiles", 3), ("smalln_depth", 1), ("verify_form", 4), ("verify_waves", 2),
                        ("verify_tiles", 8)]:
         o = O()

@@ -33,7 +33,7 @@ pytestmark = pytest.mark.gpu
 
 FORMS = {"auto": qg.FORM_AUTO, "regs": qg.FORM_SMALLN_REGS, "lds": qg.FORM_SMALLN_LDS,
          "lds1": qg.FORM_SMALLN_LDS1, "dot": qg.FORM_SMALLN_DOT, "stream": qg.FORM_SMALLN_STREAM,
-         "walk": qg.FORM_SMALLN_WALK, "split": qg.FORM_SMALLN_SPLIT}
+         "walk": qg.FORM_SMALLN_WALK, "split": qg.FORM_SMALLN_SPLIT, "slice": qg.FORM_SMALLN_SLICE}
 
 
 @functools.lru_cache(maxsize=None)
@@ -118,7 +118,7 @@ SMALLN_CASES = [("auto", N) for N in (1, 2, 3, 4, 5, 8, 9, 16, 17, 32)] + \
                [("regs", N) for N in (5, 17, 32)] + [("lds", N) for N in (5, 17, 32)] + \
                [("lds1", N) for N in (5, 8)] + [("dot", N) for N in (1, 5, 8)] + \
                [("stream", N) for N in (1, 5, 8)] + [("walk", N) for N in (1, 5, 16, 17, 32)] + \
-               [("split", N) for N in (1, 5, 17, 32)]
+               [("split", N) for N in (1, 5, 17, 32)] + [("slice", N) for N in (1, 4, 5, 8, 16)]
 
 
 @pytest.mark.parametrize("form,N", SMALLN_CASES)
@@ -131,7 +131,7 @@ def test_smalln_exact(form, N, M, K):
     wp = packed_q4k(W, M, K)
     case(f"qgemm_q4k_smalln exact form={form} M={M} K={K} N={N}")
     with qg.launch_override(smalln_form=FORMS[form]):
-        if form == "split":
+        if form in ("split", "slice"):
             Y = torch.empty((N, (M + 3) // 4 * 4), device="cuda:0")
             qg.qgemm_q4k_smalln_batch_ws([(wp, to_dev(X), Y, M, K)])
         else:

@@ -293,26 +293,22 @@ def test_walk_form(N):
                 assert_within(Yc[n], Yr[n], Ar[n], f"walk M={M} K={K} col {n}")
 
 
-@pytest.mark.parametrize("N", [1, 5, 16, 17, 32])
-def test_split_walk_form(N):
-    # the walk form over tile groups and K slices (with a workspace): slices of one
-    # to many super-blocks, a ragged last slice, problems left with one slice next
-    # to sliced ones in one batch, ragged tiles; partial sums added in slice order
-    qg.launch_override(smalln_form=qg.FORM_SMALLN_SPLIT).set()
-    batches = [[(530, 768, N), (77, 256, N), (1000, 3328, N)],
-               [(3584, 18944, N)],
-               [(33, 9984, N), (3001, 1280, N)]]
+def run_split(N, form, batches, key, what):
+    """Batches of problems through qgemm_q4k_smalln_batch_ws with a forced K-slice
+    form: nine calls on one workspace give bit-identical results, leave the
+    arrival counters zero and match the oracle per (row, column)."""
+    qg.launch_override(smalln_form=form).set()
     for bi, shapes in enumerate(batches):
         probs, refs = [], []
         for i, (M, K, n_) in enumerate(shapes):
-            W = workloads.q4k_blocks(M, K, key=(45, bi, i))
-            X = workloads.x_columns(K, n_, key=(45, bi, i, n_))
+            W = workloads.q4k_blocks(M, K, key=(key, bi, i))
+            X = workloads.x_columns(K, n_, key=(key, bi, i, n_))
             Y = torch.full((n_, (M + 3) // 4 * 4), float("nan"), device="cuda:0")
             rows = sample_rows(M, 192, seed=M + i) if M * K * n_ > 1 << 26 else None
             probs.append((packed_q4k(W, M, K), to_dev(X), Y, M, K))
             refs.append((rows, oracle.gemm_q4k(W, M, K, X, rows=rows)))
         need = qg.qgemm_q4k_smalln_batch_workspace_bytes(probs)
-        case(f"qgemm_q4k_smalln_batch_ws split N={N} batch {bi}: {shapes}, workspace {need}")
+        case(f"qgemm_q4k_smalln_batch_ws {what} N={N} batch {bi}: {shapes}, workspace {need}")
         assert need > 0
         ws = qg.Workspace("cuda:0", need)  # zero-filled: the arrival counters start at 0
         qg.qgemm_q4k_smalln_batch_ws(probs, ws)
@@ -326,16 +322,41 @@ def test_split_walk_form(N):
             qg.qgemm_q4k_smalln_batch_ws(probs, ws)
             torch.cuda.synchronize()
             for p_, Y0 in zip(probs, first):
-                assert torch.equal(p_[2][:, :p_[3]], Y0[:, :p_[3]]), f"split walk form differs on call {rep + 2}"
+                assert torch.equal(p_[2][:, :p_[3]], Y0[:, :p_[3]]), f"{what} form differs on call {rep + 2}"
         assert int(ws.buf[:64].ne(0).sum()) == 0, "arrival counters not returned to zero"
         for (w, X, Y, M, K), Y0, (rows, (Yr, Ar)) in zip(probs, first, refs):
-            assert torch.equal(Y[:, :M], Y0[:, :M]), "split walk form not deterministic"
-            assert not torch.isnan(Y[:, :M]).any(), "split walk form left outputs unwritten"
+            assert torch.equal(Y[:, :M], Y0[:, :M]), f"{what} form not deterministic"
+            assert not torch.isnan(Y[:, :M]).any(), f"{what} form left outputs unwritten"
             Yc = Y.cpu().numpy()[:, :M]
             if rows is not None:
                 Yc = Yc[:, rows]
             for n in range(X.shape[0]):
-                assert_within(Yc[n], Yr[n], Ar[n], f"split M={M} K={K} col {n}")
+                assert_within(Yc[n], Yr[n], Ar[n], f"{what} M={M} K={K} col {n}")
+
+
+@pytest.mark.parametrize("N", [1, 5, 16, 17, 32])
+def test_split_walk_form(N):
+    # the walk form over tile groups and K slices (with a workspace): slices of one
+    # to many super-blocks, a ragged last slice, problems left with one slice next
+    # to sliced ones in one batch, ragged tiles; partial sums added in slice order
+    batches = [[(530, 768, N), (77, 256, N), (1000, 3328, N)],
+               [(3584, 18944, N)],
+               [(33, 9984, N), (3001, 1280, N)]]
+    run_split(N, qg.FORM_SMALLN_SPLIT, batches, 45, "split walk")
+
+
+@pytest.mark.parametrize("N", [1, 4, 5, 8, 9, 16])
+def test_slice_form(N):
+    # tile groups and K slices with each slice's activations staged whole: the 7B
+    # down projection (slices of 18 and 19 super-blocks), slices of one to a few
+    # super-blocks next to unsliced problems, ragged tiles and tile groups; where N
+    # times a slice's super-blocks exceeds 160 (N = 9 and 16 on the down
+    # projection) the batch goes to the K-sliced walk instead
+    batches = [[(3584, 18944, N)],
+               [(530, 768, N), (77, 256, N), (1000, 3328, N)],
+               [(33, 9984, N), (3001, 1280, N)],
+               [(1234, 4608, N), (64, 2560, N)]]
+    run_split(N, qg.FORM_SMALLN_SLICE, batches, 46, "slice")
 
 
 @pytest.mark.parametrize("N", [5, 32])
