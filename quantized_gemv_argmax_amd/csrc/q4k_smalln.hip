@@ -1314,7 +1314,7 @@ __global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_walk_kernel(SnArg
 // (staged at 3.7 us instead of 2.2), and deeper weight queues (two to four units
 // ahead) or units claimed through an LDS counter were slower (14.1 us against
 // 15.0, 16.0, 16.7 and 15.2).
-constexpr int kSlGroups = 5, kSlTiles = 4;
+constexpr int kSlGroups = 5, kSlTiles = 4, kSl1Tiles = 2;
 
 template <int TMAX, int NG>
 __global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_slice_kernel(SnArgs a) {
@@ -1477,8 +1477,9 @@ struct SnCfg {
     bool walk;    // chunked walk kernel (many tiles, up to 32 columns)
     bool split;   // groups of tiles and K slices (workspace), the last workgroup of a group adding them
     bool slice;   // ... in the slice kernel where it fits, else in the walk kernel
+    bool slice1;  // the slice kernel without K slices, groups of kSl1Tiles tiles
 };
-SnCfg choose_cfg(const SnArgs& a, int C, bool ws) {
+SnCfg choose_cfg(const SnArgs& a, int C, bool ws, int cus) {
     const qg_launch_override& ov = qg::launch_override();
     const int form = ov.smalln_form;
     int units = INT_MAX;
@@ -1489,7 +1490,7 @@ SnCfg choose_cfg(const SnArgs& a, int C, bool ws) {
         tiles += a.p[i].tiles;
         ncol = std::max(ncol, (int)a.p[i].N);
     }
-    SnCfg c{1, tiles > 256 ? 2 : 1, false, 2, false, false, false, false, false, false};
+    SnCfg c{1, tiles > 256 ? 2 : 1, false, 2, false, false, false, false, false, false, false};
     if (C == 2 && tiles > 1024) c.TW = 4;
     // Form selection, from measurements on the 7B shapes (stage times in us, register
     // form -> chosen form):
@@ -1529,6 +1530,19 @@ SnCfg choose_cfg(const SnArgs& a, int C, bool ws) {
                          (C == 2 || kmin >= kSpAutoK1)));
     c.slice = c.split && form != QG_FORM_SMALLN_SPLIT;
     if (c.walk) return c;
+    // The slice form without K slices, in groups of two tiles, for batches of more
+    // tiles than CUs but at most twice as many, where the streamed form puts two
+    // workgroups on some CUs (q/k/v, 288 tiles: N = 4 7.9 -> 7.3 us (dot form
+    // before), N = 5 8.75 -> 7.3, N = 8 9.1 -> 7.8; N = 3 stays with the dot form,
+    // 6.9 against 7.2); every problem's activations within the staging, and N <= 8
+    // as measured. Forced without a workspace, it needs only the fit.
+    bool s1fit = C == 1 && wk;
+    for (int i = 0; i < a.count; ++i)
+        s1fit = s1fit && (int64_t)a.p[i].N * a.p[i].nb * 32 <= (int64_t)kSlGroups * 64 * kWkWaves &&
+                (int64_t)a.p[i].N * (a.p[i].nb * 256 + 8) * 2 + (int64_t)a.p[i].nb * 512 <= 160 * 1024;
+    c.slice1 = s1fit && ((form == QG_FORM_AUTO && ncol >= 4 && ncol <= 8 && tiles > cus && tiles <= 2 * (int64_t)cus) ||
+                         (form == QG_FORM_SMALLN_SLICE && !ws));
+    if (c.slice1) return c;
     // (three and four columns over many tiles go to the streamed form below: gate/up,
     // 2368 tiles, N = 3 23.6 -> 20.7 us, N = 4 26.6 -> 20.1)
     const bool many_short = tiles >= kStAutoTiles && ncol >= 3;
@@ -1717,9 +1731,9 @@ size_t slice_lds_bytes(const SnArgs& a) {
     return b;
 }
 
-template <int NG>
+template <int TMAX, int NG>
 void launch_slice(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
-    const auto kern = q4k_smalln_slice_kernel<kSlTiles, NG>;
+    const auto kern = q4k_smalln_slice_kernel<TMAX, NG>;
     static std::atomic<bool> attr[64];
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr[dev].load(std::memory_order_acquire)) {
@@ -1730,14 +1744,36 @@ void launch_slice(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
 }
 
 // Activation groups per thread the batch's slices need: three (the smaller
-// instance, the only one at N <= 5 on the 7B down projection) or kSlGroups.
-void launch_slice_any(const SnArgs& a, int grid, hipStream_t s) {
+// instance, enough at N <= 5 on the 7B shapes) or kSlGroups; tmax tiles per group
+// (kSlTiles with K slices, kSl1Tiles without).
+void launch_slice_any(const SnArgs& a, int grid, int tmax, hipStream_t s) {
     int64_t g = 0;
     for (int i = 0; i < a.count; ++i) g = std::max<int64_t>(g, (int64_t)a.p[i].N * a.p[i].slice_sbs * 32);
-    if (g <= 3 * 64 * kWkWaves)
-        launch_slice<3>(a, grid, slice_lds_bytes(a), s);
+    const size_t lds = slice_lds_bytes(a);
+    const bool small = g <= 3 * 64 * kWkWaves;
+    if (tmax == kSl1Tiles)
+        small ? launch_slice<kSl1Tiles, 3>(a, grid, lds, s) : launch_slice<kSl1Tiles, kSlGroups>(a, grid, lds, s);
     else
-        launch_slice<kSlGroups>(a, grid, slice_lds_bytes(a), s);
+        small ? launch_slice<kSlTiles, 3>(a, grid, lds, s) : launch_slice<kSlTiles, kSlGroups>(a, grid, lds, s);
+}
+
+// The slice form without K slices: groups of kSl1Tiles tiles, one workgroup each,
+// writing Y directly. Fills wgs, slices, slice_sbs, wg_begin and begin; returns
+// the grid.
+int64_t slice1_grid(SnArgs& a) {
+    int64_t wgs = 0;
+    for (int i = 0; i < a.count; ++i) {
+        SnProb& P = a.p[i];
+        P.wgs = (int32_t)qg::ceil_div(P.tiles, kSl1Tiles);
+        P.slices = 1;
+        P.slice_sbs = P.nb;
+        P.part = nullptr;
+        P.ctr = nullptr;
+        P.wg_begin = (int32_t)wgs;
+        a.begin[i] = (int32_t)wgs;
+        wgs += P.wgs;
+    }
+    return wgs;
 }
 
 void launch_walk_any(const WkShape& w, const SnArgs& a, int grid, int nmax, hipStream_t s) {
@@ -1843,6 +1879,14 @@ void launch(const SnArgs& a, int grid, int W, hipStream_t s) {
     }
 }
 
+// CUs of the current device (256, as on MI355X, where there is none: the plan a
+// workspace query makes on the host matches the one a launch makes).
+int plan_cus() {
+    if (qg::check_device() == QG_OK) return qg::device_cus();
+    qg::clear_error();
+    return 256;
+}
+
 // Validates the problems and fills the kernel arguments and launch shape.
 qg_status plan(const qg_gemm_problem* probs, int count, SnArgs& a, SnCfg& cfg, int& C, int64_t& wgs, int& nmax,
                bool ws = false) {
@@ -1860,7 +1904,7 @@ qg_status plan(const qg_gemm_problem* probs, int count, SnArgs& a, SnCfg& cfg, i
         nmax = std::max(nmax, a.p[i].N);
     }
     C = nmax > 16 ? 2 : 1;
-    cfg = choose_cfg(a, C, ws);
+    cfg = choose_cfg(a, C, ws, plan_cus());
     wgs = 0;
     for (int i = 0; i < count; ++i) {
         a.p[i].wg_begin = (int32_t)wgs;
@@ -1878,9 +1922,7 @@ size_t split_bytes(const qg_gemm_problem* probs, int count) {
     int C, nmax;
     int64_t wgs;
     if (plan(probs, count, a, cfg, C, wgs, nmax, true) || !cfg.split) return 0;
-    qg::clear_error();
-    const int cus = qg::check_device() == QG_OK ? qg::device_cus() : 256;
-    qg::clear_error();
+    const int cus = plan_cus();
     size_t need = 0;
     bool slice = false;
     split_plan(a, cus, C, nmax, cfg.slice, nullptr, &need, &slice);
@@ -1905,10 +1947,15 @@ qg_status run(const qg_gemm_problem* probs, int count, hipStream_t stream, void*
             return qg::fail(QG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
         if (need > 0 && !qg::aligned16(ws)) return qg::fail(QG_ERR_ALIGN, "workspace not 16-byte aligned");
         if (slice)
-            launch_slice_any(a, (int)grid, stream);
+            launch_slice_any(a, (int)grid, kSlTiles, stream);
         else
             launch_walk_any(walk_shape(C, nmax, true), a, (int)grid, nmax, stream);
         return qg::launch_status("qgemm_q4k_smalln_batch_ws");
+    }
+    if (cfg.slice1) {
+        const int64_t grid = slice1_grid(a);
+        launch_slice_any(a, (int)grid, kSl1Tiles, stream);
+        return qg::launch_status("qgemm_q4k_smalln");
     }
     if (cfg.dot) return qg::smalln_dot_launch(probs, count, stream);
     if (cfg.lds) {

@@ -33,7 +33,8 @@ pytestmark = pytest.mark.gpu
 
 FORMS = {"auto": qg.FORM_AUTO, "regs": qg.FORM_SMALLN_REGS, "lds": qg.FORM_SMALLN_LDS,
          "lds1": qg.FORM_SMALLN_LDS1, "dot": qg.FORM_SMALLN_DOT, "stream": qg.FORM_SMALLN_STREAM,
-         "walk": qg.FORM_SMALLN_WALK, "split": qg.FORM_SMALLN_SPLIT, "slice": qg.FORM_SMALLN_SLICE}
+         "walk": qg.FORM_SMALLN_WALK, "split": qg.FORM_SMALLN_SPLIT, "slice": qg.FORM_SMALLN_SLICE,
+         "slice1": qg.FORM_SMALLN_SLICE}  # slice1: the slice form without a workspace (no K slices)
 
 
 @functools.lru_cache(maxsize=None)
@@ -118,7 +119,8 @@ SMALLN_CASES = [("auto", N) for N in (1, 2, 3, 4, 5, 8, 9, 16, 17, 32)] + \
                [("regs", N) for N in (5, 17, 32)] + [("lds", N) for N in (5, 17, 32)] + \
                [("lds1", N) for N in (5, 8)] + [("dot", N) for N in (1, 5, 8)] + \
                [("stream", N) for N in (1, 5, 8)] + [("walk", N) for N in (1, 5, 16, 17, 32)] + \
-               [("split", N) for N in (1, 5, 17, 32)] + [("slice", N) for N in (1, 4, 5, 8, 16)]
+               [("split", N) for N in (1, 5, 17, 32)] + [("slice", N) for N in (1, 4, 5, 8, 16)] + \
+               [("slice1", N) for N in (1, 5, 8, 16)]
 
 
 @pytest.mark.parametrize("form,N", SMALLN_CASES)
@@ -142,7 +144,7 @@ def test_smalln_exact(form, N, M, K):
 
 @pytest.mark.parametrize("form,N", [("auto", 5), ("auto", 32), ("regs", 5), ("regs", 32), ("lds", 5),
                                     ("lds", 32), ("lds1", 5), ("dot", 5), ("stream", 5),
-                                    ("walk", 5), ("walk", 32)])
+                                    ("walk", 5), ("walk", 32), ("slice1", 5)])
 def test_smalln_zero_scales_exact_zero_random_x(form, N):
     # d = dmin = 0 in every block: exactly 0 whatever the activations
     M, K = 100, 3584
