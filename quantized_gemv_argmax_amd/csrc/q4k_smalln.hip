@@ -841,6 +841,11 @@ QG_DEV uint32_t st_mul16(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(qg_u16x2, a) * __builtin_bit_cast(qg_u16x2, b));
 }
 
+// The top nibble of each 16-bit half (a packed 16-bit shift: no mask needed).
+QG_DEV uint32_t st_hi4(uint32_t a) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(qg_u16x2, a) >> qg_u16x2{12, 12});
+}
+
 QG_DEV void st_dot2(qg_f4& acc, qg_f4& accm, const SwItem<1>& it, const unsigned char* lds, uint32_t a, uint32_t xt,
                     uint32_t sh) {
     const uint4 hd = it.hdr[0];
@@ -873,8 +878,8 @@ QG_DEV void st_dot2(qg_f4& acc, qg_f4& accm, const SwItem<1>& it, const unsigned
             qg_h8, make_uint4(st_mul16(w0 & M, s_lo), st_mul16((w0 >> 8) & M, s_lo), st_mul16(w1 & M, s_lo),
                               st_mul16((w1 >> 8) & M, s_lo)));
         const qg_h8 b_hi = __builtin_bit_cast(
-            qg_h8, make_uint4(st_mul16((w0 >> 4) & M, s_hi), st_mul16((w0 >> 12) & M, s_hi),
-                              st_mul16((w1 >> 4) & M, s_hi), st_mul16((w1 >> 12) & M, s_hi)));
+            qg_h8, make_uint4(st_mul16((w0 >> 4) & M, s_hi), st_mul16(st_hi4(w0), s_hi),
+                              st_mul16((w1 >> 4) & M, s_hi), st_mul16(st_hi4(w1), s_hi)));
         p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, p, 0, 0, 0);
         p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, p, 0, 0, 0);
     }
@@ -1110,8 +1115,8 @@ QG_DEV void wk_dot(qg_f4 (&acc)[C], const SwItem<1>& it, const unsigned char* bu
             qg_h8, make_uint4(st_mul16(w0 & M, s_lo), st_mul16((w0 >> 8) & M, s_lo), st_mul16(w1 & M, s_lo),
                               st_mul16((w1 >> 8) & M, s_lo)));
         const qg_h8 b_hi = __builtin_bit_cast(
-            qg_h8, make_uint4(st_mul16((w0 >> 4) & M, s_hi), st_mul16((w0 >> 12) & M, s_hi),
-                              st_mul16((w1 >> 4) & M, s_hi), st_mul16((w1 >> 12) & M, s_hi)));
+            qg_h8, make_uint4(st_mul16((w0 >> 4) & M, s_hi), st_mul16(st_hi4(w0), s_hi),
+                              st_mul16((w1 >> 4) & M, s_hi), st_mul16(st_hi4(w1), s_hi)));
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const qg_h8 a_lo = *reinterpret_cast<const qg_h8*>(buf + a[c] + 128 * g);
