@@ -834,7 +834,7 @@ QG_DEV void st_dot(qg_f4& acc, const SwItem<1>& it, const unsigned char* lds, ui
 //   - the min term sum_j (dmin m_j) X_j[n] is a 16 x 16 x 8 product in fp32, two
 //     v_mfma_f32_16x16x4_f32 with A = -X_j[n] from the workgroup's table (xt: byte
 //     address of this lane's entry, column l % 16, sub-block l / 16) and B = dmin m_j
-//     of this lane's row, accumulated across units in `accm`.
+//     of this lane's row, accumulated into the same running sum as the products.
 typedef unsigned short qg_u16x2 __attribute__((ext_vector_type(2)));
 
 QG_DEV uint32_t st_mul16(uint32_t a, uint32_t b) {
@@ -846,8 +846,7 @@ QG_DEV uint32_t st_hi4(uint32_t a) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(qg_u16x2, a) >> qg_u16x2{12, 12});
 }
 
-QG_DEV void st_dot2(qg_f4& acc, qg_f4& accm, const SwItem<1>& it, const unsigned char* lds, uint32_t a, uint32_t xt,
-                    uint32_t sh) {
+QG_DEV void st_dot2(qg_f4& acc, const SwItem<1>& it, const unsigned char* lds, uint32_t a, uint32_t xt, uint32_t sh) {
     const uint4 hd = it.hdr[0];
     const float dd = qg_half_lo(hd.x) * 16777216.0f;  // quants enter as q * 2^-24
     const float dm = qg_half_hi(hd.x);
@@ -859,8 +858,8 @@ QG_DEV void st_dot2(qg_f4& acc, qg_f4& accm, const SwItem<1>& it, const unsigned
     const float bm1 = dm * (float)((m47 >> sh) & 0xffu);
     const float xa0 = *reinterpret_cast<const float*>(lds + xt);
     const float xa1 = *reinterpret_cast<const float*>(lds + xt + 256);
-    accm = __builtin_amdgcn_mfma_f32_16x16x4f32(xa0, bm0, accm, 0, 0, 0);
-    accm = __builtin_amdgcn_mfma_f32_16x16x4f32(xa1, bm1, accm, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa0, bm0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa1, bm1, acc, 0, 0, 0);
 
     qg_f4 p = {0.f, 0.f, 0.f, 0.f};
     constexpr uint32_t M = 0x000f000fu;
@@ -967,16 +966,14 @@ __global__ __launch_bounds__(64 * W, 4) void q4k_smalln_stream_kernel(SnArgs a) 
     const uint32_t xtl = xsb + (uint32_t)(s * 16 + i) * 4;  // sub-block s of a super-block, column i
     const uint32_t msh = 8u * (uint32_t)s;
     qg_f4 cur[1][1] = {{qg_f4{0.f, 0.f, 0.f, 0.f}}};
-    qg_f4 curm = {0.f, 0.f, 0.f, 0.f};
     int ct = t_first, cb = b_first;  // unit being computed
     auto unit = [&](const SwItem<1>& it) {
-        st_dot2(cur[0][0], curm, it, lds, an + (uint32_t)(512 * cb), xtl + (uint32_t)(512 * cb), msh);
+        st_dot2(cur[0][0], it, lds, an + (uint32_t)(512 * cb), xtl + (uint32_t)(512 * cb), msh);
         const int pt = ct;
         advance(ct, cb);
         if (ct != pt) {  // the walk moves to the next tile: park this one's sum
-            if (lane < 32) park[(pt * W + wave) * 32 + lane] = cur[0][0] + curm;
+            if (lane < 32) park[(pt * W + wave) * 32 + lane] = cur[0][0];
             cur[0][0] = qg_f4{0.f, 0.f, 0.f, 0.f};
-            curm = qg_f4{0.f, 0.f, 0.f, 0.f};
         }
     };
 
