@@ -17,7 +17,8 @@ def test_graph_replays_match_eager():
     torch.cuda.set_device(0)
     ws = qg.Workspace(DEV, 8 << 20)
     # q/k/v stage of a 7B layer (grouped), LM head argmax, LM head top-k with a
-    # sampler, small-N verify (N=5 short and long K, N=32, N=2 and 3), int8-activation product
+    # sampler, small-N verify (N=5 short and long K, N=32, N=2 and 3, the slice form),
+    # int8-activation product
     stage = []
     for i, (M, K) in enumerate([(3584, 3584), (512, 3584), (512, 3584)]):
         W = workloads.q4k_blocks(M, K, key=(80, i))
@@ -60,6 +61,12 @@ def test_graph_replays_match_eager():
     Xg32 = to_dev(workloads.x_columns(Kg, 32, key=(88,)))
     Yg32 = torch.empty((32, Mg), device=DEV)
     wss = qg.Workspace(DEV, qg.qgemm_q4k_smalln_batch_workspace_bytes([(wd, Xd32, Yd32, Md, Kd)]))
+    # the slice form: K slices with a workspace (down projection, N=5; its counters
+    # too must come back to zero) and, without slices, the grouped q/k/v stage at N=5
+    Yd5 = torch.empty((5, Md), device=DEV)
+    wss5 = qg.Workspace(DEV, qg.qgemm_q4k_smalln_batch_workspace_bytes([(wd, Xd, Yd5, Md, Kd)]))
+    Xqkv = to_dev(workloads.x_columns(K5, 5, key=(89,)))
+    Yqkv = [torch.empty((5, p[3]), device=DEV) for p in stage]
 
     def work():
         qg.qgemv_q4k_batch(stage)
@@ -74,11 +81,13 @@ def test_graph_replays_match_eager():
         qg.qgemv_q4k_q8_1(stage[0][0], xq, M5, K5, y=y8)
         qg.qgemm_q4k_smalln_batch_ws([(wd, Xd32, Yd32, Md, Kd)], wss)
         qg.qgemm_q4k_smalln(wg, Xg32, Mg, Kg, Y=Yg32)
+        qg.qgemm_q4k_smalln_batch_ws([(wd, Xd, Yd5, Md, Kd)], wss5)
+        qg.qgemm_q4k_smalln_batch([(p[0], Xqkv, Y_, p[3], p[4]) for p, Y_ in zip(stage, Yqkv)])
 
     def snapshot():
         torch.cuda.synchronize()
         outs = [p[2] for p in stage] + [oi, ov, tk.index, tk.logit, tk.logprob, tk.lse, tk.token, lg, Y5, Yd, Y32, xq,
-                                        y8, Y2, Yd3, Yd32, Yg32]
+                                        y8, Y2, Yd3, Yd32, Yg32, Yd5] + Yqkv
         return [t.clone() for t in outs]
 
     case("graph capture: eager reference")
@@ -97,7 +106,7 @@ def test_graph_replays_match_eager():
         work()
     for rep in range(4):
         # scribble over the outputs, then replay and compare
-        for t in snapshot_targets(stage, oi, ov, tk, lg, Y5, Yd, Y32, xq, y8) + [Y2, Yd3, Yd32, Yg32]:
+        for t in snapshot_targets(stage, oi, ov, tk, lg, Y5, Yd, Y32, xq, y8) + [Y2, Yd3, Yd32, Yg32, Yd5] + Yqkv:
             t.zero_()
         case(f"graph replay {rep}")
         g.replay()
@@ -106,6 +115,7 @@ def test_graph_replays_match_eager():
             assert torch.equal(a, b), f"replay {rep}: output {k} differs from the eager result"
         assert int(ws.buf.count_nonzero()) == 0
         assert int(wss.buf[:256].count_nonzero()) == 0, "walk-form arrival counters not back to zero"
+        assert int(wss5.buf[:256].count_nonzero()) == 0, "slice-form arrival counters not back to zero"
         # eager work between replays on the same buffers
         qg.qgemv_q4k(stage[1][0], stage[1][1], stage[1][3], stage[1][4], y=stage[1][2])
         torch.cuda.synchronize()
