@@ -741,7 +741,7 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_lds1_kernel(SnArgs a) {
 // Streamed single-pass form, for the same shapes as the single-pass form when the
 // batch has more tiles than the chip holds workgroups: the grid is sized to the
 // resident workgroup slots, and workgroup j of a problem with G workgroups walks
-// tiles j, j + G, j + 2G, ... (at most kStTiles). The activations of the whole K
+// tiles j, j + G, j + 2G, ... (at most st_tiles(W)). The activations of the whole K
 // range go to LDS once per workgroup, as in the single-pass form; the W
 // wavefronts then take the (tile, super-block) units of the walk in turn, each
 // with the next unit's loads in flight while one is computed, so a CU's weight
@@ -753,12 +753,12 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_lds1_kernel(SnArgs a) {
 // products only reach output columns that are not stored), the sub-block sums of
 // the activations (K / 32 entries of 8 columns), then one parked sum per tile
 // slot and wavefront, for the 32 lanes that hold columns 0..7 (N <= 8).
-#ifndef QG_ST_WAVES
-#define QG_ST_WAVES 8
-#endif
-constexpr int kStWaves = QG_ST_WAVES;               // wavefronts per workgroup
-constexpr int kStPerCu = kStWaves >= 16 ? 1 : 2;    // resident workgroups per CU
-constexpr int kStTiles = kStWaves >= 16 ? 10 : 5;
+// Two shapes: W = 8 wavefronts, two workgroups per CU, at most 5 tiles each; and
+// for batches of many tiles W = 16, one workgroup per CU, at most 10 tiles, which
+// stages the activations once per CU instead of twice (7B gate/up, 2368 tiles:
+// N = 5 about 21.5 -> 20.7 us, N = 8 24 -> 22).
+constexpr int st_per_cu(int W) { return W >= 16 ? 1 : 2; }  // resident workgroups per CU
+constexpr int st_tiles(int W) { return W >= 16 ? 10 : 5; }  // most tiles per workgroup
 #ifndef QG_ST_RING
 #define QG_ST_RING 2
 #endif
@@ -897,7 +897,7 @@ __global__ __launch_bounds__(64 * W, 4) void q4k_smalln_stream_kernel(SnArgs a) 
     const SnProb P = a.p[k];
     const int j = wg - P.wg_begin;
     const int G = P.wgs;
-    const int nt = (P.tiles - j + G - 1) / G;  // tiles of this walk, 1..kStTiles
+    const int nt = (P.tiles - j + G - 1) / G;  // tiles of this walk, 1..st_tiles(W)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15, s = lane >> 4;
@@ -945,7 +945,7 @@ __global__ __launch_bounds__(64 * W, 4) void q4k_smalln_stream_kernel(SnArgs a) 
     }
 
     // parked sums start at zero (a wavefront may have no unit in some tile)
-    for (int o = tid; o < kStTiles * W * 32; o += 64 * W) park[o] = qg_f4{0.f, 0.f, 0.f, 0.f};
+    for (int o = tid; o < st_tiles(W) * W * 32; o += 64 * W) park[o] = qg_f4{0.f, 0.f, 0.f, 0.f};
     // fp16 activations, and the sums of each 32-element sub-block over the same
     // fp16 values (a quad of threads holds one sub-block of a column)
 #pragma unroll
@@ -1465,8 +1465,8 @@ SnProb make_sn(const void* w, const float* X, int64_t ldx, float* Y, int64_t ldy
 constexpr int64_t kStAutoTiles = 1024;
 
 // Dynamic LDS of the streamed form: nmax activation rows and the parked sums.
-size_t stream_lds_bytes(int nmax, int kmax) {
-    return (size_t)nmax * (kmax + 8) * 2 + 2 * (size_t)kmax + (size_t)kStTiles * kStWaves * 32 * 16;
+size_t stream_lds_bytes(int nmax, int kmax, int W) {
+    return (size_t)nmax * (kmax + 8) * 2 + 2 * (size_t)kmax + (size_t)st_tiles(W) * W * 32 * 16;
 }
 
 struct SnCfg {
@@ -1475,7 +1475,7 @@ struct SnCfg {
     int D;      // its weight-queue depth in chunks
     bool lds1;  // single-pass LDS kernel (short K, N <= 8)
     bool dot;   // vector-ALU dot-product kernel (N <= 8, q4k_smalln_dot.hip)
-    bool stream;  // streamed single-pass kernel (single-pass shapes, many tiles)
+    int stream;   // streamed single-pass kernel (single-pass shapes): its wavefronts per workgroup, or 0
     bool walk;    // chunked walk kernel (many tiles, up to 32 columns)
     bool split;   // groups of tiles and K slices (workspace), the last workgroup of a group adding them
     bool slice;   // ... in the slice kernel where it fits, else in the walk kernel
@@ -1565,12 +1565,15 @@ SnCfg choose_cfg(const SnArgs& a, int C, bool ws, int cus) {
         st = st && (int64_t)a.p[i].M * a.p[i].nb * 144 < (int64_t)INT32_MAX;
         kmax = std::max(kmax, a.p[i].nb * 256);
     }
-    const size_t st_lds = stream_lds_bytes(ncol, kmax);
-    // automatic choice: where the workgroups fit the CUs' LDS as planned, or where a
-    // batch of many tiles runs one workgroup per CU (N = 8 gate/up: 28.4 -> 23.4 us)
-    c.stream = st && ((form == QG_FORM_AUTO && (st_lds <= 160 * 1024 / kStPerCu ||
-                                                (tiles >= 1024 && st_lds <= 160 * 1024))) ||
-                      (form == QG_FORM_SMALLN_STREAM && st_lds <= 160 * 1024));
+    // automatic choice: the 16-wavefront shape for batches of many tiles, else the
+    // 8-wavefront shape where two workgroups fit a CU's LDS; forced, the 8-wavefront
+    // shape wherever its LDS fits
+    const size_t st8 = stream_lds_bytes(ncol, kmax, 8), st16 = stream_lds_bytes(ncol, kmax, 16);
+    if (st && form == QG_FORM_AUTO && tiles >= kStAutoTiles && st16 <= 160 * 1024)
+        c.stream = 16;
+    else if (st && ((form == QG_FORM_AUTO && st8 <= 160 * 1024 / st_per_cu(8)) ||
+                    (form == QG_FORM_SMALLN_STREAM && st8 <= 160 * 1024)))
+        c.stream = 8;
     if (c.stream) return c;
     c.lds1 = s1 && (form == QG_FORM_AUTO || form == QG_FORM_SMALLN_LDS1 || form == QG_FORM_SMALLN_STREAM);
     if (c.lds1) {
@@ -1646,21 +1649,22 @@ void launch_s1(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kS1Waves), lds, s, a);
 }
 
+template <int W>
 void launch_stream(const SnArgs& a, int grid, size_t lds, hipStream_t s) {
-    const auto kern = q4k_smalln_stream_kernel<kStWaves, QG_ST_RING>;
+    const auto kern = q4k_smalln_stream_kernel<W, QG_ST_RING>;
     static std::atomic<bool> attr[64];
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr[dev].load(std::memory_order_acquire)) {
         (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr[dev].store(true, std::memory_order_release);
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kStWaves), lds, s, a);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * W), lds, s, a);
 }
 
-// Workgroups per problem for the streamed form: the resident slots (two
-// workgroups per CU) shared in proportion to the tiles, at most kStTiles tiles
+// Workgroups per problem for the streamed form: the resident slots (per_cu
+// workgroups per CU) shared in proportion to the tiles, at most tmax tiles
 // per workgroup. Fills wg_begin, wgs and the compact begin array; returns the grid.
-int64_t stream_grid(SnArgs& a, int cus, int per_cu = kStPerCu, int tmax = kStTiles) {
+int64_t stream_grid(SnArgs& a, int cus, int per_cu, int tmax) {
     int64_t tiles = 0;
     for (int i = 0; i < a.count; ++i) tiles += a.p[i].tiles;
     const int64_t slots = per_cu * (int64_t)std::max(cus, 1);
@@ -1971,10 +1975,14 @@ qg_status run(const qg_gemm_problem* probs, int count, hipStream_t stream, void*
         return qg::launch_status("qgemm_q4k_smalln");
     }
     if (cfg.stream) {
-        const int64_t grid = stream_grid(a, qg::device_cus());
+        const int W = cfg.stream;
+        const int64_t grid = stream_grid(a, qg::device_cus(), st_per_cu(W), st_tiles(W));
         int kmax = 0;
         for (int i = 0; i < count; ++i) kmax = std::max(kmax, a.p[i].nb * 256);
-        launch_stream(a, (int)grid, stream_lds_bytes(nmax, kmax), stream);
+        if (W == 16)
+            launch_stream<16>(a, (int)grid, stream_lds_bytes(nmax, kmax, 16), stream);
+        else
+            launch_stream<8>(a, (int)grid, stream_lds_bytes(nmax, kmax, 8), stream);
         return qg::launch_status("qgemm_q4k_smalln");
     }
     if (cfg.lds1) {

@@ -142,6 +142,19 @@ def test_smalln_exact(form, N, M, K):
     check_exact(Y.cpu().numpy()[:, :M], W, M, K, X, f"{form} M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("N", [3, 5, 8])
+def test_smalln_exact_many_tiles(N):
+    # a batch of more than 1024 tiles on short K: the automatic choice takes the
+    # streamed form with one 16-wavefront workgroup per CU walking up to ten tiles
+    M, K = 16400, 768
+    W = exact_q4k_rows(M, K, seed=11)
+    X = exact_columns(K, N)
+    case(f"qgemm_q4k_smalln exact many tiles M={M} K={K} N={N}")
+    Y = qg.qgemm_q4k_smalln(packed_q4k(W, M, K), to_dev(X), M, K)
+    torch.cuda.synchronize()
+    check_exact(Y.cpu().numpy()[:, :M], W, M, K, X, f"many tiles N={N}")
+
+
 @pytest.mark.parametrize("form,N", [("auto", 5), ("auto", 32), ("regs", 5), ("regs", 32), ("lds", 5),
                                     ("lds", 32), ("lds1", 5), ("dot", 5), ("stream", 5),
                                     ("walk", 5), ("walk", 32), ("slice1", 5)])
