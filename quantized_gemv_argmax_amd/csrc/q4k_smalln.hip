@@ -1497,14 +1497,19 @@ SnCfg choose_cfg(const SnArgs& a, int C, bool ws, int cus) {
     SnCfg c{1, tiles > 256 ? 2 : 1, false, 2, false, false, false, false, false, false, false};
     if (C == 2 && tiles > 1024) c.TW = 4;
     // Form selection, from measurements on the 7B shapes (stage times in us, register
-    // form -> chosen form):
+    // form -> chosen form), in the order tested below:
+    //   - with a workspace, K slices for few tiles and long K or many columns: the
+    //     slice form where each slice's activations fit its staging, else the
+    //     K-sliced walk (reasons and times beside the rule below);
+    //   - the slice form without slices, two tiles per workgroup, for more tiles
+    //     than CUs but at most twice as many (q/k/v, 4 to 8 columns);
     //   - the vector-ALU dot-product form for up to four columns (196 decode
     //     matrices, ms per step against the matrix-core forms: N = 1 0.93 / 1.57,
     //     2 1.13 / 1.58, 3 1.29 / 1.63, 4 1.52 / 1.67, 5 1.83 / 1.74);
     //   - the single-pass LDS form for K <= 4096 and N <= 8 (N = 5: q/k/v 9.05 ->
     //     8.75, o 6.85 -> 6.44, gate/up 29.7 -> 26.6), in its streamed variant
-    //     where two workgroups fit a CU's LDS (N = 5: q/k/v 8.86 -> 8.49, o 6.36 ->
-    //     5.48, gate/up 27.2 -> 21.1; N = 8 gate/up 28.4 -> 23.4);
+    //     (N = 5: q/k/v 8.86 -> 8.49, o 6.36 -> 5.48, gate/up 27.2 -> 21.1; N = 8
+    //     gate/up 28.4 -> 23.4), with 16 wavefronts per workgroup from 1024 tiles;
     //   - the chunked LDS form for K >= 8192 (down projection: N = 5 23.6 -> 21.6,
     //     N = 32 72.3 -> 44.7) and for more than 16 columns over at most 1024 tiles
     //     (N = 32: q/k/v 18.2 -> 14.2, o 16.6 -> 12.0);
