@@ -444,7 +444,9 @@ qg_status lmhead_topk(const void* w_packed, const float* x, int64_t M, int64_t K
  *                 with a workspace only), or tile groups and K slices whose
  *                 activations are staged whole before the weights are walked (the
  *                 _ws entry point, up to 16 columns and N times the slice's
- *                 super-blocks at most 160; else as the previous value).
+ *                 super-blocks at most 160; else as the previous value; without
+ *                 a workspace, the same form with no K slices over groups of two
+ *                 tiles, where N times K / 256 is at most 160).
  *   smalln_waves  wavefronts per workgroup of the register-staged form: 1..8.
  *   smalln_tiles  16-row tiles per workgroup (matrix-core forms): 1, 2, 4.
  *   smalln_depth  weight-queue depth in chunks of the chunked-LDS form: 2..4.
