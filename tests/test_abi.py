@@ -39,8 +39,9 @@ def _declarations():
     return out
 
 
-# The boundary the survey's scope table fixes (names, return types and argument
-# counts); the library may export more.
+# The core boundary (names, return types and argument counts): the GEMV, small-N
+# and fused argmax calls of the decode and verification steps, the block packers
+# and size queries, and the error strings; the library may export more.
 SCOPE_BOUNDARY = {
     "qg_abi_version": ("int", 0),
     "qg_status_string": ("const char*", 1),
