@@ -910,17 +910,22 @@ __global__ __launch_bounds__(64 * W, 4) void q4k_smalln_stream_kernel(SnArgs a) 
     const __amdgpu_buffer_rsrc_t wr =
         __builtin_amdgcn_make_buffer_rsrc((void*)P.w, (short)0, P.M * nb * 144, kQgRawBufferFlags);
 
-    // activations: thread tid takes 8-element group tid of every column (K <= 512 W)
+    // activations: thread tid takes 8-element group tid of every column (K <= 512 W);
+    // wavefronts holding no group, and columns past N, issue no loads (the columns
+    // past N only reach output columns that are not stored)
     const int tid = threadIdx.x;
     const int gpr = K / 8;
+    const bool xw = 64 * wave < gpr;  // this wavefront holds activation groups
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)P.X, (short)0, (int)(((int64_t)(P.N - 1) * P.ldx + K) * 4), kQgRawBufferFlags);
     float4 v[kS1Cols][2];
 #pragma unroll
     for (int n = 0; n < kS1Cols; ++n) {
-        const uint32_t off = (n < P.N && tid < gpr) ? (uint32_t)(((int64_t)n * P.ldx + 8 * tid) * 4) : kOutOfRange;
-        v[n][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-        v[n][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 16, 0));
+        if (n < P.N && xw) {
+            const uint32_t off = tid < gpr ? (uint32_t)(((int64_t)n * P.ldx + 8 * tid) * 4) : kOutOfRange;
+            v[n][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+            v[n][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 16, 0));
+        }
     }
 
     // this wavefront's units: wave, wave + W, ... of the nt * nb units of the walk;
@@ -945,17 +950,20 @@ __global__ __launch_bounds__(64 * W, 4) void q4k_smalln_stream_kernel(SnArgs a) 
         advance(lt, lb);
     }
 
-    // parked sums start at zero (a wavefront may have no unit in some tile)
-    for (int o = tid; o < st_tiles(W) * W * 32; o += 64 * W) park[o] = qg_f4{0.f, 0.f, 0.f, 0.f};
     // fp16 activations, and the sums of each 32-element sub-block over the same
-    // fp16 values (a quad of threads holds one sub-block of a column)
+    // fp16 values (a quad of threads holds one sub-block of a column); the table's
+    // columns past N are zeros
 #pragma unroll
     for (int n = 0; n < kS1Cols; ++n) {
-        const qg_h8 h = qg_a_operand(v[n][0], v[n][1]);
-        if (n < P.N && tid < gpr) *reinterpret_cast<qg_h8*>(lds + n * RB + 16 * tid) = h;
-        const uint4 hw = __builtin_bit_cast(uint4, h);
-        const float xsum = qg_quad_sum(qg_sum_pairs4(hw.x, hw.y, hw.z, hw.w));
-        if ((tid & 3) == 0 && tid < gpr) *reinterpret_cast<float*>(lds + xsb + ((tid >> 2) * 16 + n) * 4) = -xsum;
+        if (n < P.N && xw) {
+            const qg_h8 h = qg_a_operand(v[n][0], v[n][1]);
+            if (tid < gpr) *reinterpret_cast<qg_h8*>(lds + n * RB + 16 * tid) = h;
+            const uint4 hw = __builtin_bit_cast(uint4, h);
+            const float xsum = qg_quad_sum(qg_sum_pairs4(hw.x, hw.y, hw.z, hw.w));
+            if ((tid & 3) == 0 && tid < gpr) *reinterpret_cast<float*>(lds + xsb + ((tid >> 2) * 16 + n) * 4) = -xsum;
+        } else if ((tid & 3) == 0 && tid < gpr) {
+            *reinterpret_cast<float*>(lds + xsb + ((tid >> 2) * 16 + n) * 4) = 0.f;
+        }
     }
     if ((tid & 3) == 0 && tid < gpr) {  // columns 8..15 of the table: zeros
         *reinterpret_cast<uint4*>(lds + xsb + ((tid >> 2) * 16 + 8) * 4) = make_uint4(0u, 0u, 0u, 0u);
@@ -998,9 +1006,14 @@ __global__ __launch_bounds__(64 * W, 4) void q4k_smalln_stream_kernel(SnArgs a) 
     const int t = j + wave * G;
     const int rt = min(T, P.M - t * T);
     if (lane >= 32) return;
-    qg_f4 sum = park[(wave * W) * 32 + lane];
+    // only wavefronts with a unit in this tile slot parked a sum for it: wavefront w
+    // takes units w, w + W, ..., so it has one of the slot's units wave nb ..
+    // wave nb + nb - 1 when nb >= W or when (w - wave nb) mod W < nb
+    const int r0 = (wave * nb) % W;
+    qg_f4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 1; w < W; ++w) sum += park[(wave * W + w) * 32 + lane];
+    for (int w = 0; w < W; ++w)
+        if (nb >= W || (w - r0 + W) % W < nb) sum += park[(wave * W + w) * 32 + lane];
     if (i < rt) {
         const int row = t * T + i;
 #pragma unroll
