@@ -323,7 +323,7 @@ struct SwGeom {
 template <int TW>
 struct SwItem {
     uint4 hdr[TW];   // d, dmin, 12 scale bytes of this lane's row
-    uint2 q[TW][4];  // quant bytes 8 (l / 16)..+7 of units g = 0..3 (sub-blocks 2g, 2g + 1)
+    uint2 q[TW][4];  // quant words: sw_load's layout (bytes 8 (l / 16)..+7 of groups 0..3), or st_load's
 };
 
 template <int C, int TW>
@@ -764,74 +764,55 @@ constexpr int st_tiles(int W) { return W >= 16 ? 10 : 5; }  // most tiles per wo
 #define QG_ST_RING 2
 #endif
 
-// Loads of unit (tile t, super-block b); valid false: offsets past the resource,
-// zeros without a memory access (so every load is still issued and the wait
-// counts stay exact). The caller passes a tile inside the matrix either way.
+// Loads of unit (tile t, super-block b) for the streamed, walk and slice forms;
+// valid false: offsets past the resource, zeros without a memory access (so every
+// load is still issued and the wait counts stay exact). The caller passes a tile
+// inside the matrix either way. Lane (i, s) takes quant segments 1 + s and 5 + s
+// of row i whole (two 16-byte loads instead of four 8-byte ones: the CU issues
+// fewer load instructions per unit), so its words q[g], g = 2h + c, hold quant
+// bytes 8c..8c+7 of segment 1 + s + 4h: weights 16 (s % 2) + 8c .. + 7 of group
+// 2h + s / 2, low nibbles in sub-block 2 (2h + s / 2), high ones in the next.
+// The products take the matching activations (st_alane) and scales (st_scale_sel).
 QG_DEV void st_load(SwItem<1>& it, __amdgpu_buffer_rsrc_t wr, const SnProb& P, int t, int b, int i, int s,
                     bool valid) {
     const int rt = min(T, P.M - t * T);
     const uint32_t r = (uint32_t)min(i, rt - 1);
     const uint32_t vh = valid ? 16u * r : kOutOfRange;
-    const uint32_t vq = valid ? 16u * r + 8u * (uint32_t)(s & 1) + (uint32_t)(s >> 1) * 16u * (uint32_t)rt : kOutOfRange;
+    const uint32_t vq = valid ? 16u * r + (uint32_t)s * 16u * (uint32_t)rt : kOutOfRange;
     const int so = valid ? t * T * P.nb * 144 + b * 9 * 16 * rt : 0;
     const qg_u4v h = __builtin_amdgcn_raw_buffer_load_b128(wr, vh, so, kNonTemporal);
     it.hdr[0] = make_uint4(h.x, h.y, h.z, h.w);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const qg_u2v q = __builtin_amdgcn_raw_buffer_load_b64(wr, vq, so + (1 + 2 * g) * 16 * rt, kNonTemporal);
-        it.q[0][g] = make_uint2(q.x, q.y);
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const qg_u4v q = __builtin_amdgcn_raw_buffer_load_b128(wr, vq, so + (1 + 4 * h2) * 16 * rt, kNonTemporal);
+        it.q[0][2 * h2] = make_uint2(q.x, q.y);
+        it.q[0][2 * h2 + 1] = make_uint2(q.z, q.w);
     }
 }
 
-// One super-block of one tile for the streamed form: as sw_dot, but the
-// sub-block sums X_j of the activations come from the table the workgroup built
-// once while staging them (xs: byte address of this lane's entry for sub-block 0
-// of the super-block), instead of a matrix-core product per sub-block.
-QG_DEV void st_dot(qg_f4& acc, const SwItem<1>& it, const unsigned char* lds, uint32_t a, uint32_t xs) {
-    const qg_f4 zero = {0.f, 0.f, 0.f, 0.f};
-    const uint4 hd = it.hdr[0];
-    const float dd = qg_half_lo(hd.x) * 16777216.0f;  // quants enter as q * 2^-24
-    const float dm = qg_half_hi(hd.x);
-    const uint32_t sc03 = hd.y & 0x3f3f3f3fu, m03 = hd.z & 0x3f3f3f3fu;
-    const uint32_t sc47 = (hd.w & 0x0f0f0f0fu) | ((hd.y >> 2) & 0x30303030u);
-    const uint32_t m47 = ((hd.w >> 4) & 0x0f0f0f0fu) | ((hd.z >> 2) & 0x30303030u);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const qg_h8 a_lo = *reinterpret_cast<const qg_h8*>(lds + a + 128 * g);
-        const qg_h8 a_hi = *reinterpret_cast<const qg_h8*>(lds + a + 128 * g + 64);
-        const qg_f4 x_lo = *reinterpret_cast<const qg_f4*>(lds + xs + 64 * g);
-        const qg_f4 x_hi = *reinterpret_cast<const qg_f4*>(lds + xs + 64 * g + 32);
-        const uint32_t scw = g < 2 ? sc03 : sc47;
-        const uint32_t mw = g < 2 ? m03 : m47;
-        const int kb = 2 * (g & 1);
-        const float s_lo = dd * qg_byte_f(scw, kb);
-        const float s_hi = dd * 0.0625f * qg_byte_f(scw, kb + 1);
-        const float m_lo = dm * qg_byte_f(mw, kb);
-        const float m_hi = dm * qg_byte_f(mw, kb + 1);
-        const uint32_t w0 = it.q[0][g].x, w1 = it.q[0][g].y;
-        const uint32_t w0s = w0 >> 8, w1s = w1 >> 8;
-        const qg_h8 b_lo = __builtin_bit_cast(
-            qg_h8, make_uint4(w0 & 0x000f000fu, w0s & 0x000f000fu, w1 & 0x000f000fu, w1s & 0x000f000fu));
-        const qg_h8 b_hi = __builtin_bit_cast(
-            qg_h8, make_uint4(w0 & 0x00f000f0u, w0s & 0x00f000f0u, w1 & 0x00f000f0u, w1s & 0x00f000f0u));
-        const qg_f4 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, zero, 0, 0, 0);
-        const qg_f4 s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, zero, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float v = acc[e];
-            v = fmaf(s_lo, s0[e], v);
-            v = fmaf(s_hi, s1[e], v);
-            v = fmaf(-m_lo, x_lo[e], v);
-            v = fmaf(-m_hi, x_hi[e], v);
-            acc[e] = v;
-        }
-    }
+// LDS offset of lane (., s)'s activations within a super-block of an fp16
+// activation row, for the words st_load gives it: the staged row holds, per
+// group g of 64 weights (128 bytes), the 32 low-nibble weights and then the 32
+// high-nibble ones, 8 per 16 bytes in the order the quant words unpack; word
+// q[2h + c] of lane s is group 2h + s / 2, eight-weight chunk 2 (s % 2) + c,
+// at 256 h + 16 c past this offset (+64 for the high nibbles).
+QG_DEV uint32_t st_alane(int s) { return 128u * (uint32_t)(s >> 1) + 32u * (uint32_t)(s & 1); }
+
+// v_perm selectors putting this lane's low- and high-nibble sub-block scales
+// (bytes 2 (s / 2) and 2 (s / 2) + 1 of sc03 for words q[0], q[1], of sc47 for
+// q[2], q[3]) into both 16-bit halves; sh = 8 s.
+QG_DEV uint32_t st_scale_sel(uint32_t sh) {
+    const uint32_t kb = (sh >> 3) & 2u;
+    return 0x0c000c00u | (kb << 16) | kb;
 }
 
-// The same super-block with the sub-block scales inside the matrix-core operands:
+// One super-block of one tile for the streamed form (a: this lane's activations in
+// the super-block's LDS row, st_alane), with the sub-block scales inside the
+// matrix-core operands:
 //   - B carries q * sc_j instead of q (at most 15 * 63 = 945, still an exact fp16
 //     subnormal, one packed 16-bit multiply per dword), so the eight products of
-//     the super-block accumulate in the matrix core and d is applied once;
+//     the super-block accumulate in the matrix core and d is applied once; each
+//     lane scales its own sub-block, so one product may span two sub-blocks;
 //   - the min term sum_j (dmin m_j) X_j[n] is a 16 x 16 x 8 product in fp32, two
 //     v_mfma_f32_16x16x4_f32 with A = -X_j[n] from the workgroup's table (xt: byte
 //     address of this lane's entry, column l % 16, sub-block l / 16) and B = dmin m_j
@@ -864,15 +845,16 @@ QG_DEV void st_dot2(qg_f4& acc, const SwItem<1>& it, const unsigned char* lds, u
 
     qg_f4 p = {0.f, 0.f, 0.f, 0.f};
     constexpr uint32_t M = 0x000f000fu;
+    const uint32_t sel = st_scale_sel(sh);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        const qg_h8 a_lo = *reinterpret_cast<const qg_h8*>(lds + a + 128 * g);
-        const qg_h8 a_hi = *reinterpret_cast<const qg_h8*>(lds + a + 128 * g + 64);
+        const uint32_t ao = 256u * (uint32_t)(g >> 1) + 16u * (uint32_t)(g & 1);
+        const qg_h8 a_lo = *reinterpret_cast<const qg_h8*>(lds + a + ao);
+        const qg_h8 a_hi = *reinterpret_cast<const qg_h8*>(lds + a + ao + 64);
         const uint32_t scw = g < 2 ? sc03 : sc47;
-        const uint32_t kb = 2 * (g & 1);
-        // sc_j in both 16-bit halves
-        const uint32_t s_lo = __builtin_amdgcn_perm(0u, scw, 0x0c000c00u | (kb << 16) | kb);
-        const uint32_t s_hi = __builtin_amdgcn_perm(0u, scw, 0x0c000c00u | ((kb + 1) << 16) | (kb + 1));
+        // this lane's sub-block scales in both 16-bit halves
+        const uint32_t s_lo = __builtin_amdgcn_perm(0u, scw, sel);
+        const uint32_t s_hi = __builtin_amdgcn_perm(0u, scw, sel + 0x00010001u);
         const uint32_t w0 = it.q[0][g].x, w1 = it.q[0][g].y;
         const qg_h8 b_lo = __builtin_bit_cast(
             qg_h8, make_uint4(st_mul16(w0 & M, s_lo), st_mul16((w0 >> 8) & M, s_lo), st_mul16(w1 & M, s_lo),
@@ -971,7 +953,7 @@ __global__ __launch_bounds__(64 * W, 4) void q4k_smalln_stream_kernel(SnArgs a) 
     }
     sw_barrier();
 
-    const uint32_t an = (uint32_t)((i < P.N ? i : 0) * RB + 16 * s);
+    const uint32_t an = (uint32_t)((i < P.N ? i : 0) * RB) + st_alane(s);
     const uint32_t xtl = xsb + (uint32_t)(s * 16 + i) * 4;  // sub-block s of a super-block, column i
     const uint32_t msh = 8u * (uint32_t)s;
     qg_f4 cur[1][1] = {{qg_f4{0.f, 0.f, 0.f, 0.f}}};
@@ -1090,9 +1072,10 @@ QG_DEV void wk_write(const float4 (&v)[2][2], unsigned char* buf, const SnProb& 
     }
 }
 
-// One super-block of one tile for C column blocks (a[c]: LDS byte address of this
-// lane's A operand for sub-block 0; xt: this lane's table entry, sub-block l / 16
-// of the super-block, column l % 16 of block 0).
+// One super-block of one tile for C column blocks, products as in st_dot2 (a[c]:
+// LDS byte address of this lane's activations in the super-block of column block
+// c, st_alane; xt: this lane's table entry, sub-block l / 16 of the super-block,
+// column l % 16 of block 0).
 template <int C>
 QG_DEV void wk_dot(qg_f4 (&acc)[C], const SwItem<1>& it, const unsigned char* buf, const uint32_t (&a)[C],
                    uint32_t xt, uint32_t sh) {
@@ -1115,12 +1098,13 @@ QG_DEV void wk_dot(qg_f4 (&acc)[C], const SwItem<1>& it, const unsigned char* bu
 #pragma unroll
     for (int c = 0; c < C; ++c) p[c] = qg_f4{0.f, 0.f, 0.f, 0.f};
     constexpr uint32_t M = 0x000f000fu;
+    const uint32_t sel = st_scale_sel(sh);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
+        const uint32_t ao = 256u * (uint32_t)(g >> 1) + 16u * (uint32_t)(g & 1);
         const uint32_t scw = g < 2 ? sc03 : sc47;
-        const uint32_t kb = 2 * (g & 1);
-        const uint32_t s_lo = __builtin_amdgcn_perm(0u, scw, 0x0c000c00u | (kb << 16) | kb);
-        const uint32_t s_hi = __builtin_amdgcn_perm(0u, scw, 0x0c000c00u | ((kb + 1) << 16) | (kb + 1));
+        const uint32_t s_lo = __builtin_amdgcn_perm(0u, scw, sel);
+        const uint32_t s_hi = __builtin_amdgcn_perm(0u, scw, sel + 0x00010001u);
         const uint32_t w0 = it.q[0][g].x, w1 = it.q[0][g].y;
         const qg_h8 b_lo = __builtin_bit_cast(
             qg_h8, make_uint4(st_mul16(w0 & M, s_lo), st_mul16((w0 >> 8) & M, s_lo), st_mul16(w1 & M, s_lo),
@@ -1130,8 +1114,8 @@ QG_DEV void wk_dot(qg_f4 (&acc)[C], const SwItem<1>& it, const unsigned char* bu
                               st_mul16((w1 >> 4) & M, s_hi), st_mul16(st_hi4(w1), s_hi)));
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const qg_h8 a_lo = *reinterpret_cast<const qg_h8*>(buf + a[c] + 128 * g);
-            const qg_h8 a_hi = *reinterpret_cast<const qg_h8*>(buf + a[c] + 128 * g + 64);
+            const qg_h8 a_lo = *reinterpret_cast<const qg_h8*>(buf + a[c] + ao);
+            const qg_h8 a_hi = *reinterpret_cast<const qg_h8*>(buf + a[c] + ao + 64);
             p[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, p[c], 0, 0, 0);
             p[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, p[c], 0, 0, 0);
         }
@@ -1290,7 +1274,7 @@ __global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_walk_kernel(SnArg
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int n = 16 * c + i;
-        an[c] = (uint32_t)((n < P.N ? n : 0) * RB + 16 * s + 512 * sb);
+        an[c] = (uint32_t)((n < P.N ? n : 0) * RB + 512 * sb) + st_alane(s);
     }
     const uint32_t xt = (uint32_t)(P.N * RB) + (uint32_t)(((sb * 8 + s) * 16 * C + i) * 4);
     const uint32_t sh = 8u * (uint32_t)s;
@@ -1397,7 +1381,7 @@ __global__ __launch_bounds__(64 * kWkWaves, 4) void q4k_smalln_slice_kernel(SnAr
     for (int r = 0; r + 1 < R; ++r)
         st_load(ring[r], wr, P, t, min(kb0 + s0 + SS * r, nb - 1), i, s, r < nu);
 
-    const uint32_t an0 = (uint32_t)((i < P.N ? i : 0) * RB + 16 * s);
+    const uint32_t an0 = (uint32_t)((i < P.N ? i : 0) * RB) + st_alane(s);
     const uint32_t xt0 = XT + (uint32_t)(s * 16 + i) * 4;
     const uint32_t sh = 8u * (uint32_t)s;
     qg_f4 acc[1] = {qg_f4{0.f, 0.f, 0.f, 0.f}};
