@@ -1198,22 +1198,37 @@ QG_DEV void wk_finish(qg_f4 (&sum)[C], unsigned char* lds, const SnProb& P, int 
         }
         __syncthreads();
         if (!*last || wave >= nt) return;
-        // per column block, all slices' loads in flight at once, then added in
-        // slice order
+        // rounds of LS slices, the loads of every column block of a round in flight
+        // at once (one memory round trip for up to LS slices), each column's sums
+        // added in slice order
+        constexpr int LS = kSpMaxSlices / C;
+        qg_f4 v[C];
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            qg_u4v pv[kSpMaxSlices];
+        for (int q = 0; q < C; ++q) {
+            if (q * LS >= P.slices) break;
+            qg_u4v pv[C][LS];
 #pragma unroll
-            for (int h2 = 0; h2 < kSpMaxSlices; ++h2)
-                pv[h2] = __builtin_amdgcn_raw_buffer_load_b128(
-                    pr, h2 < P.slices && 16 * c + 4 * s < P.N ? (uint32_t)lane * 16u : kOutOfRange,
-                    h2 < P.slices ? ((h2 * P.tiles + t) * C + c) * 1024 : 0, kCoherent);
-            qg_f4 v = __builtin_bit_cast(qg_f4, pv[0]);
+            for (int c = 0; c < C; ++c)
 #pragma unroll
-            for (int h2 = 1; h2 < kSpMaxSlices; ++h2)
-                if (h2 < P.slices) v += __builtin_bit_cast(qg_f4, pv[h2]);
-            sum[c] = v;
+                for (int r = 0; r < LS; ++r) {
+                    const int h2 = q * LS + r;
+                    pv[c][r] = __builtin_amdgcn_raw_buffer_load_b128(
+                        pr, h2 < P.slices && 16 * c + 4 * s < P.N ? (uint32_t)lane * 16u : kOutOfRange,
+                        h2 < P.slices ? ((h2 * P.tiles + t) * C + c) * 1024 : 0, kCoherent);
+                }
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int r = 0; r < LS; ++r) {
+                    const int h2 = q * LS + r;
+                    if (h2 == 0)
+                        v[c] = __builtin_bit_cast(qg_f4, pv[c][0]);
+                    else if (h2 < P.slices)
+                        v[c] += __builtin_bit_cast(qg_f4, pv[c][r]);
+                }
         }
+#pragma unroll
+        for (int c = 0; c < C; ++c) sum[c] = v[c];
     }
     if (wave >= nt) return;
 #pragma unroll
