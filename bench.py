@@ -66,6 +66,33 @@ def graph_ms(torch, fn, reps: int, warm: int = 2) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+def graph_stats(torch, fn, reps: int, warm: int = 2):
+    """As graph_ms, with an event before every replay: (mean, median, best, cv) of the
+    per-replay times in ms; the mean is the timed region over its replays."""
+    import numpy as np
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    for k in range(reps):
+        evs[k].record()
+        g.replay()
+    evs[-1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(reps)])
+    mean = evs[0].elapsed_time(evs[-1]) / reps
+    return mean, float(np.median(per)), float(per.min()), float(per.std() / per.mean())
+
+
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "q4k_gemv_7b_decode_step_traffic.md")
 TRAFFIC_SOURCES = ("quantized_gemv_argmax_amd/csrc/q4k_gemv.hip", "quantized_gemv_argmax_amd/csrc/qg_device.h")
 
@@ -511,7 +538,7 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
             for grp in sts:
                 qg.qgemm_q4k_smalln_batch_ws(grp, sws)
 
-        ms = graph_ms(torch, vstep, 5)
+        ms, ms_med, ms_best, ms_cv = graph_stats(torch, vstep, 20)
         flat = [m for grp in sstages for m in grp]
         wb = sum(m[0].numel() for m in flat)
         b = wb + sum(4 * N * (m[3] + m[4]) for m in flat)
@@ -521,7 +548,9 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
             nb_ = sum(m[0].numel() + 4 * N * (m[3] + m[4]) for m in sts[0])
             us = graph_ms(torch, lambda sts=sts: vstep(sts), 5) * 1e3 / len(sts)
             per_stage[name] = {"avg_us": round(us, 3), "GBps": round(nb_ / (us * 1e-6) / 1e9, 1)}
-        rows[f"smalln_verify_N{N}"] = {"ms_per_step": round(ms, 4), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+        rows[f"smalln_verify_N{N}"] = {"ms_per_step": round(ms, 4), "ms_per_step_median": round(ms_med, 4),
+                                       "ms_per_step_best": round(ms_best, 4), "ms_per_step_cv": round(ms_cv, 4),
+                                       "replays": 20, "GBps": round(b / (ms * 1e-3) / 1e9, 1),
                                        "bytes": int(b), "verified_tokens_per_s": round(N * 1e3 / ms, 1),
                                        "launches_per_step": len(sstages),
                                        "entry_point": "qgemm_q4k_smalln_batch_ws",
@@ -554,8 +583,8 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
                 qg.quantize_q8_1_columns(Xs, out=xq)
             qg.qgemm_q4k_q8_1_smalln_batch(grp)
 
-    ms = graph_ms(torch, ivstep, 5)
-    ms_noq = graph_ms(torch, lambda: ivstep(quantize=False), 5)
+    ms, ms_med, ms_best, ms_cv = graph_stats(torch, ivstep, 20)
+    ms_noq = graph_ms(torch, lambda: ivstep(quantize=False), 20)
     b = sum(Xs.numel() * 4 + 2 * xq.numel() + sum(m[0].numel() + 4 * N * m[3] for m in grp) for Xs, xq, grp in qv)
     per_stage = {}
     for k, name in enumerate(["qkv", "o", "gate_up", "down"]):
@@ -565,7 +594,8 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
         us = graph_ms(torch, lambda sts=sts: ivstep(sts), 5) * 1e3 / len(sts)
         per_stage[name] = {"avg_us": round(us, 3), "GBps": round(nb_ / (us * 1e-6) / 1e9, 1)}
     rows["smalln_verify_N5_int8_activations"] = {
-        "ms_per_step": round(ms, 4), "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": int(b),
+        "ms_per_step": round(ms, 4), "ms_per_step_median": round(ms_med, 4), "ms_per_step_best": round(ms_best, 4),
+        "ms_per_step_cv": round(ms_cv, 4), "replays": 20, "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": int(b),
         "verified_tokens_per_s": round(N * 1e3 / ms, 1), "launches_per_step": 2 * len(qv), "per_stage": per_stage,
         "quantization": "timed (one launch per stage for all its columns)",
         "ms_per_step_without_quantization": round(ms_noq, 4)}
