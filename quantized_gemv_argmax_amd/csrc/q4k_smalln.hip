@@ -751,9 +751,10 @@ __global__ __launch_bounds__(64 * W) void q4k_smalln_lds1_kernel(SnArgs a) {
 // registers and parks the sum in LDS when its walk moves to the next tile; the
 // parked sums of the W wavefronts meet once, at the end, in a fixed order.
 // LDS: the N activation rows (lanes of columns past N read column 0: their
-// products only reach output columns that are not stored), the sub-block sums of
-// the activations (K / 32 entries of 8 columns), then one parked sum per tile
-// slot and wavefront, for the 32 lanes that hold columns 0..7 (N <= 8).
+// products only reach output columns that are not stored), the negated sub-block
+// sums of the activations (K / 32 entries of 16 columns, those past N zero), then
+// one parked sum per tile slot and wavefront, for the 32 lanes that hold columns
+// 0..7 (N <= 8); a tile adds the parks of the wavefronts that had one of its units.
 // Two shapes: W = 8 wavefronts, two workgroups per CU, at most 5 tiles each; and
 // for batches of many tiles W = 16, one workgroup per CU, at most 10 tiles, which
 // stages the activations once per CU instead of twice (7B gate/up, 2368 tiles:
