@@ -286,11 +286,12 @@ qg_status qgemm_q4k_smalln_batch(const qg_gemm_problem* problems /* host */, int
  * qgemm_q4k_smalln_batch (with another rounding order). _workspace_bytes gives
  * the bytes the batch needs on the current device (0: none; invalid problems:
  * 0). The workspace (16-byte aligned, at least that size) must be zero-filled
- * before its first use (qg_workspace_clear); every call leaves its counters zero
- * and the rest of it with undefined contents, so a buffer shared with the LM-head
- * calls (whose workspaces must stay all-zero) has to be cleared again before they
- * use it. A smaller or NULL workspace where one is needed: QG_ERR_WORKSPACE.
- * Calls that share a workspace must not overlap.
+ * before its first use (qg_workspace_clear); the counters sit in a fixed block at
+ * its start that every call leaves zero, and the rest of it is left with undefined
+ * contents, so one workspace serves calls of any shapes, but a buffer shared with
+ * the LM-head calls (whose workspaces must stay all-zero) has to be cleared again
+ * before they use it. A smaller or NULL workspace where one is needed:
+ * QG_ERR_WORKSPACE. Calls that share a workspace must not overlap.
  */
 size_t qgemm_q4k_smalln_batch_workspace_bytes(const qg_gemm_problem* problems /* host */, int count);
 qg_status qgemm_q4k_smalln_batch_ws(const qg_gemm_problem* problems /* host */, int count, void* workspace,

@@ -1022,7 +1022,8 @@ __global__ __launch_bounds__(64 * W, 4) void q4k_smalln_stream_kernel(SnArgs a) 
 // fp32 matrix-core product); every column block c of 16 columns reuses one B.
 constexpr int kWkWaves = 16, kWkTiles = 10;
 constexpr int64_t kWkAutoTiles = 1024;
-constexpr int kSpMaxSlices = 16, kSpAutoCols = 3, kSpAutoK1 = 8192;
+constexpr int kSpMaxSlices = 16, kSpAutoCols = 3, kSpAutoK1 = 8192, kSpAutoColsShortK = 12;
+constexpr size_t kSpCtrBytes = 4096;  // the workspace's counter block
 
 
 template <int C, int KC_, int TMAX>
@@ -1496,6 +1497,8 @@ struct SnCfg {
     bool slice;   // ... in the slice kernel where it fits, else in the walk kernel
     bool slice1;  // the slice kernel without K slices, groups of kSl1Tiles tiles
 };
+bool slice_plan_fits(const SnArgs& a, int cus);  // below, with the slice form's plan
+
 SnCfg choose_cfg(const SnArgs& a, int C, bool ws, int cus) {
     const qg_launch_override& ov = qg::launch_override();
     const int form = ov.smalln_form;
@@ -1544,12 +1547,17 @@ SnCfg choose_cfg(const SnArgs& a, int C, bool ws, int cus) {
     // tiles than the many-tile walk takes, and two column blocks or long K
     // (measured on the 7B stages: N = 32 down 41.7 -> 22.2, q/k/v 15.3 -> 12.2; N = 16
     // down 30.2 -> 22.9, N = 8 down 20.1 -> 17.1, N = 5 down 19.6 -> 16.3, N = 4 down
-    // 17.7 (dot form) -> 16.0; but N = 3 down 15.4 (dot) -> 16.0, N = 16 q/k/v 11.2 ->
-    // 13.1 and o 9.9 -> 10.6: with one column block, only long K gains)
+    // 17.7 (dot form) -> 16.0; but N = 3 down 15.4 (dot) -> 16.0; with one column
+    // block and short K the K-sliced walk lost: N = 16 q/k/v 11.2 -> 13.1, o 9.9 ->
+    // 10.6), or one column block of at least kSpAutoColsShortK columns on short K
+    // where the slice form's staging fits (q/k/v and o against the unsliced forms:
+    // N = 12 10.1 -> 9.0 and 8.8 -> 8.4 us, N = 14 10.4 -> 9.5 and 9.1 -> 8.4, N = 16
+    // 11.2 -> 9.5 and 9.9 -> 8.5; at N = 10 o went 8.1 -> 8.4)
+    const bool short_slice = form == QG_FORM_AUTO && C == 1 && ncol >= kSpAutoColsShortK && kmin < kSpAutoK1;
     c.split = c.walk = ws && wk &&
                        (form == QG_FORM_SMALLN_SPLIT || form == QG_FORM_SMALLN_SLICE ||
                         (form == QG_FORM_AUTO && tiles < kWkAutoTiles && ncol >= kSpAutoCols &&
-                         (C == 2 || kmin >= kSpAutoK1)));
+                         (C == 2 || kmin >= kSpAutoK1 || (short_slice && slice_plan_fits(a, cus)))));
     c.slice = c.split && form != QG_FORM_SMALLN_SPLIT;
     if (c.walk) return c;
     // The slice form without K slices, in groups of two tiles, for batches of more
@@ -1815,10 +1823,15 @@ void launch_walk_any(const WkShape& w, const SnArgs& a, int grid, int nmax, hipS
 // Tile groups and K slices of the walk form with a workspace: per problem, groups
 // of w.T tiles (enough units per chunk for the 16 wavefronts), and as many K slices
 // as give the problem its share of one workgroup per CU (at most kSpMaxSlices).
-// Problems left with one slice write Y directly. Workspace: one counter per tile
-// group of the sliced problems (256-byte aligned block), then their partial sums.
-// Fills wgs, slices, slice_sbs, part, ctr, wg_begin and begin; returns the grid and
-// the workspace bytes.
+// Problems left with one slice write Y directly. Workspace: a block of
+// kSpCtrBytes at its start for one counter per tile group of the sliced problems,
+// then their partial sums. The counter block has the same place and size for every
+// batch, so a call's counters always fall where earlier calls on the workspace,
+// whatever their shapes, left zeros (their partial sums never reach it). A sliced
+// problem has at least two slices, so G <= share / 2 tile groups, and the shares
+// add up to at most CUs + count: (256 + 8) / 2 = 132 counters on MI355X, against
+// the block's 1024. Fills wgs, slices, slice_sbs, part, ctr, wg_begin and begin;
+// returns the grid and the workspace bytes, or -1 if the counters would not fit.
 // Workgroup order of a sliced problem, and its slice count. Slice fastest, with a
 // power-of-two slice count: with workgroups dealt to the XCDs in turn, each XCD
 // then runs whole slices only, and its L2 fetches the activations of those
@@ -1856,7 +1869,8 @@ int64_t split_grid(SnArgs& a, int cus, const WkShape& w, void* ws, size_t* need,
             npart += (size_t)H * P.tiles * C * 1024;
         }
     }
-    const size_t ctr_bytes = qg::align_up(nctr * 4, 256);
+    if (nctr * 4 > kSpCtrBytes) return -1;
+    const size_t ctr_bytes = kSpCtrBytes;
     size_t co = 0, po = ctr_bytes;
     for (int i = 0; i < a.count; ++i) {
         SnProb& P = a.p[i];
@@ -1882,7 +1896,7 @@ int64_t split_plan(SnArgs& a, int cus, int C, int nmax, bool slice_ok, void* ws,
     if (slice_ok && C == 1) {
         SnArgs b = a;
         const int64_t grid = split_grid(b, cus, WkShape{1, 8, kSlTiles, kSlTiles}, ws, need, true);
-        if (slice_fits(b)) {
+        if (grid >= 0 && slice_fits(b)) {
             a = b;
             *slice = true;
             return grid;
@@ -1890,6 +1904,14 @@ int64_t split_plan(SnArgs& a, int cus, int C, int nmax, bool slice_ok, void* ws,
     }
     *slice = false;
     return split_grid(a, cus, walk_shape(C, nmax, true), ws, need, false);
+}
+
+// Whether the slice form's plan (tile groups and K slices, one column block) fits
+// every slice's activations in its staging.
+bool slice_plan_fits(const SnArgs& a, int cus) {
+    SnArgs b = a;
+    size_t need = 0;
+    return split_grid(b, cus, WkShape{1, 8, kSlTiles, kSlTiles}, nullptr, &need, true) >= 0 && slice_fits(b);
 }
 
 void launch_lds_any(const SnArgs& a, int grid, int C, int TW, int D, size_t lds, hipStream_t s) {
@@ -1983,6 +2005,7 @@ qg_status run(const qg_gemm_problem* probs, int count, hipStream_t stream, void*
         size_t need = 0;
         bool slice = false;
         const int64_t grid = split_plan(a, qg::device_cus(), C, nmax, cfg.slice, ws, &need, &slice);
+        if (grid < 0) return qg::fail(QG_ERR_SHAPE, "more tile groups than the workspace's counter block holds");
         if (need > 0 && (!ws || ws_bytes < need))
             return qg::fail(QG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
         if (need > 0 && !qg::aligned16(ws)) return qg::fail(QG_ERR_ALIGN, "workspace not 16-byte aligned");

@@ -355,22 +355,22 @@ def test_smalln_ws_sizes_and_validation(L):
     with qg.launch_override(smalln_form=qg.FORM_SMALLN_SPLIT):
         need = L.qgemm_q4k_smalln_batch_workspace_bytes(arr, 2)
         assert need > 0 and need % 256 == 0
-        # one counter per tile group (a 256-byte aligned block), then a partial sum
+        # a fixed 4096-byte block for the tile groups' counters, then a partial sum
         # per K slice, tile and 16-column block, at most 16 slices
-        assert need <= 4 * (224 + 288) + 256 + 16 * (224 + 288) * 2 * 1024
+        assert need <= 4096 + 16 * (224 + 288) * 2 * 1024
     # the slice form's plan for the 7B down projection at N = 5: 56 groups of four
     # tiles, four K slices (18 or 19 super-blocks: 5 x 19 <= 160 staged groups)
     one = (P * 1)(P(C, A, 18944, B, 3584, 3584, 18944, 5))
     with qg.launch_override(smalln_form=qg.FORM_SMALLN_SLICE):
-        assert L.qgemm_q4k_smalln_batch_workspace_bytes(one, 1) == 256 + 4 * 224 * 1024
+        assert L.qgemm_q4k_smalln_batch_workspace_bytes(one, 1) == 4096 + 4 * 224 * 1024
     # long K in the K-sliced walk: groups of 8 tiles at N = 32 (28 groups), the
     # slice count rounded down to a power of two (9 -> 8 slices of two 16-column
     # blocks); groups of 4 at N = 16 (56 groups, 4 slices)
     d32 = (P * 1)(P(C, A, 18944, B, 3584, 3584, 18944, 32))
     d16 = (P * 1)(P(C, A, 18944, B, 3584, 3584, 18944, 16))
     with qg.launch_override(smalln_form=qg.FORM_SMALLN_SPLIT):
-        assert L.qgemm_q4k_smalln_batch_workspace_bytes(d32, 1) == 256 + 8 * 224 * 2048
-        assert L.qgemm_q4k_smalln_batch_workspace_bytes(d16, 1) == 256 + 4 * 224 * 1024
+        assert L.qgemm_q4k_smalln_batch_workspace_bytes(d32, 1) == 4096 + 8 * 224 * 2048
+        assert L.qgemm_q4k_smalln_batch_workspace_bytes(d16, 1) == 4096 + 4 * 224 * 1024
     assert L.qgemm_q4k_smalln_batch_ws(None, 1, None, 0, None) == ENULL
     assert L.qgemm_q4k_smalln_batch_ws(bad, 1, None, 0, None) == ESHAPE
 

@@ -323,7 +323,7 @@ def run_split(N, form, batches, key, what):
             torch.cuda.synchronize()
             for p_, Y0 in zip(probs, first):
                 assert torch.equal(p_[2][:, :p_[3]], Y0[:, :p_[3]]), f"{what} form differs on call {rep + 2}"
-        assert int(ws.buf[:64].ne(0).sum()) == 0, "arrival counters not returned to zero"
+        assert int(ws.buf[:4096].ne(0).sum()) == 0, "arrival counters not returned to zero"
         for (w, X, Y, M, K), Y0, (rows, (Yr, Ar)) in zip(probs, first, refs):
             assert torch.equal(Y[:, :M], Y0[:, :M]), f"{what} form not deterministic"
             assert not torch.isnan(Y[:, :M]).any(), f"{what} form left outputs unwritten"
@@ -359,10 +359,12 @@ def test_slice_form(N):
     run_split(N, qg.FORM_SMALLN_SLICE, batches, 46, "slice")
 
 
-@pytest.mark.parametrize("N", [5, 32])
+@pytest.mark.parametrize("N", [5, 12, 16, 32])
 def test_batch_ws_7b_stages(N):
     # the workspace entry point with the automatic choice on the 7B decode stages
-    # (the q/k/v, o and down stages take the K-sliced walk): sampled rows
+    # (per column count it picks the streamed form, the slice form with or without
+    # K slices, the K-sliced walk or the walk; at N = 12 and 16 the q/k/v and o
+    # stages take the slice form over K slices): sampled rows
     for si, stage in enumerate(workloads.LAYER_STAGES):
         probs, refs = [], []
         for mi in stage:
@@ -380,6 +382,41 @@ def test_batch_ws_7b_stages(N):
             Yc = Y.cpu().numpy()[:, :M][:, rows]
             for n in range(N):
                 assert_within(Yc[n], Yr[n], Ar[n], f"ws stage {si} M={M} K={K} col {n}")
+
+
+def test_ws_shared_across_shapes():
+    # one workspace for batches whose K-sliced plans differ (the 7B down projection at
+    # N = 5: 56 tile groups; q/k/v at N = 12: 72; o at N = 32: 28 in the walk form):
+    # the counters sit in a fixed block, so one batch's partial sums never land on
+    # another's counters, and every call writes all its outputs, bit-identical to a
+    # call on a fresh workspace
+    batches = [[(3584, 18944, 5)], [(3584, 3584, 12), (512, 3584, 12), (512, 3584, 12)], [(3584, 3584, 32)]]
+    runs = []
+    for bi, shapes in enumerate(batches):
+        probs = []
+        for i, (M, K, N) in enumerate(shapes):
+            W = workloads.q4k_blocks(M, K, key=(47, bi, i))
+            X = workloads.x_columns(K, N, key=(47, bi, i, N))
+            probs.append((packed_q4k(W, M, K), to_dev(X), torch.full((N, (M + 3) // 4 * 4), float("nan"),
+                                                                     device="cuda:0"), M, K))
+        need = qg.qgemm_q4k_smalln_batch_workspace_bytes(probs)
+        assert need > 0, shapes
+        case(f"qgemm_q4k_smalln_batch_ws fresh workspace, batch {bi}: {shapes}")
+        qg.qgemm_q4k_smalln_batch_ws(probs, qg.Workspace("cuda:0", need))
+        torch.cuda.synchronize()
+        runs.append((probs, need, [p[2].clone() for p in probs]))
+    shared = qg.Workspace("cuda:0", max(r[1] for r in runs))
+    for step, bi in enumerate([0, 1, 2, 1, 0, 2, 1]):
+        probs, _, ref = runs[bi]
+        for p_ in probs:
+            p_[2].fill_(float("nan"))
+        case(f"qgemm_q4k_smalln_batch_ws shared workspace, call {step}: batch {bi}")
+        qg.qgemm_q4k_smalln_batch_ws(probs, shared)
+        torch.cuda.synchronize()
+        for (w, X, Y, M, K), Y0 in zip(probs, ref):
+            assert not torch.isnan(Y[:, :M]).any(), f"call {step}, batch {bi}: outputs left unwritten"
+            assert torch.equal(Y[:, :M], Y0[:, :M]), f"call {step}, batch {bi}: differs from a fresh workspace"
+    assert int(shared.buf[:4096].count_nonzero()) == 0, "arrival counters not returned to zero"
 
 
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8])
