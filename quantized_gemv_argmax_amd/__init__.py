@@ -448,8 +448,10 @@ def qgemm_q4k_smalln_batch_workspace_bytes(problems) -> int:
 def qgemm_q4k_smalln_batch_ws(problems, ws: Workspace | None = None):
     """qgemm_q4k_smalln_batch with a workspace (sized by
     qgemm_q4k_smalln_batch_workspace_bytes; a per-device scratch buffer if None),
-    which lets the library split few-tile, many-column products over K slices. The
-    workspace's contents are left undefined."""
+    which lets the library split few-tile, many-column products over K slices. One
+    workspace serves batches of any shapes; its counters come back zero and the rest
+    of it undefined. Calls sharing a workspace (the scratch one included) must not
+    overlap: calls on concurrent streams pass workspaces of their own."""
     arr, dev = _gemm_problems(problems)
     need = lib().qgemm_q4k_smalln_batch_workspace_bytes(arr, len(problems))
     if ws is None:  # scratch contents: never the zero-kept workspace of the LM-head calls
