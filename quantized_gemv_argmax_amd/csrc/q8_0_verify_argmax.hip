@@ -24,6 +24,7 @@
 // matrix-core stage 1 serves N > 8 (and K > 4096 above 6 columns); the streamed
 // form below takes N <= 8 with K <= 4096, the vector-ALU form the rest.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstdlib>
 #include <cstring>
@@ -538,7 +539,7 @@ void vd_launch(const VdProb& P, int W, hipStream_t s) {
 // per dword), logit += d 2^24 S' in fp32; the bias -128 d X[n] of four blocks is
 // one v_mfma_f32_16x16x4_f32 (A the table entries -X, B 128 d of the lane's row),
 // accumulated across the tile's units.
-constexpr int kVsWaves = 8, kVsCols = 8;
+constexpr int kVsWaves = 8, kVsCols = 16;  // columns staged: 8 in one instance, 16 in the other
 // The automatic choice for every N it takes (152064 x 3584, us, streamed / vector-ALU
 // dot / matrix-core forms: N = 1 93.3 / 95.0 / 134.5, 2 92.2 / 96.4 / 135.7,
 // 4 92.6 / 105.2 / 138.5, 5 93.2 / 115.8 / 139.2, 6 93.1 / 125.9 / 141.3,
@@ -606,8 +607,11 @@ QG_DEV void vs_dot(qg_f4& acc, qg_f4& accm, const VsItem& it, const unsigned cha
     }
 }
 
-template <int W>
-__global__ __launch_bounds__(64 * W, 4) void lmhead_verify_stream_kernel(VsProb P) {
+template <int W, int NC>
+__global__ __launch_bounds__(64 * W, NC == 8 ? 4 : 2) void lmhead_verify_stream_kernel(VsProb P) {
+    // lanes holding real columns (column 4 (l / 16) + e of lane l): 32 for 8 columns,
+    // all 64 for 16
+    constexpr int LN = 4 * NC;
     extern __shared__ __align__(16) unsigned char lds[];
     const int j = blockIdx.x;
     const int G = P.G;
@@ -619,7 +623,7 @@ __global__ __launch_bounds__(64 * W, 4) void lmhead_verify_stream_kernel(VsProb 
     const int K = nmb * 256;
     const int RB = (K + 8) * 2;
     const uint32_t xsb = (uint32_t)(P.N * RB);          // table of -X per block, 16 columns
-    qg_f4* park = reinterpret_cast<qg_f4*>(lds + xsb + 2 * K);  // [2 buffers][2 slots][W][32 lanes]
+    qg_f4* park = reinterpret_cast<qg_f4*>(lds + xsb + 2 * K);  // [2 buffers][2 slots][W][LN lanes]
     const __amdgpu_buffer_rsrc_t wr =
         __builtin_amdgcn_make_buffer_rsrc((void*)P.w, (short)0, P.M * nmb * 272, kQgRawBufferFlags);
 
@@ -628,9 +632,9 @@ __global__ __launch_bounds__(64 * W, 4) void lmhead_verify_stream_kernel(VsProb 
     const int gpr = K / 8;
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)P.X, (short)0, (int)(((int64_t)(P.N - 1) * P.ldx + K) * 4), kQgRawBufferFlags);
-    float4 v[kVsCols][2];
+    float4 v[NC][2];
 #pragma unroll
-    for (int n = 0; n < kVsCols; ++n) {
+    for (int n = 0; n < NC; ++n) {
         const uint32_t off = (n < P.N && tid < gpr) ? (uint32_t)(((int64_t)n * P.ldx + 8 * tid) * 4) : kQgOutOfRange;
         v[n][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
         v[n][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 16, 0));
@@ -654,14 +658,14 @@ __global__ __launch_bounds__(64 * W, 4) void lmhead_verify_stream_kernel(VsProb 
     advance(lt, lb);
 
 #pragma unroll
-    for (int n = 0; n < kVsCols; ++n) {
+    for (int n = 0; n < NC; ++n) {
         const qg_h8 h = qg_a_operand(v[n][0], v[n][1]);
         if (n < P.N && tid < gpr) *reinterpret_cast<qg_h8*>(lds + n * RB + 16 * tid) = h;
         const uint4 hw = __builtin_bit_cast(uint4, h);
         const float xsum = qg_quad_sum(qg_sum_pairs4(hw.x, hw.y, hw.z, hw.w));
         if ((tid & 3) == 0 && tid < gpr) *reinterpret_cast<float*>(lds + xsb + ((tid >> 2) * 16 + n) * 4) = -xsum;
     }
-    if ((tid & 3) == 0 && tid < gpr) {  // columns 8..15 of the table: zeros
+    if (NC == 8 && (tid & 3) == 0 && tid < gpr) {  // columns 8..15 of the table: zeros
         *reinterpret_cast<uint4*>(lds + xsb + ((tid >> 2) * 16 + 8) * 4) = make_uint4(0u, 0u, 0u, 0u);
         *reinterpret_cast<uint4*>(lds + xsb + ((tid >> 2) * 16 + 12) * 4) = make_uint4(0u, 0u, 0u, 0u);
     }
@@ -684,19 +688,19 @@ __global__ __launch_bounds__(64 * W, 4) void lmhead_verify_stream_kernel(VsProb 
     // end of round `round`: park, barrier, reduce its tiles (wavefronts 2 round % W
     // and 2 round % W + 1), start the next
     auto end_round = [&]() {
-        qg_f4* pb = park + (size_t)(round & 1) * 2 * W * 32;
-        if (lane < 32) {
-            pb[(0 * W + wave) * 32 + lane] = acc[0] + accm[0];
-            pb[(1 * W + wave) * 32 + lane] = acc[1] + accm[1];
+        qg_f4* pb = park + (size_t)(round & 1) * 2 * W * LN;
+        if (lane < LN) {
+            pb[(0 * W + wave) * LN + lane] = acc[0] + accm[0];
+            pb[(1 * W + wave) * LN + lane] = acc[1] + accm[1];
         }
         acc[0] = acc[1] = accm[0] = accm[1] = qg_f4{0.f, 0.f, 0.f, 0.f};
         sw_vs_barrier();
         const int q = wave - (2 * round) % W;  // this wavefront's slot in the round, if 0 or 1
         const int ts = 2 * round + q;
-        if ((q == 0 || q == 1) && ts < nt && lane < 32) {
-            qg_f4 sum = pb[(q * W) * 32 + lane];
+        if ((q == 0 || q == 1) && ts < nt && lane < LN) {
+            qg_f4 sum = pb[(q * W) * LN + lane];
 #pragma unroll
-            for (int w = 1; w < W; ++w) sum += pb[(q * W + w) * 32 + lane];
+            for (int w = 1; w < W; ++w) sum += pb[(q * W + w) * LN + lane];
             const int t = j + ts * G;
             const int rt = min(T, P.M - t * T);
 #pragma unroll
@@ -744,10 +748,13 @@ __global__ __launch_bounds__(64 * W, 4) void lmhead_verify_stream_kernel(VsProb 
     const int nrounds = (nt + 1) / 2;
     while (round < nrounds) end_round();
 
-    // the wavefronts' running results meet in LDS (the columns are no longer read)
+    // the wavefronts' running results meet in LDS, over the columns and, for short
+    // K, the parked sums, which the last round's reducing wavefronts may still be
+    // reading: everyone waits for them first
+    sw_vs_barrier();
     float* bvs = reinterpret_cast<float*>(lds);
-    int* bis = reinterpret_cast<int*>(lds + W * 32 * 4 * 4);
-    if (lane < 32)
+    int* bis = reinterpret_cast<int*>(lds + W * LN * 4 * 4);
+    if (lane < LN)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             // rows first: the lanes i = 0..15 of column 4 s + e
@@ -762,19 +769,19 @@ __global__ __launch_bounds__(64 * W, 4) void lmhead_verify_stream_kernel(VsProb 
                     idx = oi;
                 }
             }
-            bvs[(wave * 32 + lane) * 4 + e] = vv;
-            bis[(wave * 32 + lane) * 4 + e] = idx;
+            bvs[(wave * LN + lane) * 4 + e] = vv;
+            bis[(wave * LN + lane) * 4 + e] = idx;
         }
     sw_vs_barrier();
-    if (wave != 0 || i != 0 || lane >= 32) return;
+    if (wave != 0 || i != 0 || lane >= LN) return;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         float vv = bvs[lane * 4 + e];
         int idx = bis[lane * 4 + e];
 #pragma unroll
         for (int w = 1; w < W; ++w) {
-            const float ov = bvs[(w * 32 + lane) * 4 + e];
-            const int oi = bis[(w * 32 + lane) * 4 + e];
+            const float ov = bvs[(w * LN + lane) * 4 + e];
+            const int oi = bis[(w * LN + lane) * 4 + e];
             if (va_better(ov, oi, vv, idx)) {
                 vv = ov;
                 idx = oi;
@@ -787,7 +794,7 @@ __global__ __launch_bounds__(64 * W, 4) void lmhead_verify_stream_kernel(VsProb 
 
 // Dynamic LDS of the streamed form: the columns, their block sums, the parked sums.
 size_t vs_lds_bytes(int64_t K, int64_t N) {
-    return (size_t)N * (K + 8) * 2 + 2 * (size_t)K + 2 * 2 * kVsWaves * 32 * 16;
+    return (size_t)N * (K + 8) * 2 + 2 * (size_t)K + 2 * 2 * kVsWaves * (N <= 8 ? 32 : 64) * 16;
 }
 
 // ---------------------------------------------------------------------------
@@ -1011,7 +1018,7 @@ qg_status lmhead_argmax_verify(const void* w, const float* X, int64_t ldx, int64
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
     const qg_launch_override& ov = qg::launch_override();
-    // streamed form: up to 8 columns, K <= 4096 (one round of column loads), weights
+    // streamed form: up to 16 columns, K <= 4096 (one round of column loads), weights
     // under 2 GiB (one buffer resource)
     const bool vs_ok = N <= kVsCols && K <= 512 * kVsWaves && M * (K / 256) * 272 < (int64_t)INT32_MAX &&
                        vs_lds_bytes(K, N) <= 160 * 1024;
@@ -1030,12 +1037,13 @@ qg_status lmhead_argmax_verify(const void* w, const float* X, int64_t ldx, int64
         const size_t lds = vs_lds_bytes(K, N);
         const int per_cu = lds <= 80 * 1024 ? 2 : 1;
         V.G = (int32_t)std::min<int64_t>(V.tiles, (int64_t)per_cu * qg::device_cus());
-        const auto kern = lmhead_verify_stream_kernel<kVsWaves>;
-        static bool attr_set[64];
+        const auto kern = N <= 8 ? lmhead_verify_stream_kernel<kVsWaves, 8> : lmhead_verify_stream_kernel<kVsWaves, 16>;
+        static std::atomic<bool> attr_set[2][64];  // per instance and device
+        std::atomic<bool>* set = attr_set[N <= 8 ? 0 : 1];
         int dev = 0;
-        if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr_set[dev]) {
+        if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !set[dev].load(std::memory_order_acquire)) {
             (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-            attr_set[dev] = true;
+            set[dev].store(true, std::memory_order_release);
         }
         hipLaunchKernelGGL(kern, dim3((unsigned)V.G), dim3(64 * kVsWaves), lds, s, V);
         st = qg::launch_status("lmhead_argmax_verify (tiles)");

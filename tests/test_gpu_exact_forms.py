@@ -243,7 +243,8 @@ def expected_ids(W, M, K, X):
                                           ("mfma", 20, 4, 1), ("mfma", 32, 4, 2), ("dot", 1, 1, 0),
                                           ("dot", 5, 1, 0), ("dot", 6, 4, 0), ("auto", 5, 0, 0),
                                           ("auto", 17, 0, 0), ("stream", 1, 0, 0), ("stream", 5, 0, 0),
-                                          ("stream", 8, 0, 0)])
+                                          ("stream", 8, 0, 0), ("stream", 9, 0, 0), ("stream", 16, 0, 0),
+                                          ("auto", 12, 0, 0)])
 def test_verify_integer_exact(form, N, W_, TW):
     M, K = 5000, 1536
     rng = np.random.default_rng(N)

@@ -242,12 +242,12 @@ def test_verify_vector_alu_form_shapes(cfg, N):
     assert int(ws.buf.count_nonzero()) == 0
 
 
-@pytest.mark.parametrize("N", [1, 2, 5, 8])
+@pytest.mark.parametrize("N", [1, 2, 5, 8, 9, 12, 16])
 def test_verify_streamed_form_shapes(N):
     # the streamed form (grid of resident workgroups walking tiles in rounds of
-    # two): one tile (a single round of one tile), one macro-block, a ragged last
-    # tile, walks of many tiles with K = 4096 (its largest); the workspace is left
-    # zero
+    # two), in its 8-column and 16-column instances: one tile (a single round of
+    # one tile), one macro-block, a ragged last tile, walks of many tiles with
+    # K = 4096 (its largest); the workspace is left zero
     qg.launch_override(verify_form=qg.FORM_VERIFY_STREAM).set()
     for key, (M, K) in enumerate([(16, 256), (33, 768), (1000, 2816), (20000, 4096)]):
         W = workloads.q8_0_blocks(M, K, key=(28, M))
