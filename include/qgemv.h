@@ -452,7 +452,7 @@ qg_status lmhead_topk(const void* w_packed, const float* x, int64_t M, int64_t K
  *   smalln_tiles  16-row tiles per workgroup (matrix-core forms): 1, 2, 4.
  *   smalln_depth  weight-queue depth in chunks of the chunked-LDS form: 2..4.
  *   verify_form   lmhead_argmax_verify: matrix-core, vector-ALU dot, or streamed
- *                 matrix-core form (N <= 8, K <= 4096).
+ *                 matrix-core form (N <= 16, K <= 4096).
  *   verify_waves  wavefronts per workgroup of the verify tile kernels (the dot
  *                 and int8 forms: 1 or 4; the matrix-core form: 4 or 8).
  *   verify_tiles  tiles per workgroup of the matrix-core verify form: 1, 2, 4.
