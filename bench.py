@@ -479,6 +479,17 @@ def other_rows(torch, np, qg, wl, dev, ws, layers, n_layers):
                                             "bytes": int(b), "us_per_single_column_argmax": round(
                                                 rows["lmhead_argmax_152064x3584"]["us"], 3)}
     log(f"row lmhead verify N=5: {rows['lmhead_verify_N5_152064x3584']}")
+    # sixteen columns (15 drafts + 1), still one pass over the head
+    N16 = 16
+    X16 = torch.from_numpy(wl.x_columns(K, N16, key=(4, 4))).to(dev)
+    oi16 = torch.empty(N16, dtype=torch.int32, device=dev)
+    ov16 = torch.empty(N16, dtype=torch.float32, device=dev)
+    ms = graph_ms(torch, lambda: [qg.lmhead_argmax_verify(c, X16, M, K, out_index=oi16, out_value=ov16, ws=ws)
+                                  for c in copies], 20) / 2
+    b = wp.numel() + 4 * K * N16 + 8 * (-(-M // 16)) * N16 * 2 + 8 * N16
+    rows["lmhead_verify_N16_152064x3584"] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                                             "bytes": int(b)}
+    log(f"row lmhead verify N=16: {rows['lmhead_verify_N16_152064x3584']}")
 
     # the same verification on int8 activations: the five fp32 columns are quantized
     # (one launch) and verified, both inside the timed region
